@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs shared by the oracle-side tests, the GPU parity
+tests, the benchmark and the smoke check.
+
+This module only draws random numbers in fixed shapes and distributions.  It
+holds none of the method's arithmetic: no unpacking, no dequantization, no
+matmul, no routing.  Every array is produced on the host with
+``numpy.random.default_rng(seed)`` in a fixed draw order, so the GPU path and
+the oracle read the very same bytes.
+
+Distributions (the workload the pages benchmark is a Qwen-style MoE with
+group-affine 4-bit weights; no checkpoint or prompt text is available, so
+these seeded draws stand in for it):
+
+* activations: fp16 of N(0, 1);
+* 4-bit codes: i.i.d. uniform in 0..15.  Eight independent uniform nibbles
+  are exactly one uniform 32-bit word, so the packed words are drawn directly
+  as uniform uint32 (this is a statement about the distribution, not a pack
+  step: which nibble holds which k is fixed by the layout, not here);
+* per-group scale: fp16 of U(0.002, 0.02);
+* per-group bias: fp16 of (-8 * scale_fp16 + N(0, 1e-3)), so that code 8
+  reconstructs to roughly zero;
+* router weight [D][E]: fp16 of N(0, 0.02) (0.02 read as a standard
+  deviation);
+* skewed-load logit bias: b_e = -1.1 * ln(rank_e), ranks a seeded
+  permutation of 1..E (the logarithm of a Zipf law with s = 1.1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+
+# Shapes of the Qwen-style MoE layer the pages benchmark (hidden 2048,
+# 256 routed experts of width 512, top-8, plus one shared expert).
+HIDDEN = 2048
+EXPERT_WIDTH = 512
+NUM_EXPERTS = 256
+TOPK = 8
+VOCAB = 151552
+
+
+def rng_for(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def f16(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float16)
+
+
+def activations(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
+    """fp16 [rows][cols] drawn from N(0, 1)."""
+    return f16(rng.standard_normal((rows, cols)))
+
+
+def w4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
+    """One (or a stack of) group-affine 4-bit K x N matrices.
+
+    Returns a dict with ``qweight`` uint32 [*lead, N, K/8], ``scales`` and
+    ``biases`` fp16 [*lead, N, K/64], and the sizes.  ``lead=(E,)`` draws E
+    experts stacked contiguously.
+    """
+    if K % 8:
+        raise ValueError("K must be a multiple of 8 to draw packed words")
+    G = (K + GROUP - 1) // GROUP
+    words = rng.integers(0, 2**32, size=lead + (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    scales = f16(rng.uniform(0.002, 0.02, size=lead + (N, G)))
+    noise = rng.normal(0.0, 1e-3, size=lead + (N, G))
+    biases = f16(-8.0 * scales.astype(np.float64) + noise)
+    return {"qweight": words, "scales": scales, "biases": biases, "K": K, "N": N}
+
+
+def router_weight(rng: np.random.Generator, D: int = HIDDEN, E: int = NUM_EXPERTS) -> np.ndarray:
+    """fp16 [D][E] drawn from N(0, 0.02)."""
+    return f16(rng.normal(0.0, 0.02, size=(D, E)))
+
+
+def zipf_logit_bias(rng: np.random.Generator, E: int = NUM_EXPERTS, s: float = 1.1) -> np.ndarray:
+    """fp32 [E]: -s * ln(rank_e) with ranks a seeded permutation of 1..E."""
+    ranks = rng.permutation(E) + 1
+    return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
+
+
+def synthetic_topk_ids(rng: np.random.Generator, T: int, E: int, topk: int,
+                       skew: float = 0.0) -> np.ndarray:
+    """int32 [T][topk]: distinct expert ids per token, drawn without
+    replacement.  ``skew > 0`` weights expert e by (rank_e)^-skew so some
+    experts get many rows and some none.  Used to drive the dispatch steps
+    with routing that does not come from any router."""
+    if topk > E:
+        raise ValueError("topk > E")
+    if skew > 0:
+        ranks = rng.permutation(E) + 1
+        w = ranks.astype(np.float64) ** (-skew)
+        p = w / w.sum()
+    else:
+        p = None
+    out = np.empty((T, topk), dtype=np.int32)
+    for t in range(T):
+        out[t] = rng.choice(E, size=topk, replace=False, p=p)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Workloads.  Each builder fixes the order of its draws.
+# ----------------------------------------------------------------------------
+
+def gemv_case(seed: int, K: int, N: int) -> dict:
+    """x fp16 [1][K] and one K x N w4 matrix."""
+    rng = rng_for(seed)
+    x = activations(rng, 1, K)
+    W = w4_matrix(rng, K, N)
+    return {"x": x, "W": W}
+
+
+def gemm_case(seed: int, M: int, K: int, N: int) -> dict:
+    """X fp16 [M][K] and one K x N w4 matrix."""
+    rng = rng_for(seed)
+    X = activations(rng, M, K)
+    W = w4_matrix(rng, K, N)
+    return {"X": X, "W": W}
+
+
+def moe_weights(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:
+    """Router [D][E] fp16, E stacked experts and one shared expert.
+
+    gate_up: K = D, N = 2*I (columns [0, I) gate, [I, 2I) up);
+    down:    K = I, N = D.
+    """
+    rng = rng_for(seed)
+    Wr = router_weight(rng, D, E)
+    gate_up = w4_matrix(rng, D, 2 * I, lead=(E,))
+    down = w4_matrix(rng, I, D, lead=(E,))
+    shared_gate_up = w4_matrix(rng, D, 2 * I)
+    shared_down = w4_matrix(rng, I, D)
+    return {"Wr": Wr, "gate_up": gate_up, "down": down,
+            "shared_gate_up": shared_gate_up, "shared_down": shared_down,
+            "D": D, "I": I, "E": E}
+
+
+def moe_tokens(seed: int, T: int, D: int = HIDDEN, E: int = NUM_EXPERTS,
+               skewed: bool = False) -> dict:
+    """H fp16 [T][D] ~ N(0, 1) and, if ``skewed``, the Zipf logit bias."""
+    rng = rng_for(seed)
+    H = activations(rng, T, D)
+    bias = zipf_logit_bias(rng, E) if skewed else None
+    return {"H": H, "logit_bias": bias}
+
+
+# Default configurations of the benchmarked workload.
+CONFIGS = {
+    0: dict(kind="gemv", K=512, N=512),
+    1: dict(kind="gemv", K=2048, N=(8192, VOCAB)),
+    2: dict(kind="gemm", M=4096, K=2048, N=8192, sweep=(256, 1024, 16384)),
+    3: dict(kind="moe", T=1, skewed=False),
+    4: dict(kind="moe", T=4096, skewed=True),
+}

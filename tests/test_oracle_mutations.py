@@ -1,0 +1,167 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin fails for each: the pins are only worth something if they
+catch a dropped term, a wrong sign, a wrong index or a transposed operand."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe as omoe
+import oracle.route as oroute
+import oracle.w4 as ow4
+from tests import test_oracle_moe as tm
+from tests import test_oracle_route as tr
+from tests import test_oracle_w4 as tw
+
+W4_PINS = [tw.test_gemv_hand_fixture, tw.test_one_hot_picks_single_weight,
+           tw.test_affine_identity_all_equal_codes, tw.test_zero_case_code8,
+           tw.test_integer_special_case_exact, tw.test_bruteforce_fsum_small,
+           tw.test_pack_words_hand, tw.test_dequantize_exact_rational]
+
+
+def _fails(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+_orig_unpack = ow4.unpack_codes
+
+
+def _unpack_reversed(qweight, K):
+    c = _orig_unpack(qweight, K)
+    out = c.copy()
+    for j in range(8):
+        out[..., j::8] = c[..., (7 - j)::8]
+    return out
+
+
+def _dequant_no_bias(qweight, scales, biases, K):
+    q = ow4.unpack_codes(qweight, K).astype(np.float64)
+    s = np.repeat(np.asarray(scales, np.float16).astype(np.float64), 64, axis=-1)
+    return s * q
+
+
+def _dequant_bias_sign(qweight, scales, biases, K):
+    q = ow4.unpack_codes(qweight, K).astype(np.float64)
+    s = np.repeat(np.asarray(scales, np.float16).astype(np.float64), 64, axis=-1)
+    b = np.repeat(np.asarray(biases, np.float16).astype(np.float64), 64, axis=-1)
+    return s * q - b
+
+
+def _dequant_wrong_group(qweight, scales, biases, K):
+    q = ow4.unpack_codes(qweight, K).astype(np.float64)
+    s = np.tile(np.asarray(scales, np.float16).astype(np.float64), 64)
+    b = np.tile(np.asarray(biases, np.float16).astype(np.float64), 64)
+    return s * q + b
+
+
+def _linear_transposed(X, W, row_chunk=8192):
+    X = np.atleast_2d(np.asarray(X)).astype(np.float64)
+    Wd = ow4.dequantize(W["qweight"], W["scales"], W["biases"], W["K"])
+    return X @ Wd.T[::-1, ::-1] if Wd.shape[0] == Wd.shape[1] else X @ Wd.T[:, ::-1]
+
+
+@pytest.mark.parametrize("target,attr,mutant", [
+    (ow4, "unpack_codes", _unpack_reversed),
+    (ow4, "dequantize", _dequant_no_bias),
+    (ow4, "dequantize", _dequant_bias_sign),
+    (ow4, "dequantize", _dequant_wrong_group),
+])
+def test_w4_mutants_are_caught(monkeypatch, target, attr, mutant):
+    monkeypatch.setattr(target, attr, mutant)
+    assert _fails(W4_PINS)
+
+
+def test_transposed_linear_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "linear", _linear_transposed)
+    assert _fails(W4_PINS)
+
+
+def _topk_ties_high(logits, topk):
+    L = np.asarray(logits, np.float64)
+    p = oroute.softmax(L)
+    ids = np.empty((L.shape[0], topk), np.int32)
+    gates = np.empty((L.shape[0], topk))
+    for t in range(L.shape[0]):
+        order = np.lexsort((-np.arange(L.shape[1]), -p[t]))[:topk]
+        ids[t], gates[t] = order, p[t, order] / p[t, order].sum()
+    return ids, gates
+
+
+def _topk_unnormalised(logits, topk):
+    ids, _ = _ORIG_TOPK(logits, topk)
+    p = oroute.softmax(logits)
+    return ids, np.take_along_axis(p, ids.astype(np.int64), axis=1)
+
+
+_ORIG_TOPK = oroute.topk_route
+
+
+def _perm_unstable(ids, E):
+    flat = np.asarray(ids).ravel()
+    sa = np.argsort(flat * 100000 - np.arange(flat.size))  # descending a inside groups
+    pos = np.empty_like(sa)
+    pos[sa] = np.arange(sa.size)
+    return sa.astype(np.int32), pos.astype(np.int32)
+
+
+def _scan_inclusive(counts):
+    c = np.asarray(counts, np.int64)
+    return np.concatenate([np.cumsum(c), [c.sum()]]).astype(np.int32)
+
+
+ROUTE_PINS = [tr.test_route_hand_fixture, tr.test_equal_logits_pick_lowest_indices,
+              tr.test_bruteforce_subsets_tiny_E, tr.test_dispatch_hand_fixture,
+              tr.test_dispatch_invariants_and_library_sort]
+
+
+@pytest.mark.parametrize("target,attr,mutant", [
+    (oroute, "topk_route", _topk_ties_high),
+    (oroute, "topk_route", _topk_unnormalised),
+    (oroute, "stable_permutation", _perm_unstable),
+    (oroute, "exclusive_scan", _scan_inclusive),
+])
+def test_route_mutants_are_caught(monkeypatch, target, attr, mutant):
+    monkeypatch.setattr(target, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant)
+    assert _fails(ROUTE_PINS)
+
+
+_ORIG_COMBINE = omoe.combine
+
+
+def _combine_no_shared(ydown, gates, pos, T, topk, has_shared):
+    return _ORIG_COMBINE(ydown, gates, pos, T, topk, False)
+
+
+def _combine_wrong_row(ydown, gates, pos, T, topk, has_shared):
+    ident = np.arange(len(pos))
+    return _ORIG_COMBINE(ydown, gates, ident, T, topk, has_shared)
+
+
+def _combine_gates_reversed(ydown, gates, pos, T, topk, has_shared):
+    return _ORIG_COMBINE(ydown, np.asarray(gates)[:, ::-1], pos, T, topk, has_shared)
+
+
+def _silu_sign(z):
+    z = np.asarray(z, np.float64)
+    return z / (1.0 + np.exp(z))
+
+
+MOE_PINS = [tm.test_moe_layer_matches_per_token_bruteforce, tm.test_identical_experts_give_twice_the_ffn,
+            tm.test_power_of_two_scaled_experts_pin_gate_to_id, tm.test_silu_library_and_limits]
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("combine", _combine_no_shared),
+    ("combine", _combine_wrong_row),
+    ("combine", _combine_gates_reversed),
+    ("silu", _silu_sign),
+])
+def test_moe_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(omoe, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant)
+    assert _fails(MOE_PINS)

@@ -1,0 +1,243 @@
+"""Python binding of libqlinear (group-affine 4-bit linear layers and
+routed-expert MoE on MI355X / gfx950).
+
+Argument marshalling only: every function here checks nothing beyond what
+is needed to build the C call, passes device pointers from torch tensors
+and the current HIP stream, and raises QLError on a nonzero status.  All
+arithmetic runs in the HIP kernels of the library.  There is no fallback:
+if the library is not built, importing the functions works but every call
+raises.
+
+Weights are passed as dicts of torch tensors with keys ``qweight`` (int32
+or uint32-as-int32, [N, K/8] or [E, N, K/8]), ``scales`` and ``biases``
+(float16, [N, K/64] or [E, N, K/64]) and ints ``K`` and ``N``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqlinear.so")
+
+QL_OK = 0
+QL_OP_GATE_UP_SILU = 1
+QL_OP_DOWN = 2
+QL_OP_DOWN_COMBINE = 3
+QL_MOE_TILE_ROWS = 128
+QL_DECODE_MAX_T = 4
+GROUP = 64
+
+
+class QLError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class ql_w4(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("group_size", ctypes.c_int32)]
+
+
+class ql_w4_experts(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("num_experts", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "ql_layout_version": (ctypes.c_int, []),
+    "ql_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlinear_pack": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
+    "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
+    "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "moe_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "ql_moe_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "moe_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                 _P, ctypes.c_size_t, _P]),
+    "moe_dispatch": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4), _P,
+                                        _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                        _P, _P]),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m bit_group_quantized_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != QL_OK:
+        raise QLError(fn, status, lib().ql_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_w4(W: dict) -> ql_w4:
+    return ql_w4(W["qweight"].data_ptr(), W["scales"].data_ptr(), W["biases"].data_ptr(),
+                 int(W["K"]), int(W["N"]), GROUP)
+
+
+def make_w4_experts(W: dict) -> ql_w4_experts:
+    return ql_w4_experts(W["qweight"].data_ptr(), W["scales"].data_ptr(), W["biases"].data_ptr(),
+                         int(W["K"]), int(W["N"]), GROUP, int(W["qweight"].shape[0]))
+
+
+def ql_layout_version() -> int:
+    return lib().ql_layout_version()
+
+
+def qlinear_pack(codes, qweight=None, stream=None):
+    """codes uint8 [N, K] (values 0..15) -> packed int32 [N, K/8] on the device."""
+    import torch
+    N, K = codes.shape
+    if qweight is None:
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
+    _check("qlinear_pack", lib().qlinear_pack(_ptr(codes), N, K, _ptr(qweight), _stream(stream)))
+    return qweight
+
+
+def qlinear_gemv(W: dict, x, y=None, stream=None):
+    """y [N] fp16 = x [K] fp16 . dequant(W)."""
+    import torch
+    if y is None:
+        y = torch.empty((int(W["N"]),), dtype=torch.float16, device=x.device)
+    w = make_w4(W)
+    _check("qlinear_gemv", lib().qlinear_gemv(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
+    return y
+
+
+def qlinear_gemm(W: dict, X, Y=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 . dequant(W)."""
+    import torch
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
+    w = make_w4(W)
+    _check("qlinear_gemm", lib().qlinear_gemm(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def moe_workspace_bytes(T: int, E: int, topk: int) -> int:
+    return int(lib().moe_workspace_bytes(T, E, topk))
+
+
+def ql_moe_logits_offset(T: int, E: int, topk: int) -> int:
+    return int(lib().ql_moe_logits_offset(T, E, topk))
+
+
+def alloc_route_outputs(T: int, E: int, topk: int, device):
+    """Device buffers for moe_route / moe_dispatch outputs."""
+    import torch
+    i32 = dict(dtype=torch.int32, device=device)
+    ws_bytes = moe_workspace_bytes(T, E, topk)
+    return {
+        "ids": torch.empty((T, topk), **i32),
+        "gates": torch.empty((T, topk), dtype=torch.float32, device=device),
+        "counts": torch.empty((E,), **i32),
+        "offsets": torch.empty((E + 1,), **i32),
+        "sorted_assign": torch.empty((T * topk,), **i32),
+        "pos": torch.empty((T * topk,), **i32),
+        "workspace": torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
+    }
+
+
+def moe_route(H, Wr, logit_bias, topk: int, out: dict | None = None, stream=None) -> dict:
+    T, D = H.shape
+    E = Wr.shape[1]
+    if out is None:
+        out = alloc_route_outputs(T, E, topk, H.device)
+    ws = out["workspace"]
+    _check("moe_route", lib().moe_route(
+        _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, _ptr(out["ids"]), _ptr(out["gates"]),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sorted_assign"]), _ptr(out["pos"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_dispatch(ids, E: int, out: dict | None = None, stream=None) -> dict:
+    T, topk = ids.shape
+    if out is None:
+        out = alloc_route_outputs(T, E, topk, ids.device)
+    out["ids"] = ids
+    ws = out["workspace"]
+    _check("moe_dispatch", lib().moe_dispatch(
+        _ptr(ids), T, E, topk, _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["sorted_assign"]), _ptr(out["pos"]), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_grouped_gemm(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
+                     Y=None, stream=None):
+    """Expert projections over the routed rows described by ``route`` (the
+    dict returned by moe_route / moe_dispatch)."""
+    import torch
+    w = make_w4_experts(W)
+    s = make_w4(shared) if shared is not None else None
+    rows = T * topk + (T if shared is not None else 0)
+    if Y is None:
+        if op == QL_OP_GATE_UP_SILU:
+            shape = (rows, int(W["N"]) // 2)
+        elif op == QL_OP_DOWN:
+            shape = (rows, int(W["N"]))
+        else:
+            shape = (T, int(W["N"]))
+        Y = torch.empty(shape, dtype=torch.float16, device=X.device)
+    ws = route["workspace"]
+    _check("moe_grouped_gemm", lib().moe_grouped_gemm(
+        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
+        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(route.get("gates")),
+        _ptr(route.get("pos")), _ptr(ws), ws.numel(), _ptr(Y), _stream(stream)))
+    return Y
+
+
+def moe_combine(Ydown, gates, pos, T: int, topk: int, has_shared: bool, out=None, stream=None):
+    import torch
+    N = Ydown.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=Ydown.device)
+    _check("moe_combine", lib().moe_combine(_ptr(Ydown), _ptr(gates), _ptr(pos), T, topk, N,
+                                            1 if has_shared else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+def to_device_w4(W: dict, device) -> dict:
+    """Copy a host w4 dict (numpy, as drawn by the input generators) to the
+    device as torch tensors.  Pure data movement."""
+    import numpy as np
+    import torch
+    q = np.ascontiguousarray(W["qweight"]).view(np.int32)
+    return {"qweight": torch.from_numpy(q).to(device),
+            "scales": torch.from_numpy(np.ascontiguousarray(W["scales"])).to(device),
+            "biases": torch.from_numpy(np.ascontiguousarray(W["biases"])).to(device),
+            "K": int(W["K"]), "N": int(W["N"])}

@@ -1,0 +1,201 @@
+// C ABI of the library: argument validation on the host, then asynchronous
+// launches on the caller's stream.  See include/qlinear.h for the contract
+// of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "ql_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape and pointer checks of one w4 matrix; N == 0 is allowed.
+int check_w4(const uint32_t* qw, const uint16_t* sc, const uint16_t* bi, int32_t K, int32_t N,
+             int32_t gs) {
+    if (N < 0 || K < 0) return QL_ERR_INVALID_ARG;
+    if (gs != QL_GROUP_SIZE) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (K == 0 || K % QL_GROUP_SIZE != 0 || K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0) return QL_OK;
+    if (!qw || !sc || !bi) return QL_ERR_INVALID_ARG;
+    if (!aligned(qw, 16) || !aligned(sc, 2) || !aligned(bi, 2)) return QL_ERR_MISALIGNED;
+    return QL_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int ql_layout_version(void) { return QL_LAYOUT_VERSION; }
+
+const char* ql_status_string(int status) {
+    switch (status) {
+        case QL_OK: return "ok";
+        case QL_ERR_INVALID_ARG: return "invalid argument";
+        case QL_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case QL_ERR_MISALIGNED: return "misaligned pointer";
+        case QL_ERR_WORKSPACE: return "workspace missing or too small";
+        case QL_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int qlinear_pack(const uint8_t* codes, int32_t N, int32_t K, uint32_t* qweight, void* stream) {
+    if (N < 0 || K < 0) return QL_ERR_INVALID_ARG;
+    if (K % 8 != 0) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0 || K == 0) return QL_OK;
+    if (!codes || !qweight) return QL_ERR_INVALID_ARG;
+    if (!aligned(codes, 16) || !aligned(qweight, 16)) return QL_ERR_MISALIGNED;
+    return ql::launch_pack(codes, N, K, qweight, as_stream(stream));
+}
+
+int qlinear_gemv(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (W->N == 0) return QL_OK;
+    if (!x || !y) return QL_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemvArgs a{W->qweight, W->scales, W->biases, x, y, W->K, W->N};
+    return ql::launch_gemv(a, as_stream(stream));
+}
+
+int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
+    if (!W || M < 0) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (W->N == 0 || M == 0) return QL_OK;
+    if (M > (int64_t)0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemmArgs a{W->qweight, W->scales, W->biases, X, Y, M, W->K, W->N};
+    return ql::launch_gemm(a, as_stream(stream));
+}
+
+size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk) {
+    if (T < 0 || E <= 0 || E > QL_MAX_EXPERTS || topk <= 0 || topk > E || topk > QL_MAX_TOPK)
+        return 0;
+    return ql::moe_workspace_layout(T, E, topk, 0).total;
+}
+
+size_t ql_moe_logits_offset(int32_t T, int32_t E, int32_t topk) {
+    if (moe_workspace_bytes(T, E, topk) == 0) return 0;
+    return ql::moe_workspace_layout(T, E, topk, 0).logits;
+}
+
+static int check_route_common(int32_t T, int32_t E, int32_t topk, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* sorted_assign,
+                              const int32_t* assign_pos, const void* workspace, size_t ws_bytes) {
+    if (T < 0 || E <= 0 || topk <= 0) return QL_ERR_INVALID_ARG;
+    if (topk > E) return QL_ERR_INVALID_ARG;
+    if (E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
+    if ((int64_t)T * topk > 0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!counts || !offsets) return QL_ERR_INVALID_ARG;
+    if (T > 0 && (!sorted_assign || !assign_pos)) return QL_ERR_INVALID_ARG;
+    if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_assign, 4) ||
+        !aligned(assign_pos, 4))
+        return QL_ERR_MISALIGNED;
+    if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
+    return QL_OK;
+}
+
+int moe_route(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
+              int32_t E, int32_t topk, int32_t* topk_ids, float* topk_gates, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, void* workspace,
+              size_t ws_bytes, void* stream) {
+    int rc = check_route_common(T, E, topk, counts, offsets, sorted_assign, assign_pos, workspace,
+                                ws_bytes);
+    if (rc != QL_OK) return rc;
+    if (D <= 0) return QL_ERR_INVALID_ARG;
+    if (D % QL_GROUP_SIZE != 0 || D > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (T > 0 && (!H || !Wr || !topk_ids || !topk_gates)) return QL_ERR_INVALID_ARG;
+    if (!aligned(H, 16) || !aligned(Wr, 16) || !aligned(logit_bias, 4) || !aligned(topk_ids, 4) ||
+        !aligned(topk_gates, 4))
+        return QL_ERR_MISALIGNED;
+    ql::RouteArgs a{H, Wr, logit_bias, T, D, E, topk, topk_ids, topk_gates, counts, offsets,
+                    sorted_assign, assign_pos, static_cast<unsigned char*>(workspace)};
+    if (T == 0) return ql::launch_dispatch(a, as_stream(stream));  // counts = 0, offsets = 0
+    return ql::launch_route(a, as_stream(stream));
+}
+
+int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk, int32_t* counts,
+                 int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, void* workspace,
+                 size_t ws_bytes, void* stream) {
+    int rc = check_route_common(T, E, topk, counts, offsets, sorted_assign, assign_pos, workspace,
+                                ws_bytes);
+    if (rc != QL_OK) return rc;
+    if (T > 0 && !topk_ids) return QL_ERR_INVALID_ARG;
+    if (!aligned(topk_ids, 4)) return QL_ERR_MISALIGNED;
+    ql::RouteArgs a{nullptr, nullptr, nullptr, T, 0, E, topk, const_cast<int32_t*>(topk_ids),
+                    nullptr, counts, offsets, sorted_assign, assign_pos,
+                    static_cast<unsigned char*>(workspace)};
+    return ql::launch_dispatch(a, as_stream(stream));
+}
+
+int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X, int32_t T,
+                     int32_t topk, int32_t op, const int32_t* offsets,
+                     const int32_t* sorted_assign, const float* topk_gates,
+                     const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
+                     uint16_t* Y, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    if (op != QL_OP_GATE_UP_SILU && op != QL_OP_DOWN && op != QL_OP_DOWN_COMBINE)
+        return QL_ERR_INVALID_ARG;
+    const int32_t E = W->num_experts;
+    if (T < 0 || E <= 0 || topk <= 0 || topk > E) return QL_ERR_INVALID_ARG;
+    if (E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (shared) {
+        rc = check_w4(shared->qweight, shared->scales, shared->biases, shared->K, shared->N,
+                      shared->group_size);
+        if (rc != QL_OK) return rc;
+        if (shared->K != W->K || shared->N != W->N) return QL_ERR_INVALID_ARG;
+    }
+    if (op == QL_OP_GATE_UP_SILU && W->N % 2 != 0) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0 || W->N == 0) return QL_OK;
+    if ((int64_t)T * topk > 0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!X || !Y || !offsets || !sorted_assign) return QL_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 2) || !aligned(offsets, 4) || !aligned(sorted_assign, 4))
+        return QL_ERR_MISALIGNED;
+    if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
+
+    const bool rows_path = T <= QL_DECODE_MAX_T && ql::moe_rows_supported(W->K);
+    if (op == QL_OP_DOWN_COMBINE) {
+        if (!rows_path) return QL_ERR_UNSUPPORTED_SHAPE;
+        if (!topk_gates || !assign_pos) return QL_ERR_INVALID_ARG;
+        if (!aligned(topk_gates, 4) || !aligned(assign_pos, 4)) return QL_ERR_MISALIGNED;
+        const int J = topk + (shared ? 1 : 0);
+        if ((int64_t)J * W->K * 2 > 49152) return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+    ql::GroupedArgs a{W->qweight, W->scales, W->biases,
+                      shared ? shared->qweight : nullptr,
+                      shared ? shared->scales : nullptr,
+                      shared ? shared->biases : nullptr,
+                      X, offsets, sorted_assign, topk_gates, assign_pos,
+                      static_cast<const unsigned char*>(workspace), Y,
+                      W->K, W->N, E, T, topk, op};
+    if (rows_path) return ql::launch_moe_rows(a, as_stream(stream));
+    return ql::launch_moe_grouped(a, as_stream(stream));
+}
+
+int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
+                void* stream) {
+    if (T < 0 || N < 0 || topk <= 0) return QL_ERR_INVALID_ARG;
+    if (topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0 || N == 0) return QL_OK;
+    if (!Ydown || !topk_gates || !assign_pos || !out) return QL_ERR_INVALID_ARG;
+    const uintptr_t va = (N % 8 == 0) ? 16 : 2;
+    if (!aligned(Ydown, va) || !aligned(out, va) || !aligned(topk_gates, 4) ||
+        !aligned(assign_pos, 4))
+        return QL_ERR_MISALIGNED;
+    return ql::launch_combine(Ydown, topk_gates, assign_pos, T, topk, N, has_shared ? 1 : 0, out,
+                              as_stream(stream));
+}
+
+}  // extern "C"

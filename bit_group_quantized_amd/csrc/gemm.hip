@@ -1,0 +1,406 @@
+// MFMA GEMM kernels with the w4 dequantization fused into the tile loop:
+// the dense prefill GEMM, the grouped expert GEMMs over routed tiles, and the
+// fp16 router GEMM.
+//
+// Perplexity, "Optimizing on-device inference for Apple Silicon", section
+// 在矩阵乘法期间进行权重反量化: the grouped GEMM dequantizes one small weight
+// tile at a time into on-chip memory, keeps it only long enough to multiply
+// it with the routed activation rows, accumulates in fp32 and writes 16-bit
+// outputs; the full dequantized matrix never exists in memory.  Section
+// 使瓦片大小与专家负载相匹配: each expert's rows are cut into fixed-height tiles
+// and every tile is one workgroup.
+//
+// gfx950 mapping.  A workgroup of 4 waves (2 x 2) owns a BM x BN output tile;
+// each wave owns (32*WM) x (32*WN) and issues v_mfma_f32_32x32x16_f16 on it.
+// One K step is 64 = one quantization group.  Per step the workgroup stages
+// the activation tile (BM x 64 fp16) and the dequantized weight tile
+// (BN x 64 fp16, produced from BN x 32 bytes of codes plus one scale and
+// bias per column) into LDS; both are double buffered, so the global loads
+// of step s+1 overlap the MFMAs of step s with one barrier per step.  Rows
+// in LDS are padded to 72 halves (144 bytes) so that both the 128-bit
+// staging writes and the 128-bit fragment reads are free of bank conflicts.
+//
+// MFMA operand order: for one 16-wide K slice, lane l supplies row l % 32 of
+// A and column l % 32 of B, each as 8 fp16 values; element v of half h = l/32
+// is paired across A and B.  Any bijection between (h, v) and the 16 k of
+// the slice therefore gives the same dot product.  Slice s of a K step uses
+// k = 32h + 8s + v, so a lane's 8 values are one contiguous 16-byte chunk of
+// an LDS row and one packed word of codes.
+#include "ql_device.h"
+#include "ql_internal.h"
+
+namespace ql {
+
+namespace {
+
+constexpr int kLdk = 72;  // padded LDS row length in fp16
+
+enum : int { MODE_DENSE = 0, MODE_ROUTER = 1, MODE_GATEUP = 2, MODE_DOWN = 3 };
+
+struct KParams {
+    // A operand
+    const uint16_t* A;  // rows of K fp16
+    int64_t M;          // dense / router row count
+    // B operand (w4)
+    const uint32_t* qw;
+    const uint16_t* sc;
+    const uint16_t* bi;
+    const uint32_t* sqw;  // shared expert (grouped modes)
+    const uint16_t* ssc;
+    const uint16_t* sbi;
+    // B operand (fp16 [K][N], router)
+    const uint16_t* Bh;
+    // grouped routing
+    const int* ws_header;
+    const int* tiles;
+    const int* sorted_assign;
+    int max_tiles;  // routed tile slots in the grid
+    int T, topk, E;
+    // output
+    uint16_t* Y;
+    float* Yf;
+    int K, N;
+    int ksplit;  // router: number of K splits
+};
+
+template <int WM, int WN>
+struct Tile {
+    static constexpr int BM = 64 * WM;
+    static constexpr int BN = 64 * WN;
+    static constexpr int A_LOADS = BM / 32;             // 16-byte A loads per thread per step
+    static constexpr int TPC = 256 / BN;                // threads per B column (1 or 2)
+    static constexpr int WPT = 8 / TPC;                 // code words per thread per step
+    static constexpr int LDS_A = BM * kLdk;             // fp16 per A buffer
+    static constexpr int LDS_B = BN * kLdk;             // fp16 per B buffer
+    static constexpr size_t LDS_BYTES = (size_t)2 * (LDS_A + LDS_B) * 2;
+};
+
+template <int WM, int WN, int MODE>
+__global__ void __launch_bounds__(256)
+gemm_w4_kernel(const KParams p) {
+    using TL = Tile<WM, WN>;
+    constexpr int BM = TL::BM, BN = TL::BN;
+    extern __shared__ __align__(16) f16 lds[];
+    f16* As = lds;                     // [2][BM][kLdk]
+    f16* Bs = lds + 2 * TL::LDS_A;     // [2][BN][kLdk]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave >> 1) * (32 * WM);  // wave row offset in the tile
+    const int wn0 = (wave & 1) * (32 * WN);   // wave column offset in the tile
+    const int K = p.K;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+
+    // ---- tile coordinates ---------------------------------------------------
+    int rows_valid;          // rows of this tile that exist
+    int out_row0;            // first output row
+    int n0;                  // first output column (act column for GATEUP)
+    int kbeg = 0, kend = G;  // K steps of this workgroup
+    const uint32_t* wq = p.qw;
+    const uint16_t* ws = p.sc;
+    const uint16_t* wb = p.bi;
+    int tile_kind = 0;       // grouped: 0 routed, 1 shared
+    int tile_first = 0;      // grouped: first row (routed r or shared token)
+    if constexpr (MODE == MODE_DENSE) {
+        n0 = blockIdx.x * BN;
+        out_row0 = blockIdx.y * BM;
+        rows_valid = (int)min<int64_t>(BM, p.M - out_row0);
+    } else if constexpr (MODE == MODE_ROUTER) {
+        n0 = blockIdx.y * BN;
+        out_row0 = blockIdx.x * BM;
+        rows_valid = (int)min<int64_t>(BM, p.M - out_row0);
+        const int per = (G + p.ksplit - 1) / p.ksplit;
+        kbeg = blockIdx.z * per;
+        kend = min(G, kbeg + per);
+    } else {
+        const int slot = blockIdx.x;
+        if (slot < p.max_tiles) {
+            if (slot >= p.ws_header[0]) return;  // fewer routed tiles than slots
+            const int* tp = p.tiles + (size_t)slot * 4;
+            // Clamped so that a corrupted tile map can never index out of bounds.
+            const int e = min(max(tp[0], 0), p.E - 1);
+            rows_valid = min(max(tp[2], 1), BM);
+            tile_first = min(max(tp[1], 0), p.T * p.topk - rows_valid);
+            out_row0 = tile_first;
+            wq = p.qw + (size_t)e * p.N * wpr;
+            ws = p.sc + (size_t)e * p.N * G;
+            wb = p.bi + (size_t)e * p.N * G;
+        } else {
+            tile_kind = 1;
+            const int s = slot - p.max_tiles;
+            tile_first = s * BM;
+            rows_valid = min(BM, p.T - tile_first);
+            out_row0 = p.T * p.topk + tile_first;
+            wq = p.sqw;
+            ws = p.ssc;
+            wb = p.sbi;
+        }
+        n0 = blockIdx.y * ((MODE == MODE_GATEUP) ? BN / 2 : BN);
+    }
+
+    // ---- A row sources (one per 32-row slab this thread stages) -------------
+    const uint16_t* arow[TL::A_LOADS];
+    const int a_chunk = tid & 7;
+#pragma unroll
+    for (int i = 0; i < TL::A_LOADS; ++i) {
+        const int lr = min(i * 32 + (tid >> 3), rows_valid - 1);
+        int64_t src;
+        if constexpr (MODE == MODE_DENSE || MODE == MODE_ROUTER) {
+            src = out_row0 + lr;
+        } else if constexpr (MODE == MODE_GATEUP) {
+            src = (tile_kind == 0) ? min(max(p.sorted_assign[tile_first + lr] / p.topk, 0), p.T - 1)
+                                   : tile_first + lr;
+        } else {
+            src = out_row0 + lr;  // act rows are already in output order
+        }
+        arow[i] = p.A + src * K + a_chunk * 8;
+    }
+
+    // ---- B column source for this thread -------------------------------------
+    const int bc = tid / TL::TPC;           // local column 0..BN-1
+    const int bpart = tid % TL::TPC;        // which words of the column
+    int bcol;
+    if constexpr (MODE == MODE_GATEUP) {
+        // Wave column block w holds WN/2 subtiles of gate then the matching
+        // WN/2 subtiles of up, so a lane finds gate and up of the same output
+        // column in subtiles ni and ni + WN/2.
+        const int w = bc / (32 * WN);
+        const int s = (bc % (32 * WN)) / 32;
+        const int l = bc % 32;
+        const int half = p.N / 2;
+        bcol = n0 + w * (16 * WN) + (s % (WN / 2)) * 32 + l;
+        bcol = min(bcol, half - 1) + ((s >= WN / 2) ? half : 0);
+    } else {
+        bcol = min(n0 + bc, p.N - 1);
+    }
+
+    f32x16 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    u32x4 areg[TL::A_LOADS];
+    u32x4 breg[(MODE == MODE_ROUTER) ? 1 : TL::WPT / 4];
+    uint16_t sreg = 0, bireg = 0;
+    // router B staging: 8 x 16-byte loads of 8 consecutive columns per thread
+    u32x4 hreg[(MODE == MODE_ROUTER) ? (BN / 32) : 1];
+
+    auto load_stage = [&](int ks) {
+        const int k0 = ks * kGroup;
+#pragma unroll
+        for (int i = 0; i < TL::A_LOADS; ++i) areg[i] = ld_u32x4(arow[i] + k0);
+        if constexpr (MODE == MODE_ROUTER) {
+            // tile of 64 k-rows x BN columns; load j covers k-row (tid/ (BN/8)) + ...
+#pragma unroll
+            for (int j = 0; j < BN / 32; ++j) {
+                const int idx = j * 256 + tid;            // 0 .. 8*BN-1
+                const int kr = idx / (BN / 8);
+                const int c8 = (idx % (BN / 8)) * 8;
+                const int col = min(n0 + c8, p.N - 8);
+                hreg[j] = ld_u32x4(p.Bh + (size_t)(k0 + kr) * p.N + col);
+            }
+        } else {
+            const uint32_t* src = wq + (size_t)bcol * wpr + ks * 8 + bpart * TL::WPT;
+#pragma unroll
+            for (int i = 0; i < TL::WPT / 4; ++i) breg[i] = ld_u32x4(src + 4 * i);
+            sreg = ws[(size_t)bcol * G + ks];
+            bireg = wb[(size_t)bcol * G + ks];
+        }
+    };
+
+    auto store_stage = [&](int buf) {
+        f16* a_dst = As + buf * TL::LDS_A;
+#pragma unroll
+        for (int i = 0; i < TL::A_LOADS; ++i)
+            *reinterpret_cast<u32x4*>(a_dst + (i * 32 + (tid >> 3)) * kLdk + a_chunk * 8) = areg[i];
+        f16* b_dst = Bs + buf * TL::LDS_B;
+        if constexpr (MODE == MODE_ROUTER) {
+#pragma unroll
+            for (int j = 0; j < BN / 32; ++j) {
+                const int idx = j * 256 + tid;
+                const int kr = idx / (BN / 8);
+                const int c8 = (idx % (BN / 8)) * 8;
+                const f16x8 h = __builtin_bit_cast(f16x8, hreg[j]);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) b_dst[(c8 + v) * kLdk + kr] = h[v];
+            }
+        } else {
+            const f16 s = __builtin_bit_cast(f16, sreg);
+            const f16 b = __builtin_bit_cast(f16, bireg);
+            const f16x2 s2 = {s, s};
+            const f16x2 b2 = {b, b};
+#pragma unroll
+            for (int i = 0; i < TL::WPT / 4; ++i) {
+                const uint32_t wv[4] = {breg[i].x, breg[i].y, breg[i].z, breg[i].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int word = bpart * TL::WPT + 4 * i + q;  // 0..7 within the group
+                    *reinterpret_cast<f16x8*>(b_dst + bc * kLdk + word * 8) = dequant_word(wv[q], s2, b2);
+                }
+            }
+        }
+    };
+
+    if (kbeg < kend) {
+        load_stage(kbeg);
+        store_stage(0);
+    }
+    __syncthreads();
+
+    const int fl = lane & 31;   // row (A) / column (B) inside a 32-wide subtile
+    const int fh = lane >> 5;   // which half of the 16-wide K slice
+    for (int ks = kbeg; ks < kend; ++ks) {
+        const int cur = (ks - kbeg) & 1;
+        const bool more = ks + 1 < kend;
+        if (more) load_stage(ks + 1);
+        const f16* a_src = As + cur * TL::LDS_A + (wm0 + fl) * kLdk;
+        const f16* b_src = Bs + cur * TL::LDS_B + (wn0 + fl) * kLdk;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int koff = (4 * fh + s) * 8;
+            f16x8 af[WM], bf[WN];
+#pragma unroll
+            for (int i = 0; i < WM; ++i) af[i] = *reinterpret_cast<const f16x8*>(a_src + i * 32 * kLdk + koff);
+#pragma unroll
+            for (int j = 0; j < WN; ++j) bf[j] = *reinterpret_cast<const f16x8*>(b_src + j * 32 * kLdk + koff);
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+#pragma unroll
+                for (int j = 0; j < WN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) store_stage(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue -------------------------------------------------------------
+    // acc[i][j][r]: row 32i + 8(r/4) + 4h + r%4, column 32j + l%32 of the wave tile.
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int lrow = wm0 + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
+            if (lrow >= rows_valid) continue;
+            const int64_t orow = (int64_t)out_row0 + lrow;
+            if constexpr (MODE == MODE_GATEUP) {
+                const int half = p.N / 2;
+#pragma unroll
+                for (int j = 0; j < WN / 2; ++j) {
+                    const int col = n0 + (wave & 1) * (16 * WN) + 32 * j + fl;
+                    if (col < half) {
+                        const float g = acc[i][j][r];
+                        const float u = acc[i][j + WN / 2][r];
+                        p.Y[orow * half + col] = f2h(silu(g) * u);
+                    }
+                }
+            } else if constexpr (MODE == MODE_ROUTER) {
+#pragma unroll
+                for (int j = 0; j < WN; ++j) {
+                    const int col = n0 + wn0 + 32 * j + fl;
+                    if (col < p.N) p.Yf[(orow * p.ksplit + blockIdx.z) * p.N + col] = acc[i][j][r];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < WN; ++j) {
+                    const int col = n0 + wn0 + 32 * j + fl;
+                    if (col < p.N) p.Y[orow * p.N + col] = f2h(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+template <int WM, int WN, int MODE>
+int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
+    using TL = Tile<WM, WN>;
+    static bool attr_done = false;  // benign race: the attribute is idempotent
+    if (!attr_done) {
+        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, MODE>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)TL::LDS_BYTES) != hipSuccess)
+            return QL_ERR_HIP;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, MODE>), grid, dim3(256), TL::LDS_BYTES, st, p);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_gemm(const GemmArgs& a, hipStream_t st) {
+    KParams p{};
+    p.A = a.X;
+    p.M = a.M;
+    p.qw = a.qweight;
+    p.sc = a.scales;
+    p.bi = a.biases;
+    p.Y = a.Y;
+    p.K = a.K;
+    p.N = a.N;
+    if (a.M >= 2048) {
+        using TL = Tile<4, 4>;
+        dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
+        return launch_t<4, 4, MODE_DENSE>(p, grid, st);
+    }
+    using TL = Tile<2, 4>;
+    dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
+    return launch_t<2, 4, MODE_DENSE>(p, grid, st);
+}
+
+constexpr int kRouterSplit = 4;
+
+int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
+                              int E, hipStream_t st) {
+    KParams p{};
+    p.A = H;
+    p.M = T;
+    p.Bh = Wr;
+    p.Yf = partials;
+    p.K = D;
+    p.N = E;
+    p.ksplit = kRouterSplit;
+    using TL = Tile<1, 4>;
+    dim3 grid((T + TL::BM - 1) / TL::BM, (E + TL::BN - 1) / TL::BN, kRouterSplit);
+    return launch_t<1, 4, MODE_ROUTER>(p, grid, st);
+}
+
+int router_mfma_parts() { return kRouterSplit; }
+
+int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
+    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk, 0);
+    KParams p{};
+    p.A = a.X;
+    p.qw = a.qw;
+    p.sc = a.sc;
+    p.bi = a.bi;
+    p.sqw = a.sqw;
+    p.ssc = a.ssc;
+    p.sbi = a.sbi;
+    p.ws_header = reinterpret_cast<const int*>(a.ws + L.header);
+    p.tiles = reinterpret_cast<const int*>(a.ws + L.tiles);
+    p.sorted_assign = a.sorted_assign;
+    p.max_tiles = L.max_tiles;
+    p.T = a.T;
+    p.topk = a.topk;
+    p.E = a.E;
+    p.Y = a.Y;
+    p.K = a.K;
+    p.N = a.N;
+    using TL = Tile<2, 4>;
+    static_assert(TL::BM == QL_MOE_TILE_ROWS, "grouped tile height must match the tile map");
+    const int shared_tiles = a.sqw ? (a.T + TL::BM - 1) / TL::BM : 0;
+    const unsigned slots = (unsigned)(L.max_tiles + shared_tiles);
+    if (a.op == QL_OP_GATE_UP_SILU) {
+        dim3 grid(slots, (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2));
+        return launch_t<2, 4, MODE_GATEUP>(p, grid, st);
+    }
+    dim3 grid(slots, (a.N + TL::BN - 1) / TL::BN);
+    return launch_t<2, 4, MODE_DOWN>(p, grid, st);
+}
+
+}  // namespace ql

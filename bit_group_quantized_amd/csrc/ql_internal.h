@@ -1,0 +1,99 @@
+// Internal interface between the C-ABI layer (capi.cpp) and the kernel
+// translation units.  Not installed; callers use include/qlinear.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qlinear.h"
+
+#define QL_MAX_EXPERTS_DEV QL_MAX_EXPERTS
+#define QL_MAX_TOPK_DEV QL_MAX_TOPK
+
+namespace ql {
+
+struct GemvArgs {
+    const uint32_t* qweight;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    const uint16_t* x;
+    uint16_t* y;
+    int K, N;
+};
+int launch_gemv(const GemvArgs& a, hipStream_t st);
+
+struct GemmArgs {
+    const uint32_t* qweight;
+    const uint16_t* scales;
+    const uint16_t* biases;
+    const uint16_t* X;
+    uint16_t* Y;
+    int64_t M;
+    int K, N;
+};
+int launch_gemm(const GemmArgs& a, hipStream_t st);
+
+int launch_pack(const uint8_t* codes, int N, int K, uint32_t* qweight, hipStream_t st);
+
+// Workspace carving shared by the routing and grouped-GEMM launchers.
+struct MoeWorkspace {
+    size_t header;        // int32[4]: num_tiles, tile_rows, error, reserved
+    size_t tiles;         // int32[max_tiles][4]
+    size_t logits;        // float[T][E]
+    size_t partials;      // float[T][nparts][E]   router partial sums
+    size_t chunk_counts;  // int32[nchunks][E]
+    size_t chunk_err;     // int32[nchunks]
+    size_t total;
+    int max_tiles, nchunks, nparts;
+};
+MoeWorkspace moe_workspace_layout(int T, int E, int topk, int D_for_partials);
+
+constexpr int kRouteChunkTokens = 256;  // tokens per dispatch chunk
+constexpr int kRouterPartRows = 64;     // D rows per small-T router partial
+constexpr int kRouterSmallT = 16;       // T at or below: row-parallel router
+
+struct RouteArgs {
+    const uint16_t* H;
+    const uint16_t* Wr;
+    const float* bias;
+    int T, D, E, topk;
+    int32_t* ids;
+    float* gates;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_assign;
+    int32_t* pos;
+    unsigned char* ws;
+};
+int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
+                              int E, hipStream_t st);
+int router_mfma_parts();
+bool router_uses_mfma(int T, int E);
+int launch_route(const RouteArgs& a, hipStream_t st);     // logits + top-k + dispatch
+int launch_dispatch(const RouteArgs& a, hipStream_t st);  // dispatch only (ids given)
+
+struct GroupedArgs {
+    const uint32_t* qw;
+    const uint16_t* sc;
+    const uint16_t* bi;
+    const uint32_t* sqw;  // shared expert or null
+    const uint16_t* ssc;
+    const uint16_t* sbi;
+    const uint16_t* X;
+    const int32_t* offsets;
+    const int32_t* sorted_assign;
+    const float* gates;
+    const int32_t* pos;
+    const unsigned char* ws;
+    uint16_t* Y;
+    int K, N, E, T, topk, op;
+};
+bool moe_rows_supported(int K);
+int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel
+int launch_moe_grouped(const GroupedArgs& a, hipStream_t st); // any T, MFMA tiles
+
+int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
+                   int N, int has_shared, uint16_t* out, hipStream_t st);
+
+}  // namespace ql

@@ -1,0 +1,263 @@
+/*
+ * qlinear.h - C ABI of the group-affine 4-bit linear-layer and routed-expert
+ * MoE library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page title, then section):
+ *   [PPLX] Perplexity, "Optimizing on-device inference for Apple Silicon":
+ *     "在矩阵乘法期间进行权重反量化"  dequantizing weights inside the matmul
+ *     "将专家路由保留在 GPU 上"        keeping expert routing on the GPU
+ *     "使瓦片大小与专家负载相匹配"    matching tile size to expert load
+ *     "Qwen 创建了三种不同的工作负载形状" the three workload shapes (top-8 of
+ *                                      256 experts plus one shared expert)
+ *     "优化单行权重路径"              the row-parallel single-row GEMV
+ *     "减少中间状态和流量"            the fused decode expert chains
+ *   [LAYA] laya-mlx, "工程调查：这个 MLX 端口还能再快 10× 吗？",
+ *     "选择性量化": affine quantization with group size 64.
+ *
+ * ---------------------------------------------------------------------------
+ * Packed-weight layout (version QL_LAYOUT_VERSION)
+ * ---------------------------------------------------------------------------
+ * A logical weight matrix W has K inputs and N outputs; a linear layer
+ * computes y[n] = sum_k x[k] * W[k][n].  Each weight is a 4-bit code
+ * q in 0..15; each group of 64 consecutive k of one output n shares an fp16
+ * scale and an fp16 bias, and W[k][n] = scale[n][k/64] * q(n,k) +
+ * bias[n][k/64]  ([PPLX] dequantization section; the bias form and fp16
+ * scale/bias are this library's reading of it).
+ *
+ *   qweight  uint32 [N][K/8], row-major.  Word w of row n holds codes
+ *            k = 8w .. 8w+7; code k sits in bits [4*(k%8), 4*(k%8)+4)
+ *            (least significant nibble first).
+ *   scales   fp16 bit patterns [N][K/64], row-major.
+ *   biases   fp16 bit patterns [N][K/64], row-major.
+ *   K must be a positive multiple of 64 (group_size must be 64); N >= 0.
+ *   Stacked experts: [E][N][K/8] and [E][N][K/64], expert after expert.
+ *   Expert gate_up matrices: columns [0, I) are the gate projection and
+ *   [I, 2I) the up projection of the same expert.
+ *
+ * Activations and outputs are fp16 bit patterns, row-major.  Accumulation
+ * is in fp32; outputs are rounded to fp16 to nearest even.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every entry point
+ * ---------------------------------------------------------------------------
+ * - All pointers except those documented as host values are device
+ *   pointers.  The caller owns every buffer; the library never allocates,
+ *   frees or synchronizes, and keeps no state between calls.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *   the default stream).  Calls are re-entrant.
+ * - Arguments are validated on the host before anything is enqueued; a
+ *   failing check returns an error and enqueues nothing.  Sizes of zero
+ *   (M, N or T) are valid and enqueue nothing.
+ * - Device pointers to packed weights, activations and outputs must be
+ *   16-byte aligned; scales/biases 2-byte; int32/float arrays 4-byte.
+ * - A launch failure reported by the runtime returns QL_ERR_HIP.  Faults in
+ *   kernels surface at the caller's next synchronization of the stream.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QL_LAYOUT_VERSION 1
+#define QL_GROUP_SIZE 64
+
+/* Rows per tile of the routed tile map written by moe_route/moe_dispatch. */
+#define QL_MOE_TILE_ROWS 128
+
+/* Status codes. */
+#define QL_OK 0
+#define QL_ERR_INVALID_ARG 1      /* null pointer, negative size, topk > E ... */
+#define QL_ERR_UNSUPPORTED_SHAPE 2 /* K % 64 != 0, group_size != 64, limits   */
+#define QL_ERR_MISALIGNED 3       /* a pointer violates its alignment rule    */
+#define QL_ERR_WORKSPACE 4        /* workspace null or smaller than required  */
+#define QL_ERR_HIP 5              /* the HIP runtime rejected a launch        */
+
+/* Operations of moe_grouped_gemm. */
+#define QL_OP_GATE_UP_SILU 1
+#define QL_OP_DOWN 2
+#define QL_OP_DOWN_COMBINE 3
+
+/* Limits. */
+#define QL_MAX_EXPERTS 1024
+#define QL_MAX_TOPK 32
+#define QL_MAX_K 32768
+#define QL_DECODE_MAX_T 4 /* largest T served by the row-parallel expert path */
+
+/* One w4 matrix (host struct holding device pointers). */
+typedef struct ql_w4 {
+    const uint32_t* qweight; /* [N][K/8]  */
+    const uint16_t* scales;  /* [N][K/64] */
+    const uint16_t* biases;  /* [N][K/64] */
+    int32_t K;
+    int32_t N;
+    int32_t group_size; /* must be 64 */
+} ql_w4;
+
+/* num_experts w4 matrices of the same shape stacked contiguously. */
+typedef struct ql_w4_experts {
+    const uint32_t* qweight; /* [E][N][K/8]  */
+    const uint16_t* scales;  /* [E][N][K/64] */
+    const uint16_t* biases;  /* [E][N][K/64] */
+    int32_t K;
+    int32_t N;
+    int32_t group_size; /* must be 64 */
+    int32_t num_experts;
+} ql_w4_experts;
+
+/* Version of the packed layout above. */
+int ql_layout_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* ql_status_string(int status);
+
+/*
+ * qlinear_pack - build packed words from one code per byte.
+ * Offline format step of [PPLX] dequantization section: 4-bit codes packed
+ * 8 per uint32 along K as described in the layout above.
+ *   codes    uint8 [N][K], each 0..15 (higher bits are ignored).
+ *   qweight  uint32 [N][K/8] output.
+ * K must be a positive multiple of 8.  Errors: INVALID_ARG, MISALIGNED
+ * (codes and qweight 16-byte aligned), UNSUPPORTED_SHAPE.
+ */
+int qlinear_pack(const uint8_t* codes, int32_t N, int32_t K, uint32_t* qweight, void* stream);
+
+/*
+ * qlinear_gemv - y = x . dequant(W) for one activation row (batch-1 decode).
+ * [PPLX] "优化单行权重路径" (row-parallel GEMV) with the dequantization of
+ * the same page's dequantization section done in registers.
+ *   W  a K x N w4 matrix;  x  fp16 [K];  y  fp16 [N] output.
+ * Errors: INVALID_ARG (null W/x/y with N > 0), UNSUPPORTED_SHAPE (K % 64,
+ * K > QL_MAX_K, group_size != 64), MISALIGNED, HIP.
+ */
+int qlinear_gemv(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream);
+
+/*
+ * qlinear_gemm - Y = X . dequant(W) for M activation rows (prefill).
+ * [PPLX] dequantization section: small weight tiles are dequantized into
+ * on-chip memory just long enough to be multiplied; fp32 accumulation,
+ * 16-bit output; the full dequantized matrix never exists in memory.
+ *   X  fp16 [M][K];  Y  fp16 [M][N] output.  Row m of Y depends only on row
+ *   m of X and is bit-identical whatever M is (no split over K).
+ * Errors: as qlinear_gemv, plus INVALID_ARG for M < 0.
+ */
+int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
+ * moe_workspace_bytes - bytes of device workspace that moe_route and
+ * moe_dispatch need for T tokens, E experts, top-k; 0 on invalid input.
+ *
+ * Workspace layout (offsets in bytes; readable by the caller after the
+ * stream has completed):
+ *   [0, 4)     int32 num_tiles   number of valid entries of the tile map
+ *   [4, 8)     int32 tile_rows   = QL_MOE_TILE_ROWS
+ *   [8, 12)    int32 error flag  nonzero if the ids violated the contract of
+ *                                 moe_dispatch (out of range or repeated)
+ *   [12, 16)   reserved
+ *   [16, ...)  int32 tiles[max_tiles][4] = {expert, first row, rows, 0},
+ *              max_tiles = (T*topk)/QL_MOE_TILE_ROWS + E
+ *   then, at ql_moe_logits_offset(T, E, topk): float logits[T][E] (router
+ *   logits incl. bias, written by moe_route only)
+ *   then internal scratch.
+ */
+size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk);
+size_t ql_moe_logits_offset(int32_t T, int32_t E, int32_t topk);
+
+/*
+ * moe_route - on-GPU router and dispatch with no host round trip.
+ * [PPLX] "Qwen 创建了三种不同的工作负载形状": score E experts per token and keep
+ * topk; reading taken: softmax over all E logits, keep the topk largest
+ * (ties toward the lower expert index), renormalize them to sum 1; an
+ * optional per-expert logit bias is added to the logits.  Then [PPLX]
+ * "将专家路由保留在 GPU 上": histogram, prefix scan, stable scatter of the
+ * assignments a = t*topk + j into expert groups, and the tile map.
+ *   H            fp16 [T][D] tokens
+ *   Wr           fp16 [D][E] router weight
+ *   logit_bias   fp32 [E] or NULL
+ *   topk_ids     int32 [T][topk] out: chosen experts, by descending gate
+ *   topk_gates   fp32  [T][topk] out: renormalized gates (descending)
+ *   counts       int32 [E] out: assignments per expert
+ *   offsets      int32 [E+1] out: exclusive prefix sum of counts
+ *   sorted_assign int32 [T*topk] out: assignments grouped by expert,
+ *                ascending a inside each expert
+ *   assign_pos   int32 [T*topk] out: inverse of sorted_assign
+ *   workspace    device buffer of ws_bytes >= moe_workspace_bytes(T,E,topk)
+ * Logits are accumulated in fp32.  Limits: 1 <= topk <= min(E,
+ * QL_MAX_TOPK), E <= QL_MAX_EXPERTS, D a positive multiple of 64.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED, WORKSPACE, HIP.
+ */
+int moe_route(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+              int32_t T, int32_t D, int32_t E, int32_t topk,
+              int32_t* topk_ids, float* topk_gates,
+              int32_t* counts, int32_t* offsets,
+              int32_t* sorted_assign, int32_t* assign_pos,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch - the dispatch half of moe_route for ids chosen elsewhere:
+ * histogram, prefix scan, stable scatter and tile map ([PPLX]
+ * "将专家路由保留在 GPU 上").  topk_ids int32 [T][topk]: the ids of one token
+ * must be distinct and in [0, E).  Ids that break this are skipped and set
+ * the workspace error flag; the outputs are then unspecified but every
+ * write stays in bounds.  Other arguments as moe_route.
+ */
+int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk,
+                 int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_assign, int32_t* assign_pos,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm - the expert projections over routed rows, ragged per
+ * expert, fed by the dispatch outputs on the device.
+ * [PPLX] dequantization section (fused-dequant grouped GEMM), "使瓦片大小与专
+ * 家负载相匹配" (tiles over each expert's rows) and "减少中间状态和流量"
+ * (gate+up fused with the gated activation; down fused with the routing
+ * weights and the shared expert).
+ *
+ * Rows: routed row r in [0, T*topk) is assignment sorted_assign[r] of
+ * token sorted_assign[r] / topk, multiplied by expert e with offsets[e] <=
+ * r < offsets[e+1]; if `shared` is not NULL, rows [T*topk, T*topk + T)
+ * are the T tokens in order, multiplied by the shared expert.
+ *
+ *   op = QL_OP_GATE_UP_SILU: W is [E] x (K = D, N = 2I), X = H fp16 [T][D];
+ *        Y fp16 [rows][I] = SiLU(u[:, :I]) * u[:, I:], u = X[token] . W_e.
+ *   op = QL_OP_DOWN: W is [E] x (K = I, N = D), X = act fp16 [rows][I] in
+ *        row order; Y fp16 [rows][D].
+ *   op = QL_OP_DOWN_COMBINE (T <= QL_DECODE_MAX_T): as QL_OP_DOWN, but
+ *        Y fp16 [T][D] = sum_j topk_gates[t][j] * (row assign_pos[t*topk+j])
+ *        (+ the shared row of t), summed in fp32 in the order j = 0..topk-1
+ *        then shared.
+ * topk_gates and assign_pos are read only by QL_OP_DOWN_COMBINE (may be
+ * NULL otherwise).  `workspace` is the one filled by moe_route or
+ * moe_dispatch for the same T, E, topk.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED, WORKSPACE, HIP.
+ */
+int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared,
+                     const uint16_t* X, int32_t T, int32_t topk, int32_t op,
+                     const int32_t* offsets, const int32_t* sorted_assign,
+                     const float* topk_gates, const int32_t* assign_pos,
+                     const void* workspace, size_t ws_bytes,
+                     uint16_t* Y, void* stream);
+
+/*
+ * moe_combine - out[t] = sum_j topk_gates[t][j] * Ydown[assign_pos[t*topk+j]]
+ * (+ Ydown[T*topk + t] if has_shared), fp32 in the order j = 0..topk-1 then
+ * shared, rounded to fp16.  [PPLX] "减少中间状态和流量" (routing scores and the
+ * shared expert's result applied to the expert outputs).  Deterministic: no
+ * atomics.
+ *   Ydown fp16 [T*topk (+T)][N];  out fp16 [T][N].
+ * Errors: INVALID_ARG, MISALIGNED, HIP.
+ */
+int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                int32_t T, int32_t topk, int32_t N, int32_t has_shared,
+                uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

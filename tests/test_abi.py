@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, it
+exports every function the header declares, and argument validation
+returns the documented status codes before anything is enqueued (these
+calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_group_quantized_amd as ql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+OK, INVALID, SHAPE, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4
+A16 = 0x10000  # fake, 16-byte aligned addresses: validation never dereferences them
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ql.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    assert set(names) == set(ql.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_layout_version_and_status_strings(L):
+    assert L.ql_layout_version() == 1
+    for s in range(6):
+        assert L.ql_status_string(s)
+    assert L.ql_status_string(99) == b"unknown status"
+
+
+def _w(K=2048, N=64, gs=64, qw=A16, sc=A16, bi=A16):
+    return ql.ql_w4(qw, sc, bi, K, N, gs)
+
+
+def test_gemv_validation(L):
+    f = L.qlinear_gemv
+    assert f(None, A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=100)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(K=0)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(K=65536)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(gs=32)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(N=-1)), A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(qw=A16 + 4)), A16, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w(sc=A16 + 1)), A16, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), A16 + 8, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), None, A16, None) == INVALID
+    assert f(ctypes.byref(_w(qw=0)), A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), None, None, None) == OK  # empty: nothing enqueued
+
+
+def test_gemm_validation(L):
+    f = L.qlinear_gemm
+    assert f(ctypes.byref(_w()), A16, -1, A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, 0, A16, None) == OK  # empty
+    assert f(ctypes.byref(_w(K=96)), A16, 4, A16, None) == SHAPE
+    assert f(ctypes.byref(_w()), A16 + 2, 4, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), None, 4, A16, None) == INVALID
+
+
+def test_pack_validation(L):
+    f = L.qlinear_pack
+    assert f(A16, 4, 12, A16, None) == SHAPE
+    assert f(A16, -1, 16, A16, None) == INVALID
+    assert f(A16 + 1, 4, 16, A16, None) == MISALIGNED
+    assert f(None, 4, 16, A16, None) == INVALID
+    assert f(None, 0, 16, None, None) == OK
+
+
+def test_workspace_bytes(L):
+    f = L.moe_workspace_bytes
+    assert f(4096, 256, 8) > 0
+    assert f(1, 256, 8) > 0
+    assert f(0, 256, 8) > 0
+    assert f(4096, 256, 8) >= f(1024, 256, 8) >= f(1, 256, 8)
+    assert f(4, 256, 300) == 0      # topk > E
+    assert f(4, 2048, 8) == 0       # E > QL_MAX_EXPERTS
+    assert f(4, 256, 0) == 0
+    assert f(-1, 256, 8) == 0
+    # the logits live inside the workspace, after the tile map
+    off = L.ql_moe_logits_offset(4096, 256, 8)
+    assert off >= 16 + 16 * (4096 * 8 // 128 + 256)
+    assert off + 4096 * 256 * 4 <= f(4096, 256, 8)
+
+
+def _route(L, T=8, D=2048, E=256, topk=8, ws=None, wsb=None, H=A16):
+    wsb = L.moe_workspace_bytes(max(T, 0), E, min(topk, E)) if wsb is None else wsb
+    return L.moe_route(H, A16, None, T, D, E, topk, A16, A16, A16, A16, A16, A16,
+                       A16 if ws is None else ws, wsb, None)
+
+
+def test_route_validation(L):
+    assert _route(L, topk=300) == INVALID
+    assert _route(L, T=-1) == INVALID
+    assert _route(L, E=2048, topk=8, wsb=1 << 30) == SHAPE
+    assert _route(L, topk=33, wsb=1 << 30) == SHAPE
+    assert _route(L, D=100) == SHAPE
+    assert _route(L, D=0) == INVALID
+    assert _route(L, wsb=16) == WORKSPACE
+    assert _route(L, ws=0) == WORKSPACE
+    assert _route(L, ws=A16 + 16) == MISALIGNED
+    assert _route(L, H=None) == INVALID
+    assert _route(L, H=A16 + 2) == MISALIGNED
+
+
+def test_dispatch_validation(L):
+    f = L.moe_dispatch
+    wsb = L.moe_workspace_bytes(8, 256, 8)
+    assert f(None, 8, 256, 8, A16, A16, A16, A16, A16, wsb, None) == INVALID
+    assert f(A16, 8, 256, 8, A16, A16, A16, A16, A16, 0, None) == WORKSPACE
+    assert f(A16 + 1, 8, 256, 8, A16, A16, A16, A16, A16, wsb, None) == MISALIGNED
+    assert f(A16, 8, 4, 8, A16, A16, A16, A16, A16, wsb, None) == INVALID
+
+
+def test_grouped_gemm_validation(L):
+    W = ql.ql_w4_experts(A16, A16, A16, 2048, 1024, 64, 256)
+    S = ql.ql_w4(A16, A16, A16, 2048, 1024, 64)
+    wsb = L.moe_workspace_bytes(64, 256, 8)
+    f = L.moe_grouped_gemm
+
+    def call(op=1, T=64, topk=8, w=W, s=S, wsb=wsb, X=A16):
+        return f(ctypes.byref(w), ctypes.byref(s) if s is not None else None, X, T, topk, op,
+                 A16, A16, A16, A16, A16, wsb, A16, None)
+
+    assert call(op=7) == INVALID
+    assert call(op=3) == SHAPE                 # DOWN_COMBINE is a decode path (T <= 4)
+    assert call(topk=300) == INVALID
+    assert call(wsb=0) == WORKSPACE
+    assert call(X=A16 + 2) == MISALIGNED
+    assert call(X=None) == INVALID
+    assert call(w=ql.ql_w4_experts(A16, A16, A16, 2048, 1023, 64, 256), s=None) == SHAPE  # odd gate_up width
+    assert call(s=ql.ql_w4(A16, A16, A16, 2048, 512, 64)) == INVALID           # shared shape differs
+    assert call(T=0) == OK
+
+
+def test_combine_validation(L):
+    f = L.moe_combine
+    assert f(A16, A16, A16, 4, 33, 2048, 1, A16, None) == SHAPE
+    assert f(A16, A16, A16, -1, 8, 2048, 1, A16, None) == INVALID
+    assert f(A16 + 2, A16, A16, 4, 8, 2048, 1, A16, None) == MISALIGNED
+    assert f(A16, A16, A16, 0, 8, 2048, 1, A16, None) == OK
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "bit_group_quantized_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b|oracle\.", text), fn

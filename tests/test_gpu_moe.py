@@ -1,0 +1,129 @@
+"""GPU parity of the routed-expert layer: decode (one token, fused
+row-parallel path) and prefill (ragged MFMA grouped GEMM), each against the
+oracle's own routing and expert FFN."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bit_group_quantized_amd as ql
+import oracle
+import synth
+from tests.gpu_util import assert_close, host, say, t, w4_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_weights(w):
+    return {"Wr": t(w["Wr"]), "gate_up": w4_dev(w["gate_up"]), "down": w4_dev(w["down"]),
+            "shared_gate_up": w4_dev(w["shared_gate_up"]), "shared_down": w4_dev(w["shared_down"])}
+
+
+def _run_layer(dw, H, bias, topk, T, fused_down):
+    route = ql.moe_route(H, dw["Wr"], bias, topk)
+    act = ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, topk,
+                              ql.QL_OP_GATE_UP_SILU, route)
+    if fused_down:
+        out = ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, topk,
+                                  ql.QL_OP_DOWN_COMBINE, route)
+        return route, act, None, out
+    ydown = ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, topk, ql.QL_OP_DOWN, route)
+    out = ql.moe_combine(ydown, route["gates"], route["pos"], T, topk, True)
+    return route, act, ydown, out
+
+
+def _ref_rows(route, ref, T, topk):
+    """Index of the oracle row holding the same (token, expert) pair as each
+    GPU row.  Equal expert sets are required; the order of two experts
+    whose logits are nearly tied may differ, which permutes rows."""
+    ids_g = host(route["ids"])
+    sa_g = host(route["sorted_assign"])
+    a = sa_g.astype(np.int64)
+    tok = a // topk
+    e = ids_g[tok, a % topk]
+    match = ref["ids"][tok] == e[:, None]
+    assert np.all(match.sum(axis=1) == 1), "routed expert sets differ"
+    j_ref = match.argmax(axis=1)
+    routed = ref["pos"][tok * topk + j_ref]
+    return np.concatenate([routed, np.arange(T * topk, ref["act"].shape[0])])
+
+
+def _compare(route, act, ydown, out, ref, T, topk):
+    rows = _ref_rows(route, ref, T, topk)
+    assert_close(host(act).astype(np.float64), ref["act"][rows].astype(np.float64), "act")
+    if ydown is not None:
+        assert_close(host(ydown).astype(np.float64), ref["ydown"][rows], "ydown")
+    return assert_close(host(out).astype(np.float64), ref["out"], "out")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("fused_down", [True, False])
+def test_moe_decode(seed, fused_down):
+    import torch
+    say(f"moe decode seed={seed} fused={fused_down}")
+    w = synth.moe_weights(seed)
+    tok = synth.moe_tokens(seed + 1000, 1)
+    ref = oracle.moe_layer(tok["H"], w, None, 8)
+    dw = _dev_weights(w)
+    res = _run_layer(dw, t(tok["H"]), None, 8, 1, fused_down)
+    torch.cuda.synchronize()
+    rel, mx = _compare(*res, ref, 1, 8)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_moe_decode_reads_only_selected_experts():
+    """Scales of every expert the token did not choose are NaN: any read of
+    them would poison the output."""
+    import torch
+    seed = 5
+    w = synth.moe_weights(seed)
+    tok = synth.moe_tokens(seed + 1000, 1)
+    ref = oracle.moe_layer(tok["H"], w, None, 8)
+    chosen = set(ref["ids"][0].tolist())
+    for key in ("gate_up", "down"):
+        for e in range(256):
+            if e not in chosen:
+                w[key]["scales"][e] = np.float16(np.nan)
+    dw = _dev_weights(w)
+    res = _run_layer(dw, t(tok["H"]), None, 8, 1, True)
+    torch.cuda.synchronize()
+    _compare(*res, ref, 1, 8)
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed", [
+    (2, 512, 256, 16, 4, 0),     # row-parallel path, several tokens
+    (4, 2048, 512, 256, 8, 1),
+    (5, 512, 128, 16, 4, 2),     # smallest T of the tiled path
+    (300, 256, 128, 16, 4, 3),   # ragged tiles
+    (700, 512, 256, 64, 8, 4),
+])
+def test_moe_small_shapes(T, D, I, E, topk, seed):
+    import torch
+    say(f"moe T={T} D={D} I={I} E={E} topk={topk}")
+    w = synth.moe_weights(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 50, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], topk)
+    dw = _dev_weights(w)
+    res = _run_layer(dw, t(tok["H"]), t(tok["logit_bias"]), topk, T, False)
+    torch.cuda.synchronize()
+    _compare(*res, ref, T, topk)
+
+
+SCREENED = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
+
+
+@pytest.mark.parametrize("seed", SCREENED[:1])
+def test_moe_prefill_4096(seed):
+    """The prefill workload: 4096 tokens, 256 experts + shared, Zipf logit
+    bias, in the benchmark's launch configuration."""
+    import torch
+    say(f"moe prefill T=4096 seed={seed}")
+    w = synth.moe_weights(0)
+    tok = synth.moe_tokens(seed, 4096, skewed=True)
+    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], 8)
+    dw = _dev_weights(w)
+    res = _run_layer(dw, t(tok["H"]), t(tok["logit_bias"]), 8, 4096, False)
+    torch.cuda.synchronize()
+    rel, mx = _compare(*res, ref, 4096, 8)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")

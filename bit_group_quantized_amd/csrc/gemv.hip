@@ -411,11 +411,14 @@ namespace ql {
 
 bool moe_rows_supported(int K) {
     const int G = K / kGroup;
-    return K % kGroup == 0 && (G == 8 || G == 16 || G == 32 || G == 64 || G == 128 || G == 256);
+    return K % kGroup == 0 && G >= 1 && G <= 256 && (G & (G - 1)) == 0;
 }
 
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st) {
     switch (a.K / kGroup) {
+        case 1: return launch_rows_t<1, 1>(a, st);
+        case 2: return launch_rows_t<2, 1>(a, st);
+        case 4: return launch_rows_t<4, 1>(a, st);
         case 8: return launch_rows_t<8, 1>(a, st);
         case 16: return launch_rows_t<16, 1>(a, st);
         case 32: return launch_rows_t<32, 1>(a, st);

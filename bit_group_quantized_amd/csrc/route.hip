@@ -356,8 +356,8 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
         pos[a] = r;
     }
     const int any = __syncthreads_or(err);
-    if (threadIdx.x == 0) {
-        ws_header[0] = tincl;
+    if (threadIdx.x == blockDim.x - 1) {
+        ws_header[0] = tincl;  // inclusive scan of the last thread = all tiles
         ws_header[1] = QL_MOE_TILE_ROWS;
         ws_header[2] = any;
         ws_header[3] = 0;

@@ -1,0 +1,344 @@
+"""Benchmark of the w4 hot path on one MI355X.
+
+Headline (the JSON line's `value`): the batch-1 decode GEMV at model size,
+x fp16 [1, 2048] times two group-affine 4-bit matrices, K = 2048 x N = 8192
+(a fused projection) and K = 2048 x N = 151552 (the vocabulary head).  One
+step is both GEMVs.  `value` is the effective HBM bandwidth: algorithmic
+bytes (codes + scales + biases + x + y) per step divided by the step time,
+with every input already resident in HBM.  Weight copies are rotated so the
+working set between two uses of one copy exceeds the 256 MB Infinity Cache.
+
+Also measured and reported under "workloads" (same run, same rules): the
+prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the decode MoE
+layer (one token, 8 of 256 experts + shared) and the prefill MoE layer
+(4096 tokens, Zipf-skewed expert loads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-primary]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "w4 GEMV eff. HBM GB/s; w4 GEMM/MoE TFLOP/s; both as % of MI355X peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 600e6  # > 2 x 256 MB Infinity Cache
+
+
+def w4_bytes(K, N):
+    return N * K // 2 + 4 * N * (K // 64)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-primary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# timing helpers (events on torch's current stream, which the library uses)
+# ----------------------------------------------------------------------------
+def timed_steps(step_fn, steps, warmup):
+    """Run warmup steps, then `steps` timed steps; returns (ms per step,
+    per-step list of per-launch durations in ms).  step_fn(i, ev) must record
+    ev() between launches it wants timed individually."""
+    import torch
+    for i in range(warmup):
+        step_fn(i, None)
+    torch.cuda.synchronize()
+    marks = []
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks[-1].append(e)
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        marks.append([])
+        step_fn(warmup + i, ev)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    per_launch = []
+    for m in marks:
+        per_launch.append([m[j].elapsed_time(m[j + 1]) for j in range(len(m) - 1)])
+    return total_ms / steps, np.asarray(per_launch)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_group_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key, sha):
+    """Measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE, scaled by the
+    copy-kernel calibration), if the counters were taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+def dev_w4(W, dev):
+    import torch
+    return {"qweight": torch.from_numpy(np.ascontiguousarray(W["qweight"]).view(np.int32)).to(dev),
+            "scales": torch.from_numpy(W["scales"]).to(dev),
+            "biases": torch.from_numpy(W["biases"]).to(dev), "K": W["K"], "N": W["N"]}
+
+
+def clone_w4(W):
+    return {k: (v.clone() if hasattr(v, "clone") else v) for k, v in W.items()}
+
+
+def bench_gemv(args, dev):
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K = 2048
+    Ns = (8192, synth.VOCAB)
+    cases = [synth.gemv_case(s, K, N) for s, N in zip((0, 1), Ns)]
+    step_bytes = sum(w4_bytes(K, N) + 2 * K + 2 * N for N in Ns)
+    copies = max(2, int(np.ceil(ROTATE_BYTES / step_bytes)))
+    base = [dev_w4(c["W"], dev) for c in cases]
+    Ws = [base] + [[clone_w4(w) for w in base] for _ in range(copies - 1)]
+    x = torch.from_numpy(cases[0]["x"][0]).to(dev)
+    ys = [torch.empty(N, dtype=torch.float16, device=dev) for N in Ns]
+
+    def step(i, ev):
+        Wc = Ws[i % copies]
+        if ev: ev()
+        ql.qlinear_gemv(Wc[0], x, ys[0])
+        if ev: ev()
+        ql.qlinear_gemv(Wc[1], x, ys[1])
+        if ev: ev()
+
+    ms, per = timed_steps(step, args.steps, args.warmup)
+    kern_ms = per.mean(axis=0)  # [small, head]
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    launch_bytes = [w4_bytes(K, N) + 2 * K + 2 * N for N in Ns]
+    avg_launch_bytes = sum(launch_bytes) / 2
+    avg_launch_ms = kern_ms.mean()
+    achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    sha = source_sha("gemv.hip", "ql_device.h")
+    traffic = traffic_for("gemv_w4_kernel<32,1,2>", sha)
+    return {
+        "value": gbs, "ms_per_step": ms, "step_bytes": step_bytes, "rotation_copies": copies,
+        "per_matrix": {f"N={N}": {"us": float(kern_ms[j] * 1e3),
+                                  "GB/s": launch_bytes[j] / (kern_ms[j] * 1e-3) / 1e9}
+                       for j, N in enumerate(Ns)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_w4_kernel<32,1,2>", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": avg_launch_bytes,
+                     "avg_launch_us": float(avg_launch_ms * 1e3), "source_sha": sha},
+    }
+
+
+def bench_gemm(args, dev):
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K, N = 2048, 8192
+    out = {}
+    for M in (4096, 256, 1024, 16384):
+        case = synth.gemm_case(0, M, K, N)
+        W = dev_w4(case["W"], dev)
+        X = torch.from_numpy(case["X"]).to(dev)
+        Xs = [X] + [X.clone() for _ in range(1 if M >= 4096 else 3)]
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+        def step(i, ev):
+            if ev: ev()
+            ql.qlinear_gemm(W, Xs[i % len(Xs)], Y)
+            if ev: ev()
+
+        steps = 20 if M <= 4096 else 8
+        ms, per = timed_steps(step, steps, 3)
+        flops = 2.0 * M * N * K
+        tf = flops / (per.mean() * 1e-3) / 1e12
+        out[f"M={M}"] = {"us": float(per.mean() * 1e3), "TFLOP/s": tf, "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
+        del Xs, Y, X, W
+        torch.cuda.empty_cache()
+    return out
+
+
+def moe_dev_weights(w, dev):
+    import torch
+    return {"Wr": torch.from_numpy(w["Wr"]).to(dev), "gate_up": dev_w4(w["gate_up"], dev),
+            "down": dev_w4(w["down"], dev), "shared_gate_up": dev_w4(w["shared_gate_up"], dev),
+            "shared_down": dev_w4(w["shared_down"], dev)}
+
+
+def bench_moe_decode(args, dev, w):
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    base = moe_dev_weights(w, dev)
+    copies = [base, {k: (clone_w4(v) if isinstance(v, dict) else v.clone()) for k, v in base.items()}]
+    toks = [torch.from_numpy(synth.moe_tokens(2000 + i, 1)["H"]).to(dev) for i in range(32)]
+    route = ql.alloc_route_outputs(1, 256, 8, dev)
+    act = torch.empty((9, 512), dtype=torch.float16, device=dev)
+    out = torch.empty((1, 2048), dtype=torch.float16, device=dev)
+
+    def step(i, ev):
+        dw = copies[i % 2]
+        H = toks[i % len(toks)]
+        if ev: ev()
+        ql.moe_route(H, dw["Wr"], None, 8, route)
+        if ev: ev()
+        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, 1, 8, ql.QL_OP_GATE_UP_SILU, route, act)
+        if ev: ev()
+        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, 1, 8, ql.QL_OP_DOWN_COMBINE, route, out)
+        if ev: ev()
+
+    ms, per = timed_steps(step, 200, 20)
+    algo = 2048 * 256 * 2 + 9 * (w4_bytes(2048, 1024) + w4_bytes(512, 2048)) + 2 * 2048 * 2
+    k = per.mean(axis=0)
+    return {"tokens/s": 1e3 / ms, "us_per_token": ms * 1e3, "algorithmic_bytes": algo,
+            "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
+                         "down_combine": float(k[2] * 1e3)}}
+
+
+def bench_moe_prefill(args, dev, w):
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    T = 4096
+    seeds = json.load(open(os.path.join(ROOT, "tests", "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
+    dw = moe_dev_weights(w, dev)
+    tok = synth.moe_tokens(seeds[0], T, skewed=True)
+    H = torch.from_numpy(tok["H"]).to(dev)
+    bias = torch.from_numpy(tok["logit_bias"]).to(dev)
+    route = ql.alloc_route_outputs(T, 256, 8, dev)
+    act = torch.empty((9 * T, 512), dtype=torch.float16, device=dev)
+    yd = torch.empty((9 * T, 2048), dtype=torch.float16, device=dev)
+    out = torch.empty((T, 2048), dtype=torch.float16, device=dev)
+
+    def step(i, ev):
+        if ev: ev()
+        ql.moe_route(H, dw["Wr"], bias, 8, route)
+        if ev: ev()
+        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU, route, act)
+        if ev: ev()
+        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
+        if ev: ev()
+        ql.moe_combine(yd, route["gates"], route["pos"], T, 8, True, out)
+        if ev: ev()
+
+    ms, per = timed_steps(step, 20, 3)
+    k = per.mean(axis=0)
+    routed_rows = T * 8
+    flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
+             + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)
+    return {"tokens/s": T / (ms * 1e-3), "ms_per_step": ms, "flops": flops,
+            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
+                         "down": float(k[2] * 1e3), "combine": float(k[3] * 1e3)},
+            "seed": seeds[0]}
+
+
+def cpu_baseline():
+    """The oracle as it stands, on a bounded sample of the headline workload:
+    the N = 8192 matrix plus the first 16384 rows of the vocabulary head,
+    repeated until about 10 s have elapsed.  Reported in the same unit."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    K = 2048
+    small = synth.gemv_case(0, K, 8192)
+    head = synth.gemv_case(1, K, 16384)
+    byts = sum(w4_bytes(K, N) + 2 * K + 2 * N for N in (8192, 16384))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.linear(small["x"], small["W"])
+        oracle.linear(head["x"], head["W"])
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": reps * byts / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle.linear (numpy fp64) on x[1,2048] with the 2048x8192 matrix and the "
+                      f"first 16384 rows of the 2048x151552 head, {reps} repetitions in {dt:.1f} s; "
+                      f"BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_group_quantized_amd as ql
+    ql.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    log("bench: GEMV (headline)")
+    g = bench_gemv(args, dev)
+    res = {
+        "metric": METRIC, "value": g["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": g["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "batch-1 decode w4 GEMV: x fp16[1,2048] times K=2048 x N=8192 and "
+                               "K=2048 x N=151552 (g=64, fp16 scale/bias), one step = both",
+                   "K": 2048, "N": [8192, 151552], "rotation_copies": g["rotation_copies"],
+                   "step_bytes": g["step_bytes"]},
+        "roofline": g["roofline"],
+        "per_matrix": g["per_matrix"],
+    }
+    if not args.only_primary:
+        import synth
+        log("bench: GEMM")
+        res.setdefault("workloads", {})["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
+        w = synth.moe_weights(0)
+        log("bench: MoE decode")
+        res["workloads"]["moe_decode_1tok"] = bench_moe_decode(args, dev, w)
+        log("bench: MoE prefill")
+        res["workloads"]["moe_prefill_4096tok"] = bench_moe_prefill(args, dev, w)
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

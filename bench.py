@@ -33,6 +33,7 @@ METRIC = "w4 GEMV eff. HBM GB/s; w4 GEMM/MoE TFLOP/s; both as % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 600e6  # > 2 x 256 MB Infinity Cache
+KERNEL_GEMV = "gemv_w4_chunked_kernel<64,1,8>"
 
 
 def w4_bytes(K, N):
@@ -57,34 +58,50 @@ def log(*a):
 # timing helpers (events on torch's current stream, which the library uses)
 # ----------------------------------------------------------------------------
 def timed_steps(step_fn, steps, warmup):
-    """Run warmup steps, then `steps` timed steps; returns (ms per step,
-    per-step list of per-launch durations in ms).  step_fn(i, ev) must record
-    ev() between launches it wants timed individually."""
+    """Run `warmup` untimed steps, then time exactly `steps` steps between two
+    events on torch's current stream (the stream the library launches on),
+    with a synchronize on both sides.  Returns ms per step."""
     import torch
     for i in range(warmup):
-        step_fn(i, None)
+        step_fn(i)
     torch.cuda.synchronize()
-    marks = []
-
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        marks[-1].append(e)
-
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        marks.append([])
-        step_fn(warmup + i, ev)
+        step_fn(warmup + i)
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    per_launch = []
-    for m in marks:
-        per_launch.append([m[j].elapsed_time(m[j + 1]) for j in range(len(m) - 1)])
-    return total_ms / steps, np.asarray(per_launch)
+    return start.elapsed_time(stop) / steps
+
+
+def stage_times(stage_fns, steps, warmup):
+    """Per-stage time: each stage alone, `steps` back-to-back launches between
+    two events (inputs of later stages are left from a full warm-up pass)."""
+    out = []
+    for fn in stage_fns:
+        out.append(timed_steps(fn, steps, warmup))
+    return out
+
+
+def graph_time(step_fn, ng, replays):
+    """Capture `ng` calls of step_fn(i) in one HIP graph, replay it `replays`
+    times between two events; returns ms per call."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(ng):
+            step_fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (replays * ng)
 
 
 def source_sha(*names):
@@ -137,29 +154,34 @@ def bench_gemv(args, dev):
     x = torch.from_numpy(cases[0]["x"][0]).to(dev)
     ys = [torch.empty(N, dtype=torch.float16, device=dev) for N in Ns]
 
-    def step(i, ev):
+    def step(i):
         Wc = Ws[i % copies]
-        if ev: ev()
         ql.qlinear_gemv(Wc[0], x, ys[0])
-        if ev: ev()
         ql.qlinear_gemv(Wc[1], x, ys[1])
-        if ev: ev()
 
-    ms, per = timed_steps(step, args.steps, args.warmup)
-    kern_ms = per.mean(axis=0)  # [small, head]
+    # The timed region holds only launches of the GEMV kernel (both matrices
+    # have K = 2048 and take the same kernel), so its average launch
+    # duration is the region time over the number of launches.
+    ms = timed_steps(step, args.steps, args.warmup)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launch_bytes = [w4_bytes(K, N) + 2 * K + 2 * N for N in Ns]
     avg_launch_bytes = sum(launch_bytes) / 2
-    avg_launch_ms = kern_ms.mean()
+    avg_launch_ms = ms / 2
     achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    # Each matrix alone (back-to-back launches with rotation), for context.
+    kern_ms = []
+    for j in range(2):
+        kern_ms.append(timed_steps(lambda i, j=j: ql.qlinear_gemv(Ws[i % copies][j], x, ys[j]),
+                                   args.steps, args.warmup))
+    kern_ms = np.asarray(kern_ms)
     sha = source_sha("gemv.hip", "ql_device.h")
-    traffic = traffic_for("gemv_w4_kernel<32,1,2>", sha)
+    traffic = traffic_for(KERNEL_GEMV, sha)
     return {
         "value": gbs, "ms_per_step": ms, "step_bytes": step_bytes, "rotation_copies": copies,
         "per_matrix": {f"N={N}": {"us": float(kern_ms[j] * 1e3),
                                   "GB/s": launch_bytes[j] / (kern_ms[j] * 1e-3) / 1e9}
                        for j, N in enumerate(Ns)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_w4_kernel<32,1,2>", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": KERNEL_GEMV, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": avg_launch_bytes,
                      "avg_launch_us": float(avg_launch_ms * 1e3), "source_sha": sha},
@@ -179,16 +201,14 @@ def bench_gemm(args, dev):
         Xs = [X] + [X.clone() for _ in range(1 if M >= 4096 else 3)]
         Y = torch.empty((M, N), dtype=torch.float16, device=dev)
 
-        def step(i, ev):
-            if ev: ev()
+        def step(i):
             ql.qlinear_gemm(W, Xs[i % len(Xs)], Y)
-            if ev: ev()
 
         steps = 20 if M <= 4096 else 8
-        ms, per = timed_steps(step, steps, 3)
+        ms = timed_steps(step, steps, 3)
         flops = 2.0 * M * N * K
-        tf = flops / (per.mean() * 1e-3) / 1e12
-        out[f"M={M}"] = {"us": float(per.mean() * 1e3), "TFLOP/s": tf, "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf, "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
         del Xs, Y, X, W
         torch.cuda.empty_cache()
     return out
@@ -208,28 +228,42 @@ def bench_moe_decode(args, dev, w):
     base = moe_dev_weights(w, dev)
     copies = [base, {k: (clone_w4(v) if isinstance(v, dict) else v.clone()) for k, v in base.items()}]
     toks = [torch.from_numpy(synth.moe_tokens(2000 + i, 1)["H"]).to(dev) for i in range(32)]
-    route = ql.alloc_route_outputs(1, 256, 8, dev)
+    route_buf = ql.alloc_route_outputs(1, 256, 8, dev)
     act = torch.empty((9, 512), dtype=torch.float16, device=dev)
     out = torch.empty((1, 2048), dtype=torch.float16, device=dev)
 
-    def step(i, ev):
-        dw = copies[i % 2]
-        H = toks[i % len(toks)]
-        if ev: ev()
-        ql.moe_route(H, dw["Wr"], None, 8, route)
-        if ev: ev()
-        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, 1, 8, ql.QL_OP_GATE_UP_SILU, route, act)
-        if ev: ev()
-        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, 1, 8, ql.QL_OP_DOWN_COMBINE, route, out)
-        if ev: ev()
+    def route(i):
+        ql.moe_route(toks[i % len(toks)], copies[i % 2]["Wr"], None, 8, route_buf)
 
-    ms, per = timed_steps(step, 200, 20)
+    def gate_up(i):
+        dw = copies[i % 2]
+        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], toks[i % len(toks)], 1, 8,
+                            ql.QL_OP_GATE_UP_SILU, route_buf, act)
+
+    def down(i):
+        dw = copies[i % 2]
+        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, 1, 8, ql.QL_OP_DOWN_COMBINE,
+                            route_buf, out)
+
+    def step(i):
+        route(i)
+        gate_up(i)
+        down(i)
+
+    # The per-call host path (Python, ctypes) is slower than these short
+    # kernels, so the decode layer is timed as HIP graphs: NG steps captured
+    # once (tokens and weight copies rotating), replayed back to back.
+    NG = 16
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    ms = graph_time(step, NG, 30)
+    k = [graph_time(fn, NG, 30) for fn in (route, gate_up, down)]
     algo = 2048 * 256 * 2 + 9 * (w4_bytes(2048, 1024) + w4_bytes(512, 2048)) + 2 * 2048 * 2
-    k = per.mean(axis=0)
     return {"tokens/s": 1e3 / ms, "us_per_token": ms * 1e3, "algorithmic_bytes": algo,
             "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
-                         "down_combine": float(k[2] * 1e3)}}
+            "stage_us": {"route": k[0] * 1e3, "gate_up_silu": k[1] * 1e3, "down_combine": k[2] * 1e3},
+            "timing": "HIP graph of 16 decode steps, replayed"}
 
 
 def bench_moe_prefill(args, dev, w):
@@ -247,19 +281,26 @@ def bench_moe_prefill(args, dev, w):
     yd = torch.empty((9 * T, 2048), dtype=torch.float16, device=dev)
     out = torch.empty((T, 2048), dtype=torch.float16, device=dev)
 
-    def step(i, ev):
-        if ev: ev()
+    def r_(i):
         ql.moe_route(H, dw["Wr"], bias, 8, route)
-        if ev: ev()
-        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU, route, act)
-        if ev: ev()
-        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
-        if ev: ev()
-        ql.moe_combine(yd, route["gates"], route["pos"], T, 8, True, out)
-        if ev: ev()
 
-    ms, per = timed_steps(step, 20, 3)
-    k = per.mean(axis=0)
+    def gu(i):
+        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU, route, act)
+
+    def dn(i):
+        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
+
+    def cb(i):
+        ql.moe_combine(yd, route["gates"], route["pos"], T, 8, True, out)
+
+    def step(i):
+        r_(i)
+        gu(i)
+        dn(i)
+        cb(i)
+
+    ms = timed_steps(step, 20, 3)
+    k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2))
     routed_rows = T * 8
     flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
              + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)

@@ -78,12 +78,12 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
 size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk) {
     if (T < 0 || E <= 0 || E > QL_MAX_EXPERTS || topk <= 0 || topk > E || topk > QL_MAX_TOPK)
         return 0;
-    return ql::moe_workspace_layout(T, E, topk, 0).total;
+    return ql::moe_workspace_layout(T, E, topk).total;
 }
 
 size_t ql_moe_logits_offset(int32_t T, int32_t E, int32_t topk) {
     if (moe_workspace_bytes(T, E, topk) == 0) return 0;
-    return ql::moe_workspace_layout(T, E, topk, 0).logits;
+    return ql::moe_workspace_layout(T, E, topk).logits;
 }
 
 static int check_route_common(int32_t T, int32_t E, int32_t topk, const int32_t* counts,

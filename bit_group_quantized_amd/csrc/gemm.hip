@@ -26,6 +26,8 @@
 // the slice therefore gives the same dot product.  Slice s of a K step uses
 // k = 32h + 8s + v, so a lane's 8 values are one contiguous 16-byte chunk of
 // an LDS row and one packed word of codes.
+#include <type_traits>
+
 #include "ql_device.h"
 #include "ql_internal.h"
 
@@ -184,59 +186,68 @@ gemm_w4_kernel(const KParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 areg[TL::A_LOADS];
-    u32x4 breg[(MODE == MODE_ROUTER) ? 1 : TL::WPT / 4];
-    uint16_t sreg = 0, bireg = 0;
-    // router B staging: 8 x 16-byte loads of 8 consecutive columns per thread
-    u32x4 hreg[(MODE == MODE_ROUTER) ? (BN / 32) : 1];
+    // Two register sets of staged global data: the loads of step i + 2 are
+    // issued while step i + 1 (loaded one step earlier) is dequantized into
+    // LDS and step i runs on the matrix cores.
+    constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : TL::WPT / 4;
+    constexpr int HREG = (MODE == MODE_ROUTER) ? 8 : 1;
+    u32x4 areg[2][TL::A_LOADS];
+    u32x4 breg[2][BREG];
+    uint16_t sreg[2] = {0, 0}, bireg[2] = {0, 0};
+    // router B staging: an 8 x 8 block of fp16 per thread (8 rows of 16 bytes)
+    u32x4 hreg[2][HREG];
 
-    auto load_stage = [&](int ks) {
+    auto load_stage = [&](auto set, int ks) {
+        constexpr int S = decltype(set)::value;
         const int k0 = ks * kGroup;
 #pragma unroll
-        for (int i = 0; i < TL::A_LOADS; ++i) areg[i] = ld_u32x4(arow[i] + k0);
+        for (int i = 0; i < TL::A_LOADS; ++i) areg[S][i] = ld_u32x4(arow[i] + k0);
         if constexpr (MODE == MODE_ROUTER) {
-            // tile of 64 k-rows x BN columns; load j covers k-row (tid/ (BN/8)) + ...
+            // One 8 x 8 block per thread: k rows 8*kb .. 8*kb+7 of the step,
+            // columns 8*nb .. 8*nb+7 of the tile.
+            static_assert(BN == 256, "router staging assumes 32 column blocks of 8");
+            const int kb = tid & 7, nb = tid >> 3;
+            const int col = min(n0 + 8 * nb, p.N - 8);
 #pragma unroll
-            for (int j = 0; j < BN / 32; ++j) {
-                const int idx = j * 256 + tid;            // 0 .. 8*BN-1
-                const int kr = idx / (BN / 8);
-                const int c8 = (idx % (BN / 8)) * 8;
-                const int col = min(n0 + c8, p.N - 8);
-                hreg[j] = ld_u32x4(p.Bh + (size_t)(k0 + kr) * p.N + col);
-            }
+            for (int r = 0; r < 8; ++r) hreg[S][r] = ld_u32x4(p.Bh + (size_t)(k0 + 8 * kb + r) * p.N + col);
         } else {
             const uint32_t* src = wq + (size_t)bcol * wpr + ks * 8 + bpart * TL::WPT;
 #pragma unroll
-            for (int i = 0; i < TL::WPT / 4; ++i) breg[i] = ld_u32x4(src + 4 * i);
-            sreg = ws[(size_t)bcol * G + ks];
-            bireg = wb[(size_t)bcol * G + ks];
+            for (int i = 0; i < BREG; ++i) breg[S][i] = ld_u32x4(src + 4 * i);
+            sreg[S] = ws[(size_t)bcol * G + ks];
+            bireg[S] = wb[(size_t)bcol * G + ks];
         }
     };
 
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](auto set, int buf) {
+        constexpr int S = decltype(set)::value;
         f16* a_dst = As + buf * TL::LDS_A;
 #pragma unroll
         for (int i = 0; i < TL::A_LOADS; ++i)
-            *reinterpret_cast<u32x4*>(a_dst + (i * 32 + (tid >> 3)) * kLdk + a_chunk * 8) = areg[i];
+            *reinterpret_cast<u32x4*>(a_dst + (i * 32 + (tid >> 3)) * kLdk + a_chunk * 8) = areg[S][i];
         f16* b_dst = Bs + buf * TL::LDS_B;
         if constexpr (MODE == MODE_ROUTER) {
+            // Transpose the 8 x 8 block in registers: output row j (column
+            // 8*nb + j) pairs element j of k rows (2i, 2i+1).
+            const int kb = tid & 7, nb = tid >> 3;
 #pragma unroll
-            for (int j = 0; j < BN / 32; ++j) {
-                const int idx = j * 256 + tid;
-                const int kr = idx / (BN / 8);
-                const int c8 = (idx % (BN / 8)) * 8;
-                const f16x8 h = __builtin_bit_cast(f16x8, hreg[j]);
-#pragma unroll
-                for (int v = 0; v < 8; ++v) b_dst[(c8 + v) * kLdk + kr] = h[v];
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 o;
+                o.x = __builtin_amdgcn_perm(hreg[S][1][j >> 1], hreg[S][0][j >> 1], sel);
+                o.y = __builtin_amdgcn_perm(hreg[S][3][j >> 1], hreg[S][2][j >> 1], sel);
+                o.z = __builtin_amdgcn_perm(hreg[S][5][j >> 1], hreg[S][4][j >> 1], sel);
+                o.w = __builtin_amdgcn_perm(hreg[S][7][j >> 1], hreg[S][6][j >> 1], sel);
+                *reinterpret_cast<u32x4*>(b_dst + (8 * nb + j) * kLdk + 8 * kb) = o;
             }
         } else {
-            const f16 s = __builtin_bit_cast(f16, sreg);
-            const f16 b = __builtin_bit_cast(f16, bireg);
-            const f16x2 s2 = {s, s};
-            const f16x2 b2 = {b, b};
+            const f16 sv = __builtin_bit_cast(f16, sreg[S]);
+            const f16 bv = __builtin_bit_cast(f16, bireg[S]);
+            const f16x2 s2 = {sv, sv};
+            const f16x2 b2 = {bv, bv};
 #pragma unroll
-            for (int i = 0; i < TL::WPT / 4; ++i) {
-                const uint32_t wv[4] = {breg[i].x, breg[i].y, breg[i].z, breg[i].w};
+            for (int i = 0; i < BREG; ++i) {
+                const uint32_t wv[4] = {breg[S][i].x, breg[S][i].y, breg[S][i].z, breg[S][i].w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int word = bpart * TL::WPT + 4 * i + q;  // 0..7 within the group
@@ -246,20 +257,11 @@ gemm_w4_kernel(const KParams p) {
         }
     };
 
-    if (kbeg < kend) {
-        load_stage(kbeg);
-        store_stage(0);
-    }
-    __syncthreads();
-
     const int fl = lane & 31;   // row (A) / column (B) inside a 32-wide subtile
     const int fh = lane >> 5;   // which half of the 16-wide K slice
-    for (int ks = kbeg; ks < kend; ++ks) {
-        const int cur = (ks - kbeg) & 1;
-        const bool more = ks + 1 < kend;
-        if (more) load_stage(ks + 1);
-        const f16* a_src = As + cur * TL::LDS_A + (wm0 + fl) * kLdk;
-        const f16* b_src = Bs + cur * TL::LDS_B + (wn0 + fl) * kLdk;
+    auto compute = [&](int buf) {
+        const f16* a_src = As + buf * TL::LDS_A + (wm0 + fl) * kLdk;
+        const f16* b_src = Bs + buf * TL::LDS_B + (wn0 + fl) * kLdk;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int koff = (4 * fh + s) * 8;
@@ -274,9 +276,52 @@ gemm_w4_kernel(const KParams p) {
                 for (int j = 0; j < WN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if (more) store_stage(cur ^ 1);
+    };
+
+    // Interleave the staging work of the next step with this step's MFMAs:
+    // per 16-wide K slice, the fragment reads, then each MFMA followed by a
+    // few VALU (dequantization) instructions, then the LDS stores.
+    auto interleave = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x020, TL::A_LOADS + BREG + 2 + HREG, 0);  // VMEM reads
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x100, WM + WN, 0);  // DS reads
+#pragma unroll
+            for (int m = 0; m < WM * WN; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);  // DS writes
+        }
+    };
+
+    // The loop body for the step `i` (relative to kbeg) whose data sits in
+    // LDS buffer S = i & 1.  Loads and stores past the last step are clamped
+    // to the last step (harmless repeats) so that the body has no branches.
+    auto body = [&](auto set, int i) {
+        constexpr int S = decltype(set)::value;
+        load_stage(set, min(kbeg + i + 2, kend - 1));
+        compute(S);
+        store_stage(std::integral_constant<int, S ^ 1>{}, S ^ 1);
+        interleave();
         __syncthreads();
+    };
+
+    const std::integral_constant<int, 0> set0{};
+    const std::integral_constant<int, 1> set1{};
+    const int nk = kend - kbeg;
+    if (nk > 0) {
+        load_stage(set0, kbeg);
+        store_stage(set0, 0);
+        load_stage(set1, min(kbeg + 1, kend - 1));
     }
+    __syncthreads();
+    int i = 0;
+    for (; i + 1 < nk; i += 2) {
+        body(set0, i);
+        body(set1, i + 1);
+    }
+    if (i < nk) body(set0, i);
 
     // ---- epilogue -------------------------------------------------------------
     // acc[i][j][r]: row 32i + 8(r/4) + 4h + r%4, column 32j + l%32 of the wave tile.
@@ -352,7 +397,7 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     return launch_t<2, 4, MODE_DENSE>(p, grid, st);
 }
 
-constexpr int kRouterSplit = 4;
+constexpr int kRouterSplit = kRouterMfmaSplit;
 
 int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
                               int E, hipStream_t st) {
@@ -369,10 +414,9 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
     return launch_t<1, 4, MODE_ROUTER>(p, grid, st);
 }
 
-int router_mfma_parts() { return kRouterSplit; }
 
 int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
-    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk, 0);
+    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     KParams p{};
     p.A = a.X;
     p.qw = a.qw;

@@ -143,192 +143,348 @@ gemv_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
 }
 
 // ---------------------------------------------------------------------------
-// Routed-expert rows (decode MoE).  Row r < T*topk is the assignment
-// sorted_assign[r], multiplied by the expert e with offsets[e] <= r <
-// offsets[e+1]; rows T*topk .. T*topk+T-1 are the tokens multiplied by the
-// shared expert.
+// Chunked dense GEMV: every lane owns 16-byte chunks of codes (32 codes, half
+// a quantization group) at a fixed K position and visits R consecutive rows.
+// One wave instruction then reads TPR*16 contiguous bytes of each of
+// 64/TPR rows: with K = 2048 a whole 1 KB row per instruction.  All R rows'
+// loads are issued before any arithmetic (R*V 128-bit loads in flight per
+// lane), and the R partial sums are reduced across the team by halving: at
+// each of the first log2(R) exchange steps a lane keeps half of its rows
+// and adds the partner's copy of them, so R rows cost R-1 shuffles, not
+// R*log2(TPR).
 // ---------------------------------------------------------------------------
-// Expert of routed row r from offsets staged in LDS (upper bound search).
-__device__ __forceinline__ int expert_of_row(const int* s_off, int E, int r) {
-    int lo = 0, hi = E;  // find largest e with s_off[e] <= r
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= r) lo = mid; else hi = mid;
+template <int TPR, int R>
+__device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
+    static_assert(R <= TPR, "each row needs its own lane after the halving steps");
+    int base = 0;
+#pragma unroll
+    for (int off = TPR / 2, cnt = R; off >= 1; off >>= 1) {
+        if (cnt > 1) {
+            const bool hi = (lr & off) != 0;
+            const int h = cnt / 2;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float send = hi ? v[i] : v[i + h];
+                const float keep = hi ? v[i + h] : v[i];
+                v[i] = keep + __shfl_xor(send, off, 64);
+            }
+            if (hi) base += h;
+            cnt = h;
+        } else {
+            v[0] += __shfl_xor(v[0], off, 64);
+        }
     }
-    return lo;
+    row = base;
+    return v[0];
 }
 
-__device__ __forceinline__ void stage_offsets(const int* __restrict__ offsets, int E, int* s_off) {
-    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = offsets[i];
-    __syncthreads();
-}
-
-// MODE 0: gate_up with SiLU(gate) * up   (output width N/2, x = X[token])
-// MODE 1: down                            (output width N,   x = X[row])
-template <int TPR, int GPL, int MODE>
+template <int TPR, int V, int R>
 __global__ void __launch_bounds__(256)
-moe_rows_gemv_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                     const uint16_t* __restrict__ bi,
-                     const uint32_t* __restrict__ sqw, const uint16_t* __restrict__ ssc,
-                     const uint16_t* __restrict__ sbi,
-                     const uint16_t* __restrict__ X, const int* __restrict__ offsets,
-                     const int* __restrict__ sorted_assign, uint16_t* __restrict__ Y,
-                     int K, int N, int E, int T, int topk) {
-    __shared__ int s_off[QL_MAX_EXPERTS_DEV + 1];
+gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                       const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
+                       uint16_t* __restrict__ y, int K, int N) {
     constexpr int TEAMS = 64 / TPR;
     const int lane = threadIdx.x & 63;
     const int lr = lane % TPR;
     const int team = lane / TPR;
-    const int wave = threadIdx.x / 64;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int gwave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+    const int row0 = (gwave * TEAMS + team) * R;
+
+    // Activations of this lane's chunks (L2-resident after the first wave)
+    // and then the codes, scales and biases of R rows: every load is issued
+    // before any arithmetic, activations first so that work on row 0 can
+    // start while later rows are still in flight.
+    u32x4 xr[V][4];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(x + (lr + v * TPR) * 32 + w * 8);
+    u32x4 cw[R][V];
+    uint16_t s[R][V], b[R][V];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int hg = lr + v * TPR;  // half-group index along K
+            cw[r][v] = ld_stream_u32x4(qw + (size_t)row * wpr + hg * 4);
+            s[r][v] = sc[(size_t)row * G + (hg >> 1)];
+            b[r][v] = bi[(size_t)row * G + (hg >> 1)];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    XPairs xp[V][4];
+    float xc[V], xs[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        xc[v] = 0.f;
+        xs[v] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            xp[v][w] = make_xpairs(xr[v][w]);
+            float cw_, sw_;
+            xpairs_consts(xp[v][w], xr[v][w], cw_, sw_);
+            xc[v] += cw_;
+            xs[v] += sw_;
+        }
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc[r] = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+            dot_word(cw[r][v].x, xp[v][0], d0, d1, d2, d3);
+            dot_word(cw[r][v].y, xp[v][1], d0, d1, d2, d3);
+            dot_word(cw[r][v].z, xp[v][2], d0, d1, d2, d3);
+            dot_word(cw[r][v].w, xp[v][3], d0, d1, d2, d3);
+            const float d = (d0 + d2) + (d1 + d3);
+            acc[r] += h2f(s[r][v]) * (d - xc[v]) + h2f(b[r][v]) * xs[v];
+        }
+    }
+    int rsel;
+    const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
+    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot);
+}
+
+// ---------------------------------------------------------------------------
+// Routed-expert rows (decode MoE), chunked like the dense GEMV.  Row r <
+// T*topk of the routed layout is (expert, token) = row_info[r], written by
+// the dispatch step; rows T*topk .. T*topk+T-1 are the tokens multiplied by
+// the shared expert.  One wave per block.
+//
+// MODE 0 (gate_up + SiLU): the wave's R weight rows are R/2 gate rows n and
+//   the R/2 matching up rows n + N/2; after the halving reduction the lane
+//   holding gate row n and the lane holding up row n differ only in the
+//   first halving bit, so one more exchange brings them together.
+// MODE 1 (down): R output rows.
+// ---------------------------------------------------------------------------
+template <int TPR, int V, int R, int MODE>
+__global__ void __launch_bounds__(64)
+moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
+                const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                const uint16_t* __restrict__ X, const int2* __restrict__ row_info,
+                uint16_t* __restrict__ Y, int K, int N, int E, int T, int topk) {
+    constexpr int TEAMS = 64 / TPR;
+    constexpr int OUT = (MODE == 0) ? R / 2 : R;  // outputs per team
+    const int lane = threadIdx.x;
+    const int lr = lane % TPR;
+    const int team = lane / TPR;
     const int G = K / kGroup;
     const int wpr = K / 8;
     const int r = blockIdx.y;
     const int routed = T * topk;
-
-    stage_offsets(offsets, E, s_off);
-    const uint32_t* wq;
-    const uint16_t* ws;
-    const uint16_t* wb;
+    const uint32_t* wq = sqw;
+    const uint16_t* ws = ssc;
+    const uint16_t* wb = sbi;
     int xrow;
     if (r < routed) {
-        const int e = expert_of_row(s_off, E, r);
+        const int2 info = row_info[r];
+        // Clamped so that a corrupted dispatch can never index out of bounds.
+        const int e = min(max(info.x, 0), E - 1);
         wq = qw + (size_t)e * N * wpr;
         ws = sc + (size_t)e * N * G;
         wb = bi + (size_t)e * N * G;
-        // Clamped so that a corrupted dispatch can never index outside X.
-        xrow = (MODE == 0) ? min(max(sorted_assign[r] / topk, 0), T - 1) : r;
+        xrow = (MODE == 0) ? min(max(info.y, 0), T - 1) : r;
     } else {
-        wq = sqw;
-        ws = ssc;
-        wb = sbi;
         xrow = (MODE == 0) ? r - routed : r;
     }
     const int Nout = (MODE == 0) ? N / 2 : N;
-    const int n = (blockIdx.x * (blockDim.x / 64) + wave) * TEAMS + team;
-    const int nn = min(n, Nout - 1);
+    const int n0 = (blockIdx.x * TEAMS + team) * OUT;
 
-    // Issue the weight loads first: they do not depend on the activations.
-    constexpr int NR = (MODE == 0) ? 2 : 1;
-    u32x4 cw[NR][GPL][2];
-    uint16_t s[NR][GPL], b[NR][GPL];
+    u32x4 xr[V][4];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-        const int row = nn + q * Nout;
+    for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int i = 0; i < GPL; ++i) {
-            const int g = lr + i * TPR;
-            const uint32_t* p = wq + (size_t)row * wpr + g * 8;
-            cw[q][i][0] = ld_stream_u32x4(p);
-            cw[q][i][1] = ld_stream_u32x4(p + 4);
-            s[q][i] = ws[(size_t)row * G + g];
-            b[q][i] = wb[(size_t)row * G + g];
+        for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(X + (size_t)xrow * K + (lr + v * TPR) * 32 + w * 8);
+    u32x4 cw[R][V];
+    uint16_t s[R][V], b[R][V];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int nn = min(n0 + q % OUT, Nout - 1);
+        const int row = nn + ((MODE == 0 && q >= OUT) ? Nout : 0);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int hg = lr + v * TPR;
+            cw[q][v] = ld_stream_u32x4(wq + (size_t)row * wpr + hg * 4);
+            s[q][v] = ws[(size_t)row * G + (hg >> 1)];
+            b[q][v] = wb[(size_t)row * G + (hg >> 1)];
         }
     }
-    const uint16_t* x = X + (size_t)xrow * K;
-    float acc[NR];
+    __builtin_amdgcn_sched_barrier(0);
+    XPairs xp[V][4];
+    float xc[V], xs[V];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) acc[q] = 0.f;
+    for (int v = 0; v < V; ++v) {
+        xc[v] = 0.f;
+        xs[v] = 0.f;
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-        XPairs xp[8];
-        float c, xs;
-        load_group_x(x, lr + i * TPR, xp, c, xs);
-#pragma unroll
-        for (int q = 0; q < NR; ++q) {
-            const float d = group_dot(cw[q][i][0], cw[q][i][1], xp);
-            acc[q] += h2f(s[q][i]) * (d - c) + h2f(b[q][i]) * xs;
+        for (int w = 0; w < 4; ++w) {
+            xp[v][w] = make_xpairs(xr[v][w]);
+            float c_, s_;
+            xpairs_consts(xp[v][w], xr[v][w], c_, s_);
+            xc[v] += c_;
+            xs[v] += s_;
         }
     }
+    float acc[R];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) acc[q] = team_sum<TPR>(acc[q]);
-    if (lr == 0 && n < Nout) {
-        const float v = (MODE == 0) ? silu(acc[0]) * acc[1] : acc[0];
-        Y[(size_t)r * Nout + n] = f2h(v);
+    for (int q = 0; q < R; ++q) {
+        acc[q] = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+            dot_word(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
+            dot_word(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
+            dot_word(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
+            dot_word(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
+            acc[q] += h2f(s[q][v]) * (((d0 + d2) + (d1 + d3)) - xc[v]) + h2f(b[q][v]) * xs[v];
+        }
+    }
+    int sel;
+    const float tot = reduce_rows<TPR, R>(acc, lr, sel);
+    const bool writer = (lr & (TPR / R - 1)) == 0;
+    if constexpr (MODE == 0) {
+        const float up = __shfl_xor(tot, TPR / 2, 64);  // row sel + R/2 of the same team
+        if (writer && sel < OUT && n0 + sel < Nout)
+            Y[(size_t)r * Nout + n0 + sel] = f2h(silu(tot) * up);
+    } else {
+        if (writer && n0 + sel < Nout) Y[(size_t)r * Nout + n0 + sel] = f2h(tot);
     }
 }
 
 // Decode down projection fused with the gate-weighted sum over the token's
-// routed rows and the shared row.  One block column per token.  The rows'
-// activations are pre-paired once per block into LDS.
-template <int TPR, int GPL>
-__global__ void __launch_bounds__(256)
+// routed rows and its shared row.  One wave per block owns TEAMS*R outputs
+// of one token.  The (expert, row) of each assignment comes from
+// assign_info; all code loads of all rows are issued together, the
+// activation rows are pre-paired into LDS meanwhile.  The per-output sum
+// runs in the fixed order j = 0 .. topk-1, then the shared row.
+template <int TPR, int V, int R, int JC>
+__global__ void __launch_bounds__(64)
 moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                        const uint16_t* __restrict__ bi,
-                        const uint32_t* __restrict__ sqw, const uint16_t* __restrict__ ssc,
-                        const uint16_t* __restrict__ sbi,
-                        const uint16_t* __restrict__ X, const int* __restrict__ offsets,
-                        const float* __restrict__ gates, const int* __restrict__ assign_pos,
-                        uint16_t* __restrict__ Y, int K, int N, int E, int T, int topk,
-                        int has_shared) {
+                        const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
+                        const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                        const uint16_t* __restrict__ X, const float* __restrict__ gates,
+                        const int2* __restrict__ assign_info, uint16_t* __restrict__ Y, int K,
+                        int N, int E, int T, int topk, int has_shared) {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_off[QL_MAX_EXPERTS_DEV + 1];
     __shared__ int s_exp[QL_MAX_TOPK_DEV + 1];
+    __shared__ int s_row[QL_MAX_TOPK_DEV + 1];
     __shared__ float s_gate[QL_MAX_TOPK_DEV + 1];
     constexpr int TEAMS = 64 / TPR;
     const int G = K / kGroup;
     const int wpr = K / 8;
+    const int CH = K / 32;  // 16-byte chunks of codes per row
     const int t = blockIdx.y;
-    const int J = topk + (has_shared ? 1 : 0);
-    XPairs* s_xp = reinterpret_cast<XPairs*>(smem);                 // [J][G][8]
-    float* s_c = reinterpret_cast<float*>(s_xp + (size_t)J * G * 8);  // [J][G]
-    float* s_xs = s_c + J * G;                                       // [J][G]
+    const int J = topk + has_shared;
+    const int nrows = T * topk + (has_shared ? T : 0);
+    XPairs* s_xp = reinterpret_cast<XPairs*>(smem);                   // [J][CH][4]
+    float* s_c = reinterpret_cast<float*>(s_xp + (size_t)J * CH * 4);  // [J][CH]
+    float* s_xs = s_c + J * CH;                                        // [J][CH]
 
-    stage_offsets(offsets, E, s_off);
-    if (threadIdx.x < J) {
-        const int j = threadIdx.x;
+    for (int j = threadIdx.x; j < J; j += blockDim.x) {
         if (j < topk) {
-            s_exp[j] = expert_of_row(s_off, E, min(max(assign_pos[t * topk + j], 0), T * topk - 1));
-            s_gate[j] = gates[t * topk + j];
+            const int2 info = assign_info[(size_t)t * topk + j];
+            // Clamped so that a corrupted dispatch can never index out of bounds.
+            s_exp[j] = min(max(info.x, 0), E - 1);
+            s_row[j] = min(max(info.y, 0), nrows - 1);
+            s_gate[j] = gates[(size_t)t * topk + j];
         } else {
-            s_exp[j] = -1;  // shared expert, weight 1
+            s_exp[j] = -1;
+            s_row[j] = T * topk + t;
             s_gate[j] = 1.0f;
         }
     }
-    // Stage pre-paired activations: one (row j, group g) per thread iteration.
-    for (int idx = threadIdx.x; idx < J * G; idx += blockDim.x) {
-        const int j = idx / G, g = idx % G;
-        const int nrows = T * topk + (has_shared ? T : 0);
-        const int row = (j < topk) ? min(max(assign_pos[t * topk + j], 0), nrows - 1) : T * topk + t;
-        XPairs xp[8];
-        float c, xs;
-        load_group_x(X + (size_t)row * K, g, xp, c, xs);
-#pragma unroll
-        for (int w = 0; w < 8; ++w) s_xp[((size_t)j * G + g) * 8 + w] = xp[w];
-        s_c[j * G + g] = c;
-        s_xs[j * G + g] = xs;
-    }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     const int lr = lane % TPR;
     const int team = lane / TPR;
-    const int n = (blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * TEAMS + team;
-    const int nn = min(n, N - 1);
-    float acc = 0.f;
-    for (int j = 0; j < J; ++j) {
-        const int e = s_exp[j];
-        const uint32_t* wq = (e >= 0) ? qw + (size_t)e * N * wpr : sqw;
-        const uint16_t* ws = (e >= 0) ? sc + (size_t)e * N * G : ssc;
-        const uint16_t* wb = (e >= 0) ? bi + (size_t)e * N * G : sbi;
-        float part = 0.f;
+    const int n0 = (blockIdx.x * TEAMS + team) * R;
+    float acc[R];
 #pragma unroll
-        for (int i = 0; i < GPL; ++i) {
-            const int g = lr + i * TPR;
-            const uint32_t* p = wq + (size_t)nn * wpr + g * 8;
-            const u32x4 c0 = ld_stream_u32x4(p);
-            const u32x4 c1 = ld_stream_u32x4(p + 4);
-            const float s = h2f(ws[(size_t)nn * G + g]);
-            const float b = h2f(wb[(size_t)nn * G + g]);
-            const XPairs* xp = s_xp + ((size_t)j * G + g) * 8;
-            XPairs xr[8];
+    for (int q = 0; q < R; ++q) acc[q] = 0.f;
+
+    // Rows are processed JC at a time: the code loads of JC rows are issued
+    // together (the first group before the activation staging), so a
+    // token's topk + 1 rows cost one memory round trip when topk + 1 <= JC.
+    for (int j0 = 0; j0 < J; j0 += JC) {
+        u32x4 cw[JC][R][V];
+        uint16_t s[JC][R][V], b[JC][R][V];
 #pragma unroll
-            for (int w = 0; w < 8; ++w) xr[w] = xp[w];
-            part += s * (group_dot(c0, c1, xr) - s_c[j * G + g]) + b * s_xs[j * G + g];
+        for (int jj = 0; jj < JC; ++jj) {
+            const int j = min(j0 + jj, J - 1);
+            const int e = s_exp[j];
+            const uint32_t* wq = (e >= 0) ? qw + (size_t)e * N * wpr : sqw;
+            const uint16_t* ws = (e >= 0) ? sc + (size_t)e * N * G : ssc;
+            const uint16_t* wb = (e >= 0) ? bi + (size_t)e * N * G : sbi;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int row = min(n0 + q, N - 1);
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int hg = lr + v * TPR;
+                    cw[jj][q][v] = ld_stream_u32x4(wq + (size_t)row * wpr + hg * 4);
+                    s[jj][q][v] = ws[(size_t)row * G + (hg >> 1)];
+                    b[jj][q][v] = wb[(size_t)row * G + (hg >> 1)];
+                }
+            }
         }
-        acc += s_gate[j] * part;
+        if (j0 == 0) {
+            // Activation rows, pre-paired, into LDS (one chunk per iteration).
+            for (int idx = threadIdx.x; idx < J * CH; idx += blockDim.x) {
+                const int j = idx / CH, c = idx % CH;
+                const uint16_t* xrow = X + (size_t)s_row[j] * K + c * 32;
+                u32x4 xw[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) xw[w] = ld_u32x4(xrow + w * 8);
+                float cc = 0.f, xx = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const XPairs xp = make_xpairs(xw[w]);
+                    float c_, s_;
+                    xpairs_consts(xp, xw[w], c_, s_);
+                    cc += c_;
+                    xx += s_;
+                    s_xp[((size_t)j * CH + c) * 4 + w] = xp;
+                }
+                s_c[j * CH + c] = cc;
+                s_xs[j * CH + c] = xx;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+            const int j = j0 + jj;
+            if (j >= J) break;  // uniform across the wave
+            const float g = s_gate[j];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int hg = lr + v * TPR;
+                XPairs xp[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) xp[w] = s_xp[((size_t)j * CH + hg) * 4 + w];
+                const float xc = s_c[j * CH + hg], xs = s_xs[j * CH + hg];
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+                    dot_word(cw[jj][q][v].x, xp[0], d0, d1, d2, d3);
+                    dot_word(cw[jj][q][v].y, xp[1], d0, d1, d2, d3);
+                    dot_word(cw[jj][q][v].z, xp[2], d0, d1, d2, d3);
+                    dot_word(cw[jj][q][v].w, xp[3], d0, d1, d2, d3);
+                    acc[q] += g * (h2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - xc) +
+                                   h2f(b[jj][q][v]) * xs);
+                }
+            }
+        }
     }
-    acc = team_sum<TPR>(acc);
-    if (lr == 0 && n < N) Y[(size_t)t * N + n] = f2h(acc);
+    int sel;
+    const float tot = reduce_rows<TPR, R>(acc, lr, sel);
+    if ((lr & (TPR / R - 1)) == 0 && n0 + sel < N) Y[(size_t)t * N + n0 + sel] = f2h(tot);
 }
 
 constexpr int kMaxGemvBlocks = 2048;
@@ -352,38 +508,64 @@ inline int pow2_divisor(int G) {
     return t;
 }
 
-template <int TPR, int GPL>
+template <int TPR, int V>
 int launch_rows_t(const GroupedArgs& a, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
-    constexpr int OUT_PER_BLOCK = 4 * TEAMS;
-    const int G = a.K / kGroup;
+    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
+    const int has_shared = a.sqw != nullptr;
     if (a.op == QL_OP_DOWN_COMBINE) {
-        const int has_shared = a.sqw != nullptr;
+        constexpr int R = (TPR < 2) ? TPR : 2;
         const int J = a.topk + has_shared;
-        const size_t smem = (size_t)J * G * (8 * sizeof(XPairs) + 2 * sizeof(float));
-        dim3 grid((a.N + OUT_PER_BLOCK - 1) / OUT_PER_BLOCK, a.T);
-        hipLaunchKernelGGL((moe_down_combine_kernel<TPR, GPL>), grid, dim3(256), smem, st,
-                           a.qw, a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.offsets, a.gates, a.pos,
-                           a.Y, a.K, a.N, a.E, a.T, a.topk, has_shared);
+        const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
+        dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
+        hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 9>), grid, dim3(64), smem, st, a.qw,
+                           a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates,
+                           reinterpret_cast<const int2*>(a.ws + L.assign_info), a.Y, a.K, a.N, a.E,
+                           a.T, a.topk, has_shared);
     } else {
-        const int R = a.T * a.topk + (a.sqw ? a.T : 0);
-        const int Nout = (a.op == QL_OP_GATE_UP_SILU) ? a.N / 2 : a.N;
-        dim3 grid((Nout + OUT_PER_BLOCK - 1) / OUT_PER_BLOCK, R);
-        if (a.op == QL_OP_GATE_UP_SILU)
-            hipLaunchKernelGGL((moe_rows_gemv_kernel<TPR, GPL, 0>), grid, dim3(256), 0, st,
-                               a.qw, a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.offsets,
-                               a.sorted_assign, a.Y, a.K, a.N, a.E, a.T, a.topk);
-        else
-            hipLaunchKernelGGL((moe_rows_gemv_kernel<TPR, GPL, 1>), grid, dim3(256), 0, st,
-                               a.qw, a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.offsets,
-                               a.sorted_assign, a.Y, a.K, a.N, a.E, a.T, a.topk);
+        constexpr int R = (TPR < 8) ? TPR : 8;
+        const int rows = a.T * a.topk + (has_shared ? a.T : 0);
+        const int2* rinfo = reinterpret_cast<const int2*>(a.ws + L.row_info);
+        if (a.op == QL_OP_GATE_UP_SILU) {
+            static_assert(R % 2 == 0, "gate/up pairing needs an even row count");
+            const int Nout = a.N / 2;
+            dim3 grid((Nout + TEAMS * (R / 2) - 1) / (TEAMS * (R / 2)), rows);
+            hipLaunchKernelGGL((moe_rows_kernel<TPR, V, R, 0>), grid, dim3(64), 0, st, a.qw, a.sc,
+                               a.bi, a.sqw, a.ssc, a.sbi, a.X, rinfo, a.Y, a.K, a.N, a.E, a.T,
+                               a.topk);
+        } else {
+            dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), rows);
+            hipLaunchKernelGGL((moe_rows_kernel<TPR, V, R, 1>), grid, dim3(64), 0, st, a.qw, a.sc,
+                               a.bi, a.sqw, a.ssc, a.sbi, a.X, rinfo, a.Y, a.K, a.N, a.E, a.T,
+                               a.topk);
+        }
     }
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 }  // namespace
 
+template <int TPR, int V, int R>
+int launch_chunked_t(const GemvArgs& a, hipStream_t st) {
+    constexpr int ROWS_PER_BLOCK = 4 * (64 / TPR) * R;
+    const int blocks = (a.N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    hipLaunchKernelGGL((gemv_w4_chunked_kernel<TPR, V, R>), dim3(blocks), dim3(256), 0, st,
+                       a.qweight, a.scales, a.biases, a.x, a.y, a.K, a.N);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
 int launch_gemv(const GemvArgs& a, hipStream_t st) {
+    // Chunked kernel: K/32 chunks per row spread over TPR lanes, V per lane.
+    switch (a.K) {
+        case 256: return launch_chunked_t<8, 1, 8>(a, st);
+        case 512: return launch_chunked_t<16, 1, 8>(a, st);
+        case 1024: return launch_chunked_t<32, 1, 8>(a, st);
+        case 2048: return launch_chunked_t<64, 1, 8>(a, st);
+        case 4096: return launch_chunked_t<64, 2, 8>(a, st);
+        case 8192: return launch_chunked_t<64, 4, 4>(a, st);
+        case 16384: return launch_chunked_t<64, 8, 2>(a, st);
+        default: break;
+    }
     const int G = a.K / kGroup;
     switch (G) {
         case 8: return launch_gemv_t<8, 1, 2>(a, st);
@@ -410,21 +592,25 @@ int launch_gemv(const GemvArgs& a, hipStream_t st) {
 namespace ql {
 
 bool moe_rows_supported(int K) {
-    const int G = K / kGroup;
-    return K % kGroup == 0 && G >= 1 && G <= 256 && (G & (G - 1)) == 0;
+    // K/32 chunks of codes spread over TPR <= 64 lanes, V = 1, 2, 4 or 8 per lane.
+    switch (K) {
+        case 64: case 128: case 256: case 512: case 1024: case 2048: case 4096: case 8192:
+        case 16384: return true;
+        default: return false;
+    }
 }
 
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st) {
-    switch (a.K / kGroup) {
-        case 1: return launch_rows_t<1, 1>(a, st);
-        case 2: return launch_rows_t<2, 1>(a, st);
-        case 4: return launch_rows_t<4, 1>(a, st);
-        case 8: return launch_rows_t<8, 1>(a, st);
-        case 16: return launch_rows_t<16, 1>(a, st);
-        case 32: return launch_rows_t<32, 1>(a, st);
-        case 64: return launch_rows_t<64, 1>(a, st);
-        case 128: return launch_rows_t<64, 2>(a, st);
-        case 256: return launch_rows_t<64, 4>(a, st);
+    switch (a.K) {
+        case 64: return launch_rows_t<2, 1>(a, st);
+        case 128: return launch_rows_t<4, 1>(a, st);
+        case 256: return launch_rows_t<8, 1>(a, st);
+        case 512: return launch_rows_t<16, 1>(a, st);
+        case 1024: return launch_rows_t<32, 1>(a, st);
+        case 2048: return launch_rows_t<64, 1>(a, st);
+        case 4096: return launch_rows_t<64, 2>(a, st);
+        case 8192: return launch_rows_t<64, 4>(a, st);
+        case 16384: return launch_rows_t<64, 8>(a, st);
         default: return QL_ERR_UNSUPPORTED_SHAPE;
     }
 }

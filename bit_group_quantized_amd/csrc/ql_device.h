@@ -42,15 +42,25 @@ __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// (u & mask) | magic in one v_and_or_b32.  The compiler does not form this
+// instruction by itself (it would need two literal operands); the mask goes
+// in an SGPR and the magic constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t u, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(u), "s"(mask), "v"(magic));
+    return r;
+}
+
 // Dequantize one word (codes k = 8w .. 8w+7 of one output) to 8 fp16 values
 // in natural k order: out[j] = fp16(s*q_j + b), a single rounding (fma).
 __device__ __forceinline__ f16x8 dequant_word(uint32_t u, f16x2 s2, f16x2 b2) {
     const f16x2 off = {(f16)-1024.0f, (f16)-1024.0f};
     // (q0, q4), (q1, q5), (q2, q6), (q3, q7) as exact fp16 integers.
-    f16x2 p0 = as_f16x2((u & 0x000F000Fu) | kMagic2) + off;
-    f16x2 p1 = as_f16x2(((u >> 4) & 0x000F000Fu) | kMagic2) + off;
-    f16x2 p2 = as_f16x2(((u >> 8) & 0x000F000Fu) | kMagic2) + off;
-    f16x2 p3 = as_f16x2(((u >> 12) & 0x000F000Fu) | kMagic2) + off;
+    const uint32_t magic = kMagic2;
+    f16x2 p0 = as_f16x2(and_or(u, 0x000F000Fu, magic)) + off;
+    f16x2 p1 = as_f16x2(and_or(u >> 4, 0x000F000Fu, magic)) + off;
+    f16x2 p2 = as_f16x2(and_or(u >> 8, 0x000F000Fu, magic)) + off;
+    f16x2 p3 = as_f16x2(and_or(u >> 12, 0x000F000Fu, magic)) + off;
     uint32_t w0 = as_u32(__builtin_elementwise_fma(p0, s2, b2));  // (w0, w4)
     uint32_t w1 = as_u32(__builtin_elementwise_fma(p1, s2, b2));  // (w1, w5)
     uint32_t w2 = as_u32(__builtin_elementwise_fma(p2, s2, b2));  // (w2, w6)
@@ -107,10 +117,11 @@ __device__ __forceinline__ void xpairs_consts(const XPairs& r, u32x4 xw, float& 
 // Accumulate sum dot2(x pairs, code pairs) for one word into four partials.
 __device__ __forceinline__ void dot_word(uint32_t u, const XPairs& x, float& d0, float& d1, float& d2, float& d3) {
     const uint32_t t = u >> 8;
-    d0 = dot2(x.p[0], as_f16x2((u & 0x000F000Fu) | kMagic2), d0);
-    d1 = dot2(x.p[1], as_f16x2((u & 0x00F000F0u) | kMagic2), d1);
-    d2 = dot2(x.p[2], as_f16x2((t & 0x000F000Fu) | kMagic2), d2);
-    d3 = dot2(x.p[3], as_f16x2((t & 0x00F000F0u) | kMagic2), d3);
+    const uint32_t magic = kMagic2;
+    d0 = dot2(x.p[0], as_f16x2(and_or(u, 0x000F000Fu, magic)), d0);
+    d1 = dot2(x.p[1], as_f16x2(and_or(u, 0x00F000F0u, magic)), d1);
+    d2 = dot2(x.p[2], as_f16x2(and_or(t, 0x000F000Fu, magic)), d2);
+    d3 = dot2(x.p[3], as_f16x2(and_or(t, 0x00F000F0u, magic)), d3);
 }
 
 __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {

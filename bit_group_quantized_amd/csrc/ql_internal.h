@@ -44,14 +44,16 @@ struct MoeWorkspace {
     size_t partials;      // float[T][nparts][E]   router partial sums
     size_t chunk_counts;  // int32[nchunks][E]
     size_t chunk_err;     // int32[nchunks]
+    size_t row_info;      // int32[T*topk][2]: (expert, token) of each routed row
+    size_t assign_info;   // int32[T*topk][2]: (expert, row) of each assignment
     size_t total;
     int max_tiles, nchunks, nparts;
 };
-MoeWorkspace moe_workspace_layout(int T, int E, int topk, int D_for_partials);
 
 constexpr int kRouteChunkTokens = 256;  // tokens per dispatch chunk
 constexpr int kRouterPartRows = 64;     // D rows per small-T router partial
 constexpr int kRouterSmallT = 16;       // T at or below: row-parallel router
+constexpr int kRouterMfmaSplit = 4;     // K splits of the MFMA router (partials per logit)
 
 struct RouteArgs {
     const uint16_t* H;
@@ -68,9 +70,9 @@ struct RouteArgs {
 };
 int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
                               int E, hipStream_t st);
-int router_mfma_parts();
 bool router_uses_mfma(int T, int E);
-int launch_route(const RouteArgs& a, hipStream_t st);     // logits + top-k + dispatch
+int launch_route(const RouteArgs& a, hipStream_t st);
+MoeWorkspace moe_workspace_layout(int T, int E, int topk);     // logits + top-k + dispatch
 int launch_dispatch(const RouteArgs& a, hipStream_t st);  // dispatch only (ids given)
 
 struct GroupedArgs {

@@ -27,7 +27,8 @@ namespace {
 
 constexpr int kChunk = kRouteChunkTokens;
 constexpr int kMaskWords = kChunk / 32;
-constexpr int kRouterParts = 32;
+constexpr int kRouterParts = 32;     // row-parallel router: D split in 32 slices
+constexpr int kRouterMfmaParts = kRouterMfmaSplit;  // MFMA router: K split
 
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
     return v > bv || (v == bv && e < be);
@@ -71,63 +72,156 @@ router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict
     }
 }
 
+// Same partial sums with 16-byte loads: thread (oct, dl) covers experts
+// 8*oct .. 8*oct+7 and the rows dl, dl+8, ... of the block's D slice; the 8
+// row lanes of an expert octet are summed through LDS in a fixed order.
+// Requires E % 8 == 0.
+__global__ void __launch_bounds__(256)
+router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
+                          float* __restrict__ partials, int D, int E) {
+    __shared__ float red[8][256 + 4];
+    const int t = blockIdx.y, p = blockIdx.x;
+    const int rows = D / kRouterParts;
+    const int d0 = p * rows;
+    const int dl = threadIdx.x >> 5;  // 0..7
+    const int oct = threadIdx.x & 31;
+    // Every thread runs the same number of slice iterations (the barriers
+    // below are reached uniformly).
+    for (int base = 0; base < E; base += 256) {
+        const int e8 = base + oct * 8;
+        float acc[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+        if (e8 < E) {
+#pragma unroll 8
+            for (int d = dl; d < rows; d += 8) {
+                const float h = h2f(H[(size_t)t * D + d0 + d]);
+                const f16x8 w = __builtin_bit_cast(f16x8, ld_u32x4(Wr + (size_t)(d0 + d) * E + e8));
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[v] += h * (float)w[v];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) red[dl][oct * 8 + v] = acc[v];
+        __syncthreads();
+        const int e = base + threadIdx.x;
+        if (e < E) {
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum += red[j][threadIdx.x];
+            partials[((size_t)t * kRouterParts + p) * E + e] = sum;
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Top-k of one token by one wave.  Logits are the sum of `nparts` partial
-// rows (fixed order) plus the optional bias; they are written back to
-// `logits_out`.  Lane j < topk ends up holding choice j.
+// Top-k of one token by one wave.
+//
+// Every (logit, expert) becomes one 64-bit key whose unsigned order is the
+// selection order: the upper word is the logit's bit pattern made monotone
+// (negative values inverted, positive values with the sign bit set), the
+// lower word is 0xFFFFFFFF - e so that equal logits favour the lower index.
+// Key 0 marks an expert already taken (no finite logit maps to it).  A
+// round takes the wave maximum: four DPP steps inside each row of 16 lanes
+// (xor 1, xor 2, half-row mirror, row mirror), then the four row maxima
+// are read into scalar registers, so the winner is uniform.
 // ---------------------------------------------------------------------------
-template <int EPL>
-__device__ void topk_one_token(const float* __restrict__ src, int nparts,
-                               const float* __restrict__ bias, float* __restrict__ logits_out,
-                               int t, int E, int topk, int* sel_e, float* sel_g) {
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_logit(uint64_t k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t k) {
+    return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active), uniform result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = umax64(v, dpp_u64<0x141>(v));  // row_half_mirror
+    v = umax64(v, dpp_u64<0x140>(v));  // row_mirror
+    return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                  umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+// Logits of token t are the sum of `nparts` partial rows (fixed order) plus
+// the optional bias; they are written to logits_out.  Writes the topk
+// chosen experts (descending) and their renormalized gates to sel_e/sel_g.
+template <int EPL, int NP>
+__device__ void topk_one_token(const float* __restrict__ src, const float* __restrict__ bias,
+                               float* __restrict__ logits_out, int t, int E, int topk, int* sel_e,
+                               float* sel_g) {
     const int lane = threadIdx.x & 63;
-    float v[EPL];
+    // Every partial of every logit this lane owns is loaded before the first
+    // sum (NP and EPL are compile-time), so the whole token costs one round
+    // trip to memory.
+    float part[EPL][NP];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) part[i][p] = src[((size_t)t * NP + p) * E + e];
+    }
+    uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        float s = -INFINITY;
+        key[i] = 0;
         if (e < E) {
-            s = 0.f;
-            for (int p = 0; p < nparts; ++p) s += src[((size_t)t * nparts + p) * E + e];
+            float s = 0.f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) s += part[i][p];
             if (bias) s += bias[e];
             logits_out[(size_t)t * E + e] = s;
             if (s != s) s = -INFINITY;  // NaN never wins
+            key[i] = logit_key(s, e);
         }
-        v[i] = s;
     }
-    uint32_t taken = 0;
-    float my_v = 0.f;
+    float vmax = 0.f, my_v = 0.f;
     int my_e = 0;
-    float vmax = 0.f;
     for (int j = 0; j < topk; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+        uint64_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-                bv = v[i];
-                be = e;
-            }
-        }
+        for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
+        best = wave_max_u64(best);  // uniform
+        const int be = key_expert(best);
+        const float bv = key_logit(best);
+        if ((be & 63) == lane) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-            }
+            for (int i = 0; i < EPL; ++i)
+                if (i == (be >> 6)) key[i] = 0;
         }
-        // be < E always: topk <= E and every lane saw every untaken expert.
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (j == 0) vmax = bv;
         if (lane == j) {
             my_v = bv;
             my_e = be;
         }
     }
-    float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
+    const float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
     float sum = ex;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -137,15 +231,15 @@ __device__ void topk_one_token(const float* __restrict__ src, int nparts,
     }
 }
 
-template <int EPL>
+template <int EPL, int NP>
 __global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ src, int nparts, const float* __restrict__ bias,
+topk_kernel(const float* __restrict__ src, const float* __restrict__ bias,
             float* __restrict__ logits_out, int T, int E, int topk,
             int* __restrict__ ids, float* __restrict__ gates) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave leaves together
-    topk_one_token<EPL>(src, nparts, bias, logits_out, t, E, topk, ids + (size_t)t * topk,
-                        gates + (size_t)t * topk);
+    topk_one_token<EPL, NP>(src, bias, logits_out, t, E, topk, ids + (size_t)t * topk,
+                            gates + (size_t)t * topk);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,7 +329,8 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
 __global__ void __launch_bounds__(kChunk)
 dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
                         const int* __restrict__ offsets, const int* __restrict__ chunk_base,
-                        int* __restrict__ sorted_assign, int* __restrict__ pos) {
+                        int* __restrict__ sorted_assign, int* __restrict__ pos,
+                        int2* __restrict__ row_info, int2* __restrict__ assign_info) {
     extern __shared__ uint32_t mask[];
     const int c = blockIdx.x;
     build_chunk_masks(ids, T, E, topk, c, mask);
@@ -249,6 +344,7 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
         const int e = ids[a];
         if ((unsigned)e >= (unsigned)E) {
             pos[a] = -1;
+            assign_info[a] = make_int2(-1, -1);
             continue;
         }
         int rank = __popc(mask[e * kMaskWords + w] & below);
@@ -256,11 +352,21 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
         const int r = offsets[e] + chunk_base[(size_t)c * E + e] + rank;
         sorted_assign[r] = a;
         pos[a] = r;
+        row_info[r] = make_int2(e, t);
+        assign_info[a] = make_int2(e, r);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Small T (decode): top-k and the whole dispatch in one block.
+// ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Small T (decode): top-k and the whole dispatch in one block.  With at most
+// kRouterSmallT tokens one 32-bit mask per expert records which tokens chose
+// it; counts are population counts, the rank of token t inside its expert
+// is the population count of the mask below bit t (stable by construction),
+// and one block scan over the experts gives both the row offsets and the
+// tile indices (every expert has at most one tile here).
 // ---------------------------------------------------------------------------
 template <int EPL, bool DO_TOPK>
 __global__ void __launch_bounds__(256)
@@ -268,18 +374,24 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
                    float* __restrict__ logits_out, int T, int E, int topk,
                    int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
                    int* __restrict__ offsets, int* __restrict__ sorted_assign,
-                   int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles) {
+                   int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
+                   int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+    static_assert(kRouterSmallT <= 32 && kRouterSmallT * QL_MAX_TOPK_DEV <= 4 * QL_MAX_EXPERTS_DEV,
+                  "token masks are 32 bits wide");
+    static_assert(QL_MOE_TILE_ROWS >= kRouterSmallT, "one tile per expert");
     __shared__ int s_ids[kRouterSmallT * QL_MAX_TOPK_DEV];
     __shared__ float s_gates[kRouterSmallT * QL_MAX_TOPK_DEV];
-    __shared__ int s_cnt[QL_MAX_EXPERTS_DEV];
-    __shared__ int s_off[QL_MAX_EXPERTS_DEV + 1];
+    __shared__ uint32_t s_mask[QL_MAX_EXPERTS_DEV];
+    __shared__ int s_off[QL_MAX_EXPERTS_DEV];
+    __shared__ int s_tile[QL_MAX_EXPERTS_DEV];
     __shared__ int s_tmp[16];
     const int wave = threadIdx.x >> 6;
     const int nass = T * topk;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
     if constexpr (DO_TOPK) {
         for (int t = wave; t < T; t += 4)
-            topk_one_token<EPL>(partials, nparts, bias, logits_out, t, E, topk, s_ids + t * topk,
-                                s_gates + t * topk);
+            topk_one_token<EPL, kRouterParts>(partials, bias, logits_out, t, E, topk,
+                                              s_ids + t * topk, s_gates + t * topk);
         __syncthreads();
         for (int a = threadIdx.x; a < nass; a += blockDim.x) {
             ids[a] = s_ids[a];
@@ -287,77 +399,70 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
         }
     } else {
         for (int a = threadIdx.x; a < nass; a += blockDim.x) s_ids[a] = ids[a];
+        __syncthreads();
     }
     int err = 0;
-    for (int a = threadIdx.x; a < nass; a += blockDim.x)
-        if ((unsigned)s_ids[a] >= (unsigned)E) err = 1;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
-    __syncthreads();
     for (int a = threadIdx.x; a < nass; a += blockDim.x) {
         const int e = s_ids[a];
-        if ((unsigned)e < (unsigned)E) {
-            atomicAdd(&s_cnt[e], 1);
-            // repeated expert inside one token
-            const int t = a / topk;
-            for (int j = t * topk; j < a; ++j)
-                if (s_ids[j] == e) err = 1;
+        if ((unsigned)e >= (unsigned)E) {
+            err = 1;
+            continue;
         }
+        const uint32_t bit = 1u << (a / topk);
+        if (atomicOr(&s_mask[e], bit) & bit) err = 1;  // expert repeated within a token
     }
     __syncthreads();
-    // Exclusive scan over experts, 256 threads x ceil(E/256) experts each.
+    // Per thread a contiguous run of experts; scan of (rows, tiles) packed
+    // in one int (rows < 2^16 here).
     const int per = (E + blockDim.x - 1) / blockDim.x;
     int local = 0;
     for (int i = 0; i < per; ++i) {
         const int e = threadIdx.x * per + i;
-        if (e < E) local += s_cnt[e];
+        if (e < E) {
+            const int c = __popc(s_mask[e]);
+            local += c + ((c > 0) << 16);
+        }
     }
     const int incl = block_inclusive_scan(local, s_tmp);
     int run = incl - local;
-    int tiles_local = 0;
     for (int i = 0; i < per; ++i) {
         const int e = threadIdx.x * per + i;
         if (e < E) {
-            s_off[e] = run;
-            run += s_cnt[e];
-            tiles_local += (s_cnt[e] + QL_MOE_TILE_ROWS - 1) / QL_MOE_TILE_ROWS;
-        }
-    }
-    if (threadIdx.x == blockDim.x - 1) s_off[E] = incl;
-    const int tincl = block_inclusive_scan(tiles_local, s_tmp);
-    int ts = tincl - tiles_local;
-    for (int i = 0; i < per; ++i) {
-        const int e = threadIdx.x * per + i;
-        if (e < E) {
-            const int cnt = s_cnt[e];
-            counts[e] = cnt;
-            offsets[e] = s_off[e];
-            for (int j = 0; j * QL_MOE_TILE_ROWS < cnt; ++j, ++ts) {
-                int* tp = tiles + (size_t)ts * 4;
+            const int c = __popc(s_mask[e]);
+            const int off = run & 0xFFFF, tile = run >> 16;
+            s_off[e] = off;
+            s_tile[e] = tile;
+            counts[e] = c;
+            offsets[e] = off;
+            if (c > 0) {
+                int* tp = tiles + (size_t)tile * 4;
                 tp[0] = e;
-                tp[1] = s_off[e] + j * QL_MOE_TILE_ROWS;
-                tp[2] = min(QL_MOE_TILE_ROWS, cnt - j * QL_MOE_TILE_ROWS);
+                tp[1] = off;
+                tp[2] = c;
                 tp[3] = 0;
             }
+            run += c + ((c > 0) << 16);
         }
     }
-    if (threadIdx.x == blockDim.x - 1) offsets[E] = incl;
+    if (threadIdx.x == blockDim.x - 1) offsets[E] = incl & 0xFFFF;
     __syncthreads();
-    // Stable rank: assignments of the same expert with a smaller index.
     for (int a = threadIdx.x; a < nass; a += blockDim.x) {
         const int e = s_ids[a];
         if ((unsigned)e >= (unsigned)E) {
             pos[a] = -1;
+            assign_info[a] = make_int2(-1, -1);
             continue;
         }
-        int rank = 0;
-        for (int b = 0; b < a; ++b) rank += (s_ids[b] == e);
-        const int r = min(s_off[e] + rank, s_off[e + 1] - 1);
+        const int t = a / topk;
+        const int r = s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u));
         sorted_assign[r] = a;
         pos[a] = r;
+        row_info[r] = make_int2(e, t);
+        assign_info[a] = make_int2(e, r);
     }
     const int any = __syncthreads_or(err);
     if (threadIdx.x == blockDim.x - 1) {
-        ws_header[0] = tincl;  // inclusive scan of the last thread = all tiles
+        ws_header[0] = incl >> 16;  // inclusive scan of the last thread = all tiles
         ws_header[1] = QL_MOE_TILE_ROWS;
         ws_header[2] = any;
         ws_header[3] = 0;
@@ -370,14 +475,16 @@ int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStr
     float* logits = reinterpret_cast<float*>(a.ws + L.logits);
     int* hdr = reinterpret_cast<int*>(a.ws + L.header);
     int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
+    int2* rinfo = reinterpret_cast<int2*>(a.ws + L.row_info);
+    int2* ainfo = reinterpret_cast<int2*>(a.ws + L.assign_info);
     if (do_topk)
         hipLaunchKernelGGL((route_small_kernel<EPL, true>), dim3(1), dim3(256), 0, st, partials,
                            L.nparts, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
-                           a.offsets, a.sorted_assign, a.pos, hdr, tiles);
+                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
     else
         hipLaunchKernelGGL((route_small_kernel<EPL, false>), dim3(1), dim3(256), 0, st, partials,
                            L.nparts, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
-                           a.offsets, a.sorted_assign, a.pos, hdr, tiles);
+                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -390,19 +497,25 @@ int launch_small_any(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hi
     return launch_small<16>(a, L, do_topk, st);
 }
 
-template <int EPL>
-void launch_topk_t(const float* src, int nparts, const RouteArgs& a, float* logits, hipStream_t st) {
-    hipLaunchKernelGGL((topk_kernel<EPL>), dim3((a.T + 3) / 4), dim3(256), 0, st, src, nparts,
-                       a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates);
+template <int EPL, int NP>
+void launch_topk_t(const float* src, const RouteArgs& a, float* logits, hipStream_t st) {
+    hipLaunchKernelGGL((topk_kernel<EPL, NP>), dim3((a.T + 3) / 4), dim3(256), 0, st, src, a.bias,
+                       logits, a.T, a.E, a.topk, a.ids, a.gates);
+}
+
+template <int NP>
+void launch_topk_np(const float* src, const RouteArgs& a, float* logits, hipStream_t st) {
+    const int epl = (a.E + 63) / 64;
+    if (epl <= 1) launch_topk_t<1, NP>(src, a, logits, st);
+    else if (epl <= 2) launch_topk_t<2, NP>(src, a, logits, st);
+    else if (epl <= 4) launch_topk_t<4, NP>(src, a, logits, st);
+    else if (epl <= 8) launch_topk_t<8, NP>(src, a, logits, st);
+    else launch_topk_t<16, NP>(src, a, logits, st);
 }
 
 void launch_topk(const float* src, int nparts, const RouteArgs& a, float* logits, hipStream_t st) {
-    const int epl = (a.E + 63) / 64;
-    if (epl <= 1) launch_topk_t<1>(src, nparts, a, logits, st);
-    else if (epl <= 2) launch_topk_t<2>(src, nparts, a, logits, st);
-    else if (epl <= 4) launch_topk_t<4>(src, nparts, a, logits, st);
-    else if (epl <= 8) launch_topk_t<8>(src, nparts, a, logits, st);
-    else launch_topk_t<16>(src, nparts, a, logits, st);
+    if (nparts == kRouterParts) launch_topk_np<kRouterParts>(src, a, logits, st);
+    else launch_topk_np<kRouterMfmaParts>(src, a, logits, st);
 }
 
 int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
@@ -416,7 +529,9 @@ int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, cc, cerr, L.nchunks, a.E,
                        a.counts, a.offsets, hdr, tiles);
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
-                       a.E, a.topk, a.offsets, cc, a.sorted_assign, a.pos);
+                       a.E, a.topk, a.offsets, cc, a.sorted_assign, a.pos,
+                       reinterpret_cast<int2*>(a.ws + L.row_info),
+                       reinterpret_cast<int2*>(a.ws + L.assign_info));
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -426,11 +541,11 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool router_uses_mfma(int T, int E) { return T > kRouterSmallT && E % 8 == 0; }
 
-MoeWorkspace moe_workspace_layout(int T, int E, int topk, int /*unused*/) {
+MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
     MoeWorkspace L;
     L.max_tiles = (int)(((int64_t)T * topk) / QL_MOE_TILE_ROWS) + E;
     L.nchunks = (T + kChunk - 1) / kChunk;
-    L.nparts = router_uses_mfma(T, E) ? router_mfma_parts() : kRouterParts;
+    L.nparts = router_uses_mfma(T, E) ? kRouterMfmaParts : kRouterParts;
     size_t off = 0;
     L.header = off;
     off += 16;
@@ -448,21 +563,31 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk, int /*unused*/) {
     off = align256(off);
     L.chunk_err = off;
     off += (size_t)L.nchunks * sizeof(int);
+    off = align256(off);
+    L.row_info = off;
+    off += (size_t)T * topk * 2 * sizeof(int);
+    off = align256(off);
+    L.assign_info = off;
+    off += (size_t)T * topk * 2 * sizeof(int);
     L.total = align256(off);
     return L;
 }
 
 
 int launch_route(const RouteArgs& a, hipStream_t st) {
-    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk, a.D);
+    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     float* logits = reinterpret_cast<float*>(a.ws + L.logits);
     float* partials = reinterpret_cast<float*>(a.ws + L.partials);
     if (router_uses_mfma(a.T, a.E)) {
         const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st);
         if (rc != QL_OK) return rc;
     } else {
-        hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
-                           a.Wr, partials, a.D, a.E);
+        if (a.E % 8 == 0)
+            hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st,
+                               a.H, a.Wr, partials, a.D, a.E);
+        else
+            hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
+                               a.Wr, partials, a.D, a.E);
         if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
         if (a.T <= kRouterSmallT) return launch_small_any(a, L, true, st);
     }
@@ -472,7 +597,7 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
 }
 
 int launch_dispatch(const RouteArgs& a, hipStream_t st) {
-    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk, 0);
+    const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     if (a.T <= kRouterSmallT) return launch_small_any(a, L, false, st);
     return launch_dispatch_large(a, L, st);
 }

@@ -127,3 +127,44 @@ def test_moe_prefill_4096(seed):
     torch.cuda.synchronize()
     rel, mx = _compare(*res, ref, 4096, 8)
     say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_moe_decode_graph_replays_match_eager():
+    """The decode chain captured in a HIP graph: every replay (with eager work
+    and synchronizations in between) reproduces the eager output bit for bit."""
+    import torch
+    w = synth.moe_weights(6)
+    dw = _dev_weights(w)
+    toks = [t(synth.moe_tokens(3000 + i, 1)["H"]) for i in range(3)]
+    route = ql.alloc_route_outputs(1, 256, 8, toks[0].device)
+    act = torch.empty((9, 512), dtype=torch.float16, device=toks[0].device)
+    outs = [torch.empty((1, 2048), dtype=torch.float16, device=toks[0].device) for _ in toks]
+
+    def step(i):
+        ql.moe_route(toks[i], dw["Wr"], None, 8, route)
+        ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], toks[i], 1, 8,
+                            ql.QL_OP_GATE_UP_SILU, route, act)
+        ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, 1, 8, ql.QL_OP_DOWN_COMBINE,
+                            route, outs[i])
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    eager = [host(o).copy() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            step(i)
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert np.array_equal(host(outs[i]).view(np.uint16), eager[i].view(np.uint16)), (rep, i)
+        # eager work between replays
+        ql.qlinear_gemv(dw["shared_down"], act[0].contiguous())
+        torch.cuda.synchronize()
+    ref = oracle.moe_layer(synth.moe_tokens(3000, 1)["H"], w, None, 8)
+    assert_close(eager[0].astype(np.float64), ref["out"], "decode out")

@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run a plain copy of known size (for HBM counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --only-primary --pmc-calibration` into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -312,6 +317,63 @@ def bench_moe_prefill(args, dev, w):
             "seed": seeds[0]}
 
 
+CALIB_BYTES = 256 * 1024 * 1024
+
+
+def pmc_calibration(dev):
+    """A plain elementwise copy (negation) of CALIB_BYTES of fp16: it reads
+    and writes exactly CALIB_BYTES, which calibrates FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    src = torch.randn(CALIB_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def ingest_pmc(fetch_csv, write_csv):
+    import csv
+    def per_kernel(path, counter):
+        out = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                out.setdefault(name, []).append(float(row["Counter_Value"]) * 1024.0)  # KiB
+        return out
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, pattern):
+        keys = [k for k in d if pattern in k]
+        if not keys:
+            raise SystemExit(f"no kernel matching {pattern!r} in the counter file")
+        return keys[0]
+    f_read = CALIB_BYTES / np.median(fetch[pick(fetch, "neg_kernel")])
+    f_write = CALIB_BYTES / np.median(write[pick(write, "neg_kernel")])
+    gk = pick(fetch, "gemv_w4_chunked_kernel<64, 1, 8>")
+    fr = np.asarray(fetch[gk]) * f_read
+    wr = np.asarray(write[pick(write, "gemv_w4_chunked_kernel<64, 1, 8>")]) * f_write
+    n = min(len(fr), len(wr))
+    per_launch = float(np.mean(fr[:n] + wr[:n]))
+    algo = (w4_bytes(2048, 8192) + 2 * 2048 + 2 * 8192 + w4_bytes(2048, 151552) + 2 * 2048 + 2 * 151552) / 2
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(path)) if os.path.exists(path) else {}
+    d[KERNEL_GEMV] = {
+        "source_sha": source_sha("gemv.hip", "ql_device.h"),
+        "bytes_per_launch": per_launch,
+        "algorithmic_bytes_per_launch": algo,
+        "ratio_to_algorithmic": per_launch / algo,
+        "fetch_scale": f_read, "write_scale": f_write,
+        "calibration": f"torch.neg on {CALIB_BYTES} bytes of fp16: expected reads = writes = {CALIB_BYTES}",
+        "dispatches": n,
+    }
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d[KERNEL_GEMV], indent=1))
+
+
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the headline workload:
     the N = 8192 matrix plus the first 16384 rows of the vocabulary head,
@@ -344,6 +406,9 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path; see DESIGN.md for how it would shard)",
@@ -366,6 +431,8 @@ def main():
         "roofline": g["roofline"],
         "per_matrix": g["per_matrix"],
     }
+    if args.pmc_calibration:
+        pmc_calibration(dev)
     if not args.only_primary:
         import synth
         log("bench: GEMM")

@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
+    ap.add_argument("--workload", choices=["all", "gemm", "moe_decode", "moe_prefill"], default="all",
+                    help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run a plain copy of known size (for HBM counter calibration)")
@@ -435,13 +437,18 @@ def main():
         pmc_calibration(dev)
     if not args.only_primary:
         import synth
-        log("bench: GEMM")
-        res.setdefault("workloads", {})["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
-        w = synth.moe_weights(0)
-        log("bench: MoE decode")
-        res["workloads"]["moe_decode_1tok"] = bench_moe_decode(args, dev, w)
-        log("bench: MoE prefill")
-        res["workloads"]["moe_prefill_4096tok"] = bench_moe_prefill(args, dev, w)
+        wl = res.setdefault("workloads", {})
+        if args.workload in ("all", "gemm"):
+            log("bench: GEMM")
+            wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
+        if args.workload in ("all", "moe_decode", "moe_prefill"):
+            w = synth.moe_weights(0)
+            if args.workload in ("all", "moe_decode"):
+                log("bench: MoE decode")
+                wl["moe_decode_1tok"] = bench_moe_decode(args, dev, w)
+            if args.workload in ("all", "moe_prefill"):
+                log("bench: MoE prefill")
+                wl["moe_prefill_4096tok"] = bench_moe_prefill(args, dev, w)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline()

@@ -65,22 +65,27 @@ struct KParams {
     int ksplit;  // router: number of K splits
 };
 
-template <int WM, int WN>
+// Workgroup of WGM x WGN waves; every wave owns (32*WM) x (32*WN) outputs.
+template <int WM, int WN, int WGM, int WGN>
 struct Tile {
-    static constexpr int BM = 64 * WM;
-    static constexpr int BN = 64 * WN;
-    static constexpr int A_LOADS = BM / 32;             // 16-byte A loads per thread per step
-    static constexpr int TPC = 256 / BN;                // threads per B column (1 or 2)
-    static constexpr int WPT = 8 / TPC;                 // code words per thread per step
-    static constexpr int LDS_A = BM * kLdk;             // fp16 per A buffer
-    static constexpr int LDS_B = BN * kLdk;             // fp16 per B buffer
+    static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
+    static constexpr int BM = 32 * WM * WGM;
+    static constexpr int BN = 32 * WN * WGN;
+    static constexpr int A_ROWS = NT / 8;                // A rows staged per 16-byte load round
+    static constexpr int A_LOADS = BM / A_ROWS;          // 16-byte A loads per thread per step
+    static constexpr int TPC = NT / BN;                  // threads per B column (1 or 2)
+    static constexpr int WPT = 8 / TPC;                  // code words per thread per step
+    static constexpr int LDS_A = BM * kLdk;              // fp16 per A buffer
+    static constexpr int LDS_B = BN * kLdk;              // fp16 per B buffer
     static constexpr size_t LDS_BYTES = (size_t)2 * (LDS_A + LDS_B) * 2;
+    static_assert(BM % A_ROWS == 0 && A_LOADS % 1 == 0, "A staging must tile the rows");
+    static_assert(NT % BN == 0 && (TPC == 1 || TPC == 2), "one or two threads per B column");
 };
 
-template <int WM, int WN, int MODE>
-__global__ void __launch_bounds__(256)
+template <int WM, int WN, int WGM, int WGN, int MODE>
+__global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_w4_kernel(const KParams p) {
-    using TL = Tile<WM, WN>;
+    using TL = Tile<WM, WN, WGM, WGN>;
     constexpr int BM = TL::BM, BN = TL::BN;
     extern __shared__ __align__(16) f16 lds[];
     f16* As = lds;                     // [2][BM][kLdk]
@@ -89,8 +94,9 @@ gemm_w4_kernel(const KParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm0 = (wave >> 1) * (32 * WM);  // wave row offset in the tile
-    const int wn0 = (wave & 1) * (32 * WN);   // wave column offset in the tile
+    const int wave_n = wave % WGN;
+    const int wm0 = (wave / WGN) * (32 * WM);  // wave row offset in the tile
+    const int wn0 = wave_n * (32 * WN);        // wave column offset in the tile
     const int K = p.K;
     const int G = K / kGroup;
     const int wpr = K / 8;
@@ -147,7 +153,7 @@ gemm_w4_kernel(const KParams p) {
     const int a_chunk = tid & 7;
 #pragma unroll
     for (int i = 0; i < TL::A_LOADS; ++i) {
-        const int lr = min(i * 32 + (tid >> 3), rows_valid - 1);
+        const int lr = min(i * TL::A_ROWS + (tid >> 3), rows_valid - 1);
         int64_t src;
         if constexpr (MODE == MODE_DENSE || MODE == MODE_ROUTER) {
             src = out_row0 + lr;
@@ -205,7 +211,7 @@ gemm_w4_kernel(const KParams p) {
         if constexpr (MODE == MODE_ROUTER) {
             // One 8 x 8 block per thread: k rows 8*kb .. 8*kb+7 of the step,
             // columns 8*nb .. 8*nb+7 of the tile.
-            static_assert(BN == 256, "router staging assumes 32 column blocks of 8");
+            static_assert(BN == 256 && TL::NT == 256, "router staging: one 8 x 8 block per thread");
             const int kb = tid & 7, nb = tid >> 3;
             const int col = min(n0 + 8 * nb, p.N - 8);
 #pragma unroll
@@ -219,19 +225,22 @@ gemm_w4_kernel(const KParams p) {
         }
     };
 
-    auto store_stage = [&](auto set, int buf) {
+    // Stage one quarter (piece p of 4) of a step: A chunks and dequantized B
+    // words from register set S into LDS buffer `buf`.
+    auto store_piece = [&](auto set, int buf, auto piece) {
         constexpr int S = decltype(set)::value;
+        constexpr int P = decltype(piece)::value;
         f16* a_dst = As + buf * TL::LDS_A;
 #pragma unroll
-        for (int i = 0; i < TL::A_LOADS; ++i)
-            *reinterpret_cast<u32x4*>(a_dst + (i * 32 + (tid >> 3)) * kLdk + a_chunk * 8) = areg[S][i];
+        for (int i = P * TL::A_LOADS / 4; i < (P + 1) * TL::A_LOADS / 4; ++i)
+            *reinterpret_cast<u32x4*>(a_dst + (i * TL::A_ROWS + (tid >> 3)) * kLdk + a_chunk * 8) = areg[S][i];
         f16* b_dst = Bs + buf * TL::LDS_B;
         if constexpr (MODE == MODE_ROUTER) {
             // Transpose the 8 x 8 block in registers: output row j (column
             // 8*nb + j) pairs element j of k rows (2i, 2i+1).
             const int kb = tid & 7, nb = tid >> 3;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 2 * P; j < 2 * P + 2; ++j) {
                 const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
                 u32x4 o;
                 o.x = __builtin_amdgcn_perm(hreg[S][1][j >> 1], hreg[S][0][j >> 1], sel);
@@ -245,54 +254,60 @@ gemm_w4_kernel(const KParams p) {
             const f16 bv = __builtin_bit_cast(f16, bireg[S]);
             const f16x2 s2 = {sv, sv};
             const f16x2 b2 = {bv, bv};
+            constexpr int W = TL::WPT;  // words of this thread's column per step
 #pragma unroll
-            for (int i = 0; i < BREG; ++i) {
-                const uint32_t wv[4] = {breg[S][i].x, breg[S][i].y, breg[S][i].z, breg[S][i].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int word = bpart * TL::WPT + 4 * i + q;  // 0..7 within the group
-                    *reinterpret_cast<f16x8*>(b_dst + bc * kLdk + word * 8) = dequant_word(wv[q], s2, b2);
-                }
+            for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
+                const uint32_t u = breg[S][w >> 2][w & 3];
+                const int word = bpart * W + w;  // 0..7 within the group
+                *reinterpret_cast<f16x8*>(b_dst + bc * kLdk + word * 8) = dequant_word(u, s2, b2);
             }
         }
     };
 
     const int fl = lane & 31;   // row (A) / column (B) inside a 32-wide subtile
     const int fh = lane >> 5;   // which half of the 16-wide K slice
-    auto compute = [&](int buf) {
-        const f16* a_src = As + buf * TL::LDS_A + (wm0 + fl) * kLdk;
-        const f16* b_src = Bs + buf * TL::LDS_B + (wn0 + fl) * kLdk;
+    auto read_frags = [&](int buf, int s, f16x8 (&af)[WM], f16x8 (&bf)[WN]) {
+        const f16* a_src = As + buf * TL::LDS_A + (wm0 + fl) * kLdk + (4 * fh + s) * 8;
+        const f16* b_src = Bs + buf * TL::LDS_B + (wn0 + fl) * kLdk + (4 * fh + s) * 8;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int koff = (4 * fh + s) * 8;
-            f16x8 af[WM], bf[WN];
+        for (int i = 0; i < WM; ++i) af[i] = *reinterpret_cast<const f16x8*>(a_src + i * 32 * kLdk);
 #pragma unroll
-            for (int i = 0; i < WM; ++i) af[i] = *reinterpret_cast<const f16x8*>(a_src + i * 32 * kLdk + koff);
+        for (int j = 0; j < WN; ++j) bf[j] = *reinterpret_cast<const f16x8*>(b_src + j * 32 * kLdk);
+    };
+    auto mfmas = [&](const f16x8 (&af)[WM], const f16x8 (&bf)[WN]) {
 #pragma unroll
-            for (int j = 0; j < WN; ++j) bf[j] = *reinterpret_cast<const f16x8*>(b_src + j * 32 * kLdk + koff);
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-            for (int i = 0; i < WM; ++i)
-#pragma unroll
-                for (int j = 0; j < WN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+            for (int j = 0; j < WN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     };
 
-    // Interleave the staging work of the next step with this step's MFMAs:
-    // per 16-wide K slice, the fragment reads, then each MFMA followed by a
-    // few VALU (dequantization) instructions, then the LDS stores.
-    auto interleave = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x020, TL::A_LOADS + BREG + 2 + HREG, 0);  // VMEM reads
+    // One 16-wide K slice of step data in LDS buffer S: its MFMAs, a quarter
+    // of the next step's staging (program order keeps the LDS stores after
+    // this slice's fragment reads), then the next slice's fragment reads.
+    // The group barriers interleave the staging VALU work between the MFMAs.
+    constexpr int NM = WM * WN;
+    // Staging VALU per slice: WPT/4 dequantized words of about 20 instructions.
+    constexpr int kValuPerMfma = (TL::WPT * 5 + NM / 2 - 1) / (NM / 2) + 1;
+    auto slice = [&](auto set, auto sl, f16x8 (&af)[WM], f16x8 (&bf)[WN], f16x8 (&an)[WM],
+                     f16x8 (&bn)[WN]) {
+        constexpr int S = decltype(set)::value;
+        constexpr int SL = decltype(sl)::value;
+        mfmas(af, bf);
+        store_piece(std::integral_constant<int, S ^ 1>{}, S ^ 1, sl);
+        if constexpr (SL < 3) read_frags(S, SL + 1, an, bn);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            __builtin_amdgcn_sched_group_barrier(0x100, WM + WN, 0);  // DS reads
-#pragma unroll
-            for (int m = 0; m < WM * WN; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-            }
-            __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);  // DS writes
+        for (int m = 0; m < NM / 2; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU (dequantization)
         }
+        __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);      // DS writes (staging)
+#pragma unroll
+        for (int m = 0; m < NM / 2; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next slice)
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // The loop body for the step `i` (relative to kbeg) whose data sits in
@@ -301,10 +316,20 @@ gemm_w4_kernel(const KParams p) {
     auto body = [&](auto set, int i) {
         constexpr int S = decltype(set)::value;
         load_stage(set, min(kbeg + i + 2, kend - 1));
-        compute(S);
-        store_stage(std::integral_constant<int, S ^ 1>{}, S ^ 1);
-        interleave();
+        f16x8 a0[WM], b0[WN], a1[WM], b1[WN];
+        read_frags(S, 0, a0, b0);
+        slice(set, std::integral_constant<int, 0>{}, a0, b0, a1, b1);
+        slice(set, std::integral_constant<int, 1>{}, a1, b1, a0, b0);
+        slice(set, std::integral_constant<int, 2>{}, a0, b0, a1, b1);
+        slice(set, std::integral_constant<int, 3>{}, a1, b1, a0, b0);
         __syncthreads();
+    };
+
+    auto store_stage = [&](auto set, int buf) {
+        store_piece(set, buf, std::integral_constant<int, 0>{});
+        store_piece(set, buf, std::integral_constant<int, 1>{});
+        store_piece(set, buf, std::integral_constant<int, 2>{});
+        store_piece(set, buf, std::integral_constant<int, 3>{});
     };
 
     const std::integral_constant<int, 0> set0{};
@@ -336,7 +361,7 @@ gemm_w4_kernel(const KParams p) {
                 const int half = p.N / 2;
 #pragma unroll
                 for (int j = 0; j < WN / 2; ++j) {
-                    const int col = n0 + (wave & 1) * (16 * WN) + 32 * j + fl;
+                    const int col = n0 + wave_n * (16 * WN) + 32 * j + fl;
                     if (col < half) {
                         const float g = acc[i][j][r];
                         const float u = acc[i][j + WN / 2][r];
@@ -360,18 +385,19 @@ gemm_w4_kernel(const KParams p) {
     }
 }
 
-template <int WM, int WN, int MODE>
+template <int WM, int WN, int WGM, int WGN, int MODE>
 int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
-    using TL = Tile<WM, WN>;
+    using TL = Tile<WM, WN, WGM, WGN>;
     static bool attr_done = false;  // benign race: the attribute is idempotent
     if (!attr_done) {
-        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, MODE>,
+        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)TL::LDS_BYTES) != hipSuccess)
             return QL_ERR_HIP;
         attr_done = true;
     }
-    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, MODE>), grid, dim3(256), TL::LDS_BYTES, st, p);
+    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE>), grid, dim3(TL::NT), TL::LDS_BYTES, st,
+                       p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -388,13 +414,14 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     p.K = a.K;
     p.N = a.N;
     if (a.M >= 2048) {
-        using TL = Tile<4, 4>;
+        // 256 x 256 tiles, 8 waves (two per SIMD) of 128 x 64.
+        using TL = Tile<4, 2, 2, 4>;
         dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
-        return launch_t<4, 4, MODE_DENSE>(p, grid, st);
+        return launch_t<4, 2, 2, 4, MODE_DENSE>(p, grid, st);
     }
-    using TL = Tile<2, 4>;
+    using TL = Tile<2, 4, 2, 2>;
     dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
-    return launch_t<2, 4, MODE_DENSE>(p, grid, st);
+    return launch_t<2, 4, 2, 2, MODE_DENSE>(p, grid, st);
 }
 
 constexpr int kRouterSplit = kRouterMfmaSplit;
@@ -409,9 +436,9 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
     p.K = D;
     p.N = E;
     p.ksplit = kRouterSplit;
-    using TL = Tile<1, 4>;
+    using TL = Tile<1, 4, 2, 2>;
     dim3 grid((T + TL::BM - 1) / TL::BM, (E + TL::BN - 1) / TL::BN, kRouterSplit);
-    return launch_t<1, 4, MODE_ROUTER>(p, grid, st);
+    return launch_t<1, 4, 2, 2, MODE_ROUTER>(p, grid, st);
 }
 
 
@@ -435,16 +462,16 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     p.Y = a.Y;
     p.K = a.K;
     p.N = a.N;
-    using TL = Tile<2, 4>;
+    using TL = Tile<2, 4, 2, 2>;
     static_assert(TL::BM == QL_MOE_TILE_ROWS, "grouped tile height must match the tile map");
     const int shared_tiles = a.sqw ? (a.T + TL::BM - 1) / TL::BM : 0;
     const unsigned slots = (unsigned)(L.max_tiles + shared_tiles);
     if (a.op == QL_OP_GATE_UP_SILU) {
         dim3 grid(slots, (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2));
-        return launch_t<2, 4, MODE_GATEUP>(p, grid, st);
+        return launch_t<2, 4, 2, 2, MODE_GATEUP>(p, grid, st);
     }
     dim3 grid(slots, (a.N + TL::BN - 1) / TL::BN);
-    return launch_t<2, 4, MODE_DOWN>(p, grid, st);
+    return launch_t<2, 4, 2, 2, MODE_DOWN>(p, grid, st);
 }
 
 }  // namespace ql

@@ -462,16 +462,17 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     p.Y = a.Y;
     p.K = a.K;
     p.N = a.N;
-    using TL = Tile<2, 4, 2, 2>;
+    // 128 x 256 tiles, 8 waves (two per SIMD) of 64 x 64.
+    using TL = Tile<2, 2, 2, 4>;
     static_assert(TL::BM == QL_MOE_TILE_ROWS, "grouped tile height must match the tile map");
     const int shared_tiles = a.sqw ? (a.T + TL::BM - 1) / TL::BM : 0;
     const unsigned slots = (unsigned)(L.max_tiles + shared_tiles);
     if (a.op == QL_OP_GATE_UP_SILU) {
         dim3 grid(slots, (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2));
-        return launch_t<2, 4, 2, 2, MODE_GATEUP>(p, grid, st);
+        return launch_t<2, 2, 2, 4, MODE_GATEUP>(p, grid, st);
     }
     dim3 grid(slots, (a.N + TL::BN - 1) / TL::BN);
-    return launch_t<2, 4, 2, 2, MODE_DOWN>(p, grid, st);
+    return launch_t<2, 2, 2, 4, MODE_DOWN>(p, grid, st);
 }
 
 }  // namespace ql

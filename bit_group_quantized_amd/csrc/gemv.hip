@@ -19,6 +19,8 @@
 // v_dot2_f32_f16, and kept in registers for every row the lane visits.
 // The bias term uses sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * sum_k x_k
 // with the per-group activation sum computed once.
+#include <type_traits>
+
 #include "ql_device.h"
 #include "ql_internal.h"
 
@@ -554,14 +556,30 @@ int launch_chunked_t(const GemvArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
+// Rows per team of the chunked GEMV: 8 rows in flight per wave for large N;
+// fewer for small N so that the grid still spreads over every CU.
+#ifndef QL_GEMV_ROWS
+#define QL_GEMV_ROWS 8
+#endif
+constexpr int kGemvRows = QL_GEMV_ROWS;
+constexpr int kGemvMinBlocks = 1024;
+
+template <int TPR, int V>
+int launch_chunked_r(const GemvArgs& a, hipStream_t st) {
+    constexpr int R = (kGemvRows < TPR) ? kGemvRows : TPR;
+    const long blocks_big = (a.N + 4L * (64 / TPR) * R - 1) / (4L * (64 / TPR) * R);
+    if (blocks_big >= kGemvMinBlocks || R <= 2) return launch_chunked_t<TPR, V, R>(a, st);
+    return launch_chunked_t<TPR, V, 2>(a, st);
+}
+
 int launch_gemv(const GemvArgs& a, hipStream_t st) {
     // Chunked kernel: K/32 chunks per row spread over TPR lanes, V per lane.
     switch (a.K) {
-        case 256: return launch_chunked_t<8, 1, 8>(a, st);
-        case 512: return launch_chunked_t<16, 1, 8>(a, st);
-        case 1024: return launch_chunked_t<32, 1, 8>(a, st);
-        case 2048: return launch_chunked_t<64, 1, 8>(a, st);
-        case 4096: return launch_chunked_t<64, 2, 8>(a, st);
+        case 256: return launch_chunked_r<8, 1>(a, st);
+        case 512: return launch_chunked_r<16, 1>(a, st);
+        case 1024: return launch_chunked_r<32, 1>(a, st);
+        case 2048: return launch_chunked_r<64, 1>(a, st);
+        case 4096: return launch_chunked_r<64, 2>(a, st);
         case 8192: return launch_chunked_t<64, 4, 4>(a, st);
         case 16384: return launch_chunked_t<64, 8, 2>(a, st);
         default: break;

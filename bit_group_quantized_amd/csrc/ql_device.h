@@ -128,9 +128,17 @@ __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Non-temporal streaming load for weights that are read exactly once.
+// Streaming load for weights that are read exactly once (non-temporal hint
+// unless QL_STREAM_NT is 0).
+#ifndef QL_STREAM_NT
+#define QL_STREAM_NT 1
+#endif
 __device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
+#if QL_STREAM_NT
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 
 __device__ __forceinline__ float silu(float z) {

@@ -53,14 +53,19 @@ __device__ __forceinline__ uint32_t and_or(uint32_t u, uint32_t mask, uint32_t m
 
 // Dequantize one word (codes k = 8w .. 8w+7 of one output) to 8 fp16 values
 // in natural k order: out[j] = fp16(s*q_j + b), a single rounding (fma).
+// Exact code pairs come from the 0x6400 exponent trick: (u & 0x000F000F) |
+// magic = (1024 + q0, 1024 + q4), minus 1024; (u & 0x00F000F0) | magic =
+// (1024 + 16 q1, 1024 + 16 q5), times 1/16 minus 64 (exact: 64 + q1 - 64).
 __device__ __forceinline__ f16x8 dequant_word(uint32_t u, f16x2 s2, f16x2 b2) {
     const f16x2 off = {(f16)-1024.0f, (f16)-1024.0f};
-    // (q0, q4), (q1, q5), (q2, q6), (q3, q7) as exact fp16 integers.
+    const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+    const f16x2 off64 = {(f16)-64.0f, (f16)-64.0f};
     const uint32_t magic = kMagic2;
-    f16x2 p0 = as_f16x2(and_or(u, 0x000F000Fu, magic)) + off;
-    f16x2 p1 = as_f16x2(and_or(u >> 4, 0x000F000Fu, magic)) + off;
-    f16x2 p2 = as_f16x2(and_or(u >> 8, 0x000F000Fu, magic)) + off;
-    f16x2 p3 = as_f16x2(and_or(u >> 12, 0x000F000Fu, magic)) + off;
+    const uint32_t t = u >> 8;
+    f16x2 p0 = as_f16x2(and_or(u, 0x000F000Fu, magic)) + off;                 // (q0, q4)
+    f16x2 p1 = __builtin_elementwise_fma(as_f16x2(and_or(u, 0x00F000F0u, magic)), sixteenth, off64);  // (q1, q5)
+    f16x2 p2 = as_f16x2(and_or(t, 0x000F000Fu, magic)) + off;                 // (q2, q6)
+    f16x2 p3 = __builtin_elementwise_fma(as_f16x2(and_or(t, 0x00F000F0u, magic)), sixteenth, off64);  // (q3, q7)
     uint32_t w0 = as_u32(__builtin_elementwise_fma(p0, s2, b2));  // (w0, w4)
     uint32_t w1 = as_u32(__builtin_elementwise_fma(p1, s2, b2));  // (w1, w5)
     uint32_t w2 = as_u32(__builtin_elementwise_fma(p2, s2, b2));  // (w2, w6)

@@ -33,6 +33,9 @@ METRIC = "w4 GEMV eff. HBM GB/s; w4 GEMM/MoE TFLOP/s; both as % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 600e6  # > 2 x 256 MB Infinity Cache
+# Untimed settling run before each compute-bound measurement: the clocks drop
+# to a sustained level under MFMA load within a fraction of a second.
+SETTLE_S = 0.5
 KERNEL_GEMV = "gemv_w4_chunked_kernel<64,1,8>"  # the K = 2048 vocabulary-head launch
 
 
@@ -64,14 +67,21 @@ def log(*a):
 # ----------------------------------------------------------------------------
 # timing helpers (events on torch's current stream, which the library uses)
 # ----------------------------------------------------------------------------
-def timed_steps(step_fn, steps, warmup):
-    """Run `warmup` untimed steps, then time exactly `steps` steps between two
+def timed_steps(step_fn, steps, warmup, settle_s=0.0):
+    """Run `warmup` untimed steps (and, with settle_s, keep running untimed
+    steps for that many seconds so that the clocks reach their sustained
+    level under this load), then time exactly `steps` steps between two
     events on torch's current stream (the stream the library launches on),
     with a synchronize on both sides.  Returns ms per step."""
     import torch
     for i in range(warmup):
         step_fn(i)
     torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < settle_s:
+        for i in range(8):
+            step_fn(i)
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -82,12 +92,12 @@ def timed_steps(step_fn, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
-def stage_times(stage_fns, steps, warmup):
+def stage_times(stage_fns, steps, warmup, settle_s=0.0):
     """Per-stage time: each stage alone, `steps` back-to-back launches between
     two events (inputs of later stages are left from a full warm-up pass)."""
     out = []
     for fn in stage_fns:
-        out.append(timed_steps(fn, steps, warmup))
+        out.append(timed_steps(fn, steps, warmup, settle_s))
     return out
 
 
@@ -216,7 +226,7 @@ def bench_gemm(args, dev):
             ql.qlinear_gemm(W, Xs[i % len(Xs)], Y)
 
         steps = 20 if M <= 4096 else 8
-        ms = timed_steps(step, steps, 3)
+        ms = timed_steps(step, steps, 3, settle_s=SETTLE_S)
         flops = 2.0 * M * N * K
         tf = flops / (ms * 1e-3) / 1e12
         out[f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf, "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
@@ -310,8 +320,8 @@ def bench_moe_prefill(args, dev, w):
         dn(i)
         cb(i)
 
-    ms = timed_steps(step, 20, 3)
-    k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2))
+    ms = timed_steps(step, 20, 3, settle_s=SETTLE_S)
+    k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2, settle_s=SETTLE_S / 4))
     routed_rows = T * 8
     flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
              + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)
@@ -340,13 +350,15 @@ def pmc_calibration(dev):
 def ingest_pmc(fetch_csv, write_csv):
     import csv
     def per_kernel(path, counter):
+        # Per kernel name: (grid size, bytes) of every dispatch, in dispatch order.
         out = {}
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row.get("Counter_Name") != counter:
                     continue
                 name = row.get("Kernel_Name", "")
-                out.setdefault(name, []).append(float(row["Counter_Value"]) * 1024.0)  # KiB
+                out.setdefault(name, []).append((int(row["Grid_Size"]),
+                                                 float(row["Counter_Value"]) * 1024.0))  # KiB
         return out
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
@@ -356,11 +368,15 @@ def ingest_pmc(fetch_csv, write_csv):
         if not keys:
             raise SystemExit(f"no kernel matching {pattern!r} in the counter file")
         return keys[0]
-    f_read = CALIB_BYTES / np.median(fetch[pick(fetch, "neg_kernel")])
-    f_write = CALIB_BYTES / np.median(write[pick(write, "neg_kernel")])
-    gk = pick(fetch, "gemv_w4_chunked_kernel<64, 1, 8>")
-    fr = np.asarray(fetch[gk]) * f_read
-    wr = np.asarray(write[pick(write, "gemv_w4_chunked_kernel<64, 1, 8>")]) * f_write
+    def values(rows, largest_grid=False):
+        # The N = 8192 matrix runs the same kernel instantiation with a smaller
+        # grid; the vocabulary head is the dispatch with the largest grid.
+        g = max(r[0] for r in rows)
+        return np.asarray([v for gs, v in rows if gs == g or not largest_grid])
+    f_read = CALIB_BYTES / np.median(values(fetch[pick(fetch, "neg_kernel")]))
+    f_write = CALIB_BYTES / np.median(values(write[pick(write, "neg_kernel")]))
+    fr = values(fetch[pick(fetch, "gemv_w4_chunked_kernel<64, 1, 8>")], largest_grid=True) * f_read
+    wr = values(write[pick(write, "gemv_w4_chunked_kernel<64, 1, 8>")], largest_grid=True) * f_write
     n = min(len(fr), len(wr))
     per_launch = float(np.mean(fr[:n] + wr[:n]))
     algo = w4_bytes(2048, 151552) + 2 * 2048 + 2 * 151552

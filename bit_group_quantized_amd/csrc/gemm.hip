@@ -10,22 +10,31 @@
 // 使瓦片大小与专家负载相匹配: each expert's rows are cut into fixed-height tiles
 // and every tile is one workgroup.
 //
-// gfx950 mapping.  A workgroup of 4 waves (2 x 2) owns a BM x BN output tile;
-// each wave owns (32*WM) x (32*WN) and issues v_mfma_f32_32x32x16_f16 on it.
-// One K step is 64 = one quantization group.  Per step the workgroup stages
-// the activation tile (BM x 64 fp16) and the dequantized weight tile
-// (BN x 64 fp16, produced from BN x 32 bytes of codes plus one scale and
-// bias per column) into LDS; both are double buffered, so the global loads
-// of step s+1 overlap the MFMAs of step s with one barrier per step.  Rows
-// in LDS are padded to 72 halves (144 bytes) so that both the 128-bit
-// staging writes and the 128-bit fragment reads are free of bank conflicts.
+// gfx950 mapping.  A workgroup of WGM x WGN waves owns a BM x BN output
+// tile; each wave owns (32*WM) x (32*WN) and issues v_mfma_f32_32x32x16_f16
+// on it.  Dense prefill with M >= 2048 uses 8 waves (two per SIMD) of
+// 128 x 64 on 256 x 256 tiles; the grouped expert GEMMs use 8 waves of
+// 64 x 64 on 128-row tiles.  One K step is 64 = one quantization group.
+// Per step the workgroup stages the activation tile (BM x 64 fp16) and the
+// dequantized weight tile (BN x 64 fp16, produced from BN x 32 bytes of
+// codes plus one scale and bias per column) into LDS; both are double
+// buffered, and the global loads run two steps ahead, so one barrier per
+// step suffices.  LDS rows are padded to 72 halves (144 bytes), which keeps
+// the 128-bit staging writes and fragment reads free of bank conflicts.
 //
 // MFMA operand order: for one 16-wide K slice, lane l supplies row l % 32 of
 // A and column l % 32 of B, each as 8 fp16 values; element v of half h = l/32
 // is paired across A and B.  Any bijection between (h, v) and the 16 k of
 // the slice therefore gives the same dot product.  Slice s of a K step uses
 // k = 32h + 8s + v, so a lane's 8 values are one contiguous 16-byte chunk of
-// an LDS row and one packed word of codes.
+// an LDS row and one packed word of codes.  The weight fragment is the first
+// MFMA operand, so the accumulators hold the tile transposed and a lane owns
+// runs of 4 consecutive output columns; the epilogue bounces each wave's
+// tile through LDS and writes whole 128-byte row segments.
+//
+// Tiles are dealt to the chip's 8 XCDs (each with its own L2) in contiguous
+// runs, so tiles that share activation rows or an expert's weights run on
+// the same XCD at about the same time.
 #include <type_traits>
 
 #include "ql_device.h"
@@ -63,7 +72,20 @@ struct KParams {
     float* Yf;
     int K, N;
     int ksplit;  // router: number of K splits
+    int grid_n, grid_m;  // dense: tile grid; grouped: N blocks (grid_n), shared tiles (grid_m)
 };
+
+// Work item of a workgroup when the grid is launched one-dimensional: the
+// hardware deals workgroups to the 8 XCDs in turn (workgroup w to XCD w % 8),
+// so item = (w % 8) * per + w / 8 gives every XCD one contiguous run of
+// items.  Returns -1 for workgroups past the end.
+__device__ __forceinline__ int xcd_item(int total) {
+    const int per = (total + 7) >> 3;
+    const int lin = blockIdx.x;
+    const int idx = lin >> 3;
+    const int item = (lin & 7) * per + idx;
+    return (idx < per && item < total) ? item : -1;
+}
 
 // Workgroup of WGM x WGN waves; every wave owns (32*WM) x (32*WN) outputs.
 template <int WM, int WN, int WGM, int WGN>
@@ -112,8 +134,17 @@ gemm_w4_kernel(const KParams p) {
     int tile_kind = 0;       // grouped: 0 routed, 1 shared
     int tile_first = 0;      // grouped: first row (routed r or shared token)
     if constexpr (MODE == MODE_DENSE) {
-        n0 = blockIdx.x * BN;
-        out_row0 = blockIdx.y * BM;
+        const int item = xcd_item(p.grid_n * p.grid_m);
+        if (item < 0) return;
+        // Inside an XCD's run, groups of 4 row blocks sweep the column blocks
+        // together, so concurrent tiles share both activation rows and weights.
+        constexpr int GM = 4;
+        const int in_group = GM * p.grid_n;
+        const int first_m = (item / in_group) * GM;
+        const int gm = min(p.grid_m - first_m, GM);
+        const int r = item % in_group;
+        n0 = (r / gm) * BN;
+        out_row0 = (first_m + r % gm) * BM;
         rows_valid = (int)min<int64_t>(BM, p.M - out_row0);
     } else if constexpr (MODE == MODE_ROUTER) {
         n0 = blockIdx.y * BN;
@@ -123,7 +154,14 @@ gemm_w4_kernel(const KParams p) {
         kbeg = blockIdx.z * per;
         kend = min(G, kbeg + per);
     } else {
-        const int slot = blockIdx.x;
+        // Items are (tile, column block) over the tiles that exist: routed
+        // tiles first, then the shared expert's.
+        const int nt = min(max(p.ws_header[0], 0), p.max_tiles);
+        const int item = xcd_item((nt + p.grid_m) * p.grid_n);
+        if (item < 0) return;
+        const int tslot = item / p.grid_n;
+        const int nblk = item % p.grid_n;
+        const int slot = (tslot < nt) ? tslot : p.max_tiles + (tslot - nt);
         if (slot < p.max_tiles) {
             if (slot >= p.ws_header[0]) return;  // fewer routed tiles than slots
             const int* tp = p.tiles + (size_t)slot * 4;
@@ -145,7 +183,7 @@ gemm_w4_kernel(const KParams p) {
             ws = p.ssc;
             wb = p.sbi;
         }
-        n0 = blockIdx.y * ((MODE == MODE_GATEUP) ? BN / 2 : BN);
+        n0 = nblk * ((MODE == MODE_GATEUP) ? BN / 2 : BN);
     }
 
     // ---- A row sources (one per 32-row slab this thread stages) -------------
@@ -266,62 +304,54 @@ gemm_w4_kernel(const KParams p) {
 
     const int fl = lane & 31;   // row (A) / column (B) inside a 32-wide subtile
     const int fh = lane >> 5;   // which half of the 16-wide K slice
-    auto read_frags = [&](int buf, int s, f16x8 (&af)[WM], f16x8 (&bf)[WN]) {
+    // NA (compile time) = how many of the wave's WM row subtiles hold real
+    // rows; the others are padding and get neither fragment reads nor MFMAs.
+    auto read_frags = [&](auto na, int buf, int s, f16x8 (&af)[WM], f16x8 (&bf)[WN]) {
+        constexpr int NA = decltype(na)::value;
         const f16* a_src = As + buf * TL::LDS_A + (wm0 + fl) * kLdk + (4 * fh + s) * 8;
         const f16* b_src = Bs + buf * TL::LDS_B + (wn0 + fl) * kLdk + (4 * fh + s) * 8;
 #pragma unroll
-        for (int i = 0; i < WM; ++i) af[i] = *reinterpret_cast<const f16x8*>(a_src + i * 32 * kLdk);
+        for (int i = 0; i < NA; ++i) af[i] = *reinterpret_cast<const f16x8*>(a_src + i * 32 * kLdk);
+        if constexpr (NA > 0) {
 #pragma unroll
-        for (int j = 0; j < WN; ++j) bf[j] = *reinterpret_cast<const f16x8*>(b_src + j * 32 * kLdk);
+            for (int j = 0; j < WN; ++j) bf[j] = *reinterpret_cast<const f16x8*>(b_src + j * 32 * kLdk);
+        }
     };
-    auto mfmas = [&](const f16x8 (&af)[WM], const f16x8 (&bf)[WN]) {
+    auto mfmas = [&](auto na, const f16x8 (&af)[WM], const f16x8 (&bf)[WN]) {
+        constexpr int NA = decltype(na)::value;
 #pragma unroll
-        for (int i = 0; i < WM; ++i)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
     };
 
     // One 16-wide K slice of step data in LDS buffer S: its MFMAs, a quarter
     // of the next step's staging (program order keeps the LDS stores after
     // this slice's fragment reads), then the next slice's fragment reads.
-    // The group barriers interleave the staging VALU work between the MFMAs.
-    constexpr int NM = WM * WN;
-    // Staging VALU per slice: WPT/4 dequantized words of about 20 instructions.
-    constexpr int kValuPerMfma = (TL::WPT * 5 + NM / 2 - 1) / (NM / 2) + 1;
-    auto slice = [&](auto set, auto sl, f16x8 (&af)[WM], f16x8 (&bf)[WN], f16x8 (&an)[WM],
+    // The compiler interleaves them; fixed interleaving hints measured slower.
+    auto slice = [&](auto set, auto sl, auto na, f16x8 (&af)[WM], f16x8 (&bf)[WN], f16x8 (&an)[WM],
                      f16x8 (&bn)[WN]) {
         constexpr int S = decltype(set)::value;
         constexpr int SL = decltype(sl)::value;
-        mfmas(af, bf);
+        mfmas(na, af, bf);
         store_piece(std::integral_constant<int, S ^ 1>{}, S ^ 1, sl);
-        if constexpr (SL < 3) read_frags(S, SL + 1, an, bn);
-#pragma unroll
-        for (int m = 0; m < NM / 2; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU (dequantization)
-        }
-        __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);      // DS writes (staging)
-#pragma unroll
-        for (int m = 0; m < NM / 2; ++m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next slice)
-        }
+        if constexpr (SL < 3) read_frags(na, S, SL + 1, an, bn);
         __builtin_amdgcn_sched_barrier(0);
     };
 
     // The loop body for the step `i` (relative to kbeg) whose data sits in
     // LDS buffer S = i & 1.  Loads and stores past the last step are clamped
     // to the last step (harmless repeats) so that the body has no branches.
-    auto body = [&](auto set, int i) {
+    auto body = [&](auto set, auto na, int i) {
         constexpr int S = decltype(set)::value;
         load_stage(set, min(kbeg + i + 2, kend - 1));
         f16x8 a0[WM], b0[WN], a1[WM], b1[WN];
-        read_frags(S, 0, a0, b0);
-        slice(set, std::integral_constant<int, 0>{}, a0, b0, a1, b1);
-        slice(set, std::integral_constant<int, 1>{}, a1, b1, a0, b0);
-        slice(set, std::integral_constant<int, 2>{}, a0, b0, a1, b1);
-        slice(set, std::integral_constant<int, 3>{}, a1, b1, a0, b0);
+        read_frags(na, S, 0, a0, b0);
+        slice(set, std::integral_constant<int, 0>{}, na, a0, b0, a1, b1);
+        slice(set, std::integral_constant<int, 1>{}, na, a1, b1, a0, b0);
+        slice(set, std::integral_constant<int, 2>{}, na, a0, b0, a1, b1);
+        slice(set, std::integral_constant<int, 3>{}, na, a1, b1, a0, b0);
         __syncthreads();
     };
 
@@ -341,46 +371,118 @@ gemm_w4_kernel(const KParams p) {
         load_stage(set1, min(kbeg + 1, kend - 1));
     }
     __syncthreads();
-    int i = 0;
-    for (; i + 1 < nk; i += 2) {
-        body(set0, i);
-        body(set1, i + 1);
+    auto main_loop = [&](auto na) {
+        int i = 0;
+        for (; i + 1 < nk; i += 2) {
+            body(set0, na, i);
+            body(set1, na, i + 1);
+        }
+        if (i < nk) body(set0, na, i);
+    };
+    if constexpr (MODE == MODE_GATEUP || MODE == MODE_DOWN) {
+        // Routed tiles end in padding rows; every wave still stages its share
+        // (the barriers are reached by all), but skips subtiles past the end.
+        static_assert(WM == 2, "row-subtile dispatch written for two subtiles per wave");
+        const int na = __builtin_amdgcn_readfirstlane(min(max((rows_valid - wm0 + 31) / 32, 0), WM));
+        if (na >= 2) main_loop(std::integral_constant<int, 2>{});
+        else if (na == 1) main_loop(std::integral_constant<int, 1>{});
+        else main_loop(std::integral_constant<int, 0>{});
+    } else {
+        main_loop(std::integral_constant<int, WM>{});
     }
-    if (i < nk) body(set0, i);
 
     // ---- epilogue -------------------------------------------------------------
-    // acc[i][j][r]: row 32i + 8(r/4) + 4h + r%4, column 32j + l%32 of the wave tile.
+    // The MFMAs take the weight fragment as their first operand, so each
+    // accumulator holds the transposed product: acc[i][j][r] is output row
+    // 32i + l%32 of the wave tile and column 32j + 8(r/4) + 4h + r%4.  A lane
+    // thus owns runs of 4 consecutive columns of one row.
+    const int out_cols = (MODE == MODE_GATEUP) ? p.N / 2 : p.N;
+    // Output columns of one wave per row subtile.
+    constexpr int WC = (MODE == MODE_GATEUP) ? 16 * WN : 32 * WN;
+    auto out_vals = [&](int i, int j, int g, float (&v)[4]) {
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (MODE == MODE_GATEUP)
+                v[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + WN / 2][4 * g + e];
+            else
+                v[e] = acc[i][j][4 * g + e];
+        }
+    };
+    const int wcol0 = (MODE == MODE_GATEUP) ? n0 + wave_n * (16 * WN) : n0 + wn0;
+    if constexpr (MODE == MODE_ROUTER) {
+        // fp32 partials: four consecutive experts are one 16-byte store
+        // (E % 8 == 0 on this path).
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lrow = wm0 + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
+        for (int i = 0; i < WM; ++i) {
+            const int lrow = wm0 + 32 * i + fl;
             if (lrow >= rows_valid) continue;
             const int64_t orow = (int64_t)out_row0 + lrow;
-            if constexpr (MODE == MODE_GATEUP) {
-                const int half = p.N / 2;
 #pragma unroll
-                for (int j = 0; j < WN / 2; ++j) {
-                    const int col = n0 + wave_n * (16 * WN) + 32 * j + fl;
-                    if (col < half) {
-                        const float g = acc[i][j][r];
-                        const float u = acc[i][j + WN / 2][r];
-                        p.Y[orow * half + col] = f2h(silu(g) * u);
-                    }
-                }
-            } else if constexpr (MODE == MODE_ROUTER) {
+            for (int j = 0; j < WN; ++j)
 #pragma unroll
-                for (int j = 0; j < WN; ++j) {
-                    const int col = n0 + wn0 + 32 * j + fl;
-                    if (col < p.N) p.Yf[(orow * p.ksplit + blockIdx.z) * p.N + col] = acc[i][j][r];
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+                    out_vals(i, j, g, v);
+                    const int col = wcol0 + 32 * j + 8 * g + 4 * fh;
+                    if (col < out_cols)
+                        *reinterpret_cast<f32x4*>(p.Yf + (orow * p.ksplit + blockIdx.z) * out_cols + col) =
+                            f32x4{v[0], v[1], v[2], v[3]};
                 }
-            } else {
+        }
+    } else if ((out_cols & 7) == 0 && ((uintptr_t)p.Y & 15) == 0) {
+        // Each wave bounces one 32-row subtile at a time through its own LDS
+        // region (two regions, alternating), then writes whole row segments:
+        // 16-byte stores, 8 lanes per 128 bytes of a row.
+        constexpr int LDR = WC + 8;                   // padded row, fp16
+        constexpr int CPR = WC / 8;                   // 16-byte chunks per row
+        static_assert(2 * 32 * LDR * (TL::NT / 64) <= TL::LDS_A * 2 + TL::LDS_B * 2,
+                      "epilogue regions fit in the staging buffers");
+        static_assert((32 * CPR) % 64 == 0, "whole chunks per lane");
+        __syncthreads();  // every wave is done with the staging buffers
+        f16* const region0 = lds + (size_t)wave * 2 * 32 * LDR;
 #pragma unroll
-                for (int j = 0; j < WN; ++j) {
-                    const int col = n0 + wn0 + 32 * j + fl;
-                    if (col < p.N) p.Y[orow * p.N + col] = f2h(acc[i][j][r]);
+        for (int i = 0; i < WM; ++i) {
+            f16* const reg = region0 + (i & 1) * 32 * LDR;
+#pragma unroll
+            for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+                    out_vals(i, j, g, v);
+                    const uint32_t lo = (uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(reg + fl * LDR + 32 * j + 8 * g + 4 * fh) = make_uint2(lo, hi);
                 }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 32 * CPR / 64; ++q) {
+                const int c = q * 64 + lane;
+                const int row = c / CPR, ch = c % CPR;
+                const int lrow = wm0 + 32 * i + row;
+                const int col = wcol0 + ch * 8;
+                const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * LDR + ch * 8);
+                if (lrow < rows_valid && col < out_cols)
+                    *reinterpret_cast<u32x4*>(p.Y + ((int64_t)out_row0 + lrow) * out_cols + col) = d;
             }
+        }
+    } else {
+        // Unaligned output: element stores.
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+            const int lrow = wm0 + 32 * i + fl;
+            if (lrow >= rows_valid) continue;
+            uint16_t* const yrow = p.Y + ((int64_t)out_row0 + lrow) * out_cols;
+#pragma unroll
+            for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+                    out_vals(i, j, g, v);
+                    const int col = wcol0 + 32 * j + 8 * g + 4 * fh;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < out_cols) yrow[col + e] = f2h(v[e]);
+                }
         }
     }
 }
@@ -413,14 +515,24 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     p.Y = a.Y;
     p.K = a.K;
     p.N = a.N;
+    // One-dimensional grid of tiles, rounded up to whole XCD rounds.
+    auto grid_for = [&](int bm, int bn, dim3& grid) {
+        const int64_t gn = (a.N + bn - 1) / bn, gm = (a.M + bm - 1) / bm;
+        if (gn * gm > 0x7fffff00LL) return false;
+        p.grid_n = (int)gn;
+        p.grid_m = (int)gm;
+        grid = dim3((unsigned)((gn * gm + 7) / 8 * 8));
+        return true;
+    };
+    dim3 grid;
     if (a.M >= 2048) {
         // 256 x 256 tiles, 8 waves (two per SIMD) of 128 x 64.
         using TL = Tile<4, 2, 2, 4>;
-        dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
+        if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;
         return launch_t<4, 2, 2, 4, MODE_DENSE>(p, grid, st);
     }
     using TL = Tile<2, 4, 2, 2>;
-    dim3 grid((a.N + TL::BN - 1) / TL::BN, (unsigned)((a.M + TL::BM - 1) / TL::BM));
+    if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;
     return launch_t<2, 4, 2, 2, MODE_DENSE>(p, grid, st);
 }
 
@@ -467,11 +579,11 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     static_assert(TL::BM == QL_MOE_TILE_ROWS, "grouped tile height must match the tile map");
     const int shared_tiles = a.sqw ? (a.T + TL::BM - 1) / TL::BM : 0;
     const unsigned slots = (unsigned)(L.max_tiles + shared_tiles);
-    if (a.op == QL_OP_GATE_UP_SILU) {
-        dim3 grid(slots, (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2));
-        return launch_t<2, 2, 2, 4, MODE_GATEUP>(p, grid, st);
-    }
-    dim3 grid(slots, (a.N + TL::BN - 1) / TL::BN);
+    p.grid_n = (a.op == QL_OP_GATE_UP_SILU) ? (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2)
+                                            : (a.N + TL::BN - 1) / TL::BN;
+    p.grid_m = shared_tiles;
+    dim3 grid((unsigned)(((int64_t)slots * p.grid_n + 7) / 8 * 8));
+    if (a.op == QL_OP_GATE_UP_SILU) return launch_t<2, 2, 2, 4, MODE_GATEUP>(p, grid, st);
     return launch_t<2, 2, 2, 4, MODE_DOWN>(p, grid, st);
 }
 

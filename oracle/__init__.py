@@ -30,13 +30,13 @@ brute force; the end-to-end fidelity on real checkpoint weights is
 from .w4 import (GROUP, unpack_codes, pack_codes, dequantize, linear,
                  round_f16)
 from .route import (router_logits, softmax, topk_route, histogram,
-                    exclusive_scan, stable_permutation, tile_map,
+                    exclusive_scan, stable_permutation, tile_map, load_matched_tile_map,
                     topk_near_ties)
 from .moe import silu, expert_ffn, combine, moe_layer
 
 __all__ = [
     "GROUP", "unpack_codes", "pack_codes", "dequantize", "linear", "round_f16",
     "router_logits", "softmax", "topk_route", "histogram", "exclusive_scan",
-    "stable_permutation", "tile_map", "topk_near_ties",
+    "stable_permutation", "tile_map", "load_matched_tile_map", "topk_near_ties",
     "silu", "expert_ffn", "combine", "moe_layer",
 ]

@@ -23,7 +23,11 @@ Perplexity, "Optimizing on-device inference for Apple Silicon":
   assignments keep ascending order of a = t * topk + j.
 * "使瓦片大小与专家负载相匹配": each expert's rows are cut into tiles of a
   fixed number of rows; the last tile of an expert may be partial and an
-  expert with no rows has no tile.
+  expert with no rows has no tile.  The section's point is that the tile
+  height should follow the load.  Reading taken for the two-height map the
+  grouped GEMM runs on (load_matched_tile_map): an expert's rows go into
+  tall tiles while a full tall tile remains, the rest into short tiles;
+  all tall tiles are listed first.
 """
 from __future__ import annotations
 
@@ -137,3 +141,28 @@ def tile_map(counts, tile_rows: int) -> np.ndarray:
             tiles.append((e, offsets[e] + start, rows))
             start += tile_rows
     return np.asarray(tiles, dtype=np.int32).reshape(-1, 3)
+
+
+def load_matched_tile_map(counts, small_rows: int, big_rows: int) -> np.ndarray:
+    """int32 [ntiles][4]: (expert, first row, rows, height).
+
+    Each expert's rows, in row order, are cut into tiles of exactly
+    ``big_rows`` rows while at least ``big_rows`` remain, and the remainder
+    into tiles of at most ``small_rows`` rows.  The map lists every tall tile
+    first (experts ascending, rows ascending), then every short tile (same
+    order).  ``height`` is the tile height the tile is computed with
+    (``big_rows`` or ``small_rows``); rows <= height.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    offsets = exclusive_scan(counts).astype(np.int64)
+    tall, short = [], []
+    for e in range(counts.shape[0]):
+        start = 0
+        while counts[e] - start >= big_rows:
+            tall.append((e, offsets[e] + start, big_rows, big_rows))
+            start += big_rows
+        while start < counts[e]:
+            rows = min(small_rows, counts[e] - start)
+            short.append((e, offsets[e] + start, rows, small_rows))
+            start += small_rows
+    return np.asarray(tall + short, dtype=np.int32).reshape(-1, 4)

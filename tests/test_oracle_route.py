@@ -133,3 +133,43 @@ def test_dispatch_invariants_and_library_sort():
                 assert offsets[e] <= r0 and r0 + rows <= offsets[e + 1]
                 per[e] += rows
             assert np.array_equal(per, counts)
+
+
+def test_load_matched_tile_map_hand_fixture():
+    c = _load("tiles_hand.json")
+    for case in c["cases"]:
+        got = oracle.load_matched_tile_map(case["counts"], c["small_rows"], c["big_rows"])
+        assert got.tolist() == case["tiles"]
+
+
+def test_load_matched_tile_map_invariants():
+    """Brute force over random loads: every routed row is in exactly one
+    tile of its own expert, tall tiles are full and come first, short tiles
+    cover only what is left after the full tall tiles."""
+    rng = np.random.default_rng(11)
+    for T, E, k, skew in [(1, 256, 8, 0.0), (300, 256, 8, 1.1), (4096, 256, 8, 1.1), (50, 8, 8, 0.0),
+                          (1000, 16, 4, 2.0)]:
+        ids = synth.synthetic_topk_ids(rng, T, E, k, skew)
+        counts = oracle.histogram(ids, E)
+        offsets = oracle.exclusive_scan(counts)
+        for small, big in ((128, 256), (2, 4), (32, 96)):
+            tiles = oracle.load_matched_tile_map(counts, small, big)
+            owner = np.full(T * k, -1)
+            seen_short = False
+            for e, r0, rows, h in tiles:
+                assert h in (small, big) and 1 <= rows <= h
+                if h == big:
+                    assert not seen_short and rows == big
+                else:
+                    seen_short = True
+                assert offsets[e] <= r0 and r0 + rows <= offsets[e + 1]
+                assert np.all(owner[r0:r0 + rows] == -1)
+                owner[r0:r0 + rows] = e
+            flat = np.repeat(np.arange(E), counts)
+            assert np.array_equal(owner, flat)
+            for e in range(E):
+                n_tall = sum(1 for t in tiles if t[0] == e and t[3] == big)
+                n_short = sum(1 for t in tiles if t[0] == e and t[3] == small)
+                assert n_tall == counts[e] // big
+                assert n_short == -(-(counts[e] % big) // small)
+            assert len(tiles) <= (T * k) // small + E

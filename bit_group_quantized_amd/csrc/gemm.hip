@@ -104,12 +104,25 @@ struct Tile {
     static_assert(NT % BN == 0 && (TPC == 1 || TPC == 2), "one or two threads per B column");
 };
 
+// One output tile for one workgroup: where its rows, columns, K range and
+// weights come from.
+struct Job {
+    int rows_valid;   // rows of this tile that exist
+    int out_row0;     // first output row
+    int n0;           // first output column (act column for GATEUP)
+    int kbeg, kend;   // K steps of this workgroup
+    int tile_kind;    // grouped: 0 routed, 1 shared
+    int tile_first;   // grouped: first row (routed r or shared token)
+    int kz;           // router: index of the K split
+    const uint32_t* wq;
+    const uint16_t* ws;
+    const uint16_t* wb;
+};
+
 template <int WM, int WN, int WGM, int WGN, int MODE>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-gemm_w4_kernel(const KParams p) {
+__device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
     constexpr int BM = TL::BM, BN = TL::BN;
-    extern __shared__ __align__(16) f16 lds[];
     f16* As = lds;                     // [2][BM][kLdk]
     f16* Bs = lds + 2 * TL::LDS_A;     // [2][BN][kLdk]
 
@@ -122,69 +135,16 @@ gemm_w4_kernel(const KParams p) {
     const int K = p.K;
     const int G = K / kGroup;
     const int wpr = K / 8;
-
-    // ---- tile coordinates ---------------------------------------------------
-    int rows_valid;          // rows of this tile that exist
-    int out_row0;            // first output row
-    int n0;                  // first output column (act column for GATEUP)
-    int kbeg = 0, kend = G;  // K steps of this workgroup
-    const uint32_t* wq = p.qw;
-    const uint16_t* ws = p.sc;
-    const uint16_t* wb = p.bi;
-    int tile_kind = 0;       // grouped: 0 routed, 1 shared
-    int tile_first = 0;      // grouped: first row (routed r or shared token)
-    if constexpr (MODE == MODE_DENSE) {
-        const int item = xcd_item(p.grid_n * p.grid_m);
-        if (item < 0) return;
-        // Inside an XCD's run, groups of 4 row blocks sweep the column blocks
-        // together, so concurrent tiles share both activation rows and weights.
-        constexpr int GM = 4;
-        const int in_group = GM * p.grid_n;
-        const int first_m = (item / in_group) * GM;
-        const int gm = min(p.grid_m - first_m, GM);
-        const int r = item % in_group;
-        n0 = (r / gm) * BN;
-        out_row0 = (first_m + r % gm) * BM;
-        rows_valid = (int)min<int64_t>(BM, p.M - out_row0);
-    } else if constexpr (MODE == MODE_ROUTER) {
-        n0 = blockIdx.y * BN;
-        out_row0 = blockIdx.x * BM;
-        rows_valid = (int)min<int64_t>(BM, p.M - out_row0);
-        const int per = (G + p.ksplit - 1) / p.ksplit;
-        kbeg = blockIdx.z * per;
-        kend = min(G, kbeg + per);
-    } else {
-        // Items are (tile, column block) over the tiles that exist: routed
-        // tiles first, then the shared expert's.
-        const int nt = min(max(p.ws_header[0], 0), p.max_tiles);
-        const int item = xcd_item((nt + p.grid_m) * p.grid_n);
-        if (item < 0) return;
-        const int tslot = item / p.grid_n;
-        const int nblk = item % p.grid_n;
-        const int slot = (tslot < nt) ? tslot : p.max_tiles + (tslot - nt);
-        if (slot < p.max_tiles) {
-            if (slot >= p.ws_header[0]) return;  // fewer routed tiles than slots
-            const int* tp = p.tiles + (size_t)slot * 4;
-            // Clamped so that a corrupted tile map can never index out of bounds.
-            const int e = min(max(tp[0], 0), p.E - 1);
-            rows_valid = min(max(tp[2], 1), BM);
-            tile_first = min(max(tp[1], 0), p.T * p.topk - rows_valid);
-            out_row0 = tile_first;
-            wq = p.qw + (size_t)e * p.N * wpr;
-            ws = p.sc + (size_t)e * p.N * G;
-            wb = p.bi + (size_t)e * p.N * G;
-        } else {
-            tile_kind = 1;
-            const int s = slot - p.max_tiles;
-            tile_first = s * BM;
-            rows_valid = min(BM, p.T - tile_first);
-            out_row0 = p.T * p.topk + tile_first;
-            wq = p.sqw;
-            ws = p.ssc;
-            wb = p.sbi;
-        }
-        n0 = nblk * ((MODE == MODE_GATEUP) ? BN / 2 : BN);
-    }
+    const int rows_valid = job.rows_valid;
+    const int out_row0 = job.out_row0;
+    const int n0 = job.n0;
+    const int kbeg = job.kbeg, kend = job.kend;
+    const int tile_kind = job.tile_kind;
+    const int tile_first = job.tile_first;
+    const uint32_t* const wq = job.wq;
+    const uint16_t* const ws = job.ws;
+    const uint16_t* const wb = job.wb;
+    (void)BM;
 
     // ---- A row sources (one per 32-row slab this thread stages) -------------
     const uint16_t* arow[TL::A_LOADS];
@@ -379,10 +339,10 @@ gemm_w4_kernel(const KParams p) {
         }
         if (i < nk) body(set0, na, i);
     };
-    if constexpr (MODE == MODE_GATEUP || MODE == MODE_DOWN) {
-        // Routed tiles end in padding rows; every wave still stages its share
-        // (the barriers are reached by all), but skips subtiles past the end.
-        static_assert(WM == 2, "row-subtile dispatch written for two subtiles per wave");
+    if constexpr ((MODE == MODE_GATEUP || MODE == MODE_DOWN) && WM == 2) {
+        // Short routed tiles end in padding rows; every wave still stages its
+        // share (the barriers are reached by all), but skips subtiles past
+        // the end.  (Tall routed tiles are always full.)
         const int na = __builtin_amdgcn_readfirstlane(min(max((rows_valid - wm0 + 31) / 32, 0), WM));
         if (na >= 2) main_loop(std::integral_constant<int, 2>{});
         else if (na == 1) main_loop(std::integral_constant<int, 1>{});
@@ -425,7 +385,7 @@ gemm_w4_kernel(const KParams p) {
                     out_vals(i, j, g, v);
                     const int col = wcol0 + 32 * j + 8 * g + 4 * fh;
                     if (col < out_cols)
-                        *reinterpret_cast<f32x4*>(p.Yf + (orow * p.ksplit + blockIdx.z) * out_cols + col) =
+                        *reinterpret_cast<f32x4*>(p.Yf + (orow * p.ksplit + job.kz) * out_cols + col) =
                             f32x4{v[0], v[1], v[2], v[3]};
                 }
         }
@@ -485,6 +445,117 @@ gemm_w4_kernel(const KParams p) {
                 }
         }
     }
+}
+
+// Dense prefill GEMM and the router GEMM.
+template <int WM, int WN, int WGM, int WGN, int MODE>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+gemm_w4_kernel(const KParams p) {
+    using TL = Tile<WM, WN, WGM, WGN>;
+    constexpr int BM = TL::BM, BN = TL::BN;
+    extern __shared__ __align__(16) f16 lds[];
+    const int G = p.K / kGroup;
+    Job job{};
+    job.kbeg = 0;
+    job.kend = G;
+    job.wq = p.qw;
+    job.ws = p.sc;
+    job.wb = p.bi;
+    if constexpr (MODE == MODE_DENSE) {
+        const int item = xcd_item(p.grid_n * p.grid_m);
+        if (item < 0) return;
+        // Inside an XCD's run, groups of 4 row blocks sweep the column blocks
+        // together, so concurrent tiles share both activation rows and weights.
+        constexpr int GM = 4;
+        const int in_group = GM * p.grid_n;
+        const int first_m = (item / in_group) * GM;
+        const int gm = min(p.grid_m - first_m, GM);
+        const int r = item % in_group;
+        job.n0 = (r / gm) * BN;
+        job.out_row0 = (first_m + r % gm) * BM;
+    } else {
+        static_assert(MODE == MODE_ROUTER, "dense or router");
+        job.n0 = blockIdx.y * BN;
+        job.out_row0 = blockIdx.x * BM;
+        const int per = (G + p.ksplit - 1) / p.ksplit;
+        job.kbeg = blockIdx.z * per;
+        job.kend = min(G, job.kbeg + per);
+        job.kz = blockIdx.z;
+    }
+    job.rows_valid = (int)min<int64_t>(BM, p.M - job.out_row0);
+    gemm_tile<WM, WN, WGM, WGN, MODE>(p, job, lds);
+}
+
+// Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
+// 8 waves of 128 x 64) and short tiles (128 rows, 8 waves of 64 x 64), both
+// 256 columns wide, in one launch.  The tall class (tall routed tiles, then
+// the shared expert's tiles) comes first in the grid, then the short class;
+// each class is dealt to the XCDs in contiguous runs of (tile, column block)
+// items, so that every XCD gets an equal share of each class.
+using TallTile = Tile<4, 2, 2, 4>;
+using ShortTile = Tile<2, 2, 2, 4>;
+static_assert(TallTile::NT == ShortTile::NT && TallTile::BN == ShortTile::BN, "one workgroup shape");
+static_assert(ShortTile::BM == QL_MOE_TILE_ROWS && TallTile::BM == 2 * QL_MOE_TILE_ROWS,
+              "tile heights of the tile map");
+constexpr size_t kGroupedLds =
+    TallTile::LDS_BYTES > ShortTile::LDS_BYTES ? TallTile::LDS_BYTES : ShortTile::LDS_BYTES;
+
+template <int MODE>
+__global__ void __launch_bounds__(TallTile::NT)
+gemm_w4_grouped_kernel(const KParams p) {
+    extern __shared__ __align__(16) f16 lds[];
+    const int G = p.K / kGroup;
+    const int wpr = p.K / 8;
+    const int NB = p.grid_n;  // column blocks
+    const int nt = min(max(p.ws_header[0], 0), p.max_tiles);
+    const int nbig = min(max(p.ws_header[3], 0), nt);
+    const int big_items = (nbig + p.grid_m) * NB;  // grid_m: shared-expert tiles
+    const int small_items = (nt - nbig) * NB;
+    const int per_b = (big_items + 7) >> 3, per_s = (small_items + 7) >> 3;
+    const int lin = blockIdx.x;
+    bool tall;
+    int item;
+    if (lin < 8 * per_b) {
+        item = (lin & 7) * per_b + (lin >> 3);
+        if (item >= big_items) return;
+        tall = true;
+    } else {
+        const int l2 = lin - 8 * per_b;
+        if ((l2 >> 3) >= per_s) return;
+        item = (l2 & 7) * per_s + (l2 >> 3);
+        if (item >= small_items) return;
+        tall = false;
+    }
+    const int tslot = (tall ? 0 : nbig) + item / NB;
+    const int nblk = item % NB;
+    const int height = tall ? TallTile::BM : ShortTile::BM;
+    Job job{};
+    job.kbeg = 0;
+    job.kend = G;
+    if (tall && tslot >= nbig) {
+        job.tile_kind = 1;
+        job.tile_first = (tslot - nbig) * height;
+        job.rows_valid = min(height, p.T - job.tile_first);
+        job.out_row0 = p.T * p.topk + job.tile_first;
+        job.wq = p.sqw;
+        job.ws = p.ssc;
+        job.wb = p.sbi;
+    } else {
+        const int* tp = p.tiles + (size_t)tslot * 4;
+        // Clamped so that a corrupted tile map can never index out of bounds.
+        const int e = min(max(tp[0], 0), p.E - 1);
+        job.rows_valid = min(max(tp[2], 1), height);
+        job.tile_first = min(max(tp[1], 0), p.T * p.topk - job.rows_valid);
+        job.out_row0 = job.tile_first;
+        job.wq = p.qw + (size_t)e * p.N * wpr;
+        job.ws = p.sc + (size_t)e * p.N * G;
+        job.wb = p.bi + (size_t)e * p.N * G;
+    }
+    job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
+    if (tall)
+        gemm_tile<4, 2, 2, 4, MODE>(p, job, lds);
+    else
+        gemm_tile<2, 2, 2, 4, MODE>(p, job, lds);
 }
 
 template <int WM, int WN, int WGM, int WGN, int MODE>
@@ -554,6 +625,19 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
 }
 
 
+template <int MODE>
+int launch_grouped_t(const KParams& p, dim3 grid, hipStream_t st) {
+    static bool attr_done = false;  // benign race: the attribute is idempotent
+    if (!attr_done) {
+        if (hipFuncSetAttribute((const void*)gemm_w4_grouped_kernel<MODE>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGroupedLds) != hipSuccess)
+            return QL_ERR_HIP;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
 int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     KParams p{};
@@ -574,17 +658,18 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     p.Y = a.Y;
     p.K = a.K;
     p.N = a.N;
-    // 128 x 256 tiles, 8 waves (two per SIMD) of 64 x 64.
-    using TL = Tile<2, 2, 2, 4>;
-    static_assert(TL::BM == QL_MOE_TILE_ROWS, "grouped tile height must match the tile map");
-    const int shared_tiles = a.sqw ? (a.T + TL::BM - 1) / TL::BM : 0;
-    const unsigned slots = (unsigned)(L.max_tiles + shared_tiles);
-    p.grid_n = (a.op == QL_OP_GATE_UP_SILU) ? (a.N / 2 + TL::BN / 2 - 1) / (TL::BN / 2)
-                                            : (a.N + TL::BN - 1) / TL::BN;
-    p.grid_m = shared_tiles;
-    dim3 grid((unsigned)(((int64_t)slots * p.grid_n + 7) / 8 * 8));
-    if (a.op == QL_OP_GATE_UP_SILU) return launch_t<2, 2, 2, 4, MODE_GATEUP>(p, grid, st);
-    return launch_t<2, 2, 2, 4, MODE_DOWN>(p, grid, st);
+    p.grid_n = (a.op == QL_OP_GATE_UP_SILU) ? (a.N / 2 + TallTile::BN / 2 - 1) / (TallTile::BN / 2)
+                                            : (a.N + TallTile::BN - 1) / TallTile::BN;
+    p.grid_m = a.sqw ? (a.T + TallTile::BM - 1) / TallTile::BM : 0;  // shared-expert tiles
+    // Upper bounds of both classes; workgroups past the actual items exit.
+    const int64_t max_tall = ((int64_t)a.T * a.topk) / TallTile::BM + p.grid_m;
+    const int64_t items_b = max_tall * p.grid_n, items_s = (int64_t)L.max_tiles * p.grid_n;
+    const int64_t blocks = (items_b + 7) / 8 * 8 + (items_s + 7) / 8 * 8;
+    if (blocks > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (blocks == 0) return QL_OK;
+    const dim3 grid((unsigned)blocks);
+    if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP>(p, grid, st);
+    return launch_grouped_t<MODE_DOWN>(p, grid, st);
 }
 
 }  // namespace ql

@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kChunk = kRouteChunkTokens;
 constexpr int kMaskWords = kChunk / 32;
+constexpr int kTicketWord = 4;  // header word of the decode-route ticket
 constexpr int kRouterParts = 32;     // row-parallel router: D split in 32 slices
 constexpr int kRouterMfmaParts = kRouterMfmaSplit;  // MFMA router: K split
 
@@ -56,9 +57,9 @@ __device__ int block_inclusive_scan(int v, int* s_tmp /* >= 16 ints */) {
 // Small-T router: partial logits over D/32-row slices, summed by the top-k
 // step in a fixed order.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
-                      float* __restrict__ partials, int D, int E) {
+__device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__ H,
+                                                    const uint16_t* __restrict__ Wr,
+                                                    float* __restrict__ partials, int D, int E) {
     __shared__ float hs[QL_MAX_K / kRouterParts];
     const int t = blockIdx.y, p = blockIdx.x;
     const int rows = D / kRouterParts;
@@ -76,9 +77,9 @@ router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict
 // 8*oct .. 8*oct+7 and the rows dl, dl+8, ... of the block's D slice; the 8
 // row lanes of an expert octet are summed through LDS in a fixed order.
 // Requires E % 8 == 0.
-__global__ void __launch_bounds__(256)
-router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
-                          float* __restrict__ partials, int D, int E) {
+__device__ __forceinline__ void router_partial_vec_body(const uint16_t* __restrict__ H,
+                                                        const uint16_t* __restrict__ Wr,
+                                                        float* __restrict__ partials, int D, int E) {
     __shared__ float red[8][256 + 4];
     const int t = blockIdx.y, p = blockIdx.x;
     const int rows = D / kRouterParts;
@@ -113,6 +114,18 @@ router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __rest
         }
         __syncthreads();
     }
+}
+
+__global__ void __launch_bounds__(256)
+router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
+                      float* __restrict__ partials, int D, int E) {
+    router_partial_body(H, Wr, partials, D, E);
+}
+
+__global__ void __launch_bounds__(256)
+router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
+                          float* __restrict__ partials, int D, int E) {
+    router_partial_vec_body(H, Wr, partials, D, E);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,8 +259,12 @@ topk_kernel(const float* __restrict__ src, const float* __restrict__ bias,
 // Dispatch for many tokens: per-chunk masks and counts, one scan block, and
 // the stable scatter.
 // ---------------------------------------------------------------------------
+// Per-chunk masks in LDS: bit (t % 32) of mask[e][t / 32] is set when token
+// t of the chunk chose expert e.  With s_ids given, the chunk's ids are also
+// kept in LDS ([token][topk]).  Returns 1 if an id was out of range or
+// repeated within a token.
 __device__ int build_chunk_masks(const int* __restrict__ ids, int T, int E, int topk, int c,
-                                 uint32_t* mask) {
+                                 uint32_t* mask, int* s_ids) {
     for (int i = threadIdx.x; i < E * kMaskWords; i += blockDim.x) mask[i] = 0u;
     __syncthreads();
     const int tl = threadIdx.x;
@@ -257,6 +274,7 @@ __device__ int build_chunk_masks(const int* __restrict__ ids, int T, int E, int 
         const uint32_t bit = 1u << (tl & 31);
         for (int j = 0; j < topk; ++j) {
             const int e = ids[(size_t)t * topk + j];
+            if (s_ids) s_ids[tl * topk + j] = e;
             if ((unsigned)e >= (unsigned)E) {
                 err = 1;
                 continue;
@@ -274,7 +292,7 @@ dispatch_count_kernel(const int* __restrict__ ids, int T, int E, int topk,
                       int* __restrict__ chunk_counts, int* __restrict__ chunk_err) {
     extern __shared__ uint32_t mask[];
     const int c = blockIdx.x;
-    const int err = build_chunk_masks(ids, T, E, topk, c, mask);
+    const int err = build_chunk_masks(ids, T, E, topk, c, mask, nullptr);
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int cnt = 0;
 #pragma unroll
@@ -285,18 +303,35 @@ dispatch_count_kernel(const int* __restrict__ ids, int T, int E, int topk,
     if (threadIdx.x == 0) chunk_err[c] = any;
 }
 
+// One block, one thread per expert: chunk bases (in place), counts, offsets
+// and the load-matched tile map (section 使瓦片大小与专家负载相匹配): an
+// expert's rows go into tiles of 2 * QL_MOE_TILE_ROWS rows while a full one
+// remains, the rest into tiles of at most QL_MOE_TILE_ROWS rows; the tall
+// tiles are listed first.
 __global__ void __launch_bounds__(1024)
 dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chunk_err,
                      int nchunks, int E, int* __restrict__ counts, int* __restrict__ offsets,
                      int* __restrict__ ws_header, int* __restrict__ tiles) {
+    constexpr int SR = QL_MOE_TILE_ROWS, BR = 2 * QL_MOE_TILE_ROWS;
     __shared__ int s_tmp[16];
+    __shared__ int s_tot[2];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = chunk_counts[(size_t)c * E + e];
-            chunk_counts[(size_t)c * E + e] = run;  // becomes the chunk's base inside e
-            run += v;
+        // Sixteen chunk counts are loaded before any is used, so the loop costs
+        // one memory round trip per sixteen chunks.
+        for (int c0 = 0; c0 < nchunks; c0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = (c0 + u < nchunks) ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c0 + u < nchunks) {
+                    chunk_counts[(size_t)(c0 + u) * E + e] = run;  // the chunk's base inside e
+                    run += v[u];
+                }
+            }
         }
         counts[e] = run;
     }
@@ -305,24 +340,41 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
     const int excl = incl - cnt;
     if (e < E) offsets[e] = excl;
     if (e == E - 1) offsets[E] = incl;
-    const int nt = (cnt + QL_MOE_TILE_ROWS - 1) / QL_MOE_TILE_ROWS;
-    const int tincl = block_inclusive_scan(nt, s_tmp);
-    const int ts = tincl - nt;
-    for (int j = 0; j < nt; ++j) {
-        int* tp = tiles + (size_t)(ts + j) * 4;
+    const int nb = cnt / BR;
+    const int rem = cnt - nb * BR;
+    const int ns = (rem + SR - 1) / SR;
+    const int binc = block_inclusive_scan(nb, s_tmp);
+    const int sinc = block_inclusive_scan(ns, s_tmp);
+    if (threadIdx.x == blockDim.x - 1) {
+        s_tot[0] = binc;
+        s_tot[1] = sinc;
+    }
+    __syncthreads();
+    const int nbig = s_tot[0];
+    for (int j = 0; j < nb; ++j) {
+        int* tp = tiles + (size_t)(binc - nb + j) * 4;
         tp[0] = e;
-        tp[1] = excl + j * QL_MOE_TILE_ROWS;
-        tp[2] = min(QL_MOE_TILE_ROWS, cnt - j * QL_MOE_TILE_ROWS);
-        tp[3] = 0;
+        tp[1] = excl + j * BR;
+        tp[2] = BR;
+        tp[3] = BR;
+    }
+    for (int j = 0; j < ns; ++j) {
+        int* tp = tiles + (size_t)(nbig + sinc - ns + j) * 4;
+        tp[0] = e;
+        tp[1] = excl + nb * BR + j * SR;
+        tp[2] = min(SR, rem - j * SR);
+        tp[3] = SR;
     }
     int err = 0;
     for (int c = e; c < nchunks; c += blockDim.x) err |= chunk_err[c];
     const int any = __syncthreads_or(err);
-    if (e == E - 1) ws_header[0] = tincl;
+    if (threadIdx.x == blockDim.x - 1) {
+        ws_header[0] = nbig + s_tot[1];
+        ws_header[3] = nbig;
+    }
     if (e == 0) {
-        ws_header[1] = QL_MOE_TILE_ROWS;
+        ws_header[1] = SR;
         ws_header[2] = any;
-        ws_header[3] = 0;
     }
 }
 
@@ -332,8 +384,12 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
                         int* __restrict__ sorted_assign, int* __restrict__ pos,
                         int2* __restrict__ row_info, int2* __restrict__ assign_info) {
     extern __shared__ uint32_t mask[];
+    int* const s_base = reinterpret_cast<int*>(mask + E * kMaskWords);  // [E]
+    int* const s_ids = s_base + E;                                      // [kChunk][topk]
     const int c = blockIdx.x;
-    build_chunk_masks(ids, T, E, topk, c, mask);
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        s_base[e] = offsets[e] + chunk_base[(size_t)c * E + e];
+    build_chunk_masks(ids, T, E, topk, c, mask, s_ids);  // ends with a barrier
     const int tl = threadIdx.x;
     const int t = c * kChunk + tl;
     if (t >= T) return;
@@ -341,7 +397,7 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
     const uint32_t below = (1u << (tl & 31)) - 1u;
     for (int j = 0; j < topk; ++j) {
         const int a = t * topk + j;
-        const int e = ids[a];
+        const int e = s_ids[tl * topk + j];
         if ((unsigned)e >= (unsigned)E) {
             pos[a] = -1;
             assign_info[a] = make_int2(-1, -1);
@@ -349,7 +405,7 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
         }
         int rank = __popc(mask[e * kMaskWords + w] & below);
         for (int ww = 0; ww < w; ++ww) rank += __popc(mask[e * kMaskWords + ww]);
-        const int r = offsets[e] + chunk_base[(size_t)c * E + e] + rank;
+        const int r = s_base[e] + rank;
         sorted_assign[r] = a;
         pos[a] = r;
         row_info[r] = make_int2(e, t);
@@ -369,13 +425,12 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
 // tile indices (every expert has at most one tile here).
 // ---------------------------------------------------------------------------
 template <int EPL, bool DO_TOPK>
-__global__ void __launch_bounds__(256)
-route_small_kernel(const float* __restrict__ partials, int nparts, const float* __restrict__ bias,
-                   float* __restrict__ logits_out, int T, int E, int topk,
-                   int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
-                   int* __restrict__ offsets, int* __restrict__ sorted_assign,
-                   int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
-                   int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+__device__ __forceinline__ void route_small_body(const float* __restrict__ partials, const float* __restrict__ bias,
+                 float* __restrict__ logits_out, int T, int E, int topk,
+                 int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
+                 int* __restrict__ offsets, int* __restrict__ sorted_assign,
+                 int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
+                 int2* __restrict__ row_info, int2* __restrict__ assign_info) {
     static_assert(kRouterSmallT <= 32 && kRouterSmallT * QL_MAX_TOPK_DEV <= 4 * QL_MAX_EXPERTS_DEV,
                   "token masks are 32 bits wide");
     static_assert(QL_MOE_TILE_ROWS >= kRouterSmallT, "one tile per expert");
@@ -389,9 +444,23 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
     const int nass = T * topk;
     for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
     if constexpr (DO_TOPK) {
+        // Logits of all tokens, one (token, expert) per thread: the partial
+        // rows are summed in a fixed order, all of their loads issued at once.
+        for (int idx = threadIdx.x; idx < T * E; idx += blockDim.x) {
+            const int tt = idx / E, e = idx - tt * E;
+            float part[kRouterParts];
+#pragma unroll
+            for (int p = 0; p < kRouterParts; ++p) part[p] = partials[((size_t)tt * kRouterParts + p) * E + e];
+            float sum = 0.f;
+#pragma unroll
+            for (int p = 0; p < kRouterParts; ++p) sum += part[p];
+            if (bias) sum += bias[e];
+            logits_out[(size_t)tt * E + e] = sum;
+        }
+        __syncthreads();
         for (int t = wave; t < T; t += 4)
-            topk_one_token<EPL, kRouterParts>(partials, bias, logits_out, t, E, topk,
-                                              s_ids + t * topk, s_gates + t * topk);
+            topk_one_token<EPL, 1>(logits_out, nullptr, logits_out, t, E, topk, s_ids + t * topk,
+                                   s_gates + t * topk);
         __syncthreads();
         for (int a = threadIdx.x; a < nass; a += blockDim.x) {
             ids[a] = s_ids[a];
@@ -439,7 +508,7 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
                 tp[0] = e;
                 tp[1] = off;
                 tp[2] = c;
-                tp[3] = 0;
+                tp[3] = QL_MOE_TILE_ROWS;  // tile height: short tiles only here
             }
             run += c + ((c > 0) << 16);
         }
@@ -469,6 +538,50 @@ route_small_kernel(const float* __restrict__ partials, int nparts, const float* 
     }
 }
 
+template <int EPL, bool DO_TOPK>
+__global__ void __launch_bounds__(256)
+route_small_kernel(const float* __restrict__ partials, const float* __restrict__ bias,
+                   float* __restrict__ logits_out, int T, int E, int topk,
+                   int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
+                   int* __restrict__ offsets, int* __restrict__ sorted_assign,
+                   int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
+                   int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+    route_small_body<EPL, DO_TOPK>(partials, bias, logits_out, T, E, topk, ids, gates, counts, offsets,
+                                   sorted_assign, pos, ws_header, tiles, row_info, assign_info);
+}
+
+// The whole small-T route in one launch: every block computes one router
+// partial (D slice p, token t); the block that finishes last (a ticket in
+// the workspace header, left at zero for the next call) then runs the top-k
+// and the dispatch of all tokens.
+template <int EPL, bool VEC>
+__global__ void __launch_bounds__(256)
+route_decode_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr, int D,
+                    float* __restrict__ partials, const float* __restrict__ bias,
+                    float* __restrict__ logits_out, int T, int E, int topk,
+                    int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
+                    int* __restrict__ offsets, int* __restrict__ sorted_assign,
+                    int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
+                    int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+    if constexpr (VEC)
+        router_partial_vec_body(H, Wr, partials, D, E);
+    else
+        router_partial_body(H, Wr, partials, D, E);
+    __shared__ int s_last;
+    __threadfence();  // this block's partials are visible device-wide before its ticket
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nblocks = gridDim.x * gridDim.y;
+        s_last = atomicAdd(&ws_header[kTicketWord], 1) == nblocks - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: every other block's partials
+    route_small_body<EPL, true>(partials, bias, logits_out, T, E, topk, ids, gates, counts, offsets,
+                                sorted_assign, pos, ws_header, tiles, row_info, assign_info);
+    if (threadIdx.x == 0) ws_header[kTicketWord] = 0;  // every block has taken its ticket
+}
+
 template <int EPL>
 int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStream_t st) {
     float* partials = reinterpret_cast<float*>(a.ws + L.partials);
@@ -479,13 +592,41 @@ int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStr
     int2* ainfo = reinterpret_cast<int2*>(a.ws + L.assign_info);
     if (do_topk)
         hipLaunchKernelGGL((route_small_kernel<EPL, true>), dim3(1), dim3(256), 0, st, partials,
-                           L.nparts, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
+                           a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
                            a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
     else
         hipLaunchKernelGGL((route_small_kernel<EPL, false>), dim3(1), dim3(256), 0, st, partials,
-                           L.nparts, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
+                           a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
                            a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
+template <int EPL, bool VEC>
+int launch_decode(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
+    float* partials = reinterpret_cast<float*>(a.ws + L.partials);
+    float* logits = reinterpret_cast<float*>(a.ws + L.logits);
+    int* hdr = reinterpret_cast<int*>(a.ws + L.header);
+    int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
+    int2* rinfo = reinterpret_cast<int2*>(a.ws + L.row_info);
+    int2* ainfo = reinterpret_cast<int2*>(a.ws + L.assign_info);
+    hipLaunchKernelGGL((route_decode_kernel<EPL, VEC>), dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
+                       a.Wr, a.D, partials, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
+                       a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
+template <bool VEC>
+int launch_decode_v(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
+    const int epl = (a.E + 63) / 64;
+    if (epl <= 1) return launch_decode<1, VEC>(a, L, st);
+    if (epl <= 2) return launch_decode<2, VEC>(a, L, st);
+    if (epl <= 4) return launch_decode<4, VEC>(a, L, st);
+    if (epl <= 8) return launch_decode<8, VEC>(a, L, st);
+    return launch_decode<16, VEC>(a, L, st);
+}
+
+int launch_decode_any(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
+    return (a.E % 8 == 0) ? launch_decode_v<true>(a, L, st) : launch_decode_v<false>(a, L, st);
 }
 
 int launch_small_any(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStream_t st) {
@@ -524,11 +665,21 @@ int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t
     int* hdr = reinterpret_cast<int*>(a.ws + L.header);
     int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
     const size_t smem = (size_t)a.E * kMaskWords * sizeof(uint32_t);
+    const size_t smem_scatter = smem + ((size_t)a.E + (size_t)kChunk * a.topk) * sizeof(int);
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
                        a.E, a.topk, cc, cerr);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, cc, cerr, L.nchunks, a.E,
                        a.counts, a.offsets, hdr, tiles);
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
+    static bool attr_done = false;  // benign race: the attribute is idempotent
+    if (!attr_done) {
+        const size_t max_smem = (size_t)QL_MAX_EXPERTS_DEV * kMaskWords * sizeof(uint32_t) +
+                                ((size_t)QL_MAX_EXPERTS_DEV + (size_t)kChunk * QL_MAX_TOPK_DEV) * sizeof(int);
+        if (hipFuncSetAttribute((const void*)dispatch_scatter_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem) != hipSuccess)
+            return QL_ERR_HIP;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nchunks), dim3(kChunk), smem_scatter, st, a.ids, a.T,
                        a.E, a.topk, a.offsets, cc, a.sorted_assign, a.pos,
                        reinterpret_cast<int2*>(a.ws + L.row_info),
                        reinterpret_cast<int2*>(a.ws + L.assign_info));
@@ -548,7 +699,7 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
     L.nparts = router_uses_mfma(T, E) ? kRouterMfmaParts : kRouterParts;
     size_t off = 0;
     L.header = off;
-    off += 16;
+    off += 32;
     L.tiles = off;
     off += (size_t)L.max_tiles * 16;
     off = align256(off);
@@ -582,6 +733,7 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
         const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st);
         if (rc != QL_OK) return rc;
     } else {
+        if (a.T <= kRouterSmallT) return launch_decode_any(a, L, st);
         if (a.E % 8 == 0)
             hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st,
                                a.H, a.Wr, partials, a.D, a.E);
@@ -589,7 +741,6 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
             hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
                                a.Wr, partials, a.D, a.E);
         if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
-        if (a.T <= kRouterSmallT) return launch_small_any(a, L, true, st);
     }
     launch_topk(partials, L.nparts, a, logits, st);
     if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;

@@ -23,7 +23,7 @@ TAU = 1e-4
 def _ws_tiles(out):
     ws = host(out["workspace"]).view(np.int32)
     n = int(ws[0])
-    return ws[:4], ws[4:4 + 4 * n].reshape(n, 4)[:, :3]
+    return ws[:8], ws[8:8 + 4 * n].reshape(n, 4)
 
 
 def _check_dispatch(out, ids, E, T, topk):
@@ -35,8 +35,10 @@ def _check_dispatch(out, ids, E, T, topk):
     assert np.array_equal(host(out["sorted_assign"]), sa)
     assert np.array_equal(host(out["pos"]), pos)
     hdr, tiles = _ws_tiles(out)
+    ref = oracle.load_matched_tile_map(counts, ql.QL_MOE_TILE_ROWS, 2 * ql.QL_MOE_TILE_ROWS)
     assert hdr[1] == ql.QL_MOE_TILE_ROWS and hdr[2] == 0
-    assert np.array_equal(tiles, oracle.tile_map(counts, ql.QL_MOE_TILE_ROWS))
+    assert hdr[3] == int(np.sum(ref[:, 3] == 2 * ql.QL_MOE_TILE_ROWS))
+    assert np.array_equal(tiles, ref)
 
 
 @pytest.mark.parametrize("T,E,topk,skew,seed", [
@@ -138,3 +140,28 @@ def test_route_prefill(T, skewed, seed):
     # Without a near tie at the k/k+1 boundary the chosen sets must agree.
     if not near[:, -1].any():
         assert all(set(a) == set(b) for a, b in zip(host(out["ids"]).tolist(), ids_ref.tolist()))
+
+
+def test_route_workspace_reuse_across_sizes():
+    """One zero-filled workspace serves a sequence of routes of different
+    sizes: the small-T route's completion counter is back at zero after
+    every call, and every call matches the oracle."""
+    import torch
+    say("route workspace reuse T = 1, 16, 5, 300, 1, 9")
+    w = synth.moe_weights(3)
+    big = ql.alloc_route_outputs(300, 256, 8, torch.device("cuda"))
+    for i, T in enumerate((1, 16, 5, 300, 1, 9)):
+        tok = synth.moe_tokens(5000 + i, T, skewed=True)
+        out = dict(big)
+        out["ids"] = big["ids"][:T]
+        out["gates"] = big["gates"][:T]
+        out["sorted_assign"] = big["sorted_assign"][: T * 8]
+        out["pos"] = big["pos"][: T * 8]
+        ql.moe_route(t(tok["H"]), t(w["Wr"]), t(tok["logit_bias"]), 8, out)
+        torch.cuda.synchronize()
+        assert int(host(big["workspace"]).view(np.int32)[4]) == 0
+        exact, near, ids_ref = _check_route(out, tok["H"], w["Wr"], tok["logit_bias"], 8, T, 256)
+        if exact:
+            _check_dispatch(out, ids_ref, 256, T, 8)
+        else:
+            _check_dispatch_properties(out, host(out["ids"]), 256, T, 8)

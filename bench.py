@@ -33,8 +33,9 @@ METRIC = "w4 GEMV eff. HBM GB/s; w4 GEMM/MoE TFLOP/s; both as % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 600e6  # > 2 x 256 MB Infinity Cache
-# Untimed settling run before each compute-bound measurement: the clocks drop
-# to a sustained level under MFMA load within a fraction of a second.
+# Untimed settling run before each measurement (after the W warmup steps):
+# the clocks reach their sustained level under the measured load within a
+# fraction of a second.
 SETTLE_S = 0.5
 KERNEL_GEMV = "gemv_w4_chunked_kernel<64,1,8>"  # the K = 2048 vocabulary-head launch
 
@@ -176,7 +177,7 @@ def bench_gemv(args, dev):
         ql.qlinear_gemv(Wc[0], x, ys[0])
         ql.qlinear_gemv(Wc[1], x, ys[1])
 
-    ms = timed_steps(step, args.steps, args.warmup)
+    ms = timed_steps(step, args.steps, args.warmup, settle_s=SETTLE_S)
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launch_bytes = [w4_bytes(K, N) + 2 * K + 2 * N for N in Ns]
     # Each matrix alone: back-to-back launches with rotation.  The vocabulary
@@ -186,7 +187,7 @@ def bench_gemv(args, dev):
     kern_ms = []
     for j in range(2):
         kern_ms.append(timed_steps(lambda i, j=j: ql.qlinear_gemv(Ws[i % copies][j], x, ys[j]),
-                                   args.steps, args.warmup))
+                                   args.steps, args.warmup, settle_s=SETTLE_S / 2))
     kern_ms = np.asarray(kern_ms)
     avg_launch_ms = kern_ms[1]
     avg_launch_bytes = launch_bytes[1]

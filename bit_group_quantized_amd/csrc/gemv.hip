@@ -155,9 +155,60 @@ gemv_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
 // and adds the partner's copy of them, so R rows cost R-1 shuffles, not
 // R*log2(TPR).
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// v_permlane32_swap on (a, b): lanes 0-31 get a's two halves, lanes 32-63
+// b's; their sum is a's cross-half total in the lower half of the wave and
+// b's in the upper half.  v_permlane16_swap does the same for pairs of
+// 16-lane rows (even rows end with a, odd rows with b).
+__device__ __forceinline__ float swap_add32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Whole-wave (64-lane team) row reduction: every lane holds partials of the
+// same R rows; afterwards lane l holds the total of row l / (64 / R).  The
+// halving steps across 32- and 16-lane rows exchange whole rows with the
+// permlane swaps (no selects); inside 16-lane rows DPP pairs lane i with
+// 15 - i, then 7 - i, then the quad permutations finish each group.
+template <int R>
+__device__ __forceinline__ float reduce_rows64(const float (&v)[R], int lane, int& row) {
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8, "1, 2, 4 or 8 rows");
+    constexpr int R1 = (R > 1) ? R / 2 : 1;
+    float a[R1];
+#pragma unroll
+    for (int i = 0; i < R1; ++i) a[i] = (R > 1) ? swap_add32(v[i], v[i + R1]) : swap_add32(v[0], v[0]);
+    constexpr int R2 = (R1 > 1) ? R1 / 2 : 1;
+    float b[R2];
+#pragma unroll
+    for (int i = 0; i < R2; ++i) b[i] = (R1 > 1) ? swap_add16(a[i], a[i + R2]) : swap_add16(a[0], a[0]);
+    float t;
+    if constexpr (R2 > 1) {
+        const bool hi8 = (lane & 8) != 0;  // lanes 8-15 of a 16-lane row keep b[1]
+        t = (hi8 ? b[1] : b[0]) + dpp_mov<0x140>(hi8 ? b[0] : b[1]);  // row_mirror
+    } else {
+        t = b[0] + dpp_mov<0x140>(b[0]);
+    }
+    t += dpp_mov<0x141>(t);  // row_half_mirror
+    t += dpp_mov<0x4E>(t);   // quad_perm [2,3,0,1]
+    t += dpp_mov<0xB1>(t);   // quad_perm [1,0,3,2]
+    row = lane / (64 / R);
+    return t;
+}
+
 template <int TPR, int R>
 __device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
     static_assert(R <= TPR, "each row needs its own lane after the halving steps");
+    if constexpr (TPR == 64 && (R == 1 || R == 2 || R == 4 || R == 8)) return reduce_rows64<R>(v, lr, row);
     int base = 0;
 #pragma unroll
     for (int off = TPR / 2, cnt = R; off >= 1; off >>= 1) {

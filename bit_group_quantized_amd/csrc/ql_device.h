@@ -108,14 +108,16 @@ __device__ __forceinline__ XPairs make_xpairs(u32x4 xw) {
 // Sum of the pair entries times 1024 (the constant of the dot-product form),
 // and the plain sum of the eight activations (for the bias term).
 __device__ __forceinline__ void xpairs_consts(const XPairs& r, u32x4 xw, float& c, float& xs) {
+    // Sums of fp16 values as dot products with (1, 1): exact products, fp32 sums.
+    const f16x2 one2 = {(f16)1.0f, (f16)1.0f};
     float sp = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sp += (float)r.p[i].x + (float)r.p[i].y;
+    for (int i = 0; i < 4; ++i) sp = dot2(r.p[i], one2, sp);
     c = 1024.0f * sp;
+    const f16x2 h[4] = {as_f16x2(xw.x), as_f16x2(xw.y), as_f16x2(xw.z), as_f16x2(xw.w)};
     float s = 0.f;
-    f16x2 h[4] = {as_f16x2(xw.x), as_f16x2(xw.y), as_f16x2(xw.z), as_f16x2(xw.w)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s += (float)h[i].x + (float)h[i].y;
+    for (int i = 0; i < 4; ++i) s = dot2(h[i], one2, s);
     xs = s;
 }
 

@@ -168,8 +168,7 @@ def alloc_route_outputs(T: int, E: int, topk: int, device):
         "offsets": torch.empty((E + 1,), **i32),
         "sorted_assign": torch.empty((T * topk,), **i32),
         "pos": torch.empty((T * topk,), **i32),
-        # Zero-filled once, as the library requires before first use.
-        "workspace": torch.zeros((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
+        "workspace": torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
     }
 
 

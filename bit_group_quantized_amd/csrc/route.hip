@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kChunk = kRouteChunkTokens;
 constexpr int kMaskWords = kChunk / 32;
-constexpr int kTicketWord = 4;  // header word of the decode-route ticket
 constexpr int kRouterParts = 32;     // row-parallel router: D split in 32 slices
 constexpr int kRouterMfmaParts = kRouterMfmaSplit;  // MFMA router: K split
 
@@ -550,37 +549,6 @@ route_small_kernel(const float* __restrict__ partials, const float* __restrict__
                                    sorted_assign, pos, ws_header, tiles, row_info, assign_info);
 }
 
-// The whole small-T route in one launch: every block computes one router
-// partial (D slice p, token t); the block that finishes last (a ticket in
-// the workspace header, left at zero for the next call) then runs the top-k
-// and the dispatch of all tokens.
-template <int EPL, bool VEC>
-__global__ void __launch_bounds__(256)
-route_decode_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr, int D,
-                    float* __restrict__ partials, const float* __restrict__ bias,
-                    float* __restrict__ logits_out, int T, int E, int topk,
-                    int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
-                    int* __restrict__ offsets, int* __restrict__ sorted_assign,
-                    int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
-                    int2* __restrict__ row_info, int2* __restrict__ assign_info) {
-    if constexpr (VEC)
-        router_partial_vec_body(H, Wr, partials, D, E);
-    else
-        router_partial_body(H, Wr, partials, D, E);
-    __shared__ int s_last;
-    __threadfence();  // this block's partials are visible device-wide before its ticket
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int nblocks = gridDim.x * gridDim.y;
-        s_last = atomicAdd(&ws_header[kTicketWord], 1) == nblocks - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // acquire: every other block's partials
-    route_small_body<EPL, true>(partials, bias, logits_out, T, E, topk, ids, gates, counts, offsets,
-                                sorted_assign, pos, ws_header, tiles, row_info, assign_info);
-    if (threadIdx.x == 0) ws_header[kTicketWord] = 0;  // every block has taken its ticket
-}
 
 template <int EPL>
 int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStream_t st) {
@@ -599,34 +567,6 @@ int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStr
                            a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
                            a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
-}
-
-template <int EPL, bool VEC>
-int launch_decode(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
-    float* partials = reinterpret_cast<float*>(a.ws + L.partials);
-    float* logits = reinterpret_cast<float*>(a.ws + L.logits);
-    int* hdr = reinterpret_cast<int*>(a.ws + L.header);
-    int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
-    int2* rinfo = reinterpret_cast<int2*>(a.ws + L.row_info);
-    int2* ainfo = reinterpret_cast<int2*>(a.ws + L.assign_info);
-    hipLaunchKernelGGL((route_decode_kernel<EPL, VEC>), dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
-                       a.Wr, a.D, partials, a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
-                       a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
-    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
-}
-
-template <bool VEC>
-int launch_decode_v(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
-    const int epl = (a.E + 63) / 64;
-    if (epl <= 1) return launch_decode<1, VEC>(a, L, st);
-    if (epl <= 2) return launch_decode<2, VEC>(a, L, st);
-    if (epl <= 4) return launch_decode<4, VEC>(a, L, st);
-    if (epl <= 8) return launch_decode<8, VEC>(a, L, st);
-    return launch_decode<16, VEC>(a, L, st);
-}
-
-int launch_decode_any(const RouteArgs& a, const MoeWorkspace& L, hipStream_t st) {
-    return (a.E % 8 == 0) ? launch_decode_v<true>(a, L, st) : launch_decode_v<false>(a, L, st);
 }
 
 int launch_small_any(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStream_t st) {
@@ -733,7 +673,6 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
         const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st);
         if (rc != QL_OK) return rc;
     } else {
-        if (a.T <= kRouterSmallT) return launch_decode_any(a, L, st);
         if (a.E % 8 == 0)
             hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st,
                                a.H, a.Wr, partials, a.D, a.E);
@@ -741,6 +680,7 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
             hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
                                a.Wr, partials, a.D, a.E);
         if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
+        if (a.T <= kRouterSmallT) return launch_small_any(a, L, true, st);
     }
     launch_topk(partials, L.nparts, a, logits, st);
     if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;

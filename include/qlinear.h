@@ -151,10 +151,8 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
  * moe_workspace_bytes - bytes of device workspace that moe_route and
  * moe_dispatch need for T tokens, E experts, top-k; 0 on invalid input.
  *
- * The workspace must be zero-filled once before its first use (e.g. with
- * hipMemset when it is allocated): for T <= 16 moe_route keeps a
- * completion counter in it, which every call leaves at zero again.  A
- * workspace may be reused by any sequence of calls and sizes that fit it.
+ * The workspace needs no initialization; it may be reused by any sequence
+ * of calls and sizes that fit it.
  *
  * Workspace layout (offsets in bytes; readable by the caller after the
  * stream has completed):
@@ -163,8 +161,7 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
  *   [8, 12)    int32 error flag  nonzero if the ids violated the contract of
  *                                 moe_dispatch (out of range or repeated)
  *   [12, 16)   int32 num_tall    tall tiles, listed first in the map
- *   [16, 20)   int32             internal counter (zero between calls)
- *   [20, 32)   reserved
+ *   [16, 32)   reserved
  *   [32, ...)  int32 tiles[max_tiles][4] = {expert, first row, rows, height},
  *              max_tiles = (T*topk)/QL_MOE_TILE_ROWS + E.
  *              Load-matched map ([PPLX] "使瓦片大小与专家负载相匹配"): an

@@ -143,9 +143,8 @@ def test_route_prefill(T, skewed, seed):
 
 
 def test_route_workspace_reuse_across_sizes():
-    """One zero-filled workspace serves a sequence of routes of different
-    sizes: the small-T route's completion counter is back at zero after
-    every call, and every call matches the oracle."""
+    """One workspace serves a sequence of routes of different sizes (small-T
+    and many-token paths alternating); every call matches the oracle."""
     import torch
     say("route workspace reuse T = 1, 16, 5, 300, 1, 9")
     w = synth.moe_weights(3)
@@ -159,7 +158,6 @@ def test_route_workspace_reuse_across_sizes():
         out["pos"] = big["pos"][: T * 8]
         ql.moe_route(t(tok["H"]), t(w["Wr"]), t(tok["logit_bias"]), 8, out)
         torch.cuda.synchronize()
-        assert int(host(big["workspace"]).view(np.int32)[4]) == 0
         exact, near, ids_ref = _check_route(out, tok["H"], w["Wr"], tok["logit_bias"], 8, T, 256)
         if exact:
             _check_dispatch(out, ids_ref, 256, T, 8)

@@ -239,8 +239,9 @@ int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk,
  *        row order; Y fp16 [rows][D].
  *   op = QL_OP_DOWN_COMBINE (T <= QL_DECODE_MAX_T): as QL_OP_DOWN, but
  *        Y fp16 [T][D] = sum_j topk_gates[t][j] * (row assign_pos[t*topk+j])
- *        (+ the shared row of t), summed in fp32 in the order j = 0..topk-1
- *        then shared.
+ *        (+ the shared row of t), accumulated in fp32 in a fixed order (for
+ *        each K slice over j = 0..topk-1 then the shared row, then across
+ *        K slices), so repeated calls give identical bits.
  * topk_gates and assign_pos are read only by QL_OP_DOWN_COMBINE (may be
  * NULL otherwise).  `workspace` is the one filled by moe_route or
  * moe_dispatch for the same T, E, topk.

@@ -236,6 +236,30 @@ def bench_gemm(args, dev):
     return out
 
 
+def bench_few_rows(args, dev):
+    """Few activation rows (verify-sized groups): the weight-stationary
+    qlinear_gemm_few_rows next to the tiled qlinear_gemm, K = 2048, N = 8192."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K, N = 2048, 8192
+    case = synth.gemm_case(0, 128, K, N)
+    W = dev_w4(case["W"], dev)
+    Xall = torch.from_numpy(case["X"]).to(dev)
+    out = {}
+    for M in (1, 4, 16, 32, 64, 128):
+        X = Xall[:M].contiguous()
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        flops = 2.0 * M * N * K
+        row = {}
+        for name, fn in (("few_rows", ql.qlinear_gemm_few_rows), ("tiled", ql.qlinear_gemm)):
+            ms = timed_steps(lambda i, fn=fn: fn(W, X, Y), 50, 5, settle_s=SETTLE_S / 5)
+            row[name] = {"us": float(ms * 1e3), "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                         "weight_GB/s": (w4_bytes(K, N)) / (ms * 1e-3) / 1e9}
+        out[f"M={M}"] = row
+    return out
+
+
 def moe_dev_weights(w, dev):
     import torch
     return {"Wr": torch.from_numpy(w["Wr"]).to(dev), "gate_up": dev_w4(w["gate_up"], dev),
@@ -463,6 +487,8 @@ def main():
         if args.workload in ("all", "gemm"):
             log("bench: GEMM")
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
+            log("bench: few-row GEMM")
+            wl["few_rows_gemm_K2048_N8192"] = bench_few_rows(args, dev)
         if args.workload in ("all", "moe_decode", "moe_prefill"):
             w = synth.moe_weights(0)
             if args.workload in ("all", "moe_decode"):

@@ -55,6 +55,7 @@ _SIGS = {
     "qlinear_pack": (ctypes.c_int, [_P, _I32, _I32, _P, _P]),
     "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemm_few_rows": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "moe_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "ql_moe_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
@@ -145,6 +146,19 @@ def qlinear_gemm(W: dict, X, Y=None, stream=None):
         Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
     w = make_w4(W)
     _check("qlinear_gemm", lib().qlinear_gemm(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def qlinear_gemm_few_rows(W: dict, X, Y=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 . dequant(W), weight-stationary kernel
+    for few rows (K in 512, 1024, 2048)."""
+    import torch
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
+    w = make_w4(W)
+    _check("qlinear_gemm_few_rows",
+           lib().qlinear_gemm_few_rows(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
     return Y
 
 

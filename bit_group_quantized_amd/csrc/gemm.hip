@@ -447,6 +447,116 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     }
 }
 
+// ---------------------------------------------------------------------------
+// Few-row GEMM, weight-stationary.  A workgroup of 8 waves owns 32 output
+// columns; wave w owns K range [w*K/8, (w+1)*K/8) of them (GW groups).  The
+// wave dequantizes its 32 x (K/8) weight block once into MFMA operand
+// registers (fp16 s*q + b, one rounding, as everywhere else) and then
+// streams the activation rows past it, 32 rows per chunk (the next chunk's
+// fragments load while the current one runs): they come straight from
+// global memory (small and shared by every workgroup, so they stay in L2),
+// MFMA 32x32x16 with the activations as the first operand, and the 8 K
+// partials of each output are summed in LDS in wave order (a fixed order,
+// so results are deterministic).  Every weight byte is read and dequantized
+// exactly once; the activations are read once per 32 output columns, which
+// is what bounds this kernel as M grows (the tiled GEMM reads them once per
+// 256 columns), so it is the choice for few rows only.
+// ---------------------------------------------------------------------------
+constexpr int kWsCols = 32;  // output columns per workgroup
+constexpr int kWsWaves = 8;  // K slices per workgroup
+
+template <int GW>
+__global__ void __launch_bounds__(64 * kWsWaves)
+gemm_ws_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+               const uint16_t* __restrict__ sc, const uint16_t* __restrict__ bi,
+               uint16_t* __restrict__ Y, int64_t M, int K, int N) {
+    __shared__ __align__(16) float red[kWsWaves][kWsCols][32 + 4];  // [wave][col][row]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int fl = lane & 31, fh = lane >> 5;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int n0 = blockIdx.x * kWsCols;
+    const int col = min(n0 + fl, N - 1);
+    const int g0 = wave * GW;  // first group of this wave
+
+    // Weight block: group g, slice s -> 8 fp16 weights of k = 64(g0+g) + 32h + 8s + v.
+    f16x8 wf[GW][4];
+    {
+        u32x4 cw[GW];
+        uint16_t sv[GW], bv[GW];
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+            cw[g] = ld_stream_u32x4(qw + (size_t)col * wpr + (g0 + g) * 8 + 4 * fh);
+            sv[g] = sc[(size_t)col * G + g0 + g];
+            bv[g] = bi[(size_t)col * G + g0 + g];
+        }
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+            const f16 s1 = __builtin_bit_cast(f16, sv[g]), b1 = __builtin_bit_cast(f16, bv[g]);
+            const f16x2 s2 = {s1, s1}, b2 = {b1, b1};
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) wf[g][sl] = dequant_word(cw[g][sl], s2, b2);
+        }
+    }
+
+    const int64_t nchunks = (M + 31) / 32;
+    auto load_x = [&](int64_t c, f16x8 (&xf)[GW][4]) {
+        const int64_t row = min(c * 32 + fl, M - 1);
+        const uint16_t* xr = X + row * K + (size_t)g0 * kGroup + 32 * fh;
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+                xf[g][sl] = __builtin_bit_cast(f16x8, ld_u32x4(xr + g * kGroup + 8 * sl));
+    };
+    f16x8 xa[GW][4], xb[GW][4];
+    auto chunk = [&](int64_t c, f16x8 (&xf)[GW][4], f16x8 (&xn)[GW][4]) {
+        if (c + 1 < nchunks) load_x(c + 1, xn);  // next chunk's activations in flight
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[g][sl], wf[g][sl], acc, 0, 0, 0);
+        // acc[r]: row 8(r/4) + 4h + r%4 of the chunk, column l%32.
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(&red[wave][fl][8 * q + 4 * fh]) =
+                f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        __syncthreads();
+        // 1024 outputs of the chunk, two adjacent columns of one row per thread.
+        const int orow = tid >> 4, ocol = (tid & 15) * 2;
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWsWaves; ++w) {
+            s0 += red[w][ocol][orow];
+            s1 += red[w][ocol + 1][orow];
+        }
+        const int64_t m = c * 32 + orow;
+        const int n = n0 + ocol;
+        if (m < M) {
+            uint16_t* yp = Y + m * N + n;
+            if (n + 1 < N && ((N & 1) == 0) && ((uintptr_t)Y & 3) == 0) {
+                *reinterpret_cast<uint32_t*>(yp) = (uint32_t)f2h(s0) | ((uint32_t)f2h(s1) << 16);
+            } else {
+                if (n < N) yp[0] = f2h(s0);
+                if (n + 1 < N) yp[1] = f2h(s1);
+            }
+        }
+        __syncthreads();  // red is rewritten by the next chunk
+    };
+    load_x(0, xa);
+    int64_t c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        chunk(c, xa, xb);
+        chunk(c + 1, xb, xa);
+    }
+    if (c < nchunks) chunk(c, xa, xb);
+}
+
 // Dense prefill GEMM and the router GEMM.
 template <int WM, int WN, int WGM, int WGN, int MODE>
 __global__ void __launch_bounds__(64 * WGM * WGN)
@@ -605,6 +715,30 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     using TL = Tile<2, 4, 2, 2>;
     if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;
     return launch_t<2, 4, 2, 2, MODE_DENSE>(p, grid, st);
+}
+
+bool gemm_ws_supported(int K) { return K == 512 || K == 1024 || K == 2048; }
+
+int launch_gemm_ws(const GemmArgs& a, hipStream_t st) {
+    const dim3 grid((unsigned)((a.N + kWsCols - 1) / kWsCols));
+    const dim3 block(64 * kWsWaves);
+    switch (a.K / (kGroup * kWsWaves)) {
+        case 1:
+            hipLaunchKernelGGL((gemm_ws_kernel<1>), grid, block, 0, st, a.X, a.qweight, a.scales,
+                               a.biases, a.Y, a.M, a.K, a.N);
+            break;
+        case 2:
+            hipLaunchKernelGGL((gemm_ws_kernel<2>), grid, block, 0, st, a.X, a.qweight, a.scales,
+                               a.biases, a.Y, a.M, a.K, a.N);
+            break;
+        case 4:
+            hipLaunchKernelGGL((gemm_ws_kernel<4>), grid, block, 0, st, a.X, a.qweight, a.scales,
+                               a.biases, a.Y, a.M, a.K, a.N);
+            break;
+        default:
+            return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 constexpr int kRouterSplit = kRouterMfmaSplit;

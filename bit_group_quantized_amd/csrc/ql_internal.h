@@ -33,6 +33,8 @@ struct GemmArgs {
     int K, N;
 };
 int launch_gemm(const GemmArgs& a, hipStream_t st);
+bool gemm_ws_supported(int K);                          // few-row GEMM shapes
+int launch_gemm_ws(const GemmArgs& a, hipStream_t st);  // few-row GEMM (weight-stationary)
 
 int launch_pack(const uint8_t* codes, int N, int K, uint32_t* qweight, hipStream_t st);
 

@@ -148,6 +148,23 @@ int qlinear_gemv(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream);
 int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 
 /*
+ * qlinear_gemm_few_rows - Y = X . dequant(W) for few activation rows: the
+ * verify-sized groups and small expert batches the pages discuss between
+ * the single-row and the many-row path ([PPLX] "使瓦片大小与专家负载相匹配",
+ * tile choice against row count; "优化单行权重路径").  Weight-stationary:
+ * every weight is read and dequantized once and kept in registers while all
+ * M rows stream past it, so the cost grows slowly with M; faster than
+ * qlinear_gemm up to a few hundred rows (measured crossover: see DESIGN).
+ *   X fp16 [M][K], Y fp16 [M][N]; fp16 dequantized weights, fp32 accumulation
+ *   split over 8 K slices summed in a fixed order: deterministic, but its
+ *   rounding differs from qlinear_gemm's (which does not split K).
+ * Limits: K in {512, 1024, 2048}.
+ * Errors: as qlinear_gemm; UNSUPPORTED_SHAPE for other K.
+ */
+int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y,
+                          void* stream);
+
+/*
  * moe_workspace_bytes - bytes of device workspace that moe_route and
  * moe_dispatch need for T tokens, E experts, top-k; 0 on invalid input.
  *

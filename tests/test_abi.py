@@ -72,6 +72,16 @@ def test_gemm_validation(L):
     assert f(ctypes.byref(_w()), None, 4, A16, None) == INVALID
 
 
+def test_gemm_few_rows_validation(L):
+    f = L.qlinear_gemm_few_rows
+    assert f(ctypes.byref(_w(K=2048)), A16, -1, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=2048)), A16, 0, A16, None) == OK  # empty
+    assert f(ctypes.byref(_w(K=4096)), A16, 4, A16, None) == SHAPE  # K outside {512, 1024, 2048}
+    assert f(ctypes.byref(_w(K=192)), A16, 4, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(K=2048)), A16 + 2, 4, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w(K=2048)), None, 4, A16, None) == INVALID
+
+
 def test_pack_validation(L):
     f = L.qlinear_pack
     assert f(A16, 4, 12, A16, None) == SHAPE

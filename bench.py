@@ -237,26 +237,42 @@ def bench_gemm(args, dev):
 
 
 def bench_few_rows(args, dev):
-    """Few activation rows (verify-sized groups): the weight-stationary
-    qlinear_gemm_few_rows next to the tiled qlinear_gemm, K = 2048, N = 8192."""
+    """Few activation rows (verify-sized groups, lightly loaded experts): the
+    weight-stationary qlinear_gemm_few_rows next to the tiled qlinear_gemm
+    (and qlinear_gemv at one row).  Calls are replayed from a HIP graph (the
+    per-call Python path is slower than these kernels) over enough weight
+    copies that more than 256 MB pass between two uses of one copy, so the
+    weights come from HBM as they would layer after layer."""
     import torch
     import bit_group_quantized_amd as ql
     import synth
-    K, N = 2048, 8192
-    case = synth.gemm_case(0, 128, K, N)
-    W = dev_w4(case["W"], dev)
-    Xall = torch.from_numpy(case["X"]).to(dev)
     out = {}
-    for M in (1, 4, 16, 32, 64, 128):
-        X = Xall[:M].contiguous()
-        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-        flops = 2.0 * M * N * K
-        row = {}
-        for name, fn in (("few_rows", ql.qlinear_gemm_few_rows), ("tiled", ql.qlinear_gemm)):
-            ms = timed_steps(lambda i, fn=fn: fn(W, X, Y), 50, 5, settle_s=SETTLE_S / 5)
-            row[name] = {"us": float(ms * 1e3), "TFLOP/s": flops / (ms * 1e-3) / 1e12,
-                         "weight_GB/s": (w4_bytes(K, N)) / (ms * 1e-3) / 1e9}
-        out[f"M={M}"] = row
+    for K, N in ((2048, 8192), (2048, 1024), (512, 2048)):
+        case = synth.gemm_case(0, 256, K, N)
+        W0 = dev_w4(case["W"], dev)
+        ncopy = max(2, -(-300_000_000 // w4_bytes(K, N)))
+        Ws = [W0] + [clone_w4(W0) for _ in range(ncopy - 1)]
+        Xall = torch.from_numpy(case["X"]).to(dev)
+        shape = {}
+        for M in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+            X = Xall[:M].contiguous()
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            flops = 2.0 * M * N * K
+            fns = [("few_rows", ql.qlinear_gemm_few_rows), ("tiled", ql.qlinear_gemm)]
+            if M == 1:
+                fns.append(("gemv", lambda W, X, Y: ql.qlinear_gemv(W, X[0], Y[0])))
+            row = {}
+            for name, fn in fns:
+                step = (lambda i, fn=fn: fn(Ws[i % ncopy], X, Y))
+                for i in range(2 * ncopy):
+                    step(i)
+                ms = graph_time(step, ncopy, 20)
+                row[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+                             "weight_GB/s": round(w4_bytes(K, N) / (ms * 1e-3) / 1e9, 1)}
+            shape[f"M={M}"] = row
+        out[f"K{K}_N{N}"] = shape
+        del Ws, W0
+        torch.cuda.empty_cache()
     return out
 
 
@@ -488,7 +504,7 @@ def main():
             log("bench: GEMM")
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
             log("bench: few-row GEMM")
-            wl["few_rows_gemm_K2048_N8192"] = bench_few_rows(args, dev)
+            wl["few_rows_gemm"] = bench_few_rows(args, dev)
         if args.workload in ("all", "moe_decode", "moe_prefill"):
             w = synth.moe_weights(0)
             if args.workload in ("all", "moe_decode"):

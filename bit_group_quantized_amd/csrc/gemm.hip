@@ -705,16 +705,24 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
         grid = dim3((unsigned)((gn * gm + 7) / 8 * 8));
         return true;
     };
+    // Tile shape from a static table keyed by the number of 128 x 128 output
+    // tiles (measured on MI355X for K = 512 and 2048, N = 1024 to 8192, M =
+    // 128 to 4096): the largest tile that still gives the 256 CUs enough
+    // workgroups.  Every shape accumulates each output element over the same
+    // K steps in the same order, so the choice never changes a result bit.
+    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
     dim3 grid;
-    if (a.M >= 2048) {
-        // 256 x 256 tiles, 8 waves (two per SIMD) of 128 x 64.
-        using TL = Tile<4, 2, 2, 4>;
-        if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;
-        return launch_t<4, 2, 2, 4, MODE_DENSE>(p, grid, st);
-    }
-    using TL = Tile<2, 4, 2, 2>;
-    if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;
-    return launch_t<2, 4, 2, 2, MODE_DENSE>(p, grid, st);
+#define QL_DENSE(A, B, C, D)                                                       \
+    do {                                                                           \
+        using TL = Tile<A, B, C, D>;                                               \
+        if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;      \
+        return launch_t<A, B, C, D, MODE_DENSE>(p, grid, st);                      \
+    } while (0)
+    if (t128 > 512) QL_DENSE(4, 2, 2, 4);  // 256 x 256, 8 waves of 128 x 64
+    if (t128 > 256) QL_DENSE(2, 2, 2, 4);  // 128 x 256, 8 waves of 64 x 64
+    if (t128 > 128) QL_DENSE(2, 2, 2, 2);  // 128 x 128, 4 waves of 64 x 64
+    QL_DENSE(1, 2, 2, 2);                  // 64 x 128, 4 waves of 32 x 64
+#undef QL_DENSE
 }
 
 bool gemm_ws_supported(int K) { return K == 512 || K == 1024 || K == 2048; }

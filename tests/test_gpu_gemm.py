@@ -13,8 +13,11 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("M,K,N,seed", [
     (1, 2048, 512, 0), (7, 512, 200, 1), (256, 2048, 8192, 0), (300, 2048, 1000, 2),
     (129, 64, 257, 3), (1024, 1024, 640, 4), (2048, 512, 384, 5), (2500, 192, 300, 6),
+    (700, 1024, 3000, 7), (1500, 512, 4000, 8), (2100, 256, 4100, 9),
 ])
 def test_gemm_matches_oracle(M, K, N, seed):
+    """Ragged M and N in every tile class of the shape table (64 x 128,
+    128 x 128, 128 x 256 and 256 x 256 tiles)."""
     import torch
     say(f"gemm M={M} K={K} N={N} seed={seed}")
     case = synth.gemm_case(seed, M, K, N)
@@ -41,14 +44,15 @@ def test_gemm_prefill_sampled_rows(M):
 
 def test_gemm_row_invariance():
     """Row m of the output depends only on row m of X: bit-identical across
-    M in {1, 256, 1024, 4096} (no split over K)."""
+    M in {1, 1000, 2048, 4096}, which fall in the four tile classes of the
+    shape table at N = 4096 (no split over K, same accumulation order)."""
     import torch
-    K, N = 2048, 1024
+    K, N = 2048, 4096
     case = synth.gemm_case(5, 4096, K, N)
     W = w4_dev(case["W"])
     Xd = t(case["X"])
     full = host(ql.qlinear_gemm(W, Xd)).view(np.uint16)
-    for M in (1, 256, 1024):
+    for M in (1, 1000, 2048):
         part = host(ql.qlinear_gemm(W, Xd[:M].contiguous())).view(np.uint16)
         assert np.array_equal(part, full[:M]), f"M={M}"
     torch.cuda.synchronize()

@@ -15,7 +15,8 @@ eye against the pages it cites:
   "使瓦片大小与专家负载相匹配" (matching tile size to expert load),
   "Qwen 创建了三种不同的工作负载形状" (the three workload shapes),
   "优化单行权重路径" (the single-row weight path) and
-  "减少中间状态和流量" (reducing intermediates and traffic);
+  "减少中间状态和流量" (reducing intermediates and traffic) and
+  "将 token 交接保留在 GPU 上" (keeping the token hand-off on the GPU);
 * laya-mlx, "工程调查：这个 MLX 端口还能再快 10× 吗？", section
   "选择性量化" (affine quantization with group size 64).
 
@@ -33,10 +34,12 @@ from .route import (router_logits, softmax, topk_route, histogram,
                     exclusive_scan, stable_permutation, tile_map, load_matched_tile_map,
                     topk_near_ties)
 from .moe import silu, expert_ffn, combine, moe_layer
+from .decode import rms_norm, gemv_rmsnorm, argmax_first, lm_head_token, embed_row
 
 __all__ = [
     "GROUP", "unpack_codes", "pack_codes", "dequantize", "linear", "round_f16",
     "router_logits", "softmax", "topk_route", "histogram", "exclusive_scan",
     "stable_permutation", "tile_map", "load_matched_tile_map", "topk_near_ties",
     "silu", "expert_ffn", "combine", "moe_layer",
+    "rms_norm", "gemv_rmsnorm", "argmax_first", "lm_head_token", "embed_row",
 ]

@@ -165,3 +165,65 @@ def test_moe_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(omoe, attr, mutant)
     monkeypatch.setattr(oracle, attr, mutant)
     assert _fails(MOE_PINS)
+
+
+import oracle.decode as odec
+from tests import test_oracle_decode as td
+
+DECODE_PINS = [td.test_rms_norm_hand_fixture, td.test_rms_norm_invariants,
+               td.test_gemv_rmsnorm_hand_fixture, td.test_gemv_rmsnorm_rounds_the_normalized_row_once,
+               td.test_argmax_hand_and_bruteforce, td.test_lm_head_hand_fixture,
+               td.test_lm_head_one_hot_selects_a_weight_column, td.test_embed_hand_fixture,
+               td.test_embed_matches_digit_decode]
+
+
+def _rms_no_sqrt(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.mean(x * x) + eps) * np.asarray(gamma, np.float64)
+
+
+def _rms_eps_outside(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.sqrt(np.mean(x * x)) + eps) * np.asarray(gamma, np.float64)
+
+
+def _rms_sum_not_mean(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x) + eps) * np.asarray(gamma, np.float64)
+
+
+def _rms_no_gamma(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x) + eps)
+
+
+def _argmax_last(v):
+    v = np.asarray(v, np.float64)
+    return int(np.flatnonzero(v == v.max())[-1])
+
+
+_ORIG_EMBED = odec.embed_row
+
+
+def _embed_next_row(E, token):
+    return _ORIG_EMBED(E, (token + 1) % E["N"])
+
+
+def _gemv_rmsnorm_unrounded(x, gamma, eps, W):
+    u = odec.rms_norm(x, gamma, eps)
+    return odec.linear(u[None, :], W)[0], odec.round_f16(u)
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("rms_norm", _rms_no_sqrt),
+    ("rms_norm", _rms_eps_outside),
+    ("rms_norm", _rms_sum_not_mean),
+    ("rms_norm", _rms_no_gamma),
+    ("argmax_first", _argmax_last),
+    ("embed_row", _embed_next_row),
+    ("gemv_rmsnorm", _gemv_rmsnorm_unrounded),
+])
+def test_decode_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(odec, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant)
+    assert _fails(DECODE_PINS)

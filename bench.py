@@ -474,7 +474,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(this library has no multi-GPU path; see DESIGN.md for how it would shard)",
+              "(this library has no multi-GPU path: it runs on one GPU's share of the work)",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -56,6 +56,10 @@ _SIGS = {
     "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemm_few_rows": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemv_rmsnorm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, ctypes.c_float, _P, _P]),
+    "qlinear_gemv_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
+    "qlinear_gemv_argmax": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "qlinear_embed_token": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "moe_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "ql_moe_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
@@ -136,6 +140,50 @@ def qlinear_gemv(W: dict, x, y=None, stream=None):
     w = make_w4(W)
     _check("qlinear_gemv", lib().qlinear_gemv(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
     return y
+
+
+def qlinear_gemv_rmsnorm(W: dict, x, gamma, eps: float, y=None, stream=None):
+    """y [N] fp16 = fp16(rmsnorm(x [K], gamma [K], eps)) . dequant(W)."""
+    import torch
+    if y is None:
+        y = torch.empty((int(W["N"]),), dtype=torch.float16, device=x.device)
+    w = make_w4(W)
+    _check("qlinear_gemv_rmsnorm", lib().qlinear_gemv_rmsnorm(
+        ctypes.byref(w), _ptr(x), _ptr(gamma), float(eps), _ptr(y), _stream(stream)))
+    return y
+
+
+def gemv_argmax_workspace(N: int, device):
+    """Workspace tensor for qlinear_gemv_argmax with N outputs."""
+    import torch
+    nbytes = lib().qlinear_gemv_argmax_workspace_bytes(int(N))
+    return torch.empty((max(nbytes, 8) // 8,), dtype=torch.int64, device=device)
+
+
+def qlinear_gemv_argmax(W: dict, x, token=None, logits=None, workspace=None, stream=None):
+    """token int32 [1] (device) = index of the largest logit of x . dequant(W);
+    logits fp16 [N] are written too when given."""
+    import torch
+    if token is None:
+        token = torch.empty((1,), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = gemv_argmax_workspace(int(W["N"]), x.device)
+    w = make_w4(W)
+    _check("qlinear_gemv_argmax", lib().qlinear_gemv_argmax(
+        ctypes.byref(w), _ptr(x), _ptr(logits), _ptr(token), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return token
+
+
+def qlinear_embed_token(E: dict, token, x=None, stream=None):
+    """x [K] fp16 = row token[0] (device int32) of the w4 table E."""
+    import torch
+    if x is None:
+        x = torch.empty((int(E["K"]),), dtype=torch.float16, device=token.device)
+    w = make_w4(E)
+    _check("qlinear_embed_token", lib().qlinear_embed_token(
+        ctypes.byref(w), _ptr(token), _ptr(x), _stream(stream)))
+    return x
 
 
 def qlinear_gemm(W: dict, X, Y=None, stream=None):

@@ -1,6 +1,7 @@
 // C ABI of the library: argument validation on the host, then asynchronous
 // launches on the caller's stream.  See include/qlinear.h for the contract
 // of every entry point.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -87,6 +88,56 @@ int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t
     if (!aligned(X, 16) || !aligned(Y, 2)) return QL_ERR_MISALIGNED;
     ql::GemmArgs a{W->qweight, W->scales, W->biases, X, Y, M, W->K, W->N};
     return ql::launch_gemm_ws(a, as_stream(stream));
+}
+
+int qlinear_gemv_rmsnorm(const ql_w4* W, const uint16_t* x, const uint16_t* gamma, float eps,
+                         uint16_t* y, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (!ql::gemv_fused_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return QL_ERR_INVALID_ARG;
+    if (W->N == 0) return QL_OK;
+    if (!x || !gamma || !y) return QL_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemvArgs a{W->qweight, W->scales, W->biases, x, y, W->K, W->N};
+    a.gamma = gamma;
+    a.eps = eps;
+    return ql::launch_gemv_rmsnorm(a, as_stream(stream));
+}
+
+size_t qlinear_gemv_argmax_workspace_bytes(int64_t N) {
+    if (N <= 0 || N > 0x7fffffff) return 0;
+    return (size_t)((N + 7) / 8) * 8;
+}
+
+int qlinear_gemv_argmax(const ql_w4* W, const uint16_t* x, uint16_t* logits, int32_t* token,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (!ql::gemv_fused_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N < 1 || !x || !token) return QL_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(token, 4) || (logits && !aligned(logits, 2)))
+        return QL_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < qlinear_gemv_argmax_workspace_bytes(W->N))
+        return QL_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return QL_ERR_MISALIGNED;
+    ql::GemvArgs a{W->qweight, W->scales, W->biases, x, logits, W->K, W->N};
+    a.partials = static_cast<uint64_t*>(workspace);
+    a.token = token;
+    return ql::launch_gemv_argmax(a, as_stream(stream));
+}
+
+int qlinear_embed_token(const ql_w4* E, const int32_t* token, uint16_t* x, void* stream) {
+    if (!E) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(E->qweight, E->scales, E->biases, E->K, E->N, E->group_size);
+    if (rc != QL_OK) return rc;
+    if (E->N < 1 || !token || !x) return QL_ERR_INVALID_ARG;
+    if (!aligned(token, 4) || !aligned(x, 16)) return QL_ERR_MISALIGNED;
+    ql::GemvArgs a{E->qweight, E->scales, E->biases, nullptr, x, E->K, E->N};
+    a.token = const_cast<int32_t*>(token);
+    return ql::launch_embed(a, as_stream(stream));
 }
 
 size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk) {

@@ -231,11 +231,26 @@ __device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
     return v[0];
 }
 
-template <int TPR, int V, int R>
+// Prologue and epilogue variants of the chunked GEMV (the decode steps on
+// either side of a projection; Perplexity, "Optimizing on-device inference
+// for Apple Silicon", sections 减少中间状态和流量 and 将 token 交接保留在 GPU 上):
+//  * GV_RMSNORM: the activation row is RMS-normalized first.  A team of TPR
+//    lanes holds all K activations, so the sum of squares is one team
+//    reduction (pairwise exchanges, so every lane and every team gets the
+//    same bits); each lane then scales its own chunks, x * r * gamma rounded
+//    once to fp16, before pairing them for the dot products.
+//  * GV_ARGMAX: instead of (or besides) the fp16 outputs, each block writes
+//    the largest 64-bit selection key (fp32 output value, then lower row)
+//    of its rows; argmax_finish_kernel reduces those keys to the token id.
+enum { GV_PLAIN = 0, GV_RMSNORM = 1 };
+enum { GV_STORE = 0, GV_ARGMAX = 1 };
+
+template <int TPR, int V, int R, int PRO, int EPI>
 __global__ void __launch_bounds__(256)
 gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                        const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
-                       uint16_t* __restrict__ y, int K, int N) {
+                       uint16_t* __restrict__ y, int K, int N, const uint16_t* __restrict__ gamma,
+                       float eps, uint64_t* __restrict__ partials) {
     constexpr int TEAMS = 64 / TPR;
     const int lane = threadIdx.x & 63;
     const int lr = lane % TPR;
@@ -254,6 +269,13 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
     for (int v = 0; v < V; ++v)
 #pragma unroll
         for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(x + (lr + v * TPR) * 32 + w * 8);
+    u32x4 gr[(PRO == GV_RMSNORM) ? V : 1][4];
+    if constexpr (PRO == GV_RMSNORM) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) gr[v][w] = ld_u32x4(gamma + (lr + v * TPR) * 32 + w * 8);
+    }
     u32x4 cw[R][V];
     uint16_t s[R][V], b[R][V];
 #pragma unroll
@@ -268,6 +290,36 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PRO == GV_RMSNORM) {
+        // Sum of squares: exact fp16 squares, fp32 sums (dot2 with itself).
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                ss = dot2(as_f16x2(xr[v][w].x), as_f16x2(xr[v][w].x), ss);
+                ss = dot2(as_f16x2(xr[v][w].y), as_f16x2(xr[v][w].y), ss);
+                ss = dot2(as_f16x2(xr[v][w].z), as_f16x2(xr[v][w].z), ss);
+                ss = dot2(as_f16x2(xr[v][w].w), as_f16x2(xr[v][w].w), ss);
+            }
+        ss = team_sum<TPR>(ss);
+        const float rinv = 1.0f / __builtin_sqrtf(ss / (float)K + eps);
+        auto scale2 = [&](uint32_t xu, uint32_t gu) {
+            const f16x2 xh = as_f16x2(xu), gh = as_f16x2(gu);
+            const uint32_t lo = f2h(((float)xh[0] * rinv) * (float)gh[0]);
+            const uint32_t hi = f2h(((float)xh[1] * rinv) * (float)gh[1]);
+            return lo | (hi << 16);
+        };
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                xr[v][w].x = scale2(xr[v][w].x, gr[v][w].x);
+                xr[v][w].y = scale2(xr[v][w].y, gr[v][w].y);
+                xr[v][w].z = scale2(xr[v][w].z, gr[v][w].z);
+                xr[v][w].w = scale2(xr[v][w].w, gr[v][w].w);
+            }
+    }
     XPairs xp[V][4];
     float xc[V], xs[V];
 #pragma unroll
@@ -300,7 +352,59 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
     }
     int rsel;
     const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
-    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot);
+    const bool owner = (lr & (TPR / R - 1)) == 0 && row0 + rsel < N;
+    if constexpr (EPI == GV_STORE) {
+        if (owner) y[row0 + rsel] = f2h(tot);
+    } else {
+        if (owner && y) y[row0 + rsel] = f2h(tot);
+        // NaN outputs never win (key 0, the "nothing" key).
+        uint64_t key = (owner && tot == tot) ? logit_key(tot, row0 + rsel) : 0;
+        key = wave_max_u64(key);
+        __shared__ uint64_t wkeys[4];
+        if (lane == 0) wkeys[threadIdx.x >> 6] = key;
+        __syncthreads();
+        if (threadIdx.x == 0) partials[blockIdx.x] = umax64(umax64(wkeys[0], wkeys[1]), umax64(wkeys[2], wkeys[3]));
+    }
+}
+
+// Largest of n block keys -> token id (0 when no output was comparable).
+__global__ void __launch_bounds__(1024)
+argmax_finish_kernel(const uint64_t* __restrict__ partials, int n, int N, int32_t* __restrict__ token) {
+    uint64_t best = 0;
+    for (int i = threadIdx.x; i < n; i += 1024) best = umax64(best, partials[i]);
+    best = wave_max_u64(best);
+    __shared__ uint64_t wkeys[16];
+    if ((threadIdx.x & 63) == 0) wkeys[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t b = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b = umax64(b, wkeys[i]);
+        const int t = (b == 0) ? 0 : key_index(b);
+        token[0] = min(max(t, 0), N - 1);
+    }
+}
+
+// The input row of the token held in device memory: row `token` of a w4
+// embedding table (N tokens, K = hidden width), dequantized to fp16 with one
+// rounding, one 16-byte store per word of 8 codes.  An id outside [0, N)
+// gives a row of zeros and reads no table memory.
+__global__ void __launch_bounds__(256)
+embed_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                const uint16_t* __restrict__ bi, const int32_t* __restrict__ token,
+                uint16_t* __restrict__ x, int K, int N) {
+    const int w = blockIdx.x * 256 + threadIdx.x;
+    if (w >= K / 8) return;
+    const int t = token[0];
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (t >= 0 && t < N) {
+        const int G = K / kGroup;
+        const uint32_t u = qw[(size_t)t * (K / 8) + w];
+        const f16 sv = __builtin_bit_cast(f16, sc[(size_t)t * G + (w >> 3)]);
+        const f16 bv = __builtin_bit_cast(f16, bi[(size_t)t * G + (w >> 3)]);
+        out = __builtin_bit_cast(u32x4, dequant_word(u, f16x2{sv, sv}, f16x2{bv, bv}));
+    }
+    *reinterpret_cast<u32x4*>(x + 8 * (size_t)w) = out;
 }
 
 // ---------------------------------------------------------------------------
@@ -598,13 +702,19 @@ int launch_rows_t(const GroupedArgs& a, hipStream_t st) {
 
 }  // namespace
 
-template <int TPR, int V, int R>
+template <int TPR, int V, int R, int PRO, int EPI>
 int launch_chunked_t(const GemvArgs& a, hipStream_t st) {
     constexpr int ROWS_PER_BLOCK = 4 * (64 / TPR) * R;
+    static_assert(ROWS_PER_BLOCK >= 8, "at most ceil(N / 8) argmax block keys");
     const int blocks = (a.N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-    hipLaunchKernelGGL((gemv_w4_chunked_kernel<TPR, V, R>), dim3(blocks), dim3(256), 0, st,
-                       a.qweight, a.scales, a.biases, a.x, a.y, a.K, a.N);
-    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+    hipLaunchKernelGGL((gemv_w4_chunked_kernel<TPR, V, R, PRO, EPI>), dim3(blocks), dim3(256), 0, st,
+                       a.qweight, a.scales, a.biases, a.x, a.y, a.K, a.N, a.gamma, a.eps, a.partials);
+    if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
+    if constexpr (EPI == GV_ARGMAX) {
+        hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(1024), 0, st, a.partials, blocks, a.N, a.token);
+        if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
+    }
+    return QL_OK;
 }
 
 // Rows per team of the chunked GEMV: 8 rows in flight per wave for large N;
@@ -615,26 +725,50 @@ int launch_chunked_t(const GemvArgs& a, hipStream_t st) {
 constexpr int kGemvRows = QL_GEMV_ROWS;
 constexpr int kGemvMinBlocks = 1024;
 
-template <int TPR, int V>
+template <int TPR, int V, int PRO, int EPI>
 int launch_chunked_r(const GemvArgs& a, hipStream_t st) {
     constexpr int R = (kGemvRows < TPR) ? kGemvRows : TPR;
     const long blocks_big = (a.N + 4L * (64 / TPR) * R - 1) / (4L * (64 / TPR) * R);
-    if (blocks_big >= kGemvMinBlocks || R <= 2) return launch_chunked_t<TPR, V, R>(a, st);
-    return launch_chunked_t<TPR, V, 2>(a, st);
+    if (blocks_big >= kGemvMinBlocks || R <= 2) return launch_chunked_t<TPR, V, R, PRO, EPI>(a, st);
+    return launch_chunked_t<TPR, V, 2, PRO, EPI>(a, st);
+}
+
+// Chunked kernel: K/32 chunks per row spread over TPR lanes, V per lane.
+// QL_ERR_UNSUPPORTED_SHAPE for other K.
+template <int PRO, int EPI>
+int launch_chunked(const GemvArgs& a, hipStream_t st) {
+    switch (a.K) {
+        case 256: return launch_chunked_r<8, 1, PRO, EPI>(a, st);
+        case 512: return launch_chunked_r<16, 1, PRO, EPI>(a, st);
+        case 1024: return launch_chunked_r<32, 1, PRO, EPI>(a, st);
+        case 2048: return launch_chunked_r<64, 1, PRO, EPI>(a, st);
+        case 4096: return launch_chunked_r<64, 2, PRO, EPI>(a, st);
+        case 8192: return launch_chunked_t<64, 4, 4, PRO, EPI>(a, st);
+        case 16384: return launch_chunked_t<64, 8, 2, PRO, EPI>(a, st);
+        default: return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+}
+
+bool gemv_fused_supported(int K) {
+    switch (K) {
+        case 256: case 512: case 1024: case 2048: case 4096: case 8192: case 16384: return true;
+        default: return false;
+    }
+}
+
+int launch_gemv_rmsnorm(const GemvArgs& a, hipStream_t st) { return launch_chunked<GV_RMSNORM, GV_STORE>(a, st); }
+
+int launch_gemv_argmax(const GemvArgs& a, hipStream_t st) { return launch_chunked<GV_PLAIN, GV_ARGMAX>(a, st); }
+
+int launch_embed(const GemvArgs& a, hipStream_t st) {
+    const int words = a.K / 8;
+    hipLaunchKernelGGL(embed_w4_kernel, dim3((words + 255) / 256), dim3(256), 0, st, a.qweight, a.scales,
+                       a.biases, a.token, a.y, a.K, a.N);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 int launch_gemv(const GemvArgs& a, hipStream_t st) {
-    // Chunked kernel: K/32 chunks per row spread over TPR lanes, V per lane.
-    switch (a.K) {
-        case 256: return launch_chunked_r<8, 1>(a, st);
-        case 512: return launch_chunked_r<16, 1>(a, st);
-        case 1024: return launch_chunked_r<32, 1>(a, st);
-        case 2048: return launch_chunked_r<64, 1>(a, st);
-        case 4096: return launch_chunked_r<64, 2>(a, st);
-        case 8192: return launch_chunked_t<64, 4, 4>(a, st);
-        case 16384: return launch_chunked_t<64, 8, 2>(a, st);
-        default: break;
-    }
+    if (gemv_fused_supported(a.K)) return launch_chunked<GV_PLAIN, GV_STORE>(a, st);
     const int G = a.K / kGroup;
     switch (G) {
         case 8: return launch_gemv_t<8, 1, 2>(a, st);

@@ -148,6 +148,51 @@ __device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
 #endif
 }
 
+// 64-bit selection keys: the unsigned order of logit_key(v, i) is "larger
+// v first, then smaller index i".  The upper word is the bit pattern of v
+// made monotone (negative values inverted, positive values with the sign
+// bit set), the lower word 0xFFFFFFFF - i.  No finite v maps to key 0.
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_logit(uint64_t k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_index(uint64_t k) {
+    return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active), uniform result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = umax64(v, dpp_u64<0x141>(v));  // row_half_mirror
+    v = umax64(v, dpp_u64<0x140>(v));  // row_mirror
+    return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                  umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
 __device__ __forceinline__ float silu(float z) {
     return z / (1.0f + __expf(-z));
 }

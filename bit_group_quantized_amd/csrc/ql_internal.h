@@ -20,8 +20,20 @@ struct GemvArgs {
     const uint16_t* x;
     uint16_t* y;
     int K, N;
+    const uint16_t* gamma = nullptr;  // RMSNorm prologue
+    float eps = 0.f;
+    uint64_t* partials = nullptr;     // argmax epilogue: one key per block
+    int32_t* token = nullptr;         // argmax result / embedding row id
 };
 int launch_gemv(const GemvArgs& a, hipStream_t st);
+// K with the chunked kernel (powers of two 256 .. 16384): the fused variants.
+bool gemv_fused_supported(int K);
+int launch_gemv_rmsnorm(const GemvArgs& a, hipStream_t st);
+// Writes a.y if non-null, the block keys to a.partials (at most
+// ceil(N / 8) of them) and the token id to a.token.
+int launch_gemv_argmax(const GemvArgs& a, hipStream_t st);
+// a.y = fp16 row *a.token of the w4 table (a.K wide, a.N rows).
+int launch_embed(const GemvArgs& a, hipStream_t st);
 
 struct GemmArgs {
     const uint32_t* qweight;

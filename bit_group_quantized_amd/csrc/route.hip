@@ -128,58 +128,11 @@ router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token by one wave.
-//
-// Every (logit, expert) becomes one 64-bit key whose unsigned order is the
-// selection order: the upper word is the logit's bit pattern made monotone
-// (negative values inverted, positive values with the sign bit set), the
-// lower word is 0xFFFFFFFF - e so that equal logits favour the lower index.
-// Key 0 marks an expert already taken (no finite logit maps to it).  A
-// round takes the wave maximum: four DPP steps inside each row of 16 lanes
-// (xor 1, xor 2, half-row mirror, row mirror), then the four row maxima
-// are read into scalar registers, so the winner is uniform.
+// Top-k of one token by one wave, with the 64-bit selection keys of
+// ql_device.h (logit_key): key 0 marks an expert already taken (no finite
+// logit maps to it), and each round takes the wave maximum (wave_max_u64),
+// so the winner is uniform.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t logit_key(float v, int e) {
-    uint32_t u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_logit(uint64_t k) {
-    uint32_t u = (uint32_t)(k >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    return __uint_as_float(u);
-}
-
-__device__ __forceinline__ int key_expert(uint64_t k) {
-    return (int)(0xFFFFFFFFu - (uint32_t)k);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Maximum over the 64 lanes of a wave (all lanes active), uniform result.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = umax64(v, dpp_u64<0x141>(v));  // row_half_mirror
-    v = umax64(v, dpp_u64<0x140>(v));  // row_mirror
-    return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
-                  umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
-}
-
 // Logits of token t are the sum of `nparts` partial rows (fixed order) plus
 // the optional bias; they are written to logits_out.  Writes the topk
 // chosen experts (descending) and their renormalized gates to sel_e/sel_g.
@@ -220,7 +173,7 @@ __device__ void topk_one_token(const float* __restrict__ src, const float* __res
 #pragma unroll
         for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
         best = wave_max_u64(best);  // uniform
-        const int be = key_expert(best);
+        const int be = key_index(best);
         const float bv = key_logit(best);
         if ((be & 63) == lane) {
 #pragma unroll

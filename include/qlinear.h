@@ -153,8 +153,9 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
  * the single-row and the many-row path ([PPLX] "使瓦片大小与专家负载相匹配",
  * tile choice against row count; "优化单行权重路径").  Weight-stationary:
  * every weight is read and dequantized once and kept in registers while all
- * M rows stream past it, so the cost grows slowly with M; faster than
- * qlinear_gemm up to a few hundred rows (measured crossover: see DESIGN).
+ * M rows stream past it, so the cost grows slowly with M.  Measured on
+ * MI355X it is 2-3x faster than qlinear_gemm for 2 to 64 rows, equal near
+ * 128 and slower beyond (the activations are re-read once per 32 columns).
  *   X fp16 [M][K], Y fp16 [M][N]; fp16 dequantized weights, fp32 accumulation
  *   split over 8 K slices summed in a fixed order: deterministic, but its
  *   rounding differs from qlinear_gemm's (which does not split K).
@@ -163,6 +164,64 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
  */
 int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y,
                           void* stream);
+
+/*
+ * qlinear_gemv_rmsnorm - y = fp16(rmsnorm(x)) . dequant(W): a decode
+ * projection with its normalization fused in front ([PPLX] "减少中间状态和流量":
+ * the decode chains keep intermediates in registers, normalization among
+ * the fused steps).  u[k] = x[k] / sqrt(mean(x^2) + eps) * gamma[k] is
+ * computed in fp32 inside the GEMV (every block derives the same sum of
+ * squares) and rounded to fp16 once, where an unfused path would store it;
+ * the projection then reads that row.  The norm's RMS form is this
+ * library's reading of the page.
+ *   W  K x N w4;  x, gamma  fp16 [K];  eps  >= 0, finite;  y  fp16 [N].
+ * Limits: K a power of two from 256 to 16384.
+ * Errors: as qlinear_gemv; INVALID_ARG for a null gamma or a bad eps;
+ * UNSUPPORTED_SHAPE for other K; MISALIGNED (x, gamma 16-byte aligned).
+ */
+int qlinear_gemv_rmsnorm(const ql_w4* W, const uint16_t* x, const uint16_t* gamma, float eps,
+                         uint16_t* y, void* stream);
+
+/*
+ * qlinear_gemv_argmax_workspace_bytes - device workspace of
+ * qlinear_gemv_argmax for N outputs: 8 * ceil(N / 8) bytes (0 for N <= 0).
+ */
+size_t qlinear_gemv_argmax_workspace_bytes(int64_t N);
+
+/*
+ * qlinear_gemv_argmax - the vocabulary head with the token choice on the
+ * GPU ([PPLX] "将 token 交接保留在 GPU 上": the step ends by picking the
+ * highest-scoring token and the GPU writes its id straight into the next
+ * step's input slot, with no round trip through the host).
+ *   logits = x . dequant(W) as in qlinear_gemv; *token = the index of the
+ *   largest fp32 logit (before rounding to fp16), the smallest index among
+ *   equal largest values.  NaN logits are never chosen; if no logit is
+ *   comparable the token is 0.  The result is always in [0, N).
+ *   W  K x N w4 (N >= 1);  x  fp16 [K];  logits  fp16 [N] output or NULL;
+ *   token  int32 device slot (4-byte aligned), written by the GPU;
+ *   workspace  device memory of qlinear_gemv_argmax_workspace_bytes(N)
+ *   bytes, 8-byte aligned, no initialization needed, must not be shared by
+ *   calls that may run concurrently.  Two launches on the stream.
+ * Limits: K a power of two from 256 to 16384.
+ * Errors: INVALID_ARG (null W, x or token, N < 1), UNSUPPORTED_SHAPE,
+ * MISALIGNED, WORKSPACE, HIP.
+ */
+int qlinear_gemv_argmax(const ql_w4* W, const uint16_t* x, uint16_t* logits, int32_t* token,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qlinear_embed_token - the next step's input row from the token slot:
+ * x = fp16(dequant(E)[*token]), row *token of a w4 embedding table read on
+ * the GPU ([PPLX] token hand-off section: the next step starts from the
+ * chosen token; the table in the w4 layout above, one output per token, is
+ * this library's reading).  Each value is rounded once (scale*code + bias).
+ *   E  w4 table with K = hidden width, N = number of tokens;  token  int32
+ *   device slot;  x  fp16 [K] output (16-byte aligned).  An id outside
+ *   [0, N) yields a row of zeros and reads no table memory.
+ * Errors: INVALID_ARG (null E, token or x with K > 0, N < 1),
+ * UNSUPPORTED_SHAPE (as qlinear_gemv), MISALIGNED, HIP.
+ */
+int qlinear_embed_token(const ql_w4* E, const int32_t* token, uint16_t* x, void* stream);
 
 /*
  * moe_workspace_bytes - bytes of device workspace that moe_route and

@@ -22,7 +22,9 @@ these seeded draws stand in for it):
 * router weight [D][E]: fp16 of N(0, 0.02) (0.02 read as a standard
   deviation);
 * skewed-load logit bias: b_e = -1.1 * ln(rank_e), ranks a seeded
-  permutation of 1..E (the logarithm of a Zipf law with s = 1.1).
+  permutation of 1..E (the logarithm of a Zipf law with s = 1.1);
+* decode row in front of a normalization (residual stream): fp16 of
+  N(0, 16), i.e. 4 * N(0, 1); normalization gain: fp16 of U(0.5, 1.5).
 """
 from __future__ import annotations
 
@@ -110,6 +112,21 @@ def gemv_case(seed: int, K: int, N: int) -> dict:
     x = activations(rng, 1, K)
     W = w4_matrix(rng, K, N)
     return {"x": x, "W": W}
+
+
+def norm_gain(rng: np.random.Generator, K: int) -> np.ndarray:
+    """fp16 [K] drawn from U(0.5, 1.5)."""
+    return f16(rng.uniform(0.5, 1.5, size=K))
+
+
+def decode_norm_case(seed: int, K: int, N: int) -> dict:
+    """Residual-stream row x fp16 [1][K] (4 * N(0, 1)), its normalization
+    gain fp16 [K] and one K x N w4 matrix."""
+    rng = rng_for(seed)
+    x = f16(4.0 * rng.standard_normal((1, K)))
+    gamma = norm_gain(rng, K)
+    W = w4_matrix(rng, K, N)
+    return {"x": x, "gamma": gamma, "W": W}
 
 
 def gemm_case(seed: int, M: int, K: int, N: int) -> dict:

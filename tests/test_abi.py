@@ -172,3 +172,45 @@ def test_product_path_does_not_touch_the_oracle():
             if fn.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b|oracle\.", text), fn
+
+
+def test_gemv_rmsnorm_validation(L):
+    f = L.qlinear_gemv_rmsnorm
+    assert f(None, A16, A16, 1e-6, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=192)), A16, A16, 1e-6, A16, None) == SHAPE   # not a power of two
+    assert f(ctypes.byref(_w(K=128)), A16, A16, 1e-6, A16, None) == SHAPE   # below 256
+    assert f(ctypes.byref(_w()), A16, A16, -1.0, A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, A16, float("nan"), A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, A16, float("inf"), A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, None, 1e-6, A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, A16 + 2, 1e-6, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), A16 + 8, A16, 1e-6, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), None, None, 1e-6, None, None) == OK
+
+
+def test_gemv_argmax_validation(L):
+    f = L.qlinear_gemv_argmax
+    wsb = L.qlinear_gemv_argmax_workspace_bytes
+    assert wsb(151552) == 151552 and wsb(9) == 16 and wsb(1) == 8 and wsb(0) == 0 and wsb(-3) == 0
+    ok = wsb(64)
+    assert f(None, A16, None, A16, A16, ok, None) == INVALID
+    assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), A16, None, A16, A16, ok, None) == INVALID  # N < 1
+    assert f(ctypes.byref(_w(K=192)), A16, None, A16, A16, ok, None) == SHAPE
+    assert f(ctypes.byref(_w()), None, None, A16, A16, ok, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, None, None, A16, ok, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, None, A16 + 2, A16, ok, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), A16, A16 + 1, A16, A16, ok, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), A16, None, A16, A16, ok - 8, None) == WORKSPACE
+    assert f(ctypes.byref(_w()), A16, None, A16, None, ok, None) == WORKSPACE
+    assert f(ctypes.byref(_w()), A16, None, A16, A16 + 4, ok, None) == MISALIGNED
+
+
+def test_embed_token_validation(L):
+    f = L.qlinear_embed_token
+    assert f(None, A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=100)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w()), None, A16, None) == INVALID
+    assert f(ctypes.byref(_w()), A16, None, None) == INVALID
+    assert f(ctypes.byref(_w()), A16 + 2, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), A16, A16 + 8, None) == MISALIGNED

@@ -37,7 +37,7 @@ ROTATE_BYTES = 600e6  # > 2 x 256 MB Infinity Cache
 # the clocks reach their sustained level under the measured load within a
 # fraction of a second.
 SETTLE_S = 0.5
-KERNEL_GEMV = "gemv_w4_chunked_kernel<64,1,8>"  # the K = 2048 vocabulary-head launch
+KERNEL_GEMV = "gemv_w4_chunked_kernel<64,1,8,0,0>"  # the K = 2048 vocabulary-head launch
 
 
 def w4_bytes(K, N):
@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
-    ap.add_argument("--workload", choices=["all", "gemm", "moe_decode", "moe_prefill"], default="all",
+    ap.add_argument("--workload", choices=["all", "gemm", "decode", "moe_decode", "moe_prefill"], default="all",
                     help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -276,6 +276,77 @@ def bench_few_rows(args, dev):
     return out
 
 
+def bench_decode_fusions(args, dev):
+    """The decode steps beside the GEMV, each timed from HIP graphs over
+    rotated weight copies (more than 600 MB between two uses of a copy):
+    the vocabulary head plain, with the on-GPU token choice, and with the
+    token choice plus fp16 logits; the K = 2048, N = 8192 projection plain
+    and with its RMSNorm prologue; the embedding row of the token; and one
+    chained decode tail (normalized projection, head with token choice,
+    embedding row of the chosen token)."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K, V, N = 2048, synth.VOCAB, 8192
+    head = synth.gemv_case(1, K, V)
+    proj = synth.decode_norm_case(2, K, N)
+    emb = synth.w4_matrix(synth.rng_for(3), K, V)
+    hb, pb, eb = w4_bytes(K, V), w4_bytes(K, N), w4_bytes(K, V)
+    copies = max(2, int(np.ceil(ROTATE_BYTES / hb)))
+    Hs = [dev_w4(head["W"], dev)]
+    Hs += [clone_w4(Hs[0]) for _ in range(copies - 1)]
+    pc = max(2, int(np.ceil(ROTATE_BYTES / pb)))
+    Ps = [dev_w4(proj["W"], dev)]
+    Ps += [clone_w4(Ps[0]) for _ in range(pc - 1)]
+    E = dev_w4(emb, dev)
+    x = torch.from_numpy(head["x"][0]).to(dev)
+    xp = torch.from_numpy(proj["x"][0]).to(dev)
+    gamma = torch.from_numpy(proj["gamma"]).to(dev)
+    logits = torch.empty(V, dtype=torch.float16, device=dev)
+    yp = torch.empty(N, dtype=torch.float16, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = ql.gemv_argmax_workspace(V, dev)
+    xe = torch.empty(K, dtype=torch.float16, device=dev)
+    cases = {
+        "head_gemv": (copies, hb + 2 * K + 2 * V, lambda i: ql.qlinear_gemv(Hs[i % copies], x, logits)),
+        "head_argmax": (copies, hb + 2 * K + 4,
+                        lambda i: ql.qlinear_gemv_argmax(Hs[i % copies], x, token=tok, workspace=ws)),
+        "head_argmax_and_logits": (copies, hb + 2 * K + 2 * V + 4,
+                                   lambda i: ql.qlinear_gemv_argmax(Hs[i % copies], x, token=tok,
+                                                                    logits=logits, workspace=ws)),
+        "proj_gemv": (pc, pb + 2 * K + 2 * N, lambda i: ql.qlinear_gemv(Ps[i % pc], xp, yp)),
+        "proj_rmsnorm_gemv": (pc, pb + 4 * K + 2 * N,
+                              lambda i: ql.qlinear_gemv_rmsnorm(Ps[i % pc], xp, gamma, 1e-6, yp)),
+        "embed_row": (8, K // 2 + K // 16 + 2 * K + 4, lambda i: ql.qlinear_embed_token(E, tok, xe)),
+    }
+    # Interleaved rounds, median per case (a case timed right after another
+    # can inherit its cache and clock state).
+    times = {name: [] for name in cases}
+    for _ in range(3):
+        for name, (ng, nbytes, fn) in cases.items():
+            for i in range(2 * ng):
+                fn(i)
+            times[name].append(graph_time(fn, ng, 20))
+    out = {}
+    for name, (ng, nbytes, fn) in cases.items():
+        ms = float(np.median(times[name]))
+        out[name] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "bytes": nbytes}
+
+    def tail(i):
+        ql.qlinear_gemv_rmsnorm(Ps[i % pc], xp, gamma, 1e-6, yp)
+        ql.qlinear_gemv_argmax(Hs[i % copies], x, token=tok, workspace=ws)
+        ql.qlinear_embed_token(E, tok, xe)
+    ng = max(copies, pc)
+    for i in range(ng):
+        tail(i)
+    ms = graph_time(tail, ng, 20)
+    out["decode_tail_chain"] = {"us": round(ms * 1e3, 2),
+                                "GB/s": round((hb + pb) / (ms * 1e-3) / 1e9, 1),
+                                "what": "rmsnorm projection K2048 N8192, head with token choice and embedding row, back to back in one graph (no data dependency between the projection and the head here)"}
+    return out
+
+
 def moe_dev_weights(w, dev):
     import torch
     return {"Wr": torch.from_numpy(w["Wr"]).to(dev), "gate_up": dev_w4(w["gate_up"], dev),
@@ -416,8 +487,8 @@ def ingest_pmc(fetch_csv, write_csv):
         return np.asarray([v for gs, v in rows if gs == g or not largest_grid])
     f_read = CALIB_BYTES / np.median(values(fetch[pick(fetch, "neg_kernel")]))
     f_write = CALIB_BYTES / np.median(values(write[pick(write, "neg_kernel")]))
-    fr = values(fetch[pick(fetch, "gemv_w4_chunked_kernel<64, 1, 8>")], largest_grid=True) * f_read
-    wr = values(write[pick(write, "gemv_w4_chunked_kernel<64, 1, 8>")], largest_grid=True) * f_write
+    fr = values(fetch[pick(fetch, "gemv_w4_chunked_kernel<64, 1, 8, 0, 0>")], largest_grid=True) * f_read
+    wr = values(write[pick(write, "gemv_w4_chunked_kernel<64, 1, 8, 0, 0>")], largest_grid=True) * f_write
     n = min(len(fr), len(wr))
     per_launch = float(np.mean(fr[:n] + wr[:n]))
     algo = w4_bytes(2048, 151552) + 2 * 2048 + 2 * 151552
@@ -505,6 +576,9 @@ def main():
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
             log("bench: few-row GEMM")
             wl["few_rows_gemm"] = bench_few_rows(args, dev)
+        if args.workload in ("all", "decode"):
+            log("bench: decode fusions")
+            wl["decode_fusions"] = bench_decode_fusions(args, dev)
         if args.workload in ("all", "moe_decode", "moe_prefill"):
             w = synth.moe_weights(0)
             if args.workload in ("all", "moe_decode"):

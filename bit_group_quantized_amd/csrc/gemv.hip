@@ -155,56 +155,6 @@ gemv_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
 // and adds the partner's copy of them, so R rows cost R-1 shuffles, not
 // R*log2(TPR).
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// v_permlane32_swap on (a, b): lanes 0-31 get a's two halves, lanes 32-63
-// b's; their sum is a's cross-half total in the lower half of the wave and
-// b's in the upper half.  v_permlane16_swap does the same for pairs of
-// 16-lane rows (even rows end with a, odd rows with b).
-__device__ __forceinline__ float swap_add32(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
-                                                    __builtin_bit_cast(unsigned, b), false, false);
-    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-__device__ __forceinline__ float swap_add16(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
-                                                    __builtin_bit_cast(unsigned, b), false, false);
-    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Whole-wave (64-lane team) row reduction: every lane holds partials of the
-// same R rows; afterwards lane l holds the total of row l / (64 / R).  The
-// halving steps across 32- and 16-lane rows exchange whole rows with the
-// permlane swaps (no selects); inside 16-lane rows DPP pairs lane i with
-// 15 - i, then 7 - i, then the quad permutations finish each group.
-template <int R>
-__device__ __forceinline__ float reduce_rows64(const float (&v)[R], int lane, int& row) {
-    static_assert(R == 1 || R == 2 || R == 4 || R == 8, "1, 2, 4 or 8 rows");
-    constexpr int R1 = (R > 1) ? R / 2 : 1;
-    float a[R1];
-#pragma unroll
-    for (int i = 0; i < R1; ++i) a[i] = (R > 1) ? swap_add32(v[i], v[i + R1]) : swap_add32(v[0], v[0]);
-    constexpr int R2 = (R1 > 1) ? R1 / 2 : 1;
-    float b[R2];
-#pragma unroll
-    for (int i = 0; i < R2; ++i) b[i] = (R1 > 1) ? swap_add16(a[i], a[i + R2]) : swap_add16(a[0], a[0]);
-    float t;
-    if constexpr (R2 > 1) {
-        const bool hi8 = (lane & 8) != 0;  // lanes 8-15 of a 16-lane row keep b[1]
-        t = (hi8 ? b[1] : b[0]) + dpp_mov<0x140>(hi8 ? b[0] : b[1]);  // row_mirror
-    } else {
-        t = b[0] + dpp_mov<0x140>(b[0]);
-    }
-    t += dpp_mov<0x141>(t);  // row_half_mirror
-    t += dpp_mov<0x4E>(t);   // quad_perm [2,3,0,1]
-    t += dpp_mov<0xB1>(t);   // quad_perm [1,0,3,2]
-    row = lane / (64 / R);
-    return t;
-}
-
 template <int TPR, int R>
 __device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
     static_assert(R <= TPR, "each row needs its own lane after the halving steps");
@@ -522,13 +472,17 @@ moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
 }
 
 // Decode down projection fused with the gate-weighted sum over the token's
-// routed rows and its shared row.  One wave per block owns TEAMS*R outputs
-// of one token.  The (expert, row) of each assignment comes from
-// assign_info; all code loads of all rows are issued together, the
-// activation rows are pre-paired into LDS meanwhile.  The per-output sum
-// runs in the fixed order j = 0 .. topk-1, then the shared row.
+// routed rows and its shared row.  A block of four waves owns TEAMS*R
+// outputs of one token; the rows j = 0 .. J-1 (the shared row is j = topk)
+// are dealt to the waves by j mod 4, so every SIMD of the CU works (one wave
+// holding all rows left three idle and ran their work serially).  The
+// (expert, row) of each assignment comes from assign_info.  The activation
+// loads are issued first, then each wave's code loads; the activations are
+// pre-paired into LDS while the codes are in flight.  Sums, in a fixed
+// order: per lane over the wave's rows in ascending j, across the lanes of
+// the row team, then the four wave sums in wave order.
 template <int TPR, int V, int R, int JC>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                         const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
                         const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
@@ -540,6 +494,8 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
     __shared__ int s_row[QL_MAX_TOPK_DEV + 1];
     __shared__ float s_gate[QL_MAX_TOPK_DEV + 1];
     constexpr int TEAMS = 64 / TPR;
+    constexpr int NW = 4;  // waves per block
+    __shared__ float s_red[NW][TEAMS * R];
     const int G = K / kGroup;
     const int wpr = K / 8;
     const int CH = K / 32;  // 16-byte chunks of codes per row
@@ -565,23 +521,51 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
     }
     __syncthreads();
 
-    const int lane = threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int lr = lane % TPR;
     const int team = lane / TPR;
     const int n0 = (blockIdx.x * TEAMS + team) * R;
+
+    // Activation staging (whole block), loads of the first batch first.
+    auto stage_load = [&](int idx0, u32x4 (&xw)[4]) {
+        const int idx = min(idx0, J * CH - 1);
+        const int j = idx / CH, c = idx % CH;
+        const uint16_t* xrow = X + (size_t)s_row[j] * K + c * 32;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xw[w] = ld_u32x4(xrow + w * 8);
+    };
+    auto stage_store = [&](int idx, const u32x4 (&xw)[4]) {
+        if (idx >= J * CH) return;
+        const int j = idx / CH, c = idx % CH;
+        float cc = 0.f, xx = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const XPairs xp = make_xpairs(xw[w]);
+            float c_, s_;
+            xpairs_consts(xp, xw[w], c_, s_);
+            cc += c_;
+            xx += s_;
+            s_xp[((size_t)j * CH + c) * 4 + w] = xp;
+        }
+        s_c[j * CH + c] = cc;
+        s_xs[j * CH + c] = xx;
+    };
+    u32x4 xw0[4];
+    stage_load(threadIdx.x, xw0);
+
     float acc[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) acc[q] = 0.f;
 
-    // Rows are processed JC at a time: the code loads of JC rows are issued
-    // together (the first group before the activation staging), so a
-    // token's topk + 1 rows cost one memory round trip when topk + 1 <= JC.
-    for (int j0 = 0; j0 < J; j0 += JC) {
-        u32x4 cw[JC][R][V];
-        uint16_t s[JC][R][V], b[JC][R][V];
+    // This wave's rows: j = wave, wave + 4, ..., JC of them per round.
+    u32x4 cw[JC][R][V];
+    uint16_t s[JC][R][V], b[JC][R][V];
+    auto load_round = [&](int j0) {
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
-            const int j = min(j0 + jj, J - 1);
+            const int j = j0 + NW * jj;
+            if (j >= J) break;  // uniform across the wave
             const int e = s_exp[j];
             const uint32_t* wq = (e >= 0) ? qw + (size_t)e * N * wpr : sqw;
             const uint16_t* ws = (e >= 0) ? sc + (size_t)e * N * G : ssc;
@@ -598,32 +582,11 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
                 }
             }
         }
-        if (j0 == 0) {
-            // Activation rows, pre-paired, into LDS (one chunk per iteration).
-            for (int idx = threadIdx.x; idx < J * CH; idx += blockDim.x) {
-                const int j = idx / CH, c = idx % CH;
-                const uint16_t* xrow = X + (size_t)s_row[j] * K + c * 32;
-                u32x4 xw[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) xw[w] = ld_u32x4(xrow + w * 8);
-                float cc = 0.f, xx = 0.f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const XPairs xp = make_xpairs(xw[w]);
-                    float c_, s_;
-                    xpairs_consts(xp, xw[w], c_, s_);
-                    cc += c_;
-                    xx += s_;
-                    s_xp[((size_t)j * CH + c) * 4 + w] = xp;
-                }
-                s_c[j * CH + c] = cc;
-                s_xs[j * CH + c] = xx;
-            }
-            __syncthreads();
-        }
+    };
+    auto compute_round = [&](int j0) {
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
-            const int j = j0 + jj;
+            const int j = j0 + NW * jj;
             if (j >= J) break;  // uniform across the wave
             const float g = s_gate[j];
 #pragma unroll
@@ -645,10 +608,30 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
                 }
             }
         }
+    };
+    load_round(wave);  // no loads for a wave without rows (wave >= J)
+    stage_store(threadIdx.x, xw0);
+    for (int idx = threadIdx.x + 256; idx < J * CH; idx += 256) {
+        u32x4 xw[4];
+        stage_load(idx, xw);
+        stage_store(idx, xw);
+    }
+    __syncthreads();
+    compute_round(wave);
+    for (int j0 = wave + NW * JC; j0 < J; j0 += NW * JC) {
+        load_round(j0);
+        compute_round(j0);
     }
     int sel;
     const float tot = reduce_rows<TPR, R>(acc, lr, sel);
-    if ((lr & (TPR / R - 1)) == 0 && n0 + sel < N) Y[(size_t)t * N + n0 + sel] = f2h(tot);
+    if ((lr & (TPR / R - 1)) == 0) s_red[wave][team * R + sel] = tot;
+    __syncthreads();
+    if (threadIdx.x < TEAMS * R) {
+        const int n = blockIdx.x * TEAMS * R + threadIdx.x;
+        const float y = ((s_red[0][threadIdx.x] + s_red[1][threadIdx.x]) + s_red[2][threadIdx.x]) +
+                        s_red[3][threadIdx.x];
+        if (n < N) Y[(size_t)t * N + n] = f2h(y);
+    }
 }
 
 constexpr int kMaxGemvBlocks = 2048;
@@ -682,7 +665,8 @@ int launch_rows_t(const GroupedArgs& a, hipStream_t st) {
         const int J = a.topk + has_shared;
         const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
         dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
-        hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 9>), grid, dim3(64), smem, st, a.qw,
+        // four waves; each takes the rows j = wave, wave + 4, ... (3 per round)
+        hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3>), grid, dim3(256), smem, st, a.qw,
                            a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates,
                            reinterpret_cast<const int2*>(a.ws + L.assign_info), a.Y, a.K, a.N, a.E,
                            a.T, a.topk, has_shared);

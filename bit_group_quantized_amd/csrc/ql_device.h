@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ql {
 
 typedef _Float16 f16;
@@ -146,6 +148,95 @@ __device__ __forceinline__ u32x4 ld_stream_u32x4(const void* p) {
 #else
     return *reinterpret_cast<const u32x4*>(p);
 #endif
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// v_permlane32_swap on (a, b): lanes 0-31 get a's two halves, lanes 32-63
+// b's; their sum is a's cross-half total in the lower half of the wave and
+// b's in the upper half.  v_permlane16_swap does the same for pairs of
+// 16-lane rows (even rows end with a, odd rows with b).
+__device__ __forceinline__ float swap_add32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                    __builtin_bit_cast(unsigned, b), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Whole-wave (64-lane team) row reduction: every lane holds partials of the
+// same R rows; afterwards lane l holds the total of row l / (64 / R).  The
+// halving steps across 32- and 16-lane rows exchange whole rows with the
+// permlane swaps (no selects); inside 16-lane rows DPP pairs lane i with
+// 15 - i, then 7 - i, then the quad permutations finish each group.
+template <int R>
+__device__ __forceinline__ float reduce_rows64(const float (&v)[R], int lane, int& row) {
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8, "1, 2, 4 or 8 rows");
+    constexpr int R1 = (R > 1) ? R / 2 : 1;
+    float a[R1];
+#pragma unroll
+    for (int i = 0; i < R1; ++i) a[i] = (R > 1) ? swap_add32(v[i], v[i + R1]) : swap_add32(v[0], v[0]);
+    constexpr int R2 = (R1 > 1) ? R1 / 2 : 1;
+    float b[R2];
+#pragma unroll
+    for (int i = 0; i < R2; ++i) b[i] = (R1 > 1) ? swap_add16(a[i], a[i + R2]) : swap_add16(a[0], a[0]);
+    float t;
+    if constexpr (R2 > 1) {
+        const bool hi8 = (lane & 8) != 0;  // lanes 8-15 of a 16-lane row keep b[1]
+        t = (hi8 ? b[1] : b[0]) + dpp_mov<0x140>(hi8 ? b[0] : b[1]);  // row_mirror
+    } else {
+        t = b[0] + dpp_mov<0x140>(b[0]);
+    }
+    t += dpp_mov<0x141>(t);  // row_half_mirror
+    t += dpp_mov<0x4E>(t);   // quad_perm [2,3,0,1]
+    t += dpp_mov<0xB1>(t);   // quad_perm [1,0,3,2]
+    row = lane / (64 / R);
+    return t;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active), uniform result:
+// DPP inside each 16-lane row, then the four row maxima through readlane.
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_mov<0x140>(v));  // row_mirror
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float e = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, e));
+}
+
+// Maximum of a 32-bit unsigned value over the 64 lanes of a wave, uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto dpp = [](uint32_t x, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, true);
+    };
+    v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+    v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+    v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane((int)v, 32), e = __builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, e));
+}
+
+// Monotone 32-bit key of a float: unsigned order = numeric order (the sign
+// bit flipped for positive values, all bits for negative ones); the key of
+// -inf is 0x007FFFFF, so no float maps to 0.
+__device__ __forceinline__ uint32_t mono32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unmono32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // 64-bit selection keys: the unsigned order of logit_key(v, i) is "larger

@@ -151,45 +151,54 @@ __device__ void topk_one_token(const float* __restrict__ src, const float* __res
 #pragma unroll
         for (int p = 0; p < NP; ++p) part[i][p] = src[((size_t)t * NP + p) * E + e];
     }
-    uint64_t key[EPL];
+    // Lane l holds the keys of experts l, l + 64, ...: the monotone 32-bit
+    // pattern of the logit, with -0 folded into +0 so that equal logits have
+    // equal keys; 0 marks an entry already taken (or past E).
+    uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = 0;
+        key[i] = 0u;
         if (e < E) {
             float s = 0.f;
 #pragma unroll
             for (int p = 0; p < NP; ++p) s += part[i][p];
             if (bias) s += bias[e];
             logits_out[(size_t)t * E + e] = s;
-            if (s != s) s = -INFINITY;  // NaN never wins
-            key[i] = logit_key(s, e);
+            key[i] = mono32((s != s) ? -INFINITY : s + 0.0f);  // NaN never wins
         }
     }
+    // Each round: the largest remaining key over the wave, then the smallest
+    // expert index holding it (ballots in index order, first set bit); that
+    // entry is taken.  topk <= the number of valid entries, so m > 0.
     float vmax = 0.f, my_v = 0.f;
     int my_e = 0;
     for (int j = 0; j < topk; ++j) {
-        uint64_t best = key[0];
+        uint32_t m = key[0];
 #pragma unroll
-        for (int i = 1; i < EPL; ++i) best = umax64(best, key[i]);
-        best = wave_max_u64(best);  // uniform
-        const int be = key_index(best);
-        const float bv = key_logit(best);
-        if ((be & 63) == lane) {
+        for (int i = 1; i < EPL; ++i) m = max(m, key[i]);
+        m = wave_max_u32(m);  // uniform
+        int be = -1;
 #pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == (be >> 6)) key[i] = 0;
+        for (int i = 0; i < EPL; ++i) {
+            const uint64_t b = __ballot(key[i] == m);
+            if (be < 0 && b != 0) be = 64 * i + __ffsll((unsigned long long)b) - 1;
         }
+        be = max(be, 0);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if ((be & 63) == lane && i == (be >> 6)) key[i] = 0u;
+        const float bv = unmono32(m);
         if (j == 0) vmax = bv;
         if (lane == j) {
             my_v = bv;
             my_e = be;
         }
     }
-    const float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
+    const float exs[1] = {ex};
+    int unused;
+    const float sum = reduce_rows64<1>(exs, lane, unused);  // every lane: the total
     if (lane < topk) {
         sel_e[lane] = my_e;
         sel_g[lane] = ex / sum;
@@ -376,6 +385,9 @@ dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
 // and one block scan over the experts gives both the row offsets and the
 // tile indices (every expert has at most one tile here).
 // ---------------------------------------------------------------------------
+// Logits of at most this many (token, expert) pairs stay in LDS.
+constexpr int kSmallLogitsLds = 4096;
+
 template <int EPL, bool DO_TOPK>
 __device__ __forceinline__ void route_small_body(const float* __restrict__ partials, const float* __restrict__ bias,
                  float* __restrict__ logits_out, int T, int E, int topk,
@@ -386,18 +398,24 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
     static_assert(kRouterSmallT <= 32 && kRouterSmallT * QL_MAX_TOPK_DEV <= 4 * QL_MAX_EXPERTS_DEV,
                   "token masks are 32 bits wide");
     static_assert(QL_MOE_TILE_ROWS >= kRouterSmallT, "one tile per expert");
+    // Every intermediate stays in LDS and every global store is issued after
+    // the last barrier: a barrier waits for the block's outstanding stores.
     __shared__ int s_ids[kRouterSmallT * QL_MAX_TOPK_DEV];
     __shared__ float s_gates[kRouterSmallT * QL_MAX_TOPK_DEV];
     __shared__ uint32_t s_mask[QL_MAX_EXPERTS_DEV];
     __shared__ int s_off[QL_MAX_EXPERTS_DEV];
     __shared__ int s_tile[QL_MAX_EXPERTS_DEV];
+    __shared__ float s_logits[kSmallLogitsLds];
     __shared__ int s_tmp[16];
+    __shared__ int s_total;
     const int wave = threadIdx.x >> 6;
     const int nass = T * topk;
+    const bool lds_logits = T * E <= kSmallLogitsLds;
     for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
     if constexpr (DO_TOPK) {
         // Logits of all tokens, one (token, expert) per thread: the partial
         // rows are summed in a fixed order, all of their loads issued at once.
+        float* lg = lds_logits ? s_logits : logits_out;
         for (int idx = threadIdx.x; idx < T * E; idx += blockDim.x) {
             const int tt = idx / E, e = idx - tt * E;
             float part[kRouterParts];
@@ -407,17 +425,12 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
 #pragma unroll
             for (int p = 0; p < kRouterParts; ++p) sum += part[p];
             if (bias) sum += bias[e];
-            logits_out[(size_t)tt * E + e] = sum;
+            lg[idx] = sum;
         }
         __syncthreads();
         for (int t = wave; t < T; t += 4)
-            topk_one_token<EPL, 1>(logits_out, nullptr, logits_out, t, E, topk, s_ids + t * topk,
-                                   s_gates + t * topk);
+            topk_one_token<EPL, 1>(lg, nullptr, lg, t, E, topk, s_ids + t * topk, s_gates + t * topk);
         __syncthreads();
-        for (int a = threadIdx.x; a < nass; a += blockDim.x) {
-            ids[a] = s_ids[a];
-            gates[a] = s_gates[a];
-        }
     } else {
         for (int a = threadIdx.x; a < nass; a += blockDim.x) s_ids[a] = ids[a];
         __syncthreads();
@@ -432,7 +445,7 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
         const uint32_t bit = 1u << (a / topk);
         if (atomicOr(&s_mask[e], bit) & bit) err = 1;  // expert repeated within a token
     }
-    __syncthreads();
+    const int any = __syncthreads_or(err);
     // Per thread a contiguous run of experts; scan of (rows, tiles) packed
     // in one int (rows < 2^16 here).
     const int per = (E + blockDim.x - 1) / blockDim.x;
@@ -450,23 +463,34 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
         const int e = threadIdx.x * per + i;
         if (e < E) {
             const int c = __popc(s_mask[e]);
-            const int off = run & 0xFFFF, tile = run >> 16;
-            s_off[e] = off;
-            s_tile[e] = tile;
-            counts[e] = c;
-            offsets[e] = off;
-            if (c > 0) {
-                int* tp = tiles + (size_t)tile * 4;
-                tp[0] = e;
-                tp[1] = off;
-                tp[2] = c;
-                tp[3] = QL_MOE_TILE_ROWS;  // tile height: short tiles only here
-            }
+            s_off[e] = run & 0xFFFF;
+            s_tile[e] = run >> 16;
             run += c + ((c > 0) << 16);
         }
     }
-    if (threadIdx.x == blockDim.x - 1) offsets[E] = incl & 0xFFFF;
+    if (threadIdx.x == blockDim.x - 1) s_total = incl;
     __syncthreads();
+    // ---- outputs (no barrier from here on) ----
+    if constexpr (DO_TOPK) {
+        if (lds_logits)
+            for (int idx = threadIdx.x; idx < T * E; idx += blockDim.x) logits_out[idx] = s_logits[idx];
+        for (int a = threadIdx.x; a < nass; a += blockDim.x) {
+            ids[a] = s_ids[a];
+            gates[a] = s_gates[a];
+        }
+    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int c = __popc(s_mask[e]);
+        counts[e] = c;
+        offsets[e] = s_off[e];
+        if (c > 0) {
+            int* tp = tiles + (size_t)s_tile[e] * 4;
+            tp[0] = e;
+            tp[1] = s_off[e];
+            tp[2] = c;
+            tp[3] = QL_MOE_TILE_ROWS;  // tile height: short tiles only here
+        }
+    }
     for (int a = threadIdx.x; a < nass; a += blockDim.x) {
         const int e = s_ids[a];
         if ((unsigned)e >= (unsigned)E) {
@@ -481,9 +505,9 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
         row_info[r] = make_int2(e, t);
         assign_info[a] = make_int2(e, r);
     }
-    const int any = __syncthreads_or(err);
     if (threadIdx.x == blockDim.x - 1) {
-        ws_header[0] = incl >> 16;  // inclusive scan of the last thread = all tiles
+        offsets[E] = s_total & 0xFFFF;
+        ws_header[0] = s_total >> 16;  // all tiles
         ws_header[1] = QL_MOE_TILE_ROWS;
         ws_header[2] = any;
         ws_header[3] = 0;

@@ -315,9 +315,11 @@ int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk,
  *        row order; Y fp16 [rows][D].
  *   op = QL_OP_DOWN_COMBINE (T <= QL_DECODE_MAX_T): as QL_OP_DOWN, but
  *        Y fp16 [T][D] = sum_j topk_gates[t][j] * (row assign_pos[t*topk+j])
- *        (+ the shared row of t), accumulated in fp32 in a fixed order (for
- *        each K slice over j = 0..topk-1 then the shared row, then across
- *        K slices), so repeated calls give identical bits.
+ *        (+ the shared row of t), accumulated in fp32 in a fixed order, so
+ *        repeated calls give identical bits: the rows j = 0..topk-1 and the
+ *        shared row (j = topk) are dealt to four groups by j mod 4; within a
+ *        group, for each K slice over its rows in ascending j, then across
+ *        K slices; then the four group sums in group order.
  * topk_gates and assign_pos are read only by QL_OP_DOWN_COMBINE (may be
  * NULL otherwise).  `workspace` is the one filled by moe_route or
  * moe_dispatch for the same T, E, topk.

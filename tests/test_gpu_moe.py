@@ -110,6 +110,27 @@ def test_moe_small_shapes(T, D, I, E, topk, seed):
     _compare(*res, ref, T, topk)
 
 
+@pytest.mark.parametrize("T,D,I,E,topk,seed", [
+    (1, 512, 256, 16, 2, 5),      # 3 rows per token: a wave of the block has none
+    (3, 512, 256, 16, 1, 6),      # 2 rows per token
+    (4, 2048, 512, 256, 8, 7),    # the decode shape, 4 tokens
+    (2, 1024, 512, 32, 13, 8),    # 14 rows per token: two rounds for some waves
+])
+def test_moe_decode_fused_down_shapes(T, D, I, E, topk, seed):
+    """The fused decode down projection (gate-weighted sum over the token's
+    rows and the shared row) over row counts below, at and above one row per
+    wave of its block."""
+    import torch
+    say(f"moe fused down T={T} D={D} I={I} E={E} topk={topk}")
+    w = synth.moe_weights(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 60, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], topk)
+    dw = _dev_weights(w)
+    res = _run_layer(dw, t(tok["H"]), t(tok["logit_bias"]), topk, T, True)
+    torch.cuda.synchronize()
+    _compare(*res, ref, T, topk)
+
+
 SCREENED = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
 
 

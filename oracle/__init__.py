@@ -35,6 +35,7 @@ from .route import (router_logits, softmax, topk_route, histogram,
                     topk_near_ties)
 from .moe import silu, expert_ffn, combine, moe_layer
 from .decode import rms_norm, gemv_rmsnorm, argmax_first, lm_head_token, embed_row
+from .bf16 import bf16_to_f64, round_bf16, dequantize_bf16, linear_bf16
 
 __all__ = [
     "GROUP", "unpack_codes", "pack_codes", "dequantize", "linear", "round_f16",
@@ -42,4 +43,5 @@ __all__ = [
     "stable_permutation", "tile_map", "load_matched_tile_map", "topk_near_ties",
     "silu", "expert_ffn", "combine", "moe_layer",
     "rms_norm", "gemv_rmsnorm", "argmax_first", "lm_head_token", "embed_row",
+    "bf16_to_f64", "round_bf16", "dequantize_bf16", "linear_bf16",
 ]

@@ -24,7 +24,9 @@ these seeded draws stand in for it):
 * skewed-load logit bias: b_e = -1.1 * ln(rank_e), ranks a seeded
   permutation of 1..E (the logarithm of a Zipf law with s = 1.1);
 * decode row in front of a normalization (residual stream): fp16 of
-  N(0, 16), i.e. 4 * N(0, 1); normalization gain: fp16 of U(0.5, 1.5).
+  N(0, 16), i.e. 4 * N(0, 1); normalization gain: fp16 of U(0.5, 1.5);
+* bf16 variants: the same draws stored as bf16 bit patterns (uint16, the
+  upper half of the float32 pattern, nearest even).
 """
 from __future__ import annotations
 
@@ -69,6 +71,36 @@ def w4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dic
     noise = rng.normal(0.0, 1e-3, size=lead + (N, G))
     biases = f16(-8.0 * scales.astype(np.float64) + noise)
     return {"qweight": words, "scales": scales, "biases": biases, "K": K, "N": N}
+
+
+def bf16_bits(a) -> np.ndarray:
+    """Draws stored as bf16 patterns: float32, then the upper 16 bits with
+    round to nearest even (finite draws only)."""
+    u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def w4_matrix_bf16(rng: np.random.Generator, K: int, N: int) -> dict:
+    """A K x N w4 matrix with bf16 scales and biases (uint16 patterns),
+    drawn like w4_matrix."""
+    if K % 8:
+        raise ValueError("K must be a multiple of 8 to draw packed words")
+    G = (K + GROUP - 1) // GROUP
+    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    s = rng.uniform(0.002, 0.02, size=(N, G))
+    scales = bf16_bits(s)
+    s_dec = (scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    biases = bf16_bits(-8.0 * s_dec + rng.normal(0.0, 1e-3, size=(N, G)))
+    return {"qweight": words, "scales": scales, "biases": biases, "K": K, "N": N}
+
+
+def gemm_case_bf16(seed: int, M: int, K: int, N: int) -> dict:
+    """X bf16 [M][K] (N(0, 1) draws) and one bf16-scaled K x N w4 matrix."""
+    rng = rng_for(seed)
+    X = bf16_bits(rng.standard_normal((M, K)))
+    W = w4_matrix_bf16(rng, K, N)
+    return {"X": X, "W": W}
 
 
 def router_weight(rng: np.random.Generator, D: int = HIDDEN, E: int = NUM_EXPERTS) -> np.ndarray:

@@ -227,3 +227,36 @@ def test_decode_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(odec, attr, mutant)
     monkeypatch.setattr(oracle, attr, mutant)
     assert _fails(DECODE_PINS)
+
+
+import oracle.bf16 as obf
+from tests import test_oracle_bf16 as tb
+
+BF16_PINS = [tb.test_decode_hand_patterns, tb.test_round_trip_every_pattern, tb.test_round_hand_ties,
+             tb.test_linear_hand_fixture, tb.test_one_hot_and_bruteforce]
+
+
+def _bf16_dec_shift15(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _bf16_round_truncate(a):
+    a = np.asarray(a, dtype=np.float64)
+    return (a.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_dequant_no_bias(qweight, scales_bits, biases_bits, K):
+    q = ow4.unpack_codes(qweight, K).astype(np.float64)
+    return q * np.repeat(obf.bf16_to_f64(scales_bits), 64, axis=-1)
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("bf16_to_f64", _bf16_dec_shift15),
+    ("round_bf16", _bf16_round_truncate),
+    ("dequantize_bf16", _bf16_dequant_no_bias),
+])
+def test_bf16_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(obf, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant)
+    assert _fails(BF16_PINS)

@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
-    ap.add_argument("--workload", choices=["all", "gemm", "decode", "moe_decode", "moe_prefill"], default="all",
+    ap.add_argument("--workload", choices=["all", "gemm", "decode", "bf16", "moe_decode", "moe_prefill"],
+                    default="all",
                     help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -347,6 +348,59 @@ def bench_decode_fusions(args, dev):
     return out
 
 
+def dev_w4_bits(W, dev):
+    """w4 dict whose scales and biases are 16-bit patterns (bf16)."""
+    import torch
+    return {"qweight": torch.from_numpy(np.ascontiguousarray(W["qweight"]).view(np.int32)).to(dev),
+            "scales": torch.from_numpy(W["scales"].view(np.int16)).to(dev),
+            "biases": torch.from_numpy(W["biases"].view(np.int16)).to(dev), "K": W["K"], "N": W["N"]}
+
+
+def bench_bf16(args, dev):
+    """The bf16 variant on the headline shapes: the two decode GEMVs (K = 2048,
+    N = 8192 and 151552, rotated weight copies as in the headline) and the
+    prefill GEMM at M = 4096 and 16384 (K = 2048, N = 8192)."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K = 2048
+    Ns = (8192, synth.VOCAB)
+    cases = [synth.gemm_case_bf16(s, 1, K, N) for s, N in zip((0, 1), Ns)]
+    step_bytes = sum(w4_bytes(K, N) + 2 * K + 2 * N for N in Ns)
+    copies = max(2, int(np.ceil(ROTATE_BYTES / step_bytes)))
+    base = [dev_w4_bits(c["W"], dev) for c in cases]
+    Ws = [base] + [[clone_w4(w) for w in base] for _ in range(copies - 1)]
+    x = torch.from_numpy(cases[0]["X"][0].view(np.int16)).to(dev)
+    ys = [torch.empty(N, dtype=torch.bfloat16, device=dev) for N in Ns]
+
+    def step(i):
+        Wc = Ws[i % copies]
+        ql.qlinear_gemv_bf16(Wc[0], x, ys[0])
+        ql.qlinear_gemv_bf16(Wc[1], x, ys[1])
+
+    ms = timed_steps(step, args.steps, args.warmup, settle_s=SETTLE_S)
+    head_ms = timed_steps(lambda i: ql.qlinear_gemv_bf16(Ws[i % copies][1], x, ys[1]), args.steps, args.warmup,
+                          settle_s=SETTLE_S / 2)
+    out = {"gemv_step": {"us": float(ms * 1e3), "GB/s": step_bytes / (ms * 1e-3) / 1e9,
+                         "frac_hbm": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+           "gemv_head": {"us": float(head_ms * 1e3),
+                         "GB/s": (w4_bytes(K, Ns[1]) + 2 * K + 2 * Ns[1]) / (head_ms * 1e-3) / 1e9}}
+    del Ws, base
+    torch.cuda.empty_cache()
+    N = 8192
+    for M in (4096, 16384):
+        c = synth.gemm_case_bf16(0, M, K, N)
+        W = dev_w4_bits(c["W"], dev)
+        X = torch.from_numpy(c["X"].view(np.int16)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = timed_steps(lambda i: ql.qlinear_gemm_bf16(W, X, Y), 20 if M == 4096 else 8, 3, settle_s=SETTLE_S)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[f"gemm_M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf, "frac_mfma_bf16": tf / MFMA_F16_PEAK_TFLOPS}
+        del W, X, Y
+        torch.cuda.empty_cache()
+    return out
+
+
 def moe_dev_weights(w, dev):
     import torch
     return {"Wr": torch.from_numpy(w["Wr"]).to(dev), "gate_up": dev_w4(w["gate_up"], dev),
@@ -576,6 +630,9 @@ def main():
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
             log("bench: few-row GEMM")
             wl["few_rows_gemm"] = bench_few_rows(args, dev)
+        if args.workload in ("all", "bf16"):
+            log("bench: bf16 variant")
+            wl["bf16"] = bench_bf16(args, dev)
         if args.workload in ("all", "decode"):
             log("bench: decode fusions")
             wl["decode_fusions"] = bench_decode_fusions(args, dev)

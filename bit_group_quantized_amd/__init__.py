@@ -56,6 +56,8 @@ _SIGS = {
     "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemm_few_rows": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemv_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
+    "qlinear_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemv_rmsnorm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, ctypes.c_float, _P, _P]),
     "qlinear_gemv_argmax_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
     "qlinear_gemv_argmax": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -140,6 +142,27 @@ def qlinear_gemv(W: dict, x, y=None, stream=None):
     w = make_w4(W)
     _check("qlinear_gemv", lib().qlinear_gemv(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
     return y
+
+
+def qlinear_gemv_bf16(W: dict, x, y=None, stream=None):
+    """y [N] bf16 = x [K] bf16 . dequant(W), W's scales and biases bf16."""
+    import torch
+    if y is None:
+        y = torch.empty((int(W["N"]),), dtype=torch.bfloat16, device=x.device)
+    w = make_w4(W)
+    _check("qlinear_gemv_bf16", lib().qlinear_gemv_bf16(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
+    return y
+
+
+def qlinear_gemm_bf16(W: dict, X, Y=None, stream=None):
+    """Y [M, N] bf16 = X [M, K] bf16 . dequant(W), W's scales and biases bf16."""
+    import torch
+    M = int(X.shape[0])
+    if Y is None:
+        Y = torch.empty((M, int(W["N"])), dtype=torch.bfloat16, device=X.device)
+    w = make_w4(W)
+    _check("qlinear_gemm_bf16", lib().qlinear_gemm_bf16(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
+    return Y
 
 
 def qlinear_gemv_rmsnorm(W: dict, x, gamma, eps: float, y=None, stream=None):

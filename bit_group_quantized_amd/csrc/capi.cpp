@@ -140,6 +140,30 @@ int qlinear_embed_token(const ql_w4* E, const int32_t* token, uint16_t* x, void*
     return ql::launch_embed(a, as_stream(stream));
 }
 
+int qlinear_gemv_bf16(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (!ql::gemv_fused_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N == 0) return QL_OK;
+    if (!x || !y) return QL_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemvArgs a{W->qweight, W->scales, W->biases, x, y, W->K, W->N};
+    return ql::launch_gemv_bf16(a, as_stream(stream));
+}
+
+int qlinear_gemm_bf16(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
+    if (!W || M < 0) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (W->N == 0 || M == 0) return QL_OK;
+    if (M > (int64_t)0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemmArgs a{W->qweight, W->scales, W->biases, X, Y, M, W->K, W->N};
+    return ql::launch_gemm_bf16(a, as_stream(stream));
+}
+
 size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk) {
     if (T < 0 || E <= 0 || E > QL_MAX_EXPERTS || topk <= 0 || topk > E || topk > QL_MAX_TOPK)
         return 0;

@@ -124,9 +124,12 @@ struct Job {
     const uint16_t* wb;
 };
 
-template <int WM, int WN, int WGM, int WGN, int MODE>
+// DT: 0 = fp16 activations, scales, biases, outputs and MFMA operands;
+// 1 = bf16 throughout (dense mode only).
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
+    static_assert(DT == 0 || MODE == MODE_DENSE, "bf16 is served by the dense GEMM only");
     constexpr int BM = TL::BM, BN = TL::BN;
     f16* As = lds;                     // [2][BM][kLdk]
     f16* Bs = lds + 2 * TL::LDS_A;     // [2][BN][kLdk]
@@ -252,6 +255,15 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                 o.w = __builtin_amdgcn_perm(hreg[S][7][j >> 1], hreg[S][6][j >> 1], sel);
                 *reinterpret_cast<u32x4*>(b_dst + (8 * nb + j) * kLdk + 8 * kb) = o;
             }
+        } else if constexpr (DT == 1) {
+            const float sf = bf2f(sreg[S]), bf = bf2f(bireg[S]);
+            constexpr int W = TL::WPT;  // words of this thread's column per step
+#pragma unroll
+            for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
+                const uint32_t u = breg[S][w >> 2][w & 3];
+                const int word = bpart * W + w;  // 0..7 within the group
+                *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = dequant_word_bf16(u, sf, bf);
+            }
         } else {
             const f16 sv = __builtin_bit_cast(f16, sreg[S]);
             const f16 bv = __builtin_bit_cast(f16, bireg[S]);
@@ -288,7 +300,11 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
         for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < WN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                if constexpr (DT == 1)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
     };
 
     // One 16-wide K slice of step data in LDS buffer S: its MFMAs, a quarter
@@ -377,6 +393,10 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     }
 
     // ---- epilogue -------------------------------------------------------------
+    auto to16 = [](float v) -> uint16_t {
+        if constexpr (DT == 1) return f2bf(v);
+        else return f2h(v);
+    };
     // The MFMAs take the weight fragment as their first operand, so each
     // accumulator holds the transposed product: acc[i][j][r] is output row
     // 32i + l%32 of the wave tile and column 32j + 8(r/4) + 4h + r%4.  A lane
@@ -434,8 +454,8 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                 for (int g = 0; g < 4; ++g) {
                     float v[4];
                     out_vals(i, j, g, v);
-                    const uint32_t lo = (uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16);
+                    const uint32_t lo = (uint32_t)to16(v[0]) | ((uint32_t)to16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)to16(v[2]) | ((uint32_t)to16(v[3]) << 16);
                     *reinterpret_cast<uint2*>(reg + fl * LDR + 32 * j + 8 * g + 4 * fh) = make_uint2(lo, hi);
                 }
             __syncthreads();
@@ -466,7 +486,7 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                     const int col = wcol0 + 32 * j + 8 * g + 4 * fh;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (col + e < out_cols) yrow[col + e] = f2h(v[e]);
+                        if (col + e < out_cols) yrow[col + e] = to16(v[e]);
                 }
         }
     }
@@ -583,7 +603,7 @@ gemm_ws_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
 }
 
 // Dense prefill GEMM and the router GEMM.
-template <int WM, int WN, int WGM, int WGN, int MODE>
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_w4_kernel(const KParams p) {
     using TL = Tile<WM, WN, WGM, WGN>;
@@ -618,7 +638,7 @@ gemm_w4_kernel(const KParams p) {
         job.kz = blockIdx.z;
     }
     job.rows_valid = (int)min<int64_t>(BM, p.M - job.out_row0);
-    gemm_tile<WM, WN, WGM, WGN, MODE>(p, job, lds);
+    gemm_tile<WM, WN, WGM, WGN, MODE, DT>(p, job, lds);
 }
 
 // Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
@@ -693,25 +713,26 @@ gemm_w4_grouped_kernel(const KParams p) {
         gemm_tile<2, 2, 2, 4, MODE>(p, job, lds);
 }
 
-template <int WM, int WN, int WGM, int WGN, int MODE>
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
 int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
     using TL = Tile<WM, WN, WGM, WGN>;
     static bool attr_done = false;  // benign race: the attribute is idempotent
     if (!attr_done) {
-        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE>,
+        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)TL::LDS_BYTES) != hipSuccess)
             return QL_ERR_HIP;
         attr_done = true;
     }
-    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE>), grid, dim3(TL::NT), TL::LDS_BYTES, st,
+    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>), grid, dim3(TL::NT), TL::LDS_BYTES, st,
                        p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 }  // namespace
 
-int launch_gemm(const GemmArgs& a, hipStream_t st) {
+template <int DT>
+int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
     KParams p{};
     p.A = a.X;
     p.M = a.M;
@@ -741,7 +762,7 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     do {                                                                           \
         using TL = Tile<A, B, C, D>;                                               \
         if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;      \
-        return launch_t<A, B, C, D, MODE_DENSE>(p, grid, st);                      \
+        return launch_t<A, B, C, D, MODE_DENSE, DT>(p, grid, st);                  \
     } while (0)
     if (t128 > 512) QL_DENSE(4, 2, 2, 4);  // 256 x 256, 8 waves of 128 x 64
     if (t128 > 256) QL_DENSE(2, 2, 2, 4);  // 128 x 256, 8 waves of 64 x 64
@@ -749,6 +770,10 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) {
     QL_DENSE(1, 2, 2, 2);                  // 64 x 128, 4 waves of 32 x 64
 #undef QL_DENSE
 }
+
+int launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0>(a, st); }
+
+int launch_gemm_bf16(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<1>(a, st); }
 
 bool gemm_ws_supported(int K) { return K == 512 || K == 1024 || K == 2048; }
 

@@ -324,6 +324,74 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
     }
 }
 
+// bf16 variant of the chunked GEMV: bf16 activations, scales, biases and
+// outputs ([PPLX] dequantization section: the page's checkpoint keeps scale
+// and bias in bf16).  Same lane layout as above; the codes enter v_dot2 as
+// bf16 128 + q (0x4300 exponent) against activation pairs (x_j, x_{j+4}),
+// and 128 * sum(x) is removed per chunk.
+template <int TPR, int V, int R>
+__global__ void __launch_bounds__(256)
+gemv_w4_bf16_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                    const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
+                    uint16_t* __restrict__ y, int K, int N) {
+    constexpr int TEAMS = 64 / TPR;
+    const int lane = threadIdx.x & 63;
+    const int lr = lane % TPR;
+    const int team = lane / TPR;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int gwave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+    const int row0 = (gwave * TEAMS + team) * R;
+    u32x4 xr[V][4];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(x + (lr + v * TPR) * 32 + w * 8);
+    u32x4 cw[R][V];
+    uint16_t s[R][V], b[R][V];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int hg = lr + v * TPR;
+            cw[r][v] = ld_stream_u32x4(qw + (size_t)row * wpr + hg * 4);
+            s[r][v] = sc[(size_t)row * G + (hg >> 1)];
+            b[r][v] = bi[(size_t)row * G + (hg >> 1)];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    XPairsBf xp[V][4];
+    float xs[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        xs[v] = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            xp[v][w] = make_xpairs_bf(xr[v][w]);
+            xs[v] += xsum_bf(xp[v][w]);
+        }
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc[r] = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+            dot_word_bf(cw[r][v].x, xp[v][0], d0, d1, d2, d3);
+            dot_word_bf(cw[r][v].y, xp[v][1], d0, d1, d2, d3);
+            dot_word_bf(cw[r][v].z, xp[v][2], d0, d1, d2, d3);
+            dot_word_bf(cw[r][v].w, xp[v][3], d0, d1, d2, d3);
+            const float d = (d0 + d2) + (d1 + d3);
+            acc[r] += bf2f(s[r][v]) * (d - 128.0f * xs[v]) + bf2f(b[r][v]) * xs[v];
+        }
+    }
+    int rsel;
+    const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
+    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2bf(tot);
+}
+
 // Largest of n block keys -> token id (0 when no output was comparable).
 __global__ void __launch_bounds__(1024)
 argmax_finish_kernel(const uint64_t* __restrict__ partials, int n, int N, int32_t* __restrict__ token) {
@@ -748,6 +816,36 @@ bool gemv_fused_supported(int K) {
     switch (K) {
         case 256: case 512: case 1024: case 2048: case 4096: case 8192: case 16384: return true;
         default: return false;
+    }
+}
+
+template <int TPR, int V, int R>
+int launch_bf16_t(const GemvArgs& a, hipStream_t st) {
+    constexpr int ROWS_PER_BLOCK = 4 * (64 / TPR) * R;
+    const int blocks = (a.N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    hipLaunchKernelGGL((gemv_w4_bf16_kernel<TPR, V, R>), dim3(blocks), dim3(256), 0, st, a.qweight,
+                       a.scales, a.biases, a.x, a.y, a.K, a.N);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
+template <int TPR, int V>
+int launch_bf16_r(const GemvArgs& a, hipStream_t st) {
+    constexpr int R = (kGemvRows < TPR) ? kGemvRows : TPR;
+    const long blocks_big = (a.N + 4L * (64 / TPR) * R - 1) / (4L * (64 / TPR) * R);
+    if (blocks_big >= kGemvMinBlocks || R <= 2) return launch_bf16_t<TPR, V, R>(a, st);
+    return launch_bf16_t<TPR, V, 2>(a, st);
+}
+
+int launch_gemv_bf16(const GemvArgs& a, hipStream_t st) {
+    switch (a.K) {
+        case 256: return launch_bf16_r<8, 1>(a, st);
+        case 512: return launch_bf16_r<16, 1>(a, st);
+        case 1024: return launch_bf16_r<32, 1>(a, st);
+        case 2048: return launch_bf16_r<64, 1>(a, st);
+        case 4096: return launch_bf16_r<64, 2>(a, st);
+        case 8192: return launch_bf16_t<64, 4, 4>(a, st);
+        case 16384: return launch_bf16_t<64, 8, 2>(a, st);
+        default: return QL_ERR_UNSUPPORTED_SHAPE;
     }
 }
 

@@ -81,6 +81,78 @@ __device__ __forceinline__ f16x8 dequant_word(uint32_t u, f16x2 s2, f16x2 b2) {
     return __builtin_bit_cast(f16x8, o);
 }
 
+// ---- bf16 ------------------------------------------------------------------
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 pattern -> float (exact: a bf16 is the upper half of a float).
+__device__ __forceinline__ float bf2f(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
+
+// float -> bf16 pattern, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Dequantize one word (codes k = 8w .. 8w+7) to 8 bf16 values in natural k
+// order: bf16(s*q + b) from one fp32 fma per value (exact for the weights of
+// this format, whose scale*code + bias needs far fewer than 24 bits) and one
+// rounding to bf16.  The nibbles are split into bytes and converted with
+// v_cvt_f32_ubyte.
+__device__ __forceinline__ u32x4 dequant_word_bf16(uint32_t u, float s, float b) {
+    const uint32_t lo = u & 0x0F0F0F0Fu;          // q0 q2 q4 q6 in bytes 0..3
+    const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;   // q1 q3 q5 q7
+    auto byte = [](uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); };  // v_cvt_f32_ubyteN
+    u32x4 o;
+    o.x = pack_bf16x2(fmaf(byte(lo, 0), s, b), fmaf(byte(hi, 0), s, b));
+    o.y = pack_bf16x2(fmaf(byte(lo, 1), s, b), fmaf(byte(hi, 1), s, b));
+    o.z = pack_bf16x2(fmaf(byte(lo, 2), s, b), fmaf(byte(hi, 2), s, b));
+    o.w = pack_bf16x2(fmaf(byte(lo, 3), s, b), fmaf(byte(hi, 3), s, b));
+    return o;
+}
+
+// bf16 row GEMV: for one word u and activations x0..x7 (bf16 pairs (x0,x1)
+// (x2,x3) (x4,x5) (x6,x7) in xw), code pairs come from the 0x4300 exponent
+// (bf16 128 with unit 1 in the last place): ((u >> 4j) & 0x000F000F) | magic
+// = (128 + q_j, 128 + q_{j+4}), paired with (x_j, x_{j+4}).  The products
+// are exact in fp32; sum_k x_k (128 + q_k) = sum_k x_k q_k + 128 sum_k x_k.
+struct XPairsBf {
+    bf16x2 p[4];  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+};
+
+__device__ __forceinline__ XPairsBf make_xpairs_bf(u32x4 xw) {
+    XPairsBf r;
+    r.p[0] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(xw.z, xw.x, 0x05040100u));
+    r.p[1] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(xw.z, xw.x, 0x07060302u));
+    r.p[2] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(xw.w, xw.y, 0x05040100u));
+    r.p[3] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(xw.w, xw.y, 0x07060302u));
+    return r;
+}
+
+__device__ __forceinline__ float dot2bf(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// Sum of the eight activations of one word (dot products with (1, 1)).
+__device__ __forceinline__ float xsum_bf(const XPairsBf& r) {
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = dot2bf(r.p[i], one2, s);
+    return s;
+}
+
+__device__ __forceinline__ void dot_word_bf(uint32_t u, const XPairsBf& x, float& d0, float& d1, float& d2,
+                                            float& d3) {
+    constexpr uint32_t magic = 0x43004300u;
+    d0 = dot2bf(x.p[0], __builtin_bit_cast(bf16x2, and_or(u, 0x000F000Fu, magic)), d0);
+    d1 = dot2bf(x.p[1], __builtin_bit_cast(bf16x2, and_or(u >> 4, 0x000F000Fu, magic)), d1);
+    d2 = dot2bf(x.p[2], __builtin_bit_cast(bf16x2, and_or(u >> 8, 0x000F000Fu, magic)), d2);
+    d3 = dot2bf(x.p[3], __builtin_bit_cast(bf16x2, and_or(u >> 12, 0x000F000Fu, magic)), d3);
+}
+
 // Activation pre-pairing for the dot-product form of the row GEMV.
 // For one word u of codes q0..q7 (k = 8w .. 8w+7):
 //   c0 = (u & 0x000F000F) | magic       = (1024 + q0,    1024 + q4)

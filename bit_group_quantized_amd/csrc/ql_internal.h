@@ -29,6 +29,8 @@ int launch_gemv(const GemvArgs& a, hipStream_t st);
 // K with the chunked kernel (powers of two 256 .. 16384): the fused variants.
 bool gemv_fused_supported(int K);
 int launch_gemv_rmsnorm(const GemvArgs& a, hipStream_t st);
+// bf16 activations, scales, biases and outputs; the chunked K set.
+int launch_gemv_bf16(const GemvArgs& a, hipStream_t st);
 // Writes a.y if non-null, the block keys to a.partials (at most
 // ceil(N / 8) of them) and the token id to a.token.
 int launch_gemv_argmax(const GemvArgs& a, hipStream_t st);
@@ -45,6 +47,8 @@ struct GemmArgs {
     int K, N;
 };
 int launch_gemm(const GemmArgs& a, hipStream_t st);
+// bf16 activations, scales, biases and outputs (same tile table).
+int launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 bool gemm_ws_supported(int K);                          // few-row GEMM shapes
 int launch_gemm_ws(const GemmArgs& a, hipStream_t st);  // few-row GEMM (weight-stationary)
 

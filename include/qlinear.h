@@ -11,6 +11,7 @@
  *                                      256 experts plus one shared expert)
  *     "优化单行权重路径"              the row-parallel single-row GEMV
  *     "减少中间状态和流量"            the fused decode expert chains
+ *     "将 token 交接保留在 GPU 上"    the token hand-off kept on the GPU
  *   [LAYA] laya-mlx, "工程调查：这个 MLX 端口还能再快 10× 吗？",
  *     "选择性量化": affine quantization with group size 64.
  *
@@ -164,6 +165,23 @@ int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void
  */
 int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y,
                           void* stream);
+
+/*
+ * qlinear_gemv_bf16, qlinear_gemm_bf16 - the same two layers with bf16
+ * activations, scales, biases and outputs ([PPLX] dequantization section:
+ * the page's checkpoint keeps scale and bias in bf16 and its matrix path
+ * multiplies bf16 operands).  W's scales and biases hold bf16 bit patterns
+ * (same [N][K/64] layout); x / X and y / Y are bf16, row-major.
+ * Accumulation is in fp32; outputs are rounded to bf16, nearest even.  The
+ * GEMV multiplies the exact codes (v_dot2 on bf16 pairs); the GEMM rounds
+ * each dequantized weight scale*code + bias once to bf16 for the MFMA.
+ * qlinear_gemm_bf16 keeps qlinear_gemm's tile table and its row invariance.
+ * Limits: qlinear_gemv_bf16 takes K a power of two from 256 to 16384.
+ * Errors: as qlinear_gemv / qlinear_gemm; UNSUPPORTED_SHAPE for another K
+ * in qlinear_gemv_bf16.
+ */
+int qlinear_gemv_bf16(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream);
+int qlinear_gemm_bf16(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 
 /*
  * qlinear_gemv_rmsnorm - y = fp16(rmsnorm(x)) . dequant(W): a decode

@@ -9,6 +9,15 @@ import numpy as np
 
 REL_L2 = 1e-3
 MAX_ABS_FRAC = 5e-3
+# bf16 outputs (derived, no stated bar): a bf16 has 8 significant bits, so
+# rounding an output is off by at most 2**-8 = 3.9e-3 relative and by about
+# 1.6e-3 RMS over a spread of mantissas (measured 1.2e-3 to 1.9e-3 for the
+# GEMV, which multiplies the exact codes); the GEMM also rounds each
+# dequantized weight to bf16 once, about 1.5e-3 more (measured 2.2e-3 in
+# total).  Bars: rel-L2 <= 4e-3 (the per-element bound) and max-abs <=
+# 1.6e-2 * max|ref| (four times it).
+REL_L2_BF16 = 4e-3
+MAX_ABS_FRAC_BF16 = 1.6e-2
 
 
 def dev():
@@ -17,11 +26,14 @@ def dev():
 
 
 def t(a, device=None):
-    """numpy -> torch on the GPU (uint32 arrays travel as int32 bit patterns)."""
+    """numpy -> torch on the GPU (uint32 / uint16 arrays travel as int32 /
+    int16 bit patterns)."""
     import torch
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint32:
         a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
     return torch.from_numpy(a).to(device or dev())
 
 
@@ -45,12 +57,18 @@ def errors(gpu, ref):
     return rel, mabs, mref
 
 
-def assert_close(gpu, ref, what=""):
+def assert_close(gpu, ref, what="", rel_l2=REL_L2, max_abs_frac=MAX_ABS_FRAC):
     rel, mabs, mref = errors(gpu, ref)
     assert np.all(np.isfinite(np.asarray(gpu, dtype=np.float64))), f"{what}: non-finite output"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e} > {REL_L2}"
-    assert mabs <= MAX_ABS_FRAC * mref + 1e-30, f"{what}: max-abs {mabs:.3e} > {MAX_ABS_FRAC}*{mref:.3e}"
+    assert rel <= rel_l2, f"{what}: rel-L2 {rel:.3e} > {rel_l2}"
+    assert mabs <= max_abs_frac * mref + 1e-30, f"{what}: max-abs {mabs:.3e} > {max_abs_frac}*{mref:.3e}"
     return rel, mabs / max(mref, 1e-30)
+
+
+def assert_close_bf16(gpu_bits, ref, what=""):
+    """gpu_bits: bf16 patterns (uint16 / int16 array); ref: float64."""
+    g = (np.asarray(gpu_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return assert_close(g, ref, what, REL_L2_BF16, MAX_ABS_FRAC_BF16)
 
 
 def say(*a):

@@ -214,3 +214,19 @@ def test_embed_token_validation(L):
     assert f(ctypes.byref(_w()), A16, None, None) == INVALID
     assert f(ctypes.byref(_w()), A16 + 2, A16, None) == MISALIGNED
     assert f(ctypes.byref(_w()), A16, A16 + 8, None) == MISALIGNED
+
+
+def test_bf16_validation(L):
+    f = L.qlinear_gemv_bf16
+    assert f(None, A16, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=192)), A16, A16, None) == SHAPE      # not a power of two
+    assert f(ctypes.byref(_w(K=65536)), A16, A16, None) == SHAPE
+    assert f(ctypes.byref(_w()), A16 + 8, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w()), None, A16, None) == INVALID
+    assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), None, None, None) == OK
+    g = L.qlinear_gemm_bf16
+    assert g(ctypes.byref(_w()), A16, -1, A16, None) == INVALID
+    assert g(ctypes.byref(_w()), A16, 0, A16, None) == OK
+    assert g(ctypes.byref(_w(K=96)), A16, 4, A16, None) == SHAPE
+    assert g(ctypes.byref(_w()), A16 + 2, 4, A16, None) == MISALIGNED
+    assert g(ctypes.byref(_w()), None, 4, A16, None) == INVALID

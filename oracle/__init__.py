@@ -18,7 +18,9 @@ eye against the pages it cites:
   "减少中间状态和流量" (reducing intermediates and traffic) and
   "将 token 交接保留在 GPU 上" (keeping the token hand-off on the GPU);
 * laya-mlx, "工程调查：这个 MLX 端口还能再快 10× 吗？", section
-  "选择性量化" (affine quantization with group size 64).
+  "选择性量化" (affine quantization with group size 64);
+* "待验证｜lithos-metal补Apple推理内核", section "一分钟内合并了什么" (FP8
+  E4M3 decode and an NVFP4 checkpoint: the second codecs).
 
 Where the pages leave a step open, the plainest reading is taken; each such
 reading is named in the function that applies it.
@@ -36,6 +38,8 @@ from .route import (router_logits, softmax, topk_route, histogram,
 from .moe import silu, expert_ffn, combine, moe_layer
 from .decode import rms_norm, gemv_rmsnorm, argmax_first, lm_head_token, embed_row
 from .bf16 import bf16_to_f64, round_bf16, dequantize_bf16, linear_bf16
+from .codecs import (e4m3_to_f64, e2m1_to_f64, dequantize_fp8, dequantize_nvfp4, linear_fp8,
+                     linear_nvfp4)
 
 __all__ = [
     "GROUP", "unpack_codes", "pack_codes", "dequantize", "linear", "round_f16",
@@ -44,4 +48,5 @@ __all__ = [
     "silu", "expert_ffn", "combine", "moe_layer",
     "rms_norm", "gemv_rmsnorm", "argmax_first", "lm_head_token", "embed_row",
     "bf16_to_f64", "round_bf16", "dequantize_bf16", "linear_bf16",
+    "e4m3_to_f64", "e2m1_to_f64", "dequantize_fp8", "dequantize_nvfp4", "linear_fp8", "linear_nvfp4",
 ]

@@ -26,7 +26,12 @@ these seeded draws stand in for it):
 * decode row in front of a normalization (residual stream): fp16 of
   N(0, 16), i.e. 4 * N(0, 1); normalization gain: fp16 of U(0.5, 1.5);
 * bf16 variants: the same draws stored as bf16 bit patterns (uint16, the
-  upper half of the float32 pattern, nearest even).
+  upper half of the float32 pattern, nearest even);
+* FP8-E4M3 weights: codes uniform over the 254 non-NaN bytes, one fp16 scale
+  per 64 along K from U(1e-4, 1e-3);
+* NVFP4 weights: E2M1 codes uniform (uniform 32-bit words, as the w4 codes),
+  E4M3 block scales with exponent field uniform in 5..9 and mantissa
+  uniform (values 0.25 .. 3.75), positive; global scale 0.01 (fp32).
 """
 from __future__ import annotations
 
@@ -101,6 +106,24 @@ def gemm_case_bf16(seed: int, M: int, K: int, N: int) -> dict:
     X = bf16_bits(rng.standard_normal((M, K)))
     W = w4_matrix_bf16(rng, K, N)
     return {"X": X, "W": W}
+
+
+def fp8_matrix(rng: np.random.Generator, K: int, N: int) -> dict:
+    """FP8-E4M3 weights: codes uint8 [N][K] (no NaN codes), fp16 scales [N][K/64]."""
+    codes = rng.integers(0, 254, size=(N, K), dtype=np.int64)
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)   # skip 0x7F (and 0xFF)
+    scales = f16(rng.uniform(1e-4, 1e-3, size=(N, K // 64)))
+    return {"codes": codes, "scales": scales, "K": K, "N": N}
+
+
+def nvfp4_matrix(rng: np.random.Generator, K: int, N: int) -> dict:
+    """NVFP4 weights: qweight uint32 [N][K/8] (E2M1 codes, w4 packing),
+    block scales uint8 [N][K/16] (positive E4M3), global scale fp32."""
+    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    e = rng.integers(5, 10, size=(N, K // 16))
+    m = rng.integers(0, 8, size=(N, K // 16))
+    block = ((e << 3) | m).astype(np.uint8)
+    return {"qweight": words, "block_scales": block, "global_scale": np.float32(0.01), "K": K, "N": N}
 
 
 def router_weight(rng: np.random.Generator, D: int = HIDDEN, E: int = NUM_EXPERTS) -> np.ndarray:

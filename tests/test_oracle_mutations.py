@@ -260,3 +260,50 @@ def test_bf16_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(obf, attr, mutant)
     monkeypatch.setattr(oracle, attr, mutant)
     assert _fails(BF16_PINS)
+
+
+import oracle.codecs as ocod
+from tests import test_oracle_codecs as tc
+
+CODEC_PINS = [tc.test_e4m3_hand_table_and_nan, tc.test_e2m1_table, tc.test_fp8_linear_hand_fixture,
+              tc.test_fp8_one_hot_and_bruteforce, tc.test_nvfp4_block_scales_and_global,
+              tc.test_nvfp4_bruteforce]
+
+_ORIG_E4M3 = ocod.e4m3_to_f64
+
+
+def _e4m3_bias8(codes):
+    return _ORIG_E4M3(codes) / 2.0          # exponent bias 8 instead of 7
+
+
+def _e2m1_no_subnormal(n):
+    n = np.asarray(n, dtype=np.int64)
+    s = np.where(n & 0x8, -1.0, 1.0)
+    e = (n >> 1) & 0x3
+    m = (n & 0x1).astype(np.float64)
+    return s * (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+
+
+def _nvfp4_block32(qweight, block_scales, global_scale, K):
+    q = ocod.e2m1_to_f64(ocod.unpack_codes(qweight, K))
+    bs = np.repeat(ocod.e4m3_to_f64(block_scales), 32, axis=-1)[..., :K]
+    bs = np.pad(bs, [(0, 0)] * (bs.ndim - 1) + [(0, K - bs.shape[-1])], mode="edge")
+    return q * bs * float(global_scale)
+
+
+def _fp8_scale_index(codes, scales):
+    codes = np.asarray(codes, dtype=np.uint8)
+    s = np.tile(np.asarray(scales, dtype=np.float16).astype(np.float64), 64)
+    return ocod.e4m3_to_f64(codes) * s
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("e4m3_to_f64", _e4m3_bias8),
+    ("e2m1_to_f64", _e2m1_no_subnormal),
+    ("dequantize_nvfp4", _nvfp4_block32),
+    ("dequantize_fp8", _fp8_scale_index),
+])
+def test_codec_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(ocod, attr, mutant)
+    monkeypatch.setattr(oracle, attr, mutant)
+    assert _fails(CODEC_PINS)

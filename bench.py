@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
-    ap.add_argument("--workload", choices=["all", "gemm", "decode", "bf16", "moe_decode", "moe_prefill"],
+    ap.add_argument("--workload", choices=["all", "gemm", "decode", "bf16", "codecs", "moe_decode",
+                                           "moe_prefill"],
                     default="all",
                     help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -401,6 +402,56 @@ def bench_bf16(args, dev):
     return out
 
 
+def bench_codecs(args, dev):
+    """The second weight codecs on the headline decode shapes: FP8-E4M3 (1
+    byte per weight + an fp16 scale per 64) and NVFP4 (half a byte + an E4M3
+    scale per 16) GEMVs at K = 2048, N = 8192 and 151552, rotated weight
+    copies as in the headline; bytes = codes + scales + x + y."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    K = 2048
+    Ns = (8192, synth.VOCAB)
+    out = {}
+    for codec in ("fp8", "nvfp4"):
+        mats, nbytes = [], []
+        for seed, N in zip((0, 1), Ns):
+            rng = synth.rng_for(seed)
+            if codec == "fp8":
+                W = synth.fp8_matrix(rng, K, N)
+                mats.append({"codes": torch.from_numpy(W["codes"]).to(dev),
+                             "scales": torch.from_numpy(W["scales"]).to(dev), "K": K, "N": N})
+                nbytes.append(N * K + 2 * N * (K // 64) + 2 * K + 2 * N)
+            else:
+                W = synth.nvfp4_matrix(rng, K, N)
+                mats.append({"qweight": torch.from_numpy(W["qweight"].view(np.int32)).to(dev),
+                             "block_scales": torch.from_numpy(W["block_scales"]).to(dev),
+                             "global_scale": float(W["global_scale"]), "K": K, "N": N})
+                nbytes.append(N * K // 2 + N * (K // 16) + 2 * K + 2 * N)
+        step_bytes = sum(nbytes)
+        copies = max(2, int(np.ceil(ROTATE_BYTES / step_bytes)))
+        Ws = [mats] + [[{k: (v.clone() if hasattr(v, "clone") else v) for k, v in m.items()} for m in mats]
+                       for _ in range(copies - 1)]
+        fn = ql.qlinear_gemv_fp8 if codec == "fp8" else ql.qlinear_gemv_nvfp4
+        x = torch.from_numpy(synth.activations(synth.rng_for(5), 1, K)[0]).to(dev)
+        ys = [torch.empty(N, dtype=torch.float16, device=dev) for N in Ns]
+
+        def step(i):
+            fn(Ws[i % copies][0], x, ys[0])
+            fn(Ws[i % copies][1], x, ys[1])
+
+        ms = timed_steps(step, args.steps, args.warmup, settle_s=SETTLE_S)
+        head_ms = timed_steps(lambda i: fn(Ws[i % copies][1], x, ys[1]), args.steps, args.warmup,
+                              settle_s=SETTLE_S / 2)
+        out[codec] = {"step_us": float(ms * 1e3), "step_GB/s": step_bytes / (ms * 1e-3) / 1e9,
+                      "frac_hbm": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "head_us": float(head_ms * 1e3), "head_GB/s": nbytes[1] / (head_ms * 1e-3) / 1e9,
+                      "step_bytes": step_bytes}
+        del Ws, mats
+        torch.cuda.empty_cache()
+    return out
+
+
 def moe_dev_weights(w, dev):
     import torch
     return {"Wr": torch.from_numpy(w["Wr"]).to(dev), "gate_up": dev_w4(w["gate_up"], dev),
@@ -633,6 +684,9 @@ def main():
         if args.workload in ("all", "bf16"):
             log("bench: bf16 variant")
             wl["bf16"] = bench_bf16(args, dev)
+        if args.workload in ("all", "codecs"):
+            log("bench: second codecs")
+            wl["codecs"] = bench_codecs(args, dev)
         if args.workload in ("all", "decode"):
             log("bench: decode fusions")
             wl["decode_fusions"] = bench_decode_fusions(args, dev)

@@ -47,6 +47,16 @@ class ql_w4_experts(ctypes.Structure):
                 ("group_size", ctypes.c_int32), ("num_experts", ctypes.c_int32)]
 
 
+class ql_fp8(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("K", ctypes.c_int32),
+                ("N", ctypes.c_int32)]
+
+
+class ql_nvfp4(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("block_scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_float), ("K", ctypes.c_int32), ("N", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _SIGS = {
@@ -56,6 +66,8 @@ _SIGS = {
     "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemm_few_rows": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemv_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8), _P, _P, _P]),
+    "qlinear_gemv_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4), _P, _P, _P]),
     "qlinear_gemv_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemv_rmsnorm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, ctypes.c_float, _P, _P]),
@@ -141,6 +153,29 @@ def qlinear_gemv(W: dict, x, y=None, stream=None):
         y = torch.empty((int(W["N"]),), dtype=torch.float16, device=x.device)
     w = make_w4(W)
     _check("qlinear_gemv", lib().qlinear_gemv(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
+    return y
+
+
+def qlinear_gemv_fp8(W: dict, x, y=None, stream=None):
+    """y [N] fp16 = x [K] fp16 . W, W = {"codes": uint8 [N, K] E4M3,
+    "scales": fp16 [N, K/64], "K", "N"}."""
+    import torch
+    if y is None:
+        y = torch.empty((int(W["N"]),), dtype=torch.float16, device=x.device)
+    w = ql_fp8(W["codes"].data_ptr(), W["scales"].data_ptr(), int(W["K"]), int(W["N"]))
+    _check("qlinear_gemv_fp8", lib().qlinear_gemv_fp8(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
+    return y
+
+
+def qlinear_gemv_nvfp4(W: dict, x, y=None, stream=None):
+    """y [N] fp16 = x [K] fp16 . W, W = {"qweight": int32 [N, K/8] E2M1,
+    "block_scales": uint8 [N, K/16] E4M3, "global_scale": float, "K", "N"}."""
+    import torch
+    if y is None:
+        y = torch.empty((int(W["N"]),), dtype=torch.float16, device=x.device)
+    w = ql_nvfp4(W["qweight"].data_ptr(), W["block_scales"].data_ptr(), float(W["global_scale"]),
+                 int(W["K"]), int(W["N"]))
+    _check("qlinear_gemv_nvfp4", lib().qlinear_gemv_nvfp4(ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
     return y
 
 

@@ -164,6 +164,41 @@ int qlinear_gemm_bf16(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y,
     return ql::launch_gemm_bf16(a, as_stream(stream));
 }
 
+int qlinear_gemv_fp8(const ql_fp8* W, const uint16_t* x, uint16_t* y, void* stream) {
+    if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
+    if (!ql::gemv_fp8_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N == 0) return QL_OK;
+    if (!W->codes || !W->scales || !x || !y) return QL_ERR_INVALID_ARG;
+    if (!aligned(W->codes, 16) || !aligned(W->scales, 2) || !aligned(x, 16) || !aligned(y, 2))
+        return QL_ERR_MISALIGNED;
+    ql::CodecArgs a;
+    a.codes8 = W->codes;
+    a.scales = W->scales;
+    a.x = x;
+    a.y = y;
+    a.K = W->K;
+    a.N = W->N;
+    return ql::launch_gemv_fp8(a, as_stream(stream));
+}
+
+int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* stream) {
+    if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
+    if (!ql::gemv_nvfp4_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N == 0) return QL_OK;
+    if (!W->qweight || !W->block_scales || !x || !y) return QL_ERR_INVALID_ARG;
+    if (!aligned(W->qweight, 16) || !aligned(W->block_scales, 2) || !aligned(x, 16) || !aligned(y, 2))
+        return QL_ERR_MISALIGNED;
+    ql::CodecArgs a;
+    a.codes4 = W->qweight;
+    a.block_scales = W->block_scales;
+    a.global_scale = W->global_scale;
+    a.x = x;
+    a.y = y;
+    a.K = W->K;
+    a.N = W->N;
+    return ql::launch_gemv_nvfp4(a, as_stream(stream));
+}
+
 size_t moe_workspace_bytes(int32_t T, int32_t E, int32_t topk) {
     if (T < 0 || E <= 0 || E > QL_MAX_EXPERTS || topk <= 0 || topk > E || topk > QL_MAX_TOPK)
         return 0;

@@ -28,13 +28,6 @@ namespace ql {
 
 namespace {
 
-// Team reduction over TPR consecutive lanes.
-template <int TPR>
-__device__ __forceinline__ float team_sum(float v) {
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 // Dot product of one group (8 words) with pre-paired activations.
 __device__ __forceinline__ float group_dot(const u32x4& c0, const u32x4& c1, const XPairs* xp) {
@@ -155,31 +148,6 @@ gemv_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
 // and adds the partner's copy of them, so R rows cost R-1 shuffles, not
 // R*log2(TPR).
 // ---------------------------------------------------------------------------
-template <int TPR, int R>
-__device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
-    static_assert(R <= TPR, "each row needs its own lane after the halving steps");
-    if constexpr (TPR == 64 && (R == 1 || R == 2 || R == 4 || R == 8)) return reduce_rows64<R>(v, lr, row);
-    int base = 0;
-#pragma unroll
-    for (int off = TPR / 2, cnt = R; off >= 1; off >>= 1) {
-        if (cnt > 1) {
-            const bool hi = (lr & off) != 0;
-            const int h = cnt / 2;
-#pragma unroll
-            for (int i = 0; i < h; ++i) {
-                const float send = hi ? v[i] : v[i + h];
-                const float keep = hi ? v[i + h] : v[i];
-                v[i] = keep + __shfl_xor(send, off, 64);
-            }
-            if (hi) base += h;
-            cnt = h;
-        } else {
-            v[0] += __shfl_xor(v[0], off, 64);
-        }
-    }
-    row = base;
-    return v[0];
-}
 
 // Prologue and epilogue variants of the chunked GEMV (the decode steps on
 // either side of a projection; Perplexity, "Optimizing on-device inference

@@ -272,6 +272,43 @@ __device__ __forceinline__ float reduce_rows64(const float (&v)[R], int lane, in
     return t;
 }
 
+// Team reduction over TPR consecutive lanes.
+template <int TPR>
+__device__ __forceinline__ float team_sum(float v) {
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Row reduction of a team of TPR lanes holding partials of the same R rows:
+// afterwards the lanes with (lane % TPR) & (TPR / R - 1) == 0 hold one row
+// total each, row = the returned index.
+template <int TPR, int R>
+__device__ __forceinline__ float reduce_rows(float (&v)[R], int lr, int& row) {
+    static_assert(R <= TPR, "each row needs its own lane after the halving steps");
+    if constexpr (TPR == 64 && (R == 1 || R == 2 || R == 4 || R == 8)) return reduce_rows64<R>(v, lr, row);
+    int base = 0;
+#pragma unroll
+    for (int off = TPR / 2, cnt = R; off >= 1; off >>= 1) {
+        if (cnt > 1) {
+            const bool hi = (lr & off) != 0;
+            const int h = cnt / 2;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float send = hi ? v[i] : v[i + h];
+                const float keep = hi ? v[i + h] : v[i];
+                v[i] = keep + __shfl_xor(send, off, 64);
+            }
+            if (hi) base += h;
+            cnt = h;
+        } else {
+            v[0] += __shfl_xor(v[0], off, 64);
+        }
+    }
+    row = base;
+    return v[0];
+}
+
 // Maximum over the 64 lanes of a wave (all lanes active), uniform result:
 // DPP inside each 16-lane row, then the four row maxima through readlane.
 __device__ __forceinline__ float wave_max_f32(float v) {

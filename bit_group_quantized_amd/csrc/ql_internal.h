@@ -29,6 +29,21 @@ int launch_gemv(const GemvArgs& a, hipStream_t st);
 // K with the chunked kernel (powers of two 256 .. 16384): the fused variants.
 bool gemv_fused_supported(int K);
 int launch_gemv_rmsnorm(const GemvArgs& a, hipStream_t st);
+// Second weight codecs, single-row GEMV with fp16 x and y.
+struct CodecArgs {
+    const uint8_t* codes8 = nullptr;        // FP8: E4M3 codes [N][K]
+    const uint16_t* scales = nullptr;       // FP8: fp16 scale [N][K/64]
+    const uint32_t* codes4 = nullptr;       // NVFP4: E2M1 codes [N][K/8] (w4 packing)
+    const uint8_t* block_scales = nullptr;  // NVFP4: E4M3 scale [N][K/16]
+    float global_scale = 1.f;               // NVFP4
+    const uint16_t* x = nullptr;
+    uint16_t* y = nullptr;
+    int K = 0, N = 0;
+};
+bool gemv_fp8_supported(int K);    // 256 .. 8192, powers of two
+bool gemv_nvfp4_supported(int K);  // 256 .. 16384, powers of two
+int launch_gemv_fp8(const CodecArgs& a, hipStream_t st);
+int launch_gemv_nvfp4(const CodecArgs& a, hipStream_t st);
 // bf16 activations, scales, biases and outputs; the chunked K set.
 int launch_gemv_bf16(const GemvArgs& a, hipStream_t st);
 // Writes a.y if non-null, the block keys to a.partials (at most

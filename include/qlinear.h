@@ -12,6 +12,8 @@
  *     "优化单行权重路径"              the row-parallel single-row GEMV
  *     "减少中间状态和流量"            the fused decode expert chains
  *     "将 token 交接保留在 GPU 上"    the token hand-off kept on the GPU
+ *   [LITHOS] "待验证｜lithos-metal补Apple推理内核", "一分钟内合并了什么":
+ *     FP8 E4M3 decode and the NVFP4 checkpoint (second codecs)
  *   [LAYA] laya-mlx, "工程调查：这个 MLX 端口还能再快 10× 吗？",
  *     "选择性量化": affine quantization with group size 64.
  *
@@ -182,6 +184,47 @@ int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t
  */
 int qlinear_gemv_bf16(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream);
 int qlinear_gemm_bf16(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
+ * Second weight codecs ("待验证｜lithos-metal补Apple推理内核", section
+ * "一分钟内合并了什么": FP8 E4M3 decode, two codes per half2, and an NVFP4
+ * checkpoint).  The formats are this library's reading of that page:
+ *
+ *   ql_fp8:   codes  uint8 [N][K], E4M3FN (bias 7, S.1111.111 = NaN, max 448)
+ *             scales fp16 [N][K/64];  W[k][n] = e4m3(code[n][k]) * scale[n][k/64]
+ *   ql_nvfp4: qweight uint32 [N][K/8], E2M1 codes packed as the w4 codes
+ *             (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, sign in bit 3)
+ *             block_scales uint8 [N][K/16], E4M3;  global_scale fp32
+ *             W[k][n] = e2m1(code) * e4m3(block_scale[n][k/16]) * global_scale
+ */
+typedef struct ql_fp8 {
+    const uint8_t* codes;    /* [N][K], 16-byte aligned */
+    const uint16_t* scales;  /* [N][K/64] fp16 */
+    int32_t K;
+    int32_t N;
+} ql_fp8;
+
+typedef struct ql_nvfp4 {
+    const uint32_t* qweight;      /* [N][K/8], 16-byte aligned */
+    const uint8_t* block_scales;  /* [N][K/16] E4M3, 2-byte aligned */
+    float global_scale;
+    int32_t K;
+    int32_t N;
+} ql_nvfp4;
+
+/*
+ * qlinear_gemv_fp8, qlinear_gemv_nvfp4 - y fp16 [N] = x fp16 [K] . W for
+ * one activation row.  Codes are decoded by exact bit moves into fp16 (the
+ * FP8 pairs two codes per half2), multiplied in fp32 with v_dot2, scaled
+ * per group / block and rounded once to fp16.  NaN E4M3 codes are not
+ * supported (weights are finite).
+ * Limits: K a power of two, 256 .. 8192 (FP8) or 256 .. 16384 (NVFP4).
+ * Errors: INVALID_ARG (null W/x/y with N > 0, N < 0), UNSUPPORTED_SHAPE,
+ * MISALIGNED (codes/qweight and x 16-byte, scales, block_scales and y
+ * 2-byte aligned), HIP.
+ */
+int qlinear_gemv_fp8(const ql_fp8* W, const uint16_t* x, uint16_t* y, void* stream);
+int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* stream);
 
 /*
  * qlinear_gemv_rmsnorm - y = fp16(rmsnorm(x)) . dequant(W): a decode

@@ -230,3 +230,25 @@ def test_bf16_validation(L):
     assert g(ctypes.byref(_w(K=96)), A16, 4, A16, None) == SHAPE
     assert g(ctypes.byref(_w()), A16 + 2, 4, A16, None) == MISALIGNED
     assert g(ctypes.byref(_w()), None, 4, A16, None) == INVALID
+
+
+def test_codec_validation(L):
+    f8 = L.qlinear_gemv_fp8
+    W8 = lambda K=2048, N=64, c=A16, s=A16: ql.ql_fp8(c, s, K, N)
+    assert f8(None, A16, A16, None) == INVALID
+    assert f8(ctypes.byref(W8(K=16384)), A16, A16, None) == SHAPE     # FP8 stops at 8192
+    assert f8(ctypes.byref(W8(K=192)), A16, A16, None) == SHAPE
+    assert f8(ctypes.byref(W8(N=-1)), A16, A16, None) == INVALID
+    assert f8(ctypes.byref(W8(c=A16 + 8)), A16, A16, None) == MISALIGNED
+    assert f8(ctypes.byref(W8(s=A16 + 1)), A16, A16, None) == MISALIGNED
+    assert f8(ctypes.byref(W8()), A16 + 2, A16, None) == MISALIGNED
+    assert f8(ctypes.byref(W8(c=0)), A16, A16, None) == INVALID
+    assert f8(ctypes.byref(W8(N=0, c=0, s=0)), None, None, None) == OK
+    f4 = L.qlinear_gemv_nvfp4
+    W4 = lambda K=2048, N=64, q=A16, b=A16: ql.ql_nvfp4(q, b, 0.01, K, N)
+    assert f4(None, A16, A16, None) == INVALID
+    assert f4(ctypes.byref(W4(K=128)), A16, A16, None) == SHAPE
+    assert f4(ctypes.byref(W4(q=A16 + 4)), A16, A16, None) == MISALIGNED
+    assert f4(ctypes.byref(W4(b=A16 + 1)), A16, A16, None) == MISALIGNED
+    assert f4(ctypes.byref(W4()), None, A16, None) == INVALID
+    assert f4(ctypes.byref(W4(N=0, q=0, b=0)), None, None, None) == OK

@@ -47,11 +47,13 @@ def w4_bytes(K, N):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch graph-timed sections eagerly (for counter collection)")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
-    ap.add_argument("--workload", choices=["all", "gemm", "decode", "bf16", "codecs", "moe_decode",
-                                           "moe_prefill"],
+    ap.add_argument("--workload", choices=["all", "gemm", "gemm_prefill", "decode", "bf16", "codecs",
+                                           "moe_decode", "moe_prefill"],
                     default="all",
                     help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -104,10 +106,17 @@ def stage_times(stage_fns, steps, warmup, settle_s=0.0):
     return out
 
 
+USE_GRAPHS = True
+
+
 def graph_time(step_fn, ng, replays):
     """Capture `ng` calls of step_fn(i) in one HIP graph, replay it `replays`
-    times between two events; returns ms per call."""
+    times between two events; returns ms per call.  With --eager the same
+    calls are launched directly instead (for profilers that do not follow
+    graph launches)."""
     import torch
+    if not USE_GRAPHS:
+        return timed_steps(lambda i: step_fn(i % ng), ng * replays, ng)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(ng):
@@ -501,7 +510,7 @@ def bench_moe_decode(args, dev, w):
     return {"tokens/s": 1e3 / ms, "us_per_token": ms * 1e3, "algorithmic_bytes": algo,
             "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "stage_us": {"route": k[0] * 1e3, "gate_up_silu": k[1] * 1e3, "down_combine": k[2] * 1e3},
-            "timing": "HIP graph of 16 decode steps, replayed"}
+            "timing": "HIP graph of 16 decode steps, replayed" if USE_GRAPHS else "eager launches"}
 
 
 def bench_moe_prefill(args, dev, w):
@@ -645,6 +654,8 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    global USE_GRAPHS
+    USE_GRAPHS = not args.eager
     if args.ingest_pmc:
         ingest_pmc(*args.ingest_pmc)
         return
@@ -676,9 +687,10 @@ def main():
     if not args.only_primary:
         import synth
         wl = res.setdefault("workloads", {})
-        if args.workload in ("all", "gemm"):
+        if args.workload in ("all", "gemm", "gemm_prefill"):
             log("bench: GEMM")
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)
+        if args.workload in ("all", "gemm"):
             log("bench: few-row GEMM")
             wl["few_rows_gemm"] = bench_few_rows(args, dev)
         if args.workload in ("all", "bf16"):

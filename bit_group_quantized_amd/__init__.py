@@ -83,6 +83,12 @@ _SIGS = {
                                         _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                         _P, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "moe_decode_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "moe_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
+                                  ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
+                                  ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P,
+                                  ctypes.c_size_t, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -339,6 +345,47 @@ def moe_grouped_gemm(W: dict, shared: dict | None, X, T: int, topk: int, op: int
         _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(route.get("gates")),
         _ptr(route.get("pos")), _ptr(ws), ws.numel(), _ptr(Y), _stream(stream)))
     return Y
+
+
+def moe_decode_workspace_bytes(T: int, E: int, topk: int, I: int) -> int:
+    return int(lib().moe_decode_workspace_bytes(T, E, topk, I))
+
+
+def moe_decode_logits_offset(T: int, E: int, topk: int) -> int:
+    return int(lib().moe_decode_logits_offset(T, E, topk))
+
+
+def alloc_decode_outputs(T: int, E: int, topk: int, D: int, I: int, device) -> dict:
+    """Device buffers for moe_decode."""
+    import torch
+    ws_bytes = moe_decode_workspace_bytes(T, E, topk, I)
+    return {
+        "ids": torch.empty((T, topk), dtype=torch.int32, device=device),
+        "gates": torch.empty((T, topk), dtype=torch.float32, device=device),
+        "out": torch.empty((T, D), dtype=torch.float16, device=device),
+        "workspace": torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
+    }
+
+
+def moe_decode(H, Wr, logit_bias, topk: int, gate_up: dict, down: dict, shared_gate_up=None,
+               shared_down=None, out: dict | None = None, stream=None) -> dict:
+    """The routed-expert layer of T <= QL_DECODE_MAX_T tokens in three
+    launches; returns the dict of ids, gates, out and workspace."""
+    T, D = H.shape
+    E = Wr.shape[1]
+    I = int(down["K"])
+    if out is None:
+        out = alloc_decode_outputs(T, E, topk, D, I, H.device)
+    gu, dn = make_w4_experts(gate_up), make_w4_experts(down)
+    sg = make_w4(shared_gate_up) if shared_gate_up is not None else None
+    sd = make_w4(shared_down) if shared_down is not None else None
+    ws = out["workspace"]
+    _check("moe_decode", lib().moe_decode(
+        _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, ctypes.byref(gu), ctypes.byref(dn),
+        ctypes.byref(sg) if sg is not None else None, ctypes.byref(sd) if sd is not None else None,
+        _ptr(out["ids"]), _ptr(out["gates"]), _ptr(ws), ws.numel(), _ptr(out["out"]),
+        _stream(stream)))
+    return out
 
 
 def moe_combine(Ydown, gates, pos, T: int, topk: int, has_shared: bool, out=None, stream=None):

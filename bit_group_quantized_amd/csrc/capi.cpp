@@ -307,6 +307,66 @@ int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t
     return ql::launch_moe_grouped(a, as_stream(stream));
 }
 
+size_t moe_decode_workspace_bytes(int32_t T, int32_t E, int32_t topk, int32_t I) {
+    if (T < 0 || T > QL_DECODE_MAX_T || E <= 0 || E > QL_MAX_EXPERTS || topk <= 0 || topk > E ||
+        topk > QL_MAX_TOPK || I <= 0 || I > QL_MAX_K)
+        return 0;
+    return ql::moe_decode_layout(T, E, topk, I).total;
+}
+
+size_t moe_decode_logits_offset(int32_t T, int32_t E, int32_t topk) {
+    if (moe_decode_workspace_bytes(T, E, topk, 64) == 0) return 0;
+    return ql::moe_decode_layout(T, E, topk, 64).logits;
+}
+
+int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
+               int32_t E, int32_t topk, const ql_w4_experts* gate_up, const ql_w4_experts* down,
+               const ql_w4* shared_gate_up, const ql_w4* shared_down, int32_t* topk_ids,
+               float* topk_gates, void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+    if (!gate_up || !down) return QL_ERR_INVALID_ARG;
+    if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
+    if (T < 0 || E <= 0 || topk <= 0 || topk > E || D <= 0) return QL_ERR_INVALID_ARG;
+    if (T > QL_DECODE_MAX_T || E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (gate_up->num_experts != E || down->num_experts != E) return QL_ERR_INVALID_ARG;
+    const ql_w4_experts& gu = *gate_up;
+    const ql_w4_experts& dn = *down;
+    int rc = check_w4(gu.qweight, gu.scales, gu.biases, gu.K, gu.N, gu.group_size);
+    if (rc != QL_OK) return rc;
+    rc = check_w4(dn.qweight, dn.scales, dn.biases, dn.K, dn.N, dn.group_size);
+    if (rc != QL_OK) return rc;
+    const int32_t I = dn.K;
+    if (gu.K != D || dn.N != D || gu.N != 2 * I) return QL_ERR_INVALID_ARG;
+    if (shared_gate_up) {
+        const ql_w4& sg = *shared_gate_up;
+        const ql_w4& sd = *shared_down;
+        rc = check_w4(sg.qweight, sg.scales, sg.biases, sg.K, sg.N, sg.group_size);
+        if (rc != QL_OK) return rc;
+        rc = check_w4(sd.qweight, sd.scales, sd.biases, sd.K, sd.N, sd.group_size);
+        if (rc != QL_OK) return rc;
+        if (sg.K != D || sg.N != 2 * I || sd.K != I || sd.N != D) return QL_ERR_INVALID_ARG;
+    }
+    if (!ql::moe_rows_supported(D) || !ql::moe_rows_supported(I)) return QL_ERR_UNSUPPORTED_SHAPE;
+    const int J = topk + (shared_gate_up ? 1 : 0);
+    if ((int64_t)J * I * 2 > 49152) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0) return QL_OK;
+    if (!H || !Wr || !topk_ids || !topk_gates || !out) return QL_ERR_INVALID_ARG;
+    if (!aligned(H, 16) || !aligned(Wr, 16) || !aligned(logit_bias, 4) || !aligned(topk_ids, 4) ||
+        !aligned(topk_gates, 4) || !aligned(out, 2))
+        return QL_ERR_MISALIGNED;
+    if (!workspace || ws_bytes < moe_decode_workspace_bytes(T, E, topk, I)) return QL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
+    ql::DecodeArgs a{H, Wr, logit_bias, T, D, E, topk, I,
+                     gu.qweight, gu.scales, gu.biases, dn.qweight, dn.scales, dn.biases,
+                     shared_gate_up ? shared_gate_up->qweight : nullptr,
+                     shared_gate_up ? shared_gate_up->scales : nullptr,
+                     shared_gate_up ? shared_gate_up->biases : nullptr,
+                     shared_down ? shared_down->qweight : nullptr,
+                     shared_down ? shared_down->scales : nullptr,
+                     shared_down ? shared_down->biases : nullptr,
+                     topk_ids, topk_gates, static_cast<unsigned char*>(workspace), out};
+    return ql::launch_moe_decode(a, as_stream(stream));
+}
+
 int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
                 int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
                 void* stream) {

@@ -23,6 +23,7 @@
 
 #include "ql_device.h"
 #include "ql_internal.h"
+#include "ql_topk.h"
 
 namespace ql {
 
@@ -412,45 +413,32 @@ embed_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
 //   first halving bit, so one more exchange brings them together.
 // MODE 1 (down): R output rows.
 // ---------------------------------------------------------------------------
-template <int TPR, int V, int R, int MODE>
-__global__ void __launch_bounds__(64)
-moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
-                const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
-                const uint16_t* __restrict__ X, const int2* __restrict__ row_info,
-                uint16_t* __restrict__ Y, int K, int N, int E, int T, int topk) {
-    constexpr int TEAMS = 64 / TPR;
-    constexpr int OUT = (MODE == 0) ? R / 2 : R;  // outputs per team
-    const int lane = threadIdx.x;
-    const int lr = lane % TPR;
-    const int team = lane / TPR;
-    const int G = K / kGroup;
-    const int wpr = K / 8;
-    const int r = blockIdx.y;
-    const int routed = T * topk;
-    const uint32_t* wq = sqw;
-    const uint16_t* ws = ssc;
-    const uint16_t* wb = sbi;
-    int xrow;
-    if (r < routed) {
-        const int2 info = row_info[r];
-        // Clamped so that a corrupted dispatch can never index out of bounds.
-        const int e = min(max(info.x, 0), E - 1);
-        wq = qw + (size_t)e * N * wpr;
-        ws = sc + (size_t)e * N * G;
-        wb = bi + (size_t)e * N * G;
-        xrow = (MODE == 0) ? min(max(info.y, 0), T - 1) : r;
-    } else {
-        xrow = (MODE == 0) ? r - routed : r;
-    }
-    const int Nout = (MODE == 0) ? N / 2 : N;
-    const int n0 = (blockIdx.x * TEAMS + team) * OUT;
-
-    u32x4 xr[V][4];
+// The lane's 16-byte chunks of activation row `xrow`.
+template <int TPR, int V>
+__device__ __forceinline__ void rows_load_x(const uint16_t* __restrict__ X, int xrow, int K, int lr,
+                                            u32x4 (&xr)[V][4]) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
 #pragma unroll
         for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(X + (size_t)xrow * K + (lr + v * TPR) * 32 + w * 8);
+}
+
+// One wave's outputs of row r: column block `xblock` of the expert matrix
+// (wq, ws, wb) applied to the activations xr.
+template <int TPR, int V, int R, int MODE>
+__device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_t* __restrict__ wq,
+                                          const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wb,
+                                          uint16_t* __restrict__ Y, int r, int xblock, int K, int N,
+                                          int lane) {
+    constexpr int TEAMS = 64 / TPR;
+    constexpr int OUT = (MODE == 0) ? R / 2 : R;  // outputs per team
+    const int lr = lane % TPR;
+    const int team = lane / TPR;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int Nout = (MODE == 0) ? N / 2 : N;
+    const int n0 = (xblock * TEAMS + team) * OUT;
+
     u32x4 cw[R][V];
     uint16_t s[R][V], b[R][V];
 #pragma unroll
@@ -505,6 +493,105 @@ moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
     } else {
         if (writer && n0 + sel < Nout) Y[(size_t)r * Nout + n0 + sel] = f2h(tot);
     }
+}
+
+template <int TPR, int V, int R, int MODE>
+__global__ void __launch_bounds__(64)
+moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
+                const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                const uint16_t* __restrict__ X, const int2* __restrict__ row_info,
+                uint16_t* __restrict__ Y, int K, int N, int E, int T, int topk) {
+    const int lane = threadIdx.x;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int r = blockIdx.y;
+    const int routed = T * topk;
+    const uint32_t* wq = sqw;
+    const uint16_t* ws = ssc;
+    const uint16_t* wb = sbi;
+    int xrow;
+    if (r < routed) {
+        const int2 info = row_info[r];
+        // Clamped so that a corrupted dispatch can never index out of bounds.
+        const int e = min(max(info.x, 0), E - 1);
+        wq = qw + (size_t)e * N * wpr;
+        ws = sc + (size_t)e * N * G;
+        wb = bi + (size_t)e * N * G;
+        xrow = (MODE == 0) ? min(max(info.y, 0), T - 1) : r;
+    } else {
+        xrow = (MODE == 0) ? r - routed : r;
+    }
+    u32x4 xr[V][4];
+    rows_load_x<TPR, V>(X, xrow, K, lane % TPR, xr);
+    rows_body<TPR, V, R, MODE>(xr, wq, ws, wb, Y, r, blockIdx.x, K, N, lane);
+}
+
+// Decode gate/up projection fused with the token's routing: block (x, r)
+// holds four waves, wave w computing column block 4x + w of row r (the
+// rows of moe_rows_kernel's MODE 0, in assignment order: r = t*topk + j is
+// the j-th expert chosen by token t, rows T*topk + t the shared expert).
+// A routed block first sums the router partials of its token (the same
+// fixed order as the dispatch-side router, so the choice is identical),
+// takes the top-k in wave 0 and then reads only the j-th chosen expert's
+// weights; its activation loads are issued before the routing.  Blocks with
+// x = 0 also write the token's ids, gates, logits and the (expert, row) of
+// their assignment for the down projection.
+template <int TPR, int V, int R, int EPL>
+__global__ void __launch_bounds__(256)
+moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __restrict__ bias,
+                          const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                          const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
+                          const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                          const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int K, int N,
+                          int E, int T, int topk, int* __restrict__ ids, float* __restrict__ gates,
+                          float* __restrict__ logits_out, int2* __restrict__ assign_info) {
+    __shared__ float s_lg[64 * EPL];
+    __shared__ int s_sel[QL_MAX_TOPK_DEV];
+    __shared__ float s_gate[QL_MAX_TOPK_DEV];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int G = K / kGroup;
+    const int wpr = K / 8;
+    const int r = blockIdx.y;
+    const int routed = T * topk;
+    const int t = (r < routed) ? r / topk : r - routed;
+    u32x4 xr[V][4];
+    rows_load_x<TPR, V>(X, t, K, lane % TPR, xr);
+    const uint32_t* wq = sqw;
+    const uint16_t* ws = ssc;
+    const uint16_t* wb = sbi;
+    if (r < routed) {  // uniform over the block
+        const int j = r - t * topk;
+        for (int e = threadIdx.x; e < E; e += blockDim.x) {
+            float part[kRouterSmallParts];
+#pragma unroll
+            for (int p = 0; p < kRouterSmallParts; ++p)
+                part[p] = partials[((size_t)t * kRouterSmallParts + p) * E + e];
+            float sum = 0.f;
+#pragma unroll
+            for (int p = 0; p < kRouterSmallParts; ++p) sum += part[p];
+            if (bias) sum += bias[e];
+            s_lg[e] = sum;
+        }
+        __syncthreads();
+        if (wave == 0) topk_one_token<EPL, 1>(s_lg, nullptr, s_lg, 0, E, topk, s_sel, s_gate);
+        __syncthreads();
+        const int e = min(max(s_sel[j], 0), E - 1);
+        wq = qw + (size_t)e * N * wpr;
+        ws = sc + (size_t)e * N * G;
+        wb = bi + (size_t)e * N * G;
+        if (blockIdx.x == 0) {
+            if (threadIdx.x == 0) {
+                ids[r] = e;
+                gates[r] = s_gate[j];
+                assign_info[r] = make_int2(e, r);
+            }
+            if (j == 0)
+                for (int i = threadIdx.x; i < E; i += blockDim.x) logits_out[(size_t)t * E + i] = s_lg[i];
+        }
+    }
+    rows_body<TPR, V, R, 0>(xr, wq, ws, wb, Y, r, blockIdx.x * 4 + wave, K, N, lane);
 }
 
 // Decode down projection fused with the gate-weighted sum over the token's
@@ -692,20 +779,26 @@ inline int pow2_divisor(int G) {
 }
 
 template <int TPR, int V>
+void launch_down_combine_t(const GroupedArgs& a, const int2* assign_info, hipStream_t st) {
+    constexpr int TEAMS = 64 / TPR;
+    constexpr int R = (TPR < 2) ? TPR : 2;
+    const int has_shared = a.sqw != nullptr;
+    const int J = a.topk + has_shared;
+    const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
+    dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
+    // four waves; each takes the rows j = wave, wave + 4, ... (3 per round)
+    hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3>), grid, dim3(256), smem, st, a.qw, a.sc,
+                       a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates, assign_info, a.Y, a.K, a.N, a.E, a.T,
+                       a.topk, has_shared);
+}
+
+template <int TPR, int V>
 int launch_rows_t(const GroupedArgs& a, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
     const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     const int has_shared = a.sqw != nullptr;
     if (a.op == QL_OP_DOWN_COMBINE) {
-        constexpr int R = (TPR < 2) ? TPR : 2;
-        const int J = a.topk + has_shared;
-        const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
-        dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
-        // four waves; each takes the rows j = wave, wave + 4, ... (3 per round)
-        hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3>), grid, dim3(256), smem, st, a.qw,
-                           a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates,
-                           reinterpret_cast<const int2*>(a.ws + L.assign_info), a.Y, a.K, a.N, a.E,
-                           a.T, a.topk, has_shared);
+        launch_down_combine_t<TPR, V>(a, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
     } else {
         constexpr int R = (TPR < 8) ? TPR : 8;
         const int rows = a.T * a.topk + (has_shared ? a.T : 0);
@@ -862,6 +955,91 @@ bool moe_rows_supported(int K) {
         case 16384: return true;
         default: return false;
     }
+}
+
+namespace {
+
+template <int TPR, int V, int EPL>
+void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
+    constexpr int TEAMS = 64 / TPR;
+    constexpr int R = (TPR < 8) ? TPR : 8;
+    static_assert(R % 2 == 0, "gate/up pairing needs an even row count");
+    constexpr int COLS = 4 * TEAMS * (R / 2);  // act columns per block
+    const int has_shared = a.sgu_qw != nullptr;
+    const int rows = a.T * a.topk + (has_shared ? a.T : 0);
+    dim3 grid((a.I + COLS - 1) / COLS, rows);
+    hipLaunchKernelGGL((moe_decode_gate_up_kernel<TPR, V, R, EPL>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const float*>(a.ws + L.partials), a.bias, a.gu_qw, a.gu_sc,
+                       a.gu_bi, a.sgu_qw, a.sgu_sc, a.sgu_bi, a.H,
+                       reinterpret_cast<uint16_t*>(a.ws + L.act), a.D, 2 * a.I, a.E, a.T, a.topk, a.ids,
+                       a.gates, reinterpret_cast<float*>(a.ws + L.logits),
+                       reinterpret_cast<int2*>(a.ws + L.assign_info));
+}
+
+template <int TPR, int V>
+void launch_decode_gate_up_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
+    if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4>(a, L, st);
+    else launch_decode_gate_up_t<TPR, V, 16>(a, L, st);
+}
+
+template <int TPR, int V>
+void launch_decode_down_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
+    GroupedArgs g{a.dn_qw, a.dn_sc, a.dn_bi, a.sdn_qw, a.sdn_sc, a.sdn_bi,
+                  reinterpret_cast<const uint16_t*>(a.ws + L.act), nullptr, nullptr, a.gates,
+                  nullptr, a.ws, a.out, a.I, a.D, a.E, a.T, a.topk, QL_OP_DOWN_COMBINE};
+    launch_down_combine_t<TPR, V>(g, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
+}
+
+}  // namespace
+
+size_t align_up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+DecodeLayout moe_decode_layout(int T, int E, int topk, int I) {
+    DecodeLayout L;
+    size_t off = 0;
+    L.partials = off;
+    off = align_up256(off + (size_t)T * kRouterSmallParts * E * sizeof(float));
+    L.logits = off;
+    off = align_up256(off + (size_t)T * E * sizeof(float));
+    L.assign_info = off;
+    off = align_up256(off + (size_t)T * topk * 2 * sizeof(int));
+    L.act = off;
+    off = align_up256(off + (size_t)T * (topk + 1) * I * sizeof(uint16_t));
+    L.total = off;
+    return L;
+}
+
+int launch_moe_decode(const DecodeArgs& a, hipStream_t st) {
+    const DecodeLayout L = moe_decode_layout(a.T, a.E, a.topk, a.I);
+    int rc = launch_router_partials_small(a.H, a.Wr, reinterpret_cast<float*>(a.ws + L.partials), a.T,
+                                          a.D, a.E, st);
+    if (rc != QL_OK) return rc;
+    switch (a.D) {
+        case 64: launch_decode_gate_up_v<2, 1>(a, L, st); break;
+        case 128: launch_decode_gate_up_v<4, 1>(a, L, st); break;
+        case 256: launch_decode_gate_up_v<8, 1>(a, L, st); break;
+        case 512: launch_decode_gate_up_v<16, 1>(a, L, st); break;
+        case 1024: launch_decode_gate_up_v<32, 1>(a, L, st); break;
+        case 2048: launch_decode_gate_up_v<64, 1>(a, L, st); break;
+        case 4096: launch_decode_gate_up_v<64, 2>(a, L, st); break;
+        case 8192: launch_decode_gate_up_v<64, 4>(a, L, st); break;
+        case 16384: launch_decode_gate_up_v<64, 8>(a, L, st); break;
+        default: return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+    if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
+    switch (a.I) {
+        case 64: launch_decode_down_v<2, 1>(a, L, st); break;
+        case 128: launch_decode_down_v<4, 1>(a, L, st); break;
+        case 256: launch_decode_down_v<8, 1>(a, L, st); break;
+        case 512: launch_decode_down_v<16, 1>(a, L, st); break;
+        case 1024: launch_decode_down_v<32, 1>(a, L, st); break;
+        case 2048: launch_decode_down_v<64, 1>(a, L, st); break;
+        case 4096: launch_decode_down_v<64, 2>(a, L, st); break;
+        case 8192: launch_decode_down_v<64, 4>(a, L, st); break;
+        case 16384: launch_decode_down_v<64, 8>(a, L, st); break;
+        default: return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st) {

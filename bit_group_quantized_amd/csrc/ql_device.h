@@ -337,6 +337,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(a, b), max(c, e));
 }
 
+// Minimum of a 32-bit unsigned value over the 64 lanes of a wave, uniform.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    auto dpp = [](uint32_t x, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, true);
+    };
+    v = min(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+    v = min(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+    v = min(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    v = min(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+    const uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane((int)v, 32), e = __builtin_amdgcn_readlane((int)v, 48);
+    return min(min(a, b), min(c, e));
+}
+
 // Monotone 32-bit key of a float: unsigned order = numeric order (the sign
 // bit flipped for positive values, all bits for negative ones); the key of
 // -inf is 0x007FFFFF, so no float maps to 0.

@@ -87,6 +87,7 @@ constexpr int kRouteChunkTokens = 256;  // tokens per dispatch chunk
 constexpr int kRouterPartRows = 64;     // D rows per small-T router partial
 constexpr int kRouterSmallT = 16;       // T at or below: row-parallel router
 constexpr int kRouterMfmaSplit = 4;     // K splits of the MFMA router (partials per logit)
+constexpr int kRouterSmallParts = 32;   // small-T router: D split in 32 slices, one partial each
 
 struct RouteArgs {
     const uint16_t* H;
@@ -104,6 +105,10 @@ struct RouteArgs {
 int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
                               int E, hipStream_t st);
 bool router_uses_mfma(int T, int E);
+// Small-T router partials: [T][kRouterSmallParts][E] fp32; their sum over the
+// slices in ascending order (plus the bias) is the logit.
+int launch_router_partials_small(const uint16_t* H, const uint16_t* Wr, float* partials, int T,
+                                 int D, int E, hipStream_t st);
 int launch_route(const RouteArgs& a, hipStream_t st);
 MoeWorkspace moe_workspace_layout(int T, int E, int topk);     // logits + top-k + dispatch
 int launch_dispatch(const RouteArgs& a, hipStream_t st);  // dispatch only (ids given)
@@ -127,6 +132,41 @@ struct GroupedArgs {
 bool moe_rows_supported(int K);
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel
 int launch_moe_grouped(const GroupedArgs& a, hipStream_t st); // any T, MFMA tiles
+
+// Whole decode layer (T <= QL_DECODE_MAX_T) in three launches: router
+// partials; routing fused into the gate/up rows; down rows fused with the
+// gate-weighted sum.
+struct DecodeLayout {
+    size_t partials;     // fp32 [T][kRouterSmallParts][E]
+    size_t logits;       // fp32 [T][E]
+    size_t assign_info;  // int32 [T*topk][2]: (expert, row) of each assignment
+    size_t act;          // fp16 [T*topk + T][I], assignment order, then shared rows
+    size_t total;
+};
+DecodeLayout moe_decode_layout(int T, int E, int topk, int I);
+struct DecodeArgs {
+    const uint16_t* H;
+    const uint16_t* Wr;
+    const float* bias;
+    int T, D, E, topk, I;
+    const uint32_t* gu_qw;  // routed experts, gate/up [E][2I][D/8]
+    const uint16_t* gu_sc;
+    const uint16_t* gu_bi;
+    const uint32_t* dn_qw;  // routed experts, down [E][D][I/8]
+    const uint16_t* dn_sc;
+    const uint16_t* dn_bi;
+    const uint32_t* sgu_qw;  // shared expert (all null or all set)
+    const uint16_t* sgu_sc;
+    const uint16_t* sgu_bi;
+    const uint32_t* sdn_qw;
+    const uint16_t* sdn_sc;
+    const uint16_t* sdn_bi;
+    int32_t* ids;
+    float* gates;
+    unsigned char* ws;
+    uint16_t* out;
+};
+int launch_moe_decode(const DecodeArgs& a, hipStream_t st);
 
 int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
                    int N, int has_shared, uint16_t* out, hipStream_t st);

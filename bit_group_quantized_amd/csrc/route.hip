@@ -18,6 +18,7 @@
 // its expert is a population count of the mask below it.
 #include "ql_device.h"
 #include "ql_internal.h"
+#include "ql_topk.h"
 
 #include <float.h>
 
@@ -27,7 +28,7 @@ namespace {
 
 constexpr int kChunk = kRouteChunkTokens;
 constexpr int kMaskWords = kChunk / 32;
-constexpr int kRouterParts = 32;     // row-parallel router: D split in 32 slices
+constexpr int kRouterParts = kRouterSmallParts;  // row-parallel router: D split in 32 slices
 constexpr int kRouterMfmaParts = kRouterMfmaSplit;  // MFMA router: K split
 
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
@@ -125,84 +126,6 @@ __global__ void __launch_bounds__(256)
 router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
                           float* __restrict__ partials, int D, int E) {
     router_partial_vec_body(H, Wr, partials, D, E);
-}
-
-// ---------------------------------------------------------------------------
-// Top-k of one token by one wave, with the 64-bit selection keys of
-// ql_device.h (logit_key): key 0 marks an expert already taken (no finite
-// logit maps to it), and each round takes the wave maximum (wave_max_u64),
-// so the winner is uniform.
-// ---------------------------------------------------------------------------
-// Logits of token t are the sum of `nparts` partial rows (fixed order) plus
-// the optional bias; they are written to logits_out.  Writes the topk
-// chosen experts (descending) and their renormalized gates to sel_e/sel_g.
-template <int EPL, int NP>
-__device__ void topk_one_token(const float* __restrict__ src, const float* __restrict__ bias,
-                               float* __restrict__ logits_out, int t, int E, int topk, int* sel_e,
-                               float* sel_g) {
-    const int lane = threadIdx.x & 63;
-    // Every partial of every logit this lane owns is loaded before the first
-    // sum (NP and EPL are compile-time), so the whole token costs one round
-    // trip to memory.
-    float part[EPL][NP];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = min(lane + 64 * i, E - 1);
-#pragma unroll
-        for (int p = 0; p < NP; ++p) part[i][p] = src[((size_t)t * NP + p) * E + e];
-    }
-    // Lane l holds the keys of experts l, l + 64, ...: the monotone 32-bit
-    // pattern of the logit, with -0 folded into +0 so that equal logits have
-    // equal keys; 0 marks an entry already taken (or past E).
-    uint32_t key[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = 0u;
-        if (e < E) {
-            float s = 0.f;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) s += part[i][p];
-            if (bias) s += bias[e];
-            logits_out[(size_t)t * E + e] = s;
-            key[i] = mono32((s != s) ? -INFINITY : s + 0.0f);  // NaN never wins
-        }
-    }
-    // Each round: the largest remaining key over the wave, then the smallest
-    // expert index holding it (ballots in index order, first set bit); that
-    // entry is taken.  topk <= the number of valid entries, so m > 0.
-    float vmax = 0.f, my_v = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < topk; ++j) {
-        uint32_t m = key[0];
-#pragma unroll
-        for (int i = 1; i < EPL; ++i) m = max(m, key[i]);
-        m = wave_max_u32(m);  // uniform
-        int be = -1;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const uint64_t b = __ballot(key[i] == m);
-            if (be < 0 && b != 0) be = 64 * i + __ffsll((unsigned long long)b) - 1;
-        }
-        be = max(be, 0);
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if ((be & 63) == lane && i == (be >> 6)) key[i] = 0u;
-        const float bv = unmono32(m);
-        if (j == 0) vmax = bv;
-        if (lane == j) {
-            my_v = bv;
-            my_e = be;
-        }
-    }
-    float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
-    const float exs[1] = {ex};
-    int unused;
-    const float sum = reduce_rows64<1>(exs, lane, unused);  // every lane: the total
-    if (lane < topk) {
-        sel_e[lane] = my_e;
-        sel_g[lane] = ex / sum;
-    }
 }
 
 template <int EPL, int NP>
@@ -642,6 +565,17 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
 }
 
 
+int launch_router_partials_small(const uint16_t* H, const uint16_t* Wr, float* partials, int T,
+                                 int D, int E, hipStream_t st) {
+    if (E % 8 == 0)
+        hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, T), dim3(256), 0, st, H, Wr,
+                           partials, D, E);
+    else
+        hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, T), dim3(256), 0, st, H, Wr,
+                           partials, D, E);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
 int launch_route(const RouteArgs& a, hipStream_t st) {
     const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     float* logits = reinterpret_cast<float*>(a.ws + L.logits);
@@ -650,13 +584,8 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
         const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st);
         if (rc != QL_OK) return rc;
     } else {
-        if (a.E % 8 == 0)
-            hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st,
-                               a.H, a.Wr, partials, a.D, a.E);
-        else
-            hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, a.T), dim3(256), 0, st, a.H,
-                               a.Wr, partials, a.D, a.E);
-        if (hipGetLastError() != hipSuccess) return QL_ERR_HIP;
+        const int rc = launch_router_partials_small(a.H, a.Wr, partials, a.T, a.D, a.E, st);
+        if (rc != QL_OK) return rc;
         if (a.T <= kRouterSmallT) return launch_small_any(a, L, true, st);
     }
     launch_topk(partials, L.nparts, a, logits, st);

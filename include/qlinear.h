@@ -406,6 +406,42 @@ int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* a
                 int32_t T, int32_t topk, int32_t N, int32_t has_shared,
                 uint16_t* out, void* stream);
 
+/*
+ * moe_decode - the whole routed-expert layer for a few decode tokens in
+ * three launches: router partial sums; the token's top-k fused into the
+ * gate/up rows (each routed workgroup finishes its token's logits, takes
+ * the top-k and then reads only its chosen expert's weights); the down rows
+ * fused with the gate-weighted sum and the shared expert.
+ * [PPLX] "减少中间状态和流量" (the decode step fuses routing scores and the
+ * shared expert into the expert projections) and section "解码：最小化每个 token 移动的字节数" (decode
+ * reads only the chosen experts' weights).
+ *   H            fp16 [T][D] tokens, 1 <= T <= QL_DECODE_MAX_T
+ *   Wr           fp16 [D][E] router weight;  logit_bias fp32 [E] or NULL
+ *   gate_up      [E] x (K = D, N = 2I) experts (gate columns [0, I), up [I, 2I))
+ *   down         [E] x (K = I, N = D) experts
+ *   shared_gate_up, shared_down: the shared expert, both or neither (NULL)
+ *   topk_ids     int32 [T][topk] out;  topk_gates fp32 [T][topk] out
+ *   out          fp16 [T][D] out
+ *   workspace    device buffer of ws_bytes >= moe_decode_workspace_bytes(T, E, topk, I)
+ * Routing is bit-identical to moe_route on the same inputs (same partial
+ * sums in the same order, same selection); the layer output is the one of
+ * moe_route + moe_grouped_gemm(QL_OP_GATE_UP_SILU) +
+ * moe_grouped_gemm(QL_OP_DOWN_COMBINE), bit for bit.  The workspace holds,
+ * at moe_decode_logits_offset(T, E, topk), the fp32 logits [T][E].
+ * Limits: D and I powers of two in 64 .. 16384, D a multiple of 64,
+ * (topk + 1) * I * 2 <= 49152, 1 <= topk <= min(E, QL_MAX_TOPK),
+ * E <= QL_MAX_EXPERTS.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED, WORKSPACE, HIP.
+ */
+size_t moe_decode_workspace_bytes(int32_t T, int32_t E, int32_t topk, int32_t I);
+size_t moe_decode_logits_offset(int32_t T, int32_t E, int32_t topk);
+int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+               int32_t T, int32_t D, int32_t E, int32_t topk,
+               const ql_w4_experts* gate_up, const ql_w4_experts* down,
+               const ql_w4* shared_gate_up, const ql_w4* shared_down,
+               int32_t* topk_ids, float* topk_gates,
+               void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

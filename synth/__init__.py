@@ -218,6 +218,36 @@ def moe_tokens(seed: int, T: int, D: int = HIDDEN, E: int = NUM_EXPERTS,
     return {"H": H, "logit_bias": bias}
 
 
+def router_tie_case(seed: int, T: int, topk: int, D: int = HIDDEN, E: int = NUM_EXPERTS) -> dict:
+    """Router inputs whose logits are exact in fp32 under any summation order
+    and hold exact ties at the top and across the top-k boundary.
+
+    H entries are -1, 0 or 1, with the first 512 (or D/4) all 1; router
+    weights are integers in -16..16 times 2**-8 (small integers in the
+    all-ones rows), so every partial sum is a multiple of 2**-8 below 2**7.
+    One column with weight 1/16 on the all-ones rows is copied to
+    ``n_top = max(1, topk // 2)`` positions and one with weight 1/32 to
+    ``n_edge`` further positions (up to two more than the top-k has room
+    for), all at seeded random indices: the copies have identical logits,
+    far above the rest, and the top-k cut falls inside the second group.
+    """
+    rng = rng_for(seed)
+    ones = min(512, D // 4)
+    H = rng.integers(-1, 2, size=(T, D)).astype(np.float64)
+    H[:, :ones] = 1.0
+    W = rng.integers(-16, 17, size=(D, E)).astype(np.float64)
+    W[:ones, :] = rng.integers(-2, 3, size=(ones, E))
+    cols = rng.permutation(E)
+    n_top = max(1, topk // 2)
+    n_edge = min(topk - n_top + 2, E - n_top)
+    top, edge = cols[:n_top], cols[n_top:n_top + n_edge]
+    W[:ones, top[0]] = 16.0
+    W[:ones, edge[0]] = 8.0
+    W[:, top] = W[:, [top[0]]]
+    W[:, edge] = W[:, [edge[0]]]
+    return {"H": f16(H), "Wr": f16(W / 256.0), "top": np.sort(top), "edge": np.sort(edge)}
+
+
 # Default configurations of the benchmarked workload.
 CONFIGS = {
     0: dict(kind="gemv", K=512, N=512),

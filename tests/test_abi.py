@@ -252,3 +252,38 @@ def test_codec_validation(L):
     assert f4(ctypes.byref(W4(b=A16 + 1)), A16, A16, None) == MISALIGNED
     assert f4(ctypes.byref(W4()), None, A16, None) == INVALID
     assert f4(ctypes.byref(W4(N=0, q=0, b=0)), None, None, None) == OK
+
+
+def test_moe_decode_validation(L):
+    GU = ql.ql_w4_experts(A16, A16, A16, 2048, 1024, 64, 256)
+    DN = ql.ql_w4_experts(A16, A16, A16, 512, 2048, 64, 256)
+    SG = ql.ql_w4(A16, A16, A16, 2048, 1024, 64)
+    SD = ql.ql_w4(A16, A16, A16, 512, 2048, 64)
+    wsb = L.moe_decode_workspace_bytes(1, 256, 8, 512)
+    assert wsb > 0
+    assert L.moe_decode_workspace_bytes(5, 256, 8, 512) == 0   # T > QL_DECODE_MAX_T
+    assert L.moe_decode_workspace_bytes(1, 256, 300, 512) == 0
+    assert L.moe_decode_logits_offset(1, 256, 8) >= 32 * 256 * 4
+    f = L.moe_decode
+
+    def call(T=1, D=2048, E=256, topk=8, gu=GU, dn=DN, sg=SG, sd=SD, H=A16, ws=A16, wsb=wsb, out=A16):
+        r = lambda x: ctypes.byref(x) if x is not None else None
+        return f(H, A16, None, T, D, E, topk, r(gu), r(dn), r(sg), r(sd), A16, A16, ws, wsb, out, None)
+
+    assert call(T=5) == SHAPE
+    assert call(T=-1) == INVALID
+    assert call(topk=300) == INVALID
+    assert call(topk=33) == SHAPE
+    assert call(E=128) == INVALID                    # experts in W != E
+    assert call(D=1024) == INVALID                   # gate_up K != D
+    assert call(sd=None) == INVALID                  # shared halves must come together
+    assert call(gu=None) == INVALID
+    assert call(dn=ql.ql_w4_experts(A16, A16, A16, 256, 2048, 64, 256)) == INVALID  # gate_up N != 2 I
+    assert call(gu=ql.ql_w4_experts(A16, A16, A16, 1536, 1024, 64, 256), D=1536,
+                dn=ql.ql_w4_experts(A16, A16, A16, 512, 1536, 64, 256),
+                sg=None, sd=None) == SHAPE           # D not a power of two
+    assert call(H=A16 + 2) == MISALIGNED
+    assert call(H=None) == INVALID
+    assert call(wsb=16) == WORKSPACE
+    assert call(ws=A16 + 16) == MISALIGNED
+    assert call(T=0) == OK

@@ -189,3 +189,115 @@ def test_moe_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
     ref = oracle.moe_layer(synth.moe_tokens(3000, 1)["H"], w, None, 8)
     assert_close(eager[0].astype(np.float64), ref["out"], "decode out")
+
+
+def _decode_args(dw, shared=True):
+    return dict(gate_up=dw["gate_up"], down=dw["down"],
+                shared_gate_up=dw["shared_gate_up"] if shared else None,
+                shared_down=dw["shared_down"] if shared else None)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_moe_decode_entry(seed):
+    """moe_decode (routing fused into the gate/up rows) on the decode shape:
+    the oracle's routing exactly, its output within the fp16 bar, and the
+    same bits as the three-call path."""
+    import torch
+    say(f"moe_decode seed={seed}")
+    w = synth.moe_weights(seed)
+    tok = synth.moe_tokens(seed + 1000, 1)
+    ref = oracle.moe_layer(tok["H"], w, None, 8)
+    dw = _dev_weights(w)
+    H = t(tok["H"])
+    res = ql.moe_decode(H, dw["Wr"], None, 8, **_decode_args(dw))
+    route, act, _, out3 = _run_layer(dw, H, None, 8, 1, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["ids"]), ref["ids"])
+    assert np.abs(host(res["gates"]).astype(np.float64) - ref["gates"]).max() < 2e-5
+    rel, mx = assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+    assert np.array_equal(host(res["ids"]), host(route["ids"]))
+    assert np.array_equal(host(res["gates"]).view(np.uint32), host(route["gates"]).view(np.uint32))
+    assert np.array_equal(host(res["out"]).view(np.uint16), host(out3).view(np.uint16))
+    off = ql.moe_decode_logits_offset(1, 256, 8)
+    Lg = host(res["workspace"])[off:off + 4 * 256].view(np.float32)
+    assert np.abs(Lg - ref["logits"][0]).max() < 2e-5
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
+    (1, 512, 256, 16, 2, 5, True),
+    (3, 512, 256, 16, 1, 6, True),
+    (4, 2048, 512, 256, 8, 7, True),
+    (2, 1024, 512, 32, 13, 8, True),
+    (2, 512, 128, 1000, 32, 9, True),    # E > 256: 16 keys per lane in the top-k
+    (3, 256, 64, 33, 5, 10, True),       # E % 8 != 0: scalar router partials
+    (2, 2048, 512, 256, 8, 11, False),   # no shared expert
+])
+def test_moe_decode_entry_shapes(T, D, I, E, topk, seed, shared):
+    import torch
+    say(f"moe_decode T={T} D={D} I={I} E={E} topk={topk} shared={shared}")
+    w = synth.moe_weights(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 60, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], topk, with_shared=shared)
+    dw = _dev_weights(w)
+    res = ql.moe_decode(t(tok["H"]), dw["Wr"], t(tok["logit_bias"]), topk, **_decode_args(dw, shared))
+    torch.cuda.synchronize()
+    ids = host(res["ids"])
+    near = oracle.topk_near_ties(ref["logits"], topk, 1e-4)
+    assert not near[:, -1].any(), "seed has a near tie at the top-k cut"
+    assert all(set(a) == set(b) for a, b in zip(ids.tolist(), ref["ids"].tolist()))
+    assert np.array_equal(ids[~near], ref["ids"][~near])
+    assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+
+
+def test_moe_decode_entry_reads_only_selected_experts():
+    """NaN scales in every expert the token did not choose leave moe_decode's
+    output finite and correct."""
+    import torch
+    seed = 5
+    w = synth.moe_weights(seed)
+    tok = synth.moe_tokens(seed + 1000, 1)
+    ref = oracle.moe_layer(tok["H"], w, None, 8)
+    chosen = set(ref["ids"][0].tolist())
+    for key in ("gate_up", "down"):
+        for e in range(256):
+            if e not in chosen:
+                w[key]["scales"][e] = np.float16(np.nan)
+    dw = _dev_weights(w)
+    res = ql.moe_decode(t(tok["H"]), dw["Wr"], None, 8, **_decode_args(dw))
+    torch.cuda.synchronize()
+    assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+
+
+def test_moe_decode_entry_graph_replays():
+    """moe_decode captured in a HIP graph for three tokens: every replay
+    matches the eager bits."""
+    import torch
+    w = synth.moe_weights(6)
+    dw = _dev_weights(w)
+    toks = [t(synth.moe_tokens(3100 + i, 1)["H"]) for i in range(3)]
+    outs = [ql.alloc_decode_outputs(1, 256, 8, 2048, 512, toks[0].device) for _ in toks]
+
+    def step(i):
+        ql.moe_decode(toks[i], dw["Wr"], None, 8, **_decode_args(dw), out=outs[i])
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    eager = [host(o["out"]).copy() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            step(i)
+    for rep in range(3):
+        for o in outs:
+            o["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert np.array_equal(host(outs[i]["out"]).view(np.uint16), eager[i].view(np.uint16)), (rep, i)
+        ql.qlinear_gemv(dw["shared_down"], toks[0][:, :512].contiguous())
+        torch.cuda.synchronize()
+    ref = oracle.moe_layer(synth.moe_tokens(3100, 1)["H"], w, None, 8)
+    assert_close(eager[0].astype(np.float64), ref["out"], "decode out")

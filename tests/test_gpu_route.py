@@ -142,6 +142,45 @@ def test_route_prefill(T, skewed, seed):
         assert all(set(a) == set(b) for a, b in zip(host(out["ids"]).tolist(), ids_ref.tolist()))
 
 
+@pytest.mark.parametrize("T,E,topk,seed", [
+    (1, 256, 8, 0), (16, 256, 8, 1), (300, 256, 8, 2), (1, 1000, 32, 3), (40, 1000, 32, 4),
+    (3, 33, 32, 5), (50, 33, 32, 6), (2, 64, 1, 7), (20, 200, 5, 8),
+])
+def test_route_exact_ties(T, E, topk, seed):
+    """Logits exact in fp32 with equal values at the top and across the
+    top-k cut: the selection must follow (logit descending, index
+    ascending) exactly, on every router and top-k path."""
+    import torch
+    say(f"route ties T={T} E={E} topk={topk}")
+    c = synth.router_tie_case(seed, T, topk, E=E)
+    out = ql.moe_route(t(c["H"]), t(c["Wr"]), None, topk)
+    torch.cuda.synchronize()
+    L64 = oracle.router_logits(c["H"], c["Wr"])
+    ids_ref, gates_ref = oracle.topk_route(L64, topk)
+    assert np.array_equal(host(out["ids"]), ids_ref)
+    assert np.abs(host(out["gates"]).astype(np.float64) - gates_ref).max() < 2e-5
+    off = ql.ql_moe_logits_offset(T, E, topk)
+    Lg = host(out["workspace"])[off:off + 4 * T * E].view(np.float32).reshape(T, E)
+    assert np.array_equal(Lg.astype(np.float64), L64)
+    _check_dispatch(out, ids_ref, E, T, topk)
+
+
+@pytest.mark.parametrize("T,E,topk", [(1, 256, 8), (64, 256, 8), (5, 1000, 32)])
+def test_route_all_logits_equal(T, E, topk):
+    """A zero router: every logit is 0, so experts 0..topk-1 win with equal
+    gates."""
+    import torch
+    say(f"route all-equal T={T} E={E} topk={topk}")
+    H = synth.activations(synth.rng_for(11), T, 2048)
+    Wr = np.zeros((2048, E), dtype=np.float16)
+    out = ql.moe_route(t(H), t(Wr), None, topk)
+    torch.cuda.synchronize()
+    ids = host(out["ids"])
+    assert np.array_equal(ids, np.tile(np.arange(topk, dtype=np.int32), (T, 1)))
+    assert np.abs(host(out["gates"]) - 1.0 / topk).max() < 1e-6
+    _check_dispatch(out, ids, E, T, topk)
+
+
 def test_route_workspace_reuse_across_sizes():
     """One workspace serves a sequence of routes of different sizes (small-T
     and many-token paths alternating); every call matches the oracle."""

@@ -173,3 +173,24 @@ def test_load_matched_tile_map_invariants():
                 assert n_tall == counts[e] // big
                 assert n_short == -(-(counts[e] % big) // small)
             assert len(tiles) <= (T * k) // small + E
+
+
+def test_tie_inputs_are_exact_in_float32():
+    """The exact-tie router inputs used by the GPU tests: float32 products
+    summed in a different order give the float64 logits bit for bit, the
+    copied columns tie, and the oracle takes the tied experts lowest index
+    first, with the cut inside the second group."""
+    for seed, T, E, topk in [(0, 4, 256, 8), (3, 2, 1000, 32), (5, 3, 33, 32)]:
+        c = synth.router_tie_case(seed, T, topk, E=E)
+        L64 = oracle.router_logits(c["H"], c["Wr"])
+        H32, W32 = c["H"].astype(np.float32), c["Wr"].astype(np.float32)
+        L32 = np.zeros((T, E), dtype=np.float32)
+        for d in range(H32.shape[1] - 1, -1, -1):  # reversed order
+            L32 += H32[:, d:d + 1] * W32[d:d + 1, :]
+        assert np.array_equal(L32.astype(np.float64), L64)
+        assert np.all(L64[:, c["top"]] == L64[:, [c["top"][0]]])
+        assert np.all(L64[:, c["edge"]] == L64[:, [c["edge"][0]]])
+        ids, _ = oracle.topk_route(L64, topk)
+        n_top = len(c["top"])
+        assert np.array_equal(ids[:, :n_top], np.tile(c["top"], (T, 1)))
+        assert np.array_equal(ids[:, n_top:], np.tile(c["edge"][:topk - n_top], (T, 1)))

@@ -7,11 +7,16 @@ step is both GEMVs.  `value` is the effective HBM bandwidth: algorithmic
 bytes (codes + scales + biases + x + y) per step divided by the step time,
 with every input already resident in HBM.  Weight copies are rotated so the
 working set between two uses of one copy exceeds the 256 MB Infinity Cache.
+`stats` adds the spread: the median step time (and head launch time) over
+30 event-bracketed rounds of 10 steps, with a 2,000-resample bootstrap 95%
+interval of that median, measured after the timed regions.
 
 Also measured and reported under "workloads" (same run, same rules): the
-prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the decode MoE
-layer (one token, 8 of 256 experts + shared) and the prefill MoE layer
-(4096 tokens, Zipf-skewed expert loads).
+prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the few-row
+GEMM, the bf16 variant, the FP8 / NVFP4 codecs, the decode fusions, the
+decode MoE layer (one token, 8 of 256 experts + shared; moe_decode and the
+three-call path) and the prefill MoE layer (4096 tokens, Zipf-skewed expert
+loads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-primary]
 """
@@ -104,6 +109,30 @@ def stage_times(stage_fns, steps, warmup, settle_s=0.0):
     for fn in stage_fns:
         out.append(timed_steps(fn, steps, warmup, settle_s))
     return out
+
+
+def round_stats(step_fn, rounds=30, per_round=10, resamples=2000, seed=0):
+    """Distribution of the step time: `rounds` event-bracketed rounds of
+    `per_round` back-to-back steps (after the main timed region, so that it
+    is not perturbed); returns the median ms per step over rounds and a
+    bootstrap 95% confidence interval of that median (`resamples` draws of
+    the rounds with replacement, percentile interval)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
+    evs[0].record()
+    i = 0
+    for r in range(rounds):
+        for _ in range(per_round):
+            step_fn(i)
+            i += 1
+        evs[r + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[r].elapsed_time(evs[r + 1]) / per_round for r in range(rounds)])
+    rng = np.random.default_rng(seed)
+    boot = np.median(per[rng.integers(0, rounds, size=(resamples, rounds))], axis=1)
+    lo, hi = np.percentile(boot, [2.5, 97.5])
+    return {"rounds": rounds, "steps_per_round": per_round, "median_ms": float(np.median(per)),
+            "ci95_ms": [float(lo), float(hi)], "resamples": resamples}
 
 
 USE_GRAPHS = True
@@ -203,12 +232,26 @@ def bench_gemv(args, dev):
     avg_launch_ms = kern_ms[1]
     avg_launch_bytes = launch_bytes[1]
     achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
+    # Spread of the step time and of the head launch (median over rounds and
+    # its bootstrap 95% interval), after the timed regions above.
+    st_step = round_stats(step)
+    st_head = round_stats(lambda i: ql.qlinear_gemv(Ws[i % copies][1], x, ys[1]))
+    to_gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    stats = {
+        "step": dict(st_step, **{"GB/s_median": to_gbs(step_bytes, st_step["median_ms"]),
+                                 "GB/s_ci95": [to_gbs(step_bytes, st_step["ci95_ms"][1]),
+                                               to_gbs(step_bytes, st_step["ci95_ms"][0])]}),
+        "head_launch": dict(st_head, **{"GB/s_median": to_gbs(avg_launch_bytes, st_head["median_ms"]),
+                                        "GB/s_ci95": [to_gbs(avg_launch_bytes, st_head["ci95_ms"][1]),
+                                                      to_gbs(avg_launch_bytes, st_head["ci95_ms"][0])]}),
+    }
     # The same step as a replayed HIP graph (launch overhead removed), for context.
     graph_ms = graph_time(step, copies * 2, 20) if copies * 2 <= 64 else None
     sha = source_sha("gemv.hip", "ql_device.h")
     traffic = traffic_for(KERNEL_GEMV, sha)
     return {
         "value": gbs, "ms_per_step": ms, "step_bytes": step_bytes, "rotation_copies": copies,
+        "stats": stats,
         "graph": None if graph_ms is None else {"ms_per_step": graph_ms,
                                                  "GB/s": step_bytes / (graph_ms * 1e-3) / 1e9},
         "per_matrix": {f"N={N}": {"us": float(kern_ms[j] * 1e3),
@@ -693,6 +736,7 @@ def main():
         "roofline": g["roofline"],
         "per_matrix": g["per_matrix"],
         "graph_step": g["graph"],
+        "stats": g["stats"],
     }
     if args.pmc_calibration:
         pmc_calibration(dev)

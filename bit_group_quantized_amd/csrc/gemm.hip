@@ -716,14 +716,10 @@ gemm_w4_grouped_kernel(const KParams p) {
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
 int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
     using TL = Tile<WM, WN, WGM, WGN>;
-    static bool attr_done = false;  // benign race: the attribute is idempotent
-    if (!attr_done) {
-        if (hipFuncSetAttribute((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)TL::LDS_BYTES) != hipSuccess)
-            return QL_ERR_HIP;
-        attr_done = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>,
+                                           TL::LDS_BYTES, lds_set))
+        return rc;
     hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>), grid, dim3(TL::NT), TL::LDS_BYTES, st,
                        p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
@@ -819,13 +815,9 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
 
 template <int MODE>
 int launch_grouped_t(const KParams& p, dim3 grid, hipStream_t st) {
-    static bool attr_done = false;  // benign race: the attribute is idempotent
-    if (!attr_done) {
-        if (hipFuncSetAttribute((const void*)gemm_w4_grouped_kernel<MODE>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGroupedLds) != hipSuccess)
-            return QL_ERR_HIP;
-        attr_done = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_grouped_kernel<MODE>, kGroupedLds, lds_set))
+        return rc;
     hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }

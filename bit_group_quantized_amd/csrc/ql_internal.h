@@ -6,12 +6,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/qlinear.h"
 
 #define QL_MAX_EXPERTS_DEV QL_MAX_EXPERTS
 #define QL_MAX_TOPK_DEV QL_MAX_TOPK
 
 namespace ql {
+
+// Raises a kernel's dynamic LDS limit on the current device, once per device
+// (bit d of `done` records device d; devices past 31 set it on every call).
+// Safe to call from several host threads.
+inline int set_max_dynamic_lds(const void* kernel, size_t bytes, std::atomic<uint32_t>& done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QL_ERR_HIP;
+    const uint32_t bit = (dev >= 0 && dev < 32) ? (1u << dev) : 0u;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return QL_OK;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+        return QL_ERR_HIP;
+    if (bit) done.fetch_or(bit, std::memory_order_release);
+    return QL_OK;
+}
 
 struct GemvArgs {
     const uint32_t* qweight;

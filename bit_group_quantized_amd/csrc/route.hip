@@ -506,19 +506,15 @@ int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t
     int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
     const size_t smem = (size_t)a.E * kMaskWords * sizeof(uint32_t);
     const size_t smem_scatter = smem + ((size_t)a.E + (size_t)kChunk * a.topk) * sizeof(int);
+    static std::atomic<uint32_t> lds_set{0};
+    const size_t max_smem = (size_t)QL_MAX_EXPERTS_DEV * kMaskWords * sizeof(uint32_t) +
+                            ((size_t)QL_MAX_EXPERTS_DEV + (size_t)kChunk * QL_MAX_TOPK_DEV) * sizeof(int);
+    if (const int rc = set_max_dynamic_lds((const void*)dispatch_scatter_kernel, max_smem, lds_set))
+        return rc;
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
                        a.E, a.topk, cc, cerr);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, cc, cerr, L.nchunks, a.E,
                        a.counts, a.offsets, hdr, tiles);
-    static bool attr_done = false;  // benign race: the attribute is idempotent
-    if (!attr_done) {
-        const size_t max_smem = (size_t)QL_MAX_EXPERTS_DEV * kMaskWords * sizeof(uint32_t) +
-                                ((size_t)QL_MAX_EXPERTS_DEV + (size_t)kChunk * QL_MAX_TOPK_DEV) * sizeof(int);
-        if (hipFuncSetAttribute((const void*)dispatch_scatter_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem) != hipSuccess)
-            return QL_ERR_HIP;
-        attr_done = true;
-    }
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nchunks), dim3(kChunk), smem_scatter, st, a.ids, a.T,
                        a.E, a.topk, a.offsets, cc, a.sorted_assign, a.pos,
                        reinterpret_cast<int2*>(a.ws + L.row_info),

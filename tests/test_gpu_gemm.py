@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
     (1, 2048, 512, 0), (7, 512, 200, 1), (256, 2048, 8192, 0), (300, 2048, 1000, 2),
     (129, 64, 257, 3), (1024, 1024, 640, 4), (2048, 512, 384, 5), (2500, 192, 300, 6),
     (700, 1024, 3000, 7), (1500, 512, 4000, 8), (2100, 256, 4100, 9),
+    (130, 32768, 70, 10),  # the largest K (QL_MAX_K)
 ])
 def test_gemm_matches_oracle(M, K, N, seed):
     """Ragged M and N in every tile class of the shape table (64 x 128,

@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
     (64, 5, 3), (192, 33, 4), (640, 70, 5),         # runtime-group fallbacks, ragged N
     (1024, 1000, 6), (4096, 129, 7), (8192, 65, 8), (16384, 17, 9),
     (2048, 1, 10), (2048, 3, 11),
+    (32768, 40, 12),                                # the largest K (QL_MAX_K)
 ])
 def test_gemv_matches_oracle(K, N, seed):
     say(f"gemv K={K} N={N} seed={seed}")

@@ -145,6 +145,7 @@ def test_route_prefill(T, skewed, seed):
 @pytest.mark.parametrize("T,E,topk,seed", [
     (1, 256, 8, 0), (16, 256, 8, 1), (300, 256, 8, 2), (1, 1000, 32, 3), (40, 1000, 32, 4),
     (3, 33, 32, 5), (50, 33, 32, 6), (2, 64, 1, 7), (20, 200, 5, 8),
+    (3, 1024, 32, 9), (100, 1024, 32, 10),  # QL_MAX_EXPERTS and QL_MAX_TOPK
 ])
 def test_route_exact_ties(T, E, topk, seed):
     """Logits exact in fp32 with equal values at the top and across the

@@ -614,6 +614,59 @@ def bench_moe_prefill(args, dev, w):
             "seed": seeds[0]}
 
 
+def bench_moe_prefill_bf16(args, dev):
+    """The same 4096-token layer with bf16 tokens, router weight, scales,
+    biases and outputs (moe_route_bf16 / moe_grouped_gemm_bf16 /
+    moe_combine_bf16)."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    T = 4096
+    w = synth.moe_weights_bf16(0)
+    tok = synth.moe_tokens_bf16(4, T, skewed=True)
+    as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else np.int32)).to(dev)
+    wd = lambda W: {"qweight": as_dev(W["qweight"]), "scales": as_dev(W["scales"]),
+                    "biases": as_dev(W["biases"]), "K": W["K"], "N": W["N"]}
+    dw = {k: wd(w[k]) for k in ("gate_up", "down", "shared_gate_up", "shared_down")}
+    Wr, H = as_dev(w["Wr"]), as_dev(tok["H"])
+    bias = torch.from_numpy(tok["logit_bias"]).to(dev)
+    route = ql.alloc_route_outputs(T, 256, 8, dev)
+    act = torch.empty((9 * T, 512), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((9 * T, 2048), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, 2048), dtype=torch.bfloat16, device=dev)
+
+    def r_(i):
+        ql.moe_route_bf16(H, Wr, bias, 8, route)
+
+    def gu(i):
+        ql.moe_grouped_gemm_bf16(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU,
+                                 route, act)
+
+    def dn(i):
+        ql.moe_grouped_gemm_bf16(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
+
+    def cb(i):
+        ql.moe_combine_bf16(yd, route["gates"], route["pos"], T, 8, True, out)
+
+    def step(i):
+        r_(i)
+        gu(i)
+        dn(i)
+        cb(i)
+
+    ms = timed_steps(step, 20, 3, settle_s=SETTLE_S)
+    k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2, settle_s=SETTLE_S / 4))
+    routed_rows = T * 8
+    flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
+             + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)
+    return {"tokens/s": T / (ms * 1e-3), "ms_per_step": ms, "flops": flops,
+            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma_bf16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
+                         "down": float(k[2] * 1e3), "combine": float(k[3] * 1e3)},
+            "seed": 4}
+
+
 CALIB_BYTES = 256 * 1024 * 1024
 
 
@@ -766,6 +819,8 @@ def main():
             if args.workload in ("all", "moe_prefill"):
                 log("bench: MoE prefill")
                 wl["moe_prefill_4096tok"] = bench_moe_prefill(args, dev, w)
+                log("bench: MoE prefill, bf16")
+                wl["moe_prefill_4096tok_bf16"] = bench_moe_prefill_bf16(args, dev)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline()

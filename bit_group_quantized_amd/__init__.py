@@ -83,6 +83,11 @@ _SIGS = {
                                         _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                         _P, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_route_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                      _P, ctypes.c_size_t, _P]),
+    "moe_grouped_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4), _P,
+                                             _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "moe_combine_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_decode_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
@@ -345,6 +350,49 @@ def moe_grouped_gemm(W: dict, shared: dict | None, X, T: int, topk: int, op: int
         _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(route.get("gates")),
         _ptr(route.get("pos")), _ptr(ws), ws.numel(), _ptr(Y), _stream(stream)))
     return Y
+
+
+def moe_route_bf16(H, Wr, logit_bias, topk: int, out: dict | None = None, stream=None) -> dict:
+    """moe_route with bf16 H and Wr (tensors of bf16 patterns, any 16-bit dtype)."""
+    T, D = H.shape
+    E = Wr.shape[1]
+    if out is None:
+        out = alloc_route_outputs(T, E, topk, H.device)
+    ws = out["workspace"]
+    _check("moe_route_bf16", lib().moe_route_bf16(
+        _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, _ptr(out["ids"]), _ptr(out["gates"]),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["sorted_assign"]), _ptr(out["pos"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_grouped_gemm_bf16(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
+                          Y=None, stream=None):
+    """moe_grouped_gemm with bf16 X, scales, biases and Y (QL_OP_GATE_UP_SILU or QL_OP_DOWN)."""
+    import torch
+    w = make_w4_experts(W)
+    s = make_w4(shared) if shared is not None else None
+    rows = T * topk + (T if shared is not None else 0)
+    if Y is None:
+        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        Y = torch.empty(shape, dtype=torch.bfloat16, device=X.device)
+    ws = route["workspace"]
+    _check("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
+        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
+        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
+        _stream(stream)))
+    return Y
+
+
+def moe_combine_bf16(Ydown, gates, pos, T: int, topk: int, has_shared: bool, out=None, stream=None):
+    """moe_combine over bf16 rows; out holds bf16 patterns."""
+    import torch
+    N = Ydown.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=Ydown.device)
+    _check("moe_combine_bf16", lib().moe_combine_bf16(_ptr(Ydown), _ptr(gates), _ptr(pos), T, topk, N,
+                                                      int(has_shared), _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_decode_workspace_bytes(T: int, E: int, topk: int, I: int) -> int:

@@ -227,10 +227,10 @@ static int check_route_common(int32_t T, int32_t E, int32_t topk, const int32_t*
     return QL_OK;
 }
 
-int moe_route(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
-              int32_t E, int32_t topk, int32_t* topk_ids, float* topk_gates, int32_t* counts,
-              int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, void* workspace,
-              size_t ws_bytes, void* stream) {
+static int route_impl(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                      int32_t D, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_gates,
+                      int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                      int32_t* assign_pos, void* workspace, size_t ws_bytes, void* stream, bool bf16) {
     int rc = check_route_common(T, E, topk, counts, offsets, sorted_assign, assign_pos, workspace,
                                 ws_bytes);
     if (rc != QL_OK) return rc;
@@ -241,9 +241,25 @@ int moe_route(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, in
         !aligned(topk_gates, 4))
         return QL_ERR_MISALIGNED;
     ql::RouteArgs a{H, Wr, logit_bias, T, D, E, topk, topk_ids, topk_gates, counts, offsets,
-                    sorted_assign, assign_pos, static_cast<unsigned char*>(workspace)};
+                    sorted_assign, assign_pos, static_cast<unsigned char*>(workspace), bf16};
     if (T == 0) return ql::launch_dispatch(a, as_stream(stream));  // counts = 0, offsets = 0
     return ql::launch_route(a, as_stream(stream));
+}
+
+int moe_route(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
+              int32_t E, int32_t topk, int32_t* topk_ids, float* topk_gates, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, void* workspace,
+              size_t ws_bytes, void* stream) {
+    return route_impl(H, Wr, logit_bias, T, D, E, topk, topk_ids, topk_gates, counts, offsets,
+                      sorted_assign, assign_pos, workspace, ws_bytes, stream, false);
+}
+
+int moe_route_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                   int32_t D, int32_t E, int32_t topk, int32_t* topk_ids, float* topk_gates,
+                   int32_t* counts, int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                   void* workspace, size_t ws_bytes, void* stream) {
+    return route_impl(H, Wr, logit_bias, T, D, E, topk, topk_ids, topk_gates, counts, offsets,
+                      sorted_assign, assign_pos, workspace, ws_bytes, stream, true);
 }
 
 int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk, int32_t* counts,
@@ -260,11 +276,11 @@ int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk, in
     return ql::launch_dispatch(a, as_stream(stream));
 }
 
-int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X, int32_t T,
-                     int32_t topk, int32_t op, const int32_t* offsets,
-                     const int32_t* sorted_assign, const float* topk_gates,
-                     const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
-                     uint16_t* Y, void* stream) {
+static int grouped_impl(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X, int32_t T,
+                        int32_t topk, int32_t op, const int32_t* offsets,
+                        const int32_t* sorted_assign, const float* topk_gates,
+                        const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
+                        uint16_t* Y, void* stream, bool bf16) {
     if (!W) return QL_ERR_INVALID_ARG;
     if (op != QL_OP_GATE_UP_SILU && op != QL_OP_DOWN && op != QL_OP_DOWN_COMBINE)
         return QL_ERR_INVALID_ARG;
@@ -288,7 +304,9 @@ int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t
     if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
 
-    const bool rows_path = T <= QL_DECODE_MAX_T && ql::moe_rows_supported(W->K);
+    // The row-parallel decode kernels are fp16 only; the bf16 layer runs
+    // every T on the tiled path.
+    const bool rows_path = !bf16 && T <= QL_DECODE_MAX_T && ql::moe_rows_supported(W->K);
     if (op == QL_OP_DOWN_COMBINE) {
         if (!rows_path) return QL_ERR_UNSUPPORTED_SHAPE;
         if (!topk_gates || !assign_pos) return QL_ERR_INVALID_ARG;
@@ -302,9 +320,27 @@ int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t
                       shared ? shared->biases : nullptr,
                       X, offsets, sorted_assign, topk_gates, assign_pos,
                       static_cast<const unsigned char*>(workspace), Y,
-                      W->K, W->N, E, T, topk, op};
+                      W->K, W->N, E, T, topk, op, bf16};
     if (rows_path) return ql::launch_moe_rows(a, as_stream(stream));
     return ql::launch_moe_grouped(a, as_stream(stream));
+}
+
+int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X, int32_t T,
+                     int32_t topk, int32_t op, const int32_t* offsets,
+                     const int32_t* sorted_assign, const float* topk_gates,
+                     const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
+                     uint16_t* Y, void* stream) {
+    return grouped_impl(W, shared, X, T, topk, op, offsets, sorted_assign, topk_gates, assign_pos,
+                        workspace, ws_bytes, Y, stream, false);
+}
+
+int moe_grouped_gemm_bf16(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X,
+                          int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
+                          const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
+                          uint16_t* Y, void* stream) {
+    if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
+    return grouped_impl(W, shared, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr,
+                        workspace, ws_bytes, Y, stream, true);
 }
 
 size_t moe_decode_workspace_bytes(int32_t T, int32_t E, int32_t topk, int32_t I) {
@@ -367,9 +403,9 @@ int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, i
     return ql::launch_moe_decode(a, as_stream(stream));
 }
 
-int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
-                int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
-                void* stream) {
+static int combine_impl(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                        int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
+                        void* stream, bool bf16) {
     if (T < 0 || N < 0 || topk <= 0) return QL_ERR_INVALID_ARG;
     if (topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
     if (T == 0 || N == 0) return QL_OK;
@@ -379,7 +415,19 @@ int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* a
         !aligned(assign_pos, 4))
         return QL_ERR_MISALIGNED;
     return ql::launch_combine(Ydown, topk_gates, assign_pos, T, topk, N, has_shared ? 1 : 0, out,
-                              as_stream(stream));
+                              as_stream(stream), bf16);
+}
+
+int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
+                void* stream) {
+    return combine_impl(Ydown, topk_gates, assign_pos, T, topk, N, has_shared, out, stream, false);
+}
+
+int moe_combine_bf16(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                     int32_t T, int32_t topk, int32_t N, int32_t has_shared, uint16_t* out,
+                     void* stream) {
+    return combine_impl(Ydown, topk_gates, assign_pos, T, topk, N, has_shared, out, stream, true);
 }
 
 }  // extern "C"

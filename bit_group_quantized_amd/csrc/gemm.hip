@@ -125,11 +125,11 @@ struct Job {
 };
 
 // DT: 0 = fp16 activations, scales, biases, outputs and MFMA operands;
-// 1 = bf16 throughout (dense mode only).
+// 1 = bf16 throughout (the router's weight is then bf16 too; its logits
+// stay fp32 partials in both cases).
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
-    static_assert(DT == 0 || MODE == MODE_DENSE, "bf16 is served by the dense GEMM only");
     constexpr int BM = TL::BM, BN = TL::BN;
     f16* As = lds;                     // [2][BM][kLdk]
     f16* Bs = lds + 2 * TL::LDS_A;     // [2][BN][kLdk]
@@ -655,7 +655,7 @@ static_assert(ShortTile::BM == QL_MOE_TILE_ROWS && TallTile::BM == 2 * QL_MOE_TI
 constexpr size_t kGroupedLds =
     TallTile::LDS_BYTES > ShortTile::LDS_BYTES ? TallTile::LDS_BYTES : ShortTile::LDS_BYTES;
 
-template <int MODE>
+template <int MODE, int DT>
 __global__ void __launch_bounds__(TallTile::NT)
 gemm_w4_grouped_kernel(const KParams p) {
     extern __shared__ __align__(16) f16 lds[];
@@ -708,9 +708,9 @@ gemm_w4_grouped_kernel(const KParams p) {
     }
     job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
     if (tall)
-        gemm_tile<4, 2, 2, 4, MODE>(p, job, lds);
+        gemm_tile<4, 2, 2, 4, MODE, DT>(p, job, lds);
     else
-        gemm_tile<2, 2, 2, 4, MODE>(p, job, lds);
+        gemm_tile<2, 2, 2, 4, MODE, DT>(p, job, lds);
 }
 
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
@@ -798,7 +798,7 @@ int launch_gemm_ws(const GemmArgs& a, hipStream_t st) {
 constexpr int kRouterSplit = kRouterMfmaSplit;
 
 int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
-                              int E, hipStream_t st) {
+                              int E, hipStream_t st, bool bf16) {
     KParams p{};
     p.A = H;
     p.M = T;
@@ -809,16 +809,17 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
     p.ksplit = kRouterSplit;
     using TL = Tile<1, 4, 2, 2>;
     dim3 grid((T + TL::BM - 1) / TL::BM, (E + TL::BN - 1) / TL::BN, kRouterSplit);
+    if (bf16) return launch_t<1, 4, 2, 2, MODE_ROUTER, 1>(p, grid, st);
     return launch_t<1, 4, 2, 2, MODE_ROUTER>(p, grid, st);
 }
 
 
-template <int MODE>
+template <int MODE, int DT>
 int launch_grouped_t(const KParams& p, dim3 grid, hipStream_t st) {
     static std::atomic<uint32_t> lds_set{0};
-    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_grouped_kernel<MODE>, kGroupedLds, lds_set))
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_grouped_kernel<MODE, DT>, kGroupedLds, lds_set))
         return rc;
-    hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
+    hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE, DT>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -852,8 +853,12 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     if (blocks > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
     if (blocks == 0) return QL_OK;
     const dim3 grid((unsigned)blocks);
-    if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP>(p, grid, st);
-    return launch_grouped_t<MODE_DOWN>(p, grid, st);
+    if (a.bf16) {
+        if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 1>(p, grid, st);
+        return launch_grouped_t<MODE_DOWN, 1>(p, grid, st);
+    }
+    if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 0>(p, grid, st);
+    return launch_grouped_t<MODE_DOWN, 0>(p, grid, st);
 }
 
 }  // namespace ql

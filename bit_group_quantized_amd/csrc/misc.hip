@@ -6,7 +6,8 @@
 // significant nibble first.
 //
 // Combine: same page, section 减少中间状态和流量 - the expert outputs are
-// weighted by the routing scores and the shared expert's result is added.
+// weighted by the routing scores and the shared expert's result is added
+// (fp16 rows, or bf16 rows for the bf16 variant of the layer).
 // One workgroup per token sums its rows in a fixed order, so the result
 // does not depend on scheduling (no atomics).
 #include "ql_device.h"
@@ -30,7 +31,8 @@ pack_kernel(const uint8_t* __restrict__ codes, int64_t nwords, uint32_t* __restr
 }
 
 // out[t][n] = sum_j gates[t][j] * Yd[pos[t*topk+j]][n] (+ Yd[T*topk+t][n]).
-template <bool VEC>
+// BF16: rows and output hold bf16 patterns instead of fp16.
+template <bool VEC, bool BF16>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t* __restrict__ Yd, const float* __restrict__ gates,
                const int* __restrict__ pos, int T, int topk, int N, int has_shared,
@@ -66,15 +68,33 @@ combine_kernel(const uint16_t* __restrict__ Yd, const float* __restrict__ gates,
             const int row = s_row[j];
             if (row < 0) continue;
             const u32x4 w = ld_u32x4(Yd + (size_t)row * N + n8 * 8);
-            const f16x8 h = __builtin_bit_cast(f16x8, w);
             const float g = s_g[j];
+            if constexpr (BF16) {
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int v = 0; v < 8; ++v) acc[v] += g * (float)h[v];
+                for (int v = 0; v < 4; ++v) {
+                    acc[2 * v] += g * bf2f((uint16_t)(ww[v] & 0xFFFFu));
+                    acc[2 * v + 1] += g * bf2f((uint16_t)(ww[v] >> 16));
+                }
+            } else {
+                const f16x8 h = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[v] += g * (float)h[v];
+            }
         }
-        f16x8 o;
+        if constexpr (BF16) {
+            u32x4 o;
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
+            *reinterpret_cast<u32x4*>(out + (size_t)t * N + n8 * 8) = o;
+        } else {
+            f16x8 o;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) o[v] = (f16)acc[v];
-        *reinterpret_cast<f16x8*>(out + (size_t)t * N + n8 * 8) = o;
+            for (int v = 0; v < 8; ++v) o[v] = (f16)acc[v];
+            *reinterpret_cast<f16x8*>(out + (size_t)t * N + n8 * 8) = o;
+        }
     } else {
         const int n = blockIdx.x * blockDim.x + threadIdx.x;
         if (n >= N) return;
@@ -82,9 +102,10 @@ combine_kernel(const uint16_t* __restrict__ Yd, const float* __restrict__ gates,
         for (int j = 0; j < J; ++j) {
             const int row = s_row[j];
             if (row < 0) continue;
-            acc += s_g[j] * h2f(Yd[(size_t)row * N + n]);
+            const uint16_t y = Yd[(size_t)row * N + n];
+            acc += s_g[j] * (BF16 ? bf2f(y) : h2f(y));
         }
-        out[(size_t)t * N + n] = f2h(acc);
+        out[(size_t)t * N + n] = BF16 ? f2bf(acc) : f2h(acc);
     }
 }
 
@@ -97,18 +118,29 @@ int launch_pack(const uint8_t* codes, int N, int K, uint32_t* qweight, hipStream
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
-int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
-                   int N, int has_shared, uint16_t* out, hipStream_t st) {
+namespace {
+
+template <bool BF16>
+void launch_combine_t(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
+                      int N, int has_shared, uint16_t* out, hipStream_t st) {
     const int64_t nrows = (int64_t)T * topk + (has_shared ? T : 0);
     if (N % 8 == 0) {
         dim3 grid((N / 8 + 255) / 256, T);
-        hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, st, Yd, gates, pos, T, topk,
-                           N, has_shared, nrows, out);
+        hipLaunchKernelGGL((combine_kernel<true, BF16>), grid, dim3(256), 0, st, Yd, gates, pos, T,
+                           topk, N, has_shared, nrows, out);
     } else {
         dim3 grid((N + 255) / 256, T);
-        hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, st, Yd, gates, pos, T, topk,
-                           N, has_shared, nrows, out);
+        hipLaunchKernelGGL((combine_kernel<false, BF16>), grid, dim3(256), 0, st, Yd, gates, pos, T,
+                           topk, N, has_shared, nrows, out);
     }
+}
+
+}  // namespace
+
+int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
+                   int N, int has_shared, uint16_t* out, hipStream_t st, bool bf16) {
+    if (bf16) launch_combine_t<true>(Yd, gates, pos, T, topk, N, has_shared, out, st);
+    else launch_combine_t<false>(Yd, gates, pos, T, topk, N, has_shared, out, st);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 

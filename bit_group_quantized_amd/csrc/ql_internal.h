@@ -117,14 +117,15 @@ struct RouteArgs {
     int32_t* sorted_assign;
     int32_t* pos;
     unsigned char* ws;
+    bool bf16 = false;  // H and Wr hold bf16 patterns
 };
 int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
-                              int E, hipStream_t st);
+                              int E, hipStream_t st, bool bf16 = false);
 bool router_uses_mfma(int T, int E);
 // Small-T router partials: [T][kRouterSmallParts][E] fp32; their sum over the
 // slices in ascending order (plus the bias) is the logit.
 int launch_router_partials_small(const uint16_t* H, const uint16_t* Wr, float* partials, int T,
-                                 int D, int E, hipStream_t st);
+                                 int D, int E, hipStream_t st, bool bf16 = false);
 int launch_route(const RouteArgs& a, hipStream_t st);
 MoeWorkspace moe_workspace_layout(int T, int E, int topk);     // logits + top-k + dispatch
 int launch_dispatch(const RouteArgs& a, hipStream_t st);  // dispatch only (ids given)
@@ -144,6 +145,7 @@ struct GroupedArgs {
     const unsigned char* ws;
     uint16_t* Y;
     int K, N, E, T, topk, op;
+    bool bf16 = false;  // X, scales, biases and Y hold bf16 patterns
 };
 bool moe_rows_supported(int K);
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel
@@ -185,6 +187,6 @@ struct DecodeArgs {
 int launch_moe_decode(const DecodeArgs& a, hipStream_t st);
 
 int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
-                   int N, int has_shared, uint16_t* out, hipStream_t st);
+                   int N, int has_shared, uint16_t* out, hipStream_t st, bool bf16 = false);
 
 }  // namespace ql

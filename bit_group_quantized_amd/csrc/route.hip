@@ -57,6 +57,14 @@ __device__ int block_inclusive_scan(int v, int* s_tmp /* >= 16 ints */) {
 // Small-T router: partial logits over D/32-row slices, summed by the top-k
 // step in a fixed order.
 // ---------------------------------------------------------------------------
+// 16-bit value of H or Wr as fp32: fp16, or bf16 for the bf16 variant.
+template <bool BF16>
+__device__ __forceinline__ float in16(uint16_t v) {
+    if constexpr (BF16) return bf2f(v);
+    else return h2f(v);
+}
+
+template <bool BF16>
 __device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__ H,
                                                     const uint16_t* __restrict__ Wr,
                                                     float* __restrict__ partials, int D, int E) {
@@ -64,11 +72,11 @@ __device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__
     const int t = blockIdx.y, p = blockIdx.x;
     const int rows = D / kRouterParts;
     const int d0 = p * rows;
-    for (int i = threadIdx.x; i < rows; i += blockDim.x) hs[i] = h2f(H[(size_t)t * D + d0 + i]);
+    for (int i = threadIdx.x; i < rows; i += blockDim.x) hs[i] = in16<BF16>(H[(size_t)t * D + d0 + i]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         float acc = 0.f;
-        for (int d = 0; d < rows; ++d) acc += hs[d] * h2f(Wr[(size_t)(d0 + d) * E + e]);
+        for (int d = 0; d < rows; ++d) acc += hs[d] * in16<BF16>(Wr[(size_t)(d0 + d) * E + e]);
         partials[((size_t)t * kRouterParts + p) * E + e] = acc;
     }
 }
@@ -77,6 +85,7 @@ __device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__
 // 8*oct .. 8*oct+7 and the rows dl, dl+8, ... of the block's D slice; the 8
 // row lanes of an expert octet are summed through LDS in a fixed order.
 // Requires E % 8 == 0.
+template <bool BF16>
 __device__ __forceinline__ void router_partial_vec_body(const uint16_t* __restrict__ H,
                                                         const uint16_t* __restrict__ Wr,
                                                         float* __restrict__ partials, int D, int E) {
@@ -96,10 +105,14 @@ __device__ __forceinline__ void router_partial_vec_body(const uint16_t* __restri
         if (e8 < E) {
 #pragma unroll 8
             for (int d = dl; d < rows; d += 8) {
-                const float h = h2f(H[(size_t)t * D + d0 + d]);
-                const f16x8 w = __builtin_bit_cast(f16x8, ld_u32x4(Wr + (size_t)(d0 + d) * E + e8));
+                const float h = in16<BF16>(H[(size_t)t * D + d0 + d]);
+                const u32x4 wv = ld_u32x4(Wr + (size_t)(d0 + d) * E + e8);
+                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-                for (int v = 0; v < 8; ++v) acc[v] += h * (float)w[v];
+                for (int v = 0; v < 4; ++v) {
+                    acc[2 * v] += h * in16<BF16>((uint16_t)(ww[v] & 0xFFFFu));
+                    acc[2 * v + 1] += h * in16<BF16>((uint16_t)(ww[v] >> 16));
+                }
             }
         }
 #pragma unroll
@@ -116,16 +129,18 @@ __device__ __forceinline__ void router_partial_vec_body(const uint16_t* __restri
     }
 }
 
+template <bool BF16>
 __global__ void __launch_bounds__(256)
 router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
                       float* __restrict__ partials, int D, int E) {
-    router_partial_body(H, Wr, partials, D, E);
+    router_partial_body<BF16>(H, Wr, partials, D, E);
 }
 
+template <bool BF16>
 __global__ void __launch_bounds__(256)
 router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
                           float* __restrict__ partials, int D, int E) {
-    router_partial_vec_body(H, Wr, partials, D, E);
+    router_partial_vec_body<BF16>(H, Wr, partials, D, E);
 }
 
 template <int EPL, int NP>
@@ -561,14 +576,25 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
 }
 
 
-int launch_router_partials_small(const uint16_t* H, const uint16_t* Wr, float* partials, int T,
-                                 int D, int E, hipStream_t st) {
+namespace {
+
+template <bool BF16>
+void launch_router_partials_t(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
+                              int E, hipStream_t st) {
     if (E % 8 == 0)
-        hipLaunchKernelGGL(router_partial_vec_kernel, dim3(kRouterParts, T), dim3(256), 0, st, H, Wr,
-                           partials, D, E);
+        hipLaunchKernelGGL((router_partial_vec_kernel<BF16>), dim3(kRouterParts, T), dim3(256), 0, st,
+                           H, Wr, partials, D, E);
     else
-        hipLaunchKernelGGL(router_partial_kernel, dim3(kRouterParts, T), dim3(256), 0, st, H, Wr,
-                           partials, D, E);
+        hipLaunchKernelGGL((router_partial_kernel<BF16>), dim3(kRouterParts, T), dim3(256), 0, st, H,
+                           Wr, partials, D, E);
+}
+
+}  // namespace
+
+int launch_router_partials_small(const uint16_t* H, const uint16_t* Wr, float* partials, int T,
+                                 int D, int E, hipStream_t st, bool bf16) {
+    if (bf16) launch_router_partials_t<true>(H, Wr, partials, T, D, E, st);
+    else launch_router_partials_t<false>(H, Wr, partials, T, D, E, st);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -577,10 +603,10 @@ int launch_route(const RouteArgs& a, hipStream_t st) {
     float* logits = reinterpret_cast<float*>(a.ws + L.logits);
     float* partials = reinterpret_cast<float*>(a.ws + L.partials);
     if (router_uses_mfma(a.T, a.E)) {
-        const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st);
+        const int rc = launch_router_logits_mfma(a.H, a.Wr, partials, a.T, a.D, a.E, st, a.bf16);
         if (rc != QL_OK) return rc;
     } else {
-        const int rc = launch_router_partials_small(a.H, a.Wr, partials, a.T, a.D, a.E, st);
+        const int rc = launch_router_partials_small(a.H, a.Wr, partials, a.T, a.D, a.E, st, a.bf16);
         if (rc != QL_OK) return rc;
         if (a.T <= kRouterSmallT) return launch_small_any(a, L, true, st);
     }

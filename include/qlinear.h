@@ -407,6 +407,36 @@ int moe_combine(const uint16_t* Ydown, const float* topk_gates, const int32_t* a
                 uint16_t* out, void* stream);
 
 /*
+ * bf16 variant of the routed-expert layer (prefill and any T): [PPLX]
+ * dequantization section - the page's checkpoint keeps scales and biases in
+ * bf16 and its matrix path multiplies bf16 operands.  Same layouts, rows,
+ * workspace and determinism as the fp16 calls above, with every 16-bit
+ * array holding bf16 patterns: H and the router weight Wr (moe_route_bf16;
+ * logits still accumulated in fp32), X, the experts' scales and biases and
+ * Y (moe_grouped_gemm_bf16: W and shared point at bf16 scales/biases; the
+ * dequantized weight is bf16(s*q + b), one rounding, and the products run
+ * on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; act = SiLU(gate) * up
+ * rounded to bf16), Ydown and out (moe_combine_bf16).  moe_grouped_gemm_bf16
+ * serves QL_OP_GATE_UP_SILU and QL_OP_DOWN for every T on the tiled path;
+ * QL_OP_DOWN_COMBINE returns UNSUPPORTED_SHAPE.
+ * Errors: as the fp16 calls.
+ */
+int moe_route_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+                   int32_t T, int32_t D, int32_t E, int32_t topk,
+                   int32_t* topk_ids, float* topk_gates,
+                   int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_assign, int32_t* assign_pos,
+                   void* workspace, size_t ws_bytes, void* stream);
+int moe_grouped_gemm_bf16(const ql_w4_experts* W, const ql_w4* shared,
+                          const uint16_t* X, int32_t T, int32_t topk, int32_t op,
+                          const int32_t* offsets, const int32_t* sorted_assign,
+                          const void* workspace, size_t ws_bytes,
+                          uint16_t* Y, void* stream);
+int moe_combine_bf16(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
+                     int32_t T, int32_t topk, int32_t N, int32_t has_shared,
+                     uint16_t* out, void* stream);
+
+/*
  * moe_decode - the whole routed-expert layer for a few decode tokens in
  * three launches: router partial sums; the token's top-k fused into the
  * gate/up rows (each routed workgroup finishes its token's logits, takes

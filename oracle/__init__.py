@@ -37,7 +37,8 @@ from .route import (router_logits, softmax, topk_route, histogram,
                     topk_near_ties)
 from .moe import silu, expert_ffn, combine, moe_layer
 from .decode import rms_norm, gemv_rmsnorm, argmax_first, lm_head_token, embed_row
-from .bf16 import bf16_to_f64, round_bf16, dequantize_bf16, linear_bf16
+from .bf16 import (bf16_to_f64, round_bf16, dequantize_bf16, linear_bf16, expert_ffn_bf16,
+                   moe_layer_bf16)
 from .codecs import (e4m3_to_f64, e2m1_to_f64, dequantize_fp8, dequantize_nvfp4, linear_fp8,
                      linear_nvfp4)
 
@@ -47,6 +48,7 @@ __all__ = [
     "stable_permutation", "tile_map", "load_matched_tile_map", "topk_near_ties",
     "silu", "expert_ffn", "combine", "moe_layer",
     "rms_norm", "gemv_rmsnorm", "argmax_first", "lm_head_token", "embed_row",
-    "bf16_to_f64", "round_bf16", "dequantize_bf16", "linear_bf16",
+    "bf16_to_f64", "round_bf16", "dequantize_bf16", "linear_bf16", "expert_ffn_bf16",
+    "moe_layer_bf16",
     "e4m3_to_f64", "e2m1_to_f64", "dequantize_fp8", "dequantize_nvfp4", "linear_fp8", "linear_nvfp4",
 ]

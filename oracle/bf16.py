@@ -7,7 +7,9 @@ Perplexity, "Optimizing on-device inference for Apple Silicon", section
 "在矩阵乘法期间进行权重反量化": the page's checkpoint keeps the per-group
 scale and bias in bfloat16 and the matrix path multiplies bf16 operands.
 The reconstruction is the same as in w4.py, w = scale * code + bias per
-group of 64 along K; only the 16-bit type changes.
+group of 64 along K; only the 16-bit type changes.  The routed-expert layer
+(moe_layer_bf16) is moe.moe_layer with bf16 tokens, router weight and
+expert scales/biases, and its 16-bit intermediate (act) rounded to bf16.
 
 numpy has no bf16 type, so bf16 values are carried as uint16 bit patterns
 (the upper half of the float32 pattern) and decoded exactly.
@@ -25,6 +27,9 @@ from __future__ import annotations
 
 import numpy as np
 
+from .moe import combine, silu
+from .route import (exclusive_scan, histogram, router_logits, stable_permutation,
+                    topk_route)
 from .w4 import GROUP, unpack_codes
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -76,3 +81,58 @@ def linear_bf16(X_bits, W: dict, row_chunk: int = 8192) -> np.ndarray:
         Wd = dequantize_bf16(W["qweight"][n0:n1], W["scales"][n0:n1], W["biases"][n0:n1], K)
         Y[:, n0:n1] = X @ Wd.T
     return Y
+
+
+def expert_ffn_bf16(X_bits, gate_up: dict, down: dict):
+    """One expert on bf16 rows X [R][D]: u = X . Wgu in float64; act =
+    bf16(SiLU(u[:, :I]) * u[:, I:]) (bf16 patterns, the 16-bit intermediate
+    of the layer); ydown = act . Wdn in float64."""
+    X = bf16_to_f64(np.atleast_2d(np.asarray(X_bits, dtype=np.uint16)))
+    I = gate_up["N"] // 2
+    Wgu = dequantize_bf16(gate_up["qweight"], gate_up["scales"], gate_up["biases"], gate_up["K"])
+    u = X @ Wgu.T
+    act = round_bf16(silu(u[:, :I]) * u[:, I:])
+    Wdn = dequantize_bf16(down["qweight"], down["scales"], down["biases"], down["K"])
+    ydown = bf16_to_f64(act) @ Wdn.T
+    return act, ydown
+
+
+def moe_layer_bf16(H_bits, weights: dict, logit_bias=None, topk: int = 8,
+                   with_shared: bool = True) -> dict:
+    """The routed-expert layer of moe.moe_layer with bf16 tokens H (patterns
+    [T][D]), router weight and expert scales/biases: the same routing
+    (logits from the exactly decoded bf16 values, fp64), dispatch and
+    combine; act is rounded to bf16.  Returns logits, ids, gates, counts,
+    offsets, sorted_assign, pos, act (bf16 patterns), ydown and out (float64).
+    """
+    H_bits = np.asarray(H_bits, dtype=np.uint16)
+    T = H_bits.shape[0]
+    E = weights["Wr"].shape[1]
+    logits = router_logits(bf16_to_f64(H_bits), bf16_to_f64(weights["Wr"]), logit_bias)
+    ids, gates = topk_route(logits, topk)
+    counts = histogram(ids, E)
+    offsets = exclusive_scan(counts)
+    sorted_assign, pos = stable_permutation(ids, E)
+
+    I = weights["gate_up"]["N"] // 2
+    D = weights["down"]["N"]
+    R = T * topk + (T if with_shared else 0)
+    act = np.zeros((R, I), dtype=np.uint16)
+    ydown = np.zeros((R, D), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        tokens = sorted_assign[r0:r1] // topk
+        one = lambda W: {k: (v[e] if isinstance(v, np.ndarray) else v) for k, v in W.items()}
+        a, y = expert_ffn_bf16(H_bits[tokens], one(weights["gate_up"]), one(weights["down"]))
+        act[r0:r1] = a
+        ydown[r0:r1] = y
+    if with_shared:
+        a, y = expert_ffn_bf16(H_bits, weights["shared_gate_up"], weights["shared_down"])
+        act[T * topk:] = a
+        ydown[T * topk:] = y
+    out = combine(ydown, gates, pos, T, topk, with_shared)
+    return {"logits": logits, "ids": ids, "gates": gates, "counts": counts,
+            "offsets": offsets, "sorted_assign": sorted_assign, "pos": pos,
+            "act": act, "ydown": ydown, "out": out}

@@ -86,17 +86,17 @@ def bf16_bits(a) -> np.ndarray:
     return u.astype(np.uint16)
 
 
-def w4_matrix_bf16(rng: np.random.Generator, K: int, N: int) -> dict:
-    """A K x N w4 matrix with bf16 scales and biases (uint16 patterns),
-    drawn like w4_matrix."""
+def w4_matrix_bf16(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
+    """A K x N w4 matrix (or a stack of them, as w4_matrix) with bf16 scales
+    and biases (uint16 patterns), drawn like w4_matrix."""
     if K % 8:
         raise ValueError("K must be a multiple of 8 to draw packed words")
     G = (K + GROUP - 1) // GROUP
-    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
-    s = rng.uniform(0.002, 0.02, size=(N, G))
+    words = rng.integers(0, 2**32, size=lead + (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    s = rng.uniform(0.002, 0.02, size=lead + (N, G))
     scales = bf16_bits(s)
     s_dec = (scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    biases = bf16_bits(-8.0 * s_dec + rng.normal(0.0, 1e-3, size=(N, G)))
+    biases = bf16_bits(-8.0 * s_dec + rng.normal(0.0, 1e-3, size=lead + (N, G)))
     return {"qweight": words, "scales": scales, "biases": biases, "K": K, "N": N}
 
 
@@ -246,6 +246,30 @@ def router_tie_case(seed: int, T: int, topk: int, D: int = HIDDEN, E: int = NUM_
     W[:, top] = W[:, [top[0]]]
     W[:, edge] = W[:, [edge[0]]]
     return {"H": f16(H), "Wr": f16(W / 256.0), "top": np.sort(top), "edge": np.sort(edge)}
+
+
+def moe_weights_bf16(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:
+    """moe_weights with every 16-bit array as bf16 patterns: the router
+    weight (N(0, 0.02) draws) and the experts' scales and biases."""
+    rng = rng_for(seed)
+    Wr = bf16_bits(rng.normal(0.0, 0.02, size=(D, E)))
+    gate_up = w4_matrix_bf16(rng, D, 2 * I, lead=(E,))
+    down = w4_matrix_bf16(rng, I, D, lead=(E,))
+    shared_gate_up = w4_matrix_bf16(rng, D, 2 * I)
+    shared_down = w4_matrix_bf16(rng, I, D)
+    return {"Wr": Wr, "gate_up": gate_up, "down": down,
+            "shared_gate_up": shared_gate_up, "shared_down": shared_down,
+            "D": D, "I": I, "E": E}
+
+
+def moe_tokens_bf16(seed: int, T: int, D: int = HIDDEN, E: int = NUM_EXPERTS,
+                    skewed: bool = False) -> dict:
+    """H bf16 patterns [T][D] of N(0, 1) draws and, if ``skewed``, the Zipf
+    logit bias (fp32)."""
+    rng = rng_for(seed)
+    H = bf16_bits(rng.standard_normal((T, D)))
+    bias = zipf_logit_bias(rng, E) if skewed else None
+    return {"H": H, "logit_bias": bias}
 
 
 # Default configurations of the benchmarked workload.

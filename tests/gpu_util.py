@@ -18,6 +18,15 @@ MAX_ABS_FRAC = 5e-3
 # 1.6e-2 * max|ref| (four times it).
 REL_L2_BF16 = 4e-3
 MAX_ABS_FRAC_BF16 = 1.6e-2
+# bf16 routed-expert layer (derived the same way): its output passes through
+# seven independent bf16 roundings the oracle does not share - the gate and
+# the up weights (both enter act = SiLU(gate) * up), act on each side (the
+# two round different pre-values), the down weights, ydown and the output -
+# each about 1.6e-3 RMS relative, so sqrt(7) * 1.6e-3 = 4.2e-3 RMS (measured
+# 4.0e-3 to 4.2e-3 for out).  Bars: rel-L2 <= 6e-3 and max-abs <= 2.4e-2 *
+# max|ref| (four times it), for act, ydown and out alike.
+REL_L2_BF16_MOE = 6e-3
+MAX_ABS_FRAC_BF16_MOE = 2.4e-2
 
 
 def dev():
@@ -65,10 +74,10 @@ def assert_close(gpu, ref, what="", rel_l2=REL_L2, max_abs_frac=MAX_ABS_FRAC):
     return rel, mabs / max(mref, 1e-30)
 
 
-def assert_close_bf16(gpu_bits, ref, what=""):
+def assert_close_bf16(gpu_bits, ref, what="", rel_l2=REL_L2_BF16, max_abs_frac=MAX_ABS_FRAC_BF16):
     """gpu_bits: bf16 patterns (uint16 / int16 array); ref: float64."""
     g = (np.asarray(gpu_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return assert_close(g, ref, what, REL_L2_BF16, MAX_ABS_FRAC_BF16)
+    return assert_close(g, ref, what, rel_l2, max_abs_frac)
 
 
 def say(*a):

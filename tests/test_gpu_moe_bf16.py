@@ -1,0 +1,105 @@
+"""GPU parity of the bf16 routed-expert layer (moe_route_bf16,
+moe_grouped_gemm_bf16, moe_combine_bf16) against the oracle's bf16 layer,
+with the bf16 layer tolerance derived in tests/gpu_util.py."""
+import numpy as np
+import pytest
+
+import bit_group_quantized_amd as ql
+import oracle
+import synth
+from tests.gpu_util import (MAX_ABS_FRAC_BF16_MOE, REL_L2_BF16_MOE, assert_close_bf16, host, say,
+                            t)
+
+pytestmark = pytest.mark.gpu
+
+
+def _w4_dev_bits(W):
+    return {"qweight": t(W["qweight"]), "scales": t(W["scales"]), "biases": t(W["biases"]),
+            "K": int(W["K"]), "N": int(W["N"])}
+
+
+def _dev_weights(w):
+    return {"Wr": t(w["Wr"]), "gate_up": _w4_dev_bits(w["gate_up"]), "down": _w4_dev_bits(w["down"]),
+            "shared_gate_up": _w4_dev_bits(w["shared_gate_up"]),
+            "shared_down": _w4_dev_bits(w["shared_down"])}
+
+
+def _bits(x):
+    import torch
+    return x.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _run(dw, H, bias, topk, T, shared=True):
+    route = ql.moe_route_bf16(H, dw["Wr"], bias, topk)
+    act = ql.moe_grouped_gemm_bf16(dw["gate_up"], dw["shared_gate_up"] if shared else None, H, T, topk,
+                                   ql.QL_OP_GATE_UP_SILU, route)
+    ydown = ql.moe_grouped_gemm_bf16(dw["down"], dw["shared_down"] if shared else None, act, T, topk,
+                                     ql.QL_OP_DOWN, route)
+    out = ql.moe_combine_bf16(ydown, route["gates"], route["pos"], T, topk, shared)
+    return route, act, ydown, out
+
+
+def _check(route, act, ydown, out, ref, T, topk):
+    """Routing exactly the oracle's (the cases are screened: no token's k-th
+    and (k+1)-th logits lie within 30 times the fp32 logit error), the
+    integer steps bit for bit, then act, ydown and out within the bf16 bar."""
+    assert np.array_equal(host(route["ids"]), ref["ids"])
+    assert np.abs(host(route["gates"]).astype(np.float64) - ref["gates"]).max() < 2e-5
+    assert np.array_equal(host(route["counts"]), ref["counts"])
+    assert np.array_equal(host(route["offsets"]), ref["offsets"])
+    assert np.array_equal(host(route["sorted_assign"]), ref["sorted_assign"])
+    assert np.array_equal(host(route["pos"]), ref["pos"])
+    bar = dict(rel_l2=REL_L2_BF16_MOE, max_abs_frac=MAX_ABS_FRAC_BF16_MOE)
+    assert_close_bf16(_bits(act), oracle.bf16_to_f64(ref["act"]), "act", **bar)
+    assert_close_bf16(_bits(ydown), ref["ydown"], "ydown", **bar)
+    return assert_close_bf16(_bits(out), ref["out"], "out", **bar)
+
+
+def test_moe_bf16_prefill_4096():
+    """The prefill workload in bf16: 4096 tokens, 256 experts + shared, Zipf
+    logit bias; token seed 4 (smallest k/k+1 logit gap 5.5e-5 against an
+    fp32 logit error of 1.4e-6)."""
+    import torch
+    say("moe bf16 prefill T=4096")
+    w = synth.moe_weights_bf16(0)
+    tok = synth.moe_tokens_bf16(4, 4096, skewed=True)
+    ref = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], 8)
+    dw = _dev_weights(w)
+    res = _run(dw, t(tok["H"]), t(tok["logit_bias"]), 8, 4096)
+    torch.cuda.synchronize()
+    rel, mx = _check(*res, ref, 4096, 8)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
+    (1, 2048, 512, 256, 8, 0, True),     # one token on the tiled path
+    (3, 512, 256, 16, 4, 1, True),
+    (16, 512, 128, 16, 4, 2, True),      # largest T of the one-block router
+    (300, 256, 128, 16, 4, 3, True),     # MFMA router, ragged tiles
+    (700, 512, 256, 64, 8, 7, True),
+    (200, 256, 64, 33, 5, 5, False),     # E % 8 != 0, no shared expert
+])
+def test_moe_bf16_shapes(T, D, I, E, topk, seed, shared):
+    import torch
+    say(f"moe bf16 T={T} D={D} I={I} E={E} topk={topk} shared={shared}")
+    w = synth.moe_weights_bf16(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens_bf16(seed + 70, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], topk, with_shared=shared)
+    srt = -np.sort(-ref["logits"], axis=1)
+    if topk < E:
+        assert (srt[:, topk - 1] - srt[:, topk]).min() > 5e-5, "case not screened"
+    dw = _dev_weights(w)
+    res = _run(dw, t(tok["H"]), t(tok["logit_bias"]), topk, T, shared)
+    torch.cuda.synchronize()
+    rel, mx = _check(*res, ref, T, topk)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_moe_bf16_down_combine_is_rejected():
+    w = synth.moe_weights_bf16(0, D=256, I=64, E=8)
+    dw = _dev_weights(w)
+    tok = synth.moe_tokens_bf16(1, 2, D=256, E=8)
+    route = ql.moe_route_bf16(t(tok["H"]), dw["Wr"], None, 2)
+    with pytest.raises(ql.QLError):
+        ql.moe_grouped_gemm_bf16(dw["down"], None, t(np.zeros((4, 64), np.uint16)), 2, 2,
+                                 ql.QL_OP_DOWN_COMBINE, route)

@@ -104,3 +104,62 @@ def test_one_hot_and_bruteforce():
         for n in range(N):
             ref = math.fsum(_dec(X[m, k]) * w_digit(n, k) for k in range(K))
             assert abs(Y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def _tiny_bf16(seed, T=5, D=64, I=64, E=6):
+    w = synth.moe_weights_bf16(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens_bf16(seed + 100, T, D=D, E=E, skewed=True)
+    return w, tok
+
+
+def _ffn_one_token_bf16(h_bits, gu, dn):
+    """One expert on one token, written from the definitions with a plain
+    loop over outputs (no matrix routine)."""
+    h = oracle.bf16_to_f64(h_bits)
+    Wgu = oracle.dequantize_bf16(gu["qweight"], gu["scales"], gu["biases"], gu["K"])
+    I = gu["N"] // 2
+    u = np.array([math.fsum(h * Wgu[n]) for n in range(2 * I)])
+    act = oracle.round_bf16(u[:I] / (1.0 + np.exp(-u[:I])) * u[I:])
+    Wdn = oracle.dequantize_bf16(dn["qweight"], dn["scales"], dn["biases"], dn["K"])
+    a = oracle.bf16_to_f64(act)
+    return np.array([math.fsum(a * Wdn[n]) for n in range(dn["N"])])
+
+
+def test_moe_layer_bf16_matches_per_token_bruteforce():
+    """Token by token: logits from the decoded bf16 inputs, the k best by a
+    sort, each chosen expert on that token alone, weighted, plus the shared
+    expert.  No histogram, scan or permutation."""
+    for seed, topk in [(0, 2), (1, 3), (2, 6)]:
+        w, tok = _tiny_bf16(seed)
+        res = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], topk=topk)
+        H = oracle.bf16_to_f64(tok["H"])
+        Wr = oracle.bf16_to_f64(w["Wr"])
+        for t in range(H.shape[0]):
+            L = np.array([math.fsum(H[t] * Wr[:, e]) for e in range(Wr.shape[1])])
+            L = L + tok["logit_bias"].astype(np.float64)
+            chosen = sorted(range(len(L)), key=lambda e: (-L[e], e))[:topk]
+            g = np.exp(L[chosen] - L[chosen].max())
+            g = g / g.sum()
+            assert res["ids"][t].tolist() == chosen
+            assert np.allclose(res["gates"][t], g, rtol=1e-12, atol=1e-15)
+            ref = _ffn_one_token_bf16(tok["H"][t], w["shared_gate_up"], w["shared_down"])
+            for gj, e in zip(g, chosen):
+                one = lambda W: {k: (v[e] if isinstance(v, np.ndarray) else v) for k, v in W.items()}
+                ref = ref + gj * _ffn_one_token_bf16(tok["H"][t], one(w["gate_up"]), one(w["down"]))
+            assert np.allclose(res["out"][t], ref, rtol=1e-9, atol=1e-9)
+
+
+def test_moe_layer_bf16_without_shared_and_identical_experts():
+    """Every routed expert equal to the shared one: with the shared expert
+    the output is twice one FFN, without it once (the gates sum to 1)."""
+    E = 5
+    w, tok = _tiny_bf16(3, T=4, E=E)
+    for key, skey in (("gate_up", "shared_gate_up"), ("down", "shared_down")):
+        for f in ("qweight", "scales", "biases"):
+            w[key][f] = np.repeat(w[skey][f][None], E, axis=0)
+    both = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], topk=3)
+    routed = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], topk=3, with_shared=False)
+    for t in range(4):
+        one = _ffn_one_token_bf16(tok["H"][t], w["shared_gate_up"], w["shared_down"])
+        assert np.allclose(both["out"][t], 2 * one, rtol=1e-9, atol=1e-9)
+        assert np.allclose(routed["out"][t], one, rtol=1e-9, atol=1e-9)

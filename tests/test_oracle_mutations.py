@@ -307,3 +307,42 @@ def test_codec_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(ocod, attr, mutant)
     monkeypatch.setattr(oracle, attr, mutant)
     assert _fails(CODEC_PINS)
+
+
+import oracle.bf16 as obf
+from tests import test_oracle_bf16 as tb
+
+BF16_MOE_PINS = [tb.test_moe_layer_bf16_matches_per_token_bruteforce,
+                 tb.test_moe_layer_bf16_without_shared_and_identical_experts]
+_ORIG_FFN_BF16 = obf.expert_ffn_bf16
+
+
+def _ffn_bf16_up_gate_swapped(X_bits, gate_up, down):
+    gu = dict(gate_up)
+    half = gate_up["N"] // 2
+    for f in ("qweight", "scales", "biases"):
+        gu[f] = np.concatenate([gate_up[f][..., half:, :], gate_up[f][..., :half, :]], axis=-2)
+    return _ORIG_FFN_BF16(X_bits, gu, down)
+
+
+def _ffn_bf16_no_act_rounding(X_bits, gate_up, down):
+    X = obf.bf16_to_f64(np.atleast_2d(np.asarray(X_bits, dtype=np.uint16)))
+    I = gate_up["N"] // 2
+    u = X @ obf.dequantize_bf16(gate_up["qweight"], gate_up["scales"], gate_up["biases"], gate_up["K"]).T
+    a = obf.silu(u[:, :I]) * u[:, I:]
+    ydown = a @ obf.dequantize_bf16(down["qweight"], down["scales"], down["biases"], down["K"]).T
+    return obf.round_bf16(a), ydown
+
+
+def _bf16_combine_no_shared(ydown, gates, pos, T, topk, has_shared):
+    return _ORIG_COMBINE(ydown, gates, pos, T, topk, False)
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("expert_ffn_bf16", _ffn_bf16_up_gate_swapped),
+    ("expert_ffn_bf16", _ffn_bf16_no_act_rounding),
+    ("combine", _bf16_combine_no_shared),
+])
+def test_bf16_moe_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(obf, attr, mutant)
+    assert _fails(BF16_MOE_PINS)

@@ -557,12 +557,36 @@ def bench_moe_decode(args, dev, w):
     torch.cuda.synchronize()
     ms = graph_time(layer, NG, 30)
     ms3 = graph_time(step3, NG, 30)
+    # The bf16 layer (moe_decode_bf16), same rotation of tokens and weights.
+    wb = synth.moe_weights_bf16(0)
+    as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else np.int32)).to(dev)
+    wd = lambda W: {"qweight": as_dev(W["qweight"]), "scales": as_dev(W["scales"]),
+                    "biases": as_dev(W["biases"]), "K": W["K"], "N": W["N"]}
+    bcopies = []
+    for c in range(2):
+        d = {k: wd(wb[k]) for k in ("gate_up", "down", "shared_gate_up", "shared_down")}
+        d["Wr"] = as_dev(wb["Wr"])
+        bcopies.append(d)
+    btoks = [as_dev(synth.moe_tokens_bf16(2000 + i, 1)["H"]) for i in range(32)]
+    bbuf = ql.alloc_decode_outputs(1, 256, 8, 2048, 512, dev)
+    bbuf["out"] = torch.empty((1, 2048), dtype=torch.bfloat16, device=dev)
+
+    def layer_bf16(i):
+        dw = bcopies[i % 2]
+        ql.moe_decode(btoks[i % len(btoks)], dw["Wr"], None, 8, dw["gate_up"], dw["down"],
+                      dw["shared_gate_up"], dw["shared_down"], out=bbuf, bf16=True)
+
+    for i in range(3):
+        layer_bf16(i)
+    torch.cuda.synchronize()
+    ms_bf = graph_time(layer_bf16, NG, 30)
     k = [graph_time(fn, NG, 30) for fn in (route, gate_up, down)]
     algo = 2048 * 256 * 2 + 9 * (w4_bytes(2048, 1024) + w4_bytes(512, 2048)) + 2 * 2048 * 2
     return {"tokens/s": 1e3 / ms, "us_per_token": ms * 1e3, "algorithmic_bytes": algo,
             "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "entry": "moe_decode (router partials; routing fused into gate/up; down + combine)",
             "three_call_us_per_token": ms3 * 1e3,
+            "bf16_us_per_token": ms_bf * 1e3,
             "three_call_stage_us": {"route": k[0] * 1e3, "gate_up_silu": k[1] * 1e3,
                                     "down_combine": k[2] * 1e3},
             "timing": "HIP graph of 16 decode steps, replayed" if USE_GRAPHS else "eager launches"}

@@ -94,6 +94,10 @@ _SIGS = {
                                   ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
                                   ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P,
                                   ctypes.c_size_t, _P, _P]),
+    "moe_decode_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
+                                       ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
+                                       ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P,
+                                       ctypes.c_size_t, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -416,19 +420,24 @@ def alloc_decode_outputs(T: int, E: int, topk: int, D: int, I: int, device) -> d
 
 
 def moe_decode(H, Wr, logit_bias, topk: int, gate_up: dict, down: dict, shared_gate_up=None,
-               shared_down=None, out: dict | None = None, stream=None) -> dict:
+               shared_down=None, out: dict | None = None, stream=None, bf16: bool = False) -> dict:
     """The routed-expert layer of T <= QL_DECODE_MAX_T tokens in three
-    launches; returns the dict of ids, gates, out and workspace."""
+    launches; returns the dict of ids, gates, out and workspace.  bf16=True
+    calls moe_decode_bf16 (every 16-bit array bf16; out is then bfloat16)."""
+    import torch
     T, D = H.shape
     E = Wr.shape[1]
     I = int(down["K"])
     if out is None:
         out = alloc_decode_outputs(T, E, topk, D, I, H.device)
+        if bf16:
+            out["out"] = torch.empty((T, D), dtype=torch.bfloat16, device=H.device)
     gu, dn = make_w4_experts(gate_up), make_w4_experts(down)
     sg = make_w4(shared_gate_up) if shared_gate_up is not None else None
     sd = make_w4(shared_down) if shared_down is not None else None
     ws = out["workspace"]
-    _check("moe_decode", lib().moe_decode(
+    name = "moe_decode_bf16" if bf16 else "moe_decode"
+    _check(name, getattr(lib(), name)(
         _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, ctypes.byref(gu), ctypes.byref(dn),
         ctypes.byref(sg) if sg is not None else None, ctypes.byref(sd) if sd is not None else None,
         _ptr(out["ids"]), _ptr(out["gates"]), _ptr(ws), ws.numel(), _ptr(out["out"]),

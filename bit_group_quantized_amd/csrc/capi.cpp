@@ -355,10 +355,11 @@ size_t moe_decode_logits_offset(int32_t T, int32_t E, int32_t topk) {
     return ql::moe_decode_layout(T, E, topk, 64).logits;
 }
 
-int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
-               int32_t E, int32_t topk, const ql_w4_experts* gate_up, const ql_w4_experts* down,
-               const ql_w4* shared_gate_up, const ql_w4* shared_down, int32_t* topk_ids,
-               float* topk_gates, void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                       int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
+                       const ql_w4_experts* down, const ql_w4* shared_gate_up,
+                       const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
+                       void* workspace, size_t ws_bytes, uint16_t* out, void* stream, bool bf16) {
     if (!gate_up || !down) return QL_ERR_INVALID_ARG;
     if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
     if (T < 0 || E <= 0 || topk <= 0 || topk > E || D <= 0) return QL_ERR_INVALID_ARG;
@@ -399,8 +400,25 @@ int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, i
                      shared_down ? shared_down->qweight : nullptr,
                      shared_down ? shared_down->scales : nullptr,
                      shared_down ? shared_down->biases : nullptr,
-                     topk_ids, topk_gates, static_cast<unsigned char*>(workspace), out};
+                     topk_ids, topk_gates, static_cast<unsigned char*>(workspace), out, bf16};
     return ql::launch_moe_decode(a, as_stream(stream));
+}
+
+int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
+               int32_t E, int32_t topk, const ql_w4_experts* gate_up, const ql_w4_experts* down,
+               const ql_w4* shared_gate_up, const ql_w4* shared_down, int32_t* topk_ids,
+               float* topk_gates, void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+    return decode_impl(H, Wr, logit_bias, T, D, E, topk, gate_up, down, shared_gate_up, shared_down,
+                       topk_ids, topk_gates, workspace, ws_bytes, out, stream, false);
+}
+
+int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                    int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
+                    const ql_w4_experts* down, const ql_w4* shared_gate_up,
+                    const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
+                    void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+    return decode_impl(H, Wr, logit_bias, T, D, E, topk, gate_up, down, shared_gate_up, shared_down,
+                       topk_ids, topk_gates, workspace, ws_bytes, out, stream, true);
 }
 
 static int combine_impl(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,

@@ -424,8 +424,10 @@ __device__ __forceinline__ void rows_load_x(const uint16_t* __restrict__ X, int 
 }
 
 // One wave's outputs of row r: column block `xblock` of the expert matrix
-// (wq, ws, wb) applied to the activations xr.
-template <int TPR, int V, int R, int MODE>
+// (wq, ws, wb) applied to the activations xr.  BF16: activations, scales,
+// biases and outputs are bf16 patterns (codes enter v_dot2_f32_bf16 exactly,
+// as in the bf16 GEMV).
+template <int TPR, int V, int R, int MODE, bool BF16 = false>
 __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_t* __restrict__ wq,
                                           const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wb,
                                           uint16_t* __restrict__ Y, int r, int xblock, int K, int N,
@@ -454,44 +456,76 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    XPairs xp[V][4];
-    float xc[V], xs[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        xc[v] = 0.f;
-        xs[v] = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            xp[v][w] = make_xpairs(xr[v][w]);
-            float c_, s_;
-            xpairs_consts(xp[v][w], xr[v][w], c_, s_);
-            xc[v] += c_;
-            xs[v] += s_;
-        }
-    }
     float acc[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        acc[q] = 0.f;
+    if constexpr (BF16) {
+        XPairsBf xp[V][4];
+        float xs[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-            dot_word(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
-            dot_word(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
-            dot_word(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
-            dot_word(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
-            acc[q] += h2f(s[q][v]) * (((d0 + d2) + (d1 + d3)) - xc[v]) + h2f(b[q][v]) * xs[v];
+            xs[v] = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                xp[v][w] = make_xpairs_bf(xr[v][w]);
+                xs[v] += xsum_bf(xp[v][w]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            acc[q] = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+                dot_word_bf(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
+                dot_word_bf(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
+                dot_word_bf(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
+                dot_word_bf(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
+                const float d = (d0 + d2) + (d1 + d3);
+                acc[q] += bf2f(s[q][v]) * (d - 128.0f * xs[v]) + bf2f(b[q][v]) * xs[v];
+            }
+        }
+    } else {
+        XPairs xp[V][4];
+        float xc[V], xs[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            xc[v] = 0.f;
+            xs[v] = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                xp[v][w] = make_xpairs(xr[v][w]);
+                float c_, s_;
+                xpairs_consts(xp[v][w], xr[v][w], c_, s_);
+                xc[v] += c_;
+                xs[v] += s_;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            acc[q] = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+                dot_word(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
+                dot_word(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
+                dot_word(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
+                dot_word(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
+                acc[q] += h2f(s[q][v]) * (((d0 + d2) + (d1 + d3)) - xc[v]) + h2f(b[q][v]) * xs[v];
+            }
         }
     }
+    auto out16 = [](float v) -> uint16_t {
+        if constexpr (BF16) return f2bf(v);
+        else return f2h(v);
+    };
     int sel;
     const float tot = reduce_rows<TPR, R>(acc, lr, sel);
     const bool writer = (lr & (TPR / R - 1)) == 0;
     if constexpr (MODE == 0) {
         const float up = __shfl_xor(tot, TPR / 2, 64);  // row sel + R/2 of the same team
         if (writer && sel < OUT && n0 + sel < Nout)
-            Y[(size_t)r * Nout + n0 + sel] = f2h(silu(tot) * up);
+            Y[(size_t)r * Nout + n0 + sel] = out16(silu(tot) * up);
     } else {
-        if (writer && n0 + sel < Nout) Y[(size_t)r * Nout + n0 + sel] = f2h(tot);
+        if (writer && n0 + sel < Nout) Y[(size_t)r * Nout + n0 + sel] = out16(tot);
     }
 }
 
@@ -537,7 +571,7 @@ moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
 // weights; its activation loads are issued before the routing.  Blocks with
 // x = 0 also write the token's ids, gates, logits and the (expert, row) of
 // their assignment for the down projection.
-template <int TPR, int V, int R, int EPL>
+template <int TPR, int V, int R, int EPL, bool BF16>
 __global__ void __launch_bounds__(256)
 moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __restrict__ bias,
                           const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
@@ -591,7 +625,7 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
                 for (int i = threadIdx.x; i < E; i += blockDim.x) logits_out[(size_t)t * E + i] = s_lg[i];
         }
     }
-    rows_body<TPR, V, R, 0>(xr, wq, ws, wb, Y, r, blockIdx.x * 4 + wave, K, N, lane);
+    rows_body<TPR, V, R, 0, BF16>(xr, wq, ws, wb, Y, r, blockIdx.x * 4 + wave, K, N, lane);
 }
 
 // Decode down projection fused with the gate-weighted sum over the token's
@@ -604,7 +638,7 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
 // pre-paired into LDS while the codes are in flight.  Sums, in a fixed
 // order: per lane over the wave's rows in ascending j, across the lanes of
 // the row team, then the four wave sums in wave order.
-template <int TPR, int V, int R, int JC>
+template <int TPR, int V, int R, int JC, bool BF16 = false>
 __global__ void __launch_bounds__(256)
 moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                         const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
@@ -664,12 +698,18 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
         float cc = 0.f, xx = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const XPairs xp = make_xpairs(xw[w]);
-            float c_, s_;
-            xpairs_consts(xp, xw[w], c_, s_);
-            cc += c_;
-            xx += s_;
-            s_xp[((size_t)j * CH + c) * 4 + w] = xp;
+            if constexpr (BF16) {
+                const XPairsBf xp = make_xpairs_bf(xw[w]);
+                xx += xsum_bf(xp);
+                s_xp[((size_t)j * CH + c) * 4 + w] = __builtin_bit_cast(XPairs, xp);
+            } else {
+                const XPairs xp = make_xpairs(xw[w]);
+                float c_, s_;
+                xpairs_consts(xp, xw[w], c_, s_);
+                cc += c_;
+                xx += s_;
+                s_xp[((size_t)j * CH + c) * 4 + w] = xp;
+            }
         }
         s_c[j * CH + c] = cc;
         s_xs[j * CH + c] = xx;
@@ -722,12 +762,21 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
 #pragma unroll
                 for (int q = 0; q < R; ++q) {
                     float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-                    dot_word(cw[jj][q][v].x, xp[0], d0, d1, d2, d3);
-                    dot_word(cw[jj][q][v].y, xp[1], d0, d1, d2, d3);
-                    dot_word(cw[jj][q][v].z, xp[2], d0, d1, d2, d3);
-                    dot_word(cw[jj][q][v].w, xp[3], d0, d1, d2, d3);
-                    acc[q] += g * (h2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - xc) +
-                                   h2f(b[jj][q][v]) * xs);
+                    if constexpr (BF16) {
+                        dot_word_bf(cw[jj][q][v].x, __builtin_bit_cast(XPairsBf, xp[0]), d0, d1, d2, d3);
+                        dot_word_bf(cw[jj][q][v].y, __builtin_bit_cast(XPairsBf, xp[1]), d0, d1, d2, d3);
+                        dot_word_bf(cw[jj][q][v].z, __builtin_bit_cast(XPairsBf, xp[2]), d0, d1, d2, d3);
+                        dot_word_bf(cw[jj][q][v].w, __builtin_bit_cast(XPairsBf, xp[3]), d0, d1, d2, d3);
+                        acc[q] += g * (bf2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - 128.0f * xs) +
+                                       bf2f(b[jj][q][v]) * xs);
+                    } else {
+                        dot_word(cw[jj][q][v].x, xp[0], d0, d1, d2, d3);
+                        dot_word(cw[jj][q][v].y, xp[1], d0, d1, d2, d3);
+                        dot_word(cw[jj][q][v].z, xp[2], d0, d1, d2, d3);
+                        dot_word(cw[jj][q][v].w, xp[3], d0, d1, d2, d3);
+                        acc[q] += g * (h2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - xc) +
+                                       h2f(b[jj][q][v]) * xs);
+                    }
                 }
             }
         }
@@ -753,7 +802,7 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
         const int n = blockIdx.x * TEAMS * R + threadIdx.x;
         const float y = ((s_red[0][threadIdx.x] + s_red[1][threadIdx.x]) + s_red[2][threadIdx.x]) +
                         s_red[3][threadIdx.x];
-        if (n < N) Y[(size_t)t * N + n] = f2h(y);
+        if (n < N) Y[(size_t)t * N + n] = BF16 ? f2bf(y) : f2h(y);
     }
 }
 
@@ -778,7 +827,7 @@ inline int pow2_divisor(int G) {
     return t;
 }
 
-template <int TPR, int V>
+template <int TPR, int V, bool BF16 = false>
 void launch_down_combine_t(const GroupedArgs& a, const int2* assign_info, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
     constexpr int R = (TPR < 2) ? TPR : 2;
@@ -787,7 +836,7 @@ void launch_down_combine_t(const GroupedArgs& a, const int2* assign_info, hipStr
     const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
     dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
     // four waves; each takes the rows j = wave, wave + 4, ... (3 per round)
-    hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3>), grid, dim3(256), smem, st, a.qw, a.sc,
+    hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3, BF16>), grid, dim3(256), smem, st, a.qw, a.sc,
                        a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates, assign_info, a.Y, a.K, a.N, a.E, a.T,
                        a.topk, has_shared);
 }
@@ -959,7 +1008,7 @@ bool moe_rows_supported(int K) {
 
 namespace {
 
-template <int TPR, int V, int EPL>
+template <int TPR, int V, int EPL, bool BF16>
 void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
     constexpr int R = (TPR < 8) ? TPR : 8;
@@ -968,7 +1017,7 @@ void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStre
     const int has_shared = a.sgu_qw != nullptr;
     const int rows = a.T * a.topk + (has_shared ? a.T : 0);
     dim3 grid((a.I + COLS - 1) / COLS, rows);
-    hipLaunchKernelGGL((moe_decode_gate_up_kernel<TPR, V, R, EPL>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((moe_decode_gate_up_kernel<TPR, V, R, EPL, BF16>), grid, dim3(256), 0, st,
                        reinterpret_cast<const float*>(a.ws + L.partials), a.bias, a.gu_qw, a.gu_sc,
                        a.gu_bi, a.sgu_qw, a.sgu_sc, a.sgu_bi, a.H,
                        reinterpret_cast<uint16_t*>(a.ws + L.act), a.D, 2 * a.I, a.E, a.T, a.topk, a.ids,
@@ -978,8 +1027,13 @@ void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStre
 
 template <int TPR, int V>
 void launch_decode_gate_up_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
-    if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4>(a, L, st);
-    else launch_decode_gate_up_t<TPR, V, 16>(a, L, st);
+    if (a.bf16) {
+        if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4, true>(a, L, st);
+        else launch_decode_gate_up_t<TPR, V, 16, true>(a, L, st);
+    } else {
+        if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4, false>(a, L, st);
+        else launch_decode_gate_up_t<TPR, V, 16, false>(a, L, st);
+    }
 }
 
 template <int TPR, int V>
@@ -987,7 +1041,9 @@ void launch_decode_down_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_
     GroupedArgs g{a.dn_qw, a.dn_sc, a.dn_bi, a.sdn_qw, a.sdn_sc, a.sdn_bi,
                   reinterpret_cast<const uint16_t*>(a.ws + L.act), nullptr, nullptr, a.gates,
                   nullptr, a.ws, a.out, a.I, a.D, a.E, a.T, a.topk, QL_OP_DOWN_COMBINE};
-    launch_down_combine_t<TPR, V>(g, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
+    const int2* info = reinterpret_cast<const int2*>(a.ws + L.assign_info);
+    if (a.bf16) launch_down_combine_t<TPR, V, true>(g, info, st);
+    else launch_down_combine_t<TPR, V, false>(g, info, st);
 }
 
 }  // namespace
@@ -1012,7 +1068,7 @@ DecodeLayout moe_decode_layout(int T, int E, int topk, int I) {
 int launch_moe_decode(const DecodeArgs& a, hipStream_t st) {
     const DecodeLayout L = moe_decode_layout(a.T, a.E, a.topk, a.I);
     int rc = launch_router_partials_small(a.H, a.Wr, reinterpret_cast<float*>(a.ws + L.partials), a.T,
-                                          a.D, a.E, st);
+                                          a.D, a.E, st, a.bf16);
     if (rc != QL_OK) return rc;
     switch (a.D) {
         case 64: launch_decode_gate_up_v<2, 1>(a, L, st); break;

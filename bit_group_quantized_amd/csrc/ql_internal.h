@@ -183,6 +183,7 @@ struct DecodeArgs {
     float* gates;
     unsigned char* ws;
     uint16_t* out;
+    bool bf16 = false;  // H, Wr, scales, biases, act and out hold bf16 patterns
 };
 int launch_moe_decode(const DecodeArgs& a, hipStream_t st);
 

@@ -471,6 +471,19 @@ int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
                const ql_w4* shared_gate_up, const ql_w4* shared_down,
                int32_t* topk_ids, float* topk_gates,
                void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+/*
+ * moe_decode_bf16 - moe_decode with bf16 H, Wr, expert scales and biases and
+ * out (the bf16 layer of moe_route_bf16 and friends): codes enter the row
+ * dot products exactly (v_dot2_f32_bf16 against bf16 128 + q), scale and
+ * bias are applied in fp32, act is rounded to bf16.  Same limits, workspace
+ * and errors as moe_decode.
+ */
+int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+                    int32_t T, int32_t D, int32_t E, int32_t topk,
+                    const ql_w4_experts* gate_up, const ql_w4_experts* down,
+                    const ql_w4* shared_gate_up, const ql_w4* shared_down,
+                    int32_t* topk_ids, float* topk_gates,
+                    void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -103,3 +103,33 @@ def test_moe_bf16_down_combine_is_rejected():
     with pytest.raises(ql.QLError):
         ql.moe_grouped_gemm_bf16(dw["down"], None, t(np.zeros((4, 64), np.uint16)), 2, 2,
                                  ql.QL_OP_DOWN_COMBINE, route)
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
+    (1, 2048, 512, 256, 8, 0, True),     # the decode shape
+    (1, 2048, 512, 256, 8, 1, True),
+    (4, 2048, 512, 256, 8, 2, True),
+    (3, 512, 256, 16, 1, 3, True),
+    (2, 512, 128, 1000, 32, 4, True),    # 16 keys per lane in the top-k
+    (3, 256, 64, 33, 5, 5, False),       # scalar router partials, no shared expert
+])
+def test_moe_decode_bf16(T, D, I, E, topk, seed, shared):
+    """moe_decode_bf16 (routing fused into the bf16 gate/up rows) against
+    the oracle's bf16 layer."""
+    import torch
+    say(f"moe_decode_bf16 T={T} D={D} I={I} E={E} topk={topk} shared={shared}")
+    w = synth.moe_weights_bf16(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens_bf16(seed + 80, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer_bf16(tok["H"], w, tok["logit_bias"], topk, with_shared=shared)
+    srt = -np.sort(-ref["logits"], axis=1)
+    assert (srt[:, topk - 1] - srt[:, topk]).min() > 5e-5, "case not screened"
+    dw = _dev_weights(w)
+    res = ql.moe_decode(t(tok["H"]), dw["Wr"], t(tok["logit_bias"]), topk, dw["gate_up"], dw["down"],
+                        dw["shared_gate_up"] if shared else None, dw["shared_down"] if shared else None,
+                        bf16=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["ids"]), ref["ids"])
+    assert np.abs(host(res["gates"]).astype(np.float64) - ref["gates"]).max() < 2e-5
+    rel, mx = assert_close_bf16(_bits(res["out"]), ref["out"], "out", rel_l2=REL_L2_BF16_MOE,
+                                max_abs_frac=MAX_ABS_FRAC_BF16_MOE)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")

@@ -458,7 +458,8 @@ def bench_codecs(args, dev):
     """The second weight codecs on the headline decode shapes: FP8-E4M3 (1
     byte per weight + an fp16 scale per 64) and NVFP4 (half a byte + an E4M3
     scale per 16) GEMVs at K = 2048, N = 8192 and 151552, rotated weight
-    copies as in the headline; bytes = codes + scales + x + y."""
+    copies as in the headline; bytes = codes + scales + x + y.  Then the FP8
+    GEMM (fp16 MFMA on the staged weights) on the prefill shape."""
     import torch
     import bit_group_quantized_amd as ql
     import synth
@@ -501,6 +502,20 @@ def bench_codecs(args, dev):
                       "step_bytes": step_bytes}
         del Ws, mats
         torch.cuda.empty_cache()
+    # FP8 weights on the prefill GEMM shape (K 2048, N 8192), M = 4096 and 16384.
+    rng = synth.rng_for(3)
+    W = synth.fp8_matrix(rng, K, 8192)
+    Wd = {"codes": torch.from_numpy(W["codes"]).to(dev), "scales": torch.from_numpy(W["scales"]).to(dev),
+          "K": K, "N": 8192}
+    out["fp8_gemm"] = {}
+    for M in (4096, 16384):
+        X = torch.from_numpy(synth.activations(rng, M, K)).to(dev)
+        Y = torch.empty((M, 8192), dtype=torch.float16, device=dev)
+        ms = timed_steps(lambda i: ql.qlinear_gemm_fp8(Wd, X, Y), 20 if M == 4096 else 6, 3,
+                         settle_s=SETTLE_S)
+        tf = 2.0 * M * K * 8192 / (ms * 1e-3) / 1e12
+        out["fp8_gemm"][f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf,
+                                      "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
     return out
 
 

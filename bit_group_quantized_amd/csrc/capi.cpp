@@ -181,6 +181,19 @@ int qlinear_gemv_fp8(const ql_fp8* W, const uint16_t* x, uint16_t* y, void* stre
     return ql::launch_gemv_fp8(a, as_stream(stream));
 }
 
+int qlinear_gemm_fp8(const ql_fp8* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
+    if (!W || W->N < 0 || W->K < 0 || M < 0) return QL_ERR_INVALID_ARG;
+    if (W->K == 0 || W->K % QL_GROUP_SIZE != 0 || W->K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N == 0 || M == 0) return QL_OK;
+    if (M > (int64_t)0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!W->codes || !W->scales || !X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(W->codes, 16) || !aligned(W->scales, 2) || !aligned(X, 16) || !aligned(Y, 2))
+        return QL_ERR_MISALIGNED;
+    ql::GemmArgs a{reinterpret_cast<const uint32_t*>(W->codes), W->scales, nullptr, X, Y, M, W->K,
+                   W->N};
+    return ql::launch_gemm_fp8(a, as_stream(stream));
+}
+
 int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* stream) {
     if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
     if (!ql::gemv_nvfp4_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;

@@ -12,25 +12,12 @@
 // lane 16-byte chunks at a fixed K position, R consecutive rows per team;
 // every load of a lane is issued before any arithmetic.
 #include "ql_device.h"
+#include "ql_fp8.h"
 #include "ql_internal.h"
 
 namespace ql {
 
 namespace {
-
-// Two E4M3 codes -> fp16 pair holding e4m3 * 2**-8 each, exactly: the code
-// bits seeeemmm go to fp16 bits s.0eeee.mmm0000000 (the exponent bias 15 of
-// fp16 against 7 of E4M3 is the 2**-8; E4M3 subnormals land on fp16
-// subnormals).  `t` holds the two codes in bits 15:8 and 31:24.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t t) {
-    return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
-}
-
-// E4M3 code -> float, exactly (via the fp16 pattern above).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t h = ((b & 0x80u) << 8) | ((b & 0x7Fu) << 7);
-    return h2f((uint16_t)h) * 256.0f;
-}
 
 template <int TPR, int V, int R>
 __global__ void __launch_bounds__(256)

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "ql_device.h"
+#include "ql_fp8.h"
 #include "ql_internal.h"
 
 namespace ql {
@@ -127,7 +128,10 @@ struct Job {
 // DT: 0 = fp16 activations, scales, biases, outputs and MFMA operands;
 // 1 = bf16 throughout (the router's weight is then bf16 too; its logits
 // stay fp32 partials in both cases).
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
+// WF: weight format of the dense GEMM: 0 = w4 (codes, scale, bias);
+// 1 = FP8-E4M3 codes [N][K] (bytes, through p.qw) with an fp16 scale per 64
+// along K and no bias, staged as fp16(e4m3 * scale), one rounding.
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
     constexpr int BM = TL::BM, BN = TL::BN;
@@ -201,7 +205,8 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     // Two register sets of staged global data: the loads of step i + 2 are
     // issued while step i + 1 (loaded one step earlier) is dequantized into
     // LDS and step i runs on the matrix cores.
-    constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : TL::WPT / 4;
+    static_assert(WF == 0 || (MODE == MODE_DENSE && DT == 0), "FP8 weights: fp16 dense GEMM");
+    constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : (WF == 1) ? TL::WPT / 2 : TL::WPT / 4;
     constexpr int HREG = (MODE == MODE_ROUTER) ? 8 : 1;
     u32x4 areg[2][TL::A_LOADS];
     u32x4 breg[2][BREG];
@@ -222,6 +227,13 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
             const int col = min(n0 + 8 * nb, p.N - 8);
 #pragma unroll
             for (int r = 0; r < 8; ++r) hreg[S][r] = ld_u32x4(p.Bh + (size_t)(k0 + 8 * kb + r) * p.N + col);
+        } else if constexpr (WF == 1) {
+            // this thread's WPT * 8 codes of the column's 64 in this step
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(wq) + (size_t)bcol * K + k0 +
+                                 bpart * TL::WPT * 8;
+#pragma unroll
+            for (int i = 0; i < BREG; ++i) breg[S][i] = ld_u32x4(src + 16 * i);
+            sreg[S] = ws[(size_t)bcol * G + ks];
         } else {
             const uint32_t* src = wq + (size_t)bcol * wpr + ks * 8 + bpart * TL::WPT;
 #pragma unroll
@@ -254,6 +266,27 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                 o.z = __builtin_amdgcn_perm(hreg[S][5][j >> 1], hreg[S][4][j >> 1], sel);
                 o.w = __builtin_amdgcn_perm(hreg[S][7][j >> 1], hreg[S][6][j >> 1], sel);
                 *reinterpret_cast<u32x4*>(b_dst + (8 * nb + j) * kLdk + 8 * kb) = o;
+            }
+        } else if constexpr (WF == 1) {
+            // (e4m3 * 2**-8) * (scale * 2**8) in fp16: both factors exact, so
+            // the product is fp16(e4m3 * scale) with one rounding.
+            const f16 s256 = __builtin_bit_cast(f16, sreg[S]) * (f16)256.0f;
+            const f16x2 s2 = {s256, s256};
+            constexpr int W = TL::WPT;  // groups of 8 codes of this thread per step
+#pragma unroll
+            for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
+                const uint32_t c0 = breg[S][(2 * w) >> 2][(2 * w) & 3];
+                const uint32_t c1 = breg[S][(2 * w + 1) >> 2][(2 * w + 1) & 3];
+                uint32_t q[4];
+                e4m3x4_to_f16(c0, q[0], q[1]);
+                e4m3x4_to_f16(c1, q[2], q[3]);
+                u32x4 o;
+                o.x = as_u32(as_f16x2(q[0]) * s2);
+                o.y = as_u32(as_f16x2(q[1]) * s2);
+                o.z = as_u32(as_f16x2(q[2]) * s2);
+                o.w = as_u32(as_f16x2(q[3]) * s2);
+                const int word = bpart * W + w;  // 0..7 within the group
+                *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = o;
             }
         } else if constexpr (DT == 1) {
             const float sf = bf2f(sreg[S]), bf = bf2f(bireg[S]);
@@ -603,7 +636,7 @@ gemm_ws_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
 }
 
 // Dense prefill GEMM and the router GEMM.
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT>
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT, int WF = 0>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_w4_kernel(const KParams p) {
     using TL = Tile<WM, WN, WGM, WGN>;
@@ -638,7 +671,7 @@ gemm_w4_kernel(const KParams p) {
         job.kz = blockIdx.z;
     }
     job.rows_valid = (int)min<int64_t>(BM, p.M - job.out_row0);
-    gemm_tile<WM, WN, WGM, WGN, MODE, DT>(p, job, lds);
+    gemm_tile<WM, WN, WGM, WGN, MODE, DT, WF>(p, job, lds);
 }
 
 // Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
@@ -713,21 +746,21 @@ gemm_w4_grouped_kernel(const KParams p) {
         gemm_tile<2, 2, 2, 4, MODE, DT>(p, job, lds);
 }
 
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0>
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
 int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
     using TL = Tile<WM, WN, WGM, WGN>;
     static std::atomic<uint32_t> lds_set{0};
-    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>,
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF>,
                                            TL::LDS_BYTES, lds_set))
         return rc;
-    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT>), grid, dim3(TL::NT), TL::LDS_BYTES, st,
-                       p);
+    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF>), grid, dim3(TL::NT), TL::LDS_BYTES,
+                       st, p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
 }  // namespace
 
-template <int DT>
+template <int DT, int WF = 0>
 int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
     KParams p{};
     p.A = a.X;
@@ -758,7 +791,7 @@ int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
     do {                                                                           \
         using TL = Tile<A, B, C, D>;                                               \
         if (!grid_for(TL::BM, TL::BN, grid)) return QL_ERR_UNSUPPORTED_SHAPE;      \
-        return launch_t<A, B, C, D, MODE_DENSE, DT>(p, grid, st);                  \
+        return launch_t<A, B, C, D, MODE_DENSE, DT, WF>(p, grid, st);              \
     } while (0)
     if (t128 > 512) QL_DENSE(4, 2, 2, 4);  // 256 x 256, 8 waves of 128 x 64
     if (t128 > 256) QL_DENSE(2, 2, 2, 4);  // 128 x 256, 8 waves of 64 x 64
@@ -770,6 +803,8 @@ int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
 int launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0>(a, st); }
 
 int launch_gemm_bf16(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<1>(a, st); }
+
+int launch_gemm_fp8(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0, 1>(a, st); }
 
 bool gemm_ws_supported(int K) { return K == 512 || K == 1024 || K == 2048; }
 

@@ -80,6 +80,9 @@ struct GemmArgs {
 int launch_gemm(const GemmArgs& a, hipStream_t st);
 // bf16 activations, scales, biases and outputs (same tile table).
 int launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
+// FP8-E4M3 weights: qweight points at the uint8 codes [N][K], scales fp16
+// [N][K/64], biases unused.
+int launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
 bool gemm_ws_supported(int K);                          // few-row GEMM shapes
 int launch_gemm_ws(const GemmArgs& a, hipStream_t st);  // few-row GEMM (weight-stationary)
 

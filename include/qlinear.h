@@ -227,6 +227,21 @@ int qlinear_gemv_fp8(const ql_fp8* W, const uint16_t* x, uint16_t* y, void* stre
 int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* stream);
 
 /*
+ * qlinear_gemm_fp8 - Y fp16 [M][N] = X fp16 [M][K] . W for FP8-E4M3 weights,
+ * the prefill counterpart of qlinear_gemv_fp8 ([PPLX] dequantization section:
+ * small weight tiles dequantized into on-chip memory for the matrix path).
+ * The MFMA tiles of qlinear_gemm (same shape table, same row invariance:
+ * row m's bits do not depend on M) with each staged weight
+ * fp16(e4m3(code) * scale), one rounding (exact bit moves give e4m3 * 2^-8 and
+ * scale * 2^8 in fp16; their fp16 product is the rounded weight; scales must
+ * stay below 256), fp32 accumulation, fp16 output.
+ * Limits: K a positive multiple of 64, K <= QL_MAX_K.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (codes and X 16-byte,
+ * scales and Y 2-byte aligned), HIP.
+ */
+int qlinear_gemm_fp8(const ql_fp8* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
  * qlinear_gemv_rmsnorm - y = fp16(rmsnorm(x)) . dequant(W): a decode
  * projection with its normalization fused in front ([PPLX] "减少中间状态和流量":
  * the decode chains keep intermediates in registers, normalization among

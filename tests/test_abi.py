@@ -287,3 +287,21 @@ def test_moe_decode_validation(L):
     assert call(wsb=16) == WORKSPACE
     assert call(ws=A16 + 16) == MISALIGNED
     assert call(T=0) == OK
+
+
+def test_gemm_fp8_validation(L):
+    f = L.qlinear_gemm_fp8
+
+    def call(K=2048, N=64, M=8, codes=A16, X=A16):
+        w = ql.ql_fp8(codes, A16, K, N)
+        return f(ctypes.byref(w), X, M, A16, None)
+
+    assert call(K=100) == SHAPE
+    assert call(K=65536) == SHAPE
+    assert call(M=-1) == INVALID
+    assert call(codes=None) == INVALID
+    assert call(codes=A16 + 8) == MISALIGNED
+    assert call(X=A16 + 2) == MISALIGNED
+    assert call(M=0) == OK
+    assert call(N=0) == OK
+    assert f(None, A16, 8, A16, None) == INVALID

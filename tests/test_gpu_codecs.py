@@ -101,3 +101,63 @@ def test_codecs_integer_case_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(y8.view(np.uint16), ref8.view(np.uint16))
     assert np.array_equal(y4.view(np.uint16), ref4.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,seed", [
+    (1, 2048, 512, 0), (7, 512, 200, 1), (256, 2048, 8192, 2), (300, 2048, 1000, 3),
+    (129, 64, 257, 4), (1024, 1024, 640, 5), (2048, 512, 384, 6), (2500, 192, 300, 7),
+    (700, 1024, 3000, 8), (2100, 256, 4100, 9), (130, 32768, 70, 10),
+])
+def test_gemm_fp8_matches_oracle(M, K, N, seed):
+    """FP8 weights on the MFMA tiles: ragged M and N in every tile class,
+    the largest K."""
+    import torch
+    say(f"gemm_fp8 M={M} K={K} N={N} seed={seed}")
+    rng = synth.rng_for(seed)
+    X = synth.activations(rng, M, K)
+    W = synth.fp8_matrix(rng, K, N)
+    ref = oracle.linear_fp8(X, W)
+    Y = ql.qlinear_gemm_fp8(fp8_dev(W), t(X))
+    torch.cuda.synchronize()
+    rel, mx = assert_close(host(Y).astype(np.float64), ref, f"gemm_fp8 M={M} K={K} N={N}")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_gemm_fp8_prefill_sampled_rows_and_row_invariance():
+    """The prefill shape (M = 4096, K = 2048, N = 8192): 64 sampled rows
+    against the oracle, and every row's bits equal to the same row computed
+    with M = 1 and M = 256 (no split over K, the same K order)."""
+    import torch
+    M, K, N = 4096, 2048, 8192
+    rng = synth.rng_for(20)
+    X = synth.activations(rng, M, K)
+    W = synth.fp8_matrix(rng, K, N)
+    Wd, Xd = fp8_dev(W), t(X)
+    Y = host(ql.qlinear_gemm_fp8(Wd, Xd))
+    rows = np.sort(synth.rng_for(21).choice(M, 64, replace=False))
+    ref = oracle.linear_fp8(X[rows], W)
+    assert_close(Y[rows].astype(np.float64), ref, "gemm_fp8 sampled rows")
+    for m in (0, 255, 4095):
+        for MM in (1, 256):
+            lo = min(m, M - MM)
+            part = host(ql.qlinear_gemm_fp8(Wd, Xd[lo:lo + MM].contiguous()))
+            assert np.array_equal(part[m - lo].view(np.uint16), Y[m].view(np.uint16)), (m, MM)
+    torch.cuda.synchronize()
+
+
+def test_gemm_fp8_integer_case_bit_exact():
+    """Codes of small integers (E4M3 exact), scale 1, integer activations:
+    every product and fp32 sum is exact, so the fp16 output equals the
+    oracle's rounded value bit for bit."""
+    import torch
+    M, K, N = 300, 512, 260
+    rng = synth.rng_for(30)
+    # E4M3 codes of -4 .. 4: 0x00 (0), 0x38 (1), 0x40 (2), 0x44 (3), 0x48 (4), sign bit 0x80
+    mags = np.array([0x00, 0x38, 0x40, 0x44, 0x48], dtype=np.uint8)
+    codes = mags[rng.integers(0, 5, size=(N, K))] | (rng.integers(0, 2, size=(N, K)) * 0x80).astype(np.uint8)
+    W = {"codes": codes.astype(np.uint8), "scales": np.ones((N, K // 64), dtype=np.float16), "K": K, "N": N}
+    X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    ref = oracle.linear_fp8(X, W)
+    Y = host(ql.qlinear_gemm_fp8(fp8_dev(W), t(X)))
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint16), ref.astype(np.float16).view(np.uint16))

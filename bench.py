@@ -459,7 +459,7 @@ def bench_codecs(args, dev):
     byte per weight + an fp16 scale per 64) and NVFP4 (half a byte + an E4M3
     scale per 16) GEMVs at K = 2048, N = 8192 and 151552, rotated weight
     copies as in the headline; bytes = codes + scales + x + y.  Then the FP8
-    GEMM (fp16 MFMA on the staged weights) on the prefill shape."""
+    and NVFP4 GEMMs (fp16 MFMA on the staged weights) on the prefill shape."""
     import torch
     import bit_group_quantized_amd as ql
     import synth
@@ -516,6 +516,19 @@ def bench_codecs(args, dev):
         tf = 2.0 * M * K * 8192 / (ms * 1e-3) / 1e12
         out["fp8_gemm"][f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf,
                                       "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
+    W = synth.nvfp4_matrix(rng, K, 8192)
+    Wd = {"qweight": torch.from_numpy(W["qweight"].view(np.int32)).to(dev),
+          "block_scales": torch.from_numpy(W["block_scales"]).to(dev),
+          "global_scale": float(W["global_scale"]), "K": K, "N": 8192}
+    out["nvfp4_gemm"] = {}
+    for M in (4096, 16384):
+        X = torch.from_numpy(synth.activations(rng, M, K)).to(dev)
+        Y = torch.empty((M, 8192), dtype=torch.float16, device=dev)
+        ms = timed_steps(lambda i: ql.qlinear_gemm_nvfp4(Wd, X, Y), 20 if M == 4096 else 6, 3,
+                         settle_s=SETTLE_S)
+        tf = 2.0 * M * K * 8192 / (ms * 1e-3) / 1e12
+        out["nvfp4_gemm"][f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf,
+                                        "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
     return out
 
 

@@ -69,6 +69,7 @@ _SIGS = {
     "qlinear_gemv_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8), _P, _P, _P]),
     "qlinear_gemv_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4), _P, _P, _P]),
     "qlinear_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemm_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemv_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemv_rmsnorm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, ctypes.c_float, _P, _P]),
@@ -192,6 +193,19 @@ def qlinear_gemm_fp8(W: dict, X, Y=None, stream=None):
         Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
     w = ql_fp8(W["codes"].data_ptr(), W["scales"].data_ptr(), int(W["K"]), int(W["N"]))
     _check("qlinear_gemm_fp8", lib().qlinear_gemm_fp8(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def qlinear_gemm_nvfp4(W: dict, X, Y=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 . W for NVFP4 weights (as
+    qlinear_gemv_nvfp4's W)."""
+    import torch
+    M = int(X.shape[0])
+    if Y is None:
+        Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
+    w = ql_nvfp4(W["qweight"].data_ptr(), W["block_scales"].data_ptr(), float(W["global_scale"]),
+                 int(W["K"]), int(W["N"]))
+    _check("qlinear_gemm_nvfp4", lib().qlinear_gemm_nvfp4(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
     return Y
 
 

@@ -194,6 +194,21 @@ int qlinear_gemm_fp8(const ql_fp8* W, const uint16_t* X, int64_t M, uint16_t* Y,
     return ql::launch_gemm_fp8(a, as_stream(stream));
 }
 
+int qlinear_gemm_nvfp4(const ql_nvfp4* W, const uint16_t* X, int64_t M, uint16_t* Y,
+                       void* stream) {
+    if (!W || W->N < 0 || W->K < 0 || M < 0) return QL_ERR_INVALID_ARG;
+    if (W->K == 0 || W->K % QL_GROUP_SIZE != 0 || W->K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!std::isfinite(W->global_scale)) return QL_ERR_INVALID_ARG;
+    if (W->N == 0 || M == 0) return QL_OK;
+    if (M > (int64_t)0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!W->qweight || !W->block_scales || !X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(W->qweight, 16) || !aligned(W->block_scales, 4) || !aligned(X, 16) || !aligned(Y, 2))
+        return QL_ERR_MISALIGNED;
+    ql::GemmArgs a{W->qweight, reinterpret_cast<const uint16_t*>(W->block_scales), nullptr, X, Y, M,
+                   W->K, W->N, W->global_scale};
+    return ql::launch_gemm_nvfp4(a, as_stream(stream));
+}
+
 int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* stream) {
     if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
     if (!ql::gemv_nvfp4_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;

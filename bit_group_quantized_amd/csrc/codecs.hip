@@ -12,7 +12,7 @@
 // lane 16-byte chunks at a fixed K position, R consecutive rows per team;
 // every load of a lane is issued before any arithmetic.
 #include "ql_device.h"
-#include "ql_fp8.h"
+#include "ql_codecs.h"
 #include "ql_internal.h"
 
 namespace ql {
@@ -73,20 +73,6 @@ gemv_fp8_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ 
     int rsel;
     const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
     if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot * 256.0f);
-}
-
-// A word of 8 E2M1 codes (code k at bits 4k) -> 4 fp16 pairs in natural k
-// order, each value e2m1 * 2**-14 exactly: that fp16 has high byte
-// s000eem0 (the magnitude eem lands on bits 11..9; E2M1's subnormal 0.5 on
-// the fp16 subnormal 2**-15) and low byte 0.  The high bytes of the even
-// codes (A) and the odd codes (B) are built four at a time, then paired.
-__device__ __forceinline__ void e2m1x8_to_f16x2(uint32_t u, uint32_t (&p)[4]) {
-    const uint32_t A = ((u << 1) & 0x0E0E0E0Eu) | ((u << 4) & 0x80808080u);  // codes 0, 2, 4, 6
-    const uint32_t B = ((u >> 3) & 0x0E0E0E0Eu) | (u & 0x80808080u);         // codes 1, 3, 5, 7
-    p[0] = __builtin_amdgcn_perm(B, A, 0x040C000Cu);  // (code 0, code 1)
-    p[1] = __builtin_amdgcn_perm(B, A, 0x050C010Cu);  // (2, 3)
-    p[2] = __builtin_amdgcn_perm(B, A, 0x060C020Cu);  // (4, 5)
-    p[3] = __builtin_amdgcn_perm(B, A, 0x070C030Cu);  // (6, 7)
 }
 
 template <int TPR, int V, int R>

@@ -38,7 +38,7 @@
 #include <type_traits>
 
 #include "ql_device.h"
-#include "ql_fp8.h"
+#include "ql_codecs.h"
 #include "ql_internal.h"
 
 namespace ql {
@@ -73,6 +73,7 @@ struct KParams {
     float* Yf;
     int K, N;
     int ksplit;  // router: number of K splits
+    float gscale;  // NVFP4 weights: global scale
     int grid_n, grid_m;  // dense: tile grid; grouped: N blocks (grid_n), shared tiles (grid_m)
 };
 
@@ -130,7 +131,10 @@ struct Job {
 // stay fp32 partials in both cases).
 // WF: weight format of the dense GEMM: 0 = w4 (codes, scale, bias);
 // 1 = FP8-E4M3 codes [N][K] (bytes, through p.qw) with an fp16 scale per 64
-// along K and no bias, staged as fp16(e4m3 * scale), one rounding.
+// along K and no bias, staged as fp16(e4m3 * scale), one rounding;
+// 2 = NVFP4: E2M1 codes in the w4 packing, E4M3 block scales [N][K/16]
+// (bytes, through p.sc) and the global p.gscale, staged as
+// fp16(e2m1 * fp16(e4m3 * global)).
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
@@ -205,12 +209,13 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     // Two register sets of staged global data: the loads of step i + 2 are
     // issued while step i + 1 (loaded one step earlier) is dequantized into
     // LDS and step i runs on the matrix cores.
-    static_assert(WF == 0 || (MODE == MODE_DENSE && DT == 0), "FP8 weights: fp16 dense GEMM");
+    static_assert(WF == 0 || (MODE == MODE_DENSE && DT == 0), "codec weights: fp16 dense GEMM");
     constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : (WF == 1) ? TL::WPT / 2 : TL::WPT / 4;
     constexpr int HREG = (MODE == MODE_ROUTER) ? 8 : 1;
     u32x4 areg[2][TL::A_LOADS];
     u32x4 breg[2][BREG];
     uint16_t sreg[2] = {0, 0}, bireg[2] = {0, 0};
+    uint32_t nreg[2] = {0, 0};  // NVFP4: the four block scales of a column's step
     // router B staging: an 8 x 8 block of fp16 per thread (8 rows of 16 bytes)
     u32x4 hreg[2][HREG];
 
@@ -238,8 +243,13 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
             const uint32_t* src = wq + (size_t)bcol * wpr + ks * 8 + bpart * TL::WPT;
 #pragma unroll
             for (int i = 0; i < BREG; ++i) breg[S][i] = ld_u32x4(src + 4 * i);
-            sreg[S] = ws[(size_t)bcol * G + ks];
-            bireg[S] = wb[(size_t)bcol * G + ks];
+            if constexpr (WF == 2) {
+                nreg[S] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(ws) +
+                                                             (size_t)bcol * (K / 16) + ks * 4);
+            } else {
+                sreg[S] = ws[(size_t)bcol * G + ks];
+                bireg[S] = wb[(size_t)bcol * G + ks];
+            }
         }
     };
 
@@ -286,6 +296,26 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                 o.z = as_u32(as_f16x2(q[2]) * s2);
                 o.w = as_u32(as_f16x2(q[3]) * s2);
                 const int word = bpart * W + w;  // 0..7 within the group
+                *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = o;
+            }
+        } else if constexpr (WF == 2) {
+            // e2m1 * 2**-14 (exact), times 2**14 (exact), times the block's
+            // fp16(e4m3 * global): the weight rounds at the scale and at the
+            // product.
+            const f16x2 k14 = {(f16)16384.0f, (f16)16384.0f};
+            constexpr int W = TL::WPT;  // words of 8 codes of this thread per step
+#pragma unroll
+            for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
+                const int word = bpart * W + w;  // 0..7 within the step: block word / 2
+                const f16 sc = (f16)(e4m3_to_f32((nreg[S] >> (8 * (word >> 1))) & 0xFFu) * p.gscale);
+                const f16x2 s2 = {sc, sc};
+                uint32_t q[4];
+                e2m1x8_to_f16x2(breg[S][w >> 2][w & 3], q);
+                u32x4 o;
+                o.x = as_u32((as_f16x2(q[0]) * k14) * s2);
+                o.y = as_u32((as_f16x2(q[1]) * k14) * s2);
+                o.z = as_u32((as_f16x2(q[2]) * k14) * s2);
+                o.w = as_u32((as_f16x2(q[3]) * k14) * s2);
                 *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = o;
             }
         } else if constexpr (DT == 1) {
@@ -771,6 +801,7 @@ int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
     p.Y = a.Y;
     p.K = a.K;
     p.N = a.N;
+    p.gscale = a.gscale;
     // One-dimensional grid of tiles, rounded up to whole XCD rounds.
     auto grid_for = [&](int bm, int bn, dim3& grid) {
         const int64_t gn = (a.N + bn - 1) / bn, gm = (a.M + bm - 1) / bm;
@@ -805,6 +836,8 @@ int launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0>(a,
 int launch_gemm_bf16(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<1>(a, st); }
 
 int launch_gemm_fp8(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0, 1>(a, st); }
+
+int launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0, 2>(a, st); }
 
 bool gemm_ws_supported(int K) { return K == 512 || K == 1024 || K == 2048; }
 

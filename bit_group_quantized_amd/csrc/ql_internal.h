@@ -76,6 +76,7 @@ struct GemmArgs {
     uint16_t* Y;
     int64_t M;
     int K, N;
+    float gscale = 1.f;  // NVFP4 weights: global scale
 };
 int launch_gemm(const GemmArgs& a, hipStream_t st);
 // bf16 activations, scales, biases and outputs (same tile table).
@@ -83,6 +84,9 @@ int launch_gemm_bf16(const GemmArgs& a, hipStream_t st);
 // FP8-E4M3 weights: qweight points at the uint8 codes [N][K], scales fp16
 // [N][K/64], biases unused.
 int launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
+// NVFP4 weights: qweight the E2M1 codes [N][K/8], scales points at the E4M3
+// block scales (bytes) [N][K/16], gscale the global scale.
+int launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
 bool gemm_ws_supported(int K);                          // few-row GEMM shapes
 int launch_gemm_ws(const GemmArgs& a, hipStream_t st);  // few-row GEMM (weight-stationary)
 

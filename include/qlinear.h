@@ -242,6 +242,19 @@ int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* 
 int qlinear_gemm_fp8(const ql_fp8* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 
 /*
+ * qlinear_gemm_nvfp4 - Y fp16 [M][N] = X fp16 [M][K] . W for NVFP4 weights,
+ * the prefill counterpart of qlinear_gemv_nvfp4: the MFMA tiles of
+ * qlinear_gemm (same shape table and row invariance) with each staged weight
+ * fp16(e2m1 * fp16(e4m3(block scale) * global_scale)): the block scale is
+ * rounded once to fp16 and the product once more (the e2m1 value is exact),
+ * fp32 accumulation, fp16 output.
+ * Limits: K a positive multiple of 64, K <= QL_MAX_K; global_scale finite.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (qweight and X 16-byte,
+ * block_scales 4-byte, Y 2-byte aligned), HIP.
+ */
+int qlinear_gemm_nvfp4(const ql_nvfp4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
  * qlinear_gemv_rmsnorm - y = fp16(rmsnorm(x)) . dequant(W): a decode
  * projection with its normalization fused in front ([PPLX] "减少中间状态和流量":
  * the decode chains keep intermediates in registers, normalization among

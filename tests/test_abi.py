@@ -305,3 +305,19 @@ def test_gemm_fp8_validation(L):
     assert call(M=0) == OK
     assert call(N=0) == OK
     assert f(None, A16, 8, A16, None) == INVALID
+
+
+def test_gemm_nvfp4_validation(L):
+    f = L.qlinear_gemm_nvfp4
+
+    def call(K=2048, N=64, M=8, qw=A16, bs=A16, g=1.0, X=A16):
+        w = ql.ql_nvfp4(qw, bs, g, K, N)
+        return f(ctypes.byref(w), X, M, A16, None)
+
+    assert call(K=96) == SHAPE
+    assert call(M=-1) == INVALID
+    assert call(g=float("inf")) == INVALID
+    assert call(qw=None) == INVALID
+    assert call(bs=A16 + 2) == MISALIGNED
+    assert call(qw=A16 + 4) == MISALIGNED
+    assert call(M=0) == OK

@@ -161,3 +161,64 @@ def test_gemm_fp8_integer_case_bit_exact():
     Y = host(ql.qlinear_gemm_fp8(fp8_dev(W), t(X)))
     torch.cuda.synchronize()
     assert np.array_equal(Y.view(np.uint16), ref.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,N,seed", [
+    (1, 2048, 512, 0), (7, 512, 200, 1), (256, 2048, 8192, 2), (300, 2048, 1000, 3),
+    (129, 64, 257, 4), (1024, 1024, 640, 5), (2500, 192, 300, 7), (2100, 256, 4100, 9),
+    (130, 32768, 70, 10),
+])
+def test_gemm_nvfp4_matches_oracle(M, K, N, seed):
+    """NVFP4 weights on the MFMA tiles: ragged M and N in every tile class,
+    the largest K."""
+    import torch
+    say(f"gemm_nvfp4 M={M} K={K} N={N} seed={seed}")
+    rng = synth.rng_for(seed)
+    X = synth.activations(rng, M, K)
+    W = synth.nvfp4_matrix(rng, K, N)
+    ref = oracle.linear_nvfp4(X, W)
+    Y = ql.qlinear_gemm_nvfp4(nvfp4_dev(W), t(X))
+    torch.cuda.synchronize()
+    rel, mx = assert_close(host(Y).astype(np.float64), ref, f"gemm_nvfp4 M={M} K={K} N={N}")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_gemm_nvfp4_prefill_sampled_rows_and_row_invariance():
+    import torch
+    M, K, N = 4096, 2048, 8192
+    rng = synth.rng_for(22)
+    X = synth.activations(rng, M, K)
+    W = synth.nvfp4_matrix(rng, K, N)
+    Wd, Xd = nvfp4_dev(W), t(X)
+    Y = host(ql.qlinear_gemm_nvfp4(Wd, Xd))
+    rows = np.sort(synth.rng_for(23).choice(M, 64, replace=False))
+    ref = oracle.linear_nvfp4(X[rows], W)
+    assert_close(Y[rows].astype(np.float64), ref, "gemm_nvfp4 sampled rows")
+    for m in (0, 255, 4095):
+        for MM in (1, 256):
+            lo = min(m, M - MM)
+            part = host(ql.qlinear_gemm_nvfp4(Wd, Xd[lo:lo + MM].contiguous()))
+            assert np.array_equal(part[m - lo].view(np.uint16), Y[m].view(np.uint16)), (m, MM)
+    torch.cuda.synchronize()
+
+
+def test_gemm_nvfp4_integer_case_bit_exact():
+    """E2M1 codes of integers (0, 1, 2, 3, 4, 6 and their negatives), block
+    scales 1.0, global scale 1, integer activations: every product and fp32
+    sum is exact, so the output equals the oracle's rounded value bit for
+    bit."""
+    import torch
+    M, K, N = 300, 512, 260
+    rng = synth.rng_for(31)
+    nib = np.array([0x0, 0x2, 0x4, 0x5, 0x6, 0x7], dtype=np.uint32)[rng.integers(0, 6, size=(N, K))]
+    nib = nib | (rng.integers(0, 2, size=(N, K)).astype(np.uint32) << 3)
+    words = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        words |= nib[:, j::8] << np.uint32(4 * j)
+    W = {"qweight": words, "block_scales": np.full((N, K // 16), 0x38, dtype=np.uint8),
+         "global_scale": np.float32(1.0), "K": K, "N": N}
+    X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    ref = oracle.linear_nvfp4(X, W)
+    Y = host(ql.qlinear_gemm_nvfp4(nvfp4_dev(W), t(X)))
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint16), ref.astype(np.float16).view(np.uint16))

@@ -7,9 +7,9 @@ step is both GEMVs.  `value` is the effective HBM bandwidth: algorithmic
 bytes (codes + scales + biases + x + y) per step divided by the step time,
 with every input already resident in HBM.  Weight copies are rotated so the
 working set between two uses of one copy exceeds the 256 MB Infinity Cache.
-`stats` adds the spread: the median step time (and head launch time) over
-30 event-bracketed rounds of 10 steps, with a 2,000-resample bootstrap 95%
-interval of that median, measured after the timed regions.
+`stats` adds the spread: the median step time over 30 event-bracketed
+rounds of 10 steps, with a 2,000-resample bootstrap 95% interval of that
+median, measured after the timed regions.
 
 Also measured and reported under "workloads" (same run, same rules): the
 prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the few-row
@@ -232,18 +232,14 @@ def bench_gemv(args, dev):
     avg_launch_ms = kern_ms[1]
     avg_launch_bytes = launch_bytes[1]
     achieved = avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9
-    # Spread of the step time and of the head launch (median over rounds and
-    # its bootstrap 95% interval), after the timed regions above.
+    # Spread of the step time (median over rounds and its bootstrap 95%
+    # interval), after the timed regions above.
     st_step = round_stats(step)
-    st_head = round_stats(lambda i: ql.qlinear_gemv(Ws[i % copies][1], x, ys[1]))
     to_gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
     stats = {
         "step": dict(st_step, **{"GB/s_median": to_gbs(step_bytes, st_step["median_ms"]),
                                  "GB/s_ci95": [to_gbs(step_bytes, st_step["ci95_ms"][1]),
                                                to_gbs(step_bytes, st_step["ci95_ms"][0])]}),
-        "head_launch": dict(st_head, **{"GB/s_median": to_gbs(avg_launch_bytes, st_head["median_ms"]),
-                                        "GB/s_ci95": [to_gbs(avg_launch_bytes, st_head["ci95_ms"][1]),
-                                                      to_gbs(avg_launch_bytes, st_head["ci95_ms"][0])]}),
     }
     # The same step as a replayed HIP graph (launch overhead removed), for context.
     graph_ms = graph_time(step, copies * 2, 20) if copies * 2 <= 64 else None

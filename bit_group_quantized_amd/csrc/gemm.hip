@@ -762,7 +762,7 @@ gemm_w4_grouped_kernel(const KParams p) {
         const int* tp = p.tiles + (size_t)tslot * 4;
         // Clamped so that a corrupted tile map can never index out of bounds.
         const int e = min(max(tp[0], 0), p.E - 1);
-        job.rows_valid = min(max(tp[2], 1), height);
+        job.rows_valid = min(min(max(tp[2], 1), height), p.T * p.topk);
         job.tile_first = min(max(tp[1], 0), p.T * p.topk - job.rows_valid);
         job.out_row0 = job.tile_first;
         job.wq = p.qw + (size_t)e * p.N * wpr;

@@ -301,3 +301,61 @@ def test_moe_decode_entry_graph_replays():
         torch.cuda.synchronize()
     ref = oracle.moe_layer(synth.moe_tokens(3100, 1)["H"], w, None, 8)
     assert_close(eager[0].astype(np.float64), ref["out"], "decode out")
+
+
+def test_decode_token_loop_through_moe_graph():
+    """A decode loop that never leaves the GPU: the routed-expert layer
+    (moe_decode) on the current row, the vocabulary head's token choice into
+    a device slot, the next row read from the embedding table by that slot;
+    four steps with two alternating slots, captured once in a HIP graph and
+    replayed.  Every replay's tokens and rows equal the oracle's chain, and
+    each step's layer output is within the fp16 bar.  The seed is screened
+    by the oracle: every top-8 cut clears 1e-3 and every token choice 1% of
+    the largest logit."""
+    import torch
+    K, V, steps, seed = 2048, 4096, 4, 66
+    w = synth.moe_weights(seed)
+    rng = synth.rng_for(seed + 500)
+    Wh = synth.w4_matrix(rng, K, V)
+    E = synth.w4_matrix(rng, K, V)
+    x0 = synth.activations(rng, 1, K)[0]
+    toks, rows, outs, x = [], [], [], x0
+    for _ in range(steps):
+        ref = oracle.moe_layer(x[None, :], w, None, 8)
+        srt = -np.sort(-ref["logits"][0])
+        assert srt[7] - srt[8] > 1e-3, "routing near a tie"
+        tok, logits = oracle.lm_head_token(oracle.round_f16(ref["out"][0]), Wh)
+        s2 = np.sort(logits)
+        assert s2[-1] - s2[-2] > 1e-2 * np.abs(logits).max(), "token choice near a tie"
+        x = oracle.embed_row(E, tok)
+        toks.append(tok)
+        rows.append(x)
+        outs.append(ref["out"][0])
+    dev = torch.device("cuda")
+    dw = _dev_weights(w)
+    Whd, Ed = w4_dev(Wh), w4_dev(E)
+    xs = [t(x0[None, :])] + [torch.empty((1, K), dtype=torch.float16, device=dev) for _ in range(steps)]
+    dec = [ql.alloc_decode_outputs(1, 256, 8, K, 512, dev) for _ in range(steps)]
+    slots = torch.full((2,), -7, dtype=torch.int32, device=dev)
+    ws = ql.gemv_argmax_workspace(V, dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                slot = slots[i % 2:i % 2 + 1]
+                ql.moe_decode(xs[i], dw["Wr"], None, 8, dw["gate_up"], dw["down"],
+                              dw["shared_gate_up"], dw["shared_down"], out=dec[i])
+                ql.qlinear_gemv_argmax(Whd, dec[i]["out"][0], token=slot, workspace=ws)
+                ql.qlinear_embed_token(Ed, slot, xs[i + 1][0])
+    for rep in range(3):
+        for b in xs[1:]:
+            b.fill_(7.0)  # eager work between replays
+        slots.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(steps):
+            assert np.array_equal(host(xs[i + 1][0]).view(np.uint16), rows[i].view(np.uint16)), (rep, i)
+            assert_close(host(dec[i]["out"][0]).astype(np.float64), outs[i], f"layer output {i}")
+        assert host(slots).tolist() == [toks[steps - 2], toks[steps - 1]], rep

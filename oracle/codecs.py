@@ -19,13 +19,20 @@ Readings:
   magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6;
 * NVFP4 weights: E2M1 codes packed 8 per uint32 exactly as the w4 codes,
   one E4M3 block scale per 16 consecutive k of one output and one fp32
-  scale for the whole matrix: w = e2m1(code) * e4m3(block scale) * global.
+  scale for the whole matrix: w = e2m1(code) * e4m3(block scale) * global;
+* an FP8 routed-expert layer stores every expert matrix (and the shared
+  expert's) in the FP8 format above, stacked over experts; routing, the
+  gated activation (rounded to fp16), the row order and the combine are
+  those of the w4 layer in oracle.moe.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .w4 import unpack_codes
+from .w4 import unpack_codes, round_f16
+from .moe import silu, combine
+from .route import (router_logits, topk_route, histogram, exclusive_scan,
+                    stable_permutation)
 
 FP8_GROUP = 64
 NVFP4_BLOCK = 16
@@ -97,3 +104,58 @@ def linear_nvfp4(X, W: dict, row_chunk: int = 8192) -> np.ndarray:
         Wd = dequantize_nvfp4(W["qweight"][n0:n1], W["block_scales"][n0:n1], W["global_scale"], K)
         Y[:, n0:n1] = X @ Wd.T
     return Y
+
+
+def expert_ffn_fp8(X, gate_up: dict, down: dict):
+    """One FP8 expert on fp16 rows X [R][D]: u = X @ W_gu,
+    act = fp16(SiLU(u[:, :I]) * u[:, I:]), ydown = act @ W_dn, with both
+    weights dequantized exactly (float64)."""
+    X = np.asarray(X).astype(np.float64)
+    I = gate_up["N"] // 2
+    u = X @ dequantize_fp8(gate_up["codes"], gate_up["scales"]).T
+    act = round_f16(silu(u[:, :I]) * u[:, I:])
+    ydown = act.astype(np.float64) @ dequantize_fp8(down["codes"], down["scales"]).T
+    return act, ydown
+
+
+def moe_layer_fp8(H, weights: dict, logit_bias=None, topk: int = 8,
+                  with_shared: bool = True) -> dict:
+    """The routed-expert layer on fp16 tokens H [T][D] with FP8 experts.
+
+    ``weights`` holds Wr [D][E] fp16 and gate_up / down / shared_gate_up /
+    shared_down as FP8 dicts (codes, scales; experts stacked on the first
+    axis).  Returns the same intermediates as oracle.moe.moe_layer.
+    """
+    H = np.asarray(H)
+    T = H.shape[0]
+    E = weights["Wr"].shape[1]
+    logits = router_logits(H, weights["Wr"], logit_bias)
+    ids, gates = topk_route(logits, topk)
+    counts = histogram(ids, E)
+    offsets = exclusive_scan(counts)
+    sorted_assign, pos = stable_permutation(ids, E)
+
+    gu, dn = weights["gate_up"], weights["down"]
+    I = gu["N"] // 2
+    D = dn["N"]
+    R = T * topk + (T if with_shared else 0)
+    act = np.zeros((R, I), dtype=np.float16)
+    ydown = np.zeros((R, D), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        tokens = sorted_assign[r0:r1] // topk
+        a, y = expert_ffn_fp8(H[tokens],
+                              {"codes": gu["codes"][e], "scales": gu["scales"][e], "N": gu["N"]},
+                              {"codes": dn["codes"][e], "scales": dn["scales"][e], "N": dn["N"]})
+        act[r0:r1] = a
+        ydown[r0:r1] = y
+    if with_shared:
+        a, y = expert_ffn_fp8(H, weights["shared_gate_up"], weights["shared_down"])
+        act[T * topk:] = a
+        ydown[T * topk:] = y
+    out = combine(ydown, gates, pos, T, topk, with_shared)
+    return {"logits": logits, "ids": ids, "gates": gates, "counts": counts,
+            "offsets": offsets, "sorted_assign": sorted_assign, "pos": pos,
+            "act": act, "ydown": ydown, "out": out}

@@ -108,11 +108,12 @@ def gemm_case_bf16(seed: int, M: int, K: int, N: int) -> dict:
     return {"X": X, "W": W}
 
 
-def fp8_matrix(rng: np.random.Generator, K: int, N: int) -> dict:
-    """FP8-E4M3 weights: codes uint8 [N][K] (no NaN codes), fp16 scales [N][K/64]."""
-    codes = rng.integers(0, 254, size=(N, K), dtype=np.int64)
+def fp8_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
+    """FP8-E4M3 weights: codes uint8 [N][K] (no NaN codes), fp16 scales [N][K/64];
+    ``lead`` stacks several such matrices (e.g. (E,) for E experts)."""
+    codes = rng.integers(0, 254, size=lead + (N, K), dtype=np.int64)
     codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)   # skip 0x7F (and 0xFF)
-    scales = f16(rng.uniform(1e-4, 1e-3, size=(N, K // 64)))
+    scales = f16(rng.uniform(1e-4, 1e-3, size=lead + (N, K // 64)))
     return {"codes": codes, "scales": scales, "K": K, "N": N}
 
 
@@ -204,6 +205,21 @@ def moe_weights(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_
     down = w4_matrix(rng, I, D, lead=(E,))
     shared_gate_up = w4_matrix(rng, D, 2 * I)
     shared_down = w4_matrix(rng, I, D)
+    return {"Wr": Wr, "gate_up": gate_up, "down": down,
+            "shared_gate_up": shared_gate_up, "shared_down": shared_down,
+            "D": D, "I": I, "E": E}
+
+
+def moe_weights_fp8(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:
+    """moe_weights with FP8-E4M3 experts (fp8_matrix draws).  The fp16 router
+    weight is drawn first from the same seed, so it equals moe_weights(seed)'s
+    and a token seed routes exactly as it does there."""
+    rng = rng_for(seed)
+    Wr = router_weight(rng, D, E)
+    gate_up = fp8_matrix(rng, D, 2 * I, lead=(E,))
+    down = fp8_matrix(rng, I, D, lead=(E,))
+    shared_gate_up = fp8_matrix(rng, D, 2 * I)
+    shared_down = fp8_matrix(rng, I, D)
     return {"Wr": Wr, "gate_up": gate_up, "down": down,
             "shared_gate_up": shared_gate_up, "shared_down": shared_down,
             "D": D, "I": I, "E": E}

@@ -131,3 +131,71 @@ def test_codec_shape_checks():
         oracle.dequantize_fp8(np.zeros((1, 96), np.uint8), np.ones((1, 1), np.float16))
     with pytest.raises(ValueError):
         oracle.dequantize_nvfp4(np.zeros((1, 3), np.uint32), np.zeros((1, 1), np.uint8), 1.0, 24)
+
+
+# E4M3 codes of the integers 0..8 (sign bit 0x80 gives -0..-8).
+_E4M3_INT = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50], np.uint8)
+
+
+def _w4_as_fp8(W):
+    """A w4 matrix (stack) whose biases are -8 * scale, rewritten as FP8: the
+    weight s*q - 8s is e4m3(q - 8) * s, both exact in float64."""
+    q = oracle.unpack_codes(W["qweight"], W["K"]).astype(np.int64) - 8
+    codes = _E4M3_INT[np.abs(q)] | np.where(q < 0, 0x80, 0).astype(np.uint8)
+    return {"codes": codes.astype(np.uint8), "scales": W["scales"], "K": W["K"], "N": W["N"]}
+
+
+def _w4_centered(W):
+    W = dict(W)
+    W["biases"] = (W["scales"].astype(np.float64) * -8.0).astype(np.float16)
+    return W
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_moe_fp8_equals_w4_layer_on_common_weights(shared):
+    """Weights that both formats hold exactly (w4 with bias = -8 * scale, the
+    FP8 codes of q - 8 with the same scales): the FP8 layer must reproduce the
+    separately pinned w4 layer exactly, routing, every row and the output."""
+    import synth
+    w = synth.moe_weights(11, D=128, I=64, E=8)
+    w4 = {k: (_w4_centered(v) if isinstance(v, dict) else v) for k, v in w.items()}
+    f8 = {k: (_w4_as_fp8(v) if isinstance(v, dict) else v) for k, v in w4.items()}
+    H = synth.activations(synth.rng_for(12), 37, 128)
+    a = oracle.moe_layer(H, w4, None, 3, with_shared=shared)
+    b = oracle.moe_layer_fp8(H, f8, None, 3, with_shared=shared)
+    for key in ("ids", "counts", "offsets", "sorted_assign", "pos"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["act"].view(np.uint16), b["act"].view(np.uint16))
+    assert np.array_equal(a["ydown"], b["ydown"]) and np.array_equal(a["out"], b["out"])
+
+
+def test_moe_fp8_token_loop_bruteforce():
+    """Token by token, in token order (no sorting or permutation): out[t] =
+    sum_j gate[t][j] * down_e(fp16(SiLU(gate_e(h)) * up_e(h))) + the shared
+    expert's, with e = ids[t][j] and every dot product a math.fsum."""
+    import math
+    import synth
+    T, D, I, E, topk = 4, 64, 64, 6, 2
+    w = synth.moe_weights_fp8(13, D=D, I=I, E=E)
+    H = synth.activations(synth.rng_for(14), T, D)
+    ref = oracle.moe_layer_fp8(H, w, None, topk)
+
+    def ffn(h, gu_codes, gu_scales, dn_codes, dn_scales):
+        Wg = oracle.dequantize_fp8(gu_codes, gu_scales)     # [2I][D]
+        Wd = oracle.dequantize_fp8(dn_codes, dn_scales)     # [D][I]
+        hv = [float(v) for v in h]
+        u = [math.fsum(hv[k] * Wg[n][k] for k in range(D)) for n in range(2 * I)]
+        act = [float(np.float16(u[i] / (1.0 + math.exp(-u[i])) * u[I + i])) for i in range(I)]
+        return [math.fsum(act[i] * Wd[n][i] for i in range(I)) for n in range(D)]
+
+    for tok in range(T):
+        acc = [0.0] * D
+        for j in range(topk):
+            e = int(ref["ids"][tok][j])
+            y = ffn(H[tok], w["gate_up"]["codes"][e], w["gate_up"]["scales"][e],
+                    w["down"]["codes"][e], w["down"]["scales"][e])
+            acc = [a + float(ref["gates"][tok][j]) * v for a, v in zip(acc, y)]
+        ys = ffn(H[tok], w["shared_gate_up"]["codes"], w["shared_gate_up"]["scales"],
+                 w["shared_down"]["codes"], w["shared_down"]["scales"])
+        acc = [a + v for a, v in zip(acc, ys)]
+        np.testing.assert_allclose(ref["out"][tok], acc, rtol=1e-9, atol=1e-9)

@@ -346,3 +346,41 @@ def _bf16_combine_no_shared(ydown, gates, pos, T, topk, has_shared):
 def test_bf16_moe_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(obf, attr, mutant)
     assert _fails(BF16_MOE_PINS)
+
+
+from tests import test_oracle_codecs as tcod
+
+FP8_MOE_PINS = [lambda: tcod.test_moe_fp8_equals_w4_layer_on_common_weights(True),
+                tcod.test_moe_fp8_token_loop_bruteforce]
+_ORIG_FFN_FP8 = ocod.expert_ffn_fp8
+
+
+def _ffn_fp8_up_gate_swapped(X, gate_up, down):
+    half = gate_up["N"] // 2
+    gu = {"codes": np.concatenate([gate_up["codes"][half:], gate_up["codes"][:half]]),
+          "scales": np.concatenate([gate_up["scales"][half:], gate_up["scales"][:half]]),
+          "N": gate_up["N"]}
+    return _ORIG_FFN_FP8(X, gu, down)
+
+
+def _ffn_fp8_no_act_rounding(X, gate_up, down):
+    X = np.asarray(X).astype(np.float64)
+    I = gate_up["N"] // 2
+    u = X @ ocod.dequantize_fp8(gate_up["codes"], gate_up["scales"]).T
+    a = ocod.silu(u[:, :I]) * u[:, I:]
+    ydown = a @ ocod.dequantize_fp8(down["codes"], down["scales"]).T
+    return a.astype(np.float16), ydown
+
+
+def _fp8_combine_no_shared(ydown, gates, pos, T, topk, has_shared):
+    return _ORIG_COMBINE(ydown, gates, pos, T, topk, False)
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("expert_ffn_fp8", _ffn_fp8_up_gate_swapped),
+    ("expert_ffn_fp8", _ffn_fp8_no_act_rounding),
+    ("combine", _fp8_combine_no_shared),
+])
+def test_fp8_moe_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(ocod, attr, mutant)
+    assert _fails(FP8_MOE_PINS)

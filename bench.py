@@ -16,7 +16,7 @@ prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the few-row
 GEMM, the bf16 variant, the FP8 / NVFP4 codecs, the decode fusions, the
 decode MoE layer (one token, 8 of 256 experts + shared; moe_decode and the
 three-call path) and the prefill MoE layer (4096 tokens, Zipf-skewed expert
-loads).
+loads; w4, bf16 and FP8 experts).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-primary]
 """
@@ -715,6 +715,59 @@ def bench_moe_prefill_bf16(args, dev):
             "seed": 4}
 
 
+def bench_moe_prefill_fp8(args, dev):
+    """The same 4096-token layer with FP8-E4M3 experts (moe_route /
+    moe_grouped_gemm_fp8 / moe_combine; fp16 tokens and outputs)."""
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    T = 4096
+    seeds = json.load(open(os.path.join(ROOT, "tests", "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
+    w = synth.moe_weights_fp8(0)
+    tok = synth.moe_tokens(seeds[0], T, skewed=True)
+    wd = lambda W: {"codes": torch.from_numpy(np.ascontiguousarray(W["codes"])).to(dev),
+                    "scales": torch.from_numpy(np.ascontiguousarray(W["scales"])).to(dev),
+                    "K": W["K"], "N": W["N"]}
+    dw = {k: wd(w[k]) for k in ("gate_up", "down", "shared_gate_up", "shared_down")}
+    Wr, H = torch.from_numpy(w["Wr"]).to(dev), torch.from_numpy(tok["H"]).to(dev)
+    bias = torch.from_numpy(tok["logit_bias"]).to(dev)
+    route = ql.alloc_route_outputs(T, 256, 8, dev)
+    act = torch.empty((9 * T, 512), dtype=torch.float16, device=dev)
+    yd = torch.empty((9 * T, 2048), dtype=torch.float16, device=dev)
+    out = torch.empty((T, 2048), dtype=torch.float16, device=dev)
+
+    def r_(i):
+        ql.moe_route(H, Wr, bias, 8, route)
+
+    def gu(i):
+        ql.moe_grouped_gemm_fp8(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU,
+                                route, act)
+
+    def dn(i):
+        ql.moe_grouped_gemm_fp8(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
+
+    def cb(i):
+        ql.moe_combine(yd, route["gates"], route["pos"], T, 8, True, out)
+
+    def step(i):
+        r_(i)
+        gu(i)
+        dn(i)
+        cb(i)
+
+    ms = timed_steps(step, 20, 3, settle_s=SETTLE_S)
+    k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2, settle_s=SETTLE_S / 4))
+    routed_rows = T * 8
+    flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
+             + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)
+    return {"tokens/s": T / (ms * 1e-3), "ms_per_step": ms, "flops": flops,
+            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
+                         "down": float(k[2] * 1e3), "combine": float(k[3] * 1e3)},
+            "seed": int(seeds[0])}
+
+
 CALIB_BYTES = 256 * 1024 * 1024
 
 
@@ -869,6 +922,8 @@ def main():
                 wl["moe_prefill_4096tok"] = bench_moe_prefill(args, dev, w)
                 log("bench: MoE prefill, bf16")
                 wl["moe_prefill_4096tok_bf16"] = bench_moe_prefill_bf16(args, dev)
+                log("bench: MoE prefill, FP8 experts")
+                wl["moe_prefill_4096tok_fp8"] = bench_moe_prefill_fp8(args, dev)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline()

@@ -52,6 +52,11 @@ class ql_fp8(ctypes.Structure):
                 ("N", ctypes.c_int32)]
 
 
+class ql_fp8_experts(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("K", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("num_experts", ctypes.c_int32)]
+
+
 class ql_nvfp4(ctypes.Structure):
     _fields_ = [("qweight", ctypes.c_void_p), ("block_scales", ctypes.c_void_p),
                 ("global_scale", ctypes.c_float), ("K", ctypes.c_int32), ("N", ctypes.c_int32)]
@@ -90,6 +95,8 @@ _SIGS = {
     "moe_grouped_gemm_bf16": (ctypes.c_int, [ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4), _P,
                                              _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "moe_combine_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8_experts), ctypes.POINTER(ql_fp8), _P,
+                                            _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "moe_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_decode_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
@@ -409,6 +416,29 @@ def moe_grouped_gemm_bf16(W: dict, shared: dict | None, X, T: int, topk: int, op
         Y = torch.empty(shape, dtype=torch.bfloat16, device=X.device)
     ws = route["workspace"]
     _check("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
+        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
+        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
+        _stream(stream)))
+    return Y
+
+
+def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
+                         Y=None, stream=None):
+    """moe_grouped_gemm with FP8 experts: W holds codes uint8 [E][N][K] and
+    fp16 scales [E][N][K/64] (device tensors), shared one such matrix or None
+    (QL_OP_GATE_UP_SILU or QL_OP_DOWN)."""
+    import torch
+    codes = W["codes"]
+    w = ql_fp8_experts(codes.data_ptr(), W["scales"].data_ptr(), int(W["K"]), int(W["N"]),
+                       int(codes.shape[0]))
+    s = (ql_fp8(shared["codes"].data_ptr(), shared["scales"].data_ptr(), int(shared["K"]),
+                int(shared["N"])) if shared is not None else None)
+    rows = T * topk + (T if shared is not None else 0)
+    if Y is None:
+        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        Y = torch.empty(shape, dtype=torch.float16, device=X.device)
+    ws = route["workspace"]
+    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
         _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
         _stream(stream)))

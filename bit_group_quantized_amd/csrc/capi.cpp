@@ -304,17 +304,21 @@ int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk, in
     return ql::launch_dispatch(a, as_stream(stream));
 }
 
-static int grouped_impl(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X, int32_t T,
-                        int32_t topk, int32_t op, const int32_t* offsets,
-                        const int32_t* sorted_assign, const float* topk_gates,
-                        const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
-                        uint16_t* Y, void* stream, bool bf16) {
+// Expert weights of a grouped call, already checked for format and layout.
+struct ExpertView {
+    const uint32_t* qw;
+    const uint16_t* sc;
+    const uint16_t* bi;
+    const uint32_t* sqw;  // shared expert or null
+    const uint16_t* ssc;
+    const uint16_t* sbi;
+    int32_t K, N, E;
+    bool bf16;
+    int wf;  // 0 = w4, 1 = FP8
+};
+
+static int w4_view(const ql_w4_experts* W, const ql_w4* shared, bool bf16, ExpertView& v) {
     if (!W) return QL_ERR_INVALID_ARG;
-    if (op != QL_OP_GATE_UP_SILU && op != QL_OP_DOWN && op != QL_OP_DOWN_COMBINE)
-        return QL_ERR_INVALID_ARG;
-    const int32_t E = W->num_experts;
-    if (T < 0 || E <= 0 || topk <= 0 || topk > E) return QL_ERR_INVALID_ARG;
-    if (E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
     int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
     if (rc != QL_OK) return rc;
     if (shared) {
@@ -323,8 +327,34 @@ static int grouped_impl(const ql_w4_experts* W, const ql_w4* shared, const uint1
         if (rc != QL_OK) return rc;
         if (shared->K != W->K || shared->N != W->N) return QL_ERR_INVALID_ARG;
     }
-    if (op == QL_OP_GATE_UP_SILU && W->N % 2 != 0) return QL_ERR_UNSUPPORTED_SHAPE;
-    if (T == 0 || W->N == 0) return QL_OK;
+    v = ExpertView{W->qweight, W->scales, W->biases,
+                   shared ? shared->qweight : nullptr,
+                   shared ? shared->scales : nullptr,
+                   shared ? shared->biases : nullptr,
+                   W->K, W->N, W->num_experts, bf16, 0};
+    return QL_OK;
+}
+
+static int check_fp8(const uint8_t* codes, const uint16_t* scales, int32_t K, int32_t N) {
+    if (N < 0 || K < 0) return QL_ERR_INVALID_ARG;
+    if (K == 0 || K % QL_GROUP_SIZE != 0 || K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (N == 0) return QL_OK;
+    if (!codes || !scales) return QL_ERR_INVALID_ARG;
+    if (!aligned(codes, 16) || !aligned(scales, 2)) return QL_ERR_MISALIGNED;
+    return QL_OK;
+}
+
+static int grouped_impl(const ExpertView& w, const uint16_t* X, int32_t T, int32_t topk, int32_t op,
+                        const int32_t* offsets, const int32_t* sorted_assign,
+                        const float* topk_gates, const int32_t* assign_pos, const void* workspace,
+                        size_t ws_bytes, uint16_t* Y, void* stream) {
+    if (op != QL_OP_GATE_UP_SILU && op != QL_OP_DOWN && op != QL_OP_DOWN_COMBINE)
+        return QL_ERR_INVALID_ARG;
+    const int32_t E = w.E;
+    if (T < 0 || E <= 0 || topk <= 0 || topk > E) return QL_ERR_INVALID_ARG;
+    if (E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (op == QL_OP_GATE_UP_SILU && w.N % 2 != 0) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0 || w.N == 0) return QL_OK;
     if ((int64_t)T * topk > 0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
     if (!X || !Y || !offsets || !sorted_assign) return QL_ERR_INVALID_ARG;
     if (!aligned(X, 16) || !aligned(Y, 2) || !aligned(offsets, 4) || !aligned(sorted_assign, 4))
@@ -332,23 +362,20 @@ static int grouped_impl(const ql_w4_experts* W, const ql_w4* shared, const uint1
     if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
 
-    // The row-parallel decode kernels are fp16 only; the bf16 layer runs
-    // every T on the tiled path.
-    const bool rows_path = !bf16 && T <= QL_DECODE_MAX_T && ql::moe_rows_supported(W->K);
+    // The row-parallel decode kernels take fp16 w4 weights only; the bf16
+    // and FP8 layers run every T on the tiled path.
+    const bool rows_path = !w.bf16 && w.wf == 0 && T <= QL_DECODE_MAX_T && ql::moe_rows_supported(w.K);
     if (op == QL_OP_DOWN_COMBINE) {
         if (!rows_path) return QL_ERR_UNSUPPORTED_SHAPE;
         if (!topk_gates || !assign_pos) return QL_ERR_INVALID_ARG;
         if (!aligned(topk_gates, 4) || !aligned(assign_pos, 4)) return QL_ERR_MISALIGNED;
-        const int J = topk + (shared ? 1 : 0);
-        if ((int64_t)J * W->K * 2 > 49152) return QL_ERR_UNSUPPORTED_SHAPE;
+        const int J = topk + (w.sqw ? 1 : 0);
+        if ((int64_t)J * w.K * 2 > 49152) return QL_ERR_UNSUPPORTED_SHAPE;
     }
-    ql::GroupedArgs a{W->qweight, W->scales, W->biases,
-                      shared ? shared->qweight : nullptr,
-                      shared ? shared->scales : nullptr,
-                      shared ? shared->biases : nullptr,
+    ql::GroupedArgs a{w.qw, w.sc, w.bi, w.sqw, w.ssc, w.sbi,
                       X, offsets, sorted_assign, topk_gates, assign_pos,
                       static_cast<const unsigned char*>(workspace), Y,
-                      W->K, W->N, E, T, topk, op, bf16};
+                      w.K, w.N, E, T, topk, op, w.bf16, w.wf};
     if (rows_path) return ql::launch_moe_rows(a, as_stream(stream));
     return ql::launch_moe_grouped(a, as_stream(stream));
 }
@@ -358,17 +385,42 @@ int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared, const uint16_t
                      const int32_t* sorted_assign, const float* topk_gates,
                      const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
                      uint16_t* Y, void* stream) {
-    return grouped_impl(W, shared, X, T, topk, op, offsets, sorted_assign, topk_gates, assign_pos,
-                        workspace, ws_bytes, Y, stream, false);
+    ExpertView v;
+    if (const int rc = w4_view(W, shared, false, v)) return rc;
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, topk_gates, assign_pos,
+                        workspace, ws_bytes, Y, stream);
 }
 
 int moe_grouped_gemm_bf16(const ql_w4_experts* W, const ql_w4* shared, const uint16_t* X,
                           int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
                           const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
                           uint16_t* Y, void* stream) {
+    ExpertView v;
+    if (const int rc = w4_view(W, shared, true, v)) return rc;
     if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
-    return grouped_impl(W, shared, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr,
-                        workspace, ws_bytes, Y, stream, true);
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr,
+                        workspace, ws_bytes, Y, stream);
+}
+
+int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared, const uint16_t* X,
+                         int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
+                         const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
+                         uint16_t* Y, void* stream) {
+    if (!W) return QL_ERR_INVALID_ARG;
+    int rc = check_fp8(W->codes, W->scales, W->K, W->N);
+    if (rc != QL_OK) return rc;
+    if (shared) {
+        rc = check_fp8(shared->codes, shared->scales, shared->K, shared->N);
+        if (rc != QL_OK) return rc;
+        if (shared->K != W->K || shared->N != W->N) return QL_ERR_INVALID_ARG;
+    }
+    if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
+    const ExpertView v{reinterpret_cast<const uint32_t*>(W->codes), W->scales, nullptr,
+                       shared ? reinterpret_cast<const uint32_t*>(shared->codes) : nullptr,
+                       shared ? shared->scales : nullptr, nullptr,
+                       W->K, W->N, W->num_experts, false, 1};
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr, workspace,
+                        ws_bytes, Y, stream);
 }
 
 size_t moe_decode_workspace_bytes(int32_t T, int32_t E, int32_t topk, int32_t I) {

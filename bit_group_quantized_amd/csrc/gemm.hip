@@ -209,7 +209,8 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     // Two register sets of staged global data: the loads of step i + 2 are
     // issued while step i + 1 (loaded one step earlier) is dequantized into
     // LDS and step i runs on the matrix cores.
-    static_assert(WF == 0 || (MODE == MODE_DENSE && DT == 0), "codec weights: fp16 dense GEMM");
+    static_assert(WF == 0 || (DT == 0 && MODE != MODE_ROUTER && (WF == 1 || MODE == MODE_DENSE)),
+                  "codec weights: fp16 GEMMs (FP8 also in the expert modes)");
     constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : (WF == 1) ? TL::WPT / 2 : TL::WPT / 4;
     constexpr int HREG = (MODE == MODE_ROUTER) ? 8 : 1;
     u32x4 areg[2][TL::A_LOADS];
@@ -718,7 +719,9 @@ static_assert(ShortTile::BM == QL_MOE_TILE_ROWS && TallTile::BM == 2 * QL_MOE_TI
 constexpr size_t kGroupedLds =
     TallTile::LDS_BYTES > ShortTile::LDS_BYTES ? TallTile::LDS_BYTES : ShortTile::LDS_BYTES;
 
-template <int MODE, int DT>
+// WF = 1: FP8 experts (codes [E][N][K] bytes through p.qw, fp16 scales
+// [E][N][K/64] through p.sc, no biases).
+template <int MODE, int DT, int WF = 0>
 __global__ void __launch_bounds__(TallTile::NT)
 gemm_w4_grouped_kernel(const KParams p) {
     extern __shared__ __align__(16) f16 lds[];
@@ -765,15 +768,16 @@ gemm_w4_grouped_kernel(const KParams p) {
         job.rows_valid = min(min(max(tp[2], 1), height), p.T * p.topk);
         job.tile_first = min(max(tp[1], 0), p.T * p.topk - job.rows_valid);
         job.out_row0 = job.tile_first;
-        job.wq = p.qw + (size_t)e * p.N * wpr;
+        // u32 words per expert: N * K / 8 (w4 codes) or N * K / 4 (FP8 bytes)
+        job.wq = p.qw + (size_t)e * p.N * (WF == 1 ? 2 * wpr : wpr);
         job.ws = p.sc + (size_t)e * p.N * G;
-        job.wb = p.bi + (size_t)e * p.N * G;
+        job.wb = (WF == 1) ? nullptr : p.bi + (size_t)e * p.N * G;
     }
     job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
     if (tall)
-        gemm_tile<4, 2, 2, 4, MODE, DT>(p, job, lds);
+        gemm_tile<4, 2, 2, 4, MODE, DT, WF>(p, job, lds);
     else
-        gemm_tile<2, 2, 2, 4, MODE, DT>(p, job, lds);
+        gemm_tile<2, 2, 2, 4, MODE, DT, WF>(p, job, lds);
 }
 
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
@@ -882,12 +886,13 @@ int launch_router_logits_mfma(const uint16_t* H, const uint16_t* Wr, float* part
 }
 
 
-template <int MODE, int DT>
+template <int MODE, int DT, int WF = 0>
 int launch_grouped_t(const KParams& p, dim3 grid, hipStream_t st) {
     static std::atomic<uint32_t> lds_set{0};
-    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_grouped_kernel<MODE, DT>, kGroupedLds, lds_set))
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_grouped_kernel<MODE, DT, WF>, kGroupedLds,
+                                           lds_set))
         return rc;
-    hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE, DT>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
+    hipLaunchKernelGGL((gemm_w4_grouped_kernel<MODE, DT, WF>), grid, dim3(TallTile::NT), kGroupedLds, st, p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -921,6 +926,10 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     if (blocks > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
     if (blocks == 0) return QL_OK;
     const dim3 grid((unsigned)blocks);
+    if (a.wf == 1) {
+        if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 0, 1>(p, grid, st);
+        return launch_grouped_t<MODE_DOWN, 0, 1>(p, grid, st);
+    }
     if (a.bf16) {
         if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 1>(p, grid, st);
         return launch_grouped_t<MODE_DOWN, 1>(p, grid, st);

@@ -153,6 +153,7 @@ struct GroupedArgs {
     uint16_t* Y;
     int K, N, E, T, topk, op;
     bool bf16 = false;  // X, scales, biases and Y hold bf16 patterns
+    int wf = 0;         // 1: FP8 experts (qw = codes as bytes, sc = fp16 scales, no biases)
 };
 bool moe_rows_supported(int K);
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel

@@ -204,6 +204,15 @@ typedef struct ql_fp8 {
     int32_t N;
 } ql_fp8;
 
+/* num_experts FP8 matrices of the same shape stacked contiguously. */
+typedef struct ql_fp8_experts {
+    const uint8_t* codes;    /* [E][N][K], 16-byte aligned */
+    const uint16_t* scales;  /* [E][N][K/64] fp16 */
+    int32_t K;
+    int32_t N;
+    int32_t num_experts;
+} ql_fp8_experts;
+
 typedef struct ql_nvfp4 {
     const uint32_t* qweight;      /* [N][K/8], 16-byte aligned */
     const uint8_t* block_scales;  /* [N][K/16] E4M3, 2-byte aligned */
@@ -463,6 +472,26 @@ int moe_grouped_gemm_bf16(const ql_w4_experts* W, const ql_w4* shared,
 int moe_combine_bf16(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,
                      int32_t T, int32_t topk, int32_t N, int32_t has_shared,
                      uint16_t* out, void* stream);
+
+/*
+ * moe_grouped_gemm_fp8 - moe_grouped_gemm with FP8-E4M3 experts (the
+ * ql_fp8 format of qlinear_gemm_fp8, stacked over experts; "待验证｜lithos-
+ * metal补Apple推理内核", section "一分钟内合并了什么": FP8 weight decode).
+ * Same rows, workspace, tile map and fp16 X / Y as moe_grouped_gemm; each
+ * staged weight is fp16(e4m3(code) * scale), one rounding (scales below
+ * 256), fp32 accumulation on the MFMA tiles, act = SiLU(gate) * up rounded
+ * to fp16.  Serves QL_OP_GATE_UP_SILU and QL_OP_DOWN for every T on the
+ * tiled path (the gates are applied by moe_combine); QL_OP_DOWN_COMBINE
+ * returns UNSUPPORTED_SHAPE.  `shared` (may be NULL) has the shape of one
+ * expert.  Limits: K a positive multiple of 64, K <= QL_MAX_K.
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (codes and X 16-byte,
+ * scales and Y 2-byte aligned), WORKSPACE, HIP.
+ */
+int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared,
+                         const uint16_t* X, int32_t T, int32_t topk, int32_t op,
+                         const int32_t* offsets, const int32_t* sorted_assign,
+                         const void* workspace, size_t ws_bytes,
+                         uint16_t* Y, void* stream);
 
 /*
  * moe_decode - the whole routed-expert layer for a few decode tokens in

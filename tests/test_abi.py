@@ -321,3 +321,30 @@ def test_gemm_nvfp4_validation(L):
     assert call(bs=A16 + 2) == MISALIGNED
     assert call(qw=A16 + 4) == MISALIGNED
     assert call(M=0) == OK
+
+
+def test_grouped_gemm_fp8_validation(L):
+    f = L.moe_grouped_gemm_fp8
+    wsb = L.moe_workspace_bytes(64, 256, 8)
+
+    def call(op=1, T=64, topk=8, K=2048, N=1024, E=256, codes=A16, s=True, sN=1024, wsb=wsb, X=A16):
+        w = ql.ql_fp8_experts(codes, A16, K, N, E)
+        sh = ql.ql_fp8(A16, A16, K, sN)
+        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, A16,
+                 wsb, A16, None)
+
+    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, wsb, A16, None) == INVALID
+    assert call(op=7) == INVALID
+    assert call(op=3) == SHAPE                 # no DOWN_COMBINE for FP8 experts
+    assert call(K=100) == SHAPE
+    assert call(K=65536) == SHAPE
+    assert call(codes=None) == INVALID
+    assert call(codes=A16 + 8) == MISALIGNED
+    assert call(sN=512) == INVALID             # shared shape differs
+    assert call(N=1023, s=False) == SHAPE      # odd gate_up width
+    assert call(topk=300) == INVALID
+    assert call(E=0) == INVALID
+    assert call(wsb=0) == WORKSPACE
+    assert call(X=A16 + 2) == MISALIGNED
+    assert call(X=None) == INVALID
+    assert call(T=0) == OK

@@ -40,7 +40,8 @@ from .decode import rms_norm, gemv_rmsnorm, argmax_first, lm_head_token, embed_r
 from .bf16 import (bf16_to_f64, round_bf16, dequantize_bf16, linear_bf16, expert_ffn_bf16,
                    moe_layer_bf16)
 from .codecs import (e4m3_to_f64, e2m1_to_f64, dequantize_fp8, dequantize_nvfp4, linear_fp8,
-                     linear_nvfp4, expert_ffn_fp8, moe_layer_fp8)
+                     linear_nvfp4, expert_ffn_fp8, moe_layer_fp8, expert_ffn_nvfp4,
+                     moe_layer_nvfp4)
 
 __all__ = [
     "GROUP", "unpack_codes", "pack_codes", "dequantize", "linear", "round_f16",
@@ -51,5 +52,5 @@ __all__ = [
     "bf16_to_f64", "round_bf16", "dequantize_bf16", "linear_bf16", "expert_ffn_bf16",
     "moe_layer_bf16",
     "e4m3_to_f64", "e2m1_to_f64", "dequantize_fp8", "dequantize_nvfp4", "linear_fp8", "linear_nvfp4",
-    "expert_ffn_fp8", "moe_layer_fp8",
+    "expert_ffn_fp8", "moe_layer_fp8", "expert_ffn_nvfp4", "moe_layer_nvfp4",
 ]

@@ -20,10 +20,11 @@ Readings:
 * NVFP4 weights: E2M1 codes packed 8 per uint32 exactly as the w4 codes,
   one E4M3 block scale per 16 consecutive k of one output and one fp32
   scale for the whole matrix: w = e2m1(code) * e4m3(block scale) * global;
-* an FP8 routed-expert layer stores every expert matrix (and the shared
-  expert's) in the FP8 format above, stacked over experts; routing, the
-  gated activation (rounded to fp16), the row order and the combine are
-  those of the w4 layer in oracle.moe.
+* an FP8 (or NVFP4) routed-expert layer stores every expert matrix (and
+  the shared expert's) in that format, stacked over experts, an NVFP4
+  expert with a global scale of its own; routing, the gated activation
+  (rounded to fp16), the row order and the combine are those of the w4
+  layer in oracle.moe.
 """
 from __future__ import annotations
 
@@ -106,26 +107,37 @@ def linear_nvfp4(X, W: dict, row_chunk: int = 8192) -> np.ndarray:
     return Y
 
 
-def expert_ffn_fp8(X, gate_up: dict, down: dict):
-    """One FP8 expert on fp16 rows X [R][D]: u = X @ W_gu,
-    act = fp16(SiLU(u[:, :I]) * u[:, I:]), ydown = act @ W_dn, with both
-    weights dequantized exactly (float64)."""
+def _expert_ffn(X, Wgu, Wdn):
+    """One expert on fp16 rows X [R][D] with exact (float64) weights Wgu
+    [2I][D] and Wdn [D][I]: u = X @ Wgu^T, act = fp16(SiLU(u[:, :I]) * u[:, I:]),
+    ydown = act @ Wdn^T."""
     X = np.asarray(X).astype(np.float64)
-    I = gate_up["N"] // 2
-    u = X @ dequantize_fp8(gate_up["codes"], gate_up["scales"]).T
+    I = Wgu.shape[0] // 2
+    u = X @ Wgu.T
     act = round_f16(silu(u[:, :I]) * u[:, I:])
-    ydown = act.astype(np.float64) @ dequantize_fp8(down["codes"], down["scales"]).T
-    return act, ydown
+    return act, act.astype(np.float64) @ Wdn.T
 
 
-def moe_layer_fp8(H, weights: dict, logit_bias=None, topk: int = 8,
-                  with_shared: bool = True) -> dict:
-    """The routed-expert layer on fp16 tokens H [T][D] with FP8 experts.
+def expert_ffn_fp8(X, gate_up: dict, down: dict):
+    """One FP8 expert (codes, scales) on fp16 rows X."""
+    return _expert_ffn(X, dequantize_fp8(gate_up["codes"], gate_up["scales"]),
+                       dequantize_fp8(down["codes"], down["scales"]))
 
-    ``weights`` holds Wr [D][E] fp16 and gate_up / down / shared_gate_up /
-    shared_down as FP8 dicts (codes, scales; experts stacked on the first
-    axis).  Returns the same intermediates as oracle.moe.moe_layer.
-    """
+
+def expert_ffn_nvfp4(X, gate_up: dict, down: dict):
+    """One NVFP4 expert (qweight, block_scales, global_scale) on fp16 rows X."""
+    return _expert_ffn(X, dequantize_nvfp4(gate_up["qweight"], gate_up["block_scales"],
+                                           gate_up["global_scale"], gate_up["K"]),
+                       dequantize_nvfp4(down["qweight"], down["block_scales"], down["global_scale"],
+                                        down["K"]))
+
+
+def _expert_slice(W: dict, e: int) -> dict:
+    """Expert e of a stacked weight dict (every array indexed on its first axis)."""
+    return {k: (v[e] if isinstance(v, np.ndarray) and v.ndim > 0 else v) for k, v in W.items()}
+
+
+def _moe_layer_codec(H, weights: dict, logit_bias, topk: int, with_shared: bool, ffn) -> dict:
     H = np.asarray(H)
     T = H.shape[0]
     E = weights["Wr"].shape[1]
@@ -146,16 +158,35 @@ def moe_layer_fp8(H, weights: dict, logit_bias=None, topk: int = 8,
         if r1 == r0:
             continue
         tokens = sorted_assign[r0:r1] // topk
-        a, y = expert_ffn_fp8(H[tokens],
-                              {"codes": gu["codes"][e], "scales": gu["scales"][e], "N": gu["N"]},
-                              {"codes": dn["codes"][e], "scales": dn["scales"][e], "N": dn["N"]})
+        a, y = ffn(H[tokens], _expert_slice(gu, e), _expert_slice(dn, e))
         act[r0:r1] = a
         ydown[r0:r1] = y
     if with_shared:
-        a, y = expert_ffn_fp8(H, weights["shared_gate_up"], weights["shared_down"])
+        a, y = ffn(H, weights["shared_gate_up"], weights["shared_down"])
         act[T * topk:] = a
         ydown[T * topk:] = y
     out = combine(ydown, gates, pos, T, topk, with_shared)
     return {"logits": logits, "ids": ids, "gates": gates, "counts": counts,
             "offsets": offsets, "sorted_assign": sorted_assign, "pos": pos,
             "act": act, "ydown": ydown, "out": out}
+
+
+def moe_layer_fp8(H, weights: dict, logit_bias=None, topk: int = 8,
+                  with_shared: bool = True) -> dict:
+    """The routed-expert layer on fp16 tokens H [T][D] with FP8 experts.
+
+    ``weights`` holds Wr [D][E] fp16 and gate_up / down / shared_gate_up /
+    shared_down as FP8 dicts (codes, scales; experts stacked on the first
+    axis).  Returns the same intermediates as oracle.moe.moe_layer.
+    """
+    return _moe_layer_codec(H, weights, logit_bias, topk, with_shared,
+                            lambda X, g, d: expert_ffn_fp8(X, g, d))
+
+
+def moe_layer_nvfp4(H, weights: dict, logit_bias=None, topk: int = 8,
+                    with_shared: bool = True) -> dict:
+    """The routed-expert layer on fp16 tokens H [T][D] with NVFP4 experts
+    (qweight, block_scales stacked on the first axis, global_scale one fp32
+    per expert; the shared expert one NVFP4 matrix)."""
+    return _moe_layer_codec(H, weights, logit_bias, topk, with_shared,
+                            lambda X, g, d: expert_ffn_nvfp4(X, g, d))

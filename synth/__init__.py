@@ -117,14 +117,17 @@ def fp8_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> di
     return {"codes": codes, "scales": scales, "K": K, "N": N}
 
 
-def nvfp4_matrix(rng: np.random.Generator, K: int, N: int) -> dict:
+def nvfp4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
     """NVFP4 weights: qweight uint32 [N][K/8] (E2M1 codes, w4 packing),
-    block scales uint8 [N][K/16] (positive E4M3), global scale fp32."""
-    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
-    e = rng.integers(5, 10, size=(N, K // 16))
-    m = rng.integers(0, 8, size=(N, K // 16))
+    block scales uint8 [N][K/16] (positive E4M3), global scale fp32 (0.01).
+    ``lead`` stacks several matrices; each then draws its own global scale
+    (fp32 array of shape ``lead``, uniform in [0.005, 0.02))."""
+    words = rng.integers(0, 2**32, size=lead + (N, K // 8), dtype=np.uint64).astype(np.uint32)
+    e = rng.integers(5, 10, size=lead + (N, K // 16))
+    m = rng.integers(0, 8, size=lead + (N, K // 16))
     block = ((e << 3) | m).astype(np.uint8)
-    return {"qweight": words, "block_scales": block, "global_scale": np.float32(0.01), "K": K, "N": N}
+    g = np.float32(0.01) if not lead else rng.uniform(0.005, 0.02, size=lead).astype(np.float32)
+    return {"qweight": words, "block_scales": block, "global_scale": g, "K": K, "N": N}
 
 
 def router_weight(rng: np.random.Generator, D: int = HIDDEN, E: int = NUM_EXPERTS) -> np.ndarray:
@@ -220,6 +223,20 @@ def moe_weights_fp8(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = 
     down = fp8_matrix(rng, I, D, lead=(E,))
     shared_gate_up = fp8_matrix(rng, D, 2 * I)
     shared_down = fp8_matrix(rng, I, D)
+    return {"Wr": Wr, "gate_up": gate_up, "down": down,
+            "shared_gate_up": shared_gate_up, "shared_down": shared_down,
+            "D": D, "I": I, "E": E}
+
+
+def moe_weights_nvfp4(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:
+    """moe_weights with NVFP4 experts (nvfp4_matrix draws, one global scale
+    per expert).  The fp16 router weight is drawn first, as in moe_weights."""
+    rng = rng_for(seed)
+    Wr = router_weight(rng, D, E)
+    gate_up = nvfp4_matrix(rng, D, 2 * I, lead=(E,))
+    down = nvfp4_matrix(rng, I, D, lead=(E,))
+    shared_gate_up = nvfp4_matrix(rng, D, 2 * I)
+    shared_down = nvfp4_matrix(rng, I, D)
     return {"Wr": Wr, "gate_up": gate_up, "down": down,
             "shared_gate_up": shared_gate_up, "shared_down": shared_down,
             "D": D, "I": I, "E": E}

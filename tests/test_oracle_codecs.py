@@ -199,3 +199,61 @@ def test_moe_fp8_token_loop_bruteforce():
                  w["shared_down"]["codes"], w["shared_down"]["scales"])
         acc = [a + v for a, v in zip(acc, ys)]
         np.testing.assert_allclose(ref["out"][tok], acc, rtol=1e-9, atol=1e-9)
+
+
+# E4M3 codes of the eight E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+_E4M3_OF_E2M1 = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C], np.uint8)
+
+
+def _nvfp4_as_fp8(W, K):
+    """An NVFP4 matrix (stack) whose block scales are equal within each 64
+    along K and whose e4m3(block) * global is an fp16 value, rewritten as
+    FP8: e2m1(code) is an E4M3 value, the scale the same fp16 number."""
+    q = oracle.unpack_codes(W["qweight"], K).astype(np.int64)
+    codes = _E4M3_OF_E2M1[q & 7] | np.where(q & 8, 0x80, 0).astype(np.uint8)
+    g = np.asarray(W["global_scale"], np.float64)[..., None, None]
+    s = oracle.e4m3_to_f64(W["block_scales"][..., ::4]) * g
+    assert np.array_equal(s, s.astype(np.float16).astype(np.float64))
+    return {"codes": codes.astype(np.uint8), "scales": s.astype(np.float16), "K": K, "N": W["N"]}
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_moe_nvfp4_equals_fp8_layer_on_common_weights(shared):
+    """NVFP4 weights that the FP8 format holds exactly (block scales constant
+    over each 64, global scales powers of two): the NVFP4 layer must
+    reproduce the FP8 layer, itself pinned to the w4 layer, exactly."""
+    import synth
+    w = synth.moe_weights_nvfp4(15, D=128, I=64, E=8)
+    for key in ("gate_up", "down", "shared_gate_up", "shared_down"):
+        W = w[key]
+        W["block_scales"] = np.repeat(W["block_scales"][..., ::4], 4, axis=-1)
+        W["global_scale"] = (np.float32(2.0 ** -7) if np.ndim(W["global_scale"]) == 0 else
+                             np.exp2(-np.arange(W["global_scale"].size) % 3 - 6).astype(np.float32))
+    f8 = {k: (_nvfp4_as_fp8(v, v["K"]) if isinstance(v, dict) else v) for k, v in w.items()}
+    H = synth.activations(synth.rng_for(16), 29, 128)
+    a = oracle.moe_layer_nvfp4(H, w, None, 3, with_shared=shared)
+    b = oracle.moe_layer_fp8(H, f8, None, 3, with_shared=shared)
+    for key in ("ids", "counts", "offsets", "sorted_assign", "pos"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["act"].view(np.uint16), b["act"].view(np.uint16))
+    assert np.array_equal(a["ydown"], b["ydown"]) and np.array_equal(a["out"], b["out"])
+
+
+def test_moe_nvfp4_per_expert_global_scale():
+    """Each expert's global scale multiplies only its own rows: doubling the
+    down projection's global scale of one expert doubles exactly the ydown
+    rows routed to that expert and leaves every other row unchanged."""
+    import synth
+    w = synth.moe_weights_nvfp4(17, D=128, I=64, E=8)
+    H = synth.activations(synth.rng_for(18), 40, 128)
+    a = oracle.moe_layer_nvfp4(H, w, None, 2)
+    e = int(np.argmax(a["counts"]))
+    w["down"]["global_scale"] = w["down"]["global_scale"].copy()
+    w["down"]["global_scale"][e] *= 2
+    b = oracle.moe_layer_nvfp4(H, w, None, 2)
+    r0, r1 = int(a["offsets"][e]), int(a["offsets"][e + 1])
+    assert r1 > r0
+    assert np.array_equal(b["ydown"][r0:r1], 2 * a["ydown"][r0:r1])
+    mask = np.ones(a["ydown"].shape[0], bool)
+    mask[r0:r1] = False
+    assert np.array_equal(b["ydown"][mask], a["ydown"][mask])

@@ -384,3 +384,31 @@ def _fp8_combine_no_shared(ydown, gates, pos, T, topk, has_shared):
 def test_fp8_moe_mutants_are_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(ocod, attr, mutant)
     assert _fails(FP8_MOE_PINS)
+
+
+NVFP4_MOE_PINS = [lambda: tcod.test_moe_nvfp4_equals_fp8_layer_on_common_weights(True),
+                  tcod.test_moe_nvfp4_per_expert_global_scale]
+_ORIG_SLICE = ocod._expert_slice
+_ORIG_FFN_NVFP4 = ocod.expert_ffn_nvfp4
+
+
+def _slice_first_global(W, e):
+    out = _ORIG_SLICE(W, e)
+    if "global_scale" in W:
+        out["global_scale"] = np.asarray(W["global_scale"]).ravel()[0]
+    return out
+
+
+def _ffn_nvfp4_globals_swapped(X, gate_up, down):
+    g, d = dict(gate_up), dict(down)
+    g["global_scale"], d["global_scale"] = down["global_scale"], gate_up["global_scale"]
+    return _ORIG_FFN_NVFP4(X, g, d)
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("_expert_slice", _slice_first_global),
+    ("expert_ffn_nvfp4", _ffn_nvfp4_globals_swapped),
+])
+def test_nvfp4_moe_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(ocod, attr, mutant)
+    assert _fails(NVFP4_MOE_PINS)

@@ -16,7 +16,7 @@ prefill GEMM (M = 4096, K = 2048, N = 8192 and the M sweep), the few-row
 GEMM, the bf16 variant, the FP8 / NVFP4 codecs, the decode fusions, the
 decode MoE layer (one token, 8 of 256 experts + shared; moe_decode and the
 three-call path) and the prefill MoE layer (4096 tokens, Zipf-skewed expert
-loads; w4, bf16 and FP8 experts).
+loads; w4, bf16, FP8 and NVFP4 experts).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-primary]
 """
@@ -715,21 +715,27 @@ def bench_moe_prefill_bf16(args, dev):
             "seed": 4}
 
 
-def bench_moe_prefill_fp8(args, dev):
-    """The same 4096-token layer with FP8-E4M3 experts (moe_route /
-    moe_grouped_gemm_fp8 / moe_combine; fp16 tokens and outputs)."""
+def bench_moe_prefill_codec(args, dev, codec: str):
+    """The same 4096-token layer with FP8-E4M3 or NVFP4 experts (moe_route /
+    moe_grouped_gemm_fp8 or _nvfp4 / moe_combine; fp16 tokens and outputs)."""
     import torch
     import bit_group_quantized_amd as ql
     import synth
     T = 4096
     seeds = json.load(open(os.path.join(ROOT, "tests", "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
-    w = synth.moe_weights_fp8(0)
+    w = synth.moe_weights_fp8(0) if codec == "fp8" else synth.moe_weights_nvfp4(0)
     tok = synth.moe_tokens(seeds[0], T, skewed=True)
-    wd = lambda W: {"codes": torch.from_numpy(np.ascontiguousarray(W["codes"])).to(dev),
-                    "scales": torch.from_numpy(np.ascontiguousarray(W["scales"])).to(dev),
-                    "K": W["K"], "N": W["N"]}
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def wd(W):
+        d = {k: (to_dev(v) if isinstance(v, np.ndarray) and v.ndim > 0 else v) for k, v in W.items()}
+        if "global_scale" in d and not torch.is_tensor(d["global_scale"]):
+            d["global_scale"] = float(d["global_scale"])
+        return d
+
     dw = {k: wd(w[k]) for k in ("gate_up", "down", "shared_gate_up", "shared_down")}
-    Wr, H = torch.from_numpy(w["Wr"]).to(dev), torch.from_numpy(tok["H"]).to(dev)
+    gemm = ql.moe_grouped_gemm_fp8 if codec == "fp8" else ql.moe_grouped_gemm_nvfp4
+    Wr, H = to_dev(w["Wr"]), to_dev(tok["H"])
     bias = torch.from_numpy(tok["logit_bias"]).to(dev)
     route = ql.alloc_route_outputs(T, 256, 8, dev)
     act = torch.empty((9 * T, 512), dtype=torch.float16, device=dev)
@@ -740,11 +746,10 @@ def bench_moe_prefill_fp8(args, dev):
         ql.moe_route(H, Wr, bias, 8, route)
 
     def gu(i):
-        ql.moe_grouped_gemm_fp8(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU,
-                                route, act)
+        gemm(dw["gate_up"], dw["shared_gate_up"], H, T, 8, ql.QL_OP_GATE_UP_SILU, route, act)
 
     def dn(i):
-        ql.moe_grouped_gemm_fp8(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
+        gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN, route, yd)
 
     def cb(i):
         ql.moe_combine(yd, route["gates"], route["pos"], T, 8, True, out)
@@ -923,7 +928,9 @@ def main():
                 log("bench: MoE prefill, bf16")
                 wl["moe_prefill_4096tok_bf16"] = bench_moe_prefill_bf16(args, dev)
                 log("bench: MoE prefill, FP8 experts")
-                wl["moe_prefill_4096tok_fp8"] = bench_moe_prefill_fp8(args, dev)
+                wl["moe_prefill_4096tok_fp8"] = bench_moe_prefill_codec(args, dev, "fp8")
+                log("bench: MoE prefill, NVFP4 experts")
+                wl["moe_prefill_4096tok_nvfp4"] = bench_moe_prefill_codec(args, dev, "nvfp4")
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline()

@@ -62,6 +62,12 @@ class ql_nvfp4(ctypes.Structure):
                 ("global_scale", ctypes.c_float), ("K", ctypes.c_int32), ("N", ctypes.c_int32)]
 
 
+class ql_nvfp4_experts(ctypes.Structure):
+    _fields_ = [("qweight", ctypes.c_void_p), ("block_scales", ctypes.c_void_p),
+                ("global_scales", ctypes.c_void_p), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _SIGS = {
@@ -97,6 +103,8 @@ _SIGS = {
     "moe_combine_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8_experts), ctypes.POINTER(ql_fp8), _P,
                                             _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+    "moe_grouped_gemm_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4_experts), ctypes.POINTER(ql_nvfp4),
+                                              _P, _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "moe_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_decode_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
@@ -439,6 +447,30 @@ def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op:
         Y = torch.empty(shape, dtype=torch.float16, device=X.device)
     ws = route["workspace"]
     _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
+        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
+        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
+        _stream(stream)))
+    return Y
+
+
+def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
+                           Y=None, stream=None):
+    """moe_grouped_gemm with NVFP4 experts: W holds qweight [E][N][K/8],
+    block_scales uint8 [E][N][K/16] and global_scale fp32 [E] (device
+    tensors), shared one NVFP4 matrix (global_scale a float) or None."""
+    import torch
+    qw = W["qweight"]
+    w = ql_nvfp4_experts(qw.data_ptr(), W["block_scales"].data_ptr(), W["global_scale"].data_ptr(),
+                         int(W["K"]), int(W["N"]), int(qw.shape[0]))
+    s = (ql_nvfp4(shared["qweight"].data_ptr(), shared["block_scales"].data_ptr(),
+                  float(shared["global_scale"]), int(shared["K"]), int(shared["N"]))
+         if shared is not None else None)
+    rows = T * topk + (T if shared is not None else 0)
+    if Y is None:
+        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        Y = torch.empty(shape, dtype=torch.float16, device=X.device)
+    ws = route["workspace"]
+    _check("moe_grouped_gemm_nvfp4", lib().moe_grouped_gemm_nvfp4(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
         _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
         _stream(stream)))

@@ -314,7 +314,9 @@ struct ExpertView {
     const uint16_t* sbi;
     int32_t K, N, E;
     bool bf16;
-    int wf;  // 0 = w4, 1 = FP8
+    int wf;  // 0 = w4, 1 = FP8, 2 = NVFP4
+    const float* gscales = nullptr;  // NVFP4: per-expert global scales (device)
+    float sgscale = 0.f;             // NVFP4: the shared expert's global scale
 };
 
 static int w4_view(const ql_w4_experts* W, const ql_w4* shared, bool bf16, ExpertView& v) {
@@ -375,7 +377,7 @@ static int grouped_impl(const ExpertView& w, const uint16_t* X, int32_t T, int32
     ql::GroupedArgs a{w.qw, w.sc, w.bi, w.sqw, w.ssc, w.sbi,
                       X, offsets, sorted_assign, topk_gates, assign_pos,
                       static_cast<const unsigned char*>(workspace), Y,
-                      w.K, w.N, E, T, topk, op, w.bf16, w.wf};
+                      w.K, w.N, E, T, topk, op, w.bf16, w.wf, w.gscales, w.sgscale};
     if (rows_path) return ql::launch_moe_rows(a, as_stream(stream));
     return ql::launch_moe_grouped(a, as_stream(stream));
 }
@@ -419,6 +421,36 @@ int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared, const ui
                        shared ? reinterpret_cast<const uint32_t*>(shared->codes) : nullptr,
                        shared ? shared->scales : nullptr, nullptr,
                        W->K, W->N, W->num_experts, false, 1};
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr, workspace,
+                        ws_bytes, Y, stream);
+}
+
+int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared, const uint16_t* X,
+                           int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
+                           const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
+                           uint16_t* Y, void* stream) {
+    if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
+    if (W->K == 0 || W->K % QL_GROUP_SIZE != 0 || W->K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N > 0) {
+        if (!W->qweight || !W->block_scales || !W->global_scales) return QL_ERR_INVALID_ARG;
+        if (!aligned(W->qweight, 16) || !aligned(W->block_scales, 4) || !aligned(W->global_scales, 4))
+            return QL_ERR_MISALIGNED;
+    }
+    if (shared) {
+        if (shared->K != W->K || shared->N != W->N) return QL_ERR_INVALID_ARG;
+        if (!std::isfinite(shared->global_scale)) return QL_ERR_INVALID_ARG;
+        if (W->N > 0) {
+            if (!shared->qweight || !shared->block_scales) return QL_ERR_INVALID_ARG;
+            if (!aligned(shared->qweight, 16) || !aligned(shared->block_scales, 4)) return QL_ERR_MISALIGNED;
+        }
+    }
+    if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
+    ExpertView v{W->qweight, reinterpret_cast<const uint16_t*>(W->block_scales), nullptr,
+                 shared ? shared->qweight : nullptr,
+                 shared ? reinterpret_cast<const uint16_t*>(shared->block_scales) : nullptr, nullptr,
+                 W->K, W->N, W->num_experts, false, 2};
+    v.gscales = W->global_scales;
+    v.sgscale = shared ? shared->global_scale : 0.f;
     return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr, workspace,
                         ws_bytes, Y, stream);
 }

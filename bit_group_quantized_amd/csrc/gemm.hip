@@ -73,7 +73,8 @@ struct KParams {
     float* Yf;
     int K, N;
     int ksplit;  // router: number of K splits
-    float gscale;  // NVFP4 weights: global scale
+    float gscale;           // NVFP4 weights: global scale (dense GEMM, shared expert)
+    const float* gscales;   // NVFP4 experts: one global scale per expert (device)
     int grid_n, grid_m;  // dense: tile grid; grouped: N blocks (grid_n), shared tiles (grid_m)
 };
 
@@ -124,6 +125,7 @@ struct Job {
     const uint32_t* wq;
     const uint16_t* ws;
     const uint16_t* wb;
+    float gscale;     // NVFP4: global scale of this tile's matrix
 };
 
 // DT: 0 = fp16 activations, scales, biases, outputs and MFMA operands;
@@ -133,7 +135,7 @@ struct Job {
 // 1 = FP8-E4M3 codes [N][K] (bytes, through p.qw) with an fp16 scale per 64
 // along K and no bias, staged as fp16(e4m3 * scale), one rounding;
 // 2 = NVFP4: E2M1 codes in the w4 packing, E4M3 block scales [N][K/16]
-// (bytes, through p.sc) and the global p.gscale, staged as
+// (bytes, through p.sc) and the matrix's global scale job.gscale, staged as
 // fp16(e2m1 * fp16(e4m3 * global)).
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
@@ -209,8 +211,7 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     // Two register sets of staged global data: the loads of step i + 2 are
     // issued while step i + 1 (loaded one step earlier) is dequantized into
     // LDS and step i runs on the matrix cores.
-    static_assert(WF == 0 || (DT == 0 && MODE != MODE_ROUTER && (WF == 1 || MODE == MODE_DENSE)),
-                  "codec weights: fp16 GEMMs (FP8 also in the expert modes)");
+    static_assert(WF == 0 || (DT == 0 && MODE != MODE_ROUTER), "codec weights: fp16 GEMMs");
     constexpr int BREG = (MODE == MODE_ROUTER) ? 1 : (WF == 1) ? TL::WPT / 2 : TL::WPT / 4;
     constexpr int HREG = (MODE == MODE_ROUTER) ? 8 : 1;
     u32x4 areg[2][TL::A_LOADS];
@@ -308,7 +309,7 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
 #pragma unroll
             for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
                 const int word = bpart * W + w;  // 0..7 within the step: block word / 2
-                const f16 sc = (f16)(e4m3_to_f32((nreg[S] >> (8 * (word >> 1))) & 0xFFu) * p.gscale);
+                const f16 sc = (f16)(e4m3_to_f32((nreg[S] >> (8 * (word >> 1))) & 0xFFu) * job.gscale);
                 const f16x2 s2 = {sc, sc};
                 uint32_t q[4];
                 e2m1x8_to_f16x2(breg[S][w >> 2][w & 3], q);
@@ -677,6 +678,7 @@ gemm_w4_kernel(const KParams p) {
     Job job{};
     job.kbeg = 0;
     job.kend = G;
+    job.gscale = p.gscale;
     job.wq = p.qw;
     job.ws = p.sc;
     job.wb = p.bi;
@@ -720,7 +722,9 @@ constexpr size_t kGroupedLds =
     TallTile::LDS_BYTES > ShortTile::LDS_BYTES ? TallTile::LDS_BYTES : ShortTile::LDS_BYTES;
 
 // WF = 1: FP8 experts (codes [E][N][K] bytes through p.qw, fp16 scales
-// [E][N][K/64] through p.sc, no biases).
+// [E][N][K/64] through p.sc, no biases); WF = 2: NVFP4 experts (codes as the
+// w4 words, E4M3 block scales [E][N][K/16] bytes through p.sc, global
+// scales p.gscales[E]; the shared expert's is p.gscale).
 template <int MODE, int DT, int WF = 0>
 __global__ void __launch_bounds__(TallTile::NT)
 gemm_w4_grouped_kernel(const KParams p) {
@@ -761,6 +765,7 @@ gemm_w4_grouped_kernel(const KParams p) {
         job.wq = p.sqw;
         job.ws = p.ssc;
         job.wb = p.sbi;
+        job.gscale = p.gscale;
     } else {
         const int* tp = p.tiles + (size_t)tslot * 4;
         // Clamped so that a corrupted tile map can never index out of bounds.
@@ -768,10 +773,13 @@ gemm_w4_grouped_kernel(const KParams p) {
         job.rows_valid = min(min(max(tp[2], 1), height), p.T * p.topk);
         job.tile_first = min(max(tp[1], 0), p.T * p.topk - job.rows_valid);
         job.out_row0 = job.tile_first;
-        // u32 words per expert: N * K / 8 (w4 codes) or N * K / 4 (FP8 bytes)
+        // u32 words per expert: N * K / 8 (w4 and NVFP4 codes) or N * K / 4
+        // (FP8 bytes); 16-bit words of scales: N * K / 64, or N * K / 32 for
+        // the NVFP4 block-scale bytes
         job.wq = p.qw + (size_t)e * p.N * (WF == 1 ? 2 * wpr : wpr);
-        job.ws = p.sc + (size_t)e * p.N * G;
-        job.wb = (WF == 1) ? nullptr : p.bi + (size_t)e * p.N * G;
+        job.ws = p.sc + (size_t)e * p.N * (WF == 2 ? 2 * G : G);
+        job.wb = (WF == 0) ? p.bi + (size_t)e * p.N * G : nullptr;
+        if constexpr (WF == 2) job.gscale = p.gscales[e];
     }
     job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
     if (tall)
@@ -929,6 +937,12 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     if (a.wf == 1) {
         if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 0, 1>(p, grid, st);
         return launch_grouped_t<MODE_DOWN, 0, 1>(p, grid, st);
+    }
+    if (a.wf == 2) {
+        p.gscales = a.gscales;
+        p.gscale = a.sgscale;
+        if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 0, 2>(p, grid, st);
+        return launch_grouped_t<MODE_DOWN, 0, 2>(p, grid, st);
     }
     if (a.bf16) {
         if (a.op == QL_OP_GATE_UP_SILU) return launch_grouped_t<MODE_GATEUP, 1>(p, grid, st);

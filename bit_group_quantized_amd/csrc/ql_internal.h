@@ -154,6 +154,9 @@ struct GroupedArgs {
     int K, N, E, T, topk, op;
     bool bf16 = false;  // X, scales, biases and Y hold bf16 patterns
     int wf = 0;         // 1: FP8 experts (qw = codes as bytes, sc = fp16 scales, no biases)
+                        // 2: NVFP4 experts (qw = codes, sc = E4M3 block-scale bytes, no biases)
+    const float* gscales = nullptr;  // NVFP4: per-expert global scales (device, [E])
+    float sgscale = 0.f;             // NVFP4: the shared expert's global scale
 };
 bool moe_rows_supported(int K);
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel

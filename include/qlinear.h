@@ -221,6 +221,17 @@ typedef struct ql_nvfp4 {
     int32_t N;
 } ql_nvfp4;
 
+/* num_experts NVFP4 matrices of the same shape stacked contiguously, each
+ * with a global scale of its own. */
+typedef struct ql_nvfp4_experts {
+    const uint32_t* qweight;       /* [E][N][K/8], 16-byte aligned */
+    const uint8_t* block_scales;   /* [E][N][K/16] E4M3, 4-byte aligned */
+    const float* global_scales;    /* [E] fp32 in device memory, finite */
+    int32_t K;
+    int32_t N;
+    int32_t num_experts;
+} ql_nvfp4_experts;
+
 /*
  * qlinear_gemv_fp8, qlinear_gemv_nvfp4 - y fp16 [N] = x fp16 [K] . W for
  * one activation row.  Codes are decoded by exact bit moves into fp16 (the
@@ -492,6 +503,26 @@ int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared,
                          const int32_t* offsets, const int32_t* sorted_assign,
                          const void* workspace, size_t ws_bytes,
                          uint16_t* Y, void* stream);
+
+/*
+ * moe_grouped_gemm_nvfp4 - moe_grouped_gemm with NVFP4 experts (the
+ * ql_nvfp4 format of qlinear_gemm_nvfp4, stacked over experts, a global
+ * scale per expert read from device memory; the same page and section as
+ * the FP8 call).  Same rows, workspace, tile map, fp16 X / Y and ops as
+ * moe_grouped_gemm_fp8; each staged weight is fp16(e2m1 * fp16(e4m3(block
+ * scale) * global scale)) as in qlinear_gemm_nvfp4.  `shared` (may be NULL;
+ * host global_scale, finite) has the shape of one expert.
+ * Limits: K a positive multiple of 64, K <= QL_MAX_K.
+ * Errors: INVALID_ARG (incl. a non-finite shared global scale),
+ * UNSUPPORTED_SHAPE (incl. QL_OP_DOWN_COMBINE), MISALIGNED (qweight and X
+ * 16-byte, block_scales and global_scales 4-byte, Y 2-byte aligned),
+ * WORKSPACE, HIP.
+ */
+int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared,
+                           const uint16_t* X, int32_t T, int32_t topk, int32_t op,
+                           const int32_t* offsets, const int32_t* sorted_assign,
+                           const void* workspace, size_t ws_bytes,
+                           uint16_t* Y, void* stream);
 
 /*
  * moe_decode - the whole routed-expert layer for a few decode tokens in

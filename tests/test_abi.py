@@ -348,3 +348,33 @@ def test_grouped_gemm_fp8_validation(L):
     assert call(X=A16 + 2) == MISALIGNED
     assert call(X=None) == INVALID
     assert call(T=0) == OK
+
+
+def test_grouped_gemm_nvfp4_validation(L):
+    f = L.moe_grouped_gemm_nvfp4
+    wsb = L.moe_workspace_bytes(64, 256, 8)
+
+    def call(op=1, T=64, topk=8, K=2048, N=1024, E=256, qw=A16, bs=A16, gs=A16, s=True, sN=1024,
+             sg=1.0, wsb=wsb, X=A16):
+        w = ql.ql_nvfp4_experts(qw, bs, gs, K, N, E)
+        sh = ql.ql_nvfp4(A16, A16, sg, K, sN)
+        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, A16,
+                 wsb, A16, None)
+
+    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, wsb, A16, None) == INVALID
+    assert call(op=7) == INVALID
+    assert call(op=3) == SHAPE
+    assert call(K=96) == SHAPE
+    assert call(qw=None) == INVALID
+    assert call(gs=None) == INVALID
+    assert call(qw=A16 + 8) == MISALIGNED
+    assert call(bs=A16 + 2) == MISALIGNED
+    assert call(gs=A16 + 2) == MISALIGNED
+    assert call(sN=512) == INVALID
+    assert call(sg=float("nan")) == INVALID
+    assert call(sg=float("inf")) == INVALID
+    assert call(N=1023, s=False) == SHAPE
+    assert call(topk=300) == INVALID
+    assert call(wsb=0) == WORKSPACE
+    assert call(X=A16 + 2) == MISALIGNED
+    assert call(T=0) == OK

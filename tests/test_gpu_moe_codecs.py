@@ -1,6 +1,7 @@
-"""GPU parity of the routed-expert layer with FP8-E4M3 experts (moe_route,
-moe_grouped_gemm_fp8 for gate/up and down, moe_combine) against the
-oracle's FP8 layer, with the fp16 bars of tests/gpu_util.py."""
+"""GPU parity of the routed-expert layer with FP8-E4M3 or NVFP4 experts
+(moe_route, moe_grouped_gemm_fp8 / moe_grouped_gemm_nvfp4 for gate/up and
+down, moe_combine) against the oracle's codec layers, with the fp16 bars of
+tests/gpu_util.py."""
 import numpy as np
 import pytest
 
@@ -22,12 +23,25 @@ def _dev_weights(w):
             "shared_gate_up": _fp8_dev(w["shared_gate_up"]), "shared_down": _fp8_dev(w["shared_down"])}
 
 
-def _run(dw, H, bias, topk, T, shared=True):
+def _nvfp4_dev(W):
+    import torch
+    g = W["global_scale"]
+    g = torch.from_numpy(np.ascontiguousarray(g)).cuda() if np.ndim(g) else float(g)
+    return {"qweight": t(W["qweight"]), "block_scales": t(W["block_scales"]), "global_scale": g,
+            "K": int(W["K"]), "N": int(W["N"])}
+
+
+def _dev_weights_nvfp4(w):
+    return {"Wr": t(w["Wr"]), "gate_up": _nvfp4_dev(w["gate_up"]), "down": _nvfp4_dev(w["down"]),
+            "shared_gate_up": _nvfp4_dev(w["shared_gate_up"]), "shared_down": _nvfp4_dev(w["shared_down"])}
+
+
+def _run(dw, H, bias, topk, T, shared=True, gemm=None):
+    gemm = gemm or ql.moe_grouped_gemm_fp8
     route = ql.moe_route(H, dw["Wr"], bias, topk)
-    act = ql.moe_grouped_gemm_fp8(dw["gate_up"], dw["shared_gate_up"] if shared else None, H, T, topk,
-                                  ql.QL_OP_GATE_UP_SILU, route)
-    ydown = ql.moe_grouped_gemm_fp8(dw["down"], dw["shared_down"] if shared else None, act, T, topk,
-                                    ql.QL_OP_DOWN, route)
+    act = gemm(dw["gate_up"], dw["shared_gate_up"] if shared else None, H, T, topk,
+               ql.QL_OP_GATE_UP_SILU, route)
+    ydown = gemm(dw["down"], dw["shared_down"] if shared else None, act, T, topk, ql.QL_OP_DOWN, route)
     out = ql.moe_combine(ydown, route["gates"], route["pos"], T, topk, shared)
     return route, act, ydown, out
 
@@ -140,3 +154,75 @@ def test_moe_fp8_down_combine_is_rejected():
     with pytest.raises(ql.QLError):
         ql.moe_grouped_gemm_fp8(dw["down"], None, t(np.zeros((4, 64), np.float16)), 2, 2,
                                 ql.QL_OP_DOWN_COMBINE, route)
+
+
+@pytest.mark.parametrize("seed", SCREENED[:1])
+def test_moe_nvfp4_prefill_4096(seed):
+    """The prefill workload with NVFP4 experts (a global scale per expert)."""
+    import torch
+    say(f"moe nvfp4 prefill T=4096 seed={seed}")
+    w = synth.moe_weights_nvfp4(0)
+    tok = synth.moe_tokens(seed, 4096, skewed=True)
+    ref = oracle.moe_layer_nvfp4(tok["H"], w, tok["logit_bias"], 8)
+    res = _run(_dev_weights_nvfp4(w), t(tok["H"]), t(tok["logit_bias"]), 8, 4096,
+               gemm=ql.moe_grouped_gemm_nvfp4)
+    torch.cuda.synchronize()
+    _check_routing(res[0], ref)
+    rel, mx = _compare(*res, ref, 4096, 8)
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
+    (1, 2048, 512, 256, 8, 0, True),
+    (300, 256, 128, 16, 4, 3, True),
+    (700, 512, 256, 64, 8, 7, True),
+    (200, 256, 64, 33, 5, 5, False),
+    (70, 4096, 192, 8, 2, 6, True),
+])
+def test_moe_nvfp4_shapes(T, D, I, E, topk, seed, shared):
+    import torch
+    from tests.gpu_util import assert_close
+    say(f"moe nvfp4 T={T} D={D} I={I} E={E} topk={topk} shared={shared}")
+    w = synth.moe_weights_nvfp4(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 90, T, D=D, E=E, skewed=True)
+    ref = oracle.moe_layer_nvfp4(tok["H"], w, tok["logit_bias"], topk, with_shared=shared)
+    srt = -np.sort(-ref["logits"], axis=1)
+    assert (srt[:, topk - 1] - srt[:, topk]).min() > 5e-5, "case not screened"
+    res = _run(_dev_weights_nvfp4(w), t(tok["H"]), t(tok["logit_bias"]), topk, T, shared,
+               gemm=ql.moe_grouped_gemm_nvfp4)
+    torch.cuda.synchronize()
+    _check_routing(res[0], ref)
+    assert_close(host(res[1]).astype(np.float64), ref["act"].astype(np.float64), "act")
+    assert_close(host(res[2]).astype(np.float64), ref["ydown"], "ydown")
+    rel, mx = assert_close(host(res[3]).astype(np.float64), ref["out"], "out")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_moe_nvfp4_and_fp8_bit_identical_on_common_weights():
+    """NVFP4 experts whose weights the FP8 format holds exactly (block scales
+    constant over each 64, power-of-two global scales): both kernels stage
+    the same fp16 weights, so act and ydown agree bit for bit."""
+    import torch
+    T, D, I, E, topk = 500, 512, 128, 16, 4
+    w = synth.moe_weights_nvfp4(21, D=D, I=I, E=E)
+    E4M3_OF_E2M1 = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C], np.uint8)
+    f8 = {"Wr": w["Wr"]}
+    for key in ("gate_up", "down", "shared_gate_up", "shared_down"):
+        W = w[key]
+        W["block_scales"] = np.repeat(W["block_scales"][..., ::4], 4, axis=-1)
+        stacked = np.ndim(W["global_scale"]) > 0
+        W["global_scale"] = (np.exp2(-(np.arange(E) % 3) - 6).astype(np.float32) if stacked
+                             else np.float32(2.0 ** -7))
+        q = oracle.unpack_codes(W["qweight"], W["K"]).astype(np.int64)
+        codes = (E4M3_OF_E2M1[q & 7] | np.where(q & 8, 0x80, 0)).astype(np.uint8)
+        g = np.asarray(W["global_scale"], np.float64)
+        g = g[:, None, None] if stacked else g
+        scales = (oracle.e4m3_to_f64(W["block_scales"][..., ::4]) * g).astype(np.float16)
+        f8[key] = {"codes": codes, "scales": scales, "K": W["K"], "N": W["N"]}
+    tok = synth.moe_tokens(22, T, D=D, E=E, skewed=True)
+    a = _run(_dev_weights_nvfp4(w), t(tok["H"]), t(tok["logit_bias"]), topk, T,
+             gemm=ql.moe_grouped_gemm_nvfp4)
+    b = _run(_dev_weights(f8), t(tok["H"]), t(tok["logit_bias"]), topk, T)
+    torch.cuda.synchronize()
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(host(x).view(np.uint16), host(y).view(np.uint16))

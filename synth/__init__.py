@@ -111,8 +111,8 @@ def gemm_case_bf16(seed: int, M: int, K: int, N: int) -> dict:
 def fp8_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
     """FP8-E4M3 weights: codes uint8 [N][K] (no NaN codes), fp16 scales [N][K/64];
     ``lead`` stacks several such matrices (e.g. (E,) for E experts)."""
-    codes = rng.integers(0, 254, size=lead + (N, K), dtype=np.int64)
-    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)   # skip 0x7F (and 0xFF)
+    codes = rng.integers(0, 254, size=lead + (N, K), dtype=np.uint8)
+    codes += codes >= 0x7F                                              # skip 0x7F (and 0xFF)
     scales = f16(rng.uniform(1e-4, 1e-3, size=lead + (N, K // 64)))
     return {"codes": codes, "scales": scales, "K": K, "N": N}
 

@@ -80,3 +80,46 @@ def test_random_moe_layer(i):
     assert np.array_equal(host(route["ids"]), ref["ids"])
     assert np.array_equal(host(route["sorted_assign"]), ref["sorted_assign"])
     assert_close(host(out).astype(np.float64), ref["out"], "moe out")
+
+
+def _codec_dev(W):
+    import torch
+    d = {k: (t(v) if isinstance(v, np.ndarray) and v.ndim > 0 else v) for k, v in W.items()}
+    if "global_scale" in d and not torch.is_tensor(d["global_scale"]):
+        d["global_scale"] = float(d["global_scale"])
+    return d
+
+
+@pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("i", range(len(MOE_SHAPES)))
+def test_random_moe_layer_codecs(i, codec):
+    """The same call sequence with FP8 or NVFP4 experts (moe_grouped_gemm_fp8
+    / _nvfp4); the router weight equals moe_weights(seed)'s, so the seed
+    screening is the w4 layer's."""
+    import torch
+    T, D, I, E, topk = MOE_SHAPES[i]
+    topk = min(topk, E)
+    for seed in range(400 + 100 * i, 400 + 100 * i + 50):
+        tok = synth.moe_tokens(seed + 1, T, D=D, E=E, skewed=True)
+        L = oracle.router_logits(tok["H"], synth.router_weight(synth.rng_for(seed), D, E), tok["logit_bias"])
+        srt = -np.sort(-L, axis=1)
+        if topk == E or (srt[:, topk - 1] - srt[:, topk]).min() > 1e-4:
+            break
+    else:
+        pytest.skip("no screened seed in 50 tries")
+    say(f"random moe {codec} T={T} D={D} I={I} E={E} topk={topk} seed={seed}")
+    if codec == "fp8":
+        w, layer, gemm = synth.moe_weights_fp8(seed, D=D, I=I, E=E), oracle.moe_layer_fp8, ql.moe_grouped_gemm_fp8
+    else:
+        w, layer, gemm = synth.moe_weights_nvfp4(seed, D=D, I=I, E=E), oracle.moe_layer_nvfp4, ql.moe_grouped_gemm_nvfp4
+    ref = layer(tok["H"], w, tok["logit_bias"], topk)
+    H = t(tok["H"])
+    dw = {k: _codec_dev(w[k]) for k in ("gate_up", "down", "shared_gate_up", "shared_down")}
+    route = ql.moe_route(H, t(w["Wr"]), t(tok["logit_bias"]), topk)
+    act = gemm(dw["gate_up"], dw["shared_gate_up"], H, T, topk, ql.QL_OP_GATE_UP_SILU, route)
+    yd = gemm(dw["down"], dw["shared_down"], act, T, topk, ql.QL_OP_DOWN, route)
+    out = ql.moe_combine(yd, route["gates"], route["pos"], T, topk, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(route["ids"]), ref["ids"])
+    assert np.array_equal(host(route["sorted_assign"]), ref["sorted_assign"])
+    assert_close(host(out).astype(np.float64), ref["out"], f"moe {codec} out")

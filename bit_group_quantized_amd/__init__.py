@@ -437,6 +437,8 @@ def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op:
     (QL_OP_GATE_UP_SILU or QL_OP_DOWN)."""
     import torch
     codes = W["codes"]
+    if codes.dtype != torch.uint8 or codes.dim() != 3 or W["scales"].dtype != torch.float16:
+        raise ValueError("FP8 experts: codes uint8 [E][N][K], scales float16 [E][N][K/64]")
     w = ql_fp8_experts(codes.data_ptr(), W["scales"].data_ptr(), int(W["K"]), int(W["N"]),
                        int(codes.shape[0]))
     s = (ql_fp8(shared["codes"].data_ptr(), shared["scales"].data_ptr(), int(shared["K"]),
@@ -460,6 +462,11 @@ def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, o
     tensors), shared one NVFP4 matrix (global_scale a float) or None."""
     import torch
     qw = W["qweight"]
+    g = W["global_scale"]
+    if (qw.dim() != 3 or W["block_scales"].dtype != torch.uint8 or not torch.is_tensor(g)
+            or g.dtype != torch.float32 or g.numel() != qw.shape[0] or not g.is_cuda):
+        raise ValueError("NVFP4 experts: qweight [E][N][K/8], block_scales uint8 [E][N][K/16], "
+                         "global_scale a float32 device tensor [E]")
     w = ql_nvfp4_experts(qw.data_ptr(), W["block_scales"].data_ptr(), W["global_scale"].data_ptr(),
                          int(W["K"]), int(W["N"]), int(qw.shape[0]))
     s = (ql_nvfp4(shared["qweight"].data_ptr(), shared["block_scales"].data_ptr(),

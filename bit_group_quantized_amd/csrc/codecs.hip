@@ -4,9 +4,10 @@
 //
 // "待验证｜lithos-metal补Apple推理内核", section "一分钟内合并了什么": the
 // project decodes FP8 E4M3 weights two codes per half2 and serves an NVFP4
-// checkpoint.  Both decodes here are exact bit moves into fp16 (a power-of-
-// two factor is restored after the sum), so the products in v_dot2_f32_f16
-// are exact and only the fp32 sums round, as in the w4 GEMV.
+// checkpoint.  Here one gfx950 conversion turns two codes into an fp16 pair
+// holding their exact values (NaN codes become NaN), so the products in
+// v_dot2_f32_f16 are exact and only the fp32 sums round, as in the w4 GEMV;
+// group and block scales are applied to fp32 partial sums.
 //
 // Lane layout as the chunked w4 GEMV: a team of TPR lanes owns a row, each
 // lane 16-byte chunks at a fixed K position, R consecutive rows per team;
@@ -62,17 +63,15 @@ gemv_fp8_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ 
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 // codes (b0, b1) and (b2, b3) of the word, in natural order
-                const uint32_t t01 = __builtin_amdgcn_perm(wv[w], wv[w], 0x010C000Cu);
-                const uint32_t t23 = __builtin_amdgcn_perm(wv[w], wv[w], 0x030C020Cu);
-                d0 = dot2(as_f16x2(xv[2 * w]), as_f16x2(e4m3x2_to_f16x2(t01)), d0);
-                d1 = dot2(as_f16x2(xv[2 * w + 1]), as_f16x2(e4m3x2_to_f16x2(t23)), d1);
+                d0 = dot2(as_f16x2(xv[2 * w]), e4m3x2_to_f16x2<false>(wv[w]), d0);
+                d1 = dot2(as_f16x2(xv[2 * w + 1]), e4m3x2_to_f16x2<true>(wv[w]), d1);
             }
             acc[r] += h2f(s[r][v]) * (d0 + d1);
         }
     }
     int rsel;
     const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
-    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot * 256.0f);
+    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot);
 }
 
 template <int TPR, int V, int R>
@@ -116,22 +115,21 @@ gemv_nvfp4_kernel(const uint32_t* __restrict__ qw, const uint8_t* __restrict__ b
             float d[2] = {0.f, 0.f};  // blocks 2c and 2c + 1 (words 0-1 and 2-3)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                uint32_t pr[4];
-                e2m1x8_to_f16x2(wv[w], pr);
                 const u32x4 xq = xr[v][w];  // x pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7)
                 float e = d[w >> 1];
-                e = dot2(as_f16x2(xq.x), as_f16x2(pr[0]), e);
-                e = dot2(as_f16x2(xq.y), as_f16x2(pr[1]), e);
-                e = dot2(as_f16x2(xq.z), as_f16x2(pr[2]), e);
-                e = dot2(as_f16x2(xq.w), as_f16x2(pr[3]), e);
+                e = dot2(as_f16x2(xq.x), e2m1x2_to_f16x2<0>(wv[w]), e);
+                e = dot2(as_f16x2(xq.y), e2m1x2_to_f16x2<1>(wv[w]), e);
+                e = dot2(as_f16x2(xq.z), e2m1x2_to_f16x2<2>(wv[w]), e);
+                e = dot2(as_f16x2(xq.w), e2m1x2_to_f16x2<3>(wv[w]), e);
                 d[w >> 1] = e;
             }
-            acc[r] += e4m3_to_f32(bs[r][v] & 0xFFu) * d[0] + e4m3_to_f32(bs[r][v] >> 8) * d[1];
+            const uint32_t b2 = bs[r][v];
+            acc[r] += e4m3_to_f32<0>(b2) * d[0] + e4m3_to_f32<1>(b2) * d[1];
         }
     }
     int rsel;
     const float tot = reduce_rows<TPR, R>(acc, lr, rsel);
-    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot * (16384.0f * gscale));
+    if ((lr & (TPR / R - 1)) == 0 && row0 + rsel < N) y[row0 + rsel] = f2h(tot * gscale);
 }
 
 constexpr int kCodecRows = 8;

@@ -136,7 +136,8 @@ struct Job {
 // along K and no bias, staged as fp16(e4m3 * scale), one rounding;
 // 2 = NVFP4: E2M1 codes in the w4 packing, E4M3 block scales [N][K/16]
 // (bytes, through p.sc) and the matrix's global scale job.gscale, staged as
-// fp16(e2m1 * fp16(e4m3 * global)).
+// fp16(e2m1 * (e4m3 * global)) with the block scale and the product in fp32
+// and one rounding to fp16.
 template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
 __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
     using TL = Tile<WM, WN, WGM, WGN>;
@@ -280,44 +281,46 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
                 *reinterpret_cast<u32x4*>(b_dst + (8 * nb + j) * kLdk + 8 * kb) = o;
             }
         } else if constexpr (WF == 1) {
-            // (e4m3 * 2**-8) * (scale * 2**8) in fp16: both factors exact, so
-            // the product is fp16(e4m3 * scale) with one rounding.
-            const f16 s256 = __builtin_bit_cast(f16, sreg[S]) * (f16)256.0f;
-            const f16x2 s2 = {s256, s256};
+            // The E4M3 codes decode exactly to fp16 (NaN codes to NaN); one
+            // packed fp16 multiply by the group's scale rounds each product
+            // once: the weight is fp16(e4m3 * scale).
+            const f16 sv = __builtin_bit_cast(f16, sreg[S]);
+            const f16x2 s2 = {sv, sv};
             constexpr int W = TL::WPT;  // groups of 8 codes of this thread per step
 #pragma unroll
             for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
                 const uint32_t c0 = breg[S][(2 * w) >> 2][(2 * w) & 3];
                 const uint32_t c1 = breg[S][(2 * w + 1) >> 2][(2 * w + 1) & 3];
-                uint32_t q[4];
-                e4m3x4_to_f16(c0, q[0], q[1]);
-                e4m3x4_to_f16(c1, q[2], q[3]);
                 u32x4 o;
-                o.x = as_u32(as_f16x2(q[0]) * s2);
-                o.y = as_u32(as_f16x2(q[1]) * s2);
-                o.z = as_u32(as_f16x2(q[2]) * s2);
-                o.w = as_u32(as_f16x2(q[3]) * s2);
+                o.x = as_u32(e4m3x2_to_f16x2<false>(c0) * s2);
+                o.y = as_u32(e4m3x2_to_f16x2<true>(c0) * s2);
+                o.z = as_u32(e4m3x2_to_f16x2<false>(c1) * s2);
+                o.w = as_u32(e4m3x2_to_f16x2<true>(c1) * s2);
                 const int word = bpart * W + w;  // 0..7 within the group
                 *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = o;
             }
         } else if constexpr (WF == 2) {
-            // e2m1 * 2**-14 (exact), times 2**14 (exact), times the block's
-            // fp16(e4m3 * global): the weight rounds at the scale and at the
-            // product.
-            const f16x2 k14 = {(f16)16384.0f, (f16)16384.0f};
+            // The block scale e4m3 * global is formed in fp32, each E2M1 code
+            // (exact) is multiplied by it in fp32 and the product is rounded
+            // once to fp16.  This thread's words cover blocks starting at
+            // (bpart * W) / 2 of the step's four.
             constexpr int W = TL::WPT;  // words of 8 codes of this thread per step
+            const uint32_t nsh = nreg[S] >> (8 * ((bpart * W) >> 1));
+            float bsc[(W + 1) / 2];
+#pragma unroll
+            for (int i = 0; i < (W + 1) / 2; ++i) bsc[i] = e4m3_to_f32<0>(nsh >> (8 * i)) * job.gscale;
 #pragma unroll
             for (int w = P * W / 4; w < (P + 1) * W / 4; ++w) {
                 const int word = bpart * W + w;  // 0..7 within the step: block word / 2
-                const f16 sc = (f16)(e4m3_to_f32((nreg[S] >> (8 * (word >> 1))) & 0xFFu) * job.gscale);
-                const f16x2 s2 = {sc, sc};
-                uint32_t q[4];
-                e2m1x8_to_f16x2(breg[S][w >> 2][w & 3], q);
+                const float sc = bsc[w >> 1];
+                const uint32_t u = breg[S][w >> 2][w & 3];
+                const f32x2 q0 = e2m1x2_to_f32x2<0>(u), q1 = e2m1x2_to_f32x2<1>(u);
+                const f32x2 q2 = e2m1x2_to_f32x2<2>(u), q3 = e2m1x2_to_f32x2<3>(u);
                 u32x4 o;
-                o.x = as_u32((as_f16x2(q[0]) * k14) * s2);
-                o.y = as_u32((as_f16x2(q[1]) * k14) * s2);
-                o.z = as_u32((as_f16x2(q[2]) * k14) * s2);
-                o.w = as_u32((as_f16x2(q[3]) * k14) * s2);
+                o.x = f32x2_to_f16x2(q0[0] * sc, q0[1] * sc);
+                o.y = f32x2_to_f16x2(q1[0] * sc, q1[1] * sc);
+                o.z = f32x2_to_f16x2(q2[0] * sc, q2[1] * sc);
+                o.w = f32x2_to_f16x2(q3[0] * sc, q3[1] * sc);
                 *reinterpret_cast<u32x4*>(b_dst + bc * kLdk + word * 8) = o;
             }
         } else if constexpr (DT == 1) {

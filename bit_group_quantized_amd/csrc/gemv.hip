@@ -41,7 +41,7 @@ __device__ __forceinline__ float group_dot(const u32x4& c0, const u32x4& c1, con
     dot_word(c1.y, xp[5], d0, d1, d2, d3);
     dot_word(c1.z, xp[6], d0, d1, d2, d3);
     dot_word(c1.w, xp[7], d0, d1, d2, d3);
-    return (d0 + d2) + (d1 + d3);
+    return dot_sum(d0, d1, d2, d3);
 }
 
 // Load and pre-pair the 64 activations of group g.
@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_group_x(const uint16_t* __restrict__ x, int
         u32x4 xw = ld_u32x4(x + g * kGroup + w * 8);
         xp[w] = make_xpairs(xw);
         float cw, sw;
-        xpairs_consts(xp[w], xw, cw, sw);
+        xpairs_consts(xp[w], cw, sw);
         c += cw;
         xs += sw;
     }
@@ -256,7 +256,7 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
         for (int w = 0; w < 4; ++w) {
             xp[v][w] = make_xpairs(xr[v][w]);
             float cw_, sw_;
-            xpairs_consts(xp[v][w], xr[v][w], cw_, sw_);
+            xpairs_consts(xp[v][w], cw_, sw_);
             xc[v] += cw_;
             xs[v] += sw_;
         }
@@ -272,7 +272,7 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
             dot_word(cw[r][v].y, xp[v][1], d0, d1, d2, d3);
             dot_word(cw[r][v].z, xp[v][2], d0, d1, d2, d3);
             dot_word(cw[r][v].w, xp[v][3], d0, d1, d2, d3);
-            const float d = (d0 + d2) + (d1 + d3);
+            const float d = dot_sum(d0, d1, d2, d3);
             acc[r] += h2f(s[r][v]) * (d - xc[v]) + h2f(b[r][v]) * xs[v];
         }
     }
@@ -494,7 +494,7 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
             for (int w = 0; w < 4; ++w) {
                 xp[v][w] = make_xpairs(xr[v][w]);
                 float c_, s_;
-                xpairs_consts(xp[v][w], xr[v][w], c_, s_);
+                xpairs_consts(xp[v][w], c_, s_);
                 xc[v] += c_;
                 xs[v] += s_;
             }
@@ -509,7 +509,7 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
                 dot_word(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
                 dot_word(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
                 dot_word(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
-                acc[q] += h2f(s[q][v]) * (((d0 + d2) + (d1 + d3)) - xc[v]) + h2f(b[q][v]) * xs[v];
+                acc[q] += h2f(s[q][v]) * (dot_sum(d0, d1, d2, d3) - xc[v]) + h2f(b[q][v]) * xs[v];
             }
         }
     }
@@ -705,7 +705,7 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
             } else {
                 const XPairs xp = make_xpairs(xw[w]);
                 float c_, s_;
-                xpairs_consts(xp, xw[w], c_, s_);
+                xpairs_consts(xp, c_, s_);
                 cc += c_;
                 xx += s_;
                 s_xp[((size_t)j * CH + c) * 4 + w] = xp;
@@ -774,7 +774,7 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
                         dot_word(cw[jj][q][v].y, xp[1], d0, d1, d2, d3);
                         dot_word(cw[jj][q][v].z, xp[2], d0, d1, d2, d3);
                         dot_word(cw[jj][q][v].w, xp[3], d0, d1, d2, d3);
-                        acc[q] += g * (h2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - xc) +
+                        acc[q] += g * (h2f(s[jj][q][v]) * (dot_sum(d0, d1, d2, d3) - xc) +
                                        h2f(b[jj][q][v]) * xs);
                     }
                 }

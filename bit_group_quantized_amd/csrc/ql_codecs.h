@@ -1,48 +1,53 @@
-// FP8-E4M3 and E2M1 weight codes as exact fp16 values, shared by the codec
-// GEMVs and the codec GEMMs.
+// FP8-E4M3 and E2M1 weight codes decoded with the gfx950 conversion
+// instructions, shared by the codec GEMVs and the codec GEMMs.
 //
 // "待验证｜lithos-metal补Apple推理内核", section "一分钟内合并了什么": FP8
 // E4M3 weights decoded two codes per half2, and an NVFP4 checkpoint (E2M1
 // codes with E4M3 block scales).
+//
+// The conversions take the OCP formats: E4M3FN (exponent bias 7, subnormals
+// m/8 * 2**-6, S.1111.111 = NaN, no infinity) and E2M1 (magnitudes 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6).  Every E4M3 and E2M1 value is exact in fp16, so the
+// decoded codes are the format's values, NaN codes included.  The scale
+// operand of the scaled conversions only contributes its power of two; it
+// is 1 here and every real scale is applied by the caller.
 #pragma once
 
 #include "ql_device.h"
 
 namespace ql {
 
-// Two E4M3 codes -> fp16 pair holding e4m3 * 2**-8 each, exactly: the code
-// bits seeeemmm go to fp16 bits s.0eeee.mmm0000000 (the exponent bias 15 of
-// fp16 against 7 of E4M3 is the 2**-8; E4M3 subnormals land on fp16
-// subnormals).  `t` holds the two codes in bits 15:8 and 31:24.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t t) {
-    return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Codes in bytes 0 and 1 of w (HI = false) or bytes 2 and 3 (HI = true) ->
+// their E4M3 values as an fp16 pair, lower byte first.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
-// The four codes of a word (bytes b0..b3) as two fp16 pairs (b0, b1) and
-// (b2, b3), each value e4m3 * 2**-8.
-__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, uint32_t& p01, uint32_t& p23) {
-    p01 = e4m3x2_to_f16x2(__builtin_amdgcn_perm(w, w, 0x010C000Cu));
-    p23 = e4m3x2_to_f16x2(__builtin_amdgcn_perm(w, w, 0x030C020Cu));
+// Byte B of w as an E4M3 value in fp32 (exact; NaN for S.1111.111).
+template <int B>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_f32_fp8(w, B);
 }
 
-// E4M3 code -> float, exactly (via the fp16 pattern above).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t h = ((b & 0x80u) << 8) | ((b & 0x7Fu) << 7);
-    return h2f((uint16_t)h) * 256.0f;
+// The two E2M1 codes of byte B of w (low nibble first) as an fp16 pair.
+template <int B>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
 }
 
-// A word of 8 E2M1 codes (code k at bits 4k) -> 4 fp16 pairs in natural k
-// order, each value e2m1 * 2**-14 exactly: that fp16 has high byte
-// s000eem0 (the magnitude eem lands on bits 11..9; E2M1's subnormal 0.5 on
-// the fp16 subnormal 2**-15) and low byte 0.  The high bytes of the even
-// codes (A) and the odd codes (B) are built four at a time, then paired.
-__device__ __forceinline__ void e2m1x8_to_f16x2(uint32_t u, uint32_t (&p)[4]) {
-    const uint32_t A = ((u << 1) & 0x0E0E0E0Eu) | ((u << 4) & 0x80808080u);  // codes 0, 2, 4, 6
-    const uint32_t B = ((u >> 3) & 0x0E0E0E0Eu) | (u & 0x80808080u);         // codes 1, 3, 5, 7
-    p[0] = __builtin_amdgcn_perm(B, A, 0x040C000Cu);  // (code 0, code 1)
-    p[1] = __builtin_amdgcn_perm(B, A, 0x050C010Cu);  // (2, 3)
-    p[2] = __builtin_amdgcn_perm(B, A, 0x060C020Cu);  // (4, 5)
-    p[3] = __builtin_amdgcn_perm(B, A, 0x070C030Cu);  // (6, 7)
+// The same two codes as fp32 values.
+template <int B>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
+
+// Two fp32 values -> fp16 pair, each rounded to nearest even.
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
+    const f16x2 r = {(f16)lo, (f16)hi};
+    return as_u32(r);
 }
 
 }  // namespace ql

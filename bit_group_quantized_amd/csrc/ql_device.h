@@ -159,9 +159,13 @@ __device__ __forceinline__ void dot_word_bf(uint32_t u, const XPairsBf& x, float
 //   c1 = (u & 0x00F000F0) | magic       = (1024 + 16 q1, 1024 + 16 q5)
 //   c2 = ((u>>8) & 0x000F000F) | magic  = (1024 + q2,    1024 + q6)
 //   c3 = ((u>>8) & 0x00F000F0) | magic  = (1024 + 16 q3, 1024 + 16 q7)
-// With activation pairs x0 = (x0, x4), x1 = (x1/16, x5/16), x2 = (x2, x6),
-// x3 = (x3/16, x7/16):  sum dot2(xi, ci) = sum_k x_k q_k + 1024 * (sum of
-// all pair entries).  The constant is removed once per group.
+// The activations are paired unscaled, p0 = (x0, x4), p1 = (x1, x5),
+// p2 = (x2, x6), p3 = (x3, x7), so every product x * c is exact in fp32 for
+// any fp16 x (subnormal ones included).  With d_i = sum dot2(p_i, c_i):
+//   (d0 + d2) + (d1 + d3) / 16 = sum_k x_k q_k + 1024 * (x0+x2+x4+x6)
+//                                             + 64 * (x1+x3+x5+x7);
+// the division by 16 is exact in fp32 and the constant is removed once per
+// chunk of codes.
 struct XPairs {
     f16x2 p[4];
 };
@@ -170,29 +174,22 @@ __device__ __forceinline__ XPairs make_xpairs(u32x4 xw) {
     // xw holds x0..x7 as fp16 pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7).
     XPairs r;
     r.p[0] = as_f16x2(__builtin_amdgcn_perm(xw.z, xw.x, 0x05040100u));  // (x0, x4)
+    r.p[1] = as_f16x2(__builtin_amdgcn_perm(xw.z, xw.x, 0x07060302u));  // (x1, x5)
     r.p[2] = as_f16x2(__builtin_amdgcn_perm(xw.w, xw.y, 0x05040100u));  // (x2, x6)
-    f16x2 a = as_f16x2(__builtin_amdgcn_perm(xw.z, xw.x, 0x07060302u));  // (x1, x5)
-    f16x2 b = as_f16x2(__builtin_amdgcn_perm(xw.w, xw.y, 0x07060302u));  // (x3, x7)
-    const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
-    r.p[1] = a * sixteenth;
-    r.p[3] = b * sixteenth;
+    r.p[3] = as_f16x2(__builtin_amdgcn_perm(xw.w, xw.y, 0x07060302u));  // (x3, x7)
     return r;
 }
 
-// Sum of the pair entries times 1024 (the constant of the dot-product form),
-// and the plain sum of the eight activations (for the bias term).
-__device__ __forceinline__ void xpairs_consts(const XPairs& r, u32x4 xw, float& c, float& xs) {
-    // Sums of fp16 values as dot products with (1, 1): exact products, fp32 sums.
+// The constant of the dot-product form, 1024 * (sum of the even-k
+// activations) + 64 * (sum of the odd-k ones), and the plain sum of the
+// eight activations (for the bias term).  Sums of fp16 values as dot
+// products with (1, 1): exact products, fp32 sums.
+__device__ __forceinline__ void xpairs_consts(const XPairs& r, float& c, float& xs) {
     const f16x2 one2 = {(f16)1.0f, (f16)1.0f};
-    float sp = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sp = dot2(r.p[i], one2, sp);
-    c = 1024.0f * sp;
-    const f16x2 h[4] = {as_f16x2(xw.x), as_f16x2(xw.y), as_f16x2(xw.z), as_f16x2(xw.w)};
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = dot2(h[i], one2, s);
-    xs = s;
+    const float ev = dot2(r.p[2], one2, dot2(r.p[0], one2, 0.f));
+    const float od = dot2(r.p[3], one2, dot2(r.p[1], one2, 0.f));
+    c = fmaf(1024.0f, ev, 64.0f * od);
+    xs = ev + od;
 }
 
 // Accumulate sum dot2(x pairs, code pairs) for one word into four partials.
@@ -203,6 +200,12 @@ __device__ __forceinline__ void dot_word(uint32_t u, const XPairs& x, float& d0,
     d1 = dot2(x.p[1], as_f16x2(and_or(u, 0x00F000F0u, magic)), d1);
     d2 = dot2(x.p[2], as_f16x2(and_or(t, 0x000F000Fu, magic)), d2);
     d3 = dot2(x.p[3], as_f16x2(and_or(t, 0x00F000F0u, magic)), d3);
+}
+
+// The four partials of dot_word combined: the odd-k codes entered as 16 q,
+// so their partials are scaled by 1/16 (exact in fp32).
+__device__ __forceinline__ float dot_sum(float d0, float d1, float d2, float d3) {
+    return fmaf(d1 + d3, 0.0625f, d0 + d2);
 }
 
 __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {

@@ -234,10 +234,11 @@ typedef struct ql_nvfp4_experts {
 
 /*
  * qlinear_gemv_fp8, qlinear_gemv_nvfp4 - y fp16 [N] = x fp16 [K] . W for
- * one activation row.  Codes are decoded by exact bit moves into fp16 (the
- * FP8 pairs two codes per half2), multiplied in fp32 with v_dot2, scaled
- * per group / block and rounded once to fp16.  NaN E4M3 codes are not
- * supported (weights are finite).
+ * one activation row.  Two codes at a time are converted to an fp16 pair of
+ * their exact values (the FP8 "two codes per half2"), multiplied in fp32
+ * with v_dot2, scaled per group / block in fp32 and rounded once to fp16.
+ * An E4M3 code S.1111.111 (weight code or NVFP4 block scale) is NaN, as the
+ * format defines, and makes the outputs of its row NaN.
  * Limits: K a power of two, 256 .. 8192 (FP8) or 256 .. 16384 (NVFP4).
  * Errors: INVALID_ARG (null W/x/y with N > 0, N < 0), UNSUPPORTED_SHAPE,
  * MISALIGNED (codes/qweight and x 16-byte, scales, block_scales and y
@@ -252,9 +253,11 @@ int qlinear_gemv_nvfp4(const ql_nvfp4* W, const uint16_t* x, uint16_t* y, void* 
  * small weight tiles dequantized into on-chip memory for the matrix path).
  * The MFMA tiles of qlinear_gemm (same shape table, same row invariance:
  * row m's bits do not depend on M) with each staged weight
- * fp16(e4m3(code) * scale), one rounding (exact bit moves give e4m3 * 2^-8 and
- * scale * 2^8 in fp16; their fp16 product is the rounded weight; scales must
- * stay below 256), fp32 accumulation, fp16 output.
+ * fp16(e4m3(code) * scale): the code converts exactly to fp16 and one fp16
+ * multiply rounds the product once (any finite fp16 scale; a NaN code gives a
+ * NaN weight).  Staged weights are fp16: a product above 65504 in magnitude
+ * becomes infinite and one below 2^-14 is held on fp16's subnormal grid.
+ * fp32 accumulation, fp16 output.
  * Limits: K a positive multiple of 64, K <= QL_MAX_K.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (codes and X 16-byte,
  * scales and Y 2-byte aligned), HIP.
@@ -265,9 +268,11 @@ int qlinear_gemm_fp8(const ql_fp8* W, const uint16_t* X, int64_t M, uint16_t* Y,
  * qlinear_gemm_nvfp4 - Y fp16 [M][N] = X fp16 [M][K] . W for NVFP4 weights,
  * the prefill counterpart of qlinear_gemv_nvfp4: the MFMA tiles of
  * qlinear_gemm (same shape table and row invariance) with each staged weight
- * fp16(e2m1 * fp16(e4m3(block scale) * global_scale)): the block scale is
- * rounded once to fp16 and the product once more (the e2m1 value is exact),
- * fp32 accumulation, fp16 output.
+ * fp16(e2m1 * (e4m3(block scale) * global_scale)): the block scale and the
+ * product are formed in fp32 (the e2m1 and e4m3 values are exact) and
+ * rounded once to fp16, with the fp16 range of qlinear_gemm_fp8's staged
+ * weights; a NaN block scale gives NaN weights.  fp32 accumulation, fp16
+ * output.
  * Limits: K a positive multiple of 64, K <= QL_MAX_K; global_scale finite.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (qweight and X 16-byte,
  * block_scales 4-byte, Y 2-byte aligned), HIP.
@@ -489,8 +494,8 @@ int moe_combine_bf16(const uint16_t* Ydown, const float* topk_gates, const int32
  * ql_fp8 format of qlinear_gemm_fp8, stacked over experts; "待验证｜lithos-
  * metal补Apple推理内核", section "一分钟内合并了什么": FP8 weight decode).
  * Same rows, workspace, tile map and fp16 X / Y as moe_grouped_gemm; each
- * staged weight is fp16(e4m3(code) * scale), one rounding (scales below
- * 256), fp32 accumulation on the MFMA tiles, act = SiLU(gate) * up rounded
+ * staged weight is fp16(e4m3(code) * scale), one rounding (as in
+ * qlinear_gemm_fp8, with its fp16 range), fp32 accumulation on the MFMA tiles, act = SiLU(gate) * up rounded
  * to fp16.  Serves QL_OP_GATE_UP_SILU and QL_OP_DOWN for every T on the
  * tiled path (the gates are applied by moe_combine); QL_OP_DOWN_COMBINE
  * returns UNSUPPORTED_SHAPE.  `shared` (may be NULL) has the shape of one
@@ -509,8 +514,9 @@ int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared,
  * ql_nvfp4 format of qlinear_gemm_nvfp4, stacked over experts, a global
  * scale per expert read from device memory; the same page and section as
  * the FP8 call).  Same rows, workspace, tile map, fp16 X / Y and ops as
- * moe_grouped_gemm_fp8; each staged weight is fp16(e2m1 * fp16(e4m3(block
- * scale) * global scale)) as in qlinear_gemm_nvfp4.  `shared` (may be NULL;
+ * moe_grouped_gemm_fp8; each staged weight is fp16(e2m1 * (e4m3(block
+ * scale) * global scale)), formed in fp32 and rounded once, as in
+ * qlinear_gemm_nvfp4.  `shared` (may be NULL;
  * host global_scale, finite) has the shape of one expert.
  * Limits: K a positive multiple of 64, K <= QL_MAX_K.
  * Errors: INVALID_ARG (incl. a non-finite shared global scale),

@@ -27,11 +27,19 @@ these seeded draws stand in for it):
   N(0, 16), i.e. 4 * N(0, 1); normalization gain: fp16 of U(0.5, 1.5);
 * bf16 variants: the same draws stored as bf16 bit patterns (uint16, the
   upper half of the float32 pattern, nearest even);
-* FP8-E4M3 weights: codes uniform over the 254 non-NaN bytes, one fp16 scale
-  per 64 along K from U(1e-4, 1e-3);
+* FP8-E4M3 weights: codes uniform over the 254 bytes that encode numbers
+  (a checkpoint's weights are finite), or over all 256 bytes, the two NaN
+  codes included, with ``all_codes=True``; one fp16 scale per 64 along K
+  from U(1e-4, 1e-3), or any range the caller gives;
 * NVFP4 weights: E2M1 codes uniform (uniform 32-bit words, as the w4 codes),
   E4M3 block scales with exponent field uniform in 5..9 and mantissa
-  uniform (values 0.25 .. 3.75), positive; global scale 0.01 (fp32).
+  uniform (values 0.25 .. 7.5), positive, or uniform over all 256 bytes
+  (signs, subnormals, 448 and NaN) with ``all_codes=True``; global scale
+  0.01 (fp32), or the caller's;
+* exact-arithmetic router inputs: H in {-1, 0, 1}, router weights integers
+  in -16..16 times 2**-8, logit bias the Zipf bias rounded to a multiple of
+  2**-8, so that every logit is a multiple of 2**-8 of magnitude below 2**8
+  and fp32 sums in any order are exact (exact ties are frequent).
 """
 from __future__ import annotations
 
@@ -61,19 +69,21 @@ def activations(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
     return f16(rng.standard_normal((rows, cols)))
 
 
-def w4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
+def w4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = (),
+              scale_range=(0.002, 0.02)) -> dict:
     """One (or a stack of) group-affine 4-bit K x N matrices.
 
     Returns a dict with ``qweight`` uint32 [*lead, N, K/8], ``scales`` and
     ``biases`` fp16 [*lead, N, K/64], and the sizes.  ``lead=(E,)`` draws E
-    experts stacked contiguously.
+    experts stacked contiguously.  Scales are U(scale_range) (the workload's
+    U(0.002, 0.02) by default); the bias noise grows with the scale.
     """
     if K % 8:
         raise ValueError("K must be a multiple of 8 to draw packed words")
     G = (K + GROUP - 1) // GROUP
     words = rng.integers(0, 2**32, size=lead + (N, K // 8), dtype=np.uint64).astype(np.uint32)
-    scales = f16(rng.uniform(0.002, 0.02, size=lead + (N, G)))
-    noise = rng.normal(0.0, 1e-3, size=lead + (N, G))
+    scales = f16(rng.uniform(scale_range[0], scale_range[1], size=lead + (N, G)))
+    noise = rng.normal(0.0, 1e-3 * scale_range[1] / 0.02, size=lead + (N, G))
     biases = f16(-8.0 * scales.astype(np.float64) + noise)
     return {"qweight": words, "scales": scales, "biases": biases, "K": K, "N": N}
 
@@ -108,25 +118,36 @@ def gemm_case_bf16(seed: int, M: int, K: int, N: int) -> dict:
     return {"X": X, "W": W}
 
 
-def fp8_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
-    """FP8-E4M3 weights: codes uint8 [N][K] (no NaN codes), fp16 scales [N][K/64];
-    ``lead`` stacks several such matrices (e.g. (E,) for E experts)."""
-    codes = rng.integers(0, 254, size=lead + (N, K), dtype=np.uint8)
-    codes += codes >= 0x7F                                              # skip 0x7F (and 0xFF)
-    scales = f16(rng.uniform(1e-4, 1e-3, size=lead + (N, K // 64)))
+def fp8_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = (),
+               all_codes: bool = False, scale_range=(1e-4, 1e-3)) -> dict:
+    """FP8-E4M3 weights: codes uint8 [N][K], fp16 scales [N][K/64] from
+    U(scale_range); ``lead`` stacks several such matrices (e.g. (E,) for E
+    experts).  Codes are uniform over the 254 number codes (0x7F and 0xFF,
+    the NaN codes, are skipped), or over all 256 with ``all_codes``."""
+    if all_codes:
+        codes = rng.integers(0, 256, size=lead + (N, K), dtype=np.uint16).astype(np.uint8)
+    else:
+        codes = rng.integers(0, 254, size=lead + (N, K), dtype=np.uint8)
+        codes += codes >= 0x7F                                          # skip 0x7F (and 0xFF)
+    scales = f16(rng.uniform(scale_range[0], scale_range[1], size=lead + (N, K // 64)))
     return {"codes": codes, "scales": scales, "K": K, "N": N}
 
 
-def nvfp4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = ()) -> dict:
+def nvfp4_matrix(rng: np.random.Generator, K: int, N: int, lead: tuple = (),
+                 all_codes: bool = False, global_scale: float = 0.01) -> dict:
     """NVFP4 weights: qweight uint32 [N][K/8] (E2M1 codes, w4 packing),
-    block scales uint8 [N][K/16] (positive E4M3), global scale fp32 (0.01).
+    block scales uint8 [N][K/16] (positive E4M3 of 0.25 .. 7.5, or every
+    byte with ``all_codes``), global scale fp32 (``global_scale``).
     ``lead`` stacks several matrices; each then draws its own global scale
     (fp32 array of shape ``lead``, uniform in [0.005, 0.02))."""
     words = rng.integers(0, 2**32, size=lead + (N, K // 8), dtype=np.uint64).astype(np.uint32)
-    e = rng.integers(5, 10, size=lead + (N, K // 16))
-    m = rng.integers(0, 8, size=lead + (N, K // 16))
-    block = ((e << 3) | m).astype(np.uint8)
-    g = np.float32(0.01) if not lead else rng.uniform(0.005, 0.02, size=lead).astype(np.float32)
+    if all_codes:
+        block = rng.integers(0, 256, size=lead + (N, K // 16), dtype=np.uint16).astype(np.uint8)
+    else:
+        e = rng.integers(5, 10, size=lead + (N, K // 16))
+        m = rng.integers(0, 8, size=lead + (N, K // 16))
+        block = ((e << 3) | m).astype(np.uint8)
+    g = np.float32(global_scale) if not lead else rng.uniform(0.005, 0.02, size=lead).astype(np.float32)
     return {"qweight": words, "block_scales": block, "global_scale": g, "K": K, "N": N}
 
 
@@ -165,10 +186,10 @@ def synthetic_topk_ids(rng: np.random.Generator, T: int, E: int, topk: int,
 # Workloads.  Each builder fixes the order of its draws.
 # ----------------------------------------------------------------------------
 
-def gemv_case(seed: int, K: int, N: int) -> dict:
-    """x fp16 [1][K] and one K x N w4 matrix."""
+def gemv_case(seed: int, K: int, N: int, x_scale: float = 1.0) -> dict:
+    """x fp16 [1][K] (N(0, x_scale**2) draws) and one K x N w4 matrix."""
     rng = rng_for(seed)
-    x = activations(rng, 1, K)
+    x = activations(rng, 1, K) if x_scale == 1.0 else f16(x_scale * rng.standard_normal((1, K)))
     W = w4_matrix(rng, K, N)
     return {"x": x, "W": W}
 
@@ -196,18 +217,19 @@ def gemm_case(seed: int, M: int, K: int, N: int) -> dict:
     return {"X": X, "W": W}
 
 
-def moe_weights(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:
+def moe_weights(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS,
+                scale_range=(0.002, 0.02), router_std: float = 0.02) -> dict:
     """Router [D][E] fp16, E stacked experts and one shared expert.
 
     gate_up: K = D, N = 2*I (columns [0, I) gate, [I, 2I) up);
     down:    K = I, N = D.
     """
     rng = rng_for(seed)
-    Wr = router_weight(rng, D, E)
-    gate_up = w4_matrix(rng, D, 2 * I, lead=(E,))
-    down = w4_matrix(rng, I, D, lead=(E,))
-    shared_gate_up = w4_matrix(rng, D, 2 * I)
-    shared_down = w4_matrix(rng, I, D)
+    Wr = f16(rng.normal(0.0, router_std, size=(D, E)))
+    gate_up = w4_matrix(rng, D, 2 * I, lead=(E,), scale_range=scale_range)
+    down = w4_matrix(rng, I, D, lead=(E,), scale_range=scale_range)
+    shared_gate_up = w4_matrix(rng, D, 2 * I, scale_range=scale_range)
+    shared_down = w4_matrix(rng, I, D, scale_range=scale_range)
     return {"Wr": Wr, "gate_up": gate_up, "down": down,
             "shared_gate_up": shared_gate_up, "shared_down": shared_down,
             "D": D, "I": I, "E": E}
@@ -243,10 +265,11 @@ def moe_weights_nvfp4(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int 
 
 
 def moe_tokens(seed: int, T: int, D: int = HIDDEN, E: int = NUM_EXPERTS,
-               skewed: bool = False) -> dict:
-    """H fp16 [T][D] ~ N(0, 1) and, if ``skewed``, the Zipf logit bias."""
+               skewed: bool = False, h_scale: float = 1.0) -> dict:
+    """H fp16 [T][D] ~ N(0, h_scale**2) and, if ``skewed``, the Zipf logit
+    bias."""
     rng = rng_for(seed)
-    H = activations(rng, T, D)
+    H = activations(rng, T, D) if h_scale == 1.0 else f16(h_scale * rng.standard_normal((T, D)))
     bias = zipf_logit_bias(rng, E) if skewed else None
     return {"H": H, "logit_bias": bias}
 
@@ -279,6 +302,24 @@ def router_tie_case(seed: int, T: int, topk: int, D: int = HIDDEN, E: int = NUM_
     W[:, top] = W[:, [top[0]]]
     W[:, edge] = W[:, [edge[0]]]
     return {"H": f16(H), "Wr": f16(W / 256.0), "top": np.sort(top), "edge": np.sort(edge)}
+
+
+def router_exact_case(seed: int, T: int, D: int = HIDDEN, E: int = NUM_EXPERTS,
+                      skewed: bool = True) -> dict:
+    """Router inputs whose fp32 logits are exact in any summation order, at
+    any T (varied routing, unlike router_tie_case): H fp16 [T][D] in
+    {-1, 0, 1}, router weight fp16 [D][E] of integers in -16..16 times
+    2**-8, and (if ``skewed``) the Zipf logit bias rounded to a multiple of
+    2**-8 (fp32).  Every logit is a multiple of 2**-8 below 2**8 in
+    magnitude, so exact ties between experts are common."""
+    rng = rng_for(seed)
+    H = rng.integers(-1, 2, size=(T, D)).astype(np.float64)
+    W = rng.integers(-16, 17, size=(D, E)).astype(np.float64) / 256.0
+    bias = None
+    if skewed:
+        b = zipf_logit_bias(rng, E).astype(np.float64)
+        bias = (np.round(b * 256.0) / 256.0).astype(np.float32)
+    return {"H": f16(H), "Wr": f16(W), "logit_bias": bias}
 
 
 def moe_weights_bf16(seed: int, D: int = HIDDEN, I: int = EXPERT_WIDTH, E: int = NUM_EXPERTS) -> dict:

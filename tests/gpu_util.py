@@ -82,3 +82,61 @@ def assert_close_bf16(gpu_bits, ref, what="", rel_l2=REL_L2_BF16, max_abs_frac=M
 
 def say(*a):
     print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Guard regions around outputs.  An output tensor is carved out of a larger
+# buffer: the bytes before and after it hold GUARD_BYTE and must still hold
+# it after the call (a write past either end of an output, by a ragged tile,
+# the scatter or a tile-map entry, changes them); the output itself starts
+# as FILL_BYTE (NaN in fp16 / fp32, -1 in int32), so an element no kernel
+# wrote shows up as NaN or -1.
+# ---------------------------------------------------------------------------
+GUARD_BYTE = 0x5A
+FILL_BYTE = 0xFF
+GUARD_PAD = 4096  # bytes on each side (keeps the output 256-byte aligned)
+
+
+class Guarded:
+    """An output tensor with guard regions; ``check()`` asserts the guards
+    are intact.  ``t`` is the output view."""
+
+    def __init__(self, shape, dtype, device=None):
+        import torch
+        shape = tuple(int(s) for s in (shape if isinstance(shape, (tuple, list)) else (shape,)))
+        elem = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) if shape else 1
+        self.pad = GUARD_PAD // elem
+        self.n = n
+        self.elem = elem
+        self.buf = torch.empty((2 * self.pad + n,), dtype=dtype, device=device or dev())
+        raw = self.buf.view(torch.uint8)
+        raw.fill_(GUARD_BYTE)
+        raw[self.pad * elem:(self.pad + n) * elem].fill_(FILL_BYTE)
+        self.t = self.buf[self.pad:self.pad + n].view(shape)
+
+    def check(self, what=""):
+        raw = self.buf.view(__import__("torch").uint8).cpu().numpy()
+        head = raw[:self.pad * self.elem]
+        tail = raw[(self.pad + self.n) * self.elem:]
+        bad_h = np.flatnonzero(head != GUARD_BYTE)
+        bad_t = np.flatnonzero(tail != GUARD_BYTE)
+        assert bad_h.size == 0, f"{what}: {bad_h.size} bytes written before the output (first at -{head.size - bad_h[0]})"
+        assert bad_t.size == 0, f"{what}: {bad_t.size} bytes written after the output (first at +{bad_t[0]})"
+
+
+def guarded(shape, dtype, device=None) -> Guarded:
+    return Guarded(shape, dtype, device)
+
+
+def assert_close_nan(gpu, ref, what="", rel_l2=REL_L2, max_abs_frac=MAX_ABS_FRAC):
+    """NaN-aware comparison: NaN exactly where the reference is NaN, and the
+    finite entries within the bars.  Returns the number of NaN entries."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    gn, rn = np.isnan(g), np.isnan(r)
+    assert np.array_equal(gn, rn), f"{what}: NaN at {int((gn & ~rn).sum())} extra and {int((rn & ~gn).sum())} missing positions"
+    if (~rn).any():
+        assert_close(g[~rn], r[~rn], what, rel_l2, max_abs_frac)
+    return int(rn.sum())

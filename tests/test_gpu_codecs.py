@@ -6,7 +6,7 @@ import pytest
 import bit_group_quantized_amd as ql
 import oracle
 import synth
-from tests.gpu_util import assert_close, host, say, t
+from tests.gpu_util import assert_close, assert_close_nan, guarded, host, say, t
 
 pytestmark = pytest.mark.gpu
 
@@ -55,30 +55,93 @@ def test_gemv_nvfp4_matches_oracle(K, N, seed):
 
 
 @pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
-def test_codec_vocab_head_sampled(codec):
-    """K = 2048, N = 151552: every output computed, 4096 sampled rows checked."""
+def test_codec_vocab_head_full(codec):
+    """K = 2048, N = 151552 in the benchmark's launch configuration: every
+    output against the oracle, behind guard regions."""
     import torch
     K, N = 2048, synth.VOCAB
     say(f"gemv_{codec} head")
     rng = synth.rng_for(11)
     x = synth.activations(rng, 1, K)
+    y = guarded(N, torch.float16)
     if codec == "fp8":
         W = synth.fp8_matrix(rng, K, N)
-        y = host(ql.qlinear_gemv_fp8(fp8_dev(W), t(x[0]))).astype(np.float64)
+        ql.qlinear_gemv_fp8(fp8_dev(W), t(x[0]), y=y.t)
     else:
         W = synth.nvfp4_matrix(rng, K, N)
-        y = host(ql.qlinear_gemv_nvfp4(nvfp4_dev(W), t(x[0]))).astype(np.float64)
+        ql.qlinear_gemv_nvfp4(nvfp4_dev(W), t(x[0]), y=y.t)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N),
-                                     np.linspace(0, N - 1, 3968).astype(np.int64)]))
+    y.check(f"gemv_{codec} head")
+    ref = oracle.linear_fp8(x, W)[0] if codec == "fp8" else oracle.linear_nvfp4(x, W)[0]
+    rel, mx = assert_close(host(y.t).astype(np.float64), ref, f"gemv_{codec} head")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+@pytest.mark.parametrize("codec,K,N,seed", [
+    ("fp8", 2048, 40001, 13), ("fp8", 1024, 65601, 14), ("fp8", 4096, 33001, 15),
+    ("nvfp4", 2048, 40001, 16), ("nvfp4", 1024, 65601, 17), ("nvfp4", 4096, 33001, 18),
+])
+def test_codec_gemv_eight_rows_ragged(codec, K, N, seed):
+    """The 8-rows-per-lane instances with a ragged last block."""
+    import torch
+    say(f"gemv_{codec} 8-row K={K} N={N}")
+    rng = synth.rng_for(seed)
+    x = synth.activations(rng, 1, K)
+    y = guarded(N, torch.float16)
     if codec == "fp8":
-        sub = {"codes": W["codes"][rows], "scales": W["scales"][rows], "K": K, "N": len(rows)}
-        ref = oracle.linear_fp8(x, sub)[0]
+        W = synth.fp8_matrix(rng, K, N)
+        ql.qlinear_gemv_fp8(fp8_dev(W), t(x[0]), y=y.t)
+        ref = oracle.linear_fp8(x, W)[0]
     else:
-        sub = {"qweight": W["qweight"][rows], "block_scales": W["block_scales"][rows],
-               "global_scale": W["global_scale"], "K": K, "N": len(rows)}
-        ref = oracle.linear_nvfp4(x, sub)[0]
-    assert_close(y[rows], ref, f"gemv_{codec} head sample")
+        W = synth.nvfp4_matrix(rng, K, N)
+        ql.qlinear_gemv_nvfp4(nvfp4_dev(W), t(x[0]), y=y.t)
+        ref = oracle.linear_nvfp4(x, W)[0]
+    torch.cuda.synchronize()
+    y.check(f"gemv_{codec}")
+    assert_close(host(y.t).astype(np.float64), ref, f"gemv_{codec} K={K} N={N}")
+
+
+@pytest.mark.parametrize("K,N,seed", [(256, 4096, 40), (512, 2000, 41), (2048, 300, 42)])
+def test_gemv_fp8_all_codes_nan_aware(K, N, seed):
+    """Codes drawn over all 256 bytes, the two NaN codes included: a row
+    holding a NaN code gives NaN, as in the oracle, and every other row is
+    within the bar.  Rows 0..N/2 draw from all codes, the rest from the
+    number codes only, so both kinds of rows are present at every K."""
+    import torch
+    say(f"gemv_fp8 all codes K={K} N={N}")
+    rng = synth.rng_for(seed)
+    x = synth.activations(rng, 1, K)
+    Wa = synth.fp8_matrix(rng, K, N // 2, all_codes=True)
+    Wf = synth.fp8_matrix(rng, K, N - N // 2)
+    W = {"codes": np.concatenate([Wa["codes"], Wf["codes"]]),
+         "scales": np.concatenate([Wa["scales"], Wf["scales"]]), "K": K, "N": N}
+    ref = oracle.linear_fp8(x, W)[0]
+    y = guarded(N, torch.float16)
+    ql.qlinear_gemv_fp8(fp8_dev(W), t(x[0]), y=y.t)
+    torch.cuda.synchronize()
+    y.check("gemv_fp8 all codes")
+    n_nan = assert_close_nan(host(y.t), ref, "gemv_fp8 all codes")
+    say(f"  NaN rows {n_nan} of {N}")
+    assert 0 < n_nan < N
+
+
+@pytest.mark.parametrize("K,N,seed", [(256, 3000, 43), (2048, 700, 44)])
+def test_gemv_nvfp4_all_block_scales_nan_aware(K, N, seed):
+    """E4M3 block scales over all 256 bytes (negative, subnormal, 448, NaN):
+    rows with a NaN block scale give NaN, the others are within the bar."""
+    import torch
+    say(f"gemv_nvfp4 all block scales K={K} N={N}")
+    rng = synth.rng_for(seed)
+    x = synth.activations(rng, 1, K)
+    W = synth.nvfp4_matrix(rng, K, N, all_codes=True)
+    ref = oracle.linear_nvfp4(x, W)[0]
+    y = guarded(N, torch.float16)
+    ql.qlinear_gemv_nvfp4(nvfp4_dev(W), t(x[0]), y=y.t)
+    torch.cuda.synchronize()
+    y.check("gemv_nvfp4 all codes")
+    n_nan = assert_close_nan(host(y.t), ref, "gemv_nvfp4 all block scales")
+    say(f"  NaN rows {n_nan} of {N}")
+    assert 0 < n_nan < N
 
 
 def test_codecs_integer_case_bit_exact():
@@ -123,26 +186,78 @@ def test_gemm_fp8_matches_oracle(M, K, N, seed):
     say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
-def test_gemm_fp8_prefill_sampled_rows_and_row_invariance():
-    """The prefill shape (M = 4096, K = 2048, N = 8192): 64 sampled rows
-    against the oracle, and every row's bits equal to the same row computed
-    with M = 1 and M = 256 (no split over K, the same K order)."""
+def test_gemm_fp8_prefill_full_and_row_invariance():
+    """The prefill shape (M = 4096, K = 2048, N = 8192): every output against
+    the oracle, behind guard regions, and every row's bits equal to the same
+    row computed with M = 1 and M = 256 (no split over K, the same K
+    order)."""
     import torch
     M, K, N = 4096, 2048, 8192
     rng = synth.rng_for(20)
     X = synth.activations(rng, M, K)
     W = synth.fp8_matrix(rng, K, N)
     Wd, Xd = fp8_dev(W), t(X)
-    Y = host(ql.qlinear_gemm_fp8(Wd, Xd))
-    rows = np.sort(synth.rng_for(21).choice(M, 64, replace=False))
-    ref = oracle.linear_fp8(X[rows], W)
-    assert_close(Y[rows].astype(np.float64), ref, "gemm_fp8 sampled rows")
+    Yg = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_fp8(Wd, Xd, Yg.t)
+    torch.cuda.synchronize()
+    Yg.check("gemm_fp8 prefill")
+    Y = host(Yg.t)
+    rel, mx = assert_close(Y.astype(np.float64), oracle.linear_fp8(X, W), "gemm_fp8 prefill")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
     for m in (0, 255, 4095):
         for MM in (1, 256):
             lo = min(m, M - MM)
             part = host(ql.qlinear_gemm_fp8(Wd, Xd[lo:lo + MM].contiguous()))
             assert np.array_equal(part[m - lo].view(np.uint16), Y[m].view(np.uint16)), (m, MM)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(100, 64, 300, 50), (300, 256, 520, 51)])
+def test_gemm_fp8_all_codes_nan_aware(M, K, N, seed):
+    """FP8 codes over all 256 bytes in the first half of the columns (a
+    column holding a NaN code is NaN in every row, as in the oracle), number
+    codes only in the rest."""
+    import torch
+    say(f"gemm_fp8 all codes M={M} K={K} N={N}")
+    rng = synth.rng_for(seed)
+    X = synth.activations(rng, M, K)
+    Wa = synth.fp8_matrix(rng, K, N // 2, all_codes=True)
+    Wf = synth.fp8_matrix(rng, K, N - N // 2)
+    W = {"codes": np.concatenate([Wa["codes"], Wf["codes"]]),
+         "scales": np.concatenate([Wa["scales"], Wf["scales"]]), "K": K, "N": N}
+    ref = oracle.linear_fp8(X, W)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_fp8(fp8_dev(W), t(X), Y.t)
+    torch.cuda.synchronize()
+    Y.check("gemm_fp8 all codes")
+    n_nan = assert_close_nan(host(Y.t), ref, "gemm_fp8 all codes")
+    say(f"  NaN outputs {n_nan} of {M * N}")
+    assert 0 < n_nan < M * N
+
+
+@pytest.mark.parametrize("lo,hi", [(200.0, 400.0), (4000.0, 30000.0)])
+def test_gemm_fp8_large_scales(lo, hi):
+    """Group scales near the top of the fp16 range (up to 30000), with codes
+    of magnitude at most 2 (|e4m3 * scale| <= 60000, inside fp16): the staged
+    weight is fp16(e4m3 * scale) with no intermediate overflow, so the output
+    is within the bar."""
+    import torch
+    M, K, N = 200, 512, 384
+    say(f"gemm_fp8 scales U({lo}, {hi})")
+    rng = synth.rng_for(52)
+    X = synth.f16(1e-4 * rng.standard_normal((M, K)))
+    W = synth.fp8_matrix(rng, K, N, scale_range=(lo, hi))
+    # keep |e4m3| <= 2: codes of larger magnitude become sign | 1.mmm (0x38 | m)
+    c = W["codes"]
+    W["codes"] = np.where((c & 0x7F) > 0x40, (c & 0x80) | 0x38 | (c & 0x07), c).astype(np.uint8)
+    ref = oracle.linear_fp8(X, W)
+    assert np.abs(oracle.dequantize_fp8(W["codes"], W["scales"])).max() < 65504
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_fp8(fp8_dev(W), t(X), Y.t)
+    torch.cuda.synchronize()
+    Y.check("gemm_fp8 large scales")
+    rel, mx = assert_close(host(Y.t).astype(np.float64), ref, "gemm_fp8 large scales")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
 def test_gemm_fp8_integer_case_bit_exact():
@@ -183,23 +298,71 @@ def test_gemm_nvfp4_matches_oracle(M, K, N, seed):
     say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
-def test_gemm_nvfp4_prefill_sampled_rows_and_row_invariance():
+def test_gemm_nvfp4_prefill_full_and_row_invariance():
+    """M = 4096, K = 2048, N = 8192: every output against the oracle behind
+    guard regions, and rows bit-identical across M."""
     import torch
     M, K, N = 4096, 2048, 8192
     rng = synth.rng_for(22)
     X = synth.activations(rng, M, K)
     W = synth.nvfp4_matrix(rng, K, N)
     Wd, Xd = nvfp4_dev(W), t(X)
-    Y = host(ql.qlinear_gemm_nvfp4(Wd, Xd))
-    rows = np.sort(synth.rng_for(23).choice(M, 64, replace=False))
-    ref = oracle.linear_nvfp4(X[rows], W)
-    assert_close(Y[rows].astype(np.float64), ref, "gemm_nvfp4 sampled rows")
+    Yg = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_nvfp4(Wd, Xd, Yg.t)
+    torch.cuda.synchronize()
+    Yg.check("gemm_nvfp4 prefill")
+    Y = host(Yg.t)
+    rel, mx = assert_close(Y.astype(np.float64), oracle.linear_nvfp4(X, W), "gemm_nvfp4 prefill")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
     for m in (0, 255, 4095):
         for MM in (1, 256):
             lo = min(m, M - MM)
             part = host(ql.qlinear_gemm_nvfp4(Wd, Xd[lo:lo + MM].contiguous()))
             assert np.array_equal(part[m - lo].view(np.uint16), Y[m].view(np.uint16)), (m, MM)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(100, 64, 300, 53), (300, 256, 520, 54)])
+def test_gemm_nvfp4_all_block_scales_nan_aware(M, K, N, seed):
+    """E4M3 block scales over all 256 bytes: columns with a NaN block scale
+    are NaN in every row, the rest within the bar."""
+    import torch
+    say(f"gemm_nvfp4 all block scales M={M} K={K} N={N}")
+    rng = synth.rng_for(seed)
+    X = synth.activations(rng, M, K)
+    W = synth.nvfp4_matrix(rng, K, N, all_codes=True)
+    ref = oracle.linear_nvfp4(X, W)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_nvfp4(nvfp4_dev(W), t(X), Y.t)
+    torch.cuda.synchronize()
+    Y.check("gemm_nvfp4 all block scales")
+    n_nan = assert_close_nan(host(Y.t), ref, "gemm_nvfp4 all block scales")
+    say(f"  NaN outputs {n_nan} of {M * N}")
+    assert 0 < n_nan < M * N
+
+
+def test_gemm_nvfp4_large_global_scale():
+    """A global scale of 10000 with block scales 0.25 .. 7.5: block scales up
+    to 75000, above fp16's largest value, with E2M1 codes of magnitude 0 and
+    0.5 only, so every weight (at most 37500) is representable.  The block
+    scale and the product are formed in fp32 and rounded once, so the
+    output is within the bar."""
+    import torch
+    M, K, N = 200, 512, 384
+    rng = synth.rng_for(55)
+    X = synth.f16(1e-4 * rng.standard_normal((M, K)))
+    W = synth.nvfp4_matrix(rng, K, N, global_scale=10000.0)
+    W["qweight"] = (W["qweight"] & np.uint32(0x99999999)).astype(np.uint32)  # sign and 0 / 0.5
+    bs = oracle.e4m3_to_f64(W["block_scales"]) * float(W["global_scale"])
+    assert bs.max() > 65504
+    assert np.abs(oracle.dequantize_nvfp4(W["qweight"], W["block_scales"], W["global_scale"], K)).max() < 65504
+    ref = oracle.linear_nvfp4(X, W)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_nvfp4(nvfp4_dev(W), t(X), Y.t)
+    torch.cuda.synchronize()
+    Y.check("gemm_nvfp4 large global")
+    rel, mx = assert_close(host(Y.t).astype(np.float64), ref, "gemm_nvfp4 large global scale")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
 def test_gemm_nvfp4_integer_case_bit_exact():

@@ -7,7 +7,7 @@ import pytest
 import bit_group_quantized_amd as ql
 import oracle
 import synth
-from tests.gpu_util import assert_close, host, say, t, w4_dev
+from tests.gpu_util import assert_close, guarded, host, say, t, w4_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -91,9 +91,13 @@ def test_gemv_argmax_vocab_head():
     say(f"gemv_argmax head K={K} N={N}")
     c = synth.gemv_case(1, K, N)
     tok_ref, logits_ref = oracle.lm_head_token(c["x"][0], c["W"])
-    tok = ql.qlinear_gemv_argmax(w4_dev(c["W"]), t(c["x"][0]))
+    logits = guarded(N, torch.float16)
+    tok = ql.qlinear_gemv_argmax(w4_dev(c["W"]), t(c["x"][0]), logits=logits.t)
     torch.cuda.synchronize()
+    logits.check("argmax head logits")
     _check_token(int(host(tok)[0]), logits_ref, "argmax head")
+    rel, mx = assert_close(host(logits.t).astype(np.float64), logits_ref, "argmax head logits")
+    say(f"  logits rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
 def test_gemv_argmax_ties_and_nan():

@@ -5,7 +5,7 @@ import pytest
 import bit_group_quantized_amd as ql
 import oracle
 import synth
-from tests.gpu_util import assert_close, host, say, t, w4_dev
+from tests.gpu_util import assert_close, guarded, host, say, t, w4_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -18,29 +18,49 @@ pytestmark = pytest.mark.gpu
 ])
 def test_gemm_matches_oracle(M, K, N, seed):
     """Ragged M and N in every tile class of the shape table (64 x 128,
-    128 x 128, 128 x 256 and 256 x 256 tiles)."""
+    128 x 128, 128 x 256 and 256 x 256 tiles), outputs behind guard
+    regions."""
     import torch
     say(f"gemm M={M} K={K} N={N} seed={seed}")
     case = synth.gemm_case(seed, M, K, N)
     ref = oracle.linear(case["X"], case["W"])
-    Y = host(ql.qlinear_gemm(w4_dev(case["W"]), t(case["X"]))).astype(np.float64)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm(w4_dev(case["W"]), t(case["X"]), Y.t)
     torch.cuda.synchronize()
-    assert_close(Y, ref, f"gemm M={M} K={K} N={N}")
+    Y.check(f"gemm M={M} K={K} N={N}")
+    assert_close(host(Y.t).astype(np.float64), ref, f"gemm M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M", [4096, 16384])
-def test_gemm_prefill_sampled_rows(M):
-    """The prefill workload (K = 2048, N = 8192) in the benchmark's launch
-    configuration; 192 sampled rows checked against the oracle."""
+def test_gemm_prefill_full():
+    """The prefill workload (M = 4096, K = 2048, N = 8192) in the benchmark's
+    launch configuration (256 x 256 tiles): every output against the
+    oracle, behind guard regions."""
     import torch
-    K, N = 2048, 8192
+    M, K, N = 4096, 2048, 8192
     say(f"gemm prefill M={M}")
     case = synth.gemm_case(0, M, K, N)
-    Y = host(ql.qlinear_gemm(w4_dev(case["W"]), t(case["X"]))).astype(np.float64)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm(w4_dev(case["W"]), t(case["X"]), Y.t)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, M - 1], np.linspace(0, M - 1, 189).astype(np.int64)]))
+    Y.check("gemm prefill")
+    rel, mx = assert_close(host(Y.t).astype(np.float64), oracle.linear(case["X"], case["W"]), "gemm prefill")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+def test_gemm_prefill_16384_sampled_rows():
+    """M = 16384 (the same tile instance as M = 4096, checked in full there):
+    2048 sampled rows against the oracle, the output behind guard regions."""
+    import torch
+    M, K, N = 16384, 2048, 8192
+    say(f"gemm prefill M={M}")
+    case = synth.gemm_case(0, M, K, N)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm(w4_dev(case["W"]), t(case["X"]), Y.t)
+    torch.cuda.synchronize()
+    Y.check("gemm prefill 16384")
+    rows = np.unique(np.concatenate([[0, 1, M - 1], np.linspace(0, M - 1, 2045).astype(np.int64)]))
     ref = oracle.linear(case["X"][rows], case["W"])
-    assert_close(Y[rows], ref, f"gemm M={M} sample")
+    assert_close(host(Y.t)[rows].astype(np.float64), ref, f"gemm M={M} sample")
 
 
 def test_gemm_row_invariance():
@@ -97,9 +117,11 @@ def test_gemm_few_rows_matches_oracle(M, K, N, seed):
     say(f"gemm_few_rows M={M} K={K} N={N} seed={seed}")
     case = synth.gemm_case(seed, M, K, N)
     ref = oracle.linear(case["X"], case["W"])
-    Y = host(ql.qlinear_gemm_few_rows(w4_dev(case["W"]), t(case["X"]))).astype(np.float64)
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_few_rows(w4_dev(case["W"]), t(case["X"]), Y.t)
     torch.cuda.synchronize()
-    assert_close(Y, ref, f"gemm_few_rows M={M} K={K} N={N}")
+    Y.check(f"gemm_few_rows M={M} K={K} N={N}")
+    assert_close(host(Y.t).astype(np.float64), ref, f"gemm_few_rows M={M} K={K} N={N}")
 
 
 def test_gemm_few_rows_row_invariance_and_determinism():

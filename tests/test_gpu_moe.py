@@ -10,7 +10,7 @@ import pytest
 import bit_group_quantized_amd as ql
 import oracle
 import synth
-from tests.gpu_util import assert_close, host, say, t, w4_dev
+from tests.gpu_util import assert_close, guarded, host, say, t, w4_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -131,22 +131,47 @@ def test_moe_decode_fused_down_shapes(T, D, I, E, topk, seed):
     _compare(*res, ref, T, topk)
 
 
-SCREENED = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
+_SEEDS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))
+SCREENED = _SEEDS["kept_seeds_by_gap"]
+FULL_ORDER = _SEEDS["kept_seeds_full_order"]
 
 
-@pytest.mark.parametrize("seed", SCREENED[:1])
+@pytest.mark.parametrize("seed", FULL_ORDER[:1])
 def test_moe_prefill_4096(seed):
     """The prefill workload: 4096 tokens, 256 experts + shared, Zipf logit
-    bias, in the benchmark's launch configuration."""
+    bias, in the benchmark's launch configuration, on a full-order screened
+    seed: routing ids, counts, offsets, permutation and inverse equal the
+    oracle's bit for bit, and act, ydown and out are compared row by row in
+    the oracle's own row order, every output behind guard regions."""
     import torch
     say(f"moe prefill T=4096 seed={seed}")
+    T, topk = 4096, 8
     w = synth.moe_weights(0)
-    tok = synth.moe_tokens(seed, 4096, skewed=True)
-    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], 8)
+    tok = synth.moe_tokens(seed, T, skewed=True)
+    ref = oracle.moe_layer(tok["H"], w, tok["logit_bias"], topk)
     dw = _dev_weights(w)
-    res = _run_layer(dw, t(tok["H"]), t(tok["logit_bias"]), 8, 4096, False)
+    from tests.test_gpu_route import guarded_route_outputs
+    route, check_route = guarded_route_outputs(T, 256, topk)
+    act = guarded((T * topk + T, 512), torch.float16)
+    ydown = guarded((T * topk + T, 2048), torch.float16)
+    out = guarded((T, 2048), torch.float16)
+    H = t(tok["H"])
+    ql.moe_route(H, dw["Wr"], t(tok["logit_bias"]), topk, route)
+    ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, topk, ql.QL_OP_GATE_UP_SILU, route, act.t)
+    ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act.t, T, topk, ql.QL_OP_DOWN, route, ydown.t)
+    ql.moe_combine(ydown.t, route["gates"], route["pos"], T, topk, True, out.t)
     torch.cuda.synchronize()
-    rel, mx = _compare(*res, ref, 4096, 8)
+    check_route()
+    for g, name in ((act, "act"), (ydown, "ydown"), (out, "out")):
+        g.check(name)
+    assert np.array_equal(host(route["ids"]), ref["ids"])
+    assert np.array_equal(host(route["counts"]), ref["counts"])
+    assert np.array_equal(host(route["offsets"]), ref["offsets"])
+    assert np.array_equal(host(route["sorted_assign"]), ref["sorted_assign"])
+    assert np.array_equal(host(route["pos"]), ref["pos"])
+    assert_close(host(act.t).astype(np.float64), ref["act"].astype(np.float64), "act")
+    assert_close(host(ydown.t).astype(np.float64), ref["ydown"], "ydown")
+    rel, mx = assert_close(host(out.t).astype(np.float64), ref["out"], "out")
     say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
 
 
@@ -359,3 +384,69 @@ def test_decode_token_loop_through_moe_graph():
             assert np.array_equal(host(xs[i + 1][0]).view(np.uint16), rows[i].view(np.uint16)), (rep, i)
             assert_close(host(dec[i]["out"][0]).astype(np.float64), outs[i], f"layer output {i}")
         assert host(slots).tolist() == [toks[steps - 2], toks[steps - 1]], rep
+
+
+@pytest.mark.parametrize("where,scale", [("h", 1e-4), ("h", 3e-5), ("act", 1e-4), ("act", 3e-5)])
+def test_moe_decode_small_activations(where, scale):
+    """Row-kernel inputs of order 1e-4 and 3e-5, many of them fp16
+    subnormals, on the decode shape.  where = "h": the tokens are that small
+    (the router weight and the gate/up scales are scaled up by the inverse,
+    so logits and act keep their usual size); where = "act": the gate/up
+    scales are scaled down so that act is that small (the down scales are
+    scaled up by the inverse).  moe_decode and the three-call path against
+    the oracle, routing exact."""
+    import torch
+    say(f"moe_decode small {where} scale={scale}")
+    D, I, E = 2048, 512, 256
+    if where == "h":
+        w = synth.moe_weights(7, scale_range=(0.002 / scale, 0.02 / scale), router_std=0.02 / scale)
+        rng = synth.rng_for(8)
+        w["down"] = synth.w4_matrix(rng, I, D, lead=(E,))
+        w["shared_down"] = synth.w4_matrix(rng, I, D)
+        tok = synth.moe_tokens(1007, 1, h_scale=scale)
+    else:
+        f = np.sqrt(2.0 * scale) / 2.25  # |u| ~ 2.25 f, act ~ u^2 / 2 ~ scale
+        w = synth.moe_weights(7, scale_range=(0.002 * f, 0.02 * f))
+        rng = synth.rng_for(8)
+        w["down"] = synth.w4_matrix(rng, I, D, lead=(E,), scale_range=(0.002 / scale, 0.02 / scale))
+        w["shared_down"] = synth.w4_matrix(rng, I, D, scale_range=(0.002 / scale, 0.02 / scale))
+        tok = synth.moe_tokens(1007, 1)
+    ref = oracle.moe_layer(tok["H"], w, None, 8)
+    a = np.abs(ref["act"].astype(np.float64))
+    say(f"  act: median {np.median(a):.2e}, fp16-subnormal share {np.mean(a < 2.0**-14):.2f}")
+    srt = -np.sort(-ref["logits"][0])
+    assert srt[7] - srt[8] > 1e-4 * max(1.0, abs(srt[0])), "routing near a tie"
+    dw = _dev_weights(w)
+    H = t(tok["H"])
+    res = ql.moe_decode(H, dw["Wr"], None, 8, **_decode_args(dw))
+    route, act, _, out3 = _run_layer(dw, H, None, 8, 1, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["ids"]), ref["ids"])
+    rel, mx = assert_close(host(res["out"]).astype(np.float64), ref["out"], "moe_decode out")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+    assert_close(host(act).astype(np.float64), ref["act"][_ref_rows(route, ref, 1, 8)].astype(np.float64), "act")
+    assert_close(host(out3).astype(np.float64), ref["out"], "three-call out")
+
+
+@pytest.mark.parametrize("T,seed", [(1, 2037), (2, 677), (4, 75)])
+def test_moe_decode_exact_routing_every_token(T, seed):
+    """moe_decode on router inputs with exact fp32 logits; each seed holds a
+    token with two equal logits across the top-k cut (found by searching
+    seeds with the oracle).  The ids equal the oracle's for every token (the
+    tie goes to the lower expert index), the logits bit for bit, the gates
+    within 2e-6."""
+    import torch
+    say(f"moe_decode exact routing T={T}")
+    c = synth.router_exact_case(seed, T)
+    w = synth.moe_weights(seed)
+    w["Wr"] = c["Wr"]
+    ref = oracle.moe_layer(c["H"], w, c["logit_bias"], 8)
+    dw = _dev_weights(w)
+    res = ql.moe_decode(t(c["H"]), dw["Wr"], t(c["logit_bias"]), 8, **_decode_args(dw))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["ids"]), ref["ids"])
+    assert np.abs(host(res["gates"]).astype(np.float64) - ref["gates"]).max() < 2e-6
+    off = ql.moe_decode_logits_offset(T, 256, 8)
+    Lg = host(res["workspace"])[off:off + 4 * T * 256].view(np.float32).reshape(T, 256)
+    assert np.array_equal(Lg.astype(np.float64), ref["logits"])
+    assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")

@@ -10,7 +10,7 @@ import pytest
 import bit_group_quantized_amd as ql
 import oracle
 import synth
-from tests.gpu_util import host, say, t
+from tests.gpu_util import guarded, host, say, t
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,22 @@ def _ws_tiles(out):
     ws = host(out["workspace"]).view(np.int32)
     n = int(ws[0])
     return ws[:8], ws[8:8 + 4 * n].reshape(n, 4)
+
+
+def guarded_route_outputs(T, E, topk):
+    """moe_route / moe_dispatch outputs carved out of guarded buffers; the
+    second value checks every guard."""
+    import torch
+    g = {"ids": guarded((T, topk), torch.int32), "gates": guarded((T, topk), torch.float32),
+         "counts": guarded((E,), torch.int32), "offsets": guarded((E + 1,), torch.int32),
+         "sorted_assign": guarded((T * topk,), torch.int32), "pos": guarded((T * topk,), torch.int32),
+         "workspace": guarded((max(ql.moe_workspace_bytes(T, E, topk), 256),), torch.uint8)}
+    out = {k: v.t for k, v in g.items()}
+
+    def check():
+        for k, v in g.items():
+            v.check(k)
+    return out, check
 
 
 def _check_dispatch(out, ids, E, T, topk):
@@ -51,8 +67,10 @@ def test_dispatch_bit_exact(T, E, topk, skew, seed):
     say(f"dispatch T={T} E={E} topk={topk} skew={skew}")
     rng = np.random.default_rng(seed)
     ids = synth.synthetic_topk_ids(rng, T, E, topk, skew)
-    out = ql.moe_dispatch(t(ids), E)
+    out, check = guarded_route_outputs(T, E, topk)
+    ql.moe_dispatch(t(ids), E, out)
     torch.cuda.synchronize()
+    check()
     _check_dispatch(out, ids, E, T, topk)
 
 
@@ -118,21 +136,46 @@ def test_route_decode_token(seed):
     _check_dispatch(out, ids_ref, 256, 1, 8)
 
 
-SCREENED = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))["kept_seeds_by_gap"]
+_SEEDS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "prefill_seeds.json")))
+SCREENED = _SEEDS["kept_seeds_by_gap"]
+# Seeds whose every adjacent gap among a token's 9 largest exact logits
+# exceeds 2e-5 (tests/golden/screen_prefill_seeds.py); with an fp32 logit
+# error below 1e-5 (asserted) every routing decision, order included, is
+# determined.
+FULL_ORDER = _SEEDS["kept_seeds_full_order"]
+FULL_ORDER_LOGIT_ERR = 1e-5
 
 
-@pytest.mark.parametrize("T,skewed,seed", [(4096, True, SCREENED[0]), (4096, True, SCREENED[1]),
-                                           (4096, True, 2), (333, False, 3), (16, True, 4)])
-def test_route_prefill(T, skewed, seed):
+@pytest.mark.parametrize("T,skewed,seed,screened", [
+    (4096, True, FULL_ORDER[0], True), (4096, True, FULL_ORDER[1], True),
+    (4096, True, SCREENED[0], False), (4096, True, 2, False), (333, False, 3, False),
+    (16, True, 4, False)])
+def test_route_prefill(T, skewed, seed, screened):
+    """moe_route on the prefill workload.  On the full-order screened seeds
+    (every adjacent gap among a token's 9 largest exact logits above 2e-5,
+    tests/golden/screen_prefill_seeds.py) the GPU's fp32 logits must lie
+    within 1e-5 of the exact ones, and then the ids (in order), counts,
+    offsets, permutation, inverse and tile map must equal the oracle's bit
+    for bit; elsewhere near-tied positions are checked for validity."""
     import torch
-    say(f"route T={T} skewed={skewed} seed={seed}")
+    say(f"route T={T} skewed={skewed} seed={seed} screened={screened}")
     w = synth.moe_weights(0)
     tok = synth.moe_tokens(seed, T, skewed=skewed)
     bias_dev = t(tok["logit_bias"]) if skewed else None
-    out = ql.moe_route(t(tok["H"]), t(w["Wr"]), bias_dev, 8)
+    out, check = guarded_route_outputs(T, 256, 8)
+    ql.moe_route(t(tok["H"]), t(w["Wr"]), bias_dev, 8, out)
     torch.cuda.synchronize()
+    check()
     exact, near, ids_ref = _check_route(out, tok["H"], w["Wr"], tok["logit_bias"], 8, T, 256)
     say(f"  near-tie positions: {int(near.sum())}, ids identical: {exact}")
+    if screened:
+        off = ql.ql_moe_logits_offset(T, 256, 8)
+        Lg = host(out["workspace"])[off:off + 4 * T * 256].view(np.float32).reshape(T, 256)
+        L64 = oracle.router_logits(tok["H"], w["Wr"], tok["logit_bias"])
+        err = float(np.abs(Lg - L64).max())
+        say(f"  fp32 logit error {err:.2e}")
+        assert err < FULL_ORDER_LOGIT_ERR
+        assert exact, "routing ids differ from the oracle's on a full-order screened seed"
     if exact:
         _check_dispatch(out, ids_ref, 256, T, 8)
     else:
@@ -140,6 +183,38 @@ def test_route_prefill(T, skewed, seed):
     # Without a near tie at the k/k+1 boundary the chosen sets must agree.
     if not near[:, -1].any():
         assert all(set(a) == set(b) for a, b in zip(host(out["ids"]).tolist(), ids_ref.tolist()))
+
+
+@pytest.mark.parametrize("T,E,topk,skewed,seed", [
+    (4096, 256, 8, True, 0), (4096, 256, 8, True, 1), (4096, 256, 8, False, 2),
+    (1, 256, 8, True, 3), (4, 256, 8, True, 4), (16, 256, 8, True, 5), (17, 256, 8, True, 6),
+    (777, 256, 8, True, 7),
+])
+def test_route_exact_arithmetic_every_token(T, E, topk, skewed, seed):
+    """Routing on inputs whose fp32 logits are exact (synth.router_exact_case:
+    the GPU's logits then equal the oracle's float64 logits bit for bit), so
+    the oracle's top-k, histogram, scan, permutation and tile map are the
+    only correct answer for every token, exact ties and near ties included:
+    everything must match bit for bit, on the many-token MFMA router and on
+    the small-T path."""
+    import torch
+    say(f"route exact arithmetic T={T} skewed={skewed} seed={seed}")
+    c = synth.router_exact_case(seed, T, E=E, skewed=skewed)
+    L64 = oracle.router_logits(c["H"], c["Wr"], c["logit_bias"])
+    ids_ref, gates_ref = oracle.topk_route(L64, topk)
+    srt = -np.sort(-L64, axis=1)
+    n_ties = int(np.sum(srt[:, topk - 1] == srt[:, topk]))
+    out, check = guarded_route_outputs(T, E, topk)
+    ql.moe_route(t(c["H"]), t(c["Wr"]), t(c["logit_bias"]) if skewed else None, topk, out)
+    torch.cuda.synchronize()
+    check()
+    say(f"  tokens with an exact tie across the top-k cut: {n_ties}")
+    off = ql.ql_moe_logits_offset(T, E, topk)
+    Lg = host(out["workspace"])[off:off + 4 * T * E].view(np.float32).reshape(T, E)
+    assert np.array_equal(Lg.astype(np.float64), L64)
+    assert np.array_equal(host(out["ids"]), ids_ref)
+    assert np.abs(host(out["gates"]).astype(np.float64) - gates_ref).max() < 2e-6
+    _check_dispatch(out, ids_ref, E, T, topk)
 
 
 @pytest.mark.parametrize("T,E,topk,seed", [

@@ -115,6 +115,9 @@ _SIGS = {
                                        ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
                                        ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P,
                                        ctypes.c_size_t, _P, _P]),
+    "moe_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
+                                          ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
+                                          ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -539,6 +542,33 @@ def moe_decode(H, Wr, logit_bias, topk: int, gate_up: dict, down: dict, shared_g
         _ptr(out["ids"]), _ptr(out["gates"]), _ptr(ws), ws.numel(), _ptr(out["out"]),
         _stream(stream)))
     return out
+
+
+QL_DECODE_SCRATCH_BYTES = 1 << 20
+
+
+def moe_decode_noalloc(H, Wr, logit_bias, topk: int, gate_up: dict, down: dict, shared_gate_up=None,
+                       shared_down=None, ids=None, gates=None, out=None, stream=None):
+    """moe_decode on the library's own device scratch (no workspace
+    argument); ids, gates and out are caller-owned and allocated here only
+    when not given.  Returns (ids, gates, out)."""
+    import torch
+    T, D = H.shape
+    E = Wr.shape[1]
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=H.device)
+    if gates is None:
+        gates = torch.empty((T, topk), dtype=torch.float32, device=H.device)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float16, device=H.device)
+    gu, dn = make_w4_experts(gate_up), make_w4_experts(down)
+    sg = make_w4(shared_gate_up) if shared_gate_up is not None else None
+    sd = make_w4(shared_down) if shared_down is not None else None
+    _check("moe_decode_noalloc", lib().moe_decode_noalloc(
+        _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, ctypes.byref(gu), ctypes.byref(dn),
+        ctypes.byref(sg) if sg is not None else None, ctypes.byref(sd) if sd is not None else None,
+        _ptr(ids), _ptr(gates), _ptr(out), _stream(stream)))
+    return ids, gates, out
 
 
 def moe_combine(Ydown, gates, pos, T: int, topk: int, has_shared: bool, out=None, stream=None):

@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libqlinear.so"
-SOURCES = ["gemv.hip", "gemm.hip", "route.hip", "misc.hip", "codecs.hip", "capi.cpp"]
+SOURCES = ["gemv.hip", "gemm.hip", "route.hip", "misc.hip", "codecs.hip", "noalloc.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 COMMON = [

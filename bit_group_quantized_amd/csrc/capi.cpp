@@ -467,11 +467,14 @@ size_t moe_decode_logits_offset(int32_t T, int32_t E, int32_t topk) {
     return ql::moe_decode_layout(T, E, topk, 64).logits;
 }
 
+// ws_mode 0: the caller's workspace; 1: the library's scratch array
+// (moe_decode_noalloc), checked against QL_DECODE_SCRATCH_BYTES.
 static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
                        int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
                        const ql_w4_experts* down, const ql_w4* shared_gate_up,
                        const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
-                       void* workspace, size_t ws_bytes, uint16_t* out, void* stream, bool bf16) {
+                       void* workspace, size_t ws_bytes, uint16_t* out, void* stream, bool bf16,
+                       int ws_mode = 0) {
     if (!gate_up || !down) return QL_ERR_INVALID_ARG;
     if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
     if (T < 0 || E <= 0 || topk <= 0 || topk > E || D <= 0) return QL_ERR_INVALID_ARG;
@@ -502,8 +505,15 @@ static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit
     if (!aligned(H, 16) || !aligned(Wr, 16) || !aligned(logit_bias, 4) || !aligned(topk_ids, 4) ||
         !aligned(topk_gates, 4) || !aligned(out, 2))
         return QL_ERR_MISALIGNED;
-    if (!workspace || ws_bytes < moe_decode_workspace_bytes(T, E, topk, I)) return QL_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
+    if (ws_mode == 1) {
+        if (moe_decode_workspace_bytes(T, E, topk, I) > QL_DECODE_SCRATCH_BYTES) return QL_ERR_WORKSPACE;
+        unsigned char* p = nullptr;
+        if (const int rc2 = ql::decode_scratch(&p)) return rc2;
+        workspace = p;
+    } else {
+        if (!workspace || ws_bytes < moe_decode_workspace_bytes(T, E, topk, I)) return QL_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
+    }
     ql::DecodeArgs a{H, Wr, logit_bias, T, D, E, topk, I,
                      gu.qweight, gu.scales, gu.biases, dn.qweight, dn.scales, dn.biases,
                      shared_gate_up ? shared_gate_up->qweight : nullptr,
@@ -531,6 +541,15 @@ int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bi
                     void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
     return decode_impl(H, Wr, logit_bias, T, D, E, topk, gate_up, down, shared_gate_up, shared_down,
                        topk_ids, topk_gates, workspace, ws_bytes, out, stream, true);
+}
+
+int moe_decode_noalloc(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                       int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
+                       const ql_w4_experts* down, const ql_w4* shared_gate_up,
+                       const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
+                       uint16_t* out, void* stream) {
+    return decode_impl(H, Wr, logit_bias, T, D, E, topk, gate_up, down, shared_gate_up, shared_down,
+                       topk_ids, topk_gates, nullptr, 0, out, stream, false, 1);
 }
 
 static int combine_impl(const uint16_t* Ydown, const float* topk_gates, const int32_t* assign_pos,

@@ -197,6 +197,9 @@ struct DecodeArgs {
     bool bf16 = false;  // H, Wr, scales, biases, act and out hold bf16 patterns
 };
 int launch_moe_decode(const DecodeArgs& a, hipStream_t st);
+// This device's copy of the library's decode scratch array
+// (QL_DECODE_SCRATCH_BYTES), resolved on the first call on each device.
+int decode_scratch(unsigned char** ptr);
 
 int launch_combine(const uint16_t* Yd, const float* gates, const int32_t* pos, int T, int topk,
                    int N, int has_shared, uint16_t* out, hipStream_t st, bool bf16 = false);

@@ -90,6 +90,7 @@ extern "C" {
 #define QL_MAX_TOPK 32
 #define QL_MAX_K 32768
 #define QL_DECODE_MAX_T 4 /* largest T served by the row-parallel expert path */
+#define QL_DECODE_SCRATCH_BYTES (1u << 20) /* device scratch of moe_decode_noalloc */
 
 /* One w4 matrix (host struct holding device pointers). */
 typedef struct ql_w4 {
@@ -578,6 +579,31 @@ int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bi
                     const ql_w4* shared_gate_up, const ql_w4* shared_down,
                     int32_t* topk_ids, float* topk_gates,
                     void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+
+/*
+ * moe_decode_noalloc - moe_decode for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The same three launches, the
+ * same kernels and the same results, bit for bit, as moe_decode; instead
+ * of the caller's workspace they use a device array of
+ * QL_DECODE_SCRATCH_BYTES that the library owns (one copy per GPU, held
+ * until the process ends).  It allocates nothing: the first call on a
+ * device only looks up that device's copy of the array.
+ *   Arguments as moe_decode without workspace and ws_bytes.  The scratch
+ *   needs no initialization.  Calls that may overlap on one GPU (several
+ *   streams or threads) race on the shared scratch and must be serialized
+ *   by the caller; calls on different GPUs do not interact.  The logits of
+ *   the last call stay in the scratch and are not exposed.
+ * Limits: as moe_decode, and moe_decode_workspace_bytes(T, E, topk, I) <=
+ * QL_DECODE_SCRATCH_BYTES (every shape within moe_decode's limits fits).
+ * Errors: as moe_decode; WORKSPACE if the scratch is too small; HIP if the
+ * array cannot be resolved on the current device.
+ */
+int moe_decode_noalloc(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+                       int32_t T, int32_t D, int32_t E, int32_t topk,
+                       const ql_w4_experts* gate_up, const ql_w4_experts* down,
+                       const ql_w4* shared_gate_up, const ql_w4* shared_down,
+                       int32_t* topk_ids, float* topk_gates, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

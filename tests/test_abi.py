@@ -289,6 +289,32 @@ def test_moe_decode_validation(L):
     assert call(T=0) == OK
 
 
+def test_moe_decode_noalloc_validation(L):
+    """Host validation of the no-workspace decode entry: every error is
+    returned before the scratch array is looked up."""
+    GU = ql.ql_w4_experts(A16, A16, A16, 2048, 1024, 64, 256)
+    DN = ql.ql_w4_experts(A16, A16, A16, 512, 2048, 64, 256)
+    SG = ql.ql_w4(A16, A16, A16, 2048, 1024, 64)
+    SD = ql.ql_w4(A16, A16, A16, 512, 2048, 64)
+    f = L.moe_decode_noalloc
+
+    def call(T=1, D=2048, E=256, topk=8, gu=GU, dn=DN, sg=SG, sd=SD, H=A16, out=A16):
+        r = lambda x: ctypes.byref(x) if x is not None else None
+        return f(H, A16, None, T, D, E, topk, r(gu), r(dn), r(sg), r(sd), A16, A16, out, None)
+
+    assert call(T=5) == SHAPE
+    assert call(T=-1) == INVALID
+    assert call(topk=33) == SHAPE
+    assert call(E=128) == INVALID
+    assert call(sd=None) == INVALID
+    assert call(H=A16 + 2) == MISALIGNED
+    assert call(out=None) == INVALID
+    assert call(T=0) == OK
+    assert ql.QL_DECODE_SCRATCH_BYTES == 1 << 20
+    # every shape inside moe_decode's own limits fits the scratch
+    assert L.moe_decode_workspace_bytes(4, 1024, 32, 1024) <= ql.QL_DECODE_SCRATCH_BYTES
+
+
 def test_gemm_fp8_validation(L):
     f = L.qlinear_gemm_fp8
 

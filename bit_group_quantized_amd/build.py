@@ -1,4 +1,5 @@
-"""Build the HIP library (libqlinear.so) in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950: libqlinear.so (the library)
+and libqlprobe.so (the benchmark's HBM read-bandwidth probe).
 
 Usage: python -m bit_group_quantized_amd.build   (or build() from Python)
 Each source is compiled in parallel with hipcc, then linked into a shared
@@ -17,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libqlinear.so"
 SOURCES = ["gemv.hip", "gemm.hip", "route.hip", "misc.hip", "codecs.hip", "noalloc.hip", "capi.cpp"]
+PROBE_NAME = "libqlprobe.so"
+PROBE_SOURCES = ["readprobe.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -42,26 +45,33 @@ def _run(cmd):
     return out
 
 
+def _link(hipcc, sources, name, tmp):
+    objs, cmds = [], []
+    for src in sources:
+        obj = os.path.join(tmp, name + "." + src + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+    return objs, cmds
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     out = os.path.join(PKG, LIB_NAME)
     with tempfile.TemporaryDirectory(prefix="qlbuild_") as tmp:
-        objs = []
-        cmds = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            objs.append(obj)
-            cmds.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        libs = [(out, *_link(hipcc, SOURCES, LIB_NAME, tmp)),
+                (os.path.join(PKG, PROBE_NAME), *_link(hipcc, PROBE_SOURCES, PROBE_NAME, tmp))]
+        cmds = [c for _, _, cs in libs for c in cs]
         with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
             logs = list(ex.map(_run, cmds))
-        tmp_lib = out + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs])
-        os.replace(tmp_lib, out)
+        for path, objs, _ in libs:
+            tmp_lib = path + ".tmp"
+            _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs])
+            os.replace(tmp_lib, path)
     if verbose:
         for l in logs:
             if l.strip():
                 print(l)
-        print(f"built {out}")
+        print(f"built {out} and {PROBE_NAME}")
     return out
 
 

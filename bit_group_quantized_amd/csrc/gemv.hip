@@ -609,8 +609,12 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
             s_lg[e] = sum;
         }
         __syncthreads();
-        if (wave == 0) topk_one_token<EPL, 1>(s_lg, nullptr, s_lg, 0, E, topk, s_sel, s_gate);
-        __syncthreads();
+        if constexpr (EPL <= 4) {
+            topk_block_small(s_lg, E, topk, s_sel, s_gate);  // all four waves; ends with a barrier
+        } else {
+            if (wave == 0) topk_one_token<EPL, 1>(s_lg, nullptr, s_lg, 0, E, topk, s_sel, s_gate);
+            __syncthreads();
+        }
         const int e = min(max(s_sel[j], 0), E - 1);
         wq = qw + (size_t)e * N * wpr;
         ws = sc + (size_t)e * N * G;

@@ -155,4 +155,112 @@ __device__ void topk_one_token(const float* __restrict__ src, const float* __res
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same selection by a whole 256-thread block for one token with E <= 256
+// experts (thread t holds expert t), for the fused decode expert launch where
+// all four waves would otherwise wait for one: the threshold tau of
+// topk_one_token is the topk-th largest of the 64 quad maxima (keys of
+// experts 4q .. 4q+3), each thread counting the maxima above its quad's
+// against a quarter of them; candidates (keys >= tau) are compacted into LDS
+// in expert order across the waves, ranked as in topk_one_token, and wave 0
+// writes the topk experts and their renormalized gates.  Same results as
+// topk_one_token, bit for bit.  logits: LDS, the token's E logits (with any
+// bias already added).  Called by all 256 threads; ends with a barrier.
+// ---------------------------------------------------------------------------
+struct __align__(16) TopkBlockScratch {
+    uint32_t qm[64];          // quad maxima
+    uint32_t tau[4];          // per-wave minima
+    int cnt[4];               // candidates per wave
+    uint32_t ck[256 + 4];     // candidate keys in expert order (+ zero padding)
+    uint16_t ce[256];         // candidate experts
+    uint32_t sk[QL_MAX_TOPK_DEV];
+    int se[QL_MAX_TOPK_DEV];
+};
+
+__device__ void topk_block_small(const float* __restrict__ logits, int E, int topk, int* sel_e,
+                                 float* sel_g) {
+    __shared__ TopkBlockScratch scr;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    uint32_t key = 0u;
+    if (tid < E) {
+        const float s = logits[tid];
+        key = mono32((s != s) ? -INFINITY : s + 0.0f);  // NaN never wins
+    }
+    // 1. quad maxima
+    uint32_t m = max(key, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, 0xB1, 0xF, 0xF, true));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
+    if ((tid & 3) == 0) scr.qm[tid >> 2] = m;
+    __syncthreads();
+    // 2. maxima above this quad's, a quarter per thread, summed over the quad
+    const int c = tid & 3;
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(scr.qm + 16 * c + 4 * i);
+        above += (q.x > m) + (q.y > m) + (q.z > m) + (q.w > m);
+    }
+    above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xF, 0xF, true);
+    above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xF, 0xF, true);
+    const uint32_t tw = wave_min_u32(above < topk ? m : 0xFFFFFFFFu);
+    if (lane == 0) scr.tau[wv] = tw;
+    __syncthreads();
+    const uint32_t tau = min(min(scr.tau[0], scr.tau[1]), min(scr.tau[2], scr.tau[3]));
+    // 3. candidates in expert order across the four waves
+    const bool is = key >= tau;
+    const uint64_t b = __ballot(is);
+    if (lane == 0) scr.cnt[wv] = __popcll(b);
+    __syncthreads();
+    int base = 0, C = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        base += (w < wv) ? scr.cnt[w] : 0;
+        C += scr.cnt[w];
+    }
+    if (is) {
+        const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        scr.ck[at] = key;
+        scr.ce[at] = (uint16_t)tid;
+    }
+    if (tid < 4) scr.ck[C + tid] = 0u;  // padding: never beats a candidate
+    __syncthreads();
+    // 4. ranks; the candidates of rank < topk are the result
+    const int C4 = (C + 3) & ~3;
+    for (int slot = tid; slot < C; slot += 256) {
+        const uint32_t k = scr.ck[slot];
+        int r = 0;
+        for (int cc = 0; cc < C4; cc += 4) {
+            const uint4 q = *reinterpret_cast<const uint4*>(scr.ck + cc);
+            r += (q.x > k) + (q.y > k) + (q.z > k) + (q.w > k);
+            r += (q.x == k && cc < slot) + (q.y == k && cc + 1 < slot) + (q.z == k && cc + 2 < slot) +
+                 (q.w == k && cc + 3 < slot);
+        }
+        if (r < topk) {
+            scr.sk[r] = k;
+            scr.se[r] = scr.ce[slot];
+        }
+    }
+    __syncthreads();
+    // 5. gates: softmax over the chosen logits
+    if (wv == 0) {
+        const float vmax = unmono32(scr.sk[0]);
+        float my_v = 0.f;
+        int my_e = 0;
+        if (lane < topk) {
+            my_v = unmono32(scr.sk[lane]);
+            my_e = scr.se[lane];
+        }
+        const float ex = (lane < topk) ? __expf(my_v - vmax) : 0.f;
+        const float exs[1] = {ex};
+        int unused;
+        const float sum = reduce_rows64<1>(exs, lane, unused);
+        if (lane < topk) {
+            sel_e[lane] = my_e;
+            sel_g[lane] = ex / sum;
+        }
+    }
+    __syncthreads();
+}
+
 }  // namespace ql

@@ -81,52 +81,61 @@ __device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__
     }
 }
 
-// Same partial sums with 16-byte loads: thread (oct, dl) covers experts
-// 8*oct .. 8*oct+7 and the rows dl, dl+8, ... of the block's D slice; the 8
-// row lanes of an expert octet are summed through LDS in a fixed order.
-// Requires E % 8 == 0.
+// The same partial sums, one block per (D slice, group of 32 experts), for
+// more parallelism at few tokens (8 x as many blocks, each reading 4 KB of
+// the router weight at D = 2048): thread (rl, sg) covers the slice's rows
+// rl, rl + 64, ... for experts 32g + 8sg .. 32g + 8sg + 7 (one 16-byte load
+// per row); the 64 row lanes of each expert are summed in a fixed order
+// (eight groups of eight, then the eight group sums).  Requires E % 8 == 0.
 template <bool BF16>
-__device__ __forceinline__ void router_partial_vec_body(const uint16_t* __restrict__ H,
+__device__ __forceinline__ void router_partial_grp_body(const uint16_t* __restrict__ H,
                                                         const uint16_t* __restrict__ Wr,
                                                         float* __restrict__ partials, int D, int E) {
-    __shared__ float red[8][256 + 4];
-    const int t = blockIdx.y, p = blockIdx.x;
+    __shared__ float red[64][33];
+    __shared__ float red2[8][32];
+    const int p = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
     const int rows = D / kRouterParts;
     const int d0 = p * rows;
-    const int dl = threadIdx.x >> 5;  // 0..7
-    const int oct = threadIdx.x & 31;
-    // Every thread runs the same number of slice iterations (the barriers
-    // below are reached uniformly).
-    for (int base = 0; base < E; base += 256) {
-        const int e8 = base + oct * 8;
-        float acc[8];
+    const int rl = threadIdx.x >> 2;  // 0..63
+    const int sg = threadIdx.x & 3;   // 0..3
+    const int e8 = g * 32 + sg * 8;
+    float acc[8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[v] = 0.f;
-        if (e8 < E) {
-#pragma unroll 8
-            for (int d = dl; d < rows; d += 8) {
-                const float h = in16<BF16>(H[(size_t)t * D + d0 + d]);
-                const u32x4 wv = ld_u32x4(Wr + (size_t)(d0 + d) * E + e8);
-                const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+    if (e8 < E) {
+        for (int d = rl; d < rows; d += 64) {
+            const float h = in16<BF16>(H[(size_t)t * D + d0 + d]);
+            const u32x4 wv = ld_u32x4(Wr + (size_t)(d0 + d) * E + e8);
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    acc[2 * v] += h * in16<BF16>((uint16_t)(ww[v] & 0xFFFFu));
-                    acc[2 * v + 1] += h * in16<BF16>((uint16_t)(ww[v] >> 16));
-                }
+            for (int v = 0; v < 4; ++v) {
+                acc[2 * v] += h * in16<BF16>((uint16_t)(ww[v] & 0xFFFFu));
+                acc[2 * v + 1] += h * in16<BF16>((uint16_t)(ww[v] >> 16));
             }
         }
-#pragma unroll
-        for (int v = 0; v < 8; ++v) red[dl][oct * 8 + v] = acc[v];
-        __syncthreads();
-        const int e = base + threadIdx.x;
-        if (e < E) {
-            float sum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sum += red[j][threadIdx.x];
-            partials[((size_t)t * kRouterParts + p) * E + e] = sum;
-        }
-        __syncthreads();
     }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) red[rl][sg * 8 + v] = acc[v];
+    __syncthreads();
+    const int c = threadIdx.x & 31, q = threadIdx.x >> 5;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += red[q * 8 + i][c];
+    red2[q][c] = s;
+    __syncthreads();
+    if (threadIdx.x < 32 && g * 32 + c < E) {
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tot += red2[i][c];
+        partials[((size_t)t * kRouterParts + p) * E + g * 32 + c] = tot;
+    }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+router_partial_grp_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
+                          float* __restrict__ partials, int D, int E) {
+    router_partial_grp_body<BF16>(H, Wr, partials, D, E);
 }
 
 template <bool BF16>
@@ -134,13 +143,6 @@ __global__ void __launch_bounds__(256)
 router_partial_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
                       float* __restrict__ partials, int D, int E) {
     router_partial_body<BF16>(H, Wr, partials, D, E);
-}
-
-template <bool BF16>
-__global__ void __launch_bounds__(256)
-router_partial_vec_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wr,
-                          float* __restrict__ partials, int D, int E) {
-    router_partial_vec_body<BF16>(H, Wr, partials, D, E);
 }
 
 template <int EPL, int NP>
@@ -582,8 +584,8 @@ template <bool BF16>
 void launch_router_partials_t(const uint16_t* H, const uint16_t* Wr, float* partials, int T, int D,
                               int E, hipStream_t st) {
     if (E % 8 == 0)
-        hipLaunchKernelGGL((router_partial_vec_kernel<BF16>), dim3(kRouterParts, T), dim3(256), 0, st,
-                           H, Wr, partials, D, E);
+        hipLaunchKernelGGL((router_partial_grp_kernel<BF16>), dim3(kRouterParts, (E + 31) / 32, T), dim3(256),
+                           0, st, H, Wr, partials, D, E);
     else
         hipLaunchKernelGGL((router_partial_kernel<BF16>), dim3(kRouterParts, T), dim3(256), 0, st, H,
                            Wr, partials, D, E);

@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-primary", action="store_true")
     ap.add_argument("--workload", choices=["all", "gemm", "gemm_prefill", "decode", "bf16", "codecs",
-                                           "moe_decode", "moe_prefill"],
+                                           "moe_decode", "moe_prefill", "latency"],
                     default="all",
                     help="secondary workloads to run after the headline (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -924,6 +924,68 @@ def read_probe(dev):
     return out
 
 
+def probe_lib():
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "bit_group_quantized_amd", "libqlprobe.so"))
+    L.ql_probe_empty.restype = ctypes.c_int
+    L.ql_probe_empty.argtypes = [ctypes.c_void_p]
+    L.ql_probe_chase.restype = ctypes.c_int
+    L.ql_probe_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def latency_budget(dev):
+    """The fixed costs a short dependent chain of launches pays (libqlprobe):
+    the gap one node of a replayed HIP graph adds (a graph of 64 empty
+    kernels on one stream), the cost of an eager launch of an empty kernel,
+    and the round trip of one load that depends on the previous one, as one
+    thread follows a random cycle with a 128-byte stride: "warm" repeats one
+    segment of 2,000 loads of a 2 MB buffer (every line already in L2),
+    "cold" walks fresh segments of a 2 GB buffer (every line missing every
+    cache); median of 5 launches of 2,000 loads."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+
+    def empty(i):
+        if L.ql_probe_empty(st()) != 0:
+            raise RuntimeError("ql_probe_empty failed")
+    for i in range(10):
+        empty(i)
+    torch.cuda.synchronize()
+    out["graph_node_us"] = graph_time(empty, 64, 20) * 1e3
+    out["eager_launch_us"] = timed_steps(empty, 200, 10) * 1e3
+    res = torch.empty(1, dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(0)
+    steps = 2000
+    for name, nbytes, warm in (("warm_L2_2MB", 2 << 20, True), ("cold_2GB", 2 << 30, False)):
+        n = nbytes // 4
+        slots = n // 32                        # one element per 128 bytes
+        perm = rng.permutation(slots).astype(np.int64) * 32
+        nxt = np.zeros(n, dtype=np.uint32)
+        nxt[perm] = np.roll(perm, -1).astype(np.uint32)  # one cycle through every slot
+        buf = torch.from_numpy(nxt.view(np.int32)).to(dev)
+        times = []
+        for rep in range(6):
+            start = int(perm[0 if warm else (rep + 1) * 3 * steps])
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            if L.ql_probe_chase(buf.data_ptr(), n, start, steps, res.data_ptr(), st()) != 0:
+                raise RuntimeError("ql_probe_chase failed")
+            b.record()
+            torch.cuda.synchronize()
+            if rep > 0:
+                times.append(a.elapsed_time(b) * 1e6 / steps)
+        out[f"dependent_load_ns_{name}"] = float(np.median(times))
+        del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -1088,6 +1150,9 @@ def main():
         if args.workload in ("all", "decode"):
             log("bench: decode fusions")
             wl["decode_fusions"] = bench_decode_fusions(args, dev)
+        if args.workload in ("all", "latency", "moe_decode"):
+            log("bench: latency budget")
+            wl["latency_budget"] = latency_budget(dev)
         if args.workload in ("all", "moe_decode", "moe_prefill"):
             w = synth.moe_weights(0)
             note_inputs("moe_weights_seed0", 0, w["Wr"], *w4_arrays(w["gate_up"]), *w4_arrays(w["down"]),

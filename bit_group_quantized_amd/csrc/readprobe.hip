@@ -1,4 +1,7 @@
-// HBM read-bandwidth probe for the benchmark's calibration leg (libqlprobe):
+// Measurement kernels for the benchmark (libqlprobe), not part of the
+// qlinear interface.
+//
+// HBM read-bandwidth probe for the benchmark's calibration leg:
 // the fastest sustained read rate of this chip for the weight-read pattern
 // of the row GEMV, and for a plain streaming read, so that the GEMV's
 // achieved bandwidth can be reported beside a measured ceiling as well as
@@ -67,9 +70,39 @@ __global__ void __launch_bounds__(256) read_stream_kernel(const u32x4* __restric
     block_out(acc, out);
 }
 
+// Latency probes: an empty kernel (the cost of a launch, or of one node of
+// a HIP graph, with no work in it), and one thread following a chain of
+// dependent loads through a buffer (the round trip of one load from
+// wherever the buffer lives: L2, the Infinity Cache or HBM).
+__global__ void empty_kernel() {}
+
+__global__ void chase_kernel(const uint32_t* __restrict__ next, uint32_t mask, uint32_t start, int steps,
+                             uint32_t* __restrict__ out) {
+    // The index mixes in threadIdx.x (0 here: one thread) so that the loads
+    // are vector-memory loads, not scalar ones.
+    uint32_t i = (start ^ threadIdx.x) & mask;
+    for (int s = 0; s < steps; ++s) i = (next[i] ^ threadIdx.x) & mask;  // the mask keeps every load in bounds
+    out[0] = i;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ql_probe_empty(void* stream) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// next: n uint32 indices, n a power of two (values are masked to n - 1);
+// out: one uint32.  One thread follows `steps` dependent loads from `start`.
+int ql_probe_chase(const uint32_t* next, uint32_t n, uint32_t start, int steps, uint32_t* out,
+                   void* stream) {
+    if (!next || !out || n == 0 || (n & (n - 1)) != 0 || steps < 0) return 1;
+    hipLaunchKernelGGL(chase_kernel, dim3(1), dim3(1), 0, reinterpret_cast<hipStream_t>(stream), next, n - 1,
+                       start, steps, out);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
 
 // Blocks a probe launch writes one word each to `out` (uint32).
 size_t ql_probe_out_words(int pattern, size_t bytes) {

@@ -474,11 +474,19 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     constexpr int WC = (MODE == MODE_GATEUP) ? 16 * WN : 32 * WN;
     auto out_vals = [&](int i, int j, int g, float (&v)[4]) {
 #pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+    };
+    // 16-bit outputs; gate/up: silu(gate) * up, rounded once to fp16.
+    auto out16 = [&](int i, int j, int g, uint16_t (&h)[4]) {
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (MODE == MODE_GATEUP)
-                v[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + WN / 2][4 * g + e];
-            else
-                v[e] = acc[i][j][4 * g + e];
+            if constexpr (MODE == MODE_GATEUP) {
+                const float gt = silu(acc[i][j][4 * g + e]), up = acc[i][j + WN / 2][4 * g + e];
+                if constexpr (DT == 1) h[e] = f2bf(gt * up);
+                else h[e] = mul_to_f16(gt, up);
+            } else {
+                h[e] = to16(acc[i][j][4 * g + e]);
+            }
         }
     };
     const int wcol0 = (MODE == MODE_GATEUP) ? n0 + wave_n * (16 * WN) : n0 + wn0;
@@ -520,10 +528,10 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
             for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    float v[4];
-                    out_vals(i, j, g, v);
-                    const uint32_t lo = (uint32_t)to16(v[0]) | ((uint32_t)to16(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)to16(v[2]) | ((uint32_t)to16(v[3]) << 16);
+                    uint16_t h[4];
+                    out16(i, j, g, h);
+                    const uint32_t lo = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    const uint32_t hi = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
                     *reinterpret_cast<uint2*>(reg + fl * LDR + 32 * j + 8 * g + 4 * fh) = make_uint2(lo, hi);
                 }
             __syncthreads();
@@ -549,12 +557,12 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
             for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    float v[4];
-                    out_vals(i, j, g, v);
+                    uint16_t h[4];
+                    out16(i, j, g, h);
                     const int col = wcol0 + 32 * j + 8 * g + 4 * fh;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (col + e < out_cols) yrow[col + e] = to16(v[e]);
+                        if (col + e < out_cols) yrow[col + e] = h[e];
                 }
         }
     }
@@ -710,9 +718,155 @@ gemm_w4_kernel(const KParams p) {
     gemm_tile<WM, WN, WGM, WGN, MODE, DT, WF>(p, job, lds);
 }
 
+// ---------------------------------------------------------------------------
+// Routed tile of at most 32 rows (a lightly loaded expert).  In the staged
+// tile such an expert costs as much per K step as a full one, and its time
+// goes to streaming the weights with only two K steps of loads in flight.
+// Here the tile's activation rows (32 x K fp16, at most 128 KB) are staged
+// into LDS once, behind a single barrier, and each of the 8 waves owns 32
+// weight columns (gate/up: 16 gate columns and the 16 matching up columns)
+// over the whole K: every lane streams its own fragment's 16 code bytes per
+// K step straight into registers, kTinyAhead steps ahead, dequantizes in
+// registers and issues the same MFMAs on the same operand layout in the same
+// order as the staged tile (weights first, k = 32h + 8s + v in slice s,
+// slices and steps ascending), so every output bit is the same.  G = K / 64
+// is a template argument (8, 16 or 32) so that the K loop unrolls and every
+// register ring index is static; scales and biases of the whole K sit in
+// registers.
+// ---------------------------------------------------------------------------
+constexpr int kTinyRows = 32;
+constexpr int kTinyAhead = 16;  // K steps of code loads in flight per lane
+
+__host__ __device__ constexpr size_t tiny_lds_bytes(int K) { return (size_t)kTinyRows * (K + 8) * 2; }
+
+template <int MODE, int DT, int G>
+__device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16* lds) {
+    constexpr int K = G * kGroup, wpr = K / 8;
+    constexpr int LDR = K + 8;  // padded LDS row (fp16): 16-byte fragment reads of 32 rows hit distinct banks
+    static_assert(G == 8 || G == 16 || G == 32, "tiny tile: K of 512, 1024 or 2048");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int fl = lane & 31, fh = lane >> 5;
+    // This lane's weight column (first MFMA operand row fl).
+    int bcol;
+    if constexpr (MODE == MODE_GATEUP) {
+        const int half = p.N / 2;
+        bcol = min(job.n0 + wave * 16 + (fl & 15), half - 1) + ((fl >= 16) ? half : 0);
+    } else {
+        bcol = min(job.n0 + wave * 32 + fl, p.N - 1);
+    }
+    const uint32_t* const wrow = job.wq + (size_t)bcol * wpr + 4 * fh;
+
+    // Code loads of the first kTinyAhead steps go out first.
+    constexpr int AH = kTinyAhead < G ? kTinyAhead : G;
+    u32x4 cw[AH];
+#pragma unroll
+    for (int d = 0; d < AH; ++d) cw[d] = ld_u32x4(wrow + d * 8);
+    // Scales and biases of the whole K, eight steps per 16-byte load.
+    u32x4 s8[G / 8], b8[G / 8];
+#pragma unroll
+    for (int i = 0; i < G / 8; ++i) {
+        s8[i] = ld_u32x4(job.ws + (size_t)bcol * G + 8 * i);
+        b8[i] = ld_u32x4(job.wb + (size_t)bcol * G + 8 * i);
+    }
+    // Activation rows -> LDS: 16 threads per row (32 rows), each loading
+    // every 16th 16-byte chunk of it; padding rows repeat the last real row
+    // (their outputs are not stored).
+    {
+        constexpr int CPT = K / 8 / 16;  // chunks per thread
+        const int r = tid >> 4, c0 = tid & 15;
+        const int lr = min(r, job.rows_valid - 1);
+        int64_t src_row;
+        if constexpr (MODE == MODE_GATEUP)
+            src_row = min(max(p.sorted_assign[job.tile_first + lr] / p.topk, 0), p.T - 1);
+        else
+            src_row = job.out_row0 + lr;
+        const uint16_t* const xr = p.A + src_row * K;
+        u32x4 st[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) st[i] = ld_u32x4(xr + (c0 + 16 * i) * 8);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(lds + r * LDR + (c0 + 16 * i) * 8) = st[i];
+    }
+    __syncthreads();
+
+    const f16* const arow = lds + fl * LDR + 32 * fh;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G; ++ks) {
+        const int set = ks % AH;
+        const uint32_t sw = s8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
+        const uint32_t bw = b8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
+        f16x8 xf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xf[s] = *reinterpret_cast<const f16x8*>(arow + ks * kGroup + 8 * s);
+        f16x8 wf[4];
+        if constexpr (DT == 1) {
+            const float sf = bf2f((uint16_t)sw), bf = bf2f((uint16_t)bw);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wf[s] = __builtin_bit_cast(f16x8, dequant_word_bf16(cw[set][s], sf, bf));
+        } else {
+            const f16 s1 = __builtin_bit_cast(f16, (uint16_t)sw), b1 = __builtin_bit_cast(f16, (uint16_t)bw);
+            const f16x2 s2 = {s1, s1}, b2 = {b1, b1};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wf[s] = dequant_word(cw[set][s], s2, b2);
+        }
+        if (ks + AH < G) cw[set] = ld_u32x4(wrow + (ks + AH) * 8);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if constexpr (DT == 1)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[s]),
+                                                               __builtin_bit_cast(bf16x8, xf[s]), acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[s], xf[s], acc, 0, 0, 0);
+        }
+    }
+
+    // acc[r] = output (weight column 8(r/4) + 4h + r%4 of the wave's 32,
+    // activation row fl).  Gate/up: columns c and c + 16 are gate and up of
+    // one output column, i.e. acc[r] and acc[r + 8] for r < 8.
+    if (fl >= job.rows_valid) return;
+    auto to16 = [](float v) -> uint16_t {
+        if constexpr (DT == 1) return f2bf(v);
+        else return f2h(v);
+    };
+    const int out_cols = (MODE == MODE_GATEUP) ? p.N / 2 : p.N;
+    const int wcol0 = job.n0 + wave * ((MODE == MODE_GATEUP) ? 16 : 32);
+    uint16_t* const yrow = p.Y + ((int64_t)job.out_row0 + fl) * out_cols;
+    const bool vec = (out_cols & 3) == 0 && ((uintptr_t)p.Y & 7) == 0;
+    constexpr int NG = (MODE == MODE_GATEUP) ? 2 : 4;  // runs of 4 columns per lane
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (MODE == MODE_GATEUP) {
+                const float gt = silu(acc[4 * g + e]), up = acc[4 * g + e + 8];
+                if constexpr (DT == 1) h[e] = f2bf(gt * up);
+                else h[e] = mul_to_f16(gt, up);
+            } else {
+                h[e] = to16(acc[4 * g + e]);
+            }
+        }
+        const int col = wcol0 + 8 * g + 4 * fh;
+        if (vec) {
+            if (col < out_cols)
+                *reinterpret_cast<uint2*>(yrow + col) =
+                    make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (col + e < out_cols) yrow[col + e] = h[e];
+        }
+    }
+}
+
 // Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
 // 8 waves of 128 x 64) and short tiles (128 rows, 8 waves of 64 x 64), both
-// 256 columns wide, in one launch.  The tall class (tall routed tiles, then
+// 256 columns wide, in one launch; short routed tiles of at most 32 rows
+// (w4 weights, K of 512, 1024 or 2048) take tiny_tile instead.  The tall class (tall routed tiles, then
 // the shared expert's tiles) comes first in the grid, then the short class;
 // each class is dealt to the XCDs in contiguous runs of (tile, column block)
 // items, so that every XCD gets an equal share of each class.
@@ -723,6 +877,7 @@ static_assert(ShortTile::BM == QL_MOE_TILE_ROWS && TallTile::BM == 2 * QL_MOE_TI
               "tile heights of the tile map");
 constexpr size_t kGroupedLds =
     TallTile::LDS_BYTES > ShortTile::LDS_BYTES ? TallTile::LDS_BYTES : ShortTile::LDS_BYTES;
+static_assert(tiny_lds_bytes(2048) <= kGroupedLds, "tiny tiles stage their rows in the grouped launch's LDS");
 
 // WF = 1: FP8 experts (codes [E][N][K] bytes through p.qw, fp16 scales
 // [E][N][K/64] through p.sc, no biases); WF = 2: NVFP4 experts (codes as the
@@ -785,6 +940,13 @@ gemm_w4_grouped_kernel(const KParams p) {
         if constexpr (WF == 2) job.gscale = p.gscales[e];
     }
     job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
+    if constexpr (WF == 0) {
+        if (!tall && job.rows_valid <= kTinyRows) {
+            if (G == 32) { tiny_tile<MODE, DT, 32>(p, job, lds); return; }
+            if (G == 16) { tiny_tile<MODE, DT, 16>(p, job, lds); return; }
+            if (G == 8) { tiny_tile<MODE, DT, 8>(p, job, lds); return; }
+        }
+    }
     if (tall)
         gemm_tile<4, 2, 2, 4, MODE, DT, WF>(p, job, lds);
     else

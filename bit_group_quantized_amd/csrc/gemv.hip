@@ -523,7 +523,7 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
     if constexpr (MODE == 0) {
         const float up = __shfl_xor(tot, TPR / 2, 64);  // row sel + R/2 of the same team
         if (writer && sel < OUT && n0 + sel < Nout)
-            Y[(size_t)r * Nout + n0 + sel] = out16(silu(tot) * up);
+            Y[(size_t)r * Nout + n0 + sel] = BF16 ? f2bf(silu(tot) * up) : mul_to_f16(silu(tot), up);
     } else {
         if (writer && n0 + sel < Nout) Y[(size_t)r * Nout + n0 + sel] = out16(tot);
     }

@@ -414,4 +414,15 @@ __device__ __forceinline__ float silu(float z) {
     return z / (1.0f + __expf(-z));
 }
 
+// fp16 bits of a * b with one rounding from the exact product
+// (v_fma_mixlo_f16 with fp32 sources and a zero addend).  Left to itself the
+// compiler picks this form in some kernels and an fp32 multiply followed by
+// a conversion (two roundings) in others; the gated activations of every
+// kernel go through this helper so that they round alike.
+__device__ __forceinline__ uint16_t mul_to_f16(float a, float b) {
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return (uint16_t)r;
+}
+
 }  // namespace ql

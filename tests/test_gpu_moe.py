@@ -450,3 +450,65 @@ def test_moe_decode_exact_routing_every_token(T, seed):
     Lg = host(res["workspace"])[off:off + 4 * T * 256].view(np.float32).reshape(T, 256)
     assert np.array_equal(Lg.astype(np.float64), ref["logits"])
     assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+
+
+# Per-expert row counts at the edges of the tile kinds: at most 32 rows
+# (register-streamed tile), 33 (staged short tile), tall tiles of 256 rows
+# and a short remainder, and an empty expert.
+BOUNDARY_COUNTS = [1, 31, 32, 33, 0, 97, 256, 300]
+
+
+def boundary_route(E, counts, seed):
+    """ids [T][1] that give expert e exactly counts[e] rows, in a seeded
+    token order."""
+    rng = np.random.default_rng(seed)
+    return rng.permutation(np.repeat(np.arange(E), counts)).astype(np.int32).reshape(-1, 1)
+
+
+def expert_rows_reference(ids, sorted_assign, H, w, ffn, with_shared=True):
+    """Oracle act / ydown in the GPU's row order: the rows of expert e are
+    its tokens in the order of sorted_assign (checked against the stable
+    permutation), then one shared row per token."""
+    T = ids.shape[0]
+    E = w["gate_up"]["qweight"].shape[0]
+    ref_sorted, _ = oracle.stable_permutation(ids, E)
+    assert np.array_equal(sorted_assign, ref_sorted)
+    tok = sorted_assign.astype(np.int64)  # topk = 1: assignment a is token a
+    acts, yds = [None] * T, [None] * T
+    for e in range(E):
+        rows = np.nonzero(ids[tok, 0] == e)[0]
+        if rows.size == 0:
+            continue
+        sl = lambda W: {"qweight": W["qweight"][e], "scales": W["scales"][e], "biases": W["biases"][e],
+                        "K": W["K"], "N": W["N"]}
+        a, y = ffn(H[tok[rows]], sl(w["gate_up"]), sl(w["down"]))
+        for i, r in enumerate(rows):
+            acts[r], yds[r] = a[i], y[i]
+    act, yd = np.stack(acts), np.stack(yds)
+    if with_shared:
+        sa, sy = ffn(H, w["shared_gate_up"], w["shared_down"])
+        act, yd = np.concatenate([act, sa]), np.concatenate([yd, sy])
+    return act, yd
+
+
+@pytest.mark.parametrize("D,I", [(2048, 512), (1024, 256), (512, 1024)])
+def test_moe_tile_row_boundaries(D, I):
+    """Experts with 1, 31, 32, 33, 0, 97, 256 and 300 rows (moe_dispatch on
+    given ids, topk 1) and the shared expert, at K = 2048, 1024 and 512 for
+    both projections: every act and ydown row against the oracle's FFN of
+    its own expert."""
+    import torch
+    E = len(BOUNDARY_COUNTS)
+    say(f"moe tile boundaries D={D} I={I}")
+    ids = boundary_route(E, BOUNDARY_COUNTS, D + I)
+    T = ids.shape[0]
+    w = synth.moe_weights(D + I, D=D, I=I, E=E)
+    H = synth.moe_tokens(D + I + 1, T, D=D, E=E)["H"]
+    dw = _dev_weights(w)
+    route = ql.moe_dispatch(t(ids), E)
+    act = ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], t(H), T, 1, ql.QL_OP_GATE_UP_SILU, route)
+    yd = ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, 1, ql.QL_OP_DOWN, route)
+    torch.cuda.synchronize()
+    ref_act, ref_yd = expert_rows_reference(ids, host(route["sorted_assign"]), H, w, oracle.expert_ffn)
+    assert_close(host(act).astype(np.float64), ref_act.astype(np.float64), "act")
+    assert_close(host(yd).astype(np.float64), ref_yd, "ydown")

@@ -133,3 +133,28 @@ def test_moe_decode_bf16(T, D, I, E, topk, seed, shared):
     rel, mx = assert_close_bf16(_bits(res["out"]), ref["out"], "out", rel_l2=REL_L2_BF16_MOE,
                                 max_abs_frac=MAX_ABS_FRAC_BF16_MOE)
     say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+
+
+@pytest.mark.parametrize("D,I", [(2048, 512), (512, 1024)])
+def test_moe_bf16_tile_row_boundaries(D, I):
+    """The bf16 grouped GEMMs on experts with 1, 31, 32, 33, 0, 97, 256 and
+    300 rows (moe_dispatch on given ids, topk 1) and the shared expert, at
+    K = 2048 / 512 and 512 / 1024: every act and ydown row against the
+    oracle's bf16 FFN of its own expert."""
+    import torch
+    from tests.test_gpu_moe import BOUNDARY_COUNTS, boundary_route, expert_rows_reference
+    E = len(BOUNDARY_COUNTS)
+    say(f"moe bf16 tile boundaries D={D} I={I}")
+    ids = boundary_route(E, BOUNDARY_COUNTS, D + I + 5)
+    T = ids.shape[0]
+    w = synth.moe_weights_bf16(D + I, D=D, I=I, E=E)
+    H = synth.moe_tokens_bf16(D + I + 1, T, D=D, E=E)["H"]
+    dw = _dev_weights(w)
+    route = ql.moe_dispatch(t(ids), E)
+    act = ql.moe_grouped_gemm_bf16(dw["gate_up"], dw["shared_gate_up"], t(H), T, 1, ql.QL_OP_GATE_UP_SILU, route)
+    yd = ql.moe_grouped_gemm_bf16(dw["down"], dw["shared_down"], act, T, 1, ql.QL_OP_DOWN, route)
+    torch.cuda.synchronize()
+    ref_act, ref_yd = expert_rows_reference(ids, host(route["sorted_assign"]), H, w, oracle.expert_ffn_bf16)
+    bar = dict(rel_l2=REL_L2_BF16_MOE, max_abs_frac=MAX_ABS_FRAC_BF16_MOE)
+    assert_close_bf16(_bits(act), oracle.bf16_to_f64(ref_act), "act", **bar)
+    assert_close_bf16(_bits(yd), ref_yd, "ydown", **bar)

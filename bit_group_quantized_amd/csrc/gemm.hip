@@ -725,25 +725,41 @@ gemm_w4_kernel(const KParams p) {
 // Here the tile's activation rows (32 x K fp16, at most 128 KB) are staged
 // into LDS once, behind a single barrier, and each of the 8 waves owns 32
 // weight columns (gate/up: 16 gate columns and the 16 matching up columns)
-// over the whole K: every lane streams its own fragment's 16 code bytes per
-// K step straight into registers, kTinyAhead steps ahead, dequantizes in
-// registers and issues the same MFMAs on the same operand layout in the same
-// order as the staged tile (weights first, k = 32h + 8s + v in slice s,
-// slices and steps ascending), so every output bit is the same.  G = K / 64
-// is a template argument (8, 16 or 32) so that the K loop unrolls and every
-// register ring index is static; scales and biases of the whole K sit in
-// registers.
+// over the whole K: every lane streams its own fragment's codes (16 bytes per
+// K step, 32 for FP8) straight into registers, 16 K steps ahead (8 for FP8),
+// decodes them in registers exactly as the staged tile does and issues the
+// same MFMAs on the same operand layout in the same order (weights first,
+// k = 32h + 8s + v in slice s, slices and steps ascending), so every output
+// bit is the same.  G = K / 64 is a template argument (8, 16 or 32) so that
+// the K loop unrolls and every register ring index is static; the scales
+// (and biases) of the whole K sit in registers.
 // ---------------------------------------------------------------------------
 constexpr int kTinyRows = 32;
-constexpr int kTinyAhead = 16;  // K steps of code loads in flight per lane
 
 __host__ __device__ constexpr size_t tiny_lds_bytes(int K) { return (size_t)kTinyRows * (K + 8) * 2; }
 
-template <int MODE, int DT, int G>
+// Byte b (0..3) of w as E4M3 / its two E2M1 codes as fp32; b is a constant
+// after unrolling.
+__device__ __forceinline__ float e4m3_byte(uint32_t w, int b) {
+    switch (b) {
+        case 0: return e4m3_to_f32<0>(w);
+        case 1: return e4m3_to_f32<1>(w);
+        case 2: return e4m3_to_f32<2>(w);
+        default: return e4m3_to_f32<3>(w);
+    }
+}
+
+// WF: weight format as in gemm_tile (0 w4, 1 FP8-E4M3, 2 NVFP4).
+template <int MODE, int DT, int G, int WF>
 __device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16* lds) {
     constexpr int K = G * kGroup, wpr = K / 8;
     constexpr int LDR = K + 8;  // padded LDS row (fp16): 16-byte fragment reads of 32 rows hit distinct banks
     static_assert(G == 8 || G == 16 || G == 32, "tiny tile: K of 512, 1024 or 2048");
+    static_assert(WF == 0 || DT == 0, "codec weights: fp16 activations");
+    // K steps of code loads in flight per lane (FP8 codes take twice the registers).
+    constexpr int AHEAD = (WF == 1) ? 8 : 16;
+    constexpr int AH = AHEAD < G ? AHEAD : G;
+    constexpr int CW = (WF == 1) ? 2 : 1;  // 16-byte code loads per lane and step
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int fl = lane & 31, fh = lane >> 5;
@@ -755,19 +771,30 @@ __device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16*
     } else {
         bcol = min(job.n0 + wave * 32 + fl, p.N - 1);
     }
-    const uint32_t* const wrow = job.wq + (size_t)bcol * wpr + 4 * fh;
+    // w4 / NVFP4: words 4h .. 4h+3 of a step (word 4h + s = slice s); FP8:
+    // bytes 32h .. 32h+31 of a step (bytes 32h + 8s .. +7 = slice s).
+    const uint32_t* const wrow = (WF == 1) ? job.wq + ((size_t)bcol * K + 32 * fh) / 4
+                                           : job.wq + (size_t)bcol * wpr + 4 * fh;
+    constexpr int WSTEP = (WF == 1) ? kGroup / 4 : 8;  // u32 words per K step of one column
 
-    // Code loads of the first kTinyAhead steps go out first.
-    constexpr int AH = kTinyAhead < G ? kTinyAhead : G;
-    u32x4 cw[AH];
+    // Code loads of the first AH steps go out first.
+    u32x4 cw[AH][CW];
 #pragma unroll
-    for (int d = 0; d < AH; ++d) cw[d] = ld_u32x4(wrow + d * 8);
-    // Scales and biases of the whole K, eight steps per 16-byte load.
-    u32x4 s8[G / 8], b8[G / 8];
+    for (int d = 0; d < AH; ++d)
 #pragma unroll
-    for (int i = 0; i < G / 8; ++i) {
-        s8[i] = ld_u32x4(job.ws + (size_t)bcol * G + 8 * i);
-        b8[i] = ld_u32x4(job.wb + (size_t)bcol * G + 8 * i);
+        for (int c = 0; c < CW; ++c) cw[d][c] = ld_u32x4(wrow + d * WSTEP + 4 * c);
+    // Scales (and biases) of the whole K: fp16 per step, eight steps per
+    // 16-byte load (w4, FP8); NVFP4: E4M3 block-scale bytes, four steps per
+    // 16-byte load.
+    constexpr int NS = (WF == 2) ? G / 4 : G / 8;
+    u32x4 s8[NS], b8[(WF == 0) ? G / 8 : 1];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        if constexpr (WF == 2)
+            s8[i] = ld_u32x4(reinterpret_cast<const uint8_t*>(job.ws) + (size_t)bcol * (K / 16) + 16 * i);
+        else
+            s8[i] = ld_u32x4(job.ws + (size_t)bcol * G + 8 * i);
+        if constexpr (WF == 0) b8[i] = ld_u32x4(job.wb + (size_t)bcol * G + 8 * i);
     }
     // Activation rows -> LDS: 16 threads per row (32 rows), each loading
     // every 16th 16-byte chunk of it; padding rows repeat the last real row
@@ -797,23 +824,61 @@ __device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16*
 #pragma unroll
     for (int ks = 0; ks < G; ++ks) {
         const int set = ks % AH;
-        const uint32_t sw = s8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
-        const uint32_t bw = b8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
         f16x8 xf[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) xf[s] = *reinterpret_cast<const f16x8*>(arow + ks * kGroup + 8 * s);
         f16x8 wf[4];
-        if constexpr (DT == 1) {
-            const float sf = bf2f((uint16_t)sw), bf = bf2f((uint16_t)bw);
+        if constexpr (WF == 1) {
+            // fp16(e4m3 * scale): exact decode, one packed fp16 multiply.
+            const uint32_t sw = s8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
+            const f16 sv = __builtin_bit_cast(f16, (uint16_t)sw);
+            const f16x2 s2 = {sv, sv};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wf[s] = __builtin_bit_cast(f16x8, dequant_word_bf16(cw[set][s], sf, bf));
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t c0 = cw[set][s >> 1][2 * (s & 1)], c1 = cw[set][s >> 1][2 * (s & 1) + 1];
+                u32x4 o;
+                o.x = as_u32(e4m3x2_to_f16x2<false>(c0) * s2);
+                o.y = as_u32(e4m3x2_to_f16x2<true>(c0) * s2);
+                o.z = as_u32(e4m3x2_to_f16x2<false>(c1) * s2);
+                o.w = as_u32(e4m3x2_to_f16x2<true>(c1) * s2);
+                wf[s] = __builtin_bit_cast(f16x8, o);
+            }
+        } else if constexpr (WF == 2) {
+            // fp16(e2m1 * (e4m3 * global)) with the products in fp32; the
+            // block of slice s (k = 32h + 8s ..) is byte 2h + s/2 of the step.
+            const uint32_t nw = s8[ks / 4][ks % 4] >> (16 * fh);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float sc = e4m3_byte(nw, s >> 1) * job.gscale;
+                const uint32_t u = cw[set][0][s];
+                const f32x2 q0 = e2m1x2_to_f32x2<0>(u), q1 = e2m1x2_to_f32x2<1>(u);
+                const f32x2 q2 = e2m1x2_to_f32x2<2>(u), q3 = e2m1x2_to_f32x2<3>(u);
+                u32x4 o;
+                o.x = f32x2_to_f16x2(q0[0] * sc, q0[1] * sc);
+                o.y = f32x2_to_f16x2(q1[0] * sc, q1[1] * sc);
+                o.z = f32x2_to_f16x2(q2[0] * sc, q2[1] * sc);
+                o.w = f32x2_to_f16x2(q3[0] * sc, q3[1] * sc);
+                wf[s] = __builtin_bit_cast(f16x8, o);
+            }
         } else {
-            const f16 s1 = __builtin_bit_cast(f16, (uint16_t)sw), b1 = __builtin_bit_cast(f16, (uint16_t)bw);
-            const f16x2 s2 = {s1, s1}, b2 = {b1, b1};
+            const uint32_t sw = s8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
+            const uint32_t bw = b8[ks / 8][(ks % 8) / 2] >> (16 * (ks & 1));
+            if constexpr (DT == 1) {
+                const float sf = bf2f((uint16_t)sw), bf = bf2f((uint16_t)bw);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wf[s] = dequant_word(cw[set][s], s2, b2);
+                for (int s = 0; s < 4; ++s)
+                    wf[s] = __builtin_bit_cast(f16x8, dequant_word_bf16(cw[set][0][s], sf, bf));
+            } else {
+                const f16 s1 = __builtin_bit_cast(f16, (uint16_t)sw), b1 = __builtin_bit_cast(f16, (uint16_t)bw);
+                const f16x2 s2 = {s1, s1}, b2 = {b1, b1};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) wf[s] = dequant_word(cw[set][0][s], s2, b2);
+            }
         }
-        if (ks + AH < G) cw[set] = ld_u32x4(wrow + (ks + AH) * 8);
+        if (ks + AH < G) {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) cw[set][c] = ld_u32x4(wrow + (ks + AH) * WSTEP + 4 * c);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if constexpr (DT == 1)
@@ -866,7 +931,7 @@ __device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16*
 // Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
 // 8 waves of 128 x 64) and short tiles (128 rows, 8 waves of 64 x 64), both
 // 256 columns wide, in one launch; short routed tiles of at most 32 rows
-// (w4 weights, K of 512, 1024 or 2048) take tiny_tile instead.  The tall class (tall routed tiles, then
+// (K of 512, 1024 or 2048) take tiny_tile instead.  The tall class (tall routed tiles, then
 // the shared expert's tiles) comes first in the grid, then the short class;
 // each class is dealt to the XCDs in contiguous runs of (tile, column block)
 // items, so that every XCD gets an equal share of each class.
@@ -940,12 +1005,10 @@ gemm_w4_grouped_kernel(const KParams p) {
         if constexpr (WF == 2) job.gscale = p.gscales[e];
     }
     job.n0 = nblk * ((MODE == MODE_GATEUP) ? TallTile::BN / 2 : TallTile::BN);
-    if constexpr (WF == 0) {
-        if (!tall && job.rows_valid <= kTinyRows) {
-            if (G == 32) { tiny_tile<MODE, DT, 32>(p, job, lds); return; }
-            if (G == 16) { tiny_tile<MODE, DT, 16>(p, job, lds); return; }
-            if (G == 8) { tiny_tile<MODE, DT, 8>(p, job, lds); return; }
-        }
+    if (!tall && job.rows_valid <= kTinyRows) {
+        if (G == 32) { tiny_tile<MODE, DT, 32, WF>(p, job, lds); return; }
+        if (G == 16) { tiny_tile<MODE, DT, 16, WF>(p, job, lds); return; }
+        if (G == 8) { tiny_tile<MODE, DT, 8, WF>(p, job, lds); return; }
     }
     if (tall)
         gemm_tile<4, 2, 2, 4, MODE, DT, WF>(p, job, lds);

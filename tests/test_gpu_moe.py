@@ -465,12 +465,18 @@ def boundary_route(E, counts, seed):
     return rng.permutation(np.repeat(np.arange(E), counts)).astype(np.int32).reshape(-1, 1)
 
 
-def expert_rows_reference(ids, sorted_assign, H, w, ffn, with_shared=True):
+def w4_expert(W, e):
+    return {"qweight": W["qweight"][e], "scales": W["scales"][e], "biases": W["biases"][e],
+            "K": W["K"], "N": W["N"]}
+
+
+def expert_rows_reference(ids, sorted_assign, H, w, ffn, with_shared=True, expert=w4_expert):
     """Oracle act / ydown in the GPU's row order: the rows of expert e are
     its tokens in the order of sorted_assign (checked against the stable
-    permutation), then one shared row per token."""
+    permutation), then one shared row per token.  expert(W, e) slices
+    expert e out of a stacked matrix."""
     T = ids.shape[0]
-    E = w["gate_up"]["qweight"].shape[0]
+    E = int(ids.max()) + 1
     ref_sorted, _ = oracle.stable_permutation(ids, E)
     assert np.array_equal(sorted_assign, ref_sorted)
     tok = sorted_assign.astype(np.int64)  # topk = 1: assignment a is token a
@@ -479,9 +485,7 @@ def expert_rows_reference(ids, sorted_assign, H, w, ffn, with_shared=True):
         rows = np.nonzero(ids[tok, 0] == e)[0]
         if rows.size == 0:
             continue
-        sl = lambda W: {"qweight": W["qweight"][e], "scales": W["scales"][e], "biases": W["biases"][e],
-                        "K": W["K"], "N": W["N"]}
-        a, y = ffn(H[tok[rows]], sl(w["gate_up"]), sl(w["down"]))
+        a, y = ffn(H[tok[rows]], expert(w["gate_up"], e), expert(w["down"], e))
         for i, r in enumerate(rows):
             acts[r], yds[r] = a[i], y[i]
     act, yd = np.stack(acts), np.stack(yds)

@@ -226,3 +226,41 @@ def test_moe_nvfp4_and_fp8_bit_identical_on_common_weights():
     torch.cuda.synchronize()
     for x, y in zip(a[1:], b[1:]):
         assert np.array_equal(host(x).view(np.uint16), host(y).view(np.uint16))
+
+
+def _fp8_expert(W, e):
+    return {"codes": W["codes"][e], "scales": W["scales"][e], "K": W["K"], "N": W["N"]}
+
+
+def _nvfp4_expert(W, e):
+    return {"qweight": W["qweight"][e], "block_scales": W["block_scales"][e],
+            "global_scale": float(np.asarray(W["global_scale"])[e]), "K": W["K"], "N": W["N"]}
+
+
+@pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("D,I", [(2048, 512), (512, 1024)])
+def test_moe_codec_tile_row_boundaries(codec, D, I):
+    """FP8 / NVFP4 grouped GEMMs on experts with 1, 31, 32, 33, 0, 97, 256
+    and 300 rows (moe_dispatch on given ids, topk 1) and the shared expert:
+    every act and ydown row against the oracle's codec FFN of its expert."""
+    import torch
+    from tests.gpu_util import assert_close
+    from tests.test_gpu_moe import BOUNDARY_COUNTS, boundary_route, expert_rows_reference
+    E = len(BOUNDARY_COUNTS)
+    say(f"moe {codec} tile boundaries D={D} I={I}")
+    ids = boundary_route(E, BOUNDARY_COUNTS, D + I + 9)
+    T = ids.shape[0]
+    if codec == "fp8":
+        w = synth.moe_weights_fp8(D + I, D=D, I=I, E=E)
+        dw, gemm, ffn, sl = _dev_weights(w), ql.moe_grouped_gemm_fp8, oracle.expert_ffn_fp8, _fp8_expert
+    else:
+        w = synth.moe_weights_nvfp4(D + I, D=D, I=I, E=E)
+        dw, gemm, ffn, sl = _dev_weights_nvfp4(w), ql.moe_grouped_gemm_nvfp4, oracle.expert_ffn_nvfp4, _nvfp4_expert
+    H = synth.moe_tokens(D + I + 1, T, D=D, E=E)["H"]
+    route = ql.moe_dispatch(t(ids), E)
+    act = gemm(dw["gate_up"], dw["shared_gate_up"], t(H), T, 1, ql.QL_OP_GATE_UP_SILU, route)
+    yd = gemm(dw["down"], dw["shared_down"], act, T, 1, ql.QL_OP_DOWN, route)
+    torch.cuda.synchronize()
+    ref_act, ref_yd = expert_rows_reference(ids, host(route["sorted_assign"]), H, w, ffn, expert=sl)
+    assert_close(host(act).astype(np.float64), ref_act.astype(np.float64), "act")
+    assert_close(host(yd).astype(np.float64), ref_yd, "ydown")

@@ -700,30 +700,72 @@ def bench_moe_prefill(args, dev, w):
     def cb(i):
         ql.moe_combine(yd, routes[i % 2]["gates"], routes[i % 2]["pos"], T, 8, True, out)
 
-    return prefill_timing(T, r_, gu, dn, cb, seeds)
+    SO = ql.QL_OP_SHARED_ONLY
+    split = (lambda i: ql.moe_grouped_gemm(dw["gate_up"], None, Hs[i % 2], T, 8, ql.QL_OP_GATE_UP_SILU,
+                                           routes[i % 2], act),
+             lambda i: ql.moe_grouped_gemm(dw["down"], None, act, T, 8, ql.QL_OP_DOWN, routes[i % 2], yd),
+             lambda i, st: ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], Hs[i % 2], T, 8,
+                                               ql.QL_OP_GATE_UP_SILU | SO, None, act, stream=st),
+             lambda i, st: ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN | SO,
+                                               None, yd, stream=st))
+    return prefill_timing(T, r_, gu, dn, cb, seeds, split)
 
 
-def prefill_timing(T, r_, gu, dn, cb, seeds):
+def prefill_timing(T, r_, gu, dn, cb, seeds, split=None):
     """Time the four prefill stages as one step (20 steps) and each stage
     alone (10 launches); the stage functions take the step index, whose
-    parity selects the token set."""
+    parity selects the token set.  With split = (gu_routed, dn_routed,
+    gu_shared, dn_shared) the step that sets the reported rate runs the
+    shared expert (which needs no routing) on a second stream beside the
+    route and the routed projections, joined before the combine; the
+    single-stream step is reported beside it."""
+    import torch
+
     def step(i):
         r_(i)
         gu(i)
         dn(i)
         cb(i)
 
-    ms = timed_steps(step, 20, 4, settle_s=SETTLE_S)
+    ms_single = timed_steps(step, 20, 4, settle_s=SETTLE_S)
+    ms = ms_single
+    if split is not None:
+        gu_r, dn_r, gu_s, dn_s = split
+        side = torch.cuda.Stream()  # default priority
+        forks = [torch.cuda.Event() for _ in range(2)]
+        joins = [torch.cuda.Event() for _ in range(2)]
+
+        def step2(i):
+            main = torch.cuda.current_stream()
+            forks[i % 2].record(main)
+            side.wait_event(forks[i % 2])
+            with torch.cuda.stream(side):
+                gu_s(i, side)
+                dn_s(i, side)
+            joins[i % 2].record(side)
+            r_(i)
+            gu_r(i)
+            dn_r(i)
+            main.wait_event(joins[i % 2])
+            cb(i)
+
+        ms = timed_steps(step2, 20, 4, settle_s=SETTLE_S)
     k = np.asarray(stage_times([r_, gu, dn, cb], 10, 2, settle_s=SETTLE_S / 4))
     routed_rows = T * 8
     flops = (2.0 * routed_rows * 2048 * 1024 + 2.0 * routed_rows * 512 * 2048
              + 2.0 * T * 2048 * 1024 + 2.0 * T * 512 * 2048 + 2.0 * T * 2048 * 256)
-    return {"tokens/s": T / (ms * 1e-3), "ms_per_step": ms, "flops": flops,
-            "TFLOP/s": flops / (ms * 1e-3) / 1e12,
-            "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-            "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
-                         "down": float(k[2] * 1e3), "combine": float(k[3] * 1e3)},
-            "token_seeds": [int(sd) for sd in seeds]}
+    res = {"tokens/s": T / (ms * 1e-3), "ms_per_step": ms, "flops": flops,
+           "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+           "frac_mfma_f16": flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+           "stage_us": {"route": float(k[0] * 1e3), "gate_up_silu": float(k[1] * 1e3),
+                        "down": float(k[2] * 1e3), "combine": float(k[3] * 1e3)},
+           "token_seeds": [int(sd) for sd in seeds]}
+    if split is not None:
+        res["streams"] = ("2: shared expert (QL_OP_SHARED_ONLY) on a second stream beside the route "
+                          "and the routed rows")
+        res["single_stream_ms_per_step"] = ms_single
+        res["single_stream_TFLOP/s"] = flops / (ms_single * 1e-3) / 1e12
+    return res
 
 
 def bench_moe_prefill_bf16(args, dev):
@@ -762,7 +804,14 @@ def bench_moe_prefill_bf16(args, dev):
     def cb(i):
         ql.moe_combine_bf16(yd, routes[i % 2]["gates"], routes[i % 2]["pos"], T, 8, True, out)
 
-    r = prefill_timing(T, r_, gu, dn, cb, seeds)
+    SO = ql.QL_OP_SHARED_ONLY
+    g = ql.moe_grouped_gemm_bf16
+    split = (lambda i: g(dw["gate_up"], None, Hs[i % 2], T, 8, ql.QL_OP_GATE_UP_SILU, routes[i % 2], act),
+             lambda i: g(dw["down"], None, act, T, 8, ql.QL_OP_DOWN, routes[i % 2], yd),
+             lambda i, st: g(dw["gate_up"], dw["shared_gate_up"], Hs[i % 2], T, 8, ql.QL_OP_GATE_UP_SILU | SO,
+                             None, act, stream=st),
+             lambda i, st: g(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN | SO, None, yd, stream=st))
+    r = prefill_timing(T, r_, gu, dn, cb, seeds, split)
     r["frac_mfma_bf16"] = r.pop("frac_mfma_f16")
     return r
 
@@ -808,7 +857,14 @@ def bench_moe_prefill_codec(args, dev, codec: str):
     def cb(i):
         ql.moe_combine(yd, routes[i % 2]["gates"], routes[i % 2]["pos"], T, 8, True, out)
 
-    return prefill_timing(T, r_, gu, dn, cb, seeds)
+    SO = ql.QL_OP_SHARED_ONLY
+    split = (lambda i: gemm(dw["gate_up"], None, Hs[i % 2], T, 8, ql.QL_OP_GATE_UP_SILU, routes[i % 2], act),
+             lambda i: gemm(dw["down"], None, act, T, 8, ql.QL_OP_DOWN, routes[i % 2], yd),
+             lambda i, st: gemm(dw["gate_up"], dw["shared_gate_up"], Hs[i % 2], T, 8,
+                                ql.QL_OP_GATE_UP_SILU | SO, None, act, stream=st),
+             lambda i, st: gemm(dw["down"], dw["shared_down"], act, T, 8, ql.QL_OP_DOWN | SO, None, yd,
+                                stream=st))
+    return prefill_timing(T, r_, gu, dn, cb, seeds, split)
 
 
 CALIB_BYTES = 256 * 1024 * 1024

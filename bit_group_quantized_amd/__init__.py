@@ -24,6 +24,7 @@ QL_OK = 0
 QL_OP_GATE_UP_SILU = 1
 QL_OP_DOWN = 2
 QL_OP_DOWN_COMBINE = 3
+QL_OP_SHARED_ONLY = 0x100  # or'ed into op: the shared expert's rows only
 QL_MOE_TILE_ROWS = 128
 QL_DECODE_MAX_T = 4
 GROUP = 64
@@ -377,6 +378,16 @@ def moe_dispatch(ids, E: int, out: dict | None = None, stream=None) -> dict:
     return out
 
 
+def _route_args(route):
+    """Routing pointers of a grouped-GEMM call; route may be None for the
+    QL_OP_SHARED_ONLY calls, which read none of them."""
+    if route is None:
+        return None, None, None, None, None, 0
+    ws = route["workspace"]
+    return (_ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(route.get("gates")),
+            _ptr(route.get("pos")), _ptr(ws), ws.numel())
+
+
 def moe_grouped_gemm(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
                      Y=None, stream=None):
     """Expert projections over the routed rows described by ``route`` (the
@@ -385,19 +396,19 @@ def moe_grouped_gemm(W: dict, shared: dict | None, X, T: int, topk: int, op: int
     w = make_w4_experts(W)
     s = make_w4(shared) if shared is not None else None
     rows = T * topk + (T if shared is not None else 0)
+    base = op & ~QL_OP_SHARED_ONLY
     if Y is None:
-        if op == QL_OP_GATE_UP_SILU:
+        if base == QL_OP_GATE_UP_SILU:
             shape = (rows, int(W["N"]) // 2)
-        elif op == QL_OP_DOWN:
+        elif base == QL_OP_DOWN:
             shape = (rows, int(W["N"]))
         else:
             shape = (T, int(W["N"]))
         Y = torch.empty(shape, dtype=torch.float16, device=X.device)
-    ws = route["workspace"]
+    off, sa, gates, pos, ws, nws = _route_args(route)
     _check("moe_grouped_gemm", lib().moe_grouped_gemm(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(route.get("gates")),
-        _ptr(route.get("pos")), _ptr(ws), ws.numel(), _ptr(Y), _stream(stream)))
+        off, sa, gates, pos, ws, nws, _ptr(Y), _stream(stream)))
     return Y
 
 
@@ -423,13 +434,13 @@ def moe_grouped_gemm_bf16(W: dict, shared: dict | None, X, T: int, topk: int, op
     s = make_w4(shared) if shared is not None else None
     rows = T * topk + (T if shared is not None else 0)
     if Y is None:
-        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        shape = ((rows, int(W["N"]) // 2) if (op & ~QL_OP_SHARED_ONLY) == QL_OP_GATE_UP_SILU
+                 else (rows, int(W["N"])))
         Y = torch.empty(shape, dtype=torch.bfloat16, device=X.device)
-    ws = route["workspace"]
+    off, sa, _, _, ws, nws = _route_args(route)
     _check("moe_grouped_gemm_bf16", lib().moe_grouped_gemm_bf16(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
-        _stream(stream)))
+        off, sa, ws, nws, _ptr(Y), _stream(stream)))
     return Y
 
 
@@ -448,13 +459,13 @@ def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op:
                 int(shared["N"])) if shared is not None else None)
     rows = T * topk + (T if shared is not None else 0)
     if Y is None:
-        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        shape = ((rows, int(W["N"]) // 2) if (op & ~QL_OP_SHARED_ONLY) == QL_OP_GATE_UP_SILU
+                 else (rows, int(W["N"])))
         Y = torch.empty(shape, dtype=torch.float16, device=X.device)
-    ws = route["workspace"]
+    off, sa, _, _, ws, nws = _route_args(route)
     _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
-        _stream(stream)))
+        off, sa, ws, nws, _ptr(Y), _stream(stream)))
     return Y
 
 
@@ -477,13 +488,13 @@ def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, o
          if shared is not None else None)
     rows = T * topk + (T if shared is not None else 0)
     if Y is None:
-        shape = (rows, int(W["N"]) // 2) if op == QL_OP_GATE_UP_SILU else (rows, int(W["N"]))
+        shape = ((rows, int(W["N"]) // 2) if (op & ~QL_OP_SHARED_ONLY) == QL_OP_GATE_UP_SILU
+                 else (rows, int(W["N"])))
         Y = torch.empty(shape, dtype=torch.float16, device=X.device)
-    ws = route["workspace"]
+    off, sa, _, _, ws, nws = _route_args(route)
     _check("moe_grouped_gemm_nvfp4", lib().moe_grouped_gemm_nvfp4(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        _ptr(route["offsets"]), _ptr(route["sorted_assign"]), _ptr(ws), ws.numel(), _ptr(Y),
-        _stream(stream)))
+        off, sa, ws, nws, _ptr(Y), _stream(stream)))
     return Y
 
 

@@ -350,17 +350,28 @@ static int grouped_impl(const ExpertView& w, const uint16_t* X, int32_t T, int32
                         const int32_t* offsets, const int32_t* sorted_assign,
                         const float* topk_gates, const int32_t* assign_pos, const void* workspace,
                         size_t ws_bytes, uint16_t* Y, void* stream) {
+    const bool shared_only = (op & QL_OP_SHARED_ONLY) != 0;
+    op &= ~QL_OP_SHARED_ONLY;
     if (op != QL_OP_GATE_UP_SILU && op != QL_OP_DOWN && op != QL_OP_DOWN_COMBINE)
         return QL_ERR_INVALID_ARG;
+    if (shared_only && (op == QL_OP_DOWN_COMBINE || !w.sqw)) return QL_ERR_INVALID_ARG;
     const int32_t E = w.E;
     if (T < 0 || E <= 0 || topk <= 0 || topk > E) return QL_ERR_INVALID_ARG;
     if (E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
     if (op == QL_OP_GATE_UP_SILU && w.N % 2 != 0) return QL_ERR_UNSUPPORTED_SHAPE;
     if (T == 0 || w.N == 0) return QL_OK;
     if ((int64_t)T * topk > 0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
-    if (!X || !Y || !offsets || !sorted_assign) return QL_ERR_INVALID_ARG;
-    if (!aligned(X, 16) || !aligned(Y, 2) || !aligned(offsets, 4) || !aligned(sorted_assign, 4))
-        return QL_ERR_MISALIGNED;
+    if (!X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 2)) return QL_ERR_MISALIGNED;
+    if (shared_only) {
+        ql::GroupedArgs a{w.qw, w.sc, w.bi, w.sqw, w.ssc, w.sbi,
+                          X, nullptr, nullptr, nullptr, nullptr, nullptr, Y,
+                          w.K, w.N, E, T, topk, op, w.bf16, w.wf, w.gscales, w.sgscale};
+        a.shared_only = true;
+        return ql::launch_moe_grouped(a, as_stream(stream));
+    }
+    if (!offsets || !sorted_assign) return QL_ERR_INVALID_ARG;
+    if (!aligned(offsets, 4) || !aligned(sorted_assign, 4)) return QL_ERR_MISALIGNED;
     if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
 

@@ -955,8 +955,9 @@ gemm_w4_grouped_kernel(const KParams p) {
     const int G = p.K / kGroup;
     const int wpr = p.K / 8;
     const int NB = p.grid_n;  // column blocks
-    const int nt = min(max(p.ws_header[0], 0), p.max_tiles);
-    const int nbig = min(max(p.ws_header[3], 0), nt);
+    // No header: the shared expert's tiles only.
+    const int nt = p.ws_header ? min(max(p.ws_header[0], 0), p.max_tiles) : 0;
+    const int nbig = p.ws_header ? min(max(p.ws_header[3], 0), nt) : 0;
     const int big_items = (nbig + p.grid_m) * NB;  // grid_m: shared-expert tiles
     const int small_items = (nt - nbig) * NB;
     const int per_b = (big_items + 7) >> 3, per_s = (small_items + 7) >> 3;
@@ -1142,10 +1143,16 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     p.sqw = a.sqw;
     p.ssc = a.ssc;
     p.sbi = a.sbi;
-    p.ws_header = reinterpret_cast<const int*>(a.ws + L.header);
-    p.tiles = reinterpret_cast<const int*>(a.ws + L.tiles);
+    if (a.shared_only) {
+        p.ws_header = nullptr;  // no routed tiles
+        p.tiles = nullptr;
+        p.max_tiles = 0;
+    } else {
+        p.ws_header = reinterpret_cast<const int*>(a.ws + L.header);
+        p.tiles = reinterpret_cast<const int*>(a.ws + L.tiles);
+        p.max_tiles = L.max_tiles;
+    }
     p.sorted_assign = a.sorted_assign;
-    p.max_tiles = L.max_tiles;
     p.T = a.T;
     p.topk = a.topk;
     p.E = a.E;
@@ -1156,8 +1163,8 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
                                             : (a.N + TallTile::BN - 1) / TallTile::BN;
     p.grid_m = a.sqw ? (a.T + TallTile::BM - 1) / TallTile::BM : 0;  // shared-expert tiles
     // Upper bounds of both classes; workgroups past the actual items exit.
-    const int64_t max_tall = ((int64_t)a.T * a.topk) / TallTile::BM + p.grid_m;
-    const int64_t items_b = max_tall * p.grid_n, items_s = (int64_t)L.max_tiles * p.grid_n;
+    const int64_t max_tall = (a.shared_only ? 0 : ((int64_t)a.T * a.topk) / TallTile::BM) + p.grid_m;
+    const int64_t items_b = max_tall * p.grid_n, items_s = (int64_t)p.max_tiles * p.grid_n;
     const int64_t blocks = (items_b + 7) / 8 * 8 + (items_s + 7) / 8 * 8;
     if (blocks > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
     if (blocks == 0) return QL_OK;

@@ -157,6 +157,7 @@ struct GroupedArgs {
                         // 2: NVFP4 experts (qw = codes, sc = E4M3 block-scale bytes, no biases)
     const float* gscales = nullptr;  // NVFP4: per-expert global scales (device, [E])
     float sgscale = 0.f;             // NVFP4: the shared expert's global scale
+    bool shared_only = false;        // the shared expert's rows only (no routing inputs read)
 };
 bool moe_rows_supported(int K);
 int launch_moe_rows(const GroupedArgs& a, hipStream_t st);    // small T, row-parallel

@@ -84,6 +84,9 @@ extern "C" {
 #define QL_OP_GATE_UP_SILU 1
 #define QL_OP_DOWN 2
 #define QL_OP_DOWN_COMBINE 3
+/* Flag or'ed into the op of the grouped GEMMs (with QL_OP_GATE_UP_SILU or
+ * QL_OP_DOWN): compute only the shared expert's rows. */
+#define QL_OP_SHARED_ONLY 0x100
 
 /* Limits. */
 #define QL_MAX_EXPERTS 1024
@@ -438,6 +441,16 @@ int moe_dispatch(const int32_t* topk_ids, int32_t T, int32_t E, int32_t topk,
  * topk_gates and assign_pos are read only by QL_OP_DOWN_COMBINE (may be
  * NULL otherwise).  `workspace` is the one filled by moe_route or
  * moe_dispatch for the same T, E, topk.
+ *
+ * Splitting the layer across two streams: the shared expert does not
+ * depend on the routing, so it can run beside it.  A call with shared =
+ * NULL computes the routed rows only; a call with op | QL_OP_SHARED_ONLY
+ * (QL_OP_GATE_UP_SILU or QL_OP_DOWN, shared not NULL) computes the shared
+ * rows [T*topk, T*topk + T) of Y only and reads neither the experts of W
+ * (W still gives K, N and E), nor offsets, sorted_assign or the workspace,
+ * which may then be NULL / 0.  The two calls together write exactly the
+ * rows, and the bits, of the one call with both; they touch disjoint rows
+ * of X and Y, so they may run concurrently on different streams.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED, WORKSPACE, HIP.
  */
 int moe_grouped_gemm(const ql_w4_experts* W, const ql_w4* shared,

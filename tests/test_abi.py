@@ -155,6 +155,12 @@ def test_grouped_gemm_validation(L):
     assert call(w=ql.ql_w4_experts(A16, A16, A16, 2048, 1023, 64, 256), s=None) == SHAPE  # odd gate_up width
     assert call(s=ql.ql_w4(A16, A16, A16, 2048, 512, 64)) == INVALID           # shared shape differs
     assert call(T=0) == OK
+    # the shared expert alone: needs the shared matrix, not DOWN_COMBINE
+    assert call(op=1 | 0x100, s=None) == INVALID
+    assert call(op=3 | 0x100) == INVALID
+    assert call(op=1 | 0x100, X=A16 + 2) == MISALIGNED
+    assert call(op=1 | 0x100, T=0) == OK
+    assert call(op=2 | 0x100, T=0, wsb=0) == OK   # no workspace needed
 
 
 def test_combine_validation(L):

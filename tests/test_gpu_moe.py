@@ -516,3 +516,53 @@ def test_moe_tile_row_boundaries(D, I):
     ref_act, ref_yd = expert_rows_reference(ids, host(route["sorted_assign"]), H, w, oracle.expert_ffn)
     assert_close(host(act).astype(np.float64), ref_act.astype(np.float64), "act")
     assert_close(host(yd).astype(np.float64), ref_yd, "ydown")
+
+
+def test_moe_shared_expert_on_a_second_stream():
+    """The layer split across two streams: routing and the routed rows
+    (shared = None) on one, the shared expert's rows (QL_OP_SHARED_ONLY, no
+    routing inputs) on another, joined by events.  Every act, ydown and out
+    bit equals the single-stream layer's, over several back-to-back steps
+    that alternate two token sets."""
+    import torch
+    T, topk = 4096, 8
+    w = synth.moe_weights(0)
+    dw = _dev_weights(w)
+    seeds = FULL_ORDER[:2]
+    toks = [synth.moe_tokens(sd, T, skewed=True) for sd in seeds]
+    Hs = [t(tk["H"]) for tk in toks]
+    bs = [t(tk["logit_bias"]) for tk in toks]
+    ref = []
+    for H, b in zip(Hs, bs):
+        route, act, yd, out = _run_layer(dw, H, b, topk, T, False)
+        ref.append((host(act), host(yd), host(out)))
+    dev = Hs[0].device
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    routes = [ql.alloc_route_outputs(T, 256, topk, dev) for _ in seeds]
+    act = torch.empty((T * topk + T, 512), dtype=torch.float16, device=dev)
+    yd = torch.empty((T * topk + T, 2048), dtype=torch.float16, device=dev)
+    outs = [torch.empty((T, 2048), dtype=torch.float16, device=dev) for _ in seeds]
+    for step in range(6):
+        i = step % 2
+        fork = torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], Hs[i], T, topk,
+                                ql.QL_OP_GATE_UP_SILU | ql.QL_OP_SHARED_ONLY, None, act, stream=side)
+            ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, topk,
+                                ql.QL_OP_DOWN | ql.QL_OP_SHARED_ONLY, None, yd, stream=side)
+        join = torch.cuda.Event()
+        join.record(side)
+        ql.moe_route(Hs[i], dw["Wr"], bs[i], topk, routes[i])
+        ql.moe_grouped_gemm(dw["gate_up"], None, Hs[i], T, topk, ql.QL_OP_GATE_UP_SILU, routes[i], act)
+        ql.moe_grouped_gemm(dw["down"], None, act, T, topk, ql.QL_OP_DOWN, routes[i], yd)
+        main.wait_event(join)
+        ql.moe_combine(yd, routes[i]["gates"], routes[i]["pos"], T, topk, True, outs[i])
+        if step >= 4:
+            torch.cuda.synchronize()
+            a_ref, y_ref, o_ref = ref[i]
+            assert np.array_equal(host(act).view(np.uint16), a_ref.view(np.uint16))
+            assert np.array_equal(host(yd).view(np.uint16), y_ref.view(np.uint16))
+            assert np.array_equal(host(outs[i]).view(np.uint16), o_ref.view(np.uint16))

@@ -265,6 +265,19 @@ def bench_gemv(args, dev):
     }
     # The same step as a replayed HIP graph (launch overhead removed), for context.
     graph_ms = graph_time(step, copies * 2, 20) if copies * 2 <= 64 else None
+    # The same two matrices in one launch (qlinear_gemv_multi: they share x),
+    # and the projection alone in a graph of back-to-back launches.
+    def step_multi(i):
+        Wc = Ws[i % copies]
+        ql.qlinear_gemv_multi([Wc[0], Wc[1]], x, ys)
+
+    ms_multi = timed_steps(step_multi, args.steps, args.warmup, settle_s=SETTLE_S / 2)
+    # (a graph of 64 launches over 64 copies, 605 MB: past the Infinity
+    # Cache, and long enough that the replay's own overhead is amortized)
+    pc = 64
+    Wp = [base[0]] + [clone_w4(base[0]) for _ in range(pc - 1)]
+    proj_graph_ms = graph_time(lambda i: ql.qlinear_gemv(Wp[i % pc], x, ys[0]), pc, 20)
+    del Wp
     sha = source_sha("gemv.hip", "ql_device.h")
     traffic = traffic_for(KERNEL_GEMV, sha)
     return {
@@ -275,6 +288,11 @@ def bench_gemv(args, dev):
         "per_matrix": {f"N={N}": {"us": float(kern_ms[j] * 1e3),
                                   "GB/s": launch_bytes[j] / (kern_ms[j] * 1e-3) / 1e9}
                        for j, N in enumerate(Ns)},
+        "projection_in_graph": {"us": float(proj_graph_ms * 1e3),
+                                "GB/s": launch_bytes[0] / (proj_graph_ms * 1e-3) / 1e9,
+                                "note": "N=8192 alone: 64 back-to-back launches over 64 weight copies, replayed from a HIP graph"},
+        "step_one_launch": {"ms_per_step": ms_multi, "GB/s": step_bytes / (ms_multi * 1e-3) / 1e9,
+                            "note": "both matrices in one qlinear_gemv_multi launch (same x)"},
         "roofline": {"bound": "hbm", "kernel": KERNEL_GEMV, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": avg_launch_bytes,
@@ -1176,6 +1194,8 @@ def main():
                    "step_bytes": g["step_bytes"]},
         "roofline": g["roofline"],
         "per_matrix": g["per_matrix"],
+        "projection_in_graph": g["projection_in_graph"],
+        "step_one_launch": g["step_one_launch"],
         "graph_step": g["graph"],
         "stats": g["stats"],
     }

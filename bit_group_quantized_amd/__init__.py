@@ -92,6 +92,7 @@ _SIGS = {
     "ql_moe_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_route": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                  _P, ctypes.c_size_t, _P]),
+    "qlinear_gemv_multi": (ctypes.c_int, [ctypes.POINTER(ql_w4), _I32, _P, ctypes.POINTER(ctypes.c_void_p), _P]),
     "moe_dispatch": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4), _P,
                                         _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t,
@@ -376,6 +377,21 @@ def moe_dispatch(ids, E: int, out: dict | None = None, stream=None) -> dict:
         _ptr(ids), T, E, topk, _ptr(out["counts"]), _ptr(out["offsets"]),
         _ptr(out["sorted_assign"]), _ptr(out["pos"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+QL_GEMV_MULTI_MAX = 8
+
+
+def qlinear_gemv_multi(Ws: list, x, ys: list | None = None, stream=None) -> list:
+    """y_i = x . dequant(W_i) for matrices sharing x (same K), one launch."""
+    import torch
+    n = len(Ws)
+    arr = (ql_w4 * n)(*[make_w4(W) for W in Ws])
+    if ys is None:
+        ys = [torch.empty(int(W["N"]), dtype=torch.float16, device=x.device) for W in Ws]
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    _check("qlinear_gemv_multi", lib().qlinear_gemv_multi(arr, n, _ptr(x), yp, _stream(stream)))
+    return ys
 
 
 def _route_args(route):

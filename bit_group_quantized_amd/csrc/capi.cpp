@@ -64,6 +64,37 @@ int qlinear_gemv(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream) {
     return ql::launch_gemv(a, as_stream(stream));
 }
 
+int qlinear_gemv_multi(const ql_w4* Ws, int32_t count, const uint16_t* x, uint16_t* const* ys,
+                       void* stream) {
+    if (!Ws || !ys || count < 1 || count > QL_GEMV_MULTI_MAX) return QL_ERR_INVALID_ARG;
+    ql::GemvMultiArgs a{};
+    a.count = count;
+    a.K = Ws[0].K;
+    a.x = x;
+    bool any = false;
+    for (int i = 0; i < count; ++i) {
+        const ql_w4& W = Ws[i];
+        const int rc = check_w4(W.qweight, W.scales, W.biases, W.K, W.N, W.group_size);
+        if (rc != QL_OK) return rc;
+        if (W.K != a.K) return QL_ERR_INVALID_ARG;
+        if (W.N > 0) {
+            if (!ys[i]) return QL_ERR_INVALID_ARG;
+            if (!aligned(ys[i], 2)) return QL_ERR_MISALIGNED;
+            any = true;
+        }
+        a.qweight[i] = W.qweight;
+        a.scales[i] = W.scales;
+        a.biases[i] = W.biases;
+        a.y[i] = ys[i];
+        a.N[i] = W.N;
+    }
+    if (!ql::gemv_fused_supported(a.K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!any) return QL_OK;
+    if (!x) return QL_ERR_INVALID_ARG;
+    if (!aligned(x, 16)) return QL_ERR_MISALIGNED;
+    return ql::launch_gemv_multi(a, as_stream(stream));
+}
+
 int qlinear_gemm(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
     if (!W || M < 0) return QL_ERR_INVALID_ARG;
     int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);

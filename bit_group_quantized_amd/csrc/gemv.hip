@@ -164,19 +164,20 @@ gemv_w4_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
 enum { GV_PLAIN = 0, GV_RMSNORM = 1 };
 enum { GV_STORE = 0, GV_ARGMAX = 1 };
 
+// The work of block `blk` of the chunked GEMV (rows 4 * TEAMS * R * blk ..).
 template <int TPR, int V, int R, int PRO, int EPI>
-__global__ void __launch_bounds__(256)
-gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
-                       const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
-                       uint16_t* __restrict__ y, int K, int N, const uint16_t* __restrict__ gamma,
-                       float eps, uint64_t* __restrict__ partials) {
+__device__ __forceinline__ void chunked_body(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                                             const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
+                                             uint16_t* __restrict__ y, int K, int N,
+                                             const uint16_t* __restrict__ gamma, float eps,
+                                             uint64_t* __restrict__ partials, int blk) {
     constexpr int TEAMS = 64 / TPR;
     const int lane = threadIdx.x & 63;
     const int lr = lane % TPR;
     const int team = lane / TPR;
     const int G = K / kGroup;
     const int wpr = K / 8;
-    const int gwave = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+    const int gwave = blk * (blockDim.x / 64) + threadIdx.x / 64;
     const int row0 = (gwave * TEAMS + team) * R;
 
     // Activations of this lane's chunks (L2-resident after the first wave)
@@ -289,8 +290,53 @@ gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restri
         __shared__ uint64_t wkeys[4];
         if (lane == 0) wkeys[threadIdx.x >> 6] = key;
         __syncthreads();
-        if (threadIdx.x == 0) partials[blockIdx.x] = umax64(umax64(wkeys[0], wkeys[1]), umax64(wkeys[2], wkeys[3]));
+        if (threadIdx.x == 0) partials[blk] = umax64(umax64(wkeys[0], wkeys[1]), umax64(wkeys[2], wkeys[3]));
     }
+}
+
+template <int TPR, int V, int R, int PRO, int EPI>
+__global__ void __launch_bounds__(256)
+gemv_w4_chunked_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+                       const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
+                       uint16_t* __restrict__ y, int K, int N, const uint16_t* __restrict__ gamma,
+                       float eps, uint64_t* __restrict__ partials) {
+    chunked_body<TPR, V, R, PRO, EPI>(qw, sc, bi, x, y, K, N, gamma, eps, partials, blockIdx.x);
+}
+
+// Several matrices that share the activation row x (same K) in one launch:
+// the grid is the concatenation of the matrices' own chunked-GEMV grids
+// (matrix i owns blocks block0[i] .. block0[i+1]-1) and every matrix keeps
+// the rows per wave (R or 2) its own launch would use, so each output has
+// the bits of the separate call.  One launch instead of several saves the
+// per-launch dispatch gap, which at K = 2048, N = 8192 is a third of the
+// kernel's time.
+struct GemvMulti {
+    const uint32_t* qw[QL_GEMV_MULTI_MAX];
+    const uint16_t* sc[QL_GEMV_MULTI_MAX];
+    const uint16_t* bi[QL_GEMV_MULTI_MAX];
+    uint16_t* y[QL_GEMV_MULTI_MAX];
+    int N[QL_GEMV_MULTI_MAX];
+    int small_r[QL_GEMV_MULTI_MAX];  // 1: two rows per wave
+    int block0[QL_GEMV_MULTI_MAX + 1];
+    int count;
+};
+
+template <int TPR, int V, int R>
+__global__ void __launch_bounds__(256)
+gemv_w4_multi_kernel(const GemvMulti m, const uint16_t* __restrict__ x, int K) {
+    int i = 0;
+    for (int j = 1; j < m.count; ++j)
+        if ((int)blockIdx.x >= m.block0[j]) i = j;
+    const int blk = blockIdx.x - m.block0[i];
+    if constexpr (R > 2) {
+        if (m.small_r[i]) {
+            chunked_body<TPR, V, 2, GV_PLAIN, GV_STORE>(m.qw[i], m.sc[i], m.bi[i], x, m.y[i], K, m.N[i], nullptr,
+                                                        0.f, nullptr, blk);
+            return;
+        }
+    }
+    chunked_body<TPR, V, R, GV_PLAIN, GV_STORE>(m.qw[i], m.sc[i], m.bi[i], x, m.y[i], K, m.N[i], nullptr, 0.f,
+                                                nullptr, blk);
 }
 
 // bf16 variant of the chunked GEMV: bf16 activations, scales, biases and
@@ -959,6 +1005,47 @@ int launch_gemv_bf16(const GemvArgs& a, hipStream_t st) {
         case 4096: return launch_bf16_r<64, 2>(a, st);
         case 8192: return launch_bf16_t<64, 4, 4>(a, st);
         case 16384: return launch_bf16_t<64, 8, 2>(a, st);
+        default: return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+}
+
+// FALLBACK: the matrix's own launch drops to two rows per wave when it has
+// few blocks (launch_chunked_r); K = 8192 and 16384 keep fixed rows.
+template <int TPR, int V, int R, bool FALLBACK = true>
+int launch_multi_t(const GemvMultiArgs& a, hipStream_t st) {
+    GemvMulti m{};
+    m.count = a.count;
+    long blocks = 0;
+    for (int i = 0; i < a.count; ++i) {
+        m.qw[i] = a.qweight[i];
+        m.sc[i] = a.scales[i];
+        m.bi[i] = a.biases[i];
+        m.y[i] = a.y[i];
+        m.N[i] = a.N[i];
+        // The rows per wave of the matrix's own launch (launch_chunked_r).
+        const long big = (a.N[i] + 4L * (64 / TPR) * R - 1) / (4L * (64 / TPR) * R);
+        m.small_r[i] = (FALLBACK && R > 2 && big < kGemvMinBlocks) ? 1 : 0;
+        const int rpb = 4 * (64 / TPR) * (m.small_r[i] ? 2 : R);
+        m.block0[i] = (int)blocks;
+        blocks += (a.N[i] + rpb - 1) / rpb;
+        if (blocks > 0x7fffffffL) return QL_ERR_UNSUPPORTED_SHAPE;
+    }
+    m.block0[a.count] = (int)blocks;
+    if (blocks == 0) return QL_OK;
+    hipLaunchKernelGGL((gemv_w4_multi_kernel<TPR, V, R>), dim3((unsigned)blocks), dim3(256), 0, st, m, a.x, a.K);
+    return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
+}
+
+int launch_gemv_multi(const GemvMultiArgs& a, hipStream_t st) {
+    constexpr int R = kGemvRows;
+    switch (a.K) {
+        case 256: return launch_multi_t<8, 1, (R < 8 ? R : 8)>(a, st);
+        case 512: return launch_multi_t<16, 1, (R < 16 ? R : 16)>(a, st);
+        case 1024: return launch_multi_t<32, 1, R>(a, st);
+        case 2048: return launch_multi_t<64, 1, R>(a, st);
+        case 4096: return launch_multi_t<64, 2, R>(a, st);
+        case 8192: return launch_multi_t<64, 4, 4, false>(a, st);  // the fixed rows of launch_chunked
+        case 16384: return launch_multi_t<64, 8, 2, false>(a, st);
         default: return QL_ERR_UNSUPPORTED_SHAPE;
     }
 }

@@ -45,6 +45,18 @@ int launch_gemv(const GemvArgs& a, hipStream_t st);
 // K with the chunked kernel (powers of two 256 .. 16384): the fused variants.
 bool gemv_fused_supported(int K);
 int launch_gemv_rmsnorm(const GemvArgs& a, hipStream_t st);
+// Up to QL_GEMV_MULTI_MAX matrices sharing x (same K, a chunked-kernel K).
+struct GemvMultiArgs {
+    const uint32_t* qweight[QL_GEMV_MULTI_MAX];
+    const uint16_t* scales[QL_GEMV_MULTI_MAX];
+    const uint16_t* biases[QL_GEMV_MULTI_MAX];
+    uint16_t* y[QL_GEMV_MULTI_MAX];
+    int N[QL_GEMV_MULTI_MAX];
+    int count;
+    int K;
+    const uint16_t* x;
+};
+int launch_gemv_multi(const GemvMultiArgs& a, hipStream_t st);
 // Second weight codecs, single-row GEMV with fp16 x and y.
 struct CodecArgs {
     const uint8_t* codes8 = nullptr;        // FP8: E4M3 codes [N][K]

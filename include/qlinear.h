@@ -94,6 +94,7 @@ extern "C" {
 #define QL_MAX_K 32768
 #define QL_DECODE_MAX_T 4 /* largest T served by the row-parallel expert path */
 #define QL_DECODE_SCRATCH_BYTES (1u << 20) /* device scratch of moe_decode_noalloc */
+#define QL_GEMV_MULTI_MAX 8 /* matrices of one qlinear_gemv_multi call */
 
 /* One w4 matrix (host struct holding device pointers). */
 typedef struct ql_w4 {
@@ -142,6 +143,22 @@ int qlinear_pack(const uint8_t* codes, int32_t N, int32_t K, uint32_t* qweight, 
  * K > QL_MAX_K, group_size != 64), MISALIGNED, HIP.
  */
 int qlinear_gemv(const ql_w4* W, const uint16_t* x, uint16_t* y, void* stream);
+
+/*
+ * qlinear_gemv_multi - y_i = x . dequant(W_i) for `count` matrices that
+ * share one activation row (a decode step's projections of the same
+ * input), in one launch.  [PPLX] "优化单行权重路径" as qlinear_gemv; the
+ * single launch removes the per-launch dispatch gap of the separate calls.
+ *   Ws     host array of count K x N_i w4 matrices, all with the same K, K
+ *          one of 256, 512, 1024, 2048, 4096, 8192, 16384;
+ *   x      fp16 [K];  ys  host array of count device pointers, fp16 [N_i].
+ * Every output has the bits qlinear_gemv gives for its matrix.
+ * 1 <= count <= QL_GEMV_MULTI_MAX; matrices with N_i = 0 are skipped.
+ * Errors: INVALID_ARG (null Ws/ys/x/ys[i], count out of range, K differs),
+ * UNSUPPORTED_SHAPE (K not in the list, or as qlinear_gemv), MISALIGNED, HIP.
+ */
+int qlinear_gemv_multi(const ql_w4* Ws, int32_t count, const uint16_t* x, uint16_t* const* ys,
+                       void* stream);
 
 /*
  * qlinear_gemm - Y = X . dequant(W) for M activation rows (prefill).

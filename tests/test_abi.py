@@ -63,6 +63,28 @@ def test_gemv_validation(L):
     assert f(ctypes.byref(_w(N=0, qw=0, sc=0, bi=0)), None, None, None) == OK  # empty: nothing enqueued
 
 
+def test_gemv_multi_validation(L):
+    f = L.qlinear_gemv_multi
+
+    def call(ws, x=A16, ys=None, count=None):
+        arr = (ql.ql_w4 * len(ws))(*ws)
+        yp = (ctypes.c_void_p * len(ws))(*([A16] * len(ws) if ys is None else ys))
+        return f(arr, len(ws) if count is None else count, x, yp, None)
+
+    assert call([_w()], count=0) == INVALID
+    assert call([_w()] * 9) == INVALID                       # more than QL_GEMV_MULTI_MAX
+    assert f(None, 1, A16, None, None) == INVALID
+    assert call([_w(), _w(K=1024)]) == INVALID               # K differs
+    assert call([_w(K=192), _w(K=192)]) == SHAPE             # K not a chunked-kernel K
+    assert call([_w(K=100)]) == SHAPE
+    assert call([_w(), _w(qw=A16 + 4)]) == MISALIGNED
+    assert call([_w()], x=A16 + 8) == MISALIGNED
+    assert call([_w()], x=None) == INVALID
+    assert call([_w(), _w()], ys=[A16, None]) == INVALID
+    assert call([_w(), _w()], ys=[A16, A16 + 1]) == MISALIGNED
+    assert call([_w(N=0, qw=0, sc=0, bi=0)] * 2, x=None, ys=[None, None]) == OK  # nothing to do
+
+
 def test_gemm_validation(L):
     f = L.qlinear_gemm
     assert f(ctypes.byref(_w()), A16, -1, A16, None) == INVALID

@@ -139,3 +139,36 @@ def test_pack_matches_oracle():
         got = host(ql.qlinear_pack(t(codes))).view(np.uint32)
         torch.cuda.synchronize()
         assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("K,Ns,seed", [
+    (2048, (8192, synth.VOCAB), 20),        # the decode step's projection and vocabulary head
+    (512, (512, 100, 0, 7), 21),            # a skipped empty matrix, ragged N, fallback rows
+    (8192, (1000, 33), 22),                 # fixed rows per wave
+    (1024, (64,) * 8, 23),                  # QL_GEMV_MULTI_MAX matrices
+])
+def test_gemv_multi_matches_separate_calls(K, Ns, seed):
+    """qlinear_gemv_multi: every output has the bits of qlinear_gemv on its
+    matrix (same x), the guard regions stay intact, and the matrices that
+    the oracle finishes quickly match it."""
+    import torch
+    say(f"gemv multi K={K} Ns={Ns}")
+    cases = [synth.gemv_case(seed + 100 * i, K, N) if N > 0 else None for i, N in enumerate(Ns)]
+    x = synth.gemv_case(seed, K, 1)["x"]
+    Ws = [w4_dev(c["W"]) if c is not None else
+          {"qweight": torch.empty(0, dtype=torch.int32, device="cuda"),
+           "scales": torch.empty(0, dtype=torch.int16, device="cuda"),
+           "biases": torch.empty(0, dtype=torch.int16, device="cuda"), "K": K, "N": 0} for c in cases]
+    ys = [guarded(max(N, 1), torch.float16) for N in Ns]
+    ql.qlinear_gemv_multi(Ws, t(x[0]), [y.t[:N] for y, N in zip(ys, Ns)])
+    torch.cuda.synchronize()
+    for i, (N, y) in enumerate(zip(Ns, ys)):
+        y.check(f"multi matrix {i}")
+        if N == 0:
+            continue
+        ref = torch.empty(N, dtype=torch.float16, device="cuda")
+        ql.qlinear_gemv(Ws[i], t(x[0]), ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y.t[:N]).view(np.uint16), host(ref).view(np.uint16)), f"matrix {i}"
+        if N * K <= 8192 * 2048:
+            assert_close(host(y.t[:N]).astype(np.float64), oracle.linear(x, cases[i]["W"])[0], f"matrix {i}")

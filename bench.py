@@ -674,7 +674,42 @@ def bench_moe_decode(args, dev, w):
     ms_bf = graph_time(layer_bf16, NG, 30)
     k = [graph_time(fn, NG, 30) for fn in (route, gate_up, down)]
     algo = 2048 * 256 * 2 + 9 * (w4_bytes(2048, 1024) + w4_bytes(512, 2048)) + 2 * 2048 * 2
+    # FP8 and NVFP4 experts (moe_decode_fp8 / moe_decode_nvfp4), same tokens.
+    codec = {}
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    for name in ("fp8", "nvfp4"):
+        wc = synth.moe_weights_fp8(0) if name == "fp8" else synth.moe_weights_nvfp4(0)
+        ccopies = []
+        for c in range(2):
+            d = {}
+            for key in ("gate_up", "down", "shared_gate_up", "shared_down"):
+                d[key] = {kk: (to_dev(v) if isinstance(v, np.ndarray) and v.ndim > 0 else v)
+                          for kk, v in wc[key].items()}
+                if "global_scale" in d[key] and not torch.is_tensor(d[key]["global_scale"]):
+                    d[key]["global_scale"] = float(d[key]["global_scale"])
+            d["Wr"] = to_dev(wc["Wr"])
+            ccopies.append(d)
+        cbuf = ql.alloc_decode_outputs(1, 256, 8, 2048, 512, dev)
+
+        def layer_c(i, ccopies=ccopies, cbuf=cbuf, name=name):
+            dw = ccopies[i % 2]
+            ql.moe_decode_codec(name, toks[i % len(toks)], dw["Wr"], None, 8, dw["gate_up"], dw["down"],
+                                dw["shared_gate_up"], dw["shared_down"], out=cbuf)
+
+        for i in range(3):
+            layer_c(i)
+        torch.cuda.synchronize()
+        msc = graph_time(layer_c, NG, 30)
+        if name == "fp8":
+            mat = lambda K, N: N * K + 2 * N * (K // 64)
+        else:
+            mat = lambda K, N: N * K // 2 + N * (K // 16)
+        cb = 2048 * 256 * 2 + 9 * (mat(2048, 1024) + mat(512, 2048)) + 2 * 2048 * 2
+        codec[name] = {"us_per_token": msc * 1e3, "algorithmic_bytes": cb,
+                       "GB/s": cb / (msc * 1e-3) / 1e9, "entry": f"moe_decode_{name}"}
+        del ccopies
     return {"tokens/s": 1e3 / ms, "us_per_token": ms * 1e3, "algorithmic_bytes": algo,
+            "codec_experts": codec,
             "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "entry": "moe_decode (router partials; routing fused into gate/up; down + combine)",
             "three_call_us_per_token": ms3 * 1e3,

@@ -104,9 +104,10 @@ _SIGS = {
                                              _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "moe_combine_bf16": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8_experts), ctypes.POINTER(ql_fp8), _P,
-                                            _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+                                            _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "moe_grouped_gemm_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4_experts), ctypes.POINTER(ql_nvfp4),
-                                              _P, _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P, _P]),
+                                              _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P,
+                                              _P]),
     "moe_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "moe_decode_logits_offset": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "moe_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
@@ -117,6 +118,14 @@ _SIGS = {
                                        ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
                                        ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P,
                                        ctypes.c_size_t, _P, _P]),
+    "moe_decode_fp8": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
+                                      ctypes.POINTER(ql_fp8_experts), ctypes.POINTER(ql_fp8_experts),
+                                      ctypes.POINTER(ql_fp8), ctypes.POINTER(ql_fp8), _P, _P, _P,
+                                      ctypes.c_size_t, _P, _P]),
+    "moe_decode_nvfp4": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
+                                        ctypes.POINTER(ql_nvfp4_experts), ctypes.POINTER(ql_nvfp4_experts),
+                                        ctypes.POINTER(ql_nvfp4), ctypes.POINTER(ql_nvfp4), _P, _P, _P,
+                                        ctypes.c_size_t, _P, _P]),
     "moe_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32,
                                           ctypes.POINTER(ql_w4_experts), ctypes.POINTER(ql_w4_experts),
                                           ctypes.POINTER(ql_w4), ctypes.POINTER(ql_w4), _P, _P, _P, _P]),
@@ -466,6 +475,32 @@ def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op:
     fp16 scales [E][N][K/64] (device tensors), shared one such matrix or None
     (QL_OP_GATE_UP_SILU or QL_OP_DOWN)."""
     import torch
+    w, s = _fp8_structs(W, shared)
+    rows = T * topk + (T if shared is not None else 0)
+    Y = _grouped_out(Y, W, T, rows, op, X.device)
+    off, sa, gates, pos, ws, nws = _route_args(route)
+    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
+        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
+        off, sa, gates, pos, ws, nws, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def _grouped_out(Y, W, T, rows, op, device):
+    import torch
+    if Y is not None:
+        return Y
+    base = op & ~QL_OP_SHARED_ONLY
+    if base == QL_OP_GATE_UP_SILU:
+        shape = (rows, int(W["N"]) // 2)
+    elif base == QL_OP_DOWN:
+        shape = (rows, int(W["N"]))
+    else:
+        shape = (T, int(W["N"]))
+    return torch.empty(shape, dtype=torch.float16, device=device)
+
+
+def _fp8_structs(W, shared):
+    import torch
     codes = W["codes"]
     if codes.dtype != torch.uint8 or codes.dim() != 3 or W["scales"].dtype != torch.float16:
         raise ValueError("FP8 experts: codes uint8 [E][N][K], scales float16 [E][N][K/64]")
@@ -473,23 +508,10 @@ def moe_grouped_gemm_fp8(W: dict, shared: dict | None, X, T: int, topk: int, op:
                        int(codes.shape[0]))
     s = (ql_fp8(shared["codes"].data_ptr(), shared["scales"].data_ptr(), int(shared["K"]),
                 int(shared["N"])) if shared is not None else None)
-    rows = T * topk + (T if shared is not None else 0)
-    if Y is None:
-        shape = ((rows, int(W["N"]) // 2) if (op & ~QL_OP_SHARED_ONLY) == QL_OP_GATE_UP_SILU
-                 else (rows, int(W["N"])))
-        Y = torch.empty(shape, dtype=torch.float16, device=X.device)
-    off, sa, _, _, ws, nws = _route_args(route)
-    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
-        ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        off, sa, ws, nws, _ptr(Y), _stream(stream)))
-    return Y
+    return w, s
 
 
-def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
-                           Y=None, stream=None):
-    """moe_grouped_gemm with NVFP4 experts: W holds qweight [E][N][K/8],
-    block_scales uint8 [E][N][K/16] and global_scale fp32 [E] (device
-    tensors), shared one NVFP4 matrix (global_scale a float) or None."""
+def _nvfp4_structs(W, shared):
     import torch
     qw = W["qweight"]
     g = W["global_scale"]
@@ -502,15 +524,21 @@ def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, o
     s = (ql_nvfp4(shared["qweight"].data_ptr(), shared["block_scales"].data_ptr(),
                   float(shared["global_scale"]), int(shared["K"]), int(shared["N"]))
          if shared is not None else None)
+    return w, s
+
+
+def moe_grouped_gemm_nvfp4(W: dict, shared: dict | None, X, T: int, topk: int, op: int, route: dict,
+                           Y=None, stream=None):
+    """moe_grouped_gemm with NVFP4 experts: W holds qweight [E][N][K/8],
+    block_scales uint8 [E][N][K/16] and global_scale fp32 [E] (device
+    tensors), shared one NVFP4 matrix (global_scale a float) or None."""
+    w, s = _nvfp4_structs(W, shared)
     rows = T * topk + (T if shared is not None else 0)
-    if Y is None:
-        shape = ((rows, int(W["N"]) // 2) if (op & ~QL_OP_SHARED_ONLY) == QL_OP_GATE_UP_SILU
-                 else (rows, int(W["N"])))
-        Y = torch.empty(shape, dtype=torch.float16, device=X.device)
-    off, sa, _, _, ws, nws = _route_args(route)
+    Y = _grouped_out(Y, W, T, rows, op, X.device)
+    off, sa, gates, pos, ws, nws = _route_args(route)
     _check("moe_grouped_gemm_nvfp4", lib().moe_grouped_gemm_nvfp4(
         ctypes.byref(w), ctypes.byref(s) if s is not None else None, _ptr(X), T, topk, op,
-        off, sa, ws, nws, _ptr(Y), _stream(stream)))
+        off, sa, gates, pos, ws, nws, _ptr(Y), _stream(stream)))
     return Y
 
 
@@ -563,6 +591,29 @@ def moe_decode(H, Wr, logit_bias, topk: int, gate_up: dict, down: dict, shared_g
     sd = make_w4(shared_down) if shared_down is not None else None
     ws = out["workspace"]
     name = "moe_decode_bf16" if bf16 else "moe_decode"
+    _check(name, getattr(lib(), name)(
+        _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, ctypes.byref(gu), ctypes.byref(dn),
+        ctypes.byref(sg) if sg is not None else None, ctypes.byref(sd) if sd is not None else None,
+        _ptr(out["ids"]), _ptr(out["gates"]), _ptr(ws), ws.numel(), _ptr(out["out"]),
+        _stream(stream)))
+    return out
+
+
+def moe_decode_codec(codec: str, H, Wr, logit_bias, topk: int, gate_up: dict, down: dict,
+                     shared_gate_up=None, shared_down=None, out: dict | None = None, stream=None) -> dict:
+    """moe_decode_fp8 (codec "fp8") or moe_decode_nvfp4 ("nvfp4"): the decode
+    layer with codec experts, fp16 H / Wr / out; returns the dict of ids,
+    gates, out and workspace."""
+    T, D = H.shape
+    E = Wr.shape[1]
+    I = int(down["K"])
+    if out is None:
+        out = alloc_decode_outputs(T, E, topk, D, I, H.device)
+    make = _fp8_structs if codec == "fp8" else _nvfp4_structs
+    gu, sg = make(gate_up, shared_gate_up)
+    dn, sd = make(down, shared_down)
+    ws = out["workspace"]
+    name = "moe_decode_fp8" if codec == "fp8" else "moe_decode_nvfp4"
     _check(name, getattr(lib(), name)(
         _ptr(H), _ptr(Wr), _ptr(logit_bias), T, D, E, topk, ctypes.byref(gu), ctypes.byref(dn),
         ctypes.byref(sg) if sg is not None else None, ctypes.byref(sd) if sd is not None else None,

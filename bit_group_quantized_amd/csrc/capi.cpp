@@ -406,9 +406,9 @@ static int grouped_impl(const ExpertView& w, const uint16_t* X, int32_t T, int32
     if (!workspace || ws_bytes < moe_workspace_bytes(T, E, topk)) return QL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
 
-    // The row-parallel decode kernels take fp16 w4 weights only; the bf16
-    // and FP8 layers run every T on the tiled path.
-    const bool rows_path = !w.bf16 && w.wf == 0 && T <= QL_DECODE_MAX_T && ql::moe_rows_supported(w.K);
+    // The row-parallel decode kernels take fp16 activations (w4, FP8 or
+    // NVFP4 weights); the bf16 layer runs every T on the tiled path.
+    const bool rows_path = !w.bf16 && T <= QL_DECODE_MAX_T && ql::moe_rows_supported(w.K);
     if (op == QL_OP_DOWN_COMBINE) {
         if (!rows_path) return QL_ERR_UNSUPPORTED_SHAPE;
         if (!topk_gates || !assign_pos) return QL_ERR_INVALID_ARG;
@@ -446,10 +446,7 @@ int moe_grouped_gemm_bf16(const ql_w4_experts* W, const ql_w4* shared, const uin
                         workspace, ws_bytes, Y, stream);
 }
 
-int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared, const uint16_t* X,
-                         int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
-                         const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
-                         uint16_t* Y, void* stream) {
+static int fp8_view(const ql_fp8_experts* W, const ql_fp8* shared, ExpertView& v) {
     if (!W) return QL_ERR_INVALID_ARG;
     int rc = check_fp8(W->codes, W->scales, W->K, W->N);
     if (rc != QL_OK) return rc;
@@ -458,19 +455,14 @@ int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared, const ui
         if (rc != QL_OK) return rc;
         if (shared->K != W->K || shared->N != W->N) return QL_ERR_INVALID_ARG;
     }
-    if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
-    const ExpertView v{reinterpret_cast<const uint32_t*>(W->codes), W->scales, nullptr,
-                       shared ? reinterpret_cast<const uint32_t*>(shared->codes) : nullptr,
-                       shared ? shared->scales : nullptr, nullptr,
-                       W->K, W->N, W->num_experts, false, 1};
-    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr, workspace,
-                        ws_bytes, Y, stream);
+    v = ExpertView{reinterpret_cast<const uint32_t*>(W->codes), W->scales, nullptr,
+                   shared ? reinterpret_cast<const uint32_t*>(shared->codes) : nullptr,
+                   shared ? shared->scales : nullptr, nullptr,
+                   W->K, W->N, W->num_experts, false, 1};
+    return QL_OK;
 }
 
-int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared, const uint16_t* X,
-                           int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
-                           const int32_t* sorted_assign, const void* workspace, size_t ws_bytes,
-                           uint16_t* Y, void* stream) {
+static int nvfp4_view(const ql_nvfp4_experts* W, const ql_nvfp4* shared, ExpertView& v) {
     if (!W || W->N < 0 || W->K < 0) return QL_ERR_INVALID_ARG;
     if (W->K == 0 || W->K % QL_GROUP_SIZE != 0 || W->K > QL_MAX_K) return QL_ERR_UNSUPPORTED_SHAPE;
     if (W->N > 0) {
@@ -486,14 +478,34 @@ int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared, co
             if (!aligned(shared->qweight, 16) || !aligned(shared->block_scales, 4)) return QL_ERR_MISALIGNED;
         }
     }
-    if (op == QL_OP_DOWN_COMBINE) return QL_ERR_UNSUPPORTED_SHAPE;
-    ExpertView v{W->qweight, reinterpret_cast<const uint16_t*>(W->block_scales), nullptr,
-                 shared ? shared->qweight : nullptr,
-                 shared ? reinterpret_cast<const uint16_t*>(shared->block_scales) : nullptr, nullptr,
-                 W->K, W->N, W->num_experts, false, 2};
+    v = ExpertView{W->qweight, reinterpret_cast<const uint16_t*>(W->block_scales), nullptr,
+                   shared ? shared->qweight : nullptr,
+                   shared ? reinterpret_cast<const uint16_t*>(shared->block_scales) : nullptr, nullptr,
+                   W->K, W->N, W->num_experts, false, 2};
     v.gscales = W->global_scales;
     v.sgscale = shared ? shared->global_scale : 0.f;
-    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, nullptr, nullptr, workspace,
+    return QL_OK;
+}
+
+int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared, const uint16_t* X,
+                         int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
+                         const int32_t* sorted_assign, const float* topk_gates,
+                         const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
+                         uint16_t* Y, void* stream) {
+    ExpertView v;
+    if (const int rc = fp8_view(W, shared, v)) return rc;
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, topk_gates, assign_pos, workspace,
+                        ws_bytes, Y, stream);
+}
+
+int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared, const uint16_t* X,
+                           int32_t T, int32_t topk, int32_t op, const int32_t* offsets,
+                           const int32_t* sorted_assign, const float* topk_gates,
+                           const int32_t* assign_pos, const void* workspace, size_t ws_bytes,
+                           uint16_t* Y, void* stream) {
+    ExpertView v;
+    if (const int rc = nvfp4_view(W, shared, v)) return rc;
+    return grouped_impl(v, X, T, topk, op, offsets, sorted_assign, topk_gates, assign_pos, workspace,
                         ws_bytes, Y, stream);
 }
 
@@ -509,38 +521,21 @@ size_t moe_decode_logits_offset(int32_t T, int32_t E, int32_t topk) {
     return ql::moe_decode_layout(T, E, topk, 64).logits;
 }
 
-// ws_mode 0: the caller's workspace; 1: the library's scratch array
-// (moe_decode_noalloc), checked against QL_DECODE_SCRATCH_BYTES.
-static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
-                       int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
-                       const ql_w4_experts* down, const ql_w4* shared_gate_up,
-                       const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
-                       void* workspace, size_t ws_bytes, uint16_t* out, void* stream, bool bf16,
-                       int ws_mode = 0) {
-    if (!gate_up || !down) return QL_ERR_INVALID_ARG;
-    if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
+// The whole decode layer for two expert views (gate/up and down, each with
+// its shared matrix or none).  ws_mode 0: the caller's workspace; 1: the
+// library's scratch array (moe_decode_noalloc), checked against
+// QL_DECODE_SCRATCH_BYTES.
+static int decode_run(const ExpertView& gu, const ExpertView& dn, bool has_shared, const uint16_t* H,
+                      const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D, int32_t E,
+                      int32_t topk, int32_t* topk_ids, float* topk_gates, void* workspace,
+                      size_t ws_bytes, uint16_t* out, void* stream, int ws_mode) {
     if (T < 0 || E <= 0 || topk <= 0 || topk > E || D <= 0) return QL_ERR_INVALID_ARG;
     if (T > QL_DECODE_MAX_T || E > QL_MAX_EXPERTS || topk > QL_MAX_TOPK) return QL_ERR_UNSUPPORTED_SHAPE;
-    if (gate_up->num_experts != E || down->num_experts != E) return QL_ERR_INVALID_ARG;
-    const ql_w4_experts& gu = *gate_up;
-    const ql_w4_experts& dn = *down;
-    int rc = check_w4(gu.qweight, gu.scales, gu.biases, gu.K, gu.N, gu.group_size);
-    if (rc != QL_OK) return rc;
-    rc = check_w4(dn.qweight, dn.scales, dn.biases, dn.K, dn.N, dn.group_size);
-    if (rc != QL_OK) return rc;
+    if (gu.E != E || dn.E != E) return QL_ERR_INVALID_ARG;
     const int32_t I = dn.K;
     if (gu.K != D || dn.N != D || gu.N != 2 * I) return QL_ERR_INVALID_ARG;
-    if (shared_gate_up) {
-        const ql_w4& sg = *shared_gate_up;
-        const ql_w4& sd = *shared_down;
-        rc = check_w4(sg.qweight, sg.scales, sg.biases, sg.K, sg.N, sg.group_size);
-        if (rc != QL_OK) return rc;
-        rc = check_w4(sd.qweight, sd.scales, sd.biases, sd.K, sd.N, sd.group_size);
-        if (rc != QL_OK) return rc;
-        if (sg.K != D || sg.N != 2 * I || sd.K != I || sd.N != D) return QL_ERR_INVALID_ARG;
-    }
     if (!ql::moe_rows_supported(D) || !ql::moe_rows_supported(I)) return QL_ERR_UNSUPPORTED_SHAPE;
-    const int J = topk + (shared_gate_up ? 1 : 0);
+    const int J = topk + (has_shared ? 1 : 0);
     if ((int64_t)J * I * 2 > 49152) return QL_ERR_UNSUPPORTED_SHAPE;
     if (T == 0) return QL_OK;
     if (!H || !Wr || !topk_ids || !topk_gates || !out) return QL_ERR_INVALID_ARG;
@@ -557,15 +552,32 @@ static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit
         if (!aligned(workspace, 256)) return QL_ERR_MISALIGNED;
     }
     ql::DecodeArgs a{H, Wr, logit_bias, T, D, E, topk, I,
-                     gu.qweight, gu.scales, gu.biases, dn.qweight, dn.scales, dn.biases,
-                     shared_gate_up ? shared_gate_up->qweight : nullptr,
-                     shared_gate_up ? shared_gate_up->scales : nullptr,
-                     shared_gate_up ? shared_gate_up->biases : nullptr,
-                     shared_down ? shared_down->qweight : nullptr,
-                     shared_down ? shared_down->scales : nullptr,
-                     shared_down ? shared_down->biases : nullptr,
-                     topk_ids, topk_gates, static_cast<unsigned char*>(workspace), out, bf16};
+                     gu.qw, gu.sc, gu.bi, dn.qw, dn.sc, dn.bi,
+                     has_shared ? gu.sqw : nullptr, has_shared ? gu.ssc : nullptr,
+                     has_shared ? gu.sbi : nullptr, has_shared ? dn.sqw : nullptr,
+                     has_shared ? dn.ssc : nullptr, has_shared ? dn.sbi : nullptr,
+                     topk_ids, topk_gates, static_cast<unsigned char*>(workspace), out, gu.bf16};
+    a.wf = gu.wf;
+    a.gu_gscales = gu.gscales;
+    a.dn_gscales = dn.gscales;
+    a.sgu_gscale = gu.sgscale;
+    a.sdn_gscale = dn.sgscale;
     return ql::launch_moe_decode(a, as_stream(stream));
+}
+
+static int decode_impl(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                       int32_t D, int32_t E, int32_t topk, const ql_w4_experts* gate_up,
+                       const ql_w4_experts* down, const ql_w4* shared_gate_up,
+                       const ql_w4* shared_down, int32_t* topk_ids, float* topk_gates,
+                       void* workspace, size_t ws_bytes, uint16_t* out, void* stream, bool bf16,
+                       int ws_mode = 0) {
+    if (!gate_up || !down) return QL_ERR_INVALID_ARG;
+    if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
+    ExpertView gu, dn;
+    if (const int rc = w4_view(gate_up, shared_gate_up, bf16, gu)) return rc;
+    if (const int rc = w4_view(down, shared_down, bf16, dn)) return rc;
+    return decode_run(gu, dn, shared_gate_up != nullptr, H, Wr, logit_bias, T, D, E, topk, topk_ids,
+                      topk_gates, workspace, ws_bytes, out, stream, ws_mode);
 }
 
 int moe_decode(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
@@ -583,6 +595,33 @@ int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bi
                     void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
     return decode_impl(H, Wr, logit_bias, T, D, E, topk, gate_up, down, shared_gate_up, shared_down,
                        topk_ids, topk_gates, workspace, ws_bytes, out, stream, true);
+}
+
+int moe_decode_fp8(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T, int32_t D,
+                   int32_t E, int32_t topk, const ql_fp8_experts* gate_up, const ql_fp8_experts* down,
+                   const ql_fp8* shared_gate_up, const ql_fp8* shared_down, int32_t* topk_ids,
+                   float* topk_gates, void* workspace, size_t ws_bytes, uint16_t* out, void* stream) {
+    if (!gate_up || !down) return QL_ERR_INVALID_ARG;
+    if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
+    ExpertView gu, dn;
+    if (const int rc = fp8_view(gate_up, shared_gate_up, gu)) return rc;
+    if (const int rc = fp8_view(down, shared_down, dn)) return rc;
+    return decode_run(gu, dn, shared_gate_up != nullptr, H, Wr, logit_bias, T, D, E, topk, topk_ids,
+                      topk_gates, workspace, ws_bytes, out, stream, 0);
+}
+
+int moe_decode_nvfp4(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,
+                     int32_t D, int32_t E, int32_t topk, const ql_nvfp4_experts* gate_up,
+                     const ql_nvfp4_experts* down, const ql_nvfp4* shared_gate_up,
+                     const ql_nvfp4* shared_down, int32_t* topk_ids, float* topk_gates, void* workspace,
+                     size_t ws_bytes, uint16_t* out, void* stream) {
+    if (!gate_up || !down) return QL_ERR_INVALID_ARG;
+    if ((shared_gate_up == nullptr) != (shared_down == nullptr)) return QL_ERR_INVALID_ARG;
+    ExpertView gu, dn;
+    if (const int rc = nvfp4_view(gate_up, shared_gate_up, gu)) return rc;
+    if (const int rc = nvfp4_view(down, shared_down, dn)) return rc;
+    return decode_run(gu, dn, shared_gate_up != nullptr, H, Wr, logit_bias, T, D, E, topk, topk_ids,
+                      topk_gates, workspace, ws_bytes, out, stream, 0);
 }
 
 int moe_decode_noalloc(const uint16_t* H, const uint16_t* Wr, const float* logit_bias, int32_t T,

@@ -21,6 +21,7 @@
 // with the per-group activation sum computed once.
 #include <type_traits>
 
+#include "ql_codecs.h"
 #include "ql_device.h"
 #include "ql_internal.h"
 #include "ql_topk.h"
@@ -469,15 +470,87 @@ __device__ __forceinline__ void rows_load_x(const uint16_t* __restrict__ X, int 
         for (int w = 0; w < 4; ++w) xr[v][w] = ld_u32x4(X + (size_t)xrow * K + (lr + v * TPR) * 32 + w * 8);
 }
 
+// Weight formats of the decode rows (WF): 0 = w4 (codes, fp16 scale and bias
+// per 64); 1 = FP8-E4M3 codes [N][K] (bytes, through wq) with an fp16 scale
+// per 64 (ws) and no bias; 2 = NVFP4: E2M1 codes in the w4 packing, E4M3
+// block-scale bytes [N][K/16] (through ws) and the matrix's global scale.
+// A lane's chunk is always 32 codes (k = 32c .. 32c+31) against the same 32
+// activations; the codec chunks are dotted as the codec GEMVs do (exact
+// fp16 code values in v_dot2_f32_f16, scales on fp32 partial sums).
+template <int WF>
+struct RowChunk {
+    u32x4 c[(WF == 1) ? 2 : 1];  // codes: 16 bytes (w4, NVFP4) or 32 (FP8)
+    uint16_t s, b;               // fp16 scale and bias (w4), scale (FP8), the two block-scale bytes (NVFP4)
+};
+
+template <int WF>
+__device__ __forceinline__ RowChunk<WF> row_chunk_load(const uint32_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ ws,
+                                                       const uint16_t* __restrict__ wb, int row, int hg,
+                                                       int K) {
+    RowChunk<WF> ch;
+    const int G = K / kGroup;
+    if constexpr (WF == 1) {
+        const uint8_t* c8 = reinterpret_cast<const uint8_t*>(wq) + (size_t)row * K + hg * 32;
+        ch.c[0] = ld_stream_u32x4(c8);
+        ch.c[1] = ld_stream_u32x4(c8 + 16);
+        ch.s = ws[(size_t)row * G + (hg >> 1)];
+        ch.b = 0;
+    } else if constexpr (WF == 2) {
+        ch.c[0] = ld_stream_u32x4(wq + (size_t)row * (K / 8) + hg * 4);
+        ch.s = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(ws) + (size_t)row * (K / 16) +
+                                                  2 * hg);
+        ch.b = 0;
+    } else {
+        ch.c[0] = ld_stream_u32x4(wq + (size_t)row * (K / 8) + hg * 4);
+        ch.s = ws[(size_t)row * G + (hg >> 1)];
+        ch.b = wb[(size_t)row * G + (hg >> 1)];
+    }
+    return ch;
+}
+
+// Codec chunk dot product against the 32 raw activations xw (fp16 pairs in
+// natural order): FP8 scale * sum, NVFP4 e4m3(block) * sum per block of 16
+// (the global scale is applied by the caller).
+template <int WF>
+__device__ __forceinline__ float codec_chunk_dot(const RowChunk<WF>& ch, const u32x4 (&xw)[4]) {
+    if constexpr (WF == 1) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {  // code word i: codes 4i .. 4i+3
+            const uint32_t cwd = ch.c[i >> 2][i & 3];
+            const u32x4 xq = xw[i >> 1];
+            d0 = dot2(as_f16x2(xq[2 * (i & 1)]), e4m3x2_to_f16x2<false>(cwd), d0);
+            d1 = dot2(as_f16x2(xq[2 * (i & 1) + 1]), e4m3x2_to_f16x2<true>(cwd), d1);
+        }
+        return h2f(ch.s) * (d0 + d1);
+    } else {
+        float d[2] = {0.f, 0.f};  // blocks 2c and 2c + 1 (words 0-1 and 2-3)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const u32x4 xq = xw[w];
+            const uint32_t cwd = ch.c[0][w];
+            float e = d[w >> 1];
+            e = dot2(as_f16x2(xq.x), e2m1x2_to_f16x2<0>(cwd), e);
+            e = dot2(as_f16x2(xq.y), e2m1x2_to_f16x2<1>(cwd), e);
+            e = dot2(as_f16x2(xq.z), e2m1x2_to_f16x2<2>(cwd), e);
+            e = dot2(as_f16x2(xq.w), e2m1x2_to_f16x2<3>(cwd), e);
+            d[w >> 1] = e;
+        }
+        return e4m3_to_f32<0>(ch.s) * d[0] + e4m3_to_f32<1>(ch.s) * d[1];
+    }
+}
+
 // One wave's outputs of row r: column block `xblock` of the expert matrix
-// (wq, ws, wb) applied to the activations xr.  BF16: activations, scales,
-// biases and outputs are bf16 patterns (codes enter v_dot2_f32_bf16 exactly,
-// as in the bf16 GEMV).
-template <int TPR, int V, int R, int MODE, bool BF16 = false>
+// (wq, ws, wb; WF as above, gscale the NVFP4 global scale) applied to the
+// activations xr.  BF16: activations, scales, biases and outputs are bf16
+// patterns (codes enter v_dot2_f32_bf16 exactly, as in the bf16 GEMV).
+template <int TPR, int V, int R, int MODE, bool BF16 = false, int WF = 0>
 __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_t* __restrict__ wq,
                                           const uint16_t* __restrict__ ws, const uint16_t* __restrict__ wb,
-                                          uint16_t* __restrict__ Y, int r, int xblock, int K, int N,
-                                          int lane) {
+                                          float gscale, uint16_t* __restrict__ Y, int r, int xblock, int K,
+                                          int N, int lane) {
+    static_assert(WF == 0 || !BF16, "codec rows: fp16 activations");
     constexpr int TEAMS = 64 / TPR;
     constexpr int OUT = (MODE == 0) ? R / 2 : R;  // outputs per team
     const int lr = lane % TPR;
@@ -487,23 +560,26 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
     const int Nout = (MODE == 0) ? N / 2 : N;
     const int n0 = (xblock * TEAMS + team) * OUT;
 
-    u32x4 cw[R][V];
-    uint16_t s[R][V], b[R][V];
+    RowChunk<WF> chk[R][V];
 #pragma unroll
     for (int q = 0; q < R; ++q) {
         const int nn = min(n0 + q % OUT, Nout - 1);
         const int row = nn + ((MODE == 0 && q >= OUT) ? Nout : 0);
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int hg = lr + v * TPR;
-            cw[q][v] = ld_stream_u32x4(wq + (size_t)row * wpr + hg * 4);
-            s[q][v] = ws[(size_t)row * G + (hg >> 1)];
-            b[q][v] = wb[(size_t)row * G + (hg >> 1)];
-        }
+        for (int v = 0; v < V; ++v) chk[q][v] = row_chunk_load<WF>(wq, ws, wb, row, lr + v * TPR, K);
     }
+    (void)G;
+    (void)wpr;
     __builtin_amdgcn_sched_barrier(0);
     float acc[R];
-    if constexpr (BF16) {
+    if constexpr (WF != 0) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            acc[q] = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[q] += codec_chunk_dot<WF>(chk[q][v], xr[v]);
+        }
+    } else if constexpr (BF16) {
         XPairsBf xp[V][4];
         float xs[V];
 #pragma unroll
@@ -521,12 +597,13 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-                dot_word_bf(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
-                dot_word_bf(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
-                dot_word_bf(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
-                dot_word_bf(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
+                const u32x4 cwv = chk[q][v].c[0];
+                dot_word_bf(cwv.x, xp[v][0], d0, d1, d2, d3);
+                dot_word_bf(cwv.y, xp[v][1], d0, d1, d2, d3);
+                dot_word_bf(cwv.z, xp[v][2], d0, d1, d2, d3);
+                dot_word_bf(cwv.w, xp[v][3], d0, d1, d2, d3);
                 const float d = (d0 + d2) + (d1 + d3);
-                acc[q] += bf2f(s[q][v]) * (d - 128.0f * xs[v]) + bf2f(b[q][v]) * xs[v];
+                acc[q] += bf2f(chk[q][v].s) * (d - 128.0f * xs[v]) + bf2f(chk[q][v].b) * xs[v];
             }
         }
     } else {
@@ -551,11 +628,12 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-                dot_word(cw[q][v].x, xp[v][0], d0, d1, d2, d3);
-                dot_word(cw[q][v].y, xp[v][1], d0, d1, d2, d3);
-                dot_word(cw[q][v].z, xp[v][2], d0, d1, d2, d3);
-                dot_word(cw[q][v].w, xp[v][3], d0, d1, d2, d3);
-                acc[q] += h2f(s[q][v]) * (dot_sum(d0, d1, d2, d3) - xc[v]) + h2f(b[q][v]) * xs[v];
+                const u32x4 cwv = chk[q][v].c[0];
+                dot_word(cwv.x, xp[v][0], d0, d1, d2, d3);
+                dot_word(cwv.y, xp[v][1], d0, d1, d2, d3);
+                dot_word(cwv.z, xp[v][2], d0, d1, d2, d3);
+                dot_word(cwv.w, xp[v][3], d0, d1, d2, d3);
+                acc[q] += h2f(chk[q][v].s) * (dot_sum(d0, d1, d2, d3) - xc[v]) + h2f(chk[q][v].b) * xs[v];
             }
         }
     }
@@ -564,7 +642,8 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
         else return f2h(v);
     };
     int sel;
-    const float tot = reduce_rows<TPR, R>(acc, lr, sel);
+    float tot = reduce_rows<TPR, R>(acc, lr, sel);
+    if constexpr (WF == 2) tot *= gscale;  // both rows of a gate/up pair come from one expert
     const bool writer = (lr & (TPR / R - 1)) == 0;
     if constexpr (MODE == 0) {
         const float up = __shfl_xor(tot, TPR / 2, 64);  // row sel + R/2 of the same team
@@ -575,36 +654,57 @@ __device__ __forceinline__ void rows_body(const u32x4 (&xr)[V][4], const uint32_
     }
 }
 
-template <int TPR, int V, int R, int MODE>
+// Expert e's matrix within stacked experts of weight format WF (pointers
+// as rows_body takes them).
+template <int WF>
+__device__ __forceinline__ void expert_ptrs(const uint32_t* qw, const uint16_t* sc, const uint16_t* bi,
+                                            int e, int N, int K, const uint32_t*& wq, const uint16_t*& ws,
+                                            const uint16_t*& wb) {
+    const size_t n = (size_t)e * N;
+    if constexpr (WF == 1) {
+        wq = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(qw) + n * K);
+        ws = sc + n * (K / kGroup);
+        wb = nullptr;
+    } else if constexpr (WF == 2) {
+        wq = qw + n * (K / 8);
+        ws = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sc) + n * (K / 16));
+        wb = nullptr;
+    } else {
+        wq = qw + n * (K / 8);
+        ws = sc + n * (K / kGroup);
+        wb = bi + n * (K / kGroup);
+    }
+}
+
+template <int TPR, int V, int R, int MODE, int WF = 0>
 __global__ void __launch_bounds__(64)
 moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                 const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
                 const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                const float* __restrict__ gscales, float sgscale,
                 const uint16_t* __restrict__ X, const int2* __restrict__ row_info,
                 uint16_t* __restrict__ Y, int K, int N, int E, int T, int topk) {
     const int lane = threadIdx.x;
-    const int G = K / kGroup;
-    const int wpr = K / 8;
     const int r = blockIdx.y;
     const int routed = T * topk;
     const uint32_t* wq = sqw;
     const uint16_t* ws = ssc;
     const uint16_t* wb = sbi;
+    float gscale = sgscale;
     int xrow;
     if (r < routed) {
         const int2 info = row_info[r];
         // Clamped so that a corrupted dispatch can never index out of bounds.
         const int e = min(max(info.x, 0), E - 1);
-        wq = qw + (size_t)e * N * wpr;
-        ws = sc + (size_t)e * N * G;
-        wb = bi + (size_t)e * N * G;
+        expert_ptrs<WF>(qw, sc, bi, e, N, K, wq, ws, wb);
+        if constexpr (WF == 2) gscale = gscales[e];
         xrow = (MODE == 0) ? min(max(info.y, 0), T - 1) : r;
     } else {
         xrow = (MODE == 0) ? r - routed : r;
     }
     u32x4 xr[V][4];
     rows_load_x<TPR, V>(X, xrow, K, lane % TPR, xr);
-    rows_body<TPR, V, R, MODE>(xr, wq, ws, wb, Y, r, blockIdx.x, K, N, lane);
+    rows_body<TPR, V, R, MODE, false, WF>(xr, wq, ws, wb, gscale, Y, r, blockIdx.x, K, N, lane);
 }
 
 // Decode gate/up projection fused with the token's routing: block (x, r)
@@ -617,12 +717,13 @@ moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
 // weights; its activation loads are issued before the routing.  Blocks with
 // x = 0 also write the token's ids, gates, logits and the (expert, row) of
 // their assignment for the down projection.
-template <int TPR, int V, int R, int EPL, bool BF16>
+template <int TPR, int V, int R, int EPL, bool BF16, int WF = 0>
 __global__ void __launch_bounds__(256)
 moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __restrict__ bias,
                           const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                           const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
                           const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                          const float* __restrict__ gscales, float sgscale,
                           const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int K, int N,
                           int E, int T, int topk, int* __restrict__ ids, float* __restrict__ gates,
                           float* __restrict__ logits_out, int2* __restrict__ assign_info) {
@@ -641,6 +742,7 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
     const uint32_t* wq = sqw;
     const uint16_t* ws = ssc;
     const uint16_t* wb = sbi;
+    float gscale = sgscale;
     if (r < routed) {  // uniform over the block
         const int j = r - t * topk;
         for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -662,9 +764,8 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
             __syncthreads();
         }
         const int e = min(max(s_sel[j], 0), E - 1);
-        wq = qw + (size_t)e * N * wpr;
-        ws = sc + (size_t)e * N * G;
-        wb = bi + (size_t)e * N * G;
+        expert_ptrs<WF>(qw, sc, bi, e, N, K, wq, ws, wb);
+        if constexpr (WF == 2) gscale = gscales[e];
         if (blockIdx.x == 0) {
             if (threadIdx.x == 0) {
                 ids[r] = e;
@@ -675,7 +776,7 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
                 for (int i = threadIdx.x; i < E; i += blockDim.x) logits_out[(size_t)t * E + i] = s_lg[i];
         }
     }
-    rows_body<TPR, V, R, 0, BF16>(xr, wq, ws, wb, Y, r, blockIdx.x * 4 + wave, K, N, lane);
+    rows_body<TPR, V, R, 0, BF16, WF>(xr, wq, ws, wb, gscale, Y, r, blockIdx.x * 4 + wave, K, N, lane);
 }
 
 // Decode down projection fused with the gate-weighted sum over the token's
@@ -688,14 +789,18 @@ moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __res
 // pre-paired into LDS while the codes are in flight.  Sums, in a fixed
 // order: per lane over the wave's rows in ascending j, across the lanes of
 // the row team, then the four wave sums in wave order.
-template <int TPR, int V, int R, int JC, bool BF16 = false>
+// WF: weight format as in rows_body (codec rows keep the activation chunks
+// raw in LDS; the NVFP4 global scale of each row joins its gate).
+template <int TPR, int V, int R, int JC, bool BF16 = false, int WF = 0>
 __global__ void __launch_bounds__(256)
 moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                         const uint16_t* __restrict__ bi, const uint32_t* __restrict__ sqw,
                         const uint16_t* __restrict__ ssc, const uint16_t* __restrict__ sbi,
+                        const float* __restrict__ gscales, float sgscale,
                         const uint16_t* __restrict__ X, const float* __restrict__ gates,
                         const int2* __restrict__ assign_info, uint16_t* __restrict__ Y, int K,
                         int N, int E, int T, int topk, int has_shared) {
+    static_assert(WF == 0 || !BF16, "codec rows: fp16 activations");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_exp[QL_MAX_TOPK_DEV + 1];
     __shared__ int s_row[QL_MAX_TOPK_DEV + 1];
@@ -720,10 +825,11 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
             s_exp[j] = min(max(info.x, 0), E - 1);
             s_row[j] = min(max(info.y, 0), nrows - 1);
             s_gate[j] = gates[(size_t)t * topk + j];
+            if constexpr (WF == 2) s_gate[j] *= gscales[s_exp[j]];
         } else {
             s_exp[j] = -1;
             s_row[j] = T * topk + t;
-            s_gate[j] = 1.0f;
+            s_gate[j] = (WF == 2) ? sgscale : 1.0f;
         }
     }
     __syncthreads();
@@ -748,7 +854,9 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
         float cc = 0.f, xx = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            if constexpr (BF16) {
+            if constexpr (WF != 0) {
+                s_xp[((size_t)j * CH + c) * 4 + w] = __builtin_bit_cast(XPairs, xw[w]);  // raw pairs
+            } else if constexpr (BF16) {
                 const XPairsBf xp = make_xpairs_bf(xw[w]);
                 xx += xsum_bf(xp);
                 s_xp[((size_t)j * CH + c) * 4 + w] = __builtin_bit_cast(XPairs, xp);
@@ -772,30 +880,27 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
     for (int q = 0; q < R; ++q) acc[q] = 0.f;
 
     // This wave's rows: j = wave, wave + 4, ..., JC of them per round.
-    u32x4 cw[JC][R][V];
-    uint16_t s[JC][R][V], b[JC][R][V];
+    RowChunk<WF> chk[JC][R][V];
     auto load_round = [&](int j0) {
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
             const int j = j0 + NW * jj;
             if (j >= J) break;  // uniform across the wave
             const int e = s_exp[j];
-            const uint32_t* wq = (e >= 0) ? qw + (size_t)e * N * wpr : sqw;
-            const uint16_t* ws = (e >= 0) ? sc + (size_t)e * N * G : ssc;
-            const uint16_t* wb = (e >= 0) ? bi + (size_t)e * N * G : sbi;
+            const uint32_t* wq = sqw;
+            const uint16_t* ws = ssc;
+            const uint16_t* wb = sbi;
+            if (e >= 0) expert_ptrs<WF>(qw, sc, bi, e, N, K, wq, ws, wb);
 #pragma unroll
             for (int q = 0; q < R; ++q) {
                 const int row = min(n0 + q, N - 1);
 #pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const int hg = lr + v * TPR;
-                    cw[jj][q][v] = ld_stream_u32x4(wq + (size_t)row * wpr + hg * 4);
-                    s[jj][q][v] = ws[(size_t)row * G + (hg >> 1)];
-                    b[jj][q][v] = wb[(size_t)row * G + (hg >> 1)];
-                }
+                for (int v = 0; v < V; ++v) chk[jj][q][v] = row_chunk_load<WF>(wq, ws, wb, row, lr + v * TPR, K);
             }
         }
     };
+    (void)G;
+    (void)wpr;
     auto compute_round = [&](int j0) {
 #pragma unroll
         for (int jj = 0; jj < JC; ++jj) {
@@ -808,24 +913,32 @@ moe_down_combine_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restr
                 XPairs xp[4];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) xp[w] = s_xp[((size_t)j * CH + hg) * 4 + w];
+                if constexpr (WF != 0) {
+                    const u32x4 xw[4] = {__builtin_bit_cast(u32x4, xp[0]), __builtin_bit_cast(u32x4, xp[1]),
+                                         __builtin_bit_cast(u32x4, xp[2]), __builtin_bit_cast(u32x4, xp[3])};
+#pragma unroll
+                    for (int q = 0; q < R; ++q) acc[q] += g * codec_chunk_dot<WF>(chk[jj][q][v], xw);
+                    continue;
+                }
                 const float xc = s_c[j * CH + hg], xs = s_xs[j * CH + hg];
 #pragma unroll
                 for (int q = 0; q < R; ++q) {
                     float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+                    const u32x4 cwv = chk[jj][q][v].c[0];
                     if constexpr (BF16) {
-                        dot_word_bf(cw[jj][q][v].x, __builtin_bit_cast(XPairsBf, xp[0]), d0, d1, d2, d3);
-                        dot_word_bf(cw[jj][q][v].y, __builtin_bit_cast(XPairsBf, xp[1]), d0, d1, d2, d3);
-                        dot_word_bf(cw[jj][q][v].z, __builtin_bit_cast(XPairsBf, xp[2]), d0, d1, d2, d3);
-                        dot_word_bf(cw[jj][q][v].w, __builtin_bit_cast(XPairsBf, xp[3]), d0, d1, d2, d3);
-                        acc[q] += g * (bf2f(s[jj][q][v]) * (((d0 + d2) + (d1 + d3)) - 128.0f * xs) +
-                                       bf2f(b[jj][q][v]) * xs);
+                        dot_word_bf(cwv.x, __builtin_bit_cast(XPairsBf, xp[0]), d0, d1, d2, d3);
+                        dot_word_bf(cwv.y, __builtin_bit_cast(XPairsBf, xp[1]), d0, d1, d2, d3);
+                        dot_word_bf(cwv.z, __builtin_bit_cast(XPairsBf, xp[2]), d0, d1, d2, d3);
+                        dot_word_bf(cwv.w, __builtin_bit_cast(XPairsBf, xp[3]), d0, d1, d2, d3);
+                        acc[q] += g * (bf2f(chk[jj][q][v].s) * (((d0 + d2) + (d1 + d3)) - 128.0f * xs) +
+                                       bf2f(chk[jj][q][v].b) * xs);
                     } else {
-                        dot_word(cw[jj][q][v].x, xp[0], d0, d1, d2, d3);
-                        dot_word(cw[jj][q][v].y, xp[1], d0, d1, d2, d3);
-                        dot_word(cw[jj][q][v].z, xp[2], d0, d1, d2, d3);
-                        dot_word(cw[jj][q][v].w, xp[3], d0, d1, d2, d3);
-                        acc[q] += g * (h2f(s[jj][q][v]) * (dot_sum(d0, d1, d2, d3) - xc) +
-                                       h2f(b[jj][q][v]) * xs);
+                        dot_word(cwv.x, xp[0], d0, d1, d2, d3);
+                        dot_word(cwv.y, xp[1], d0, d1, d2, d3);
+                        dot_word(cwv.z, xp[2], d0, d1, d2, d3);
+                        dot_word(cwv.w, xp[3], d0, d1, d2, d3);
+                        acc[q] += g * (h2f(chk[jj][q][v].s) * (dot_sum(d0, d1, d2, d3) - xc) +
+                                       h2f(chk[jj][q][v].b) * xs);
                     }
                 }
             }
@@ -877,7 +990,7 @@ inline int pow2_divisor(int G) {
     return t;
 }
 
-template <int TPR, int V, bool BF16 = false>
+template <int TPR, int V, bool BF16 = false, int WF = 0>
 void launch_down_combine_t(const GroupedArgs& a, const int2* assign_info, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
     constexpr int R = (TPR < 2) ? TPR : 2;
@@ -886,9 +999,17 @@ void launch_down_combine_t(const GroupedArgs& a, const int2* assign_info, hipStr
     const size_t smem = (size_t)J * (a.K / 32) * (4 * sizeof(XPairs) + 2 * sizeof(float));
     dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), a.T);
     // four waves; each takes the rows j = wave, wave + 4, ... (3 per round)
-    hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3, BF16>), grid, dim3(256), smem, st, a.qw, a.sc,
-                       a.bi, a.sqw, a.ssc, a.sbi, a.X, a.gates, assign_info, a.Y, a.K, a.N, a.E, a.T,
-                       a.topk, has_shared);
+    hipLaunchKernelGGL((moe_down_combine_kernel<TPR, V, R, 3, BF16, WF>), grid, dim3(256), smem, st, a.qw,
+                       a.sc, a.bi, a.sqw, a.ssc, a.sbi, a.gscales, a.sgscale, a.X, a.gates, assign_info, a.Y,
+                       a.K, a.N, a.E, a.T, a.topk, has_shared);
+}
+
+template <int TPR, int V>
+void launch_down_combine_wf(const GroupedArgs& a, const int2* assign_info, hipStream_t st) {
+    if (a.wf == 1) launch_down_combine_t<TPR, V, false, 1>(a, assign_info, st);
+    else if (a.wf == 2) launch_down_combine_t<TPR, V, false, 2>(a, assign_info, st);
+    else if (a.bf16) launch_down_combine_t<TPR, V, true>(a, assign_info, st);
+    else launch_down_combine_t<TPR, V, false>(a, assign_info, st);
 }
 
 template <int TPR, int V>
@@ -897,24 +1018,30 @@ int launch_rows_t(const GroupedArgs& a, hipStream_t st) {
     const MoeWorkspace L = moe_workspace_layout(a.T, a.E, a.topk);
     const int has_shared = a.sqw != nullptr;
     if (a.op == QL_OP_DOWN_COMBINE) {
-        launch_down_combine_t<TPR, V>(a, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
+        launch_down_combine_wf<TPR, V>(a, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
     } else {
         constexpr int R = (TPR < 8) ? TPR : 8;
         const int rows = a.T * a.topk + (has_shared ? a.T : 0);
         const int2* rinfo = reinterpret_cast<const int2*>(a.ws + L.row_info);
-        if (a.op == QL_OP_GATE_UP_SILU) {
-            static_assert(R % 2 == 0, "gate/up pairing needs an even row count");
-            const int Nout = a.N / 2;
-            dim3 grid((Nout + TEAMS * (R / 2) - 1) / (TEAMS * (R / 2)), rows);
-            hipLaunchKernelGGL((moe_rows_kernel<TPR, V, R, 0>), grid, dim3(64), 0, st, a.qw, a.sc,
-                               a.bi, a.sqw, a.ssc, a.sbi, a.X, rinfo, a.Y, a.K, a.N, a.E, a.T,
-                               a.topk);
-        } else {
-            dim3 grid((a.N + TEAMS * R - 1) / (TEAMS * R), rows);
-            hipLaunchKernelGGL((moe_rows_kernel<TPR, V, R, 1>), grid, dim3(64), 0, st, a.qw, a.sc,
-                               a.bi, a.sqw, a.ssc, a.sbi, a.X, rinfo, a.Y, a.K, a.N, a.E, a.T,
-                               a.topk);
-        }
+        auto go = [&](auto mode, auto wf) {
+            constexpr int MODE = decltype(mode)::value, WF = decltype(wf)::value;
+            const int outs = (MODE == 0) ? a.N / 2 : a.N;
+            const int per = (MODE == 0) ? TEAMS * (R / 2) : TEAMS * R;
+            dim3 grid((outs + per - 1) / per, rows);
+            hipLaunchKernelGGL((moe_rows_kernel<TPR, V, R, MODE, WF>), grid, dim3(64), 0, st, a.qw, a.sc,
+                               a.bi, a.sqw, a.ssc, a.sbi, a.gscales, a.sgscale, a.X, rinfo, a.Y, a.K, a.N,
+                               a.E, a.T, a.topk);
+        };
+        static_assert(R % 2 == 0, "gate/up pairing needs an even row count");
+        using M0 = std::integral_constant<int, 0>;
+        using M1 = std::integral_constant<int, 1>;
+        using W0 = std::integral_constant<int, 0>;
+        using W1 = std::integral_constant<int, 1>;
+        using W2 = std::integral_constant<int, 2>;
+        const bool gu = a.op == QL_OP_GATE_UP_SILU;
+        if (a.wf == 1) gu ? go(M0{}, W1{}) : go(M1{}, W1{});
+        else if (a.wf == 2) gu ? go(M0{}, W2{}) : go(M1{}, W2{});
+        else gu ? go(M0{}, W0{}) : go(M1{}, W0{});
     }
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
@@ -1099,7 +1226,7 @@ bool moe_rows_supported(int K) {
 
 namespace {
 
-template <int TPR, int V, int EPL, bool BF16>
+template <int TPR, int V, int EPL, bool BF16, int WF = 0>
 void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
     constexpr int R = (TPR < 8) ? TPR : 8;
@@ -1108,9 +1235,9 @@ void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStre
     const int has_shared = a.sgu_qw != nullptr;
     const int rows = a.T * a.topk + (has_shared ? a.T : 0);
     dim3 grid((a.I + COLS - 1) / COLS, rows);
-    hipLaunchKernelGGL((moe_decode_gate_up_kernel<TPR, V, R, EPL, BF16>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((moe_decode_gate_up_kernel<TPR, V, R, EPL, BF16, WF>), grid, dim3(256), 0, st,
                        reinterpret_cast<const float*>(a.ws + L.partials), a.bias, a.gu_qw, a.gu_sc,
-                       a.gu_bi, a.sgu_qw, a.sgu_sc, a.sgu_bi, a.H,
+                       a.gu_bi, a.sgu_qw, a.sgu_sc, a.sgu_bi, a.gu_gscales, a.sgu_gscale, a.H,
                        reinterpret_cast<uint16_t*>(a.ws + L.act), a.D, 2 * a.I, a.E, a.T, a.topk, a.ids,
                        a.gates, reinterpret_cast<float*>(a.ws + L.logits),
                        reinterpret_cast<int2*>(a.ws + L.assign_info));
@@ -1118,7 +1245,13 @@ void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStre
 
 template <int TPR, int V>
 void launch_decode_gate_up_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
-    if (a.bf16) {
+    if (a.wf == 1) {
+        if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4, false, 1>(a, L, st);
+        else launch_decode_gate_up_t<TPR, V, 16, false, 1>(a, L, st);
+    } else if (a.wf == 2) {
+        if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4, false, 2>(a, L, st);
+        else launch_decode_gate_up_t<TPR, V, 16, false, 2>(a, L, st);
+    } else if (a.bf16) {
         if (a.E <= 256) launch_decode_gate_up_t<TPR, V, 4, true>(a, L, st);
         else launch_decode_gate_up_t<TPR, V, 16, true>(a, L, st);
     } else {
@@ -1132,9 +1265,11 @@ void launch_decode_down_v(const DecodeArgs& a, const DecodeLayout& L, hipStream_
     GroupedArgs g{a.dn_qw, a.dn_sc, a.dn_bi, a.sdn_qw, a.sdn_sc, a.sdn_bi,
                   reinterpret_cast<const uint16_t*>(a.ws + L.act), nullptr, nullptr, a.gates,
                   nullptr, a.ws, a.out, a.I, a.D, a.E, a.T, a.topk, QL_OP_DOWN_COMBINE};
-    const int2* info = reinterpret_cast<const int2*>(a.ws + L.assign_info);
-    if (a.bf16) launch_down_combine_t<TPR, V, true>(g, info, st);
-    else launch_down_combine_t<TPR, V, false>(g, info, st);
+    g.bf16 = a.bf16;
+    g.wf = a.wf;
+    g.gscales = a.dn_gscales;
+    g.sgscale = a.sdn_gscale;
+    launch_down_combine_wf<TPR, V>(g, reinterpret_cast<const int2*>(a.ws + L.assign_info), st);
 }
 
 }  // namespace

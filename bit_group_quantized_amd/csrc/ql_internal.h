@@ -208,6 +208,12 @@ struct DecodeArgs {
     unsigned char* ws;
     uint16_t* out;
     bool bf16 = false;  // H, Wr, scales, biases, act and out hold bf16 patterns
+    int wf = 0;         // expert weight format: 0 w4, 1 FP8 (codes as bytes, fp16 scales, no biases),
+                        // 2 NVFP4 (codes, E4M3 block-scale bytes through the scale pointers)
+    const float* gu_gscales = nullptr;  // NVFP4: per-expert global scales (device, [E])
+    const float* dn_gscales = nullptr;
+    float sgu_gscale = 0.f;             // NVFP4: the shared expert's global scales
+    float sdn_gscale = 0.f;
 };
 int launch_moe_decode(const DecodeArgs& a, hipStream_t st);
 // This device's copy of the library's decode scratch array

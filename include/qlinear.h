@@ -527,16 +527,21 @@ int moe_combine_bf16(const uint16_t* Ydown, const float* topk_gates, const int32
  * Same rows, workspace, tile map and fp16 X / Y as moe_grouped_gemm; each
  * staged weight is fp16(e4m3(code) * scale), one rounding (as in
  * qlinear_gemm_fp8, with its fp16 range), fp32 accumulation on the MFMA tiles, act = SiLU(gate) * up rounded
- * to fp16.  Serves QL_OP_GATE_UP_SILU and QL_OP_DOWN for every T on the
- * tiled path (the gates are applied by moe_combine); QL_OP_DOWN_COMBINE
- * returns UNSUPPORTED_SHAPE.  `shared` (may be NULL) has the shape of one
- * expert.  Limits: K a positive multiple of 64, K <= QL_MAX_K.
+ * to fp16.  Ops, rows, QL_OP_SHARED_ONLY and the arguments as
+ * moe_grouped_gemm.  For T <= QL_DECODE_MAX_T and K a power of two in
+ * 64 .. 16384 the rows run on the row-parallel decode kernels, which dot
+ * exact fp16 code values with the activations in fp32 (v_dot2) and apply
+ * each scale to its group's fp32 partial sum, as qlinear_gemv_fp8 does;
+ * QL_OP_DOWN_COMBINE (the gate-weighted sum of moe_grouped_gemm) needs that
+ * path.  `shared` (may be NULL) has the shape of one expert.  Limits: K a
+ * positive multiple of 64, K <= QL_MAX_K.
  * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, MISALIGNED (codes and X 16-byte,
  * scales and Y 2-byte aligned), WORKSPACE, HIP.
  */
 int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared,
                          const uint16_t* X, int32_t T, int32_t topk, int32_t op,
                          const int32_t* offsets, const int32_t* sorted_assign,
+                         const float* topk_gates, const int32_t* assign_pos,
                          const void* workspace, size_t ws_bytes,
                          uint16_t* Y, void* stream);
 
@@ -547,17 +552,19 @@ int moe_grouped_gemm_fp8(const ql_fp8_experts* W, const ql_fp8* shared,
  * the FP8 call).  Same rows, workspace, tile map, fp16 X / Y and ops as
  * moe_grouped_gemm_fp8; each staged weight is fp16(e2m1 * (e4m3(block
  * scale) * global scale)), formed in fp32 and rounded once, as in
- * qlinear_gemm_nvfp4.  `shared` (may be NULL;
- * host global_scale, finite) has the shape of one expert.
+ * qlinear_gemm_nvfp4; on the row-parallel decode path (as for the FP8
+ * call) the block scales multiply fp32 partial sums of 16 codes and the
+ * global scale the row's total, as in qlinear_gemv_nvfp4.  `shared` (may be
+ * NULL; host global_scale, finite) has the shape of one expert.
  * Limits: K a positive multiple of 64, K <= QL_MAX_K.
  * Errors: INVALID_ARG (incl. a non-finite shared global scale),
- * UNSUPPORTED_SHAPE (incl. QL_OP_DOWN_COMBINE), MISALIGNED (qweight and X
- * 16-byte, block_scales and global_scales 4-byte, Y 2-byte aligned),
- * WORKSPACE, HIP.
+ * UNSUPPORTED_SHAPE, MISALIGNED (qweight and X 16-byte, block_scales and
+ * global_scales 4-byte, Y 2-byte aligned), WORKSPACE, HIP.
  */
 int moe_grouped_gemm_nvfp4(const ql_nvfp4_experts* W, const ql_nvfp4* shared,
                            const uint16_t* X, int32_t T, int32_t topk, int32_t op,
                            const int32_t* offsets, const int32_t* sorted_assign,
+                           const float* topk_gates, const int32_t* assign_pos,
                            const void* workspace, size_t ws_bytes,
                            uint16_t* Y, void* stream);
 
@@ -609,6 +616,33 @@ int moe_decode_bf16(const uint16_t* H, const uint16_t* Wr, const float* logit_bi
                     const ql_w4* shared_gate_up, const ql_w4* shared_down,
                     int32_t* topk_ids, float* topk_gates,
                     void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+
+/*
+ * moe_decode_fp8, moe_decode_nvfp4 - moe_decode with FP8-E4M3 or NVFP4
+ * experts (the ql_fp8 / ql_nvfp4 formats, stacked; "待验证｜lithos-metal补
+ * Apple推理内核", section "一分钟内合并了什么") and fp16 H, Wr, out.  The same
+ * three launches, routing and fixed summation orders as moe_decode; the
+ * rows dot exact fp16 code values with the activations in fp32 (v_dot2) and
+ * apply the FP8 group scale, or the NVFP4 block scale and then the
+ * expert's global scale, to fp32 partial sums (qlinear_gemv_fp8 /
+ * qlinear_gemv_nvfp4); act = SiLU(gate) * up rounded once to fp16.  The
+ * output is that of moe_route + moe_grouped_gemm_fp8 / _nvfp4
+ * (QL_OP_GATE_UP_SILU, then QL_OP_DOWN_COMBINE), bit for bit.  Same
+ * limits, workspace and errors as moe_decode (MISALIGNED also for the
+ * codec alignment rules of moe_grouped_gemm_fp8 / _nvfp4).
+ */
+int moe_decode_fp8(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+                   int32_t T, int32_t D, int32_t E, int32_t topk,
+                   const ql_fp8_experts* gate_up, const ql_fp8_experts* down,
+                   const ql_fp8* shared_gate_up, const ql_fp8* shared_down,
+                   int32_t* topk_ids, float* topk_gates,
+                   void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
+int moe_decode_nvfp4(const uint16_t* H, const uint16_t* Wr, const float* logit_bias,
+                     int32_t T, int32_t D, int32_t E, int32_t topk,
+                     const ql_nvfp4_experts* gate_up, const ql_nvfp4_experts* down,
+                     const ql_nvfp4* shared_gate_up, const ql_nvfp4* shared_down,
+                     int32_t* topk_ids, float* topk_gates,
+                     void* workspace, size_t ws_bytes, uint16_t* out, void* stream);
 
 /*
  * moe_decode_noalloc - moe_decode for callers that cannot allocate device

@@ -317,6 +317,44 @@ def test_moe_decode_validation(L):
     assert call(T=0) == OK
 
 
+def test_moe_decode_codec_validation(L):
+    """Host validation of moe_decode_fp8 / moe_decode_nvfp4: the decode
+    limits of moe_decode plus each format's own rules."""
+    wsb = L.moe_decode_workspace_bytes(1, 256, 8, 512)
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    f8 = L.moe_decode_fp8
+    GU8 = ql.ql_fp8_experts(A16, A16, 2048, 1024, 256)
+    DN8 = ql.ql_fp8_experts(A16, A16, 512, 2048, 256)
+    SG8, SD8 = ql.ql_fp8(A16, A16, 2048, 1024), ql.ql_fp8(A16, A16, 512, 2048)
+
+    def c8(T=1, D=2048, E=256, topk=8, gu=GU8, dn=DN8, sg=SG8, sd=SD8, H=A16, wsb=wsb):
+        return f8(H, A16, None, T, D, E, topk, r(gu), r(dn), r(sg), r(sd), A16, A16, A16, wsb, A16, None)
+
+    assert c8(T=5) == SHAPE
+    assert c8(E=128) == INVALID
+    assert c8(sd=None) == INVALID
+    assert c8(gu=ql.ql_fp8_experts(A16 + 8, A16, 2048, 1024, 256)) == MISALIGNED  # codes 16-byte aligned
+    assert c8(sg=ql.ql_fp8(A16, A16, 2048, 512)) == INVALID                       # shared shape differs
+    assert c8(H=A16 + 2) == MISALIGNED
+    assert c8(wsb=16) == WORKSPACE
+    assert c8(T=0) == OK
+    f4 = L.moe_decode_nvfp4
+    GU4 = ql.ql_nvfp4_experts(A16, A16, A16, 2048, 1024, 256)
+    DN4 = ql.ql_nvfp4_experts(A16, A16, A16, 512, 2048, 256)
+    SG4, SD4 = ql.ql_nvfp4(A16, A16, 1.0, 2048, 1024), ql.ql_nvfp4(A16, A16, 1.0, 512, 2048)
+
+    def c4(T=1, D=2048, E=256, topk=8, gu=GU4, dn=DN4, sg=SG4, sd=SD4, H=A16, wsb=wsb):
+        return f4(H, A16, None, T, D, E, topk, r(gu), r(dn), r(sg), r(sd), A16, A16, A16, wsb, A16, None)
+
+    assert c4(T=5) == SHAPE
+    assert c4(topk=33) == SHAPE
+    assert c4(gu=ql.ql_nvfp4_experts(A16, A16, None, 2048, 1024, 256)) == INVALID  # global scales needed
+    assert c4(sg=ql.ql_nvfp4(A16, A16, float("nan"), 2048, 1024)) == INVALID
+    assert c4(dn=ql.ql_nvfp4_experts(A16, A16 + 2, A16, 512, 2048, 256)) == MISALIGNED
+    assert c4(D=1024) == INVALID
+    assert c4(T=0) == OK
+
+
 def test_moe_decode_noalloc_validation(L):
     """Host validation of the no-workspace decode entry: every error is
     returned before the scratch array is looked up."""
@@ -384,12 +422,16 @@ def test_grouped_gemm_fp8_validation(L):
     def call(op=1, T=64, topk=8, K=2048, N=1024, E=256, codes=A16, s=True, sN=1024, wsb=wsb, X=A16):
         w = ql.ql_fp8_experts(codes, A16, K, N, E)
         sh = ql.ql_fp8(A16, A16, K, sN)
-        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, A16,
-                 wsb, A16, None)
+        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, gp, gp,
+                 A16, wsb, A16, None)
 
-    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, wsb, A16, None) == INVALID
+    gp = A16
+    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, A16, A16, wsb, A16, None) == INVALID
     assert call(op=7) == INVALID
-    assert call(op=3) == SHAPE                 # no DOWN_COMBINE for FP8 experts
+    assert call(op=3) == SHAPE                 # DOWN_COMBINE is a decode path (T <= 4)
+    gp = None
+    assert call(op=3, T=2) == INVALID          # ... and needs the gates and positions
+    gp = A16
     assert call(K=100) == SHAPE
     assert call(K=65536) == SHAPE
     assert call(codes=None) == INVALID
@@ -412,12 +454,12 @@ def test_grouped_gemm_nvfp4_validation(L):
              sg=1.0, wsb=wsb, X=A16):
         w = ql.ql_nvfp4_experts(qw, bs, gs, K, N, E)
         sh = ql.ql_nvfp4(A16, A16, sg, K, sN)
-        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, A16,
-                 wsb, A16, None)
+        return f(ctypes.byref(w), ctypes.byref(sh) if s else None, X, T, topk, op, A16, A16, A16, A16,
+                 A16, wsb, A16, None)
 
-    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, wsb, A16, None) == INVALID
+    assert f(None, None, A16, 64, 8, 1, A16, A16, A16, A16, A16, wsb, A16, None) == INVALID
     assert call(op=7) == INVALID
-    assert call(op=3) == SHAPE
+    assert call(op=3) == SHAPE                 # DOWN_COMBINE is a decode path (T <= 4)
     assert call(K=96) == SHAPE
     assert call(qw=None) == INVALID
     assert call(gs=None) == INVALID

@@ -72,7 +72,7 @@ def test_moe_fp8_prefill_4096(seed):
 
 
 @pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
-    (1, 2048, 512, 256, 8, 0, True),     # one token on the tiled path
+    (1, 2048, 512, 256, 8, 0, True),     # one token: the row-parallel decode path
     (3, 512, 256, 16, 4, 1, True),
     (300, 256, 128, 16, 4, 3, True),     # MFMA router, ragged tiles
     (700, 512, 256, 64, 8, 7, True),     # tall and short tiles
@@ -146,13 +146,15 @@ def test_moe_fp8_integer_experts_bit_exact():
     assert np.array_equal(host(ydown).view(np.uint16), y.astype(np.float16).view(np.uint16))
 
 
-def test_moe_fp8_down_combine_is_rejected():
+def test_moe_fp8_down_combine_needs_the_decode_path():
+    """QL_OP_DOWN_COMBINE runs on the row-parallel decode path only
+    (T <= QL_DECODE_MAX_T); more tokens are rejected."""
     w = synth.moe_weights_fp8(0, D=256, I=64, E=8)
     dw = _dev_weights(w)
-    tok = synth.moe_tokens(1, 2, D=256, E=8)
+    tok = synth.moe_tokens(1, 5, D=256, E=8)
     route = ql.moe_route(t(tok["H"]), dw["Wr"], None, 2)
     with pytest.raises(ql.QLError):
-        ql.moe_grouped_gemm_fp8(dw["down"], None, t(np.zeros((4, 64), np.float16)), 2, 2,
+        ql.moe_grouped_gemm_fp8(dw["down"], None, t(np.zeros((10, 64), np.float16)), 5, 2,
                                 ql.QL_OP_DOWN_COMBINE, route)
 
 
@@ -264,3 +266,76 @@ def test_moe_codec_tile_row_boundaries(codec, D, I):
     ref_act, ref_yd = expert_rows_reference(ids, host(route["sorted_assign"]), H, w, ffn, expert=sl)
     assert_close(host(act).astype(np.float64), ref_act.astype(np.float64), "act")
     assert_close(host(yd).astype(np.float64), ref_yd, "ydown")
+
+
+def _codec_weights(codec, seed, **kw):
+    if codec == "fp8":
+        w = synth.moe_weights_fp8(seed, **kw)
+        return w, _dev_weights(w), ql.moe_grouped_gemm_fp8, oracle.moe_layer_fp8
+    w = synth.moe_weights_nvfp4(seed, **kw)
+    return w, _dev_weights_nvfp4(w), ql.moe_grouped_gemm_nvfp4, oracle.moe_layer_nvfp4
+
+
+@pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("T,D,I,E,topk,seed,shared", [
+    (1, 2048, 512, 256, 8, 0, True),     # the decode shape
+    (4, 2048, 512, 256, 8, 1, True),
+    (2, 512, 256, 16, 4, 2, True),
+    (3, 1024, 512, 32, 13, 3, True),     # 14 rows per token: two rounds for some waves
+    (2, 2048, 512, 256, 8, 4, False),    # no shared expert
+])
+def test_moe_decode_codec(codec, T, D, I, E, topk, seed, shared):
+    """moe_decode_fp8 / moe_decode_nvfp4 against the oracle's codec layer:
+    routing exactly the oracle's (no token of these cases has two of its
+    top-(k+1) logits within 1e-4), act and out within the fp16 bar; and the
+    bits of the three-call path (moe_route, the codec grouped GEMM's gate/up
+    rows and its QL_OP_DOWN_COMBINE)."""
+    import torch
+    from tests.gpu_util import assert_close
+    from tests.test_gpu_moe import _ref_rows
+    say(f"moe_decode_{codec} T={T} D={D} I={I} E={E} topk={topk} shared={shared}")
+    w, dw, gemm, layer = _codec_weights(codec, seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 120, T, D=D, E=E, skewed=True)
+    ref = layer(tok["H"], w, tok["logit_bias"], topk, with_shared=shared)
+    assert not oracle.topk_near_ties(ref["logits"], topk, 1e-4).any(), "case not screened"
+    H, bias = t(tok["H"]), t(tok["logit_bias"])
+    sg = dw["shared_gate_up"] if shared else None
+    sd = dw["shared_down"] if shared else None
+    res = ql.moe_decode_codec(codec, H, dw["Wr"], bias, topk, dw["gate_up"], dw["down"], sg, sd)
+    route = ql.moe_route(H, dw["Wr"], bias, topk)
+    act = gemm(dw["gate_up"], sg, H, T, topk, ql.QL_OP_GATE_UP_SILU, route)
+    out3 = gemm(dw["down"], sd, act, T, topk, ql.QL_OP_DOWN_COMBINE, route)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(res["ids"]), ref["ids"])
+    assert np.abs(host(res["gates"]).astype(np.float64) - ref["gates"]).max() < 2e-5
+    _check_routing(route, ref)
+    rows = _ref_rows(route, ref, T, topk)
+    assert_close(host(act).astype(np.float64), ref["act"][rows].astype(np.float64), "act")
+    rel, mx = assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+    say(f"  rel-L2 {rel:.2e} max-abs/max|ref| {mx:.2e}")
+    assert np.array_equal(host(res["out"]).view(np.uint16), host(out3).view(np.uint16))
+
+
+@pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
+def test_moe_decode_codec_reads_only_selected_experts(codec):
+    """NaN in every expert the token did not choose (FP8: every code 0x7F;
+    NVFP4: every block scale 0x7F) leaves the decode output finite and equal
+    to the oracle's on the clean weights."""
+    import torch
+    from tests.gpu_util import assert_close
+    w, _, _, layer = _codec_weights(codec, 8)
+    tok = synth.moe_tokens(1008, 1)
+    ref = layer(tok["H"], w, None, 8)
+    chosen = set(ref["ids"][0].tolist())
+    for key in ("gate_up", "down"):
+        for e in range(256):
+            if e not in chosen:
+                if codec == "fp8":
+                    w[key]["codes"][e] = 0x7F
+                else:
+                    w[key]["block_scales"][e] = 0x7F
+    dw = _dev_weights(w) if codec == "fp8" else _dev_weights_nvfp4(w)
+    res = ql.moe_decode_codec(codec, t(tok["H"]), dw["Wr"], None, 8, dw["gate_up"], dw["down"],
+                              dw["shared_gate_up"], dw["shared_down"])
+    torch.cuda.synchronize()
+    assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")

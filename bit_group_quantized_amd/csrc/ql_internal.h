@@ -112,6 +112,7 @@ struct MoeWorkspace {
     size_t partials;      // float[T][nparts][E]   router partial sums
     size_t chunk_counts;  // int32[nchunks][E]
     size_t chunk_err;     // int32[nchunks]
+    size_t chunk_masks;   // uint32[nchunks][E][8]   which tokens of each 256-token chunk chose each expert
     size_t row_info;      // int32[T*topk][2]: (expert, token) of each routed row
     size_t assign_info;   // int32[T*topk][2]: (expert, row) of each assignment
     size_t total;

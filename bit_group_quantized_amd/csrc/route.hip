@@ -173,15 +173,25 @@ __device__ int build_chunk_masks(const int* __restrict__ ids, int T, int E, int 
     int err = 0;
     if (t < T) {
         const uint32_t bit = 1u << (tl & 31);
-        for (int j = 0; j < topk; ++j) {
-            const int e = ids[(size_t)t * topk + j];
-            if (s_ids) s_ids[tl * topk + j] = e;
-            if ((unsigned)e >= (unsigned)E) {
-                err = 1;
-                continue;
+        // Eight ids are loaded before any is used (clamped, unconditional
+        // loads: a conditional one would be waited for on its own).
+        for (int j0 = 0; j0 < topk; j0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = ids[(size_t)t * topk + min(j0 + u, topk - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                if (j >= topk) break;
+                const int e = v[u];
+                if (s_ids) s_ids[tl * topk + j] = e;
+                if ((unsigned)e >= (unsigned)E) {
+                    err = 1;
+                    continue;
+                }
+                const uint32_t old = atomicOr(&mask[e * kMaskWords + (tl >> 5)], bit);
+                if (old & bit) err = 1;
             }
-            const uint32_t old = atomicOr(&mask[e * kMaskWords + (tl >> 5)], bit);
-            if (old & bit) err = 1;
         }
     }
     __syncthreads();
@@ -190,15 +200,21 @@ __device__ int build_chunk_masks(const int* __restrict__ ids, int T, int E, int 
 
 __global__ void __launch_bounds__(kChunk)
 dispatch_count_kernel(const int* __restrict__ ids, int T, int E, int topk,
-                      int* __restrict__ chunk_counts, int* __restrict__ chunk_err) {
-    extern __shared__ uint32_t mask[];
+                      int* __restrict__ chunk_counts, int* __restrict__ chunk_err,
+                      uint32_t* __restrict__ chunk_masks) {
+    extern __shared__ __align__(16) uint32_t mask[];
     const int c = blockIdx.x;
     const int err = build_chunk_masks(ids, T, E, topk, c, mask, nullptr);
+    static_assert(kMaskWords == 8, "two 16-byte stores per expert");
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int cnt = 0;
 #pragma unroll
         for (int w = 0; w < kMaskWords; ++w) cnt += __popc(mask[e * kMaskWords + w]);
         chunk_counts[(size_t)c * E + e] = cnt;
+        // the expert's masks of this chunk, for the scatter
+        u32x4* dst = reinterpret_cast<u32x4*>(chunk_masks + ((size_t)c * E + e) * kMaskWords);
+        dst[0] = *reinterpret_cast<const u32x4*>(mask + e * kMaskWords);
+        dst[1] = *reinterpret_cast<const u32x4*>(mask + e * kMaskWords + 4);
     }
     const int any = __syncthreads_or(err);
     if (threadIdx.x == 0) chunk_err[c] = any;
@@ -222,10 +238,11 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
         // Sixteen chunk counts are loaded before any is used, so the loop costs
         // one memory round trip per sixteen chunks.
         for (int c0 = 0; c0 < nchunks; c0 += 16) {
+            // clamped, unconditional loads (a conditional load would be
+            // waited for on its own)
             int v[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = (c0 + u < nchunks) ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+            for (int u = 0; u < 16; ++u) v[u] = chunk_counts[(size_t)min(c0 + u, nchunks - 1) * E + e];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 if (c0 + u < nchunks) {
@@ -279,39 +296,44 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
     }
 }
 
-__global__ void __launch_bounds__(kChunk)
-dispatch_scatter_kernel(const int* __restrict__ ids, int T, int E, int topk,
-                        const int* __restrict__ offsets, const int* __restrict__ chunk_base,
-                        int* __restrict__ sorted_assign, int* __restrict__ pos,
-                        int2* __restrict__ row_info, int2* __restrict__ assign_info) {
-    extern __shared__ uint32_t mask[];
-    int* const s_base = reinterpret_cast<int*>(mask + E * kMaskWords);  // [E]
-    int* const s_ids = s_base + E;                                      // [kChunk][topk]
-    const int c = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        s_base[e] = offsets[e] + chunk_base[(size_t)c * E + e];
-    build_chunk_masks(ids, T, E, topk, c, mask, s_ids);  // ends with a barrier
-    const int tl = threadIdx.x;
-    const int t = c * kChunk + tl;
+// The scatter with one block per 32 tokens (one mask word of a chunk) and
+// one thread per assignment: the rank of token t inside expert e is the
+// population count of the chunk's mask words of e before t's word, plus
+// that of t's word below bit t; the chunk's base inside e comes from the
+// scan (chunk_counts, rewritten in place).
+__global__ void __launch_bounds__(1024)
+dispatch_scatter_words_kernel(const int* __restrict__ ids, int T, int E, int topk,
+                              const int* __restrict__ offsets, const int* __restrict__ chunk_base,
+                              const uint32_t* __restrict__ chunk_masks, int* __restrict__ sorted_assign,
+                              int* __restrict__ pos, int2* __restrict__ row_info,
+                              int2* __restrict__ assign_info) {
+    const int c = blockIdx.x / kMaskWords, w = blockIdx.x % kMaskWords;
+    const int al = threadIdx.x;
+    if (al >= 32 * topk) return;
+    const int tl = al / topk;  // token within the word
+    const int t = c * kChunk + w * 32 + tl;
     if (t >= T) return;
-    const int w = tl >> 5;
-    const uint32_t below = (1u << (tl & 31)) - 1u;
-    for (int j = 0; j < topk; ++j) {
-        const int a = t * topk + j;
-        const int e = s_ids[tl * topk + j];
-        if ((unsigned)e >= (unsigned)E) {
-            pos[a] = -1;
-            assign_info[a] = make_int2(-1, -1);
-            continue;
-        }
-        int rank = __popc(mask[e * kMaskWords + w] & below);
-        for (int ww = 0; ww < w; ++ww) rank += __popc(mask[e * kMaskWords + ww]);
-        const int r = s_base[e] + rank;
-        sorted_assign[r] = a;
-        pos[a] = r;
-        row_info[r] = make_int2(e, t);
-        assign_info[a] = make_int2(e, r);
+    const int a = t * topk + al % topk;
+    const int e = ids[a];
+    if ((unsigned)e >= (unsigned)E) {
+        pos[a] = -1;
+        assign_info[a] = make_int2(-1, -1);
+        return;
     }
+    const u32x4* mk = reinterpret_cast<const u32x4*>(chunk_masks + ((size_t)c * E + e) * kMaskWords);
+    const u32x4 m0 = mk[0], m1 = mk[1];
+    const uint32_t words[kMaskWords] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    int rank = 0;
+#pragma unroll
+    for (int ww = 0; ww < kMaskWords; ++ww) {
+        if (ww < w) rank += __popc(words[ww]);
+        else if (ww == w) rank += __popc(words[ww] & ((1u << tl) - 1u));
+    }
+    const int r = offsets[e] + chunk_base[(size_t)c * E + e] + rank;
+    sorted_assign[r] = a;
+    pos[a] = r;
+    row_info[r] = make_int2(e, t);
+    assign_info[a] = make_int2(e, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,19 +543,15 @@ int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t
     int* cerr = reinterpret_cast<int*>(a.ws + L.chunk_err);
     int* hdr = reinterpret_cast<int*>(a.ws + L.header);
     int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
-    const size_t smem = (size_t)a.E * kMaskWords * sizeof(uint32_t);
-    const size_t smem_scatter = smem + ((size_t)a.E + (size_t)kChunk * a.topk) * sizeof(int);
-    static std::atomic<uint32_t> lds_set{0};
-    const size_t max_smem = (size_t)QL_MAX_EXPERTS_DEV * kMaskWords * sizeof(uint32_t) +
-                            ((size_t)QL_MAX_EXPERTS_DEV + (size_t)kChunk * QL_MAX_TOPK_DEV) * sizeof(int);
-    if (const int rc = set_max_dynamic_lds((const void*)dispatch_scatter_kernel, max_smem, lds_set))
-        return rc;
+    const size_t smem = (size_t)a.E * kMaskWords * sizeof(uint32_t);  // at most 32 KB
+    uint32_t* masks = reinterpret_cast<uint32_t*>(a.ws + L.chunk_masks);
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
-                       a.E, a.topk, cc, cerr);
+                       a.E, a.topk, cc, cerr, masks);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, cc, cerr, L.nchunks, a.E,
                        a.counts, a.offsets, hdr, tiles);
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(L.nchunks), dim3(kChunk), smem_scatter, st, a.ids, a.T,
-                       a.E, a.topk, a.offsets, cc, a.sorted_assign, a.pos,
+    const int threads = (32 * a.topk + 63) / 64 * 64;
+    hipLaunchKernelGGL(dispatch_scatter_words_kernel, dim3(L.nchunks * kMaskWords), dim3(threads), 0, st,
+                       a.ids, a.T, a.E, a.topk, a.offsets, cc, masks, a.sorted_assign, a.pos,
                        reinterpret_cast<int2*>(a.ws + L.row_info),
                        reinterpret_cast<int2*>(a.ws + L.assign_info));
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
@@ -567,6 +585,9 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
     off = align256(off);
     L.chunk_err = off;
     off += (size_t)L.nchunks * sizeof(int);
+    off = align256(off);
+    L.chunk_masks = off;
+    off += (size_t)L.nchunks * E * kMaskWords * sizeof(uint32_t);
     off = align256(off);
     L.row_info = off;
     off += (size_t)T * topk * 2 * sizeof(int);

@@ -61,6 +61,8 @@ def _check_dispatch(out, ids, E, T, topk):
     (1, 256, 8, 0.0, 0), (3, 256, 8, 0.0, 1), (16, 256, 8, 1.1, 2), (17, 256, 8, 1.1, 3),
     (300, 256, 8, 1.1, 4), (4096, 256, 8, 1.1, 5), (4096, 256, 8, 0.0, 6),
     (257, 8, 8, 0.0, 7), (1000, 1000, 2, 0.5, 8), (513, 64, 1, 2.0, 9), (40, 33, 32, 0.0, 10),
+    (32, 256, 8, 0.0, 11), (33, 256, 8, 1.1, 12),   # one full 32-token mask chunk, and one more token
+    (4097, 256, 8, 1.1, 13), (2000, 1000, 4, 0.5, 14), (9000, 64, 2, 1.1, 15),  # masks past one block's LDS
 ])
 def test_dispatch_bit_exact(T, E, topk, skew, seed):
     import torch
@@ -72,6 +74,29 @@ def test_dispatch_bit_exact(T, E, topk, skew, seed):
     torch.cuda.synchronize()
     check()
     _check_dispatch(out, ids, E, T, topk)
+
+
+@pytest.mark.parametrize("T,E,topk", [(300, 256, 8), (5000, 256, 8)])
+def test_dispatch_invalid_ids_set_the_error_flag(T, E, topk):
+    """Ids out of range or repeated within a token (both dispatch paths:
+    masks in one block's LDS, and the three-launch path for more tokens)
+    set the workspace error flag and write nothing outside the outputs."""
+    import torch
+    rng = np.random.default_rng(T)
+    ids = synth.synthetic_topk_ids(rng, T, E, topk, 0.0)
+    ids[7, 3] = E + 5          # out of range
+    ids[11, 2] = ids[11, 1]    # repeated within token 11
+    ids[T - 1, 0] = -1         # negative
+    out, check = guarded_route_outputs(T, E, topk)
+    ql.moe_dispatch(t(ids), E, out)
+    torch.cuda.synchronize()
+    check()
+    hdr, _ = _ws_tiles(out)
+    assert hdr[2] != 0
+    pos = host(out["pos"]).reshape(T, topk)
+    assert pos[7, 3] == -1 and pos[T - 1, 0] == -1
+    valid = (ids >= 0) & (ids < E)
+    assert np.all((pos[valid] >= 0) & (pos[valid] < T * topk))
 
 
 def test_dispatch_one_hot_load():

@@ -713,10 +713,11 @@ moe_rows_kernel(const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc
 // the j-th expert chosen by token t, rows T*topk + t the shared expert).
 // A routed block first sums the router partials of its token (the same
 // fixed order as the dispatch-side router, so the choice is identical),
-// takes the top-k in wave 0 and then reads only the j-th chosen expert's
-// weights; its activation loads are issued before the routing.  Blocks with
-// x = 0 also write the token's ids, gates, logits and the (expert, row) of
-// their assignment for the down projection.
+// takes the top-k (all four waves for E <= 256, else wave 0) and then
+// reads only the j-th chosen expert's weights; its activation loads are
+// issued before the routing.  Blocks with x = 0 also write the token's ids,
+// gates, logits and the (expert, row) of their assignment for the down
+// projection.
 template <int TPR, int V, int R, int EPL, bool BF16, int WF = 0>
 __global__ void __launch_bounds__(256)
 moe_decode_gate_up_kernel(const float* __restrict__ partials, const float* __restrict__ bias,

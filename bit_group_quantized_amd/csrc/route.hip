@@ -337,9 +337,6 @@ dispatch_scatter_words_kernel(const int* __restrict__ ids, int T, int E, int top
 }
 
 // ---------------------------------------------------------------------------
-// Small T (decode): top-k and the whole dispatch in one block.
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // Small T (decode): top-k and the whole dispatch in one block.  With at most
 // kRouterSmallT tokens one 32-bit mask per expert records which tokens chose
 // it; counts are population counts, the rank of token t inside its expert

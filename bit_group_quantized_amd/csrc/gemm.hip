@@ -65,6 +65,7 @@ struct KParams {
     // grouped routing
     const int* ws_header;
     const int* tiles;
+    const int* short_order;  // short tiles by cost (indices after the tall ones)
     const int* sorted_assign;
     int max_tiles;  // routed tile slots in the grid
     int T, topk, E;
@@ -734,7 +735,7 @@ gemm_w4_kernel(const KParams p) {
 // the K loop unrolls and every register ring index is static; the scales
 // (and biases) of the whole K sit in registers.
 // ---------------------------------------------------------------------------
-constexpr int kTinyRows = 32;
+constexpr int kTinyRows = kTinyTileRows;
 
 __host__ __device__ constexpr size_t tiny_lds_bytes(int K) { return (size_t)kTinyRows * (K + 8) * 2; }
 
@@ -931,10 +932,12 @@ __device__ __forceinline__ void tiny_tile(const KParams& p, const Job& job, f16*
 // Grouped expert GEMM over the load-matched tile map: tall tiles (256 rows,
 // 8 waves of 128 x 64) and short tiles (128 rows, 8 waves of 64 x 64), both
 // 256 columns wide, in one launch; short routed tiles of at most 32 rows
-// (K of 512, 1024 or 2048) take tiny_tile instead.  The tall class (tall routed tiles, then
-// the shared expert's tiles) comes first in the grid, then the short class;
-// each class is dealt to the XCDs in contiguous runs of (tile, column block)
-// items, so that every XCD gets an equal share of each class.
+// (K of 512, 1024 or 2048) take tiny_tile instead.  The tall class (tall
+// routed tiles, then the shared expert's tiles) comes first in the grid,
+// dealt to the XCDs in contiguous runs of (tile, column block) items; then
+// the short class, whole tiles dealt to the XCDs in turn in the order the
+// dispatch wrote (wider tiles before tiny ones), so that every XCD gets an
+// equal share of each kind and starts its cheapest items last.
 using TallTile = Tile<4, 2, 2, 4>;
 using ShortTile = Tile<2, 2, 2, 4>;
 static_assert(TallTile::NT == ShortTile::NT && TallTile::BN == ShortTile::BN, "one workgroup shape");
@@ -959,24 +962,29 @@ gemm_w4_grouped_kernel(const KParams p) {
     const int nt = p.ws_header ? min(max(p.ws_header[0], 0), p.max_tiles) : 0;
     const int nbig = p.ws_header ? min(max(p.ws_header[3], 0), nt) : 0;
     const int big_items = (nbig + p.grid_m) * NB;  // grid_m: shared-expert tiles
-    const int small_items = (nt - nbig) * NB;
-    const int per_b = (big_items + 7) >> 3, per_s = (small_items + 7) >> 3;
+    const int nshort = nt - nbig;
+    const int per_b = (big_items + 7) >> 3;
     const int lin = blockIdx.x;
     bool tall;
-    int item;
+    int tslot, nblk;
     if (lin < 8 * per_b) {
-        item = (lin & 7) * per_b + (lin >> 3);
+        const int item = (lin & 7) * per_b + (lin >> 3);
         if (item >= big_items) return;
         tall = true;
+        tslot = item / NB;
+        nblk = item % NB;
     } else {
+        // Short tiles are dealt to the XCDs in turn in the order of
+        // short_order (the costlier ones first), all column blocks of a tile
+        // on one XCD: the workgroups an XCD starts last are its cheapest.
         const int l2 = lin - 8 * per_b;
-        if ((l2 >> 3) >= per_s) return;
-        item = (l2 & 7) * per_s + (l2 >> 3);
-        if (item >= small_items) return;
+        const int idx = l2 >> 3;
+        const int pos = (l2 & 7) + 8 * (idx / NB);
+        if (pos >= nshort) return;
         tall = false;
+        tslot = nbig + min(max(p.short_order[pos], 0), nshort - 1);
+        nblk = idx % NB;
     }
-    const int tslot = (tall ? 0 : nbig) + item / NB;
-    const int nblk = item % NB;
     const int height = tall ? TallTile::BM : ShortTile::BM;
     Job job{};
     job.kbeg = 0;
@@ -1150,6 +1158,7 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     } else {
         p.ws_header = reinterpret_cast<const int*>(a.ws + L.header);
         p.tiles = reinterpret_cast<const int*>(a.ws + L.tiles);
+        p.short_order = reinterpret_cast<const int*>(a.ws + L.short_order);
         p.max_tiles = L.max_tiles;
     }
     p.sorted_assign = a.sorted_assign;
@@ -1164,8 +1173,9 @@ int launch_moe_grouped(const GroupedArgs& a, hipStream_t st) {
     p.grid_m = a.sqw ? (a.T + TallTile::BM - 1) / TallTile::BM : 0;  // shared-expert tiles
     // Upper bounds of both classes; workgroups past the actual items exit.
     const int64_t max_tall = (a.shared_only ? 0 : ((int64_t)a.T * a.topk) / TallTile::BM) + p.grid_m;
-    const int64_t items_b = max_tall * p.grid_n, items_s = (int64_t)p.max_tiles * p.grid_n;
-    const int64_t blocks = (items_b + 7) / 8 * 8 + (items_s + 7) / 8 * 8;
+    // Short class: up to ceil(max_tiles / 8) tiles of grid_n items per XCD.
+    const int64_t items_b = max_tall * p.grid_n, items_s = ((int64_t)p.max_tiles + 7) / 8 * 8 * p.grid_n;
+    const int64_t blocks = (items_b + 7) / 8 * 8 + items_s;
     if (blocks > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
     if (blocks == 0) return QL_OK;
     const dim3 grid((unsigned)blocks);

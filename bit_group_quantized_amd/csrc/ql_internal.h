@@ -115,11 +115,13 @@ struct MoeWorkspace {
     size_t chunk_masks;   // uint32[nchunks][E][8]   which tokens of each 256-token chunk chose each expert
     size_t row_info;      // int32[T*topk][2]: (expert, token) of each routed row
     size_t assign_info;   // int32[T*topk][2]: (expert, row) of each assignment
+    size_t short_order;   // int32[max_tiles]: the short tiles by cost (see dispatch_scan_kernel)
     size_t total;
     int max_tiles, nchunks, nparts;
 };
 
 constexpr int kRouteChunkTokens = 256;  // tokens per dispatch chunk
+constexpr int kTinyTileRows = 32;       // short tiles of at most this many rows take the register-streamed tile
 constexpr int kRouterPartRows = 64;     // D rows per small-T router partial
 constexpr int kRouterSmallT = 16;       // T at or below: row-parallel router
 constexpr int kRouterMfmaSplit = 4;     // K splits of the MFMA router (partials per logit)

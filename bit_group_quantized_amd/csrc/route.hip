@@ -224,14 +224,16 @@ dispatch_count_kernel(const int* __restrict__ ids, int T, int E, int topk,
 // and the load-matched tile map (section 使瓦片大小与专家负载相匹配): an
 // expert's rows go into tiles of 2 * QL_MOE_TILE_ROWS rows while a full one
 // remains, the rest into tiles of at most QL_MOE_TILE_ROWS rows; the tall
-// tiles are listed first.
+// tiles are listed first.  short_order lists the short tiles (as indices
+// after the tall ones) by cost for the grouped GEMM's scheduling: those of
+// more than kTinyTileRows rows first, then the rest, each group in map order.
 __global__ void __launch_bounds__(1024)
 dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chunk_err,
                      int nchunks, int E, int* __restrict__ counts, int* __restrict__ offsets,
-                     int* __restrict__ ws_header, int* __restrict__ tiles) {
+                     int* __restrict__ ws_header, int* __restrict__ tiles, int* __restrict__ short_order) {
     constexpr int SR = QL_MOE_TILE_ROWS, BR = 2 * QL_MOE_TILE_ROWS;
     __shared__ int s_tmp[16];
-    __shared__ int s_tot[2];
+    __shared__ int s_tot[3];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
@@ -261,14 +263,20 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
     const int nb = cnt / BR;
     const int rem = cnt - nb * BR;
     const int ns = (rem + SR - 1) / SR;
+    // Only an expert's last short tile can have kTinyTileRows rows or fewer.
+    const int ntiny = (ns > 0 && rem - (ns - 1) * SR <= kTinyTileRows) ? 1 : 0;
     const int binc = block_inclusive_scan(nb, s_tmp);
     const int sinc = block_inclusive_scan(ns, s_tmp);
+    const int winc = block_inclusive_scan(ns - ntiny, s_tmp);
     if (threadIdx.x == blockDim.x - 1) {
         s_tot[0] = binc;
         s_tot[1] = sinc;
+        s_tot[2] = winc;
     }
     __syncthreads();
     const int nbig = s_tot[0];
+    const int nwide = s_tot[2];
+    const int tinc = (sinc - winc);  // tiny tiles of experts 0 .. e (inclusive)
     for (int j = 0; j < nb; ++j) {
         int* tp = tiles + (size_t)(binc - nb + j) * 4;
         tp[0] = e;
@@ -282,6 +290,8 @@ dispatch_scan_kernel(int* __restrict__ chunk_counts, const int* __restrict__ chu
         tp[1] = excl + nb * BR + j * SR;
         tp[2] = min(SR, rem - j * SR);
         tp[3] = SR;
+        const bool tiny = ntiny && j == ns - 1;
+        short_order[tiny ? nwide + tinc - 1 : winc - (ns - ntiny) + j] = sinc - ns + j;
     }
     int err = 0;
     for (int c = e; c < nchunks; c += blockDim.x) err |= chunk_err[c];
@@ -353,10 +363,11 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
                  int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
                  int* __restrict__ offsets, int* __restrict__ sorted_assign,
                  int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
-                 int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+                 int2* __restrict__ row_info, int2* __restrict__ assign_info, int* __restrict__ short_order) {
     static_assert(kRouterSmallT <= 32 && kRouterSmallT * QL_MAX_TOPK_DEV <= 4 * QL_MAX_EXPERTS_DEV,
                   "token masks are 32 bits wide");
     static_assert(QL_MOE_TILE_ROWS >= kRouterSmallT, "one tile per expert");
+    static_assert(kTinyTileRows >= kRouterSmallT, "every tile is one of the cheapest kind");
     // Every intermediate stays in LDS and every global store is issued after
     // the last barrier: a barrier waits for the block's outstanding stores.
     __shared__ int s_ids[kRouterSmallT * QL_MAX_TOPK_DEV];
@@ -448,6 +459,7 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ parti
             tp[1] = s_off[e];
             tp[2] = c;
             tp[3] = QL_MOE_TILE_ROWS;  // tile height: short tiles only here
+            short_order[s_tile[e]] = s_tile[e];  // all of them have at most kRouterSmallT rows
         }
     }
     for (int a = threadIdx.x; a < nass; a += blockDim.x) {
@@ -480,9 +492,9 @@ route_small_kernel(const float* __restrict__ partials, const float* __restrict__
                    int* __restrict__ ids, float* __restrict__ gates, int* __restrict__ counts,
                    int* __restrict__ offsets, int* __restrict__ sorted_assign,
                    int* __restrict__ pos, int* __restrict__ ws_header, int* __restrict__ tiles,
-                   int2* __restrict__ row_info, int2* __restrict__ assign_info) {
+                   int2* __restrict__ row_info, int2* __restrict__ assign_info, int* __restrict__ short_order) {
     route_small_body<EPL, DO_TOPK>(partials, bias, logits_out, T, E, topk, ids, gates, counts, offsets,
-                                   sorted_assign, pos, ws_header, tiles, row_info, assign_info);
+                                   sorted_assign, pos, ws_header, tiles, row_info, assign_info, short_order);
 }
 
 
@@ -494,14 +506,15 @@ int launch_small(const RouteArgs& a, const MoeWorkspace& L, bool do_topk, hipStr
     int* tiles = reinterpret_cast<int*>(a.ws + L.tiles);
     int2* rinfo = reinterpret_cast<int2*>(a.ws + L.row_info);
     int2* ainfo = reinterpret_cast<int2*>(a.ws + L.assign_info);
+    int* sorder = reinterpret_cast<int*>(a.ws + L.short_order);
     if (do_topk)
         hipLaunchKernelGGL((route_small_kernel<EPL, true>), dim3(1), dim3(256), 0, st, partials,
                            a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
-                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
+                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo, sorder);
     else
         hipLaunchKernelGGL((route_small_kernel<EPL, false>), dim3(1), dim3(256), 0, st, partials,
                            a.bias, logits, a.T, a.E, a.topk, a.ids, a.gates, a.counts,
-                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo);
+                           a.offsets, a.sorted_assign, a.pos, hdr, tiles, rinfo, ainfo, sorder);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -545,7 +558,7 @@ int launch_dispatch_large(const RouteArgs& a, const MoeWorkspace& L, hipStream_t
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.nchunks), dim3(kChunk), smem, st, a.ids, a.T,
                        a.E, a.topk, cc, cerr, masks);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, cc, cerr, L.nchunks, a.E,
-                       a.counts, a.offsets, hdr, tiles);
+                       a.counts, a.offsets, hdr, tiles, reinterpret_cast<int*>(a.ws + L.short_order));
     const int threads = (32 * a.topk + 63) / 64 * 64;
     hipLaunchKernelGGL(dispatch_scatter_words_kernel, dim3(L.nchunks * kMaskWords), dim3(threads), 0, st,
                        a.ids, a.T, a.E, a.topk, a.offsets, cc, masks, a.sorted_assign, a.pos,
@@ -591,6 +604,9 @@ MoeWorkspace moe_workspace_layout(int T, int E, int topk) {
     off = align256(off);
     L.assign_info = off;
     off += (size_t)T * topk * 2 * sizeof(int);
+    off = align256(off);
+    L.short_order = off;
+    off += (size_t)L.max_tiles * sizeof(int);
     L.total = align256(off);
     return L;
 }

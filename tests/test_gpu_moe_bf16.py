@@ -158,3 +158,35 @@ def test_moe_bf16_tile_row_boundaries(D, I):
     bar = dict(rel_l2=REL_L2_BF16_MOE, max_abs_frac=MAX_ABS_FRAC_BF16_MOE)
     assert_close_bf16(_bits(act), oracle.bf16_to_f64(ref_act), "act", **bar)
     assert_close_bf16(_bits(yd), ref_yd, "ydown", **bar)
+
+
+@pytest.mark.parametrize("T", [600, 4096])
+def test_moe_bf16_shared_expert_split(T):
+    """The bf16 routed rows (shared = None) and the shared expert's rows
+    (QL_OP_SHARED_ONLY) as two launches into one buffer, the shared ones on
+    a second stream: act and ydown equal the single launch's bit for bit."""
+    import torch
+    topk = 8
+    say(f"bf16 shared-expert split T={T}")
+    w = synth.moe_weights_bf16(0)
+    dw = _dev_weights(w)
+    tk = synth.moe_tokens_bf16(4, T, skewed=True)
+    H, b = t(tk["H"]), t(tk["logit_bias"])
+    route, act, yd, _ = _run(dw, H, b, topk, T, shared=True)
+    torch.cuda.synchronize()
+    act2 = torch.zeros_like(act)
+    yd2 = torch.zeros_like(yd)
+    side = torch.cuda.Stream()
+    fork = torch.cuda.Event()
+    fork.record(torch.cuda.current_stream())
+    side.wait_event(fork)
+    with torch.cuda.stream(side):
+        ql.moe_grouped_gemm_bf16(dw["gate_up"], dw["shared_gate_up"], H, T, topk,
+                                 ql.QL_OP_GATE_UP_SILU | ql.QL_OP_SHARED_ONLY, None, act2, stream=side)
+        ql.moe_grouped_gemm_bf16(dw["down"], dw["shared_down"], act, T, topk,
+                                 ql.QL_OP_DOWN | ql.QL_OP_SHARED_ONLY, None, yd2, stream=side)
+    ql.moe_grouped_gemm_bf16(dw["gate_up"], None, H, T, topk, ql.QL_OP_GATE_UP_SILU, route, act2)
+    ql.moe_grouped_gemm_bf16(dw["down"], None, act, T, topk, ql.QL_OP_DOWN, route, yd2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(act2), _bits(act))
+    assert np.array_equal(_bits(yd2), _bits(yd))

@@ -339,3 +339,38 @@ def test_moe_decode_codec_reads_only_selected_experts(codec):
                               dw["shared_gate_up"], dw["shared_down"])
     torch.cuda.synchronize()
     assert_close(host(res["out"]).astype(np.float64), ref["out"], "out")
+
+
+@pytest.mark.parametrize("codec", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [600, 4096])
+def test_moe_codec_shared_expert_split(codec, T):
+    """The routed rows (shared = None) and the shared expert's rows
+    (QL_OP_SHARED_ONLY, no routing inputs) as two launches into one buffer,
+    the shared ones on a second stream: act and ydown equal the single
+    launch's bit for bit."""
+    import torch
+    topk = 8
+    say(f"{codec} shared-expert split T={T}")
+    w = synth.moe_weights_fp8(0) if codec == "fp8" else synth.moe_weights_nvfp4(0)
+    dw = _dev_weights(w) if codec == "fp8" else _dev_weights_nvfp4(w)
+    gemm = ql.moe_grouped_gemm_fp8 if codec == "fp8" else ql.moe_grouped_gemm_nvfp4
+    tk = synth.moe_tokens(SCREENED[0], T, skewed=True)
+    H, b = t(tk["H"]), t(tk["logit_bias"])
+    route, act, yd, _ = _run(dw, H, b, topk, T, shared=True, gemm=gemm)
+    torch.cuda.synchronize()
+    act2 = torch.full_like(act, float("nan"))
+    yd2 = torch.full_like(yd, float("nan"))
+    side = torch.cuda.Stream()
+    fork = torch.cuda.Event()
+    fork.record(torch.cuda.current_stream())
+    side.wait_event(fork)
+    with torch.cuda.stream(side):
+        gemm(dw["gate_up"], dw["shared_gate_up"], H, T, topk, ql.QL_OP_GATE_UP_SILU | ql.QL_OP_SHARED_ONLY,
+             None, act2, stream=side)
+        gemm(dw["down"], dw["shared_down"], act, T, topk, ql.QL_OP_DOWN | ql.QL_OP_SHARED_ONLY, None, yd2,
+             stream=side)
+    gemm(dw["gate_up"], None, H, T, topk, ql.QL_OP_GATE_UP_SILU, route, act2)
+    gemm(dw["down"], None, act, T, topk, ql.QL_OP_DOWN, route, yd2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(act2).view(np.uint16), host(act).view(np.uint16))
+    assert np.array_equal(host(yd2).view(np.uint16), host(yd).view(np.uint16))

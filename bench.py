@@ -347,6 +347,17 @@ def bench_gemm(args, dev):
         flops = 2.0 * M * N * K
         tf = flops / (ms * 1e-3) / 1e12
         out[f"M={M}"] = {"us": float(ms * 1e3), "TFLOP/s": tf, "frac_mfma_f16": tf / MFMA_F16_PEAK_TFLOPS}
+        if M <= 1024:
+            # The K-split entry point (K in two halves per workgroup; its own
+            # rounding), for the caller who trades qlinear_gemm's bits for speed.
+            def step_ks(i):
+                ql.qlinear_gemm_ksplit(W, Xs[i % len(Xs)], Y)
+
+            ms_ks = timed_steps(step_ks, steps, 3, settle_s=SETTLE_S / 2)
+            tf_ks = flops / (ms_ks * 1e-3) / 1e12
+            out[f"M={M}"]["ksplit"] = {"us": float(ms_ks * 1e3), "TFLOP/s": tf_ks,
+                                      "frac_mfma_f16": tf_ks / MFMA_F16_PEAK_TFLOPS,
+                                      "entry": "qlinear_gemm_ksplit"}
         del Xs, Y, X, W
         torch.cuda.empty_cache()
     return out

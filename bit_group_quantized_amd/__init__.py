@@ -78,6 +78,7 @@ _SIGS = {
     "qlinear_gemv": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, _P, _P]),
     "qlinear_gemm": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemm_few_rows": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
+    "qlinear_gemm_ksplit": (ctypes.c_int, [ctypes.POINTER(ql_w4), _P, ctypes.c_int64, _P, _P]),
     "qlinear_gemv_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8), _P, _P, _P]),
     "qlinear_gemv_nvfp4": (ctypes.c_int, [ctypes.POINTER(ql_nvfp4), _P, _P, _P]),
     "qlinear_gemm_fp8": (ctypes.c_int, [ctypes.POINTER(ql_fp8), _P, ctypes.c_int64, _P, _P]),
@@ -336,6 +337,19 @@ def qlinear_gemm_few_rows(W: dict, X, Y=None, stream=None):
     w = make_w4(W)
     _check("qlinear_gemm_few_rows",
            lib().qlinear_gemm_few_rows(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
+    return Y
+
+
+def qlinear_gemm_ksplit(W: dict, X, Y=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 . dequant(W), each workgroup's K in two
+    halves side by side (a few hundred rows; K a multiple of 128)."""
+    import torch
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, int(W["N"])), dtype=torch.float16, device=X.device)
+    w = make_w4(W)
+    _check("qlinear_gemm_ksplit",
+           lib().qlinear_gemm_ksplit(ctypes.byref(w), _ptr(X), M, _ptr(Y), _stream(stream)))
     return Y
 
 

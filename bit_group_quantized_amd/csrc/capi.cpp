@@ -121,6 +121,19 @@ int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t
     return ql::launch_gemm_ws(a, as_stream(stream));
 }
 
+int qlinear_gemm_ksplit(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
+    if (!W || M < 0) return QL_ERR_INVALID_ARG;
+    int rc = check_w4(W->qweight, W->scales, W->biases, W->K, W->N, W->group_size);
+    if (rc != QL_OK) return rc;
+    if (!ql::gemm_ksplit_supported(W->K)) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (W->N == 0 || M == 0) return QL_OK;
+    if (M > (int64_t)0x7fffffff / 2) return QL_ERR_UNSUPPORTED_SHAPE;
+    if (!X || !Y) return QL_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 2)) return QL_ERR_MISALIGNED;
+    ql::GemmArgs a{W->qweight, W->scales, W->biases, X, Y, M, W->K, W->N};
+    return ql::launch_gemm_ksplit(a, as_stream(stream));
+}
+
 int qlinear_gemv_rmsnorm(const ql_w4* W, const uint16_t* x, const uint16_t* gamma, float eps,
                          uint16_t* y, void* stream) {
     if (!W) return QL_ERR_INVALID_ARG;

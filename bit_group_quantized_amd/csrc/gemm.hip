@@ -139,14 +139,24 @@ struct Job {
 // (bytes, through p.sc) and the matrix's global scale job.gscale, staged as
 // fp16(e2m1 * (e4m3 * global)) with the block scale and the product in fp32
 // and one rounding to fp16.
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
-__device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds) {
+// KG: K groups.  With KG = 2 the workgroup holds two copies of the tile's
+// waves; group g stages and multiplies K steps [kbeg + g*h, kbeg + (g+1)*h)
+// (h = half the steps, their count must be even) in LDS of its own, so the
+// two halves' latency chains run side by side on every SIMD, and group 1
+// hands its fp32 sums to group 0 through LDS: each output is (sum over the
+// first half) + (sum over the second half), rounded once.
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0, int KG = 1>
+__device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16* lds_all) {
     using TL = Tile<WM, WN, WGM, WGN>;
     constexpr int BM = TL::BM, BN = TL::BN;
+    static_assert(KG == 1 || (KG == 2 && MODE == MODE_DENSE), "K groups: dense GEMM only");
+    // Group of this wave (uniform) and the thread's index inside its group.
+    const int grp = (KG == 2) ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / TL::NT) : 0;
+    f16* const lds = lds_all + (size_t)grp * (TL::LDS_BYTES / 2);
     f16* As = lds;                     // [2][BM][kLdk]
     f16* Bs = lds + 2 * TL::LDS_A;     // [2][BN][kLdk]
 
-    const int tid = threadIdx.x;
+    const int tid = (int)threadIdx.x - grp * TL::NT;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wave_n = wave % WGN;
@@ -158,7 +168,8 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     const int rows_valid = job.rows_valid;
     const int out_row0 = job.out_row0;
     const int n0 = job.n0;
-    const int kbeg = job.kbeg, kend = job.kend;
+    const int khalf = (job.kend - job.kbeg) / KG;
+    const int kbeg = job.kbeg + grp * khalf, kend = (KG == 2) ? kbeg + khalf : job.kend;
     const int tile_kind = job.tile_kind;
     const int tile_first = job.tile_first;
     const uint32_t* const wq = job.wq;
@@ -460,6 +471,33 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
     } else {
         main_loop(std::integral_constant<int, WM>{});
     }
+    // Only group 0 writes outputs; group 1 still passes every barrier below.
+    const bool writer = (grp == 0);
+    if constexpr (KG == 2) {
+        // Group 1's sums to group 0 through LDS (the staging buffers are
+        // free once both groups pass the barrier): [i][j][r][thread].
+        __syncthreads();
+        float* const xch = reinterpret_cast<float*>(lds_all);
+        static_assert((size_t)TL::NT * WM * WN * 16 * 4 <= (size_t)TL::LDS_BYTES, "exchange fits");
+        if (!writer) {
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+#pragma unroll
+                for (int j = 0; j < WN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) xch[((i * WN + j) * 16 + r) * TL::NT + tid] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (writer) {
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+#pragma unroll
+                for (int j = 0; j < WN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] = acc[i][j][r] + xch[((i * WN + j) * 16 + r) * TL::NT + tid];
+        }
+    }
 
     // ---- epilogue -------------------------------------------------------------
     auto to16 = [](float v) -> uint16_t {
@@ -525,29 +563,33 @@ __device__ __forceinline__ void gemm_tile(const KParams& p, const Job& job, f16*
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
             f16* const reg = region0 + (i & 1) * 32 * LDR;
+            if (writer) {
 #pragma unroll
-            for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
+                for (int j = 0; j < ((MODE == MODE_GATEUP) ? WN / 2 : WN); ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint16_t h[4];
-                    out16(i, j, g, h);
-                    const uint32_t lo = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-                    const uint32_t hi = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-                    *reinterpret_cast<uint2*>(reg + fl * LDR + 32 * j + 8 * g + 4 * fh) = make_uint2(lo, hi);
-                }
+                    for (int g = 0; g < 4; ++g) {
+                        uint16_t h[4];
+                        out16(i, j, g, h);
+                        const uint32_t lo = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                        const uint32_t hi = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                        *reinterpret_cast<uint2*>(reg + fl * LDR + 32 * j + 8 * g + 4 * fh) = make_uint2(lo, hi);
+                    }
+            }
             __syncthreads();
+            if (writer) {
 #pragma unroll
-            for (int q = 0; q < 32 * CPR / 64; ++q) {
-                const int c = q * 64 + lane;
-                const int row = c / CPR, ch = c % CPR;
-                const int lrow = wm0 + 32 * i + row;
-                const int col = wcol0 + ch * 8;
-                const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * LDR + ch * 8);
-                if (lrow < rows_valid && col < out_cols)
-                    *reinterpret_cast<u32x4*>(p.Y + ((int64_t)out_row0 + lrow) * out_cols + col) = d;
+                for (int q = 0; q < 32 * CPR / 64; ++q) {
+                    const int c = q * 64 + lane;
+                    const int row = c / CPR, ch = c % CPR;
+                    const int lrow = wm0 + 32 * i + row;
+                    const int col = wcol0 + ch * 8;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(reg + row * LDR + ch * 8);
+                    if (lrow < rows_valid && col < out_cols)
+                        *reinterpret_cast<u32x4*>(p.Y + ((int64_t)out_row0 + lrow) * out_cols + col) = d;
+                }
             }
         }
-    } else {
+    } else if (writer) {
         // Unaligned output: element stores.
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
@@ -679,9 +721,9 @@ gemm_ws_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     if (c < nchunks) chunk(c, xa, xb);
 }
 
-// Dense prefill GEMM and the router GEMM.
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT, int WF = 0>
-__global__ void __launch_bounds__(64 * WGM * WGN)
+// Dense prefill GEMM and the router GEMM (KG: K groups, see gemm_tile).
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT, int WF = 0, int KG = 1>
+__global__ void __launch_bounds__(64 * WGM * WGN * KG)
 gemm_w4_kernel(const KParams p) {
     using TL = Tile<WM, WN, WGM, WGN>;
     constexpr int BM = TL::BM, BN = TL::BN;
@@ -716,7 +758,7 @@ gemm_w4_kernel(const KParams p) {
         job.kz = blockIdx.z;
     }
     job.rows_valid = (int)min<int64_t>(BM, p.M - job.out_row0);
-    gemm_tile<WM, WN, WGM, WGN, MODE, DT, WF>(p, job, lds);
+    gemm_tile<WM, WN, WGM, WGN, MODE, DT, WF, KG>(p, job, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,15 +1067,15 @@ gemm_w4_grouped_kernel(const KParams p) {
         gemm_tile<2, 2, 2, 4, MODE, DT, WF>(p, job, lds);
 }
 
-template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0>
+template <int WM, int WN, int WGM, int WGN, int MODE, int DT = 0, int WF = 0, int KG = 1>
 int launch_t(const KParams& p, dim3 grid, hipStream_t st) {
     using TL = Tile<WM, WN, WGM, WGN>;
     static std::atomic<uint32_t> lds_set{0};
-    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF>,
-                                           TL::LDS_BYTES, lds_set))
+    if (const int rc = set_max_dynamic_lds((const void*)gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF, KG>,
+                                           TL::LDS_BYTES * KG, lds_set))
         return rc;
-    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF>), grid, dim3(TL::NT), TL::LDS_BYTES,
-                       st, p);
+    hipLaunchKernelGGL((gemm_w4_kernel<WM, WN, WGM, WGN, MODE, DT, WF, KG>), grid, dim3(TL::NT * KG),
+                       TL::LDS_BYTES * KG, st, p);
     return hipGetLastError() == hipSuccess ? QL_OK : QL_ERR_HIP;
 }
 
@@ -1081,6 +1123,38 @@ int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
 }
 
 int launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<0>(a, st); }
+
+bool gemm_ksplit_supported(int K) { return K % (2 * kGroup) == 0 && K >= 2 * kGroup; }
+
+// Two-group tiles (gemm_tile with KG = 2): 64 x 128 while that gives at
+// most 128 of them (the smallest class of qlinear_gemm's table), 128 x 128
+// for every larger shape.  Both split K into the same two halves, so a
+// row's bits do not depend on M within this entry point either.
+int launch_gemm_ksplit(const GemmArgs& a, hipStream_t st) {
+    KParams p{};
+    p.A = a.X;
+    p.M = a.M;
+    p.qw = a.qweight;
+    p.sc = a.scales;
+    p.bi = a.biases;
+    p.Y = a.Y;
+    p.K = a.K;
+    p.N = a.N;
+    p.gscale = 1.f;
+    const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    auto go = [&](auto tl) -> int {
+        using TL = decltype(tl);
+        const int64_t gn = (a.N + TL::BN - 1) / TL::BN, gm = (a.M + TL::BM - 1) / TL::BM;
+        if (gn * gm > 0x7fffff00LL) return QL_ERR_UNSUPPORTED_SHAPE;
+        p.grid_n = (int)gn;
+        p.grid_m = (int)gm;
+        const dim3 grid((unsigned)((gn * gm + 7) / 8 * 8));
+        if constexpr (TL::BM == 64) return launch_t<1, 2, 2, 2, MODE_DENSE, 0, 0, 2>(p, grid, st);
+        else return launch_t<2, 2, 2, 2, MODE_DENSE, 0, 0, 2>(p, grid, st);
+    };
+    if (t128 <= 128) return go(Tile<1, 2, 2, 2>{});
+    return go(Tile<2, 2, 2, 2>{});
+}
 
 int launch_gemm_bf16(const GemmArgs& a, hipStream_t st) { return launch_gemm_dt<1>(a, st); }
 

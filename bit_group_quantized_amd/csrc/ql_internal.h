@@ -99,6 +99,9 @@ int launch_gemm_fp8(const GemmArgs& a, hipStream_t st);
 // NVFP4 weights: qweight the E2M1 codes [N][K/8], scales points at the E4M3
 // block scales (bytes) [N][K/16], gscale the global scale.
 int launch_gemm_nvfp4(const GemmArgs& a, hipStream_t st);
+// K split in two halves inside each workgroup (K a multiple of 128).
+bool gemm_ksplit_supported(int K);
+int launch_gemm_ksplit(const GemmArgs& a, hipStream_t st);
 bool gemm_ws_supported(int K);                          // few-row GEMM shapes
 int launch_gemm_ws(const GemmArgs& a, hipStream_t st);  // few-row GEMM (weight-stationary)
 

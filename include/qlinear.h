@@ -190,6 +190,24 @@ int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t
                           void* stream);
 
 /*
+ * qlinear_gemm_ksplit - Y = X . dequant(W) for a few hundred rows ([PPLX]
+ * dequantization section, as qlinear_gemm; "使瓦片大小与专家负载相匹配", tile
+ * choice against row count).  At such M qlinear_gemm gives each CU a single
+ * workgroup whose K steps form one dependent chain; here every workgroup
+ * holds two copies of its tile's waves that take the two halves of K side
+ * by side, and adds the halves' fp32 sums at the end.  For the caller to
+ * pick (like qlinear_gemm_few_rows): faster than qlinear_gemm for a few
+ * hundred rows, slower for thousands.
+ *   X fp16 [M][K], Y fp16 [M][N]; fp16 dequantized weights; each output is
+ *   (fp32 sum over the first K/2) + (fp32 sum over the second K/2), rounded
+ *   once to fp16: deterministic, and row m of Y is bit-identical whatever M
+ *   is, but its rounding differs from qlinear_gemm's (which does not split K).
+ * Limits: K a multiple of 128.
+ * Errors: as qlinear_gemm; UNSUPPORTED_SHAPE for other K.
+ */
+int qlinear_gemm_ksplit(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
  * qlinear_gemv_bf16, qlinear_gemm_bf16 - the same two layers with bf16
  * activations, scales, biases and outputs ([PPLX] dequantization section:
  * the page's checkpoint keeps scale and bias in bf16 and its matrix path

@@ -104,6 +104,16 @@ def test_gemm_few_rows_validation(L):
     assert f(ctypes.byref(_w(K=2048)), None, 4, A16, None) == INVALID
 
 
+def test_gemm_ksplit_validation(L):
+    f = L.qlinear_gemm_ksplit
+    assert f(ctypes.byref(_w(K=2048)), A16, -1, A16, None) == INVALID
+    assert f(ctypes.byref(_w(K=2048)), A16, 0, A16, None) == OK  # empty
+    assert f(ctypes.byref(_w(K=192)), A16, 4, A16, None) == SHAPE  # K not a multiple of 128
+    assert f(ctypes.byref(_w(K=64)), A16, 4, A16, None) == SHAPE
+    assert f(ctypes.byref(_w(K=2048)), A16 + 2, 4, A16, None) == MISALIGNED
+    assert f(ctypes.byref(_w(K=2048)), None, 4, A16, None) == INVALID
+
+
 def test_pack_validation(L):
     f = L.qlinear_pack
     assert f(A16, 4, 12, A16, None) == SHAPE

@@ -123,6 +123,61 @@ def test_gemm_few_rows_matches_oracle(M, K, N, seed):
     assert_close(host(Y.t).astype(np.float64), ref, f"gemm_few_rows M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,seed", [
+    (1, 2048, 512, 30), (7, 128, 200, 31), (63, 1024, 1000, 32), (64, 2048, 8192, 33),
+    (129, 256, 257, 34), (256, 2048, 8192, 35), (300, 4096, 700, 36), (513, 512, 384, 37),
+    (1024, 2048, 8192, 38), (1500, 1024, 4100, 39),
+])
+def test_gemm_ksplit_matches_oracle(M, K, N, seed):
+    """The K-split GEMM (two halves of K per workgroup, summed at the end):
+    full parity over ragged M and N in both of its tile classes, K from one
+    pair of groups up."""
+    import torch
+    say(f"gemm_ksplit M={M} K={K} N={N} seed={seed}")
+    case = synth.gemm_case(seed, M, K, N)
+    ref = oracle.linear(case["X"], case["W"])
+    Y = guarded((M, N), torch.float16)
+    ql.qlinear_gemm_ksplit(w4_dev(case["W"]), t(case["X"]), Y.t)
+    torch.cuda.synchronize()
+    Y.check(f"gemm_ksplit M={M} K={K} N={N}")
+    assert_close(host(Y.t).astype(np.float64), ref, f"gemm_ksplit M={M} K={K} N={N}")
+
+
+def test_gemm_ksplit_row_invariance_and_determinism():
+    """Row m of the K-split GEMM is the same bits for M = 1, 64, 256, 1024
+    (both tile classes split K the same way), and repeated calls agree."""
+    import torch
+    K, N = 2048, 8192
+    case = synth.gemm_case(40, 1024, K, N)
+    W = w4_dev(case["W"])
+    X = t(case["X"])
+    full = host(ql.qlinear_gemm_ksplit(W, X))
+    again = host(ql.qlinear_gemm_ksplit(W, X))
+    torch.cuda.synchronize()
+    assert np.array_equal(full.view(np.uint16), again.view(np.uint16))
+    for M in (1, 64, 256):
+        part = host(ql.qlinear_gemm_ksplit(W, X[:M].contiguous()))
+        torch.cuda.synchronize()
+        assert np.array_equal(part.view(np.uint16), full[:M].view(np.uint16)), M
+
+
+def test_gemm_ksplit_integer_case_bit_exact():
+    """Scale 1, bias 0 and small integer activations: every fp32 partial sum
+    is exact, so both halves and their sum are too, and the K-split GEMM
+    equals the oracle's rounded result bit for bit."""
+    import torch
+    rng = np.random.default_rng(41)
+    M, K, N = 200, 1024, 300
+    words = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    W = {"qweight": words, "scales": np.ones((N, K // 64), np.float16),
+         "biases": np.zeros((N, K // 64), np.float16), "K": K, "N": N}
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float16)
+    ref = oracle.round_f16(oracle.linear(X, W))
+    Y = host(ql.qlinear_gemm_ksplit(w4_dev(W), t(X)))
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.view(np.uint16), ref.view(np.uint16))
+
+
 def test_gemm_few_rows_row_invariance_and_determinism():
     """Row m of the few-row GEMM depends only on row m of X (the same bits
     for M = 1, 7, 96, 300), and repeated calls give identical bits."""

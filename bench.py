@@ -19,7 +19,8 @@ shared; moe_decode and the three-call path) and the prefill MoE layer (4096
 tokens, Zipf-skewed expert loads, two token sets alternating; w4, bf16, FP8
 and NVFP4 experts).  "read_probe" gives the chip's measured HBM read rate
 (the GEMV's code-load pattern and a plain streaming read, libqlprobe) beside
-the 8 TB/s specification; "cpu_baseline" times the oracle on the host cores
+the 8 TB/s specification; "workloads.lds_probe" the LDS read and write rates
+of one CU that bound the GEMM tiles' staging; "cpu_baseline" times the oracle on the host cores
 on bounded samples of every workload; "meta" records the device, software,
 clocks, seeds and hashes of the inputs and of the sources.
 
@@ -1052,7 +1053,42 @@ def probe_lib():
     L.ql_probe_chase.restype = ctypes.c_int
     L.ql_probe_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.ql_probe_lds_blocks.restype = ctypes.c_int
+    L.ql_probe_lds_blocks.argtypes = []
+    L.ql_probe_lds_bytes.restype = ctypes.c_double
+    L.ql_probe_lds_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.ql_probe_lds.restype = ctypes.c_int
+    L.ql_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return L
+
+
+LDS_PROBE_MODES = ((0, "read_b128_contiguous"), (1, "read_b128_mfma_fragment_rows"),
+                   (2, "write_b128_staging_rows"), (3, "write_b64_contiguous"))
+
+
+def lds_probe(dev):
+    """LDS throughput of one CU (libqlprobe): 8 waves of one workgroup per CU
+    issue back-to-back 16- or 8-byte LDS accesses; bytes per shader clock
+    (s_memtime in the kernel), median over the 256 workgroups of the second
+    of two launches, for reads in the contiguous and the matrix-fragment
+    pattern and for writes in the staging pattern."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks = int(L.ql_probe_lds_blocks())
+    cyc = torch.empty(blocks, dtype=torch.int64, device=dev)
+    out = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+    iters = 4096
+    res = {}
+    for mode, name in LDS_PROBE_MODES:
+        for _ in range(2):
+            if L.ql_probe_lds(mode, iters, ctypes.c_void_p(cyc.data_ptr()), ctypes.c_void_p(out.data_ptr()), st) != 0:
+                raise RuntimeError("ql_probe_lds failed")
+        torch.cuda.synchronize()
+        c = cyc.cpu().numpy().astype(np.float64)
+        res[name] = {"bytes_per_clock_per_CU": float(L.ql_probe_lds_bytes(mode, iters) / np.median(c))}
+    return res
 
 
 def latency_budget(dev):
@@ -1257,6 +1293,9 @@ def main():
         wl = res.setdefault("workloads", {})
         log("bench: small GEMV")
         wl["gemv_K512_N512"] = bench_gemv_small(args, dev)
+        if args.workload in ("all", "gemm", "gemm_prefill", "latency"):
+            log("bench: LDS probe")
+            wl["lds_probe"] = lds_probe(dev)
         if args.workload in ("all", "gemm", "gemm_prefill"):
             log("bench: GEMM")
             wl["prefill_gemm_K2048_N8192"] = bench_gemm(args, dev)

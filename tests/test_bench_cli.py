@@ -28,3 +28,17 @@ def test_traffic_only_for_the_profiled_source():
         assert 0.99 < t / 174895104 < 1.05
     assert bench.traffic_for(key, "0" * 16) is None
     assert bench.traffic_for("no_such_kernel", sha) is None
+
+
+def test_lds_probe_host_side():
+    """The LDS probe's bindings load and its host-side arithmetic and argument
+    checks hold without a device (no launch is made)."""
+    import ctypes
+    import bench
+    L = bench.probe_lib()
+    assert L.ql_probe_lds_blocks() == 256
+    assert L.ql_probe_lds_bytes(0, 4096) == 8 * 4096 * 8 * 1024
+    assert L.ql_probe_lds_bytes(3, 4096) == 8 * 4096 * 8 * 512
+    assert L.ql_probe_lds(0, 4096, None, None, None) == 1          # no buffers
+    assert L.ql_probe_lds(0, 0, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == 1  # no iterations
+    assert [m for m, _ in bench.LDS_PROBE_MODES] == [0, 1, 2, 3]

@@ -196,8 +196,9 @@ int qlinear_gemm_few_rows(const ql_w4* W, const uint16_t* X, int64_t M, uint16_t
  * workgroup whose K steps form one dependent chain; here every workgroup
  * holds two copies of its tile's waves that take the two halves of K side
  * by side, and adds the halves' fp32 sums at the end.  For the caller to
- * pick (like qlinear_gemm_few_rows): faster than qlinear_gemm for a few
- * hundred rows, slower for thousands.
+ * pick (like qlinear_gemm_few_rows): up to about 10% faster than
+ * qlinear_gemm for a few hundred rows (the gain varies with the board and
+ * can vanish), slower for a thousand rows and more.
  *   X fp16 [M][K], Y fp16 [M][N]; fp16 dequantized weights; each output is
  *   (fp32 sum over the first K/2) + (fp32 sum over the second K/2), rounded
  *   once to fp16: deterministic, and row m of Y is bit-identical whatever M

@@ -1,7 +1,9 @@
 """GPU behaviour on special values, against the oracle.
 
 A NaN activation poisons exactly the outputs that depend on it: every
-output of the GEMV, one row of the GEMM (the rows stay independent).
+output of the GEMV, one row of the GEMM (the rows stay independent), one
+token's output of the routed-expert layer (its NaN logits rank below every
+number, so its experts stay valid ids).
 Outputs beyond the fp16 range overflow to infinity exactly where rounding
 the oracle's exact result to fp16 does: with scale 512 and bias -4096 on
 every other output column (dequantized weights 512 q - 4096, exact in fp16,
@@ -107,3 +109,66 @@ def test_gemm_overflow_to_infinity(M, K, N):
     Y = ql.qlinear_gemm(w4_dev(W), t(X))
     torch.cuda.synchronize()
     check_overflow(host(Y), oracle.linear(X, W), f"gemm M={M} K={K} N={N}")
+
+
+def _moe_dev_weights(w):
+    return {"Wr": t(w["Wr"]), "gate_up": w4_dev(w["gate_up"]), "down": w4_dev(w["down"]),
+            "shared_gate_up": w4_dev(w["shared_gate_up"]), "shared_down": w4_dev(w["shared_down"])}
+
+
+def _check_nan_token(ids, out, r, E, topk, ref_out, what):
+    """The poisoned token still has topk distinct experts in range; its
+    output row is NaN; every other row matches the oracle run on the other
+    tokens alone."""
+    ids = np.asarray(ids)
+    assert ids.min() >= 0 and ids.max() < E, f"{what}: expert id out of range"
+    assert all(len(set(row)) == topk for row in ids.tolist()), f"{what}: repeated expert"
+    o = np.asarray(out, dtype=np.float64)
+    assert np.isnan(o[r]).all(), f"{what}: the NaN token's output is not NaN"
+    keep = np.delete(np.arange(o.shape[0]), r)
+    assert_close(o[keep], ref_out, f"{what}: the other tokens")
+
+
+@pytest.mark.parametrize("T,D,I,E,topk,seed", [(300, 256, 128, 16, 4, 3), (700, 512, 256, 64, 8, 4)])
+def test_moe_nan_token_poisons_only_its_output(T, D, I, E, topk, seed):
+    """Prefill path (route, grouped gate/up, down, combine): a token whose
+    hidden state holds a NaN has NaN logits, which the top-k ranks below
+    every number, so it still takes topk valid experts; its rows share tiles
+    with other tokens' rows, which stay independent."""
+    import torch
+    say(f"moe NaN token T={T} D={D} E={E} topk={topk}")
+    w = synth.moe_weights(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 50, T, D=D, E=E, skewed=True)
+    H = tok["H"].copy()
+    r = T // 3
+    H[r, D // 2] = np.float16(np.nan)
+    dw = _moe_dev_weights(w)
+    Hd = t(H)
+    route = ql.moe_route(Hd, dw["Wr"], t(tok["logit_bias"]), topk)
+    act = ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], Hd, T, topk, ql.QL_OP_GATE_UP_SILU, route)
+    ydown = ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, topk, ql.QL_OP_DOWN, route)
+    out = ql.moe_combine(ydown, route["gates"], route["pos"], T, topk, True)
+    torch.cuda.synchronize()
+    keep = np.delete(np.arange(T), r)
+    ref = oracle.moe_layer(H[keep], w, tok["logit_bias"], topk)
+    _check_nan_token(host(route["ids"]), host(out), r, E, topk, ref["out"], f"moe T={T}")
+
+
+def test_moe_decode_nan_token_poisons_only_its_output():
+    """The fused decode layer (moe_decode) on four tokens, one of them with a
+    NaN in its hidden state."""
+    import torch
+    T, D, I, E, topk, seed = 4, 2048, 512, 256, 8, 7
+    say("moe_decode NaN token")
+    w = synth.moe_weights(seed, D=D, I=I, E=E)
+    tok = synth.moe_tokens(seed + 60, T, D=D, E=E, skewed=True)
+    H = tok["H"].copy()
+    r = 2
+    H[r, 7] = np.float16(np.nan)
+    dw = _moe_dev_weights(w)
+    res = ql.moe_decode(t(H), dw["Wr"], t(tok["logit_bias"]), topk, gate_up=dw["gate_up"], down=dw["down"],
+                        shared_gate_up=dw["shared_gate_up"], shared_down=dw["shared_down"])
+    torch.cuda.synchronize()
+    keep = np.delete(np.arange(T), r)
+    ref = oracle.moe_layer(H[keep], w, tok["logit_bias"], topk)
+    _check_nan_token(host(res["ids"]), host(res["out"]), r, E, topk, ref["out"], "moe_decode")

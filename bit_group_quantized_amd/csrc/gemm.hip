@@ -1118,6 +1118,11 @@ int launch_gemm_dt(const GemmArgs& a, hipStream_t st) {
     if (t128 > 512) QL_DENSE(4, 2, 2, 4);  // 256 x 256, 8 waves of 128 x 64
     if (t128 > 256) QL_DENSE(2, 2, 2, 4);  // 128 x 256, 8 waves of 64 x 64
     if (t128 > 128) QL_DENSE(2, 2, 2, 2);  // 128 x 128, 4 waves of 64 x 64
+    // At most 128 tiles of 64 x 128 leave CUs idle: 64 x 64 tiles of two
+    // waves double the workgroups (each activation row is then staged once
+    // per 64 columns instead of 128, which costs more than it gains once
+    // the 64 x 128 grid fills the chip).
+    if (((a.M + 63) / 64) * ((a.N + 127) / 128) <= 128) QL_DENSE(1, 2, 2, 1);  // 64 x 64, 2 waves of 32 x 64
     QL_DENSE(1, 2, 2, 2);                  // 64 x 128, 4 waves of 32 x 64
 #undef QL_DENSE
 }

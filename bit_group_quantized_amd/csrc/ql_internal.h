@@ -128,7 +128,7 @@ constexpr int kTinyTileRows = 32;       // short tiles of at most this many rows
 constexpr int kRouterPartRows = 64;     // D rows per small-T router partial
 constexpr int kRouterSmallT = 16;       // T at or below: row-parallel router
 constexpr int kRouterMfmaSplit = 4;     // K splits of the MFMA router (partials per logit)
-constexpr int kRouterSmallParts = 32;   // small-T router: D split in 32 slices, one partial each
+constexpr int kRouterSmallParts = 8;    // small-T router: D split in 8 slices, one partial each
 
 struct RouteArgs {
     const uint16_t* H;

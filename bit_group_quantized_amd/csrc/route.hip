@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kChunk = kRouteChunkTokens;
 constexpr int kMaskWords = kChunk / 32;
-constexpr int kRouterParts = kRouterSmallParts;  // row-parallel router: D split in 32 slices
+constexpr int kRouterParts = kRouterSmallParts;  // row-parallel router: D split in 8 slices
 constexpr int kRouterMfmaParts = kRouterMfmaSplit;  // MFMA router: K split
 
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
@@ -82,7 +82,7 @@ __device__ __forceinline__ void router_partial_body(const uint16_t* __restrict__
 }
 
 // The same partial sums, one block per (D slice, group of 32 experts), for
-// more parallelism at few tokens (8 x as many blocks, each reading 4 KB of
+// more parallelism at few tokens (8 x as many blocks, each reading 16 KB of
 // the router weight at D = 2048): thread (rl, sg) covers the slice's rows
 // rl, rl + 64, ... for experts 32g + 8sg .. 32g + 8sg + 7 (one 16-byte load
 // per row); the 64 row lanes of each expert are summed in a fixed order
@@ -103,6 +103,7 @@ __device__ __forceinline__ void router_partial_grp_body(const uint16_t* __restri
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[v] = 0.f;
     if (e8 < E) {
+#pragma unroll 4  // a slice of 256 rows: the four row loads of a thread go out together
         for (int d = rl; d < rows; d += 64) {
             const float h = in16<BF16>(H[(size_t)t * D + d0 + d]);
             const u32x4 wv = ld_u32x4(Wr + (size_t)(d0 + d) * E + e8);

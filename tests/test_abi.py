@@ -301,7 +301,7 @@ def test_moe_decode_validation(L):
     assert wsb > 0
     assert L.moe_decode_workspace_bytes(5, 256, 8, 512) == 0   # T > QL_DECODE_MAX_T
     assert L.moe_decode_workspace_bytes(1, 256, 300, 512) == 0
-    assert L.moe_decode_logits_offset(1, 256, 8) >= 32 * 256 * 4
+    assert L.moe_decode_logits_offset(1, 256, 8) >= 8 * 256 * 4   # after the 8 router partials of 256 fp32
     f = L.moe_decode
 
     def call(T=1, D=2048, E=256, topk=8, gu=GU, dn=DN, sg=SG, sd=SD, H=A16, ws=A16, wsb=wsb, out=A16):

@@ -1230,7 +1230,11 @@ namespace {
 template <int TPR, int V, int EPL, bool BF16, int WF = 0>
 void launch_decode_gate_up_t(const DecodeArgs& a, const DecodeLayout& L, hipStream_t st) {
     constexpr int TEAMS = 64 / TPR;
-    constexpr int R = (TPR < 8) ? TPR : 8;
+    // Rows per team: 8, or 4 where each row's decode costs more (bf16
+    // activations, FP8 codes), which spreads the launch over twice the
+    // workgroups (measured faster for those two, no change for w4 fp16).
+    constexpr int RMAX = (BF16 || WF == 1) ? 4 : 8;
+    constexpr int R = (TPR < RMAX) ? TPR : RMAX;
     static_assert(R % 2 == 0, "gate/up pairing needs an even row count");
     constexpr int COLS = 4 * TEAMS * (R / 2);  // act columns per block
     const int has_shared = a.sgu_qw != nullptr;

@@ -661,6 +661,19 @@ def bench_moe_decode(args, dev, w):
     torch.cuda.synchronize()
     ms = graph_time(layer, NG, 30)
     ms3 = graph_time(step3, NG, 30)
+
+    # The same layer without the shared expert: what the shared expert costs
+    # in this launch chain at all (an upper bound on what moving its rows
+    # to an earlier launch could save).
+    def layer_ns(i):
+        dw = copies[i % 2]
+        ql.moe_decode(toks[i % len(toks)], dw["Wr"], None, 8, dw["gate_up"], dw["down"], None, None,
+                      out=dec_buf)
+
+    for i in range(3):
+        layer_ns(i)
+    torch.cuda.synchronize()
+    ms_ns = graph_time(layer_ns, NG, 30)
     # The bf16 layer (moe_decode_bf16), same rotation of tokens and weights.
     wb = synth.moe_weights_bf16(0)
     as_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else np.int32)).to(dev)
@@ -725,6 +738,7 @@ def bench_moe_decode(args, dev, w):
             "GB/s": algo / (ms * 1e-3) / 1e9, "frac_hbm": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "entry": "moe_decode (router partials; routing fused into gate/up; down + combine)",
             "three_call_us_per_token": ms3 * 1e3,
+            "no_shared_expert_us_per_token": ms_ns * 1e3,
             "bf16_us_per_token": ms_bf * 1e3,
             "three_call_stage_us": {"route": k[0] * 1e3, "gate_up_silu": k[1] * 1e3,
                                     "down_combine": k[2] * 1e3},
@@ -1041,8 +1055,70 @@ def read_probe(dev):
     del buf
     torch.cuda.empty_cache()
     out["bytes_per_launch"] = PROBE_BYTES
+    out["short_reads"] = short_reads(dev, L)
     out["spec_peak_GB/s"] = HBM_PEAK_GBS
     return out
+
+
+def short_reads(dev, L):
+    """Reads of a few MB with the "rows" pattern, one launch per HIP-graph
+    node (64 nodes, replayed), each launch on a buffer of its own (together
+    more than the 256 MB Infinity Cache), beside the K 2048 x N 8192
+    projection GEMV timed the same way over rotated weight copies: the read
+    floor of a launch of that size.  The fit over the sizes gives the fixed
+    cost of a launch and the marginal read rate."""
+    import ctypes
+    import torch
+    import bit_group_quantized_amd as ql
+    import synth
+    proj = w4_bytes(2048, 8192)  # 9,457,664 B, a multiple of 1024
+    sizes = [proj, 2 * proj, 4 * proj]
+    res = {"projection_bytes": proj, "reads": []}
+    for nbytes in sizes:
+        nbuf = max(4, (700 << 20) // nbytes)
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nbuf)]
+        words = torch.empty(int(L.ql_probe_out_words(0, nbytes)), dtype=torch.int32, device=dev)
+
+        def rd(i, bufs=bufs, words=words, nbytes=nbytes):
+            # the current stream: the capture stream while a graph is recorded
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            rc = L.ql_read_probe(0, bufs[i % len(bufs)].data_ptr(), nbytes, words.data_ptr(), st)
+            if rc != 0:
+                raise RuntimeError(f"ql_read_probe failed with status {rc}")
+
+        for i in range(3):
+            rd(i)
+        torch.cuda.synchronize()
+        ms = graph_time(rd, 64, 20)
+        res["reads"].append({"bytes": nbytes, "us_per_launch": ms * 1e3, "GB/s": nbytes / (ms * 1e-3) / 1e9})
+        del bufs
+    torch.cuda.empty_cache()
+    xs = np.array([r["bytes"] for r in res["reads"]], dtype=np.float64)
+    ys = np.array([r["us_per_launch"] for r in res["reads"]], dtype=np.float64)
+    slope, icpt = np.polyfit(xs, ys, 1)
+    res["fit_fixed_us"] = float(icpt)
+    res["fit_marginal_GB/s"] = float(1e-3 / slope)
+    case = synth.gemv_case(0, 2048, 8192)
+    base = {"qweight": torch.from_numpy(case["W"]["qweight"].view(np.int32)).to(dev),
+            "scales": torch.from_numpy(case["W"]["scales"]).to(dev),
+            "biases": torch.from_numpy(case["W"]["biases"]).to(dev), "K": 2048, "N": 8192}
+    ncopy = max(4, (700 << 20) // proj)
+    copies = [base] + [clone_w4(base) for _ in range(ncopy - 1)]
+    x = torch.from_numpy(case["x"][0]).to(dev)
+    y = torch.empty(8192, dtype=torch.float16, device=dev)
+
+    def gv(i):
+        ql.qlinear_gemv(copies[i % ncopy], x, y)
+
+    for i in range(3):
+        gv(i)
+    torch.cuda.synchronize()
+    ms = graph_time(gv, 64, 20)
+    res["projection_gemv_us"] = ms * 1e3
+    res["projection_gemv_over_read"] = ms * 1e3 / res["reads"][0]["us_per_launch"]
+    del copies
+    torch.cuda.empty_cache()
+    return res
 
 
 def probe_lib():

@@ -566,3 +566,35 @@ def test_moe_shared_expert_on_a_second_stream():
             assert np.array_equal(host(act).view(np.uint16), a_ref.view(np.uint16))
             assert np.array_equal(host(yd).view(np.uint16), y_ref.view(np.uint16))
             assert np.array_equal(host(outs[i]).view(np.uint16), o_ref.view(np.uint16))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [40, 600])
+def test_moe_shared_only_ragged_rows(T):
+    """A launch of the shared expert alone (QL_OP_SHARED_ONLY) with a token
+    count that ends in a partial tile: the shared rows of act and ydown
+    equal the single launch's bit for bit and the routed rows are left
+    untouched (guard value)."""
+    import torch
+    topk = 8
+    say(f"shared-only ragged T={T}")
+    w = synth.moe_weights(0)
+    dw = _dev_weights(w)
+    tk = synth.moe_tokens(7, T, skewed=True)
+    H, b = t(tk["H"]), t(tk["logit_bias"])
+    route, act, yd, _ = _run_layer(dw, H, b, topk, T, False)
+    torch.cuda.synchronize()
+    fill = np.float16(-3.0).view(np.uint16)
+    act2 = torch.full_like(act, -3.0)
+    yd2 = torch.full_like(yd, -3.0)
+    ql.moe_grouped_gemm(dw["gate_up"], dw["shared_gate_up"], H, T, topk,
+                        ql.QL_OP_GATE_UP_SILU | ql.QL_OP_SHARED_ONLY, None, act2)
+    ql.moe_grouped_gemm(dw["down"], dw["shared_down"], act, T, topk,
+                        ql.QL_OP_DOWN | ql.QL_OP_SHARED_ONLY, None, yd2)
+    torch.cuda.synchronize()
+    r = T * topk
+    a_g, a_r = host(act2).view(np.uint16), host(act).view(np.uint16)
+    y_g, y_r = host(yd2).view(np.uint16), host(yd).view(np.uint16)
+    assert np.array_equal(a_g[r:], a_r[r:])
+    assert np.array_equal(y_g[r:], y_r[r:])
+    assert np.all(a_g[:r] == fill) and np.all(y_g[:r] == fill)

@@ -1253,7 +1253,7 @@ def cpu_baseline():
     c0 = synth.gemv_case(0, 512, 512)
     reps, dt = _repeat(lambda: oracle.linear(c0["x"], c0["W"]), 2.0)
     b0 = w4_bytes(512, 512) + 2 * 512 * 2
-    per["config0_gemv_K512_N512"] = {"GB/s": reps * b0 / dt / 1e9, "s_per_call": dt / reps,
+    per["gemv_K512_N512"] = {"GB/s": reps * b0 / dt / 1e9, "s_per_call": dt / reps,
                                      "sample": f"whole workload, {reps} calls in {dt:.1f} s"}
     # config 1: the 8192-row projection and the first 16384 rows of the head
     small = synth.gemv_case(0, K, 8192)
@@ -1261,21 +1261,21 @@ def cpu_baseline():
     b1 = sum(w4_bytes(K, N) + 2 * K + 2 * N for N in (8192, 16384))
     reps, dt = _repeat(lambda: (oracle.linear(small["x"], small["W"]), oracle.linear(head["x"], head["W"])), 8.0)
     g1 = reps * b1 / dt / 1e9
-    per["config1_gemv_K2048_N8192_N151552"] = {
+    per["gemv_K2048_N8192_and_N151552"] = {
         "GB/s": g1, "s_per_step_extrapolated": (w4_bytes(K, 8192) + w4_bytes(K, 151552)) / (g1 * 1e9),
         "sample": f"the 2048x8192 matrix and 16384 of the head's 151552 rows, {reps} repetitions in {dt:.1f} s"}
     # config 2: 64 of the 4096 rows of X through the whole 2048 x 8192 matrix
     c2 = synth.gemm_case(0, 64, K, 8192)
     reps, dt = _repeat(lambda: oracle.linear(c2["X"], c2["W"]), 4.0)
     f2 = 2.0 * 64 * K * 8192
-    per["config2_gemm_K2048_N8192"] = {"GFLOP/s": reps * f2 / dt / 1e9, "rows_per_s": reps * 64 / dt,
+    per["gemm_K2048_N8192"] = {"GFLOP/s": reps * f2 / dt / 1e9, "rows_per_s": reps * 64 / dt,
                                       "sample": f"64 rows of X, {reps} calls in {dt:.1f} s"}
     # config 3: one decode token through the whole layer
     w = synth.moe_weights(0)
     tok = synth.moe_tokens(2000, 1)
     reps, dt = _repeat(lambda: oracle.moe_layer(tok["H"], w, None, 8), 4.0)
     b3 = 2048 * 256 * 2 + 9 * (w4_bytes(2048, 1024) + w4_bytes(512, 2048)) + 2 * 2048 * 2
-    per["config3_moe_decode_1tok"] = {"tokens/s": reps / dt, "GB/s": reps * b3 / dt / 1e9,
+    per["moe_decode_1tok"] = {"tokens/s": reps / dt, "GB/s": reps * b3 / dt / 1e9,
                                       "sample": f"one token, {reps} calls in {dt:.1f} s"}
     # config 4: 64 of the 4096 Zipf-biased prefill tokens through the layer
     seed = json.load(open(os.path.join(ROOT, "tests", "golden", "prefill_seeds.json")))["kept_seeds_by_gap"][0]
@@ -1284,10 +1284,10 @@ def cpu_baseline():
     reps, dt = _repeat(lambda: oracle.moe_layer(H4, w, t4["logit_bias"], 8), 4.0)
     f4 = 64 * (2.0 * 8 * 2048 * 1024 + 2.0 * 8 * 512 * 2048 + 2.0 * 2048 * 1024 + 2.0 * 512 * 2048
                + 2.0 * 2048 * 256)
-    per["config4_moe_prefill"] = {"tokens/s": reps * 64 / dt, "GFLOP/s": reps * f4 / dt / 1e9,
+    per["moe_prefill_4096tok"] = {"tokens/s": reps * 64 / dt, "GFLOP/s": reps * f4 / dt / 1e9,
                                   "sample": f"64 of the 4096 tokens (seed {seed}), {reps} calls in {dt:.1f} s"}
     return {"value": g1, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": per["config1_gemv_K2048_N8192_N151552"]["sample"] +
+            "sample": per["gemv_K2048_N8192_and_N151552"]["sample"] +
                       f" (oracle.linear, numpy fp64); BLAS threads {threads}, host cpu_count {os.cpu_count()}, "
                       f"affinity {len(os.sched_getaffinity(0))}",
             "per_config": per}
